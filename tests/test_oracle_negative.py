@@ -1,0 +1,65 @@
+"""Negative controls: a pin set that never goes red proves nothing.
+
+Each case copies oracle.c, plants one plausible mistake (a dropped term, a
+wrong sign, index or operand order), builds it into a temporary library and
+checks that at least one pin fails on it.  Runs on the CPU only.
+"""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+import oracle_pins as P
+
+MUTATIONS = [
+    ("nibble_halves_swapped", "(i < 16) ? (blk[2 + i] & 0x0F)", "(i >= 16) ? (blk[2 + i] & 0x0F)"),
+    ("q4_bias_off_by_one", "out[i] = d * (double)(c - 8);", "out[i] = d * (double)(c - 7);"),
+    ("q3_high_bit_weight", "int c = lo | (hi << 2);", "int c = lo | (hi << 1);"),
+    ("q3_low_field_index", "(blk[2 + (i % 8)] >> (2 * (i / 8))) & 3", "(blk[2 + (i / 4)] >> (2 * (i % 4))) & 3"),
+    ("half_exponent_bias", "expo - 15", "expo - 14"),
+    ("half_subnormal", "ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
+    ("tie_to_higher_id", "l[e] > l[best]", "l[e] >= l[best]"),
+    ("softmax_not_renormalised", "exp((double)l[idx[(int64_t)t * k + j]] - lmax) / sum;",
+     "exp((double)l[idx[(int64_t)t * k + j]] - lmax) / (sum + 1.0);"),
+    ("group_order_reversed", "pairs[offsets[e] + fill[e]] = (int32_t)p;",
+     "pairs[offsets[e + 1] - 1 - fill[e]] = (int32_t)p;"),
+    ("swiglu_operands_swapped", "hid[f] = g / (1.0 + exp(-g)) * u;", "hid[f] = u / (1.0 + exp(-u)) * g;"),
+    ("down_input_reversed", "acc += dr[f] * hid[f];", "acc += dr[f] * hid[F - 1 - f];"),
+    ("shared_expert_dropped", "    if (shared) {\n        orc_expert sx;", "    if (0) {\n        orc_expert sx;"),
+    ("combine_drops_last_slot", "for (j = 1; j < k; ++j) acc += w", "for (j = 1; j < k - 1; ++j) acc += w"),
+    ("gate_up_swapped", "orc_dequant_matrix(bits, blob, F, H, ex->gate);",
+     "orc_dequant_matrix(bits, blob, F, H, ex->up);"),
+]
+
+
+@pytest.fixture(scope="module")
+def tmpdir_mod():
+    d = tempfile.mkdtemp(prefix="orc_mut_")
+    yield d
+    shutil.rmtree(d, ignore_errors=True)
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(tmpdir_mod, name, old, new):
+    src = open(oracle._SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique for {name}"
+    mut = src.replace(old, new)
+    if name == "gate_up_swapped":  # load up into gate's slot too, so up reads gate's bytes
+        mut = mut.replace("orc_dequant_matrix(bits, blob + mat, F, H, ex->up);",
+                          "orc_dequant_matrix(bits, blob + mat, F, H, ex->gate);")
+    c_path = os.path.join(tmpdir_mod, f"{name}.c")
+    so_path = os.path.join(tmpdir_mod, f"lib{name}.so")
+    open(c_path, "w").write(mut)
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", so_path, c_path, "-lm"],
+                   check=True)
+    bad = oracle.Oracle(oracle.load(so_path))
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            pin(bad)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {name}"
