@@ -1,0 +1,176 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed mixture-of-experts layer over
+ * block-quantized expert weights.
+ *
+ * The layer (what the calls below compute, in order):
+ *   1. router: per token, the k experts with the largest router logits and a
+ *      softmax over those k logits (forum thread "把 Strata 搬上 SGLang 引擎
+ *      的嘗試", TL;DR and §三: top-10 of 512 experts; extended-strata-moe
+ *      "Reference", section "Routing trace format": k expert ids and k
+ *      weights per token and layer);
+ *   2. grouping: the (token, expert) pairs bucketed per expert, so each
+ *      expert computes only the rows routed to it (thread §二, the
+ *      expert-scoped layout);
+ *   3. per expert: gather of its rows, dequantization inside the kernel,
+ *      gate/up projection, SwiGLU, down projection, weighted scatter-add back
+ *      to the tokens, all in one grouped call per layer (thread TL;DR and §三,
+ *      the grouped expert kernel and its one-call-per-layer timing);
+ *   4. the shared expert, applied to every row of the window (Strata "Several
+ *      requests at once (batch slots)", opening section: the shared expert is
+ *      read once per window for all rows).
+ *
+ * Weight format.  Block of 32 weights with an fp16 scale d (thread §四: the
+ * 4-bit block of 32 values in 18 bytes):
+ *   bits = 4: 18 bytes = d (2 bytes, little-endian binary16) + 16 bytes;
+ *             byte 2+i holds code i in its low nibble, code i+16 in its high
+ *             nibble; weight = d * (code - 8).
+ *   bits = 3: 14 bytes = d + 8 bytes of low parts (code i's two low bits at
+ *             bit 2*(i/8) of byte 2+(i%8)) + a 32-bit little-endian word at
+ *             bytes 10..13 whose bit i is code i's third bit;
+ *             weight = d * (code - 4).
+ * A matrix [rows][cols] is stored row by row, cols/32 blocks per row, with
+ * no padding.  One expert's blob is gate [F][H] | up [F][H] | down [H][F]
+ * (gate, up and down concatenated per expert, thread §三: the blob fed to the
+ * kernel without conversion); experts follow each other with no padding.
+ * The nibble order and the whole 3-bit layout are readings of points the
+ * pages leave open.
+ *
+ * Conventions for every call:
+ *  - Pointers marked (device) point to GPU memory on the current HIP device;
+ *    (host) to host memory.  The caller owns every buffer and the stream.
+ *    The library allocates nothing, frees nothing and never synchronizes;
+ *    all work is enqueued on `stream` (a hipStream_t passed as int64_t,
+ *    0 = the null stream), so calls can be captured into a hipGraph.
+ *  - Row-major, contiguous tensors; device pointers 16-byte aligned.
+ *  - Errors: 0 (MOE_OK) or a negative MOE_ERR_* code.  Arguments are
+ *    validated on the host before anything is launched; on an error nothing
+ *    is launched and no output is touched.  MOE_ERR_LAUNCH reports a failed
+ *    kernel launch (hipGetLastError after the launch).  Device-side input
+ *    checks are not made: logits must be finite.
+ *  - The workspace (device) must be at least moe_workspace_bytes(...) bytes
+ *    and zero-filled before its first use.  Every call leaves its counters
+ *    at zero again, so a workspace can be reused by later calls (and graph
+ *    replays) without clearing.  Two calls that run at the same time must
+ *    not share a workspace.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1)  /* null pointer, negative or inconsistent size */
+#define MOE_ERR_UNSUPPORTED (-2)  /* bits not 3/4, H or F not a multiple of 256, ... */
+#define MOE_ERR_WORKSPACE (-3)    /* workspace smaller than moe_workspace_bytes */
+#define MOE_ERR_LAUNCH (-4)       /* a kernel launch failed */
+#define MOE_ERR_DEVICE (-5)       /* no usable gfx950 device / device query failed */
+
+/* activation dtypes */
+#define MOE_DTYPE_F32 0
+#define MOE_DTYPE_BF16 1
+
+/* which kernels run the expert FFN */
+#define MOE_PATH_AUTO 0     /* DECODE when T <= MOE_DECODE_MAX_ROWS, else PREFILL */
+#define MOE_PATH_DECODE 1   /* one fused launch per layer, T <= MOE_DECODE_MAX_ROWS */
+#define MOE_PATH_PREFILL 2  /* grouped GEMM over per-expert row tiles, any T */
+
+/* Rows per decode window: one token per batch slot plus its MTP proposal,
+ * up to 16 rows (Strata "Several requests at once", section "Windows of 16
+ * rows": HIP builds take windows of 16 rows). */
+#define MOE_DECODE_MAX_ROWS 16
+
+/* Limits of this build. */
+#define MOE_MAX_EXPERTS 4096
+#define MOE_MAX_TOPK 32
+
+/* Quantized expert weights (host struct; `data` is a device pointer). */
+typedef struct moe_qweights {
+    const void *data;   /* (device) n_experts blobs back to back, see above */
+    int32_t bits;       /* 3 or 4 */
+    int32_t n_experts;  /* routed: E; shared: 1 */
+    int32_t hidden;     /* H, multiple of 256 */
+    int32_t ffn;        /* F, multiple of 256 */
+} moe_qweights;
+
+/* Library version (major*100 + minor). */
+int moe_version(void);
+
+/* Text for a status code; never NULL. */
+const char *moe_status_string(int status);
+
+/* Bytes of one expert blob: 3 * hidden * ffn/32 * (18 or 14); -1 if the
+ * arguments are not a valid shape (pure host function). */
+int64_t moe_expert_bytes(int32_t bits, int32_t hidden, int32_t ffn);
+
+/* Workspace bytes needed by moe_layer_forward / moe_expert_ffn for these
+ * shapes on `path` (AUTO resolves as the calls do).  shared_ffn = 0 when
+ * there is no shared expert.  Returns a negative MOE_ERR_* for invalid
+ * shapes.  Pure host function. */
+int64_t moe_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t hidden, int32_t ffn,
+                            int32_t shared_ffn, int32_t path);
+
+/*
+ * Router (step 1).  logits (device) fp32 [T][E]; writes topk_idx (device)
+ * int32 [T][k] and topk_w (device) fp32 [T][k].  Per token the k experts are
+ * listed by decreasing logit, an equal logit going to the lower expert id
+ * (selection compares the fp32 logits themselves); topk_w[t][j] =
+ * exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k selected, so a row's
+ * weights sum to one.  1 <= k <= min(E, MOE_MAX_TOPK), E <= MOE_MAX_EXPERTS.
+ */
+int moe_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *topk_idx,
+              float *topk_w, int64_t stream);
+
+/*
+ * Grouping (step 2).  topk_idx (device) int32 [T][k], every id in [0, E).
+ * Pair id p = t*k + j.  Writes (device): offsets int32 [E+1] (exclusive
+ * prefix sum of the per-expert pair counts, offsets[E] = T*k); pairs int32
+ * [T*k] (the pair ids of expert 0, then expert 1, ..., each expert's in
+ * increasing p, i.e. ordered by (expert, token, slot)); active int32 [E+1]
+ * (active[0] = number of experts with at least one pair, then their ids in
+ * ascending order; the tail is not written).  The placement is stable and
+ * deterministic.  ws (device) is scratch of at least
+ * moe_workspace_bytes(T, E, k, ...) bytes (any path).
+ */
+int moe_group(const int32_t *topk_idx, int32_t T, int32_t E, int32_t k, int32_t *offsets,
+              int32_t *pairs, int32_t *active, void *ws, int64_t ws_bytes, int64_t stream);
+
+/*
+ * Routed expert FFN (step 3) on a given grouping.  x (device) [T][H] fp32 or
+ * bf16 (x_dtype).  offsets/pairs/active (device) as written by moe_group for
+ * w->n_experts experts and top-k = k.  pair_w (device) fp32 [T*k] or NULL
+ * (weight 1).  For every listed pair p (token t = p/k) of every active
+ * expert e:
+ *     out_pairs[p][:] = pair_w[p] * down_e( silu(gate_e x_t) * (up_e x_t) )
+ * out_pairs (device) fp32 [T*k][H]; rows of pairs that are not listed are
+ * not written.  path selects the kernels (DECODE needs T <= 16).
+ */
+int moe_expert_ffn(const void *x, int32_t x_dtype, int32_t T, const moe_qweights *w,
+                   const int32_t *offsets, const int32_t *pairs, const int32_t *active,
+                   const float *pair_w, int32_t k, float *out_pairs, int32_t path, void *ws,
+                   int64_t ws_bytes, int64_t stream);
+
+/*
+ * The whole layer (steps 1-4).  x (device) [T][H] fp32 or bf16; logits
+ * (device) fp32 [T][E] with E = routed->n_experts; shared (host struct, may
+ * be NULL) with n_experts = 1 and the same hidden.  Writes y (device) fp32
+ * [T][H]:
+ *     y_t = (((w_t0 o_t0 + w_t1 o_t1) + ...) + w_t,k-1 o_t,k-1) + s_t
+ * with o_tj the output of token t's j-th expert, w_tj its router weight and
+ * s_t the shared expert's output, summed in that fixed order (the result
+ * does not depend on launch geometry or timing).  topk_idx_out / topk_w_out
+ * (device, may be NULL) receive the routing ([T][k] int32 / fp32).
+ */
+int moe_layer_forward(const void *x, int32_t x_dtype, const float *logits, int32_t T,
+                      int32_t k, const moe_qweights *routed, const moe_qweights *shared,
+                      float *y, int32_t *topk_idx_out, float *topk_w_out, int32_t path,
+                      void *ws, int64_t ws_bytes, int64_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

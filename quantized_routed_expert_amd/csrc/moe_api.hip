@@ -1,0 +1,437 @@
+// moe_api.hip -- the C ABI (include/moe.h): host-side validation, workspace
+// layout and dispatch.  Arguments follow the statement of the layer on the
+// pages (hidden states, router logits, top-k, quantized expert tensors, the
+// shared expert); conventions on errors and sizing follow the
+// extended-strata-moe "Reference", section "C API" (a query that does not
+// apply reports it and leaves its outputs untouched).  The stream is taken as
+// an int64 so no HIP type appears in the interface (the forum thread
+// "把 Strata 搬上 SGLang 引擎 的嘗試", §三, passes its stream the same way).
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace moe {
+hipError_t decode_launch(const DecodeParams &P, int grid, hipStream_t st);
+int decode_occupancy(int bits, int x_f32, int lds);
+hipError_t decode_set_lds(int bits, int x_f32, int lds);
+int decode_chunk_blocks(int nkb);
+hipError_t route_launch(const RouteParams &P, hipStream_t st);
+hipError_t group_launch(const GroupParams &P, hipStream_t st);
+}  // namespace moe
+
+namespace moe {
+hipError_t prefill_plan_launch(const PlanParams &P, hipStream_t st);
+hipError_t prefill_gemm_launch(int mode, int bits, const GemmParams &P, int grid, hipStream_t st);
+hipError_t prefill_combine_launch(const CombineParams &P, hipStream_t st);
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+// ----------------------------------------------------------------------------
+// Device facts (cached per device)
+// ----------------------------------------------------------------------------
+struct DevInfo {
+    int ok = 0;
+    int cus = 0;
+    int lds_max = 0;
+};
+std::mutex g_mu;
+DevInfo g_dev[64];
+
+int dev_info(DevInfo &out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_DEVICE;
+    std::lock_guard<std::mutex> lk(g_mu);
+    DevInfo &d = g_dev[dev];
+    if (!d.ok) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess) return MOE_ERR_DEVICE;
+        if (strncmp(p.gcnArchName, "gfx950", 6) != 0) return MOE_ERR_DEVICE;
+        d.cus = p.multiProcessorCount;
+        d.lds_max = (int)p.maxSharedMemoryPerMultiProcessor;
+        d.ok = 1;
+    }
+    out = d;
+    return MOE_OK;
+}
+
+// ----------------------------------------------------------------------------
+// Workspace layout
+// ----------------------------------------------------------------------------
+struct Layout {
+    size_t counters = 0, n_counters = 0;       // decode: gu[MS] dn[MS] slice[H/128] err[4]
+    size_t harr = 0, out_pairs = 0, out_shared = 0;
+    size_t idx = 0, w = 0, offsets = 0, pairs = 0, active = 0, chunk_counts = 0;
+    size_t slot_exp = 0, slot_row0 = 0, slot_cnt = 0, slot_hrow0 = 0, prefix_gu = 0, prefix_dn = 0;
+    size_t hbuf = 0;
+    size_t total = 0;
+    int max_slots = 0, nchunks = 0;
+};
+
+Layout make_layout(int T, int E, int k, int H, int F, int Fs, int path) {
+    Layout L;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    const size_t TK = (size_t)T * k;
+    const int Fmax = F > Fs ? F : Fs;
+    L.nchunks = (T + GRP_CHUNK_TOKENS - 1) / GRP_CHUNK_TOKENS;
+    L.max_slots = (int)((TK < (size_t)E ? TK : (size_t)E) + 1);
+    // routing and grouping (all paths; moe_group uses chunk_counts)
+    L.idx = take(TK * 4);
+    L.w = take(TK * 4);
+    L.offsets = take((size_t)(E + 1) * 4);
+    L.pairs = take(TK * 4);
+    L.active = take((size_t)(E + 1) * 4);
+    L.chunk_counts = take((size_t)L.nchunks * E * 4);
+    L.out_pairs = take(TK * H * 4);
+    L.out_shared = take((size_t)T * H * 4);
+    if (path == MOE_PATH_DECODE) {
+        L.n_counters = (size_t)2 * L.max_slots + H / DEC_DN_ROWS + 4;
+        L.counters = take(L.n_counters * 4);
+        L.harr = take((TK + T) * (size_t)Fmax * 4);
+    } else {
+        L.slot_exp = take((size_t)(E + 1) * 4);
+        L.slot_row0 = take((size_t)(E + 1) * 4);
+        L.slot_cnt = take((size_t)(E + 1) * 4);
+        L.slot_hrow0 = take((size_t)(E + 1) * 4);
+        L.prefix_gu = take((size_t)(E + 3) * 4);
+        L.prefix_dn = take((size_t)(E + 3) * 4);
+        L.hbuf = take((TK + T) * (size_t)Fmax * 4);
+    }
+    L.total = off;
+    return L;
+}
+
+template <class Tp>
+Tp *at(void *ws, size_t off) {
+    return (Tp *)((uint8_t *)ws + off);
+}
+
+// ----------------------------------------------------------------------------
+// Validation helpers
+// ----------------------------------------------------------------------------
+int check_shape(int32_t T, int32_t E, int32_t k, int32_t H, int32_t F) {
+    if (T < 0 || E <= 0 || k <= 0 || H <= 0 || F <= 0) return MOE_ERR_INVALID_ARG;
+    if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || k > E) return MOE_ERR_UNSUPPORTED;
+    if (H % 256 || F % 256 || H > 65536 || F > 65536) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)T * k > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int check_weights(const moe_qweights *w, int H, int n_experts) {
+    if (!w || !w->data) return MOE_ERR_INVALID_ARG;
+    if (w->bits != 3 && w->bits != 4) return MOE_ERR_UNSUPPORTED;
+    if (w->hidden != H) return MOE_ERR_INVALID_ARG;
+    if (n_experts >= 0 && w->n_experts != n_experts) return MOE_ERR_INVALID_ARG;
+    if (w->ffn <= 0) return MOE_ERR_INVALID_ARG;
+    if (w->ffn % 256) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int resolve_path(int path, int T) {
+    if (path == MOE_PATH_AUTO) return T <= MOE_DECODE_MAX_ROWS ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+    return path;
+}
+
+inline hipStream_t S(int64_t s) { return (hipStream_t)(intptr_t)s; }
+
+// Fill the decode kernel's LDS layout; returns the byte total.
+int decode_lds_layout(DecodeParams &P, int xparts) {
+    const int TK = P.T * P.k;
+    const int Fmax = P.F > P.Fs ? P.F : P.Fs;
+    int off = 0;
+    auto take = [&](int bytes) {
+        int a = off;
+        off = (int)align_up((size_t)(off + bytes), 16);
+        return a;
+    };
+    P.lds_idx = take(TK * 4);
+    P.lds_w = take(TK * 4);
+    P.lds_sorted = take(TK * 4);
+    P.lds_hist = take((P.E + 1) * 4);
+    P.lds_slot_start = take(P.max_slots * 4);
+    P.lds_slot_exp = take(P.max_slots * 4);
+    P.lds_slot_cnt = take(P.max_slots * 4);
+    P.lds_tinv = take(P.T * 4);
+    P.lds_misc = take(64);
+    const int xa_bytes = xparts * P.T * P.H * 2;
+    const int ha_bytes = P.T * Fmax * 4;
+    P.lds_xa = take(xa_bytes > ha_bytes ? xa_bytes : ha_bytes);
+    const int bb = P.bits == 4 ? 18 : 14;
+    const int cbH = decode_chunk_blocks(P.H / 32);
+    int cbF = decode_chunk_blocks(P.F / 32);
+    if (P.Fs) {
+        int c2 = decode_chunk_blocks(P.Fs / 32);
+        cbF = c2 > cbF ? c2 : cbF;
+    }
+    const int cmax = cbH > cbF ? cbH : cbF;
+    P.chunk_stride = (int)align_up((size_t)(16 * cmax * bb + 16), 16);
+    P.lds_chunk = take(DEC_WAVES * P.chunk_stride);
+    P.lds_total = off;
+    return off;
+}
+
+int launch_err(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int moe_version(void) { return 100; }
+
+const char *moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument (null pointer, negative or inconsistent size)";
+        case MOE_ERR_UNSUPPORTED: return "unsupported configuration (bits, shape or path)";
+        case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_bytes()";
+        case MOE_ERR_LAUNCH: return "kernel launch failed";
+        case MOE_ERR_DEVICE: return "no usable gfx950 device";
+        default: return "unknown status";
+    }
+}
+
+int64_t moe_expert_bytes(int32_t bits, int32_t hidden, int32_t ffn) {
+    if ((bits != 3 && bits != 4) || hidden <= 0 || ffn <= 0 || hidden % 32 || ffn % 32) return -1;
+    return (int64_t)3 * hidden * (ffn / 32) * (bits == 4 ? 18 : 14);
+}
+
+int64_t moe_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t hidden, int32_t ffn,
+                            int32_t shared_ffn, int32_t path) {
+    int rc = check_shape(T, E, k, hidden, ffn);
+    if (rc) return rc;
+    if (shared_ffn < 0 || shared_ffn % 256) return MOE_ERR_UNSUPPORTED;
+    if (path < MOE_PATH_AUTO || path > MOE_PATH_PREFILL) return MOE_ERR_INVALID_ARG;
+    Layout L = make_layout(T, E, k, hidden, ffn, shared_ffn, resolve_path(path, T));
+    return (int64_t)L.total;
+}
+
+int moe_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *topk_idx, float *topk_w,
+              int64_t stream) {
+    if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+    int rc = check_shape(T, E, k, 256, 256);
+    if (rc) return rc;
+    if (T == 0) return MOE_OK;
+    RouteParams P{logits, T, E, k, topk_idx, topk_w};
+    return launch_err(route_launch(P, S(stream)));
+}
+
+int moe_group(const int32_t *topk_idx, int32_t T, int32_t E, int32_t k, int32_t *offsets, int32_t *pairs,
+              int32_t *active, void *ws, int64_t ws_bytes, int64_t stream) {
+    if (!topk_idx || !offsets || !pairs || !active || !ws) return MOE_ERR_INVALID_ARG;
+    int rc = check_shape(T, E, k, 256, 256);
+    if (rc) return rc;
+    Layout L = make_layout(T, E, k, 256, 256, 0, MOE_PATH_PREFILL);
+    if (ws_bytes < (int64_t)(L.chunk_counts + (size_t)L.nchunks * E * 4)) return MOE_ERR_WORKSPACE;
+    GroupParams G{topk_idx, T, E, k, L.nchunks, at<uint32_t>(ws, L.chunk_counts), offsets, pairs, active};
+    return launch_err(group_launch(G, S(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Fused decode launch (routing in-kernel when logits != nullptr).
+int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_off, const int32_t *g_pairs,
+               const int32_t *g_act, const float *g_pw, int T, int E, int k, const moe_qweights *routed,
+               const moe_qweights *shared, float *y, float *out_pairs, int32_t *tidx, float *tw, const Layout &L,
+               void *ws, int mode, hipStream_t st) {
+    DevInfo dv;
+    int rc = dev_info(dv);
+    if (rc) return rc;
+    DecodeParams P;
+    memset(&P, 0, sizeof(P));
+    P.x = x;
+    P.logits = logits;
+    P.g_offsets = g_off;
+    P.g_pairs = g_pairs;
+    P.g_active = g_act;
+    P.g_pair_w = g_pw;
+    P.w_routed = (const uint8_t *)routed->data;
+    P.w_shared = shared ? (const uint8_t *)shared->data : nullptr;
+    P.y = y;
+    P.out_pairs = out_pairs;
+    P.out_shared = at<float>(ws, L.out_shared);
+    P.topk_idx_out = tidx;
+    P.topk_w_out = tw;
+    P.h_arr = at<uint8_t>(ws, L.harr);
+    uint32_t *cnt = at<uint32_t>(ws, L.counters);
+    P.gu_count = cnt;
+    P.dn_count = cnt + L.max_slots;
+    P.slice_count = cnt + 2 * L.max_slots;
+    P.err = cnt + 2 * L.max_slots + routed->hidden / DEC_DN_ROWS;
+    P.T = T;
+    P.E = E;
+    P.k = k;
+    P.H = routed->hidden;
+    P.F = routed->ffn;
+    P.Fs = shared ? shared->ffn : 0;
+    P.bits = routed->bits;
+    P.x_f32 = x_f32;
+    P.mode = mode | (shared ? DEC_MODE_SHARED : 0);
+    P.max_slots = L.max_slots;
+    const int Fmax = P.F > P.Fs ? P.F : P.Fs;
+    P.h_row_bytes = Fmax * 4;
+    const int lds = decode_lds_layout(P, x_f32 ? 2 : 1);
+    if (lds > dv.lds_max) return MOE_ERR_UNSUPPORTED;
+    static std::mutex mu;
+    static int lds_set[2][2] = {{0, 0}, {0, 0}};
+    int occ;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        int &cur = lds_set[P.bits == 4][x_f32 ? 1 : 0];
+        if (lds > cur) {
+            if (decode_set_lds(P.bits, x_f32, lds) != hipSuccess) return MOE_ERR_LAUNCH;
+            cur = lds;
+        }
+        occ = decode_occupancy(P.bits, x_f32, lds);
+    }
+    if (occ <= 0) return MOE_ERR_UNSUPPORTED;
+    // persistent grid: every workgroup resident (the down tiles wait on
+    // counters written by other workgroups' gate/up items)
+    const int grid = dv.cus * occ;
+    return launch_err(decode_launch(P, grid, st));
+}
+
+int prefill_gemms(const void *x, int x_f32, int T, int E, int k, const moe_qweights *routed,
+                  const moe_qweights *shared, const int32_t *pairs, const float *pair_w, float *out_pairs,
+                  float *out_shared, const Layout &L, void *ws, hipStream_t st) {
+    DevInfo dv;
+    int rc = dev_info(dv);
+    if (rc) return rc;
+    const int Fs = shared ? shared->ffn : 0;
+    const int Fmax = routed->ffn > Fs ? routed->ffn : Fs;
+    GemmParams G;
+    memset(&G, 0, sizeof(G));
+    G.x = x;
+    G.hbuf = at<float>(ws, L.hbuf);
+    G.hout = at<float>(ws, L.hbuf);
+    G.w_routed = (const uint8_t *)routed->data;
+    G.w_shared = shared ? (const uint8_t *)shared->data : nullptr;
+    G.pairs = pairs;
+    G.pair_w = pair_w;
+    G.out_pairs = out_pairs;
+    G.out_shared = out_shared;
+    G.slot_exp = at<int32_t>(ws, L.slot_exp);
+    G.slot_row0 = at<int32_t>(ws, L.slot_row0);
+    G.slot_cnt = at<int32_t>(ws, L.slot_cnt);
+    G.slot_hrow0 = at<int32_t>(ws, L.slot_hrow0);
+    G.T = T;
+    G.E = E;
+    G.k = k;
+    G.H = routed->hidden;
+    G.F = routed->ffn;
+    G.Fs = Fs;
+    G.h_stride = Fmax;
+    G.x_f32 = x_f32;
+    const int grid = dv.cus * 4;
+    G.prefix = at<int32_t>(ws, L.prefix_gu);
+    hipError_t e = prefill_gemm_launch(0, routed->bits, G, grid, st);
+    if (e != hipSuccess) return MOE_ERR_LAUNCH;
+    G.prefix = at<int32_t>(ws, L.prefix_dn);
+    e = prefill_gemm_launch(1, routed->bits, G, grid, st);
+    return launch_err(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_expert_ffn(const void *x, int32_t x_dtype, int32_t T, const moe_qweights *w, const int32_t *offsets,
+                   const int32_t *pairs, const int32_t *active, const float *pair_w, int32_t k, float *out_pairs,
+                   int32_t path, void *ws, int64_t ws_bytes, int64_t stream) {
+    if (!x || !w || !offsets || !pairs || !active || !out_pairs || !ws) return MOE_ERR_INVALID_ARG;
+    if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+    if (path < MOE_PATH_AUTO || path > MOE_PATH_PREFILL) return MOE_ERR_INVALID_ARG;
+    int rc = check_weights(w, w->hidden, -1);
+    if (rc) return rc;
+    rc = check_shape(T, w->n_experts, k, w->hidden, w->ffn);
+    if (rc) return rc;
+    const int p = resolve_path(path, T);
+    if (p == MOE_PATH_DECODE && T > MOE_DECODE_MAX_ROWS) return MOE_ERR_UNSUPPORTED;
+    Layout L = make_layout(T, w->n_experts, k, w->hidden, w->ffn, 0, p);
+    if (ws_bytes < (int64_t)L.total) return MOE_ERR_WORKSPACE;
+    if (T == 0) return MOE_OK;
+    const int xf = x_dtype == MOE_DTYPE_F32;
+    if (p == MOE_PATH_DECODE)
+        return run_decode(x, xf, nullptr, offsets, pairs, active, pair_w, T, w->n_experts, k, w, nullptr, nullptr,
+                          out_pairs, nullptr, nullptr, L, ws, 0, S(stream));
+    PlanParams PP{offsets, active, T, w->n_experts, k, 0, w->ffn, 0, w->hidden,
+                  at<int32_t>(ws, L.slot_exp), at<int32_t>(ws, L.slot_row0), at<int32_t>(ws, L.slot_cnt),
+                  at<int32_t>(ws, L.slot_hrow0), at<int32_t>(ws, L.prefix_gu), at<int32_t>(ws, L.prefix_dn)};
+    if (prefill_plan_launch(PP, S(stream)) != hipSuccess) return MOE_ERR_LAUNCH;
+    return prefill_gemms(x, xf, T, w->n_experts, k, w, nullptr, pairs, pair_w, out_pairs, nullptr, L, ws,
+                         S(stream));
+}
+
+int moe_layer_forward(const void *x, int32_t x_dtype, const float *logits, int32_t T, int32_t k,
+                      const moe_qweights *routed, const moe_qweights *shared, float *y, int32_t *topk_idx_out,
+                      float *topk_w_out, int32_t path, void *ws, int64_t ws_bytes, int64_t stream) {
+    if (!x || !logits || !routed || !y || !ws) return MOE_ERR_INVALID_ARG;
+    if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+    if (path < MOE_PATH_AUTO || path > MOE_PATH_PREFILL) return MOE_ERR_INVALID_ARG;
+    int rc = check_weights(routed, routed->hidden, -1);
+    if (rc) return rc;
+    if (shared) {
+        rc = check_weights(shared, routed->hidden, 1);
+        if (rc) return rc;
+    }
+    const int E = routed->n_experts, H = routed->hidden;
+    rc = check_shape(T, E, k, H, routed->ffn);
+    if (rc) return rc;
+    const int Fs = shared ? shared->ffn : 0;
+    int p = resolve_path(path, T);
+    const bool same_bits = !shared || shared->bits == routed->bits;
+    if (p == MOE_PATH_DECODE && (T > MOE_DECODE_MAX_ROWS || !same_bits)) {
+        if (path == MOE_PATH_DECODE) return MOE_ERR_UNSUPPORTED;
+        p = MOE_PATH_PREFILL;
+    }
+    Layout L = make_layout(T, E, k, H, routed->ffn, Fs, p);
+    if (ws_bytes < (int64_t)L.total) return MOE_ERR_WORKSPACE;
+    if (T == 0) return MOE_OK;
+    const int xf = x_dtype == MOE_DTYPE_F32;
+    hipStream_t st = S(stream);
+    int32_t *idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.idx);
+    float *wts = topk_w_out ? topk_w_out : at<float>(ws, L.w);
+    if (p == MOE_PATH_DECODE) {
+        if (E <= DEC_MAX_E_FUSED)
+            return run_decode(x, xf, logits, nullptr, nullptr, nullptr, nullptr, T, E, k, routed, shared, y,
+                              at<float>(ws, L.out_pairs), topk_idx_out, topk_w_out, L, ws,
+                              DEC_MODE_ROUTE | DEC_MODE_COMBINE, st);
+        RouteParams R{logits, T, E, k, idx, wts};
+        if (route_launch(R, st) != hipSuccess) return MOE_ERR_LAUNCH;
+        GroupParams G{idx, T, E, k, L.nchunks, at<uint32_t>(ws, L.chunk_counts), at<int32_t>(ws, L.offsets),
+                      at<int32_t>(ws, L.pairs), at<int32_t>(ws, L.active)};
+        if (group_launch(G, st) != hipSuccess) return MOE_ERR_LAUNCH;
+        return run_decode(x, xf, nullptr, at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.pairs),
+                          at<int32_t>(ws, L.active), wts, T, E, k, routed, shared, y, at<float>(ws, L.out_pairs),
+                          nullptr, nullptr, L, ws, DEC_MODE_COMBINE, st);
+    }
+    // prefill: route, group, plan, gate/up GEMM, down GEMM, combine
+    RouteParams R{logits, T, E, k, idx, wts};
+    if (route_launch(R, st) != hipSuccess) return MOE_ERR_LAUNCH;
+    GroupParams G{idx, T, E, k, L.nchunks, at<uint32_t>(ws, L.chunk_counts), at<int32_t>(ws, L.offsets),
+                  at<int32_t>(ws, L.pairs), at<int32_t>(ws, L.active)};
+    if (group_launch(G, st) != hipSuccess) return MOE_ERR_LAUNCH;
+    PlanParams PP{at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.active), T, E, k, shared ? 1 : 0, routed->ffn,
+                  Fs, H, at<int32_t>(ws, L.slot_exp), at<int32_t>(ws, L.slot_row0), at<int32_t>(ws, L.slot_cnt),
+                  at<int32_t>(ws, L.slot_hrow0), at<int32_t>(ws, L.prefix_gu), at<int32_t>(ws, L.prefix_dn)};
+    if (prefill_plan_launch(PP, st) != hipSuccess) return MOE_ERR_LAUNCH;
+    rc = prefill_gemms(x, xf, T, E, k, routed, shared, at<int32_t>(ws, L.pairs), wts, at<float>(ws, L.out_pairs),
+                       shared ? at<float>(ws, L.out_shared) : nullptr, L, ws, st);
+    if (rc) return rc;
+    CombineParams C{at<float>(ws, L.out_pairs), shared ? at<float>(ws, L.out_shared) : nullptr, y, T, k, H};
+    return launch_err(prefill_combine_launch(C, st));
+}
+
+}  // extern "C"

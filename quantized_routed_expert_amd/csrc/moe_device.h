@@ -1,0 +1,233 @@
+// moe_device.h -- device-side building blocks shared by the gfx950 kernels.
+//
+// Quantized blocks (block of 32 weights with an fp16 scale; the 4-bit block
+// is the one the forum thread "把 Strata 搬上 SGLang 引擎 的嘗試" names in §四):
+//   4-bit, 18 bytes: d, then byte 2+i = code i (low nibble) | code i+16 (high nibble)
+//   3-bit, 14 bytes: d, 8 bytes of 2-bit low parts (code i at bit 2*(i/8) of byte
+//                    2+(i%8)), 32-bit word at bytes 10..13 holding bit 2 of code i at bit i
+//
+// MFMA mapping (v_mfma_f32_16x16x32_{f16,bf16}, K = 32 = one block): lane l holds
+// row l%16 of A, column l%16 of B and the k-group l/16 of both; the result D
+// has rows 4*(l/16)+r, column l%16.  The eight k values a lane feeds in a
+// k-group are any eight of the block's 32 as long as A and B use the same
+// ones in the same order, so each format picks the order that makes its
+// codes cheapest to unpack, and activations are stored in that order.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int block_bytes(int bits) { return bits == 4 ? 18 : 14; }
+
+// ---------------------------------------------------------------------------
+// Element order inside one k-group (8 values) for each format.
+// pos_in_block(bits, g, e): which of the block's 32 weights is the e-th value
+// a lane of k-group g feeds.  Used to lay activations out to match.
+// ---------------------------------------------------------------------------
+__host__ __device__ __forceinline__ int pos_in_block(int bits, int g, int e) {
+    if (bits == 4) {
+        // e: 0:(4g) 1:(4g+2) 2:(16+4g) 3:(16+4g+2) 4:(4g+1) 5:(4g+3) 6:(16+4g+1) 7:(16+4g+3)
+        int r = ((e >> 2) & 1) + ((e & 1) << 1);
+        return 4 * g + r + ((e >> 1) & 1) * 16;
+    } else {
+        // e: 0:(2g) 1:(2g+16) 2:(2g+8) 3:(2g+24) 4:(2g+1) 5:(2g+17) 6:(2g+9) 7:(2g+25)
+        int f = ((e & 1) << 1) | ((e >> 1) & 1);  // 2-bit field index 0..3
+        return 2 * g + ((e >> 2) & 1) + 8 * f;
+    }
+}
+
+// Inverse: weight i of a block -> (k-group g, slot e).
+__host__ __device__ __forceinline__ void group_slot_of(int bits, int i, int &g, int &e) {
+    if (bits == 4) {
+        int r = i & 3, hi = (i >> 4) & 1;
+        g = (i & 15) >> 2;
+        e = ((r & 1) << 2) | (hi << 1) | (r >> 1);
+    } else {
+        int f8 = i >> 3;
+        g = (i & 7) >> 1;
+        e = ((i & 1) << 2) | ((f8 & 1) << 1) | (f8 >> 1);
+    }
+}
+
+__device__ __forceinline__ uint32_t pk_fma_h2(uint32_t v, uint32_t scale, uint32_t add) {
+    half2v a = __builtin_bit_cast(half2v, v);
+    half2v s = __builtin_bit_cast(half2v, scale);
+    half2v c = __builtin_bit_cast(half2v, add);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(a, s, c));
+}
+
+// fp16 constants as packed bit patterns (lo half first)
+#define H2(lo, hi) ((uint32_t)(lo) | ((uint32_t)(hi) << 16))
+// 1024 + m is exact in fp16 for 0 <= m < 1024: OR-ing a code into the low
+// mantissa bits of 0x6400 builds it without a conversion instruction.
+#define FP16_MAGIC 0x64006400u
+
+// 4-bit: q = bytes qs[4g..4g+3] of one block -> 8 exact fp16 values (code - 8)
+// in the order of pos_in_block(4, g, .).
+__device__ __forceinline__ half8 unpack4(uint32_t q) {
+    const uint32_t one = H2(0x3C00, 0x3C00);        // 1.0
+    const uint32_t s16 = H2(0x2C00, 0x2C00);        // 1/16
+    const uint32_t o_lo = H2(0xE408, 0xE408);       // -1032
+    const uint32_t o_hi = H2(0xD480, 0xD480);       // -72
+    uint32_t q8 = q >> 8;
+    uint32_t v0 = (q & 0x000F000Fu) | FP16_MAGIC;   // 1024 + c
+    uint32_t v1 = (q & 0x00F000F0u) | FP16_MAGIC;   // 1024 + 16 c
+    uint32_t v2 = (q8 & 0x000F000Fu) | FP16_MAGIC;
+    uint32_t v3 = (q8 & 0x00F000F0u) | FP16_MAGIC;
+    u32x4 r;
+    r.x = pk_fma_h2(v0, one, o_lo);
+    r.y = pk_fma_h2(v1, s16, o_hi);
+    r.z = pk_fma_h2(v2, one, o_lo);
+    r.w = pk_fma_h2(v3, s16, o_hi);
+    return __builtin_bit_cast(half8, r);
+}
+
+// 3-bit: two fp16 operands whose MFMA products add up to (code - 4):
+//   lo = (2-bit low part - 4), hb = 4 * third bit, both exact, in the order of
+//   pos_in_block(3, g, .).  p0/p1: ql[2g] / ql[2g+1] replicated into bytes 0
+//   and 2 (other bytes zero); th = qh >> 2g.
+__device__ __forceinline__ void unpack3(uint32_t p0, uint32_t p1, uint32_t th, half8 &lo, half8 &hb) {
+    // low parts: field f of byte j in the lower half, field f+2 in the upper half
+    const uint32_t sA = H2(0x3C00, 0x2C00), oA = H2(0xE404, 0xD440);  // (1, 1/16), (-1028, -68)
+    const uint32_t sB = H2(0x3400, 0x2400), oB = H2(0xDC10, 0xCD00);  // (1/4, 1/64), (-260, -20)
+    u32x4 a;
+    a.x = pk_fma_h2((p0 & 0x00300003u) | FP16_MAGIC, sA, oA);
+    a.y = pk_fma_h2((p0 & 0x00C0000Cu) | FP16_MAGIC, sB, oB);
+    a.z = pk_fma_h2((p1 & 0x00300003u) | FP16_MAGIC, sA, oA);
+    a.w = pk_fma_h2((p1 & 0x00C0000Cu) | FP16_MAGIC, sB, oB);
+    lo = __builtin_bit_cast(half8, a);
+    // third bits: positions 0, 8, 1, 9 (and +16) of th
+    const uint32_t s0 = H2(0x4400, 0x4400), o0 = H2(0xEC00, 0xEC00);  // 4, -4096
+    const uint32_t s8 = H2(0x2400, 0x2400), o8 = H2(0xCC00, 0xCC00);  // 1/64, -16
+    const uint32_t s1 = H2(0x4000, 0x4000), o1 = H2(0xE800, 0xE800);  // 2, -2048
+    const uint32_t s9 = H2(0x2000, 0x2000), o9 = H2(0xC800, 0xC800);  // 1/128, -8
+    u32x4 b;
+    b.x = pk_fma_h2((th & 0x00010001u) | FP16_MAGIC, s0, o0);
+    b.y = pk_fma_h2((th & 0x01000100u) | FP16_MAGIC, s8, o8);
+    b.z = pk_fma_h2((th & 0x00020002u) | FP16_MAGIC, s1, o1);
+    b.w = pk_fma_h2((th & 0x02000200u) | FP16_MAGIC, s9, o9);
+    hb = __builtin_bit_cast(half8, b);
+}
+
+__device__ __forceinline__ float4v mfma16(half8 a, half8 b, float4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float4v mfma16bf(bf16x8 a, bf16x8 b, float4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(h16 & 0xFFFFu));
+}
+
+// Round-to-nearest-even fp32 -> fp16 bits.
+__device__ __forceinline__ uint16_t f2h_bits(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+// Orderable key of an fp32 value (larger float -> larger key), -0 == +0.
+__device__ __forceinline__ uint32_t float_key(float v) {
+    uint32_t u = __builtin_bit_cast(uint32_t, v == 0.0f ? 0.0f : v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Wave-wide max of a 64-bit key.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
+        uint32_t olo = __shfl_xor(lo, off, 64), ohi = __shfl_xor(hi, off, 64);
+        uint64_t o = ((uint64_t)ohi << 32) | olo;
+        k = o > k ? o : k;
+    }
+    return k;
+}
+
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Device-scope release/acquire helpers for the cross-workgroup counters.
+__device__ __forceinline__ uint32_t atomic_add_release(uint32_t *p, uint32_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t atomic_load_acquire(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_store_relaxed(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fence_acq_rel_agent() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+}
+
+// Router for one logits row by one wave: the k largest logits (an equal logit
+// goes to the lower expert id; the comparison is on the fp32 values, -0 == +0)
+// and the softmax over those k, lane j < k writing entry j.  EPL = logits per
+// lane (E <= 64 * EPL).  k rounds of a wave-wide max over 64-bit keys
+// (orderable value << 32 | inverted id).
+template <int EPL>
+__device__ void wave_topk_row(const float *row, int E, int k, int *out_idx, float *out_w, int lane) {
+    float v[EPL];
+    uint64_t avail = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        int e = lane + 64 * i;
+        v[i] = 0.0f;
+        if (e < E) {
+            v[i] = row[e];
+            avail |= 1ull << i;
+        }
+    }
+    float mine = 0.0f;
+    int mine_id = 0;
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            if ((avail >> i) & 1ull) {
+                uint64_t key = ((uint64_t)float_key(v[i]) << 32) |
+                               (uint32_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * i));
+                best = key > best ? key : best;
+            }
+        }
+        uint64_t win = wave_max_u64(best);
+        int e = (int)(0xFFFFFFFFu - (uint32_t)win);
+        uint32_t kh = (uint32_t)(win >> 32);
+        uint32_t u = (kh & 0x80000000u) ? (kh & 0x7FFFFFFFu) : ~kh;
+        if ((e & 63) == lane) avail &= ~(1ull << (e >> 6));
+        if (lane == j) {
+            mine = __builtin_bit_cast(float, u);
+            mine_id = e;
+        }
+    }
+    float l0 = __shfl(mine, 0, 64);
+    float ex = lane < k ? expf(mine - l0) : 0.0f;
+    float s = wave_sum_f(ex);
+    if (lane < k) {
+        out_idx[lane] = mine_id;
+        out_w[lane] = ex / s;
+    }
+}
+
+}  // namespace moe

@@ -1,0 +1,163 @@
+// moe_route.hip -- router (top-k + softmax) and the stable counting-sort
+// grouping of (token, expert) pairs, for any number of rows.
+//
+// Router: the k largest fp32 logits per token (an equal logit goes to the
+// lower expert id) and a softmax over those k (forum thread "把 Strata 搬上
+// SGLang 引擎 的嘗試", TL;DR and §三: top-10 of 512 experts; the
+// extended-strata-moe "Reference", "Routing trace format": k ids and k
+// weights per token).  One wave per row.
+//
+// Grouping: pairs p = t*k + j bucketed per expert so each expert computes only
+// its own rows (thread §二, the expert-scoped layout), ordered by
+// (expert, token, slot).  Three passes over chunks of 64 tokens: per-chunk
+// histograms (LDS atomics: counts do not depend on order), one workgroup
+// scanning (expert, chunk) counts into start positions, then each chunk
+// placing its pairs in token order.  No global atomics, so the placement is
+// the same on every run.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+template <int EPL>
+__global__ __launch_bounds__(256) void k_route(RouteParams P) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= P.T) return;
+    __shared__ int s_idx[4][MOE_TOPK_MAX_LDS];
+    __shared__ float s_w[4][MOE_TOPK_MAX_LDS];
+    const int wv = threadIdx.x >> 6;
+    wave_topk_row<EPL>(P.logits + (size_t)t * P.E, P.E, P.k, s_idx[wv], s_w[wv], lane);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < P.k) {
+        P.idx[(size_t)t * P.k + lane] = s_idx[wv][lane];
+        P.w[(size_t)t * P.k + lane] = s_w[wv][lane];
+    }
+}
+
+// Per-chunk expert histogram.
+__global__ __launch_bounds__(256) void k_group_count(GroupParams P) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    uint32_t *hist = (uint32_t *)smem;
+    const int c = blockIdx.x;
+    for (int e = threadIdx.x; e < P.E; e += 256) hist[e] = 0;
+    __syncthreads();
+    const size_t p0 = (size_t)c * GRP_CHUNK_TOKENS * P.k;
+    const size_t p1 = min((size_t)(c + 1) * GRP_CHUNK_TOKENS * P.k, (size_t)P.T * P.k);
+    for (size_t p = p0 + threadIdx.x; p < p1; p += 256) {
+        const int e = P.idx[p];
+        if ((unsigned)e < (unsigned)P.E) atomicAdd(&hist[e], 1u);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < P.E; e += 256) P.chunk_counts[(size_t)c * P.E + e] = hist[e];
+}
+
+// One workgroup: chunk_counts[c][e] -> first position of chunk c's pairs of
+// expert e; offsets; active list.
+__global__ __launch_bounds__(1024) void k_group_scan(GroupParams P) {
+    __shared__ int s_part[1024];
+    __shared__ int s_act[1024];
+    const int tid = threadIdx.x;
+    const int E = P.E, per = (E + 1023) / 1024;
+    // per expert: exclusive running sum over chunks; total
+    int tot[MOE_SCAN_PER_MAX];
+    int my = 0, myact = 0;
+    for (int i = 0; i < per; ++i) {
+        int e = tid * per + i;
+        int run = 0;
+        if (e < E) {
+            for (int c = 0; c < P.nchunks; ++c) {
+                uint32_t *cc = P.chunk_counts + (size_t)c * E + e;
+                int v = (int)*cc;
+                *cc = (uint32_t)run;
+                run += v;
+            }
+        }
+        tot[i] = run;
+        my += run;
+        myact += (run > 0);
+    }
+    s_part[tid] = my;
+    s_act[tid] = myact;
+    __syncthreads();
+    // Hillis-Steele inclusive scans over the 1024 partial sums
+    for (int off = 1; off < 1024; off <<= 1) {
+        int a = tid >= off ? s_part[tid - off] : 0;
+        int b = tid >= off ? s_act[tid - off] : 0;
+        __syncthreads();
+        s_part[tid] += a;
+        s_act[tid] += b;
+        __syncthreads();
+    }
+    int base = s_part[tid] - my, abase = s_act[tid] - myact;
+    for (int i = 0; i < per; ++i) {
+        int e = tid * per + i;
+        if (e < E) {
+            P.offsets[e] = base;
+            for (int c = 0; c < P.nchunks; ++c) P.chunk_counts[(size_t)c * E + e] += (uint32_t)base;
+            if (tot[i] > 0) P.active[1 + abase++] = e;
+            base += tot[i];
+        }
+    }
+    if (tid == 1023) {
+        P.offsets[E] = s_part[1023];
+        P.active[0] = s_act[1023];
+    }
+}
+
+// Each chunk places its pairs in (token, slot) order.
+__global__ __launch_bounds__(64) void k_group_place(GroupParams P) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    uint32_t *cnt = (uint32_t *)smem;
+    const int c = blockIdx.x, lane = threadIdx.x;
+    for (int e = lane; e < P.E; e += 64) cnt[e] = P.chunk_counts[(size_t)c * P.E + e];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    const int t0 = c * GRP_CHUNK_TOKENS, t1 = min(t0 + GRP_CHUNK_TOKENS, P.T);
+    const int k = P.k;
+    for (int t = t0; t < t1; ++t) {
+        int e = lane < k ? P.idx[(size_t)t * k + lane] : -1;
+        if ((unsigned)e >= (unsigned)P.E) e = -1;  // ids outside [0, E) are not placed
+        // slots of this token earlier in the row that name the same expert
+        int dup = 0, later = 0;
+        for (int j = 0; j < k; ++j) {
+            int ej = __shfl(e, j, 64);
+            dup += (j < lane) && (ej == e);
+            later += (j > lane) && (ej == e);
+        }
+        uint32_t base = 0;
+        if (e >= 0) base = cnt[e];
+        __syncthreads();
+        if (e >= 0) {
+            P.pairs[base + dup] = t * k + lane;
+            if (later == 0) cnt[e] = base + dup + 1;
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t route_launch(const RouteParams &P, hipStream_t st) {
+    const int grid = (P.T + 3) / 4;
+    if (grid == 0) return hipSuccess;
+    const int epl = (P.E + 63) / 64;
+    if (epl <= 2) hipLaunchKernelGGL(k_route<2>, dim3(grid), dim3(256), 0, st, P);
+    else if (epl <= 4) hipLaunchKernelGGL(k_route<4>, dim3(grid), dim3(256), 0, st, P);
+    else if (epl <= 8) hipLaunchKernelGGL(k_route<8>, dim3(grid), dim3(256), 0, st, P);
+    else if (epl <= 16) hipLaunchKernelGGL(k_route<16>, dim3(grid), dim3(256), 0, st, P);
+    else if (epl <= 32) hipLaunchKernelGGL(k_route<32>, dim3(grid), dim3(256), 0, st, P);
+    else hipLaunchKernelGGL(k_route<64>, dim3(grid), dim3(256), 0, st, P);
+    return hipGetLastError();
+}
+
+hipError_t group_launch(const GroupParams &P, hipStream_t st) {
+    const size_t lds = (size_t)P.E * 4;
+    if (P.nchunks > 0) hipLaunchKernelGGL(k_group_count, dim3(P.nchunks), dim3(256), lds, st, P);
+    hipLaunchKernelGGL(k_group_scan, dim3(1), dim3(1024), 0, st, P);
+    if (P.nchunks > 0) hipLaunchKernelGGL(k_group_place, dim3(P.nchunks), dim3(64), lds, st, P);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,121 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+function include/moe.h declares, and rejects bad arguments before touching a
+device.  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from quantized_routed_expert_amd import moe
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.fail("libmoe_gfx950.so is not built (run quantized_routed_expert_amd.build)")
+    return moe.lib()
+
+
+def test_exports_match_header(L):
+    names = header_functions()
+    from quantized_routed_expert_amd import moe
+    assert sorted(moe.EXPORTS) == names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status(L):
+    from quantized_routed_expert_amd import moe
+    assert L.moe_version() == 100
+    for s in (0, -1, -2, -3, -4, -5, -99):
+        assert len(moe.status_string(s)) > 0
+    assert moe.status_string(-3).startswith("workspace")
+
+
+def test_expert_bytes(L):
+    from quantized_routed_expert_amd import moe
+    # bytes per expert = 3*H*F/32*B, B = 18 (4-bit) or 14 (3-bit)
+    assert moe.expert_bytes(4, 256, 512) == 221184
+    assert moe.expert_bytes(4, 2048, 768) == 2654208
+    assert moe.expert_bytes(3, 2048, 768) == 2064384
+    assert moe.expert_bytes(3, 2048, 512) == 1376256
+    assert moe.expert_bytes(5, 2048, 512) == -1
+    assert moe.expert_bytes(4, 2047, 512) == -1
+
+
+def test_workspace_bytes(L):
+    from quantized_routed_expert_amd import moe
+    for path in (0, 1, 2):
+        n = moe.workspace_bytes(16, 128, 8, 2048, 768, 768, path)
+        assert n > 16 * 8 * 2048 * 4
+    assert L.moe_workspace_bytes(4, 8, 9, 256, 512, 512, 0) == moe.MOE_ERR_UNSUPPORTED  # k > E
+    assert L.moe_workspace_bytes(-1, 8, 2, 256, 512, 512, 0) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_workspace_bytes(4, 8, 2, 250, 512, 512, 0) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_workspace_bytes(4, 8, 2, 256, 512, 100, 0) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_workspace_bytes(4, 8, 2, 256, 512, 0, 7) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_workspace_bytes(4, 5000, 2, 256, 512, 0, 0) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_rejects_before_launch(L):
+    """Every error path returns its code on the host (no device is touched)."""
+    from quantized_routed_expert_amd import moe
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    assert L.moe_route(None, 4, 8, 2, fake, fake, 0) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_route(fake, 4, 8, 9, fake, fake, 0) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_route(fake, 4, 8, 0, fake, fake, 0) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_route(fake, -4, 8, 2, fake, fake, 0) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_route(fake, 4, 8, 33, fake, fake, 0) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_group(fake, 4, 8, 2, fake, None, fake, fake, 1 << 20, 0) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_group(fake, 4, 8, 2, fake, fake, fake, fake, 0, 0) == moe.MOE_ERR_WORKSPACE
+
+    w = moe.QWeights(fake, 4, 8, 256, 512)
+    bad_bits = moe.QWeights(fake, 5, 8, 256, 512)
+    bad_h = moe.QWeights(fake, 4, 8, 200, 512)
+    bad_sh = moe.QWeights(fake, 4, 2, 256, 512)   # shared must hold one expert
+    nodata = moe.QWeights(None, 4, 8, 256, 512)
+    sh = moe.QWeights(fake, 4, 1, 256, 512)
+    big = 1 << 30
+
+    def lf(x=fake, dt=0, lg=fake, T=4, k=2, r=w, s=sh, y=fake, path=0, ws=fake, wsb=big):
+        return L.moe_layer_forward(x, dt, lg, T, k, ctypes.byref(r), ctypes.byref(s) if s else None, y, None,
+                                   None, path, ws, wsb, 0)
+
+    assert lf(x=None) == moe.MOE_ERR_INVALID_ARG
+    assert lf(lg=None) == moe.MOE_ERR_INVALID_ARG
+    assert lf(y=None) == moe.MOE_ERR_INVALID_ARG
+    assert lf(ws=None) == moe.MOE_ERR_INVALID_ARG
+    assert lf(dt=3) == moe.MOE_ERR_INVALID_ARG
+    assert lf(path=5) == moe.MOE_ERR_INVALID_ARG
+    assert lf(r=bad_bits) == moe.MOE_ERR_UNSUPPORTED
+    assert lf(r=bad_h) == moe.MOE_ERR_INVALID_ARG        # hidden differs from the shared expert's
+    assert lf(r=bad_h, s=None) == moe.MOE_ERR_UNSUPPORTED  # hidden not a multiple of 256
+    assert lf(r=nodata) == moe.MOE_ERR_INVALID_ARG
+    assert lf(s=bad_sh) == moe.MOE_ERR_INVALID_ARG
+    assert lf(k=9) == moe.MOE_ERR_UNSUPPORTED
+    assert lf(T=-1) == moe.MOE_ERR_INVALID_ARG
+    assert lf(wsb=16) == moe.MOE_ERR_WORKSPACE
+    assert lf(T=17, path=moe.PATH_DECODE) == moe.MOE_ERR_UNSUPPORTED
+    # mixed bit widths cannot take the fused decode launch when forced
+    assert lf(s=moe.QWeights(fake, 3, 1, 256, 512), path=moe.PATH_DECODE) == moe.MOE_ERR_UNSUPPORTED
+    # T == 0 is a valid empty call: nothing is launched
+    assert lf(T=0) == moe.MOE_OK
+
+    def ef(x=fake, T=4, ww=w, off=fake, path=0, wsb=big, out=fake):
+        return L.moe_expert_ffn(x, 1, T, ctypes.byref(ww), off, fake, fake, None, 2, out, path, fake, wsb, 0)
+
+    assert ef(x=None) == moe.MOE_ERR_INVALID_ARG
+    assert ef(off=None) == moe.MOE_ERR_INVALID_ARG
+    assert ef(out=None) == moe.MOE_ERR_INVALID_ARG
+    assert ef(ww=bad_bits) == moe.MOE_ERR_UNSUPPORTED
+    assert ef(T=17, path=moe.PATH_DECODE) == moe.MOE_ERR_UNSUPPORTED
+    assert ef(wsb=0) == moe.MOE_ERR_WORKSPACE
+    assert ef(T=0) == moe.MOE_OK

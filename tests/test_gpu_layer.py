@@ -1,0 +1,209 @@
+"""The whole layer (moe_layer_forward) and the expert FFN (moe_expert_ffn)
+through the C ABI against the oracle (GPU).
+
+Bar: routing bit-exact; outputs within max |err| <= 2e-3 * rms(oracle)."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import DEV, TOL, DevLayer, layer_inputs, oracle_forward, rel_err, x_to_dev
+from quantized_routed_expert_amd import moe, synth
+
+pytestmark = pytest.mark.gpu
+
+D, P = moe.PATH_DECODE, moe.PATH_PREFILL
+
+
+def _check(orc, li, path, rows=None, tol=TOL):
+    dl = DevLayer(li)
+    y, idx, w = dl.forward(path)
+    yr, ir, wr = oracle_forward(orc, li, rows=rows)
+    assert np.array_equal(idx, ir), "routing differs"
+    assert np.max(np.abs(w - wr)) <= 2e-6
+    yy = y if rows is None else y[rows]
+    assert np.all(np.isfinite(y))
+    e = rel_err(yy, yr)
+    print(f"    rel err {e:.3e}", flush=True)
+    assert e <= tol, e
+    return y
+
+
+# ---- the five workloads at their own sizes (one layer) -------------------------
+
+@pytest.mark.parametrize("name,T,path", [
+    ("tiny", 4, D), ("tiny", 4, P),
+    ("decode", 1, D), ("decode", 1, P),
+    ("mtp16", 16, D),
+    ("e512", 1, D), ("e512", 4, D), ("e512", 4, P),
+])
+def test_workload_full(orc, name, T, path):
+    print(f"[layer] {name} T={T} path={path}", flush=True)
+    _check(orc, layer_inputs(name, T), path)
+
+
+def test_prefill_chunk_sampled(orc):
+    """The 2048-token chunk in the launch configuration the benchmark times;
+    rows sampled (first, last, spread) because the oracle is slow."""
+    print("[layer] prefill T=2048 sampled rows", flush=True)
+    li = layer_inputs("prefill", 2048)
+    rows = np.array([0, 1, 17, 63, 64, 511, 1024, 1500, 2000, 2046, 2047], dtype=np.int32)
+    _check(orc, li, P, rows=rows)
+
+
+def test_mtp16_other_layers(orc):
+    for layer in (1, 47):
+        print(f"[layer] mtp16 layer={layer}", flush=True)
+        _check(orc, synth.layer_inputs(synth.CONFIGS["mtp16"], layer=layer, T=16), D)
+
+
+# ---- reduced shapes that the oracle runs whole, with ragged tiles ---------------
+
+def _cfg(name, **kw):
+    return synth.scaled_config(synth.CONFIGS[name], **kw)
+
+
+@pytest.mark.parametrize("T", [17, 65, 200])
+def test_prefill_scaled_full(orc, T):
+    """Full comparison on the prefill path with ragged 64-row tiles."""
+    print(f"[layer] prefill scaled T={T}", flush=True)
+    cfg = _cfg("prefill", name="pf_scaled", hidden=512, n_experts=24, ffn=256, shared_ffn=512)
+    _check(orc, synth.layer_inputs(cfg, T=T, threads=4), P)
+
+
+def test_prefill_fp32_x(orc):
+    print("[layer] prefill fp32 activations", flush=True)
+    cfg = _cfg("tiny", name="tiny_pf", n_experts=16, top_k=4)
+    _check(orc, synth.layer_inputs(cfg, T=40, threads=2), P)
+
+
+def test_decode_no_shared_mixed_f(orc):
+    print("[layer] decode without shared / shared with other F", flush=True)
+    cfg = _cfg("mtp16", name="noshared", shared_ffn=0, n_experts=32, hidden=1024, ffn=512)
+    _check(orc, synth.layer_inputs(cfg, T=5, threads=4), D)
+    cfg = _cfg("decode", name="fs", shared_ffn=1024, n_experts=16, hidden=512, ffn=256)
+    _check(orc, synth.layer_inputs(cfg, T=3, threads=4), D)
+    _check(orc, synth.layer_inputs(cfg, T=3, threads=4), P)
+
+
+def test_edge_cases(orc):
+    # top-k = E (every expert on every row), one expert, all-equal logits (ties)
+    print("[layer] k = E", flush=True)
+    cfg = _cfg("tiny", name="kE", n_experts=6, top_k=6)
+    _check(orc, synth.layer_inputs(cfg, T=16, threads=2), D)
+    print("[layer] E = k = 1", flush=True)
+    cfg = _cfg("tiny", name="e1", n_experts=1, top_k=1)
+    _check(orc, synth.layer_inputs(cfg, T=9, threads=2), D)
+    print("[layer] equal logits", flush=True)
+    li = synth.layer_inputs(_cfg("e512", name="tie", n_experts=64), T=16, threads=4)
+    li = dataclasses.replace(li, logits=np.zeros_like(li.logits))
+    _check(orc, li, D)
+    print("[layer] zero activations", flush=True)
+    li = dataclasses.replace(li, x=np.zeros_like(li.x))
+    y = DevLayer(li).forward(D)[0]
+    assert np.all(y == 0.0)
+    print("[layer] large-magnitude activations", flush=True)
+    li = synth.layer_inputs(_cfg("decode", name="big", n_experts=16, hidden=512, ffn=256, shared_ffn=256),
+                            T=4, threads=2)
+    xb = (synth.bf16_bits_to_f32(li.x) * 3000.0).astype(np.float32)
+    li = dataclasses.replace(li, x=synth.f32_to_bf16_bits(xb))
+    _check(orc, li, D)
+    _check(orc, li, P)
+
+
+def test_decode_matches_prefill(orc):
+    """The two kernel families agree with each other on the same inputs."""
+    print("[layer] decode vs prefill kernels", flush=True)
+    li = layer_inputs("mtp16", 16)
+    dl = DevLayer(li)
+    yd = dl.forward(D)[0]
+    yp = dl.forward(P)[0]
+    assert rel_err(yd, yp) <= TOL
+
+
+# ---- determinism and batch invariance -------------------------------------------
+
+def test_run_twice_bitwise():
+    print("[layer] run twice", flush=True)
+    for name, T, path in [("mtp16", 16, D), ("e512", 4, D), ("prefill", 512, P)]:
+        li = layer_inputs(name, T) if T == synth.CONFIGS[name].rows[0] else synth.layer_inputs(
+            synth.CONFIGS[name], T=T)
+        dl = DevLayer(li)
+        cfg = li.cfg
+        ws = moe.workspace(T, cfg.n_experts, cfg.top_k, cfg.hidden, cfg.ffn, cfg.shared_ffn, path)
+        a = dl.forward(path, ws=ws)[0]
+        b = dl.forward(path, ws=ws)[0]
+        assert np.array_equal(a, b), (name, T)
+
+
+def test_batch_invariance_decode():
+    """A row's output is bitwise the same alone as inside a 16-row window."""
+    print("[layer] batch invariance", flush=True)
+    li = layer_inputs("mtp16", 16)
+    y16 = DevLayer(li).forward(D)[0]
+    for t in (0, 5, 15):
+        one = dataclasses.replace(li, T=1, x=li.x[t:t + 1].copy(), logits=li.logits[t:t + 1].copy())
+        y1 = DevLayer(one).forward(D)[0]
+        assert np.array_equal(y1[0], y16[t]), t
+
+
+def test_workspace_reuse_across_shapes(orc):
+    """One workspace serves calls of different sizes in a row (its counters
+    return to zero after every call)."""
+    print("[layer] workspace reuse", flush=True)
+    cfg = synth.CONFIGS["e512"]
+    ws = moe.workspace(16, cfg.n_experts, cfg.top_k, cfg.hidden, cfg.ffn, cfg.shared_ffn, D)
+    for T in (4, 1, 16, 3, 4):
+        li = synth.layer_inputs(cfg, T=T, layer=T)
+        y, idx, _ = DevLayer(li).forward(D, ws=ws)
+        yr, ir, _ = oracle_forward(orc, li)
+        assert np.array_equal(idx, ir)
+        assert rel_err(y, yr) <= TOL, T
+
+
+# ---- the expert FFN entry point on a given grouping -------------------------------
+
+@pytest.mark.parametrize("name,T,path", [("tiny", 4, D), ("mtp16", 16, D), ("e512", 4, P), ("tiny", 40, P)])
+def test_expert_ffn(orc, name, T, path):
+    print(f"[expert_ffn] {name} T={T} path={path}", flush=True)
+    cfg = synth.CONFIGS[name]
+    li = synth.layer_inputs(cfg, T=T)
+    ri, rw = orc.route(li.logits, cfg.top_k)
+    ro, rp, ra = orc.group(ri, cfg.n_experts)
+    ref = orc.expert_ffn(li.x, li.x_code, cfg.top_k, cfg.bits, cfg.n_experts, cfg.hidden, cfg.ffn,
+                         li.routed, ro, rp, ra, rw)
+    x = x_to_dev(li.x, cfg.x_dtype)
+    routed_t = torch.from_numpy(li.routed).to(DEV)
+    qw = moe.qweights(routed_t, cfg.bits, cfg.n_experts, cfg.hidden, cfg.ffn)
+    off = torch.from_numpy(ro).to(DEV)
+    pairs = torch.from_numpy(np.ascontiguousarray(rp)).to(DEV)
+    act = torch.from_numpy(ra).to(DEV)
+    pw = torch.from_numpy(rw.astype(np.float32)).to(DEV)
+    out = torch.full((T * cfg.top_k, cfg.hidden), float("nan"), device=DEV)
+    ws = moe.workspace(T, cfg.n_experts, cfg.top_k, cfg.hidden, cfg.ffn, 0, path)
+    moe.expert_ffn(x, qw, off, pairs, act, cfg.top_k, out, ws, pair_w=pw, path=path)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert rel_err(got, ref) <= TOL
+
+
+# ---- negative control -----------------------------------------------------------
+
+def test_negative_control_corrupted_expert(orc):
+    """Flip one byte of a selected expert on the device: the parity check must
+    go red, so a green check carries evidence."""
+    print("[layer] negative control", flush=True)
+    li = layer_inputs("decode", 1)
+    cfg = li.cfg
+    dl = DevLayer(li)
+    y0 = dl.forward(D)[0]
+    yr, ir, _ = oracle_forward(orc, li)
+    assert rel_err(y0, yr) <= TOL
+    e = int(ir[0, 0])
+    eb = cfg.expert_bytes
+    # a down-projection block of the top expert: scale byte (high) of block 0, row 0
+    off = e * eb + 2 * cfg.ffn * (cfg.hidden // 32) * cfg.block_bytes + 1
+    dl.routed_t[off] ^= 0x40
+    y1 = dl.forward(D)[0]
+    assert rel_err(y1, yr) > TOL
