@@ -74,6 +74,12 @@ struct Layout {
     int max_slots = 0, nchunks = 0;
 };
 
+// The counters sit at offset 0 with a size that depends on no shape, in every
+// layout, so a workspace that is zero before its first use stays valid for
+// calls of any shape and path (each call returns the counters to zero).
+constexpr size_t COUNTER_SLOTS = MOE_MAX_EXPERTS + 1;
+constexpr size_t COUNTER_WORDS = 2 * COUNTER_SLOTS + 65536 / DEC_DN_ROWS + 4;
+
 Layout make_layout(int T, int E, int k, int H, int F, int Fs, int path) {
     Layout L;
     size_t off = 0;
@@ -85,7 +91,9 @@ Layout make_layout(int T, int E, int k, int H, int F, int Fs, int path) {
     const size_t TK = (size_t)T * k;
     const int Fmax = F > Fs ? F : Fs;
     L.nchunks = (T + GRP_CHUNK_TOKENS - 1) / GRP_CHUNK_TOKENS;
-    L.max_slots = (int)((TK < (size_t)E ? TK : (size_t)E) + 1);
+    L.max_slots = (int)COUNTER_SLOTS;
+    L.n_counters = COUNTER_WORDS;
+    L.counters = take(COUNTER_WORDS * 4);
     // routing and grouping (all paths; moe_group uses chunk_counts)
     L.idx = take(TK * 4);
     L.w = take(TK * 4);
@@ -96,8 +104,6 @@ Layout make_layout(int T, int E, int k, int H, int F, int Fs, int path) {
     L.out_pairs = take(TK * H * 4);
     L.out_shared = take((size_t)T * H * 4);
     if (path == MOE_PATH_DECODE) {
-        L.n_counters = (size_t)2 * L.max_slots + H / DEC_DN_ROWS + 4;
-        L.counters = take(L.n_counters * 4);
         L.harr = take((TK + T) * (size_t)Fmax * 4);
     } else {
         L.slot_exp = take((size_t)(E + 1) * 4);
@@ -163,6 +169,7 @@ int decode_lds_layout(DecodeParams &P, int xparts) {
     P.lds_slot_exp = take(P.max_slots * 4);
     P.lds_slot_cnt = take(P.max_slots * 4);
     P.lds_tinv = take(P.T * 4);
+    P.lds_hinv = take(P.T * 4);
     P.lds_misc = take(64);
     const int xa_bytes = xparts * P.T * P.H * 2;
     const int ha_bytes = P.T * Fmax * 4;
@@ -218,10 +225,10 @@ int64_t moe_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t hidden, int
 
 int moe_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *topk_idx, float *topk_w,
               int64_t stream) {
-    if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
     int rc = check_shape(T, E, k, 256, 256);
     if (rc) return rc;
-    if (T == 0) return MOE_OK;
+    if (T == 0) return MOE_OK;  // nothing to read or write
+    if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
     RouteParams P{logits, T, E, k, topk_idx, topk_w};
     return launch_err(route_launch(P, S(stream)));
 }
@@ -269,7 +276,7 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
     P.gu_count = cnt;
     P.dn_count = cnt + L.max_slots;
     P.slice_count = cnt + 2 * L.max_slots;
-    P.err = cnt + 2 * L.max_slots + routed->hidden / DEC_DN_ROWS;
+    P.err = cnt + 2 * L.max_slots + 65536 / DEC_DN_ROWS;
     P.T = T;
     P.E = E;
     P.k = k;
@@ -279,7 +286,7 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
     P.bits = routed->bits;
     P.x_f32 = x_f32;
     P.mode = mode | (shared ? DEC_MODE_SHARED : 0);
-    P.max_slots = L.max_slots;
+    P.max_slots = ((T * k < E) ? T * k : E) + 1;  // LDS slot tables (counters use the fixed stride)
     const int Fmax = P.F > P.Fs ? P.F : P.Fs;
     P.h_row_bytes = Fmax * 4;
     const int lds = decode_lds_layout(P, x_f32 ? 2 : 1);
@@ -350,7 +357,8 @@ extern "C" {
 int moe_expert_ffn(const void *x, int32_t x_dtype, int32_t T, const moe_qweights *w, const int32_t *offsets,
                    const int32_t *pairs, const int32_t *active, const float *pair_w, int32_t k, float *out_pairs,
                    int32_t path, void *ws, int64_t ws_bytes, int64_t stream) {
-    if (!x || !w || !offsets || !pairs || !active || !out_pairs || !ws) return MOE_ERR_INVALID_ARG;
+    if (!w) return MOE_ERR_INVALID_ARG;
+    if (T != 0 && (!x || !offsets || !pairs || !active || !out_pairs || !ws)) return MOE_ERR_INVALID_ARG;
     if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
     if (path < MOE_PATH_AUTO || path > MOE_PATH_PREFILL) return MOE_ERR_INVALID_ARG;
     int rc = check_weights(w, w->hidden, -1);
@@ -377,7 +385,8 @@ int moe_expert_ffn(const void *x, int32_t x_dtype, int32_t T, const moe_qweights
 int moe_layer_forward(const void *x, int32_t x_dtype, const float *logits, int32_t T, int32_t k,
                       const moe_qweights *routed, const moe_qweights *shared, float *y, int32_t *topk_idx_out,
                       float *topk_w_out, int32_t path, void *ws, int64_t ws_bytes, int64_t stream) {
-    if (!x || !logits || !routed || !y || !ws) return MOE_ERR_INVALID_ARG;
+    if (!routed) return MOE_ERR_INVALID_ARG;
+    if (T != 0 && (!x || !logits || !y || !ws)) return MOE_ERR_INVALID_ARG;
     if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
     if (path < MOE_PATH_AUTO || path > MOE_PATH_PREFILL) return MOE_ERR_INVALID_ARG;
     int rc = check_weights(routed, routed->hidden, -1);

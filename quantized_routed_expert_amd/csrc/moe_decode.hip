@@ -23,9 +23,10 @@
 //     once per window for all rows sharing the expert (the read-once-per-window
 //     rule of Strata "Several requests at once", opening section).  The fp16
 //     block scale is applied to each block's fp32 partial.  SwiGLU in fp32;
-//     h is published as fp16 hi+lo (about 22 bits) for the down projection.
+//     h is published in fp32.
 //  C. down: workgroup tiles (one expert, 128 output rows).  The tile waits on
-//     its expert's gate/up counter, stages that expert's h in LDS, streams the
+//     its expert's gate/up counter, stages that expert's h in LDS as fp16
+//     hi + lo (about 22 bits) with a per-token power-of-two scale, streams the
 //     down rows, and writes w * o per (token, slot) pair.  The workgroup that
 //     completes the last expert of a 128-row slice sums that slice in the
 //     fixed slot order into y (deterministic; no floating-point atomics).
@@ -158,6 +159,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
     int *s_slot_exp = (int *)(smem + P.lds_slot_exp);
     int *s_slot_cnt = (int *)(smem + P.lds_slot_cnt);
     float *s_tinv = (float *)(smem + P.lds_tinv);
+    float *s_hinv = (float *)(smem + P.lds_hinv);
     int *s_misc = (int *)(smem + P.lds_misc);
     uint8_t *s_xa = smem + P.lds_xa;
     uint8_t *s_chunk = smem + P.lds_chunk + wave * P.chunk_stride;
@@ -388,7 +390,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
         }
-        // SwiGLU in fp32 and publish h as fp16 hi/lo (h * 2^-8)
+        // SwiGLU in fp32; h published as fp32 in the down projection's k order
         const int f = fg * 16 + n_lane;
         int pb = f >> 5, pg, pe;
         group_slot_of(BITS, f & 31, pg, pe);
@@ -402,13 +404,8 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
                 float ti = s_tinv[tk];
                 float g1 = gv[r] * ti, u1 = uv[r] * ti;
                 float h = g1 / (1.0f + expf(-g1)) * u1;
-                float h8 = ldexpf(h, -DEC_H_SHIFT);
-                _Float16 hh = (_Float16)h8;
-                _Float16 hl = (_Float16)(h8 - (float)hh);
                 int row = shared_slot ? TK + m : s_slot_start[s] + m;
-                uint8_t *dst = P.h_arr + (size_t)row * P.h_row_bytes + (size_t)pb * 128 + pg * 32 + pe * 2;
-                *(_Float16 *)dst = hh;
-                *(_Float16 *)(dst + 16) = hl;
+                *(float *)(P.h_arr + (size_t)row * P.h_row_bytes + (size_t)pb * 128 + pg * 32 + pe * 4) = h;
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
@@ -451,12 +448,51 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             }
             __syncthreads();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            // stage this expert's h rows (contiguous) into LDS
+            // stage this expert's h rows into LDS as fp16 hi + lo of h * 2^sc_t,
+            // sc_t a per-token power of two putting max|h_t| in [2^13, 2^14)
             const int row0 = shared_slot ? TK : s_slot_start[s];
-            const int nbytes = n_tok * Fx * 4;  // per row: Fx/32 blocks * 4 groups * 32 B
-            for (int i = tid * 16; i < nbytes; i += DEC_THREADS * 16) {
-                int r = i / (Fx * 4), cidx = i - r * (Fx * 4);
-                *(u32x4 *)(s_xa + i) = *(const u32x4 *)(P.h_arr + (size_t)(row0 + r) * P.h_row_bytes + cidx);
+            const int ngrp = Fx >> 3;  // groups of 8 values (one k-group of one block)
+            for (int r = wave; r < n_tok; r += DEC_WAVES) {
+                const float *hr = (const float *)(P.h_arr + (size_t)(row0 + r) * P.h_row_bytes);
+                float mx = 0.0f;
+                for (int gi = lane; gi < ngrp; gi += 64) {
+                    u32x4 a = *(const u32x4 *)(hr + gi * 8), b = *(const u32x4 *)(hr + gi * 8 + 4);
+                    float v[8] = {__builtin_bit_cast(float, a.x), __builtin_bit_cast(float, a.y),
+                                  __builtin_bit_cast(float, a.z), __builtin_bit_cast(float, a.w),
+                                  __builtin_bit_cast(float, b.x), __builtin_bit_cast(float, b.y),
+                                  __builtin_bit_cast(float, b.z), __builtin_bit_cast(float, b.w)};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
+                }
+                mx = wave_max_f(mx);
+                int ex = 0;
+                if (mx > 0.0f) frexpf(mx, &ex);
+                const int sc = mx > 0.0f ? 14 - ex : 0;
+                if (lane == 0) s_hinv[r] = ldexpf(1.0f, -sc);
+                for (int gi = lane; gi < ngrp; gi += 64) {
+                    u32x4 a = *(const u32x4 *)(hr + gi * 8), b = *(const u32x4 *)(hr + gi * 8 + 4);
+                    uint32_t w8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+                    uint16_t hv[8], lv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        float v = ldexpf(__builtin_bit_cast(float, w8[e]), sc);
+                        _Float16 hh = (_Float16)v;
+                        hv[e] = __builtin_bit_cast(uint16_t, hh);
+                        lv[e] = f2h_bits(v - (float)hh);
+                    }
+                    u32x4 h4, l4;
+                    h4.x = hv[0] | ((uint32_t)hv[1] << 16);
+                    h4.y = hv[2] | ((uint32_t)hv[3] << 16);
+                    h4.z = hv[4] | ((uint32_t)hv[5] << 16);
+                    h4.w = hv[6] | ((uint32_t)hv[7] << 16);
+                    l4.x = lv[0] | ((uint32_t)lv[1] << 16);
+                    l4.y = lv[2] | ((uint32_t)lv[3] << 16);
+                    l4.z = lv[4] | ((uint32_t)lv[5] << 16);
+                    l4.w = lv[6] | ((uint32_t)lv[7] << 16);
+                    uint8_t *dst = s_xa + (size_t)r * (Fx * 4) + (size_t)gi * 32;
+                    *(u32x4 *)dst = h4;
+                    *(u32x4 *)(dst + 16) = l4;
+                }
             }
             __syncthreads();
             cur_slot = s;
@@ -501,7 +537,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             for (int r = 0; r < 4; ++r) {
                 int m = 4 * g_lane + r;
                 if (m < n_tok) {
-                    float o = ldexpf(ov[r], DEC_H_SHIFT);
+                    float o = ov[r] * s_hinv[m];
                     if (shared_slot) {
                         P.out_shared[(size_t)m * H + hrow] = o;
                     } else {

@@ -15,7 +15,6 @@ constexpr int DEC_DN_ROWS = DEC_WAVES * 16;  // down-projection rows per workgro
 constexpr int DEC_CB_MAX = 32;               // quant blocks per row in one streamed chunk
 constexpr int DEC_MAX_LD = 9;                // 16-byte loads per lane per chunk (16 rows x 32 x 18 B)
 constexpr int DEC_MAX_E_FUSED = 1024;        // router fused into the kernel up to this many experts
-constexpr int DEC_H_SHIFT = 8;               // h is carried as fp16 hi/lo of h * 2^-8
 constexpr uint32_t DEC_SPIN_LIMIT = 1u << 20;  // bounded waits: a wait that runs out sets err bit 0
 #define MOE_MAX_EXPERTS_DEV 4096
 #define MOE_DECODE_ROWS_DEV 16
@@ -39,7 +38,7 @@ struct DecodeParams {
     float *out_shared;         // [T][H]
     int32_t *topk_idx_out;     // may be null
     float *topk_w_out;         // may be null
-    uint8_t *h_arr;            // [(T*k + T)][Fmax*4 bytes]
+    uint8_t *h_arr;            // [(T*k + T)][Fmax] fp32, down projection's k order
     uint32_t *gu_count;        // [max_slots]
     uint32_t *dn_count;        // [max_slots]
     uint32_t *slice_count;     // [H / DEC_DN_ROWS]
@@ -49,7 +48,7 @@ struct DecodeParams {
     int h_row_bytes;           // Fmax * 4
     // dynamic LDS layout (byte offsets)
     int lds_idx, lds_w, lds_sorted, lds_hist, lds_slot_start, lds_slot_exp, lds_slot_cnt,
-        lds_tinv, lds_misc, lds_xa, lds_chunk, chunk_stride, lds_total;
+        lds_tinv, lds_hinv, lds_misc, lds_xa, lds_chunk, chunk_stride, lds_total;
 };
 
 // ---------------------------------------------------------------------------

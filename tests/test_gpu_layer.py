@@ -60,8 +60,8 @@ def test_mtp16_other_layers(orc):
 
 # ---- reduced shapes that the oracle runs whole, with ragged tiles ---------------
 
-def _cfg(name, **kw):
-    return synth.scaled_config(synth.CONFIGS[name], **kw)
+def _cfg(base, **kw):
+    return synth.scaled_config(synth.CONFIGS[base], **kw)
 
 
 @pytest.mark.parametrize("T", [17, 65, 200])
