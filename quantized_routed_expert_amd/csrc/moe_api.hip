@@ -104,7 +104,9 @@ Layout make_layout(int T, int E, int k, int H, int F, int Fs, int path) {
     L.out_pairs = take(TK * H * 4);
     L.out_shared = take((size_t)T * H * 4);
     if (path == MOE_PATH_DECODE) {
-        L.harr = take((TK + T) * (size_t)Fmax * 4);
+        const int nkb = H / 32;
+        const int nch = nkb / decode_chunk_blocks(nkb);
+        L.harr = take((TK + T) * (size_t)2 * nch * Fmax * 4);  // partial gate/up sums
     } else {
         L.slot_exp = take((size_t)(E + 1) * 4);
         L.slot_row0 = take((size_t)(E + 1) * 4);
@@ -170,6 +172,7 @@ int decode_lds_layout(DecodeParams &P, int xparts) {
     P.lds_slot_cnt = take(P.max_slots * 4);
     P.lds_tinv = take(P.T * 4);
     P.lds_hinv = take(P.T * 4);
+    P.lds_xmax = take(P.T * 4);
     P.lds_misc = take(64);
     const int xa_bytes = xparts * P.T * P.H * 2;
     const int ha_bytes = P.T * Fmax * 4;
@@ -189,6 +192,16 @@ int decode_lds_layout(DecodeParams &P, int xparts) {
 }
 
 int launch_err(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+// Shapes the fused decode launch takes: every thread stages at most
+// DEC_X_BLOCKS_PER_THREAD activation blocks (half for fp32) and an expert's
+// FFN width is at most DEC_MAX_F.
+bool decode_fits(int T, int H, int F, int Fs, int x_dtype) {
+    const int per = x_dtype == MOE_DTYPE_F32 ? DEC_X_BLOCKS_PER_THREAD / 2 : DEC_X_BLOCKS_PER_THREAD;
+    if ((long long)T * (H / 32) > (long long)per * DEC_THREADS) return false;
+    if (F > DEC_MAX_F || Fs > DEC_MAX_F) return false;
+    return true;
+}
 
 }  // namespace
 
@@ -219,8 +232,15 @@ int64_t moe_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t hidden, int
     if (rc) return rc;
     if (shared_ffn < 0 || shared_ffn % 256) return MOE_ERR_UNSUPPORTED;
     if (path < MOE_PATH_AUTO || path > MOE_PATH_PREFILL) return MOE_ERR_INVALID_ARG;
-    Layout L = make_layout(T, E, k, hidden, ffn, shared_ffn, resolve_path(path, T));
-    return (int64_t)L.total;
+    // a decode request may be served by the prefill kernels (mixed bit widths,
+    // shapes beyond the fused launch), so size for both
+    const int p = resolve_path(path, T);
+    size_t n = make_layout(T, E, k, hidden, ffn, shared_ffn, p).total;
+    if (p == MOE_PATH_DECODE) {
+        const size_t n2 = make_layout(T, E, k, hidden, ffn, shared_ffn, MOE_PATH_PREFILL).total;
+        n = n > n2 ? n : n2;
+    }
+    return (int64_t)n;
 }
 
 int moe_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *topk_idx, float *topk_w,
@@ -271,7 +291,7 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
     P.out_shared = at<float>(ws, L.out_shared);
     P.topk_idx_out = tidx;
     P.topk_w_out = tw;
-    P.h_arr = at<uint8_t>(ws, L.harr);
+    P.gu_part = at<float>(ws, L.harr);
     uint32_t *cnt = at<uint32_t>(ws, L.counters);
     P.gu_count = cnt;
     P.dn_count = cnt + L.max_slots;
@@ -288,7 +308,8 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
     P.mode = mode | (shared ? DEC_MODE_SHARED : 0);
     P.max_slots = ((T * k < E) ? T * k : E) + 1;  // LDS slot tables (counters use the fixed stride)
     const int Fmax = P.F > P.Fs ? P.F : P.Fs;
-    P.h_row_bytes = Fmax * 4;
+    P.nch = (P.H / 32) / decode_chunk_blocks(P.H / 32);
+    P.part_stride = 2 * P.nch * Fmax;
     const int lds = decode_lds_layout(P, x_f32 ? 2 : 1);
     if (lds > dv.lds_max) return MOE_ERR_UNSUPPORTED;
     static std::mutex mu;
@@ -365,8 +386,11 @@ int moe_expert_ffn(const void *x, int32_t x_dtype, int32_t T, const moe_qweights
     if (rc) return rc;
     rc = check_shape(T, w->n_experts, k, w->hidden, w->ffn);
     if (rc) return rc;
-    const int p = resolve_path(path, T);
-    if (p == MOE_PATH_DECODE && T > MOE_DECODE_MAX_ROWS) return MOE_ERR_UNSUPPORTED;
+    int p = resolve_path(path, T);
+    if (p == MOE_PATH_DECODE && (T > MOE_DECODE_MAX_ROWS || !decode_fits(T, w->hidden, w->ffn, 0, x_dtype))) {
+        if (path == MOE_PATH_DECODE) return MOE_ERR_UNSUPPORTED;
+        p = MOE_PATH_PREFILL;
+    }
     Layout L = make_layout(T, w->n_experts, k, w->hidden, w->ffn, 0, p);
     if (ws_bytes < (int64_t)L.total) return MOE_ERR_WORKSPACE;
     if (T == 0) return MOE_OK;
@@ -401,7 +425,7 @@ int moe_layer_forward(const void *x, int32_t x_dtype, const float *logits, int32
     const int Fs = shared ? shared->ffn : 0;
     int p = resolve_path(path, T);
     const bool same_bits = !shared || shared->bits == routed->bits;
-    if (p == MOE_PATH_DECODE && (T > MOE_DECODE_MAX_ROWS || !same_bits)) {
+    if (p == MOE_PATH_DECODE && (T > MOE_DECODE_MAX_ROWS || !same_bits || !decode_fits(T, H, routed->ffn, Fs, x_dtype))) {
         if (path == MOE_PATH_DECODE) return MOE_ERR_UNSUPPORTED;
         p = MOE_PATH_PREFILL;
     }

@@ -9,35 +9,116 @@
 // FFNs and the combine share one launch here.
 //
 // Structure (persistent grid, every workgroup resident):
-//  A. every workgroup computes the routing of the <= 16 rows itself (top-k of
-//     fp32 logits, ties to the lower id, softmax over the k selected) and the
-//     stable grouping by (expert, token, slot); the rows' activations are
-//     staged in LDS as fp16 in each format's k order, with a per-token
-//     power-of-two scale (exact) so any bf16/fp32 range fits fp16.
-//  B. gate/up: wave-level items (one expert, 16 output features, gate AND up,
-//     all of K).  Each wave streams its expert rows from HBM in 16-row chunks
-//     with 16-byte loads (two chunks in flight in registers), passes them
-//     through a wave-private LDS buffer to reach the MFMA lane layout,
-//     unpacks exact fp16 codes, and runs v_mfma_f32_16x16x32_f16 with the
-//     (<= 16) rows of the expert as the M dimension: every weight byte is read
-//     once per window for all rows sharing the expert (the read-once-per-window
-//     rule of Strata "Several requests at once", opening section).  The fp16
-//     block scale is applied to each block's fp32 partial.  SwiGLU in fp32;
-//     h is published in fp32.
-//  C. down: workgroup tiles (one expert, 128 output rows).  The tile waits on
-//     its expert's gate/up counter, stages that expert's h in LDS as fp16
-//     hi + lo (about 22 bits) with a per-token power-of-two scale, streams the
-//     down rows, and writes w * o per (token, slot) pair.  The workgroup that
-//     completes the last expert of a 128-row slice sums that slice in the
-//     fixed slot order into y (deterministic; no floating-point atomics).
+//  A. every workgroup loads the rows' activations (all threads, one quant
+//     block each) while the waves owning a row compute its routing (top-k of
+//     the fp32 logits, ties to the lower id, softmax over the k selected;
+//     wave reductions on DPP).  Grouping is a counting sort in LDS.  The
+//     activations are stored in LDS as fp16 in each format's k order with a
+//     per-token power-of-two scale (exact), so any bf16/fp32 range fits fp16.
+//  B. gate/up units: (expert, 16 output rows, gate or up, one K chunk of up
+//     to 32 quant blocks), a few KB each, spread over every wave of the grid.
+//     A wave streams its unit's quantized rows from HBM with 16-byte loads
+//     (the next unit's chunk in flight while the current one computes),
+//     passes them through a wave-private LDS buffer into the MFMA lane
+//     layout, unpacks exact fp16 codes and runs v_mfma_f32_16x16x32_f16 with
+//     the expert's (<= 16) rows as the M dimension: every weight byte is read
+//     once per window for all rows that share the expert (the read-once-per-
+//     window rule of Strata "Several requests at once", opening section).  The
+//     fp16 block scale multiplies each block's fp32 partial.  A unit publishes
+//     its fp32 partial sums and counts itself done for its expert.
+//  C. down tiles: (expert, 128 output rows) per workgroup.  The tile prefetches
+//     its weights, waits for its expert's units, sums the partials in a fixed
+//     order, applies SwiGLU in fp32 and stages h in LDS as fp16 hi + lo (about
+//     22 bits) with a per-token power-of-two scale, streams the down rows and
+//     writes w * o per (token, slot) pair.  The workgroup that completes the
+//     last expert of a 128-row slice sums that slice in the fixed slot order
+//     into y (deterministic; no floating-point atomics).
+//
+// Data crossing workgroups (partials, pair rows) uses device-coherent accesses
+// and per-wave store completion instead of agent-scope fences, which on this
+// chip would write back or invalidate a whole XCD's L2.
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 
+#ifdef MOE_PHASE_TRACE
+// Phase timestamps (100 MHz device clock) per workgroup, for analysis builds only.
+__device__ uint64_t *g_trace = nullptr;
+#define TRACE(slot)                                                                                        \
+    do {                                                                                                   \
+        if (g_trace && threadIdx.x == 0) g_trace[blockIdx.x * 16 + (slot)] = __builtin_amdgcn_s_memrealtime(); \
+    } while (0)
+#else
+#define TRACE(slot) \
+    do {            \
+    } while (0)
+#endif
+
 // ---------------------------------------------------------------------------
-// Phase A helpers
+// Wave reductions on DPP (gfx9 row broadcasts); result valid in every lane.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
+
+// Router for one row by one wave (E <= 64 * EPL): k rounds of a wave-wide
+// argmax, an equal logit going to the lower expert id; softmax over the k.
+template <int EPL>
+__device__ void route_row(const float *row, int E, int k, int *out_idx, float *out_w, int lane) {
+    uint32_t key[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        key[i] = e < E ? float_key(row[e]) : 0u;  // finite values have keys > 0
+    }
+    float mine = 0.0f;
+    int mine_id = 0;
+    for (int j = 0; j < k; ++j) {
+        uint32_t bk = 0;
+        int bi = 0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (key[i] > bk) {  // strict: the lowest i wins among equal keys
+                bk = key[i];
+                bi = i;
+            }
+        const uint32_t m = wave_max_u32(bk);
+        const uint64_t tied = __ballot(bk == m);
+        int e;
+        if (__popcll(tied) == 1) {
+            const int wl = __ffsll((unsigned long long)tied) - 1;
+            e = wl + 64 * __builtin_amdgcn_readlane(bi, wl);
+        } else {
+            e = (int)wave_min_u32(bk == m ? (uint32_t)(lane + 64 * bi) : 0xFFFFFFFFu);
+        }
+        if ((e & 63) == lane) {
+#pragma unroll
+            for (int i = 0; i < EPL; ++i)
+                if (i == (e >> 6)) key[i] = 0u;
+        }
+        const uint32_t u = (m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m;
+        if (lane == j) {
+            mine = __builtin_bit_cast(float, u);
+            mine_id = e;
+        }
+    }
+    const float l0 = __shfl(mine, 0, 64);
+    const float ex = lane < k ? expf(mine - l0) : 0.0f;
+    const float s = wave_sum_f(ex);
+    if (lane < k) {
+        out_idx[lane] = mine_id;
+        out_w[lane] = ex / s;
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Chunk streaming: 16 consecutive rows x CB blocks of one matrix.
@@ -46,33 +127,33 @@ struct Chunk {
     u32x4 r[DEC_MAX_LD];
 };
 
-__device__ __forceinline__ void chunk_load(Chunk &c, const uint8_t *rows, int row_bytes, int seg_off,
-                                           int seg, int lane) {
+__device__ __forceinline__ void chunk_load(Chunk &c, const uint8_t *rows, int row_bytes, int seg_off, int seg,
+                                           int lane) {
     const int per_row = seg >> 4;  // 16-byte pieces per row segment
 #pragma unroll
     for (int u = 0; u < DEC_MAX_LD; ++u) {
-        int j = lane + 64 * u;
+        const int j = lane + 64 * u;
         if (j < 16 * per_row) {
-            int r = j / per_row, col = j - r * per_row;
+            const int r = j / per_row, col = j - r * per_row;
             c.r[u] = *(const u32x4 *)(rows + (size_t)r * row_bytes + seg_off + col * 16);
         }
     }
 }
 
 __device__ __forceinline__ void chunk_store_lds(const Chunk &c, uint8_t *buf, int seg, int lane) {
-    const int n16 = seg;  // 16 rows * seg bytes / 16
 #pragma unroll
     for (int u = 0; u < DEC_MAX_LD; ++u) {
-        int j = lane + 64 * u;
-        if (j < n16) *(u32x4 *)(buf + j * 16) = c.r[u];
+        const int j = lane + 64 * u;
+        if (j < seg) *(u32x4 *)(buf + j * 16) = c.r[u];  // 16 rows * seg bytes = seg pieces
     }
 }
 
 __device__ __forceinline__ uint32_t lds_u32(const uint8_t *p) { return *(const uint32_t *)p; }
 __device__ __forceinline__ uint32_t lds_u16(const uint8_t *p) { return *(const uint16_t *)p; }
 
-// One block of the chunk in LDS, as this lane's MFMA B operand(s) and scale.
+// One block of the chunk in LDS as this lane's MFMA B operand(s) and scale.
 // Lane layout: weight row n = lane % 16 of the chunk, k-group g = lane / 16.
+// buf is 4-byte aligned; offsets stay integers so the accesses stay LDS reads.
 template <int BITS>
 struct BOp;
 
@@ -80,13 +161,11 @@ template <>
 struct BOp<4> {
     half8 b;
     float d;
-    // buf: 4-byte aligned LDS chunk; offsets are kept as integers so the
-    // accesses stay LDS reads.
     __device__ __forceinline__ void load(const uint8_t *buf, int seg, int blk, int n, int g) {
         const int o = n * seg + blk * 18;
         d = half_bits_to_float(lds_u16(buf + o));
         const int qa = o + 2 + 4 * g, al = qa & ~3;
-        uint32_t w0 = lds_u32(buf + al), w1 = lds_u32(buf + al + 4);
+        const uint32_t w0 = lds_u32(buf + al), w1 = lds_u32(buf + al + 4);
         b = unpack4(__builtin_amdgcn_alignbyte(w1, w0, (uint32_t)(qa & 3)));
     }
 };
@@ -98,7 +177,7 @@ struct BOp<3> {
     __device__ __forceinline__ void load(const uint8_t *buf, int seg, int blk, int n, int g) {
         const int o = n * seg + blk * 14;
         d = half_bits_to_float(lds_u16(buf + o));
-        // ql[2g], ql[2g+1] replicated into bytes 0 and 2
+        // low-part bytes ql[2g], ql[2g+1], each replicated into bytes 0 and 2
         const int qa = o + 2 + 2 * g;
         const uint32_t qw = lds_u32(buf + (qa & ~3));
         const uint32_t sh = (uint32_t)(qa & 3);
@@ -112,18 +191,18 @@ struct BOp<3> {
     }
 };
 
-// acc += d * (A . B) for one block; A given as XPARTS fp16 parts.
-template <int BITS, int XPARTS>
+// acc += d * (A . B) for one block; A given as NP fp16 parts.
+template <int BITS, int NP>
 __device__ __forceinline__ void block_mma(float4v &acc, const BOp<BITS> &op, const half8 *a) {
-    float4v z = {0.f, 0.f, 0.f, 0.f};
+    const float4v z = {0.f, 0.f, 0.f, 0.f};
     float4v dd;
     if constexpr (BITS == 4) {
         dd = mfma16(a[0], op.b, z);
-        if constexpr (XPARTS == 2) dd = mfma16(a[1], op.b, dd);
+        if constexpr (NP == 2) dd = mfma16(a[1], op.b, dd);
     } else {
         dd = mfma16(a[0], op.lo, z);
         dd = mfma16(a[0], op.hb, dd);
-        if constexpr (XPARTS == 2) {
+        if constexpr (NP == 2) {
             dd = mfma16(a[1], op.lo, dd);
             dd = mfma16(a[1], op.hb, dd);
         }
@@ -139,6 +218,28 @@ __host__ __device__ __forceinline__ int chunk_blocks(int nkb) {
     return (nkb % 32 == 0) ? 32 : (nkb % 24 == 0) ? 24 : (nkb % 16 == 0) ? 16 : 8;
 }
 
+// Multiply-accumulate a whole chunk in LDS (cb blocks, a multiple of 4) into
+// acc.  A operands: a_base points at this lane's first block, a_stride bytes
+// between blocks, part_off bytes between the NP parts.
+template <int BITS, int NP>
+__device__ __forceinline__ void chunk_mma(float4v &acc, const uint8_t *buf, int seg, int cb, int n, int g,
+                                          const uint8_t *a_base, int a_stride, int part_off, bool a_valid) {
+    for (int b0 = 0; b0 < cb; b0 += 4) {
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi) {
+            const int b = b0 + bi;
+            half8 a[NP];
+#pragma unroll
+            for (int xp = 0; xp < NP; ++xp)
+                a[xp] = a_valid ? *(const half8 *)(a_base + (size_t)b * a_stride + xp * part_off)
+                                : half8{0, 0, 0, 0, 0, 0, 0, 0};
+            BOp<BITS> op;
+            op.load(buf, seg, b, n, g);
+            block_mma<BITS, NP>(acc, op, a);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
@@ -150,6 +251,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
     const int TK = T * k;
     const bool has_shared = (P.mode & DEC_MODE_SHARED) != 0;
     const int hs = has_shared ? 1 : 0;
+    const int G = gridDim.x;
 
     int *s_idx = (int *)(smem + P.lds_idx);
     float *s_w = (float *)(smem + P.lds_w);
@@ -160,42 +262,97 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
     int *s_slot_cnt = (int *)(smem + P.lds_slot_cnt);
     float *s_tinv = (float *)(smem + P.lds_tinv);
     float *s_hinv = (float *)(smem + P.lds_hinv);
+    uint32_t *s_xmax = (uint32_t *)(smem + P.lds_xmax);
     int *s_misc = (int *)(smem + P.lds_misc);
     uint8_t *s_xa = smem + P.lds_xa;
     uint8_t *s_chunk = smem + P.lds_chunk + wave * P.chunk_stride;
 
-    // ======================= Phase A: routing and grouping =======================
-    if (P.mode & DEC_MODE_ROUTE) {
-        for (int t = wave; t < T; t += DEC_WAVES)
-            wave_topk_row<16>(P.logits + (size_t)t * E, E, k, s_idx + t * k, s_w + t * k, lane);
+    TRACE(0);
+    // ======================= Phase A: activations, routing, grouping =======================
+    const int nkbH = H >> 5;
+    for (int i = tid; i < T; i += DEC_THREADS) s_xmax[i] = 0u;
+    if (P.mode & DEC_MODE_ROUTE)
         for (int e = tid; e <= E; e += DEC_THREADS) s_hist[e] = 0;
-        __syncthreads();
+    __syncthreads();
+
+    // activation blocks: thread owns blocks tid + 512 q (token t, block b)
+    constexpr int QX = XPARTS == 1 ? DEC_X_BLOCKS_PER_THREAD : DEC_X_BLOCKS_PER_THREAD / 2;
+    constexpr int NV = XPARTS == 1 ? 4 : 8;  // 16-byte pieces per block (bf16: 64 B, fp32: 128 B)
+    u32x4 xr[QX][NV];
+    const int nxb = T * nkbH;
+#pragma unroll
+    for (int q = 0; q < QX; ++q) {
+        const int j = tid + DEC_THREADS * q;
+        if (j < nxb) {
+            const u32x4 *src = (const u32x4 *)((const uint8_t *)P.x + (size_t)j * 32 * (XPARTS == 1 ? 2 : 4));
+#pragma unroll
+            for (int v = 0; v < NV; ++v) xr[q][v] = src[v];
+        }
+    }
+    // routing of the rows owned by this wave (overlaps the activation loads)
+    if (P.mode & DEC_MODE_ROUTE) {
+        const int epl = (E + 63) >> 6;
+        for (int t = wave; t < T; t += DEC_WAVES) {
+            const float *row = P.logits + (size_t)t * E;
+            if (epl <= 2) route_row<2>(row, E, k, s_idx + t * k, s_w + t * k, lane);
+            else if (epl <= 4) route_row<4>(row, E, k, s_idx + t * k, s_w + t * k, lane);
+            else if (epl <= 8) route_row<8>(row, E, k, s_idx + t * k, s_w + t * k, lane);
+            else route_row<16>(row, E, k, s_idx + t * k, s_w + t * k, lane);
+        }
+    }
+    // per-token max |x|
+#pragma unroll
+    for (int q = 0; q < QX; ++q) {
+        const int j = tid + DEC_THREADS * q;
+        if (j < nxb) {
+            float mx = 0.0f;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const uint32_t w4[4] = {xr[q][v].x, xr[q][v].y, xr[q][v].z, xr[q][v].w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if (XPARTS == 1) {
+                        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w4[c] << 16)));
+                        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w4[c] & 0xFFFF0000u)));
+                    } else {
+                        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w4[c])));
+                    }
+                }
+            }
+            atomicMax(&s_xmax[j / nkbH], __builtin_bit_cast(uint32_t, mx));
+        }
+    }
+    TRACE(1);
+    __syncthreads();
+
+    // grouping: histogram, scan (wave 0), stable placement
+    if (P.mode & DEC_MODE_ROUTE) {
         for (int p = tid; p < TK; p += DEC_THREADS) atomicAdd(&s_hist[s_idx[p]], 1);
         __syncthreads();
         if (wave == 0) {
             // exclusive scan of (count | active flag << 16) over E <= 1024 experts
             const int per = (E + 63) / 64;
-            int base = lane * per;
+            const int base = lane * per;
             int sum = 0;
             for (int i = 0; i < per; ++i) {
-                int e = base + i;
+                const int e = base + i;
                 if (e < E) {
-                    int c = s_hist[e];
+                    const int c = s_hist[e];
                     sum += c | ((c > 0) << 16);
                 }
             }
             int incl = sum;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
-                int o = __shfl_up(incl, off, 64);
+                const int o = __shfl_up(incl, off, 64);
                 if (lane >= off) incl += o;
             }
             int run = incl - sum;
             for (int i = 0; i < per; ++i) {
-                int e = base + i;
+                const int e = base + i;
                 if (e < E) {
-                    int c = s_hist[e];
-                    int off = run & 0xFFFF, act = run >> 16;
+                    const int c = s_hist[e];
+                    const int off = run & 0xFFFF, act = run >> 16;
                     if (c > 0) {
                         s_slot_exp[hs + act] = e;
                         s_slot_start[hs + act] = off;
@@ -208,9 +365,9 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             if (lane == 63) s_misc[0] = hs + (incl >> 16);  // number of slots
         }
         __syncthreads();
-        // stable placement: rank of pair p among earlier pairs of the same expert
         for (int p = tid; p < TK; p += DEC_THREADS) {
-            int e = s_idx[p], rank = 0;
+            const int e = s_idx[p];
+            int rank = 0;
             for (int q = 0; q < p; ++q) rank += (s_idx[q] == e);
             s_sorted[s_hist[e] + rank] = p;
         }
@@ -266,158 +423,157 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         s_slot_start[0] = 0;
         s_slot_cnt[0] = T;
     }
-
-    // activations: per-token power-of-two scale, fp16 in the format's k order
-    {
-        const int nkb = H >> 5;
-        for (int t = wave; t < T; t += DEC_WAVES) {
-            float mx = 0.0f;
-            if (P.x_f32) {
-                const float *xr = (const float *)P.x + (size_t)t * H;
-                for (int i = lane; i < H; i += 64) mx = fmaxf(mx, fabsf(xr[i]));
-            } else {
-                const uint16_t *xr = (const uint16_t *)P.x + (size_t)t * H;
-                for (int i = lane; i < H; i += 64) mx = fmaxf(mx, fabsf(bf16_bits_to_float(xr[i])));
-            }
-            mx = wave_max_f(mx);
+    // activations to fp16 (hi [+ lo]) of x * 2^sc_t in the format's k order
+#pragma unroll
+    for (int q = 0; q < QX; ++q) {
+        const int j = tid + DEC_THREADS * q;
+        if (j < nxb) {
+            const int t = j / nkbH, b = j - t * nkbH;
+            const float mx = __builtin_bit_cast(float, s_xmax[t]);
             int ex = 0;
             if (mx > 0.0f) frexpf(mx, &ex);
-            int sc = (mx > 0.0f) ? 14 - ex : 0;  // max * 2^sc in [2^13, 2^14)
-            if (lane == 0) s_tinv[t] = ldexpf(1.0f, -sc);
-            for (int grp = lane; grp < nkb * 4; grp += 64) {
-                int b = grp >> 2, g = grp & 3;
-                u32x4 hi4, lo4;
-                uint16_t hv[8], lv[8];
+            const int sc = mx > 0.0f ? 14 - ex : 0;  // max * 2^sc in [2^13, 2^14)
+            const float scale = __builtin_bit_cast(float, (uint32_t)(127 + sc) << 23);  // 2^sc, exact
+            if (b == 0) s_tinv[t] = __builtin_bit_cast(float, (uint32_t)(127 - sc) << 23);
+            uint32_t w[NV * 4];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    int pos = b * 32 + pos_in_block(BITS, g, e);
-                    float xv = P.x_f32 ? ((const float *)P.x)[(size_t)t * H + pos]
-                                       : bf16_bits_to_float(((const uint16_t *)P.x)[(size_t)t * H + pos]);
-                    xv = ldexpf(xv, sc);
-                    _Float16 h = (_Float16)xv;
-                    hv[e] = __builtin_bit_cast(uint16_t, h);
-                    lv[e] = f2h_bits(xv - (float)h);
+            for (int v = 0; v < NV; ++v) {
+                w[4 * v] = xr[q][v].x;
+                w[4 * v + 1] = xr[q][v].y;
+                w[4 * v + 2] = xr[q][v].z;
+                w[4 * v + 3] = xr[q][v].w;
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                uint32_t hv[4], lv[4];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    uint16_t hb2[2], lb2[2];
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int pos = pos_in_block(BITS, g, 2 * e2 + h2);
+                        float xv;
+                        if (XPARTS == 1) xv = __builtin_bit_cast(float, (w[pos >> 1] >> (16 * (pos & 1))) << 16);
+                        else xv = __builtin_bit_cast(float, w[pos]);
+                        xv *= scale;
+                        const _Float16 hh = (_Float16)xv;
+                        hb2[h2] = __builtin_bit_cast(uint16_t, hh);
+                        lb2[h2] = f2h_bits(xv - (float)hh);
+                    }
+                    hv[e2] = hb2[0] | ((uint32_t)hb2[1] << 16);
+                    lv[e2] = lb2[0] | ((uint32_t)lb2[1] << 16);
                 }
-                hi4.x = hv[0] | ((uint32_t)hv[1] << 16);
-                hi4.y = hv[2] | ((uint32_t)hv[3] << 16);
-                hi4.z = hv[4] | ((uint32_t)hv[5] << 16);
-                hi4.w = hv[6] | ((uint32_t)hv[7] << 16);
-                *(u32x4 *)(s_xa + (((size_t)t * nkb + b) * 4 + g) * 16) = hi4;
-                if (XPARTS == 2) {
-                    lo4.x = lv[0] | ((uint32_t)lv[1] << 16);
-                    lo4.y = lv[2] | ((uint32_t)lv[3] << 16);
-                    lo4.z = lv[4] | ((uint32_t)lv[5] << 16);
-                    lo4.w = lv[6] | ((uint32_t)lv[7] << 16);
-                    *(u32x4 *)(s_xa + (((size_t)(T + t) * nkb + b) * 4 + g) * 16) = lo4;
-                }
+                *(u32x4 *)(s_xa + (((size_t)t * nkbH + b) * 4 + g) * 16) = u32x4{hv[0], hv[1], hv[2], hv[3]};
+                if (XPARTS == 2)
+                    *(u32x4 *)(s_xa + (((size_t)(T + t) * nkbH + b) * 4 + g) * 16) = u32x4{lv[0], lv[1], lv[2], lv[3]};
             }
         }
     }
     __syncthreads();
+    TRACE(2);
 
     const int n_slots = s_misc[0];
     const int bb = block_bytes(BITS);
     const int F = P.F, Fs = has_shared ? P.Fs : 0;
-    const int nkbH = H >> 5;
     const int cbH = chunk_blocks(nkbH), nchH = nkbH / cbH, segH = cbH * bb;
     const size_t rowH = (size_t)nkbH * bb;
     const size_t eb = (size_t)3 * F * rowH;  // routed expert blob bytes
-    const int items_sh = Fs >> 4, items_rt = F >> 4;
-    const int n_items = items_sh + (n_slots - hs) * items_rt;
+    const int units_sh = (Fs >> 4) * 2 * nchH, units_rt = (F >> 4) * 2 * nchH;
+    const int n_units = units_sh + (n_slots - hs) * units_rt;
     const int n_lane = lane & 15, g_lane = lane >> 4;
+    const int fstride = P.part_stride / (2 * nchH);  // Fmax
 
-    // ======================= Phase B: gate/up + SwiGLU =======================
-    for (int it = blockIdx.x * DEC_WAVES + wave; it < n_items; it += gridDim.x * DEC_WAVES) {
-        int s, fg, Fx;
-        const uint8_t *blob;
-        if (it < items_sh) {
-            s = 0;
-            fg = it;
-            Fx = Fs;
-            blob = P.w_shared;
-        } else {
-            int r = it - items_sh;
-            s = hs + r / items_rt;
-            fg = r - (s - hs) * items_rt;
-            Fx = F;
-            blob = P.w_routed + (size_t)s_slot_exp[s] * eb;
-        }
-        const size_t mat = (size_t)Fx * rowH;
-        const uint8_t *rows_g = blob + (size_t)fg * 16 * rowH;
-        const uint8_t *rows_u = rows_g + mat;
-        const int n_tok = s_slot_cnt[s];
-        const bool shared_slot = (s_slot_exp[s] < 0);
-        const int m_tok = n_lane;  // A row (slot-local token) of this lane
-        int tok = 0;
-        if (m_tok < n_tok) tok = shared_slot ? m_tok : s_sorted[s_slot_start[s] + m_tok] / k;
-        const bool a_valid = m_tok < n_tok;
-
-        float4v accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-        const int nch = 2 * nchH;  // gate chunks then up chunks
-        Chunk c0, c1;
-        chunk_load(c0, rows_g, (int)rowH, 0, segH, lane);
-        for (int ci = 0; ci < nch; ++ci) {
-            // next chunk into the other register set
-            if (ci + 1 < nch) {
-                int cn = ci + 1;
-                const uint8_t *rb = cn < nchH ? rows_g : rows_u;
-                int kc = cn < nchH ? cn : cn - nchH;
-                if (ci & 1) chunk_load(c0, rb, (int)rowH, kc * segH, segH, lane);
-                else chunk_load(c1, rb, (int)rowH, kc * segH, segH, lane);
+    // ======================= Phase B: gate/up units =======================
+    {
+        struct Unit {
+            const uint8_t *rows;
+            int s, fg, mat, kc;
+        };
+        auto unit_of = [&](int u) {
+            Unit U;
+            int Fx, r;
+            const uint8_t *blob;
+            if (u < units_sh) {
+                U.s = 0;
+                r = u;
+                Fx = Fs;
+                blob = P.w_shared;
+            } else {
+                const int v = u - units_sh;
+                U.s = hs + v / units_rt;
+                r = v - (U.s - hs) * units_rt;
+                Fx = F;
+                blob = P.w_routed + (size_t)s_slot_exp[U.s] * eb;
             }
+            U.fg = r / (2 * nchH);
+            const int rem = r - U.fg * 2 * nchH;
+            U.mat = rem / nchH;
+            U.kc = rem - U.mat * nchH;
+            U.rows = blob + (size_t)U.mat * Fx * rowH + (size_t)U.fg * 16 * rowH;
+            return U;
+        };
+        // unit order: wave 0 of every workgroup first, then wave 1, ...
+        int u = wave * G + blockIdx.x;
+        const int ustep = G * DEC_WAVES;
+        Chunk c;
+        if (u < n_units) {
+            const Unit U = unit_of(u);
+            chunk_load(c, U.rows, (int)rowH, U.kc * segH, segH, lane);
+        }
+        for (; u < n_units; u += ustep) {
+            const Unit U = unit_of(u);
             __builtin_amdgcn_wave_barrier();
-            if (ci & 1) chunk_store_lds(c1, s_chunk, segH, lane);
-            else chunk_store_lds(c0, s_chunk, segH, lane);
+            chunk_store_lds(c, s_chunk, segH, lane);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const int kc = ci < nchH ? ci : ci - nchH;
-            float4v &acc = ci < nchH ? accg : accu;
-            for (int b = 0; b < cbH; ++b) {
-                const int gb = kc * cbH + b;  // block index along K
-                half8 a[XPARTS];
+            // the registers are free again: the next unit's chunk streams in
+            // while this one computes
+            const int un = u + ustep;
+            if (un < n_units) {
+                const Unit N = unit_of(un);
+                chunk_load(c, N.rows, (int)rowH, N.kc * segH, segH, lane);
+            }
+
+            const int n_tok = s_slot_cnt[U.s];
+            const bool shared_slot = s_slot_exp[U.s] < 0;
+            const bool a_valid = n_lane < n_tok;
+            int tok = 0;
+            if (a_valid) tok = shared_slot ? n_lane : s_sorted[s_slot_start[U.s] + n_lane] / k;
+            const uint8_t *a_base = s_xa + (((size_t)tok * nkbH + U.kc * cbH) * 4 + g_lane) * 16;
+            float4v acc = {0.f, 0.f, 0.f, 0.f};
+            chunk_mma<BITS, XPARTS>(acc, s_chunk, segH, cbH, n_lane, g_lane, a_base, 64, T * nkbH * 64, a_valid);
+
+            // publish the partial sums (back in the units of x), laid out in the
+            // down projection's k order so the consumer reads whole groups
+            const float av[4] = {acc.x, acc.y, acc.z, acc.w};
+            const int f = U.fg * 16 + n_lane;
+            int pg, pe;
+            group_slot_of(BITS, f & 31, pg, pe);
+            const int fo = (f >> 5) * 32 + pg * 8 + pe;
 #pragma unroll
-                for (int xp = 0; xp < XPARTS; ++xp) {
-                    if (a_valid)
-                        a[xp] = *(const half8 *)(s_xa + (((size_t)(xp * T + tok) * nkbH + gb) * 4 + g_lane) * 16);
-                    else
-                        a[xp] = half8{0, 0, 0, 0, 0, 0, 0, 0};
+            for (int r = 0; r < 4; ++r) {
+                const int m = 4 * g_lane + r;
+                if (m < n_tok) {
+                    const int tk = shared_slot ? m : s_sorted[s_slot_start[U.s] + m] / k;
+                    const int row = shared_slot ? TK + m : s_slot_start[U.s] + m;
+                    st_dev(P.gu_part + (size_t)row * P.part_stride + (size_t)(U.mat * nchH + U.kc) * fstride + fo,
+                           av[r] * s_tinv[tk]);
                 }
-                BOp<BITS> op;
-                op.load(s_chunk, segH, b, n_lane, g_lane);
-                block_mma<BITS, XPARTS>(acc, op, a);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            wait_all_mem();  // this wave's partial stores are complete before the count goes up
             __builtin_amdgcn_wave_barrier();
+            if (lane == 0) add_dev(&P.gu_count[U.s], 1u);
         }
-        // SwiGLU in fp32; h published as fp32 in the down projection's k order
-        const int f = fg * 16 + n_lane;
-        int pb = f >> 5, pg, pe;
-        group_slot_of(BITS, f & 31, pg, pe);
-        float gv[4] = {accg.x, accg.y, accg.z, accg.w};
-        float uv[4] = {accu.x, accu.y, accu.z, accu.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            int m = 4 * g_lane + r;
-            if (m < n_tok) {
-                int tk = shared_slot ? m : s_sorted[s_slot_start[s] + m] / k;
-                float ti = s_tinv[tk];
-                float g1 = gv[r] * ti, u1 = uv[r] * ti;
-                float h = g1 / (1.0f + expf(-g1)) * u1;
-                int row = shared_slot ? TK + m : s_slot_start[s] + m;
-                *(float *)(P.h_arr + (size_t)row * P.h_row_bytes + (size_t)pb * 128 + pg * 32 + pe * 4) = h;
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __builtin_amdgcn_wave_barrier();
-        if (lane == 0) atomic_add_release(&P.gu_count[s], 1u);
     }
+    TRACE(3);
 
     // ======================= Phase C: down + weighted write + combine =======================
     const int tiles_per_slot = H / DEC_DN_ROWS;
     const int n_tiles = n_slots * tiles_per_slot;
-    const int t0 = (int)(((long long)blockIdx.x * n_tiles) / gridDim.x);
-    const int t1 = (int)(((long long)(blockIdx.x + 1) * n_tiles) / gridDim.x);
+    const int t0 = (int)(((long long)blockIdx.x * n_tiles) / G);
+    const int t1 = (int)(((long long)(blockIdx.x + 1) * n_tiles) / G);
     int cur_slot = -1;
     for (int ti = t0; ti < t1; ++ti) {
         const int s = ti / tiles_per_slot, rg = ti - s * tiles_per_slot;
@@ -430,152 +586,152 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         const uint8_t *rows_d = blob + (size_t)2 * Fx * rowH + (size_t)(rg * DEC_DN_ROWS + wave * 16) * rowF;
         const int n_tok = s_slot_cnt[s];
 
-        Chunk c0, c1;
-        chunk_load(c0, rows_d, (int)rowF, 0, segF, lane);  // prefetch before the wait
+        Chunk c;
+        chunk_load(c, rows_d, (int)rowF, 0, segF, lane);  // prefetch before the wait
 
         if (s != cur_slot) {
             __syncthreads();  // previous tile's readers of s_xa are done
+            if (ti == t0) TRACE(4);
             if (tid == 0) {
-                const uint32_t need = (uint32_t)(Fx >> 4);
+                const uint32_t need = (uint32_t)((Fx >> 4) * 2 * nchH);
                 uint32_t spins = 0;
-                while (atomic_load_acquire(&P.gu_count[s]) < need) {
-                    __builtin_amdgcn_s_sleep(2);
-                    if (++spins > DEC_SPIN_LIMIT || (atomic_load_acquire(P.err) & 1u)) {
+                while (ld_dev_u32(&P.gu_count[s]) < need) {
+                    __builtin_amdgcn_s_sleep(1);
+                    if (++spins > DEC_SPIN_LIMIT || (ld_dev_u32(P.err) & 1u)) {
                         atomicOr(P.err, 1u);
                         break;
                     }
                 }
             }
+            if (ti == t0) TRACE(5);
             __syncthreads();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            // stage this expert's h rows into LDS as fp16 hi + lo of h * 2^sc_t,
-            // sc_t a per-token power of two putting max|h_t| in [2^13, 2^14)
+            // h = silu(g) * u from the fixed-order sum of the partials; staged in
+            // LDS as fp16 hi + lo of h * 2^sc_t (per-token power of two)
             const int row0 = shared_slot ? TK : s_slot_start[s];
             const int ngrp = Fx >> 3;  // groups of 8 values (one k-group of one block)
             for (int r = wave; r < n_tok; r += DEC_WAVES) {
-                const float *hr = (const float *)(P.h_arr + (size_t)(row0 + r) * P.h_row_bytes);
+                const float *pr = P.gu_part + (size_t)(row0 + r) * P.part_stride;
+                float hv[2][8];
                 float mx = 0.0f;
-                for (int gi = lane; gi < ngrp; gi += 64) {
-                    u32x4 a = *(const u32x4 *)(hr + gi * 8), b = *(const u32x4 *)(hr + gi * 8 + 4);
-                    float v[8] = {__builtin_bit_cast(float, a.x), __builtin_bit_cast(float, a.y),
-                                  __builtin_bit_cast(float, a.z), __builtin_bit_cast(float, a.w),
-                                  __builtin_bit_cast(float, b.x), __builtin_bit_cast(float, b.y),
-                                  __builtin_bit_cast(float, b.z), __builtin_bit_cast(float, b.w)};
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
+                for (int q = 0; q < 2; ++q) {
+                    const int gi = lane + 64 * q;
+                    if (gi < ngrp) {
+                        float gs[8], us[8];
+                        const float *pg0 = pr + gi * 8;
+                        const float *pu0 = pr + (size_t)nchH * fstride + gi * 8;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            gs[e] = ld_dev(pg0 + e);
+                            us[e] = ld_dev(pu0 + e);
+                        }
+                        for (int kc = 1; kc < nchH; ++kc) {  // fixed order: chunk 0, 1, ...
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                gs[e] += ld_dev(pg0 + (size_t)kc * fstride + e);
+                                us[e] += ld_dev(pu0 + (size_t)kc * fstride + e);
+                            }
+                        }
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float h = gs[e] / (1.0f + expf(-gs[e])) * us[e];
+                            hv[q][e] = h;
+                            mx = fmaxf(mx, fabsf(h));
+                        }
+                    }
                 }
-                mx = wave_max_f(mx);
+                mx = __builtin_bit_cast(float, wave_max_u32(__builtin_bit_cast(uint32_t, mx)));
                 int ex = 0;
                 if (mx > 0.0f) frexpf(mx, &ex);
                 const int sc = mx > 0.0f ? 14 - ex : 0;
-                if (lane == 0) s_hinv[r] = ldexpf(1.0f, -sc);
-                for (int gi = lane; gi < ngrp; gi += 64) {
-                    u32x4 a = *(const u32x4 *)(hr + gi * 8), b = *(const u32x4 *)(hr + gi * 8 + 4);
-                    uint32_t w8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-                    uint16_t hv[8], lv[8];
+                const float scale = __builtin_bit_cast(float, (uint32_t)(127 + sc) << 23);
+                if (lane == 0) s_hinv[r] = __builtin_bit_cast(float, (uint32_t)(127 - sc) << 23);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        float v = ldexpf(__builtin_bit_cast(float, w8[e]), sc);
-                        _Float16 hh = (_Float16)v;
-                        hv[e] = __builtin_bit_cast(uint16_t, hh);
-                        lv[e] = f2h_bits(v - (float)hh);
+                for (int q = 0; q < 2; ++q) {
+                    const int gi = lane + 64 * q;
+                    if (gi < ngrp) {
+                        uint32_t h4[4], l4[4];
+#pragma unroll
+                        for (int e2 = 0; e2 < 4; ++e2) {
+                            const float v0 = hv[q][2 * e2] * scale, v1 = hv[q][2 * e2 + 1] * scale;
+                            const _Float16 a0 = (_Float16)v0, a1 = (_Float16)v1;
+                            h4[e2] = __builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
+                            l4[e2] = f2h_bits(v0 - (float)a0) | ((uint32_t)f2h_bits(v1 - (float)a1) << 16);
+                        }
+                        uint8_t *dst = s_xa + (size_t)r * (Fx * 4) + (size_t)gi * 32;
+                        *(u32x4 *)dst = u32x4{h4[0], h4[1], h4[2], h4[3]};
+                        *(u32x4 *)(dst + 16) = u32x4{l4[0], l4[1], l4[2], l4[3]};
                     }
-                    u32x4 h4, l4;
-                    h4.x = hv[0] | ((uint32_t)hv[1] << 16);
-                    h4.y = hv[2] | ((uint32_t)hv[3] << 16);
-                    h4.z = hv[4] | ((uint32_t)hv[5] << 16);
-                    h4.w = hv[6] | ((uint32_t)hv[7] << 16);
-                    l4.x = lv[0] | ((uint32_t)lv[1] << 16);
-                    l4.y = lv[2] | ((uint32_t)lv[3] << 16);
-                    l4.z = lv[4] | ((uint32_t)lv[5] << 16);
-                    l4.w = lv[6] | ((uint32_t)lv[7] << 16);
-                    uint8_t *dst = s_xa + (size_t)r * (Fx * 4) + (size_t)gi * 32;
-                    *(u32x4 *)dst = h4;
-                    *(u32x4 *)(dst + 16) = l4;
                 }
             }
             __syncthreads();
+            if (ti == t0) TRACE(6);
             cur_slot = s;
         }
 
         float4v acc = {0.f, 0.f, 0.f, 0.f};
         const bool a_valid = n_lane < n_tok;
+        const uint8_t *a_base = s_xa + (size_t)n_lane * (Fx * 4) + g_lane * 32;
         for (int ci = 0; ci < nchF; ++ci) {
-            if (ci + 1 < nchF) {
-                if (ci & 1) chunk_load(c0, rows_d, (int)rowF, (ci + 1) * segF, segF, lane);
-                else chunk_load(c1, rows_d, (int)rowF, (ci + 1) * segF, segF, lane);
-            }
             __builtin_amdgcn_wave_barrier();
-            if (ci & 1) chunk_store_lds(c1, s_chunk, segF, lane);
-            else chunk_store_lds(c0, s_chunk, segF, lane);
+            chunk_store_lds(c, s_chunk, segF, lane);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            for (int b = 0; b < cbF; ++b) {
-                const int gb = ci * cbF + b;
-                half8 a[2];
-                if (a_valid) {
-                    const uint8_t *ap = s_xa + (size_t)n_lane * (Fx * 4) + (size_t)gb * 128 + g_lane * 32;
-                    a[0] = *(const half8 *)ap;
-                    a[1] = *(const half8 *)(ap + 16);
-                } else {
-                    a[0] = half8{0, 0, 0, 0, 0, 0, 0, 0};
-                    a[1] = a[0];
-                }
-                BOp<BITS> op;
-                op.load(s_chunk, segF, b, n_lane, g_lane);
-                block_mma<BITS, 2>(acc, op, a);
-            }
+            if (ci + 1 < nchF) chunk_load(c, rows_d, (int)rowF, (ci + 1) * segF, segF, lane);
+            chunk_mma<BITS, 2>(acc, s_chunk, segF, cbF, n_lane, g_lane, a_base + (size_t)ci * cbF * 128, 128, 16,
+                               a_valid);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
         }
-        // o = acc * 2^8; weighted write per pair
+        // o = acc * 2^-sc_t; weighted write per pair
         {
             const int hrow = rg * DEC_DN_ROWS + wave * 16 + n_lane;
-            float ov[4] = {acc.x, acc.y, acc.z, acc.w};
+            const float ov[4] = {acc.x, acc.y, acc.z, acc.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                int m = 4 * g_lane + r;
+                const int m = 4 * g_lane + r;
                 if (m < n_tok) {
-                    float o = ov[r] * s_hinv[m];
+                    const float o = ov[r] * s_hinv[m];
                     if (shared_slot) {
-                        P.out_shared[(size_t)m * H + hrow] = o;
+                        st_dev(&P.out_shared[(size_t)m * H + hrow], o);
                     } else {
-                        int p = s_sorted[s_slot_start[s] + m];
-                        P.out_pairs[(size_t)p * H + hrow] = s_w[p] * o;
+                        const int p = s_sorted[s_slot_start[s] + m];
+                        st_dev(&P.out_pairs[(size_t)p * H + hrow], s_w[p] * o);
                     }
                 }
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __syncthreads();
+        if (ti == t0) TRACE(7);
+        wait_all_mem();   // every wave's output stores are complete ...
+        __syncthreads();  // ... before the workgroup counts this tile
         if (tid == 0) {
             int do_combine = 0;
             if (P.mode & DEC_MODE_COMBINE) {
-                uint32_t old = atomic_add_release(&P.slice_count[rg], 1u);
+                const uint32_t old = add_dev(&P.slice_count[rg], 1u);
                 do_combine = (old == (uint32_t)(n_slots - 1));
             }
-            uint32_t dn = atomic_add_release(&P.dn_count[s], 1u);
+            const uint32_t dn = add_dev(&P.dn_count[s], 1u);
             if (dn == (uint32_t)(tiles_per_slot - 1)) {
-                atomic_store_relaxed(&P.gu_count[s], 0u);
-                atomic_store_relaxed(&P.dn_count[s], 0u);
+                store_dev_u32(&P.gu_count[s], 0u);
+                store_dev_u32(&P.dn_count[s], 0u);
             }
             s_misc[1] = do_combine;
         }
         __syncthreads();
         if (s_misc[1]) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             for (int i = tid; i < T * DEC_DN_ROWS; i += DEC_THREADS) {
                 const int t = i / DEC_DN_ROWS, hrow = rg * DEC_DN_ROWS + (i - t * DEC_DN_ROWS);
-                float acc2 = P.out_pairs[((size_t)t * k) * H + hrow];
-                for (int j = 1; j < k; ++j) acc2 += P.out_pairs[((size_t)t * k + j) * H + hrow];
-                if (has_shared) acc2 += P.out_shared[(size_t)t * H + hrow];
+                float acc2 = ld_dev(&P.out_pairs[((size_t)t * k) * H + hrow]);
+                for (int j = 1; j < k; ++j) acc2 += ld_dev(&P.out_pairs[((size_t)t * k + j) * H + hrow]);
+                if (has_shared) acc2 += ld_dev(&P.out_shared[(size_t)t * H + hrow]);
                 P.y[(size_t)t * H + hrow] = acc2;
             }
             __syncthreads();
-            if (tid == 0) atomic_store_relaxed(&P.slice_count[rg], 0u);
+            if (tid == 0) store_dev_u32(&P.slice_count[rg], 0u);
         }
     }
+    TRACE(8);
 }
 
 // ---------------------------------------------------------------------------
@@ -597,14 +753,13 @@ static int occupancy_t(int lds) {
 
 template <int BITS, int XPARTS>
 static hipError_t set_lds_t(int lds) {
-    return hipFuncSetAttribute((const void *)k_decode_layer<BITS, XPARTS>,
-                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    return hipFuncSetAttribute((const void *)k_decode_layer<BITS, XPARTS>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               lds);
 }
 
 hipError_t decode_launch(const DecodeParams &P, int grid, hipStream_t st) {
-    const int xp = P.x_f32 ? 2 : 1;
-    if (P.bits == 4) return xp == 2 ? launch_t<4, 2>(P, grid, st) : launch_t<4, 1>(P, grid, st);
-    return xp == 2 ? launch_t<3, 2>(P, grid, st) : launch_t<3, 1>(P, grid, st);
+    if (P.bits == 4) return P.x_f32 ? launch_t<4, 2>(P, grid, st) : launch_t<4, 1>(P, grid, st);
+    return P.x_f32 ? launch_t<3, 2>(P, grid, st) : launch_t<3, 1>(P, grid, st);
 }
 
 int decode_occupancy(int bits, int x_f32, int lds) {
@@ -618,5 +773,11 @@ hipError_t decode_set_lds(int bits, int x_f32, int lds) {
 }
 
 int decode_chunk_blocks(int nkb) { return chunk_blocks(nkb); }
+
+#ifdef MOE_PHASE_TRACE
+extern "C" int moe_trace_set(void *buf) {
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_trace), &buf, sizeof(buf)) == hipSuccess ? 0 : -1;
+}
+#endif
 
 }  // namespace moe

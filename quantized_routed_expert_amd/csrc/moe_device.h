@@ -167,19 +167,30 @@ __device__ __forceinline__ float wave_sum_f(float v) {
     return v;
 }
 
-// Device-scope release/acquire helpers for the cross-workgroup counters.
-__device__ __forceinline__ uint32_t atomic_add_release(uint32_t *p, uint32_t v) {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+// Cross-workgroup handoff without cache-wide maintenance.  On gfx950 each
+// XCD has its own L2, so an agent-scope release/acquire fence turns into an
+// L2 write-back / invalidate of the whole XCD cache.  Instead the data that
+// crosses workgroups is written and read with device-coherent (agent-scope)
+// relaxed atomic accesses, a wave waits for its own stores to complete
+// (s_waitcnt) before it raises a counter, and counters are polled with relaxed
+// agent-scope loads.
+__device__ __forceinline__ void st_dev(float *p, float v) {
+    __hip_atomic_store((uint32_t *)p, __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t atomic_load_acquire(const uint32_t *p) {
-    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ float ld_dev(const float *p) {
+    return __builtin_bit_cast(float, __hip_atomic_load((const uint32_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
-__device__ __forceinline__ void atomic_store_relaxed(uint32_t *p, uint32_t v) {
+__device__ __forceinline__ uint32_t ld_dev_u32(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_dev(uint32_t *p, uint32_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev_u32(uint32_t *p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void fence_acq_rel_agent() {
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
-}
+// all of this wave's memory operations have completed
+__device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Router for one logits row by one wave: the k largest logits (an equal logit
 // goes to the lower expert id; the comparison is on the fp32 values, -0 == +0)

@@ -15,6 +15,8 @@ constexpr int DEC_DN_ROWS = DEC_WAVES * 16;  // down-projection rows per workgro
 constexpr int DEC_CB_MAX = 32;               // quant blocks per row in one streamed chunk
 constexpr int DEC_MAX_LD = 9;                // 16-byte loads per lane per chunk (16 rows x 32 x 18 B)
 constexpr int DEC_MAX_E_FUSED = 1024;        // router fused into the kernel up to this many experts
+constexpr int DEC_MAX_F = 1024;              // expert FFN width handled by the fused decode launch
+constexpr int DEC_X_BLOCKS_PER_THREAD = 4;   // activation blocks staged per thread (bf16; 2 for fp32)
 constexpr uint32_t DEC_SPIN_LIMIT = 1u << 20;  // bounded waits: a wait that runs out sets err bit 0
 #define MOE_MAX_EXPERTS_DEV 4096
 #define MOE_DECODE_ROWS_DEV 16
@@ -38,17 +40,18 @@ struct DecodeParams {
     float *out_shared;         // [T][H]
     int32_t *topk_idx_out;     // may be null
     float *topk_w_out;         // may be null
-    uint8_t *h_arr;            // [(T*k + T)][Fmax] fp32, down projection's k order
+    float *gu_part;            // [(T*k + T)][2][nch][Fmax] fp32 partial gate/up sums per K chunk
     uint32_t *gu_count;        // [max_slots]
     uint32_t *dn_count;        // [max_slots]
     uint32_t *slice_count;     // [H / DEC_DN_ROWS]
     uint32_t *err;             // error word (bit 0: a wait hit its spin limit)
     int T, E, k, H, F, Fs;     // Fs = shared ffn (0 = none)
     int bits, x_f32, mode, max_slots;
-    int h_row_bytes;           // Fmax * 4
+    int part_stride;           // floats per gu_part row = 2 * nch * Fmax
+    int nch;                   // K chunks of the gate/up rows
     // dynamic LDS layout (byte offsets)
     int lds_idx, lds_w, lds_sorted, lds_hist, lds_slot_start, lds_slot_exp, lds_slot_cnt,
-        lds_tinv, lds_hinv, lds_misc, lds_xa, lds_chunk, chunk_stride, lds_total;
+        lds_tinv, lds_hinv, lds_xmax, lds_misc, lds_xa, lds_chunk, chunk_stride, lds_total;
 };
 
 // ---------------------------------------------------------------------------
