@@ -18,7 +18,6 @@ namespace moe {
 hipError_t decode_launch(const DecodeParams &P, int grid, hipStream_t st);
 int decode_occupancy(int bits, int x_f32, int lds);
 hipError_t decode_set_lds(int bits, int x_f32, int lds);
-int decode_chunk_blocks(int nkb);
 hipError_t route_launch(const RouteParams &P, hipStream_t st);
 hipError_t group_launch(const GroupParams &P, hipStream_t st);
 }  // namespace moe
@@ -76,10 +75,9 @@ struct Layout {
 
 // The counters sit at offset 0 with a size that depends on no shape, in every
 // layout, so a workspace that is zero before its first use stays valid for
-// calls of any shape and path (each call returns the counters to zero).
-constexpr size_t COUNTER_SLOTS = MOE_MAX_EXPERTS + 1;
-constexpr size_t COUNTER_WORDS = 2 * COUNTER_SLOTS + 65536 / DEC_DN_ROWS + 4;
-
+// calls of any shape and path (each call returns the counters to zero).  Each
+// counter has a 256-byte line of its own.
+constexpr size_t COUNTER_WORDS = (size_t)(2 * DEC_MAX_SLOTS + DEC_MAX_SLICES + 1) * DEC_CSTRIDE;
 Layout make_layout(int T, int E, int k, int H, int F, int Fs, int path) {
     Layout L;
     size_t off = 0;
@@ -91,7 +89,7 @@ Layout make_layout(int T, int E, int k, int H, int F, int Fs, int path) {
     const size_t TK = (size_t)T * k;
     const int Fmax = F > Fs ? F : Fs;
     L.nchunks = (T + GRP_CHUNK_TOKENS - 1) / GRP_CHUNK_TOKENS;
-    L.max_slots = (int)COUNTER_SLOTS;
+    L.max_slots = DEC_MAX_SLOTS;
     L.n_counters = COUNTER_WORDS;
     L.counters = take(COUNTER_WORDS * 4);
     // routing and grouping (all paths; moe_group uses chunk_counts)
@@ -104,9 +102,7 @@ Layout make_layout(int T, int E, int k, int H, int F, int Fs, int path) {
     L.out_pairs = take(TK * H * 4);
     L.out_shared = take((size_t)T * H * 4);
     if (path == MOE_PATH_DECODE) {
-        const int nkb = H / 32;
-        const int nch = nkb / decode_chunk_blocks(nkb);
-        L.harr = take((TK + T) * (size_t)2 * nch * Fmax * 4);  // partial gate/up sums
+        L.harr = take((TK + T) * (size_t)Fmax * 4);  // SwiGLU outputs per pair row (+ shared rows)
     } else {
         L.slot_exp = take((size_t)(E + 1) * 4);
         L.slot_row0 = take((size_t)(E + 1) * 4);
@@ -157,6 +153,7 @@ inline hipStream_t S(int64_t s) { return (hipStream_t)(intptr_t)s; }
 int decode_lds_layout(DecodeParams &P, int xparts) {
     const int TK = P.T * P.k;
     const int Fmax = P.F > P.Fs ? P.F : P.Fs;
+    const int bb = P.bits == 4 ? 18 : 14;
     int off = 0;
     auto take = [&](int bytes) {
         int a = off;
@@ -174,18 +171,23 @@ int decode_lds_layout(DecodeParams &P, int xparts) {
     P.lds_hinv = take(P.T * 4);
     P.lds_xmax = take(P.T * 4);
     P.lds_misc = take(64);
-    const int xa_bytes = xparts * P.T * P.H * 2;
-    const int ha_bytes = P.T * Fmax * 4;
+    // activations (one 16-byte pad per token row keeps the 16 rows of an
+    // MFMA operand read in distinct banks); later the staged h
+    P.x_rs = (P.H / 32) * 64 + 16;
+    P.h_rs = Fmax * 4 + 16;
+    const int xa_bytes = xparts * P.T * P.x_rs;
+    const int ha_bytes = P.T * P.h_rs;
     P.lds_xa = take(xa_bytes > ha_bytes ? xa_bytes : ha_bytes);
-    const int bb = P.bits == 4 ? 18 : 14;
-    const int cbH = decode_chunk_blocks(P.H / 32);
-    int cbF = decode_chunk_blocks(P.F / 32);
+    // wave-private chunk buffers (also the gate/up unit partials: 2 x 16 x 16 floats)
+    int cmax = 16 * decode_chunk_rstride(P.cbH * bb);
+    const int cf = 16 * decode_chunk_rstride(decode_f_chunk_blocks(P.F / 32) * bb);
+    cmax = cf > cmax ? cf : cmax;
     if (P.Fs) {
-        int c2 = decode_chunk_blocks(P.Fs / 32);
-        cbF = c2 > cbF ? c2 : cbF;
+        const int cs = 16 * decode_chunk_rstride(decode_f_chunk_blocks(P.Fs / 32) * bb);
+        cmax = cs > cmax ? cs : cmax;
     }
-    const int cmax = cbH > cbF ? cbH : cbF;
-    P.chunk_stride = (int)align_up((size_t)(16 * cmax * bb + 16), 16);
+    cmax = cmax > 2048 ? cmax : 2048;
+    P.chunk_stride = (int)align_up((size_t)cmax, 16);
     P.lds_chunk = take(DEC_WAVES * P.chunk_stride);
     P.lds_total = off;
     return off;
@@ -194,13 +196,28 @@ int decode_lds_layout(DecodeParams &P, int xparts) {
 int launch_err(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
 
 // Shapes the fused decode launch takes: every thread stages at most
-// DEC_X_BLOCKS_PER_THREAD activation blocks (half for fp32) and an expert's
-// FFN width is at most DEC_MAX_F.
-bool decode_fits(int T, int H, int F, int Fs, int x_dtype) {
-    const int per = x_dtype == MOE_DTYPE_F32 ? DEC_X_BLOCKS_PER_THREAD / 2 : DEC_X_BLOCKS_PER_THREAD;
+// DEC_X_BLOCKS_PER_THREAD activation blocks (half for fp32), an expert's FFN
+// width is at most DEC_MAX_F, the gate/up rows split into 1, 2, 4 or 8 K
+// chunks, and the LDS layout fits one workgroup per CU.
+constexpr int DEC_LDS_BUDGET = 160 * 1024;
+bool decode_fits(int T, int E, int k, int H, int F, int Fs, int bits, int x_dtype) {
+    const int xf = x_dtype == MOE_DTYPE_F32;
+    const int per = xf ? DEC_X_BLOCKS_PER_THREAD / 2 : DEC_X_BLOCKS_PER_THREAD;
     if ((long long)T * (H / 32) > (long long)per * DEC_THREADS) return false;
     if (F > DEC_MAX_F || Fs > DEC_MAX_F) return false;
-    return true;
+    if (decode_h_chunk_blocks(H / 32) == 0) return false;
+    DecodeParams P;
+    memset(&P, 0, sizeof(P));
+    P.T = T;
+    P.E = E;
+    P.k = k;
+    P.H = H;
+    P.F = F;
+    P.Fs = Fs;
+    P.bits = bits;
+    P.cbH = decode_h_chunk_blocks(H / 32);
+    P.max_slots = ((T * k < E) ? T * k : E) + 1;
+    return decode_lds_layout(P, xf ? 2 : 1) <= DEC_LDS_BUDGET;
 }
 
 }  // namespace
@@ -291,12 +308,12 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
     P.out_shared = at<float>(ws, L.out_shared);
     P.topk_idx_out = tidx;
     P.topk_w_out = tw;
-    P.gu_part = at<float>(ws, L.harr);
+    P.hbuf = at<float>(ws, L.harr);
     uint32_t *cnt = at<uint32_t>(ws, L.counters);
     P.gu_count = cnt;
-    P.dn_count = cnt + L.max_slots;
-    P.slice_count = cnt + 2 * L.max_slots;
-    P.err = cnt + 2 * L.max_slots + 65536 / DEC_DN_ROWS;
+    P.dn_count = cnt + (size_t)DEC_MAX_SLOTS * DEC_CSTRIDE;
+    P.slice_count = cnt + (size_t)2 * DEC_MAX_SLOTS * DEC_CSTRIDE;
+    P.err = cnt + (size_t)(2 * DEC_MAX_SLOTS + DEC_MAX_SLICES) * DEC_CSTRIDE;
     P.T = T;
     P.E = E;
     P.k = k;
@@ -307,9 +324,8 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
     P.x_f32 = x_f32;
     P.mode = mode | (shared ? DEC_MODE_SHARED : 0);
     P.max_slots = ((T * k < E) ? T * k : E) + 1;  // LDS slot tables (counters use the fixed stride)
-    const int Fmax = P.F > P.Fs ? P.F : P.Fs;
-    P.nch = (P.H / 32) / decode_chunk_blocks(P.H / 32);
-    P.part_stride = 2 * P.nch * Fmax;
+    P.h_stride = P.F > P.Fs ? P.F : P.Fs;
+    P.cbH = decode_h_chunk_blocks(P.H / 32);
     const int lds = decode_lds_layout(P, x_f32 ? 2 : 1);
     if (lds > dv.lds_max) return MOE_ERR_UNSUPPORTED;
     static std::mutex mu;
@@ -387,7 +403,8 @@ int moe_expert_ffn(const void *x, int32_t x_dtype, int32_t T, const moe_qweights
     rc = check_shape(T, w->n_experts, k, w->hidden, w->ffn);
     if (rc) return rc;
     int p = resolve_path(path, T);
-    if (p == MOE_PATH_DECODE && (T > MOE_DECODE_MAX_ROWS || !decode_fits(T, w->hidden, w->ffn, 0, x_dtype))) {
+    if (p == MOE_PATH_DECODE &&
+        (T > MOE_DECODE_MAX_ROWS || !decode_fits(T, w->n_experts, k, w->hidden, w->ffn, 0, w->bits, x_dtype))) {
         if (path == MOE_PATH_DECODE) return MOE_ERR_UNSUPPORTED;
         p = MOE_PATH_PREFILL;
     }
@@ -425,7 +442,8 @@ int moe_layer_forward(const void *x, int32_t x_dtype, const float *logits, int32
     const int Fs = shared ? shared->ffn : 0;
     int p = resolve_path(path, T);
     const bool same_bits = !shared || shared->bits == routed->bits;
-    if (p == MOE_PATH_DECODE && (T > MOE_DECODE_MAX_ROWS || !same_bits || !decode_fits(T, H, routed->ffn, Fs, x_dtype))) {
+    if (p == MOE_PATH_DECODE && (T > MOE_DECODE_MAX_ROWS || !same_bits ||
+                                 !decode_fits(T, E, k, H, routed->ffn, Fs, routed->bits, x_dtype))) {
         if (path == MOE_PATH_DECODE) return MOE_ERR_UNSUPPORTED;
         p = MOE_PATH_PREFILL;
     }

@@ -47,11 +47,21 @@ namespace moe {
 __device__ uint64_t *g_trace = nullptr;
 #define TRACE(slot)                                                                                        \
     do {                                                                                                   \
-        if (g_trace && threadIdx.x == 0) g_trace[blockIdx.x * 16 + (slot)] = __builtin_amdgcn_s_memrealtime(); \
+        if (g_trace && threadIdx.x == 0) g_trace[blockIdx.x * 64 + (slot)] = __builtin_amdgcn_s_memrealtime(); \
+    } while (0)
+// per wave (after this wave's outstanding memory operations)
+#define TRACEW(slot)                                                                                        \
+    do {                                                                                                    \
+        __builtin_amdgcn_s_waitcnt(0);                                                                      \
+        if (g_trace && (threadIdx.x & 63) == 0)                                                             \
+            g_trace[blockIdx.x * 64 + 16 + (threadIdx.x >> 6) * 6 + (slot)] = __builtin_amdgcn_s_memrealtime(); \
     } while (0)
 #else
 #define TRACE(slot) \
     do {            \
+    } while (0)
+#define TRACEW(slot) \
+    do {             \
     } while (0)
 #endif
 
@@ -121,123 +131,209 @@ __device__ void route_row(const float *row, int E, int k, int *out_idx, float *o
 }
 
 // ---------------------------------------------------------------------------
-// Chunk streaming: 16 consecutive rows x CB blocks of one matrix.
+// Chunk streaming: 16 consecutive rows x cb blocks of one matrix, read with
+// 16-byte loads (consecutive lanes on consecutive bytes of a row) and staged
+// in a wave-private LDS buffer whose rows are decode_chunk_rstride() apart.
 // ---------------------------------------------------------------------------
 struct Chunk {
     u32x4 r[DEC_MAX_LD];
 };
 
-__device__ __forceinline__ void chunk_load(Chunk &c, const uint8_t *rows, int row_bytes, int seg_off, int seg,
-                                           int lane) {
-    const int per_row = seg >> 4;  // 16-byte pieces per row segment
+// Per-lane byte offsets of a chunk's pieces: in global memory (from the first
+// row's segment start) and in the LDS buffer (-1: no piece for this lane).
+struct ChunkMap {
+    int g[DEC_MAX_LD];
+    int l[DEC_MAX_LD];
+};
+
+__device__ __forceinline__ void chunk_map(ChunkMap &m, int seg, int row_bytes, int lane) {
+    const int per_row = seg >> 4;  // 16-byte pieces per row segment (<= 36)
+    const int rs = decode_chunk_rstride(seg);
+    const uint32_t inv = 65536u / (uint32_t)per_row + 1u;  // j / per_row exactly for j < 1024, per_row <= 42
 #pragma unroll
     for (int u = 0; u < DEC_MAX_LD; ++u) {
         const int j = lane + 64 * u;
-        if (j < 16 * per_row) {
-            const int r = j / per_row, col = j - r * per_row;
-            c.r[u] = *(const u32x4 *)(rows + (size_t)r * row_bytes + seg_off + col * 16);
-        }
+        const int r = (int)(((uint32_t)j * inv) >> 16);
+        const int col = j - r * per_row;
+        m.g[u] = r * row_bytes + col * 16;
+        m.l[u] = j < 16 * per_row ? r * rs + col * 16 : -1;
     }
 }
 
-__device__ __forceinline__ void chunk_store_lds(const Chunk &c, uint8_t *buf, int seg, int lane) {
+__device__ __forceinline__ void chunk_load(Chunk &c, const uint8_t *base, const ChunkMap &m) {
 #pragma unroll
-    for (int u = 0; u < DEC_MAX_LD; ++u) {
-        const int j = lane + 64 * u;
-        if (j < seg) *(u32x4 *)(buf + j * 16) = c.r[u];  // 16 rows * seg bytes = seg pieces
-    }
+    for (int u = 0; u < DEC_MAX_LD; ++u)
+        if (m.l[u] >= 0) c.r[u] = *(const u32x4 *)(base + m.g[u]);
+}
+
+__device__ __forceinline__ void chunk_store(const Chunk &c, uint8_t *buf, const ChunkMap &m) {
+#pragma unroll
+    for (int u = 0; u < DEC_MAX_LD; ++u)
+        if (m.l[u] >= 0) *(u32x4 *)(buf + m.l[u]) = c.r[u];
 }
 
 __device__ __forceinline__ uint32_t lds_u32(const uint8_t *p) { return *(const uint32_t *)p; }
-__device__ __forceinline__ uint32_t lds_u16(const uint8_t *p) { return *(const uint16_t *)p; }
 
-// One block of the chunk in LDS as this lane's MFMA B operand(s) and scale.
-// Lane layout: weight row n = lane % 16 of the chunk, k-group g = lane / 16.
-// buf is 4-byte aligned; offsets stay integers so the accesses stay LDS reads.
+// ---------------------------------------------------------------------------
+// MFMA operands from a staged chunk, two blocks (36 or 28 bytes, 4-byte
+// aligned) at a time.  Lane layout: weight row n = lane % 16 of the chunk,
+// k-group g = lane / 16.  All reads are aligned dwords; with the odd-granule
+// row stride the 16 rows x 4 k-groups of one read fall in distinct banks.
+// ---------------------------------------------------------------------------
 template <int BITS>
-struct BOp;
-
+struct BVal;
 template <>
-struct BOp<4> {
+struct BVal<4> {
     half8 b;
     float d;
-    __device__ __forceinline__ void load(const uint8_t *buf, int seg, int blk, int n, int g) {
-        const int o = n * seg + blk * 18;
-        d = half_bits_to_float(lds_u16(buf + o));
-        const int qa = o + 2 + 4 * g, al = qa & ~3;
-        const uint32_t w0 = lds_u32(buf + al), w1 = lds_u32(buf + al + 4);
-        b = unpack4(__builtin_amdgcn_alignbyte(w1, w0, (uint32_t)(qa & 3)));
+};
+template <>
+struct BVal<3> {
+    half8 lo, hb;
+    float d;
+};
+
+// A operands of blocks b, b+1.  Rows past the window's tokens read a valid
+// row too: an MFMA output row depends on its own A row only, and those rows
+// are never used.
+template <int NP>
+__device__ __forceinline__ void load_a(half8 (&a)[2][NP], const uint8_t *ab, int b, int a_stride, int part_off) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int xp = 0; xp < NP; ++xp) a[i][xp] = *(const half8 *)(ab + (b + i) * a_stride + xp * part_off);
+}
+
+template <int BITS, int NP>
+struct Pair;
+
+// 4-bit pair: block b = bytes 0..17 (scale 0-1, codes 2..17), block b+1 = 18..35.
+template <int NP>
+struct Pair<4, NP> {
+    uint32_t d0, d4, w0, w1, w5;
+    half8 a[2][NP];
+    __device__ __forceinline__ void load(const uint8_t *buf, int ro, int p, int g, const uint8_t *ab, int a_stride,
+                                         int part_off) {
+        const int o = ro + 36 * p;
+        d0 = lds_u32(buf + o);
+        d4 = lds_u32(buf + o + 16);
+        w0 = lds_u32(buf + o + 4 * g);
+        w1 = lds_u32(buf + o + 4 * g + 4);
+        w5 = lds_u32(buf + o + 20 + 4 * g);
+        load_a<NP>(a, ab, 2 * p, a_stride, part_off);
+    }
+    __device__ __forceinline__ BVal<4> get(int i, int g) const {
+        BVal<4> v;
+        if (i == 0) {
+            v.b = unpack4(__builtin_amdgcn_alignbyte(w1, w0, 2u));  // code bytes 2+4g .. 5+4g
+            v.d = half_bits_to_float(d0);
+        } else {
+            v.b = unpack4(w5);  // code bytes 20+4g .. 23+4g
+            v.d = half_bits_to_float(d4 >> 16);
+        }
+        return v;
     }
 };
 
-template <>
-struct BOp<3> {
-    half8 lo, hb;
-    float d;
-    __device__ __forceinline__ void load(const uint8_t *buf, int seg, int blk, int n, int g) {
-        const int o = n * seg + blk * 14;
-        d = half_bits_to_float(lds_u16(buf + o));
-        // low-part bytes ql[2g], ql[2g+1], each replicated into bytes 0 and 2
-        const int qa = o + 2 + 2 * g;
-        const uint32_t qw = lds_u32(buf + (qa & ~3));
-        const uint32_t sh = (uint32_t)(qa & 3);
+// 3-bit pair: block b = bytes 0..13 (scale 0-1, low parts 2..9, third bits
+// 10..13), block b+1 = 14..27.
+template <int NP>
+struct Pair<3, NP> {
+    uint32_t d0, d2, d3, d6, qb, qb1;
+    half8 a[2][NP];
+    __device__ __forceinline__ void load(const uint8_t *buf, int ro, int p, int g, const uint8_t *ab, int a_stride,
+                                         int part_off) {
+        const int o = ro + 28 * p;
+        d0 = lds_u32(buf + o);
+        d3 = lds_u32(buf + o + 12);
+        d2 = lds_u32(buf + o + 8);
+        d6 = lds_u32(buf + o + 24);
+        qb = lds_u32(buf + o + 4 * ((g + 1) >> 1));  // holds low-part bytes 2+2g, 3+2g
+        qb1 = lds_u32(buf + o + 16 + 4 * (g >> 1));  // holds low-part bytes 16+2g, 17+2g
+        load_a<NP>(a, ab, 2 * p, a_stride, part_off);
+    }
+    __device__ __forceinline__ BVal<3> get(int i, int g) const {
+        BVal<3> v;
+        uint32_t qw, qh, sh;
+        if (i == 0) {
+            qw = qb;
+            sh = (g & 1) ? 0u : 2u;
+            qh = __builtin_amdgcn_alignbyte(d3, d2, 2u);  // bytes 10..13
+            v.d = half_bits_to_float(d0);
+        } else {
+            qw = qb1;
+            sh = (g & 1) ? 2u : 0u;
+            qh = d6;  // bytes 24..27
+            v.d = half_bits_to_float(d3 >> 16);
+        }
+        // low-part bytes 2g and 2g+1 of the block, each replicated into bytes 0 and 2
         const uint32_t sel0 = 0x0C000C00u | (sh << 16) | sh;
         const uint32_t p0 = __builtin_amdgcn_perm(qw, qw, sel0);
         const uint32_t p1 = __builtin_amdgcn_perm(qw, qw, sel0 + 0x00010001u);
-        // third-bit word at bytes 10..13
-        const int ha = o + 10, hal = ha & ~3;
-        const uint32_t qh = __builtin_amdgcn_alignbyte(lds_u32(buf + hal + 4), lds_u32(buf + hal), (uint32_t)(ha & 3));
-        unpack3(p0, p1, qh >> (2 * g), lo, hb);
+        unpack3(p0, p1, qh >> (2 * g), v.lo, v.hb);
+        return v;
     }
 };
 
-// acc += d * (A . B) for one block; A given as NP fp16 parts.
+// d * (A . B) of one block, before scaling; A given as NP fp16 parts.
 template <int BITS, int NP>
-__device__ __forceinline__ void block_mma(float4v &acc, const BOp<BITS> &op, const half8 *a) {
+__device__ __forceinline__ float4v block_dot(const BVal<BITS> &v, const half8 *a) {
     const float4v z = {0.f, 0.f, 0.f, 0.f};
     float4v dd;
     if constexpr (BITS == 4) {
-        dd = mfma16(a[0], op.b, z);
-        if constexpr (NP == 2) dd = mfma16(a[1], op.b, dd);
+        dd = mfma16(a[0], v.b, z);
+        if constexpr (NP == 2) dd = mfma16(a[1], v.b, dd);
     } else {
-        dd = mfma16(a[0], op.lo, z);
-        dd = mfma16(a[0], op.hb, dd);
+        dd = mfma16(a[0], v.lo, z);
+        dd = mfma16(a[0], v.hb, dd);
         if constexpr (NP == 2) {
-            dd = mfma16(a[1], op.lo, dd);
-            dd = mfma16(a[1], op.hb, dd);
+            dd = mfma16(a[1], v.lo, dd);
+            dd = mfma16(a[1], v.hb, dd);
         }
     }
-    acc.x = fmaf(op.d, dd.x, acc.x);
-    acc.y = fmaf(op.d, dd.y, acc.y);
-    acc.z = fmaf(op.d, dd.z, acc.z);
-    acc.w = fmaf(op.d, dd.w, acc.w);
+    return dd;
 }
 
-__host__ __device__ __forceinline__ int chunk_blocks(int nkb) {
-    // largest of 32, 24, 16, 8 dividing nkb (nkb is a multiple of 8)
-    return (nkb % 32 == 0) ? 32 : (nkb % 24 == 0) ? 24 : (nkb % 16 == 0) ? 16 : 8;
-}
-
-// Multiply-accumulate a whole chunk in LDS (cb blocks, a multiple of 4) into
-// acc.  A operands: a_base points at this lane's first block, a_stride bytes
-// between blocks, part_off bytes between the NP parts.
+// acc += d0 * dot(block 0) then d1 * dot(block 1): both blocks' MFMAs issue
+// before either result is scaled.
 template <int BITS, int NP>
-__device__ __forceinline__ void chunk_mma(float4v &acc, const uint8_t *buf, int seg, int cb, int n, int g,
-                                          const uint8_t *a_base, int a_stride, int part_off, bool a_valid) {
-    for (int b0 = 0; b0 < cb; b0 += 4) {
-#pragma unroll
-        for (int bi = 0; bi < 4; ++bi) {
-            const int b = b0 + bi;
-            half8 a[NP];
-#pragma unroll
-            for (int xp = 0; xp < NP; ++xp)
-                a[xp] = a_valid ? *(const half8 *)(a_base + (size_t)b * a_stride + xp * part_off)
-                                : half8{0, 0, 0, 0, 0, 0, 0, 0};
-            BOp<BITS> op;
-            op.load(buf, seg, b, n, g);
-            block_mma<BITS, NP>(acc, op, a);
-        }
+__device__ __forceinline__ void pair_mma(float4v &acc, const Pair<BITS, NP> &pr, int g) {
+    const BVal<BITS> v0 = pr.get(0, g), v1 = pr.get(1, g);
+    const float4v d0 = block_dot<BITS, NP>(v0, pr.a[0]);
+    const float4v d1 = block_dot<BITS, NP>(v1, pr.a[1]);
+    acc.x = fmaf(v0.d, d0.x, acc.x);
+    acc.y = fmaf(v0.d, d0.y, acc.y);
+    acc.z = fmaf(v0.d, d0.z, acc.z);
+    acc.w = fmaf(v0.d, d0.w, acc.w);
+    acc.x = fmaf(v1.d, d1.x, acc.x);
+    acc.y = fmaf(v1.d, d1.y, acc.y);
+    acc.z = fmaf(v1.d, d1.z, acc.z);
+    acc.w = fmaf(v1.d, d1.w, acc.w);
+}
+
+// Multiply-accumulate a staged chunk of cb blocks (cb a multiple of 4) into
+// acc: two operand sets, the reads of one pair in flight while the other
+// pair computes.  A operands: ab points at this lane's first block, a_stride
+// bytes between blocks, part_off bytes between the NP parts.
+template <int BITS, int NP>
+__device__ __forceinline__ void chunk_mma(float4v &acc, const uint8_t *buf, int rs, int cb, int n, int g,
+                                          const uint8_t *ab, int a_stride, int part_off) {
+    const int ro = n * rs;
+    const int np = cb >> 1;
+    Pair<BITS, NP> pa, pb;
+    pa.load(buf, ro, 0, g, ab, a_stride, part_off);
+    for (int p = 0; p < np; p += 2) {
+        pb.load(buf, ro, p + 1, g, ab, a_stride, part_off);
+        pair_mma<BITS, NP>(acc, pa, g);
+        pa.load(buf, ro, p + 2 < np ? p + 2 : 0, g, ab, a_stride, part_off);  // (last round: unused re-read)
+        pair_mma<BITS, NP>(acc, pb, g);
     }
+}
+
+__device__ __forceinline__ void wave_lds_handoff() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // ---------------------------------------------------------------------------
@@ -267,9 +363,55 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
     uint8_t *s_xa = smem + P.lds_xa;
     uint8_t *s_chunk = smem + P.lds_chunk + wave * P.chunk_stride;
 
-    TRACE(0);
-    // ======================= Phase A: activations, routing, grouping =======================
+    // ---- gate/up geometry: a unit is 16 feature rows x one K chunk of one
+    // matrix (one wave); a task is the 8 (or 16) units that complete whole
+    // 16-feature groups (one workgroup)
+    constexpr int bb = BITS == 4 ? 18 : 14;
     const int nkbH = H >> 5;
+    const int cbH = P.cbH, nchH = nkbH / cbH, segH = cbH * bb;
+    const int rowH = nkbH * bb;
+    const int rsH = decode_chunk_rstride(segH);
+    const int F = P.F, Fs = has_shared ? P.Fs : 0;
+    const size_t eb = (size_t)3 * F * rowH;  // routed expert blob bytes
+    const int upt = 2 * nchH;                 // units per 16-feature group: (gate, up) x K chunks
+    const int nfgT = upt >= 8 ? 1 : 8 / upt;  // 16-feature groups per task
+    const int rounds = upt > 8 ? upt / 8 : 1;
+    const int tasks_sh = Fs / (16 * nfgT), tasks_rt = F / (16 * nfgT);
+    const int n_lane = lane & 15, g_lane = lane >> 4;
+
+    ChunkMap mapH;
+    chunk_map(mapH, segH, rowH, lane);
+    // this wave's chunk of unit (task, round)
+    auto unit_rows = [&](int task, int rho) -> const uint8_t * {
+        int Fx, tl;
+        const uint8_t *blob;
+        if (task < tasks_sh) {
+            tl = task;
+            Fx = Fs;
+            blob = P.w_shared;
+        } else {
+            const int v = task - tasks_sh, si = v / tasks_rt;
+            tl = v - si * tasks_rt;
+            Fx = F;
+            blob = P.w_routed + (size_t)s_slot_exp[hs + si] * eb;
+        }
+        const int ui = rho * 8 + wave;
+        const int fl = ui / upt, rem = ui - fl * upt;
+        const int mat = rem / nchH, kc = rem - mat * nchH;
+        return blob + (size_t)mat * Fx * rowH + (size_t)(tl * nfgT + fl) * 16 * rowH + (size_t)kc * segH;
+    };
+
+    TRACE(0);
+    // A first unit of the shared expert depends on no routing: it starts streaming now.
+    Chunk c;
+    bool pref = false;
+    if ((int)blockIdx.x < tasks_sh) {
+        TRACEW(0);
+        chunk_load(c, unit_rows(blockIdx.x, 0), mapH);
+        pref = true;
+    }
+
+    // ======================= Phase A: activations, routing, grouping =======================
     for (int i = tid; i < T; i += DEC_THREADS) s_xmax[i] = 0u;
     if (P.mode & DEC_MODE_ROUTE)
         for (int e = tid; e <= E; e += DEC_THREADS) s_hist[e] = 0;
@@ -310,12 +452,12 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             for (int v = 0; v < NV; ++v) {
                 const uint32_t w4[4] = {xr[q][v].x, xr[q][v].y, xr[q][v].z, xr[q][v].w};
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
+                for (int c2 = 0; c2 < 4; ++c2) {
                     if (XPARTS == 1) {
-                        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w4[c] << 16)));
-                        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w4[c] & 0xFFFF0000u)));
+                        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w4[c2] << 16)));
+                        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w4[c2] & 0xFFFF0000u)));
                     } else {
-                        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w4[c])));
+                        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w4[c2])));
                     }
                 }
             }
@@ -337,8 +479,8 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             for (int i = 0; i < per; ++i) {
                 const int e = base + i;
                 if (e < E) {
-                    const int c = s_hist[e];
-                    sum += c | ((c > 0) << 16);
+                    const int cnt = s_hist[e];
+                    sum += cnt | ((cnt > 0) << 16);
                 }
             }
             int incl = sum;
@@ -351,15 +493,15 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             for (int i = 0; i < per; ++i) {
                 const int e = base + i;
                 if (e < E) {
-                    const int c = s_hist[e];
+                    const int cnt = s_hist[e];
                     const int off = run & 0xFFFF, act = run >> 16;
-                    if (c > 0) {
+                    if (cnt > 0) {
                         s_slot_exp[hs + act] = e;
                         s_slot_start[hs + act] = off;
-                        s_slot_cnt[hs + act] = c;
+                        s_slot_cnt[hs + act] = cnt;
                     }
                     s_hist[e] = off;  // becomes the expert's first position
-                    run += c | ((c > 0) << 16);
+                    run += cnt | ((cnt > 0) << 16);
                 }
             }
             if (lane == 63) s_misc[0] = hs + (incl >> 16);  // number of slots
@@ -393,20 +535,20 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         const int na = s_misc[0] - hs;
         for (int a = tid; a < na; a += DEC_THREADS) {
             int e = P.g_active[1 + a];
-            int st = 0, c = 0;
+            int st = 0, cnt = 0;
             if (e >= 0 && e < E) {
                 st = P.g_offsets[e];
-                c = P.g_offsets[e + 1] - st;
+                cnt = P.g_offsets[e + 1] - st;
             }
-            if (e < 0 || e >= E || st < 0 || c < 0 || c > MOE_DECODE_ROWS_DEV || st + c > TK) {
+            if (e < 0 || e >= E || st < 0 || cnt < 0 || cnt > MOE_DECODE_ROWS_DEV || st + cnt > TK) {
                 atomicOr(P.err, 2u);
                 e = (e >= 0 && e < E) ? e : 0;
                 st = 0;
-                c = 0;
+                cnt = 0;
             }
             s_slot_exp[hs + a] = e;
             s_slot_start[hs + a] = st;
-            s_slot_cnt[hs + a] = c;
+            s_slot_cnt[hs + a] = cnt;
         }
         for (int q = tid; q < TK; q += DEC_THREADS) {
             int p = P.g_pairs[q];
@@ -423,7 +565,16 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         s_slot_start[0] = 0;
         s_slot_cnt[0] = T;
     }
-    // activations to fp16 (hi [+ lo]) of x * 2^sc_t in the format's k order
+    __syncthreads();  // slot tables complete
+    const int n_slots = s_misc[0];
+    const int n_tasks = tasks_sh + (n_slots - hs) * tasks_rt;
+    if (!pref && (int)blockIdx.x < n_tasks) {
+        TRACEW(0);
+        chunk_load(c, unit_rows(blockIdx.x, 0), mapH);
+    }
+
+    // activations to fp16 (hi [+ lo]) of x * 2^sc_t in the format's k order:
+    // part p, token t, block b, k-group g at p*T*x_rs + t*x_rs + (4b+g)*16
 #pragma unroll
     for (int q = 0; q < QX; ++q) {
         const int j = tid + DEC_THREADS * q;
@@ -463,228 +614,202 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
                     hv[e2] = hb2[0] | ((uint32_t)hb2[1] << 16);
                     lv[e2] = lb2[0] | ((uint32_t)lb2[1] << 16);
                 }
-                *(u32x4 *)(s_xa + (((size_t)t * nkbH + b) * 4 + g) * 16) = u32x4{hv[0], hv[1], hv[2], hv[3]};
-                if (XPARTS == 2)
-                    *(u32x4 *)(s_xa + (((size_t)(T + t) * nkbH + b) * 4 + g) * 16) = u32x4{lv[0], lv[1], lv[2], lv[3]};
+                uint8_t *dst = s_xa + (size_t)t * P.x_rs + (size_t)(4 * b + g) * 16;
+                *(u32x4 *)dst = u32x4{hv[0], hv[1], hv[2], hv[3]};
+                if (XPARTS == 2) *(u32x4 *)(dst + (size_t)T * P.x_rs) = u32x4{lv[0], lv[1], lv[2], lv[3]};
             }
         }
     }
     __syncthreads();
     TRACE(2);
 
-    const int n_slots = s_misc[0];
-    const int bb = block_bytes(BITS);
-    const int F = P.F, Fs = has_shared ? P.Fs : 0;
-    const int cbH = chunk_blocks(nkbH), nchH = nkbH / cbH, segH = cbH * bb;
-    const size_t rowH = (size_t)nkbH * bb;
-    const size_t eb = (size_t)3 * F * rowH;  // routed expert blob bytes
-    const int units_sh = (Fs >> 4) * 2 * nchH, units_rt = (F >> 4) * 2 * nchH;
-    const int n_units = units_sh + (n_slots - hs) * units_rt;
-    const int n_lane = lane & 15, g_lane = lane >> 4;
-    const int fstride = P.part_stride / (2 * nchH);  // Fmax
-
-    // ======================= Phase B: gate/up units =======================
-    {
-        struct Unit {
-            const uint8_t *rows;
-            int s, fg, mat, kc;
-        };
-        auto unit_of = [&](int u) {
-            Unit U;
-            int Fx, r;
-            const uint8_t *blob;
-            if (u < units_sh) {
-                U.s = 0;
-                r = u;
-                Fx = Fs;
-                blob = P.w_shared;
-            } else {
-                const int v = u - units_sh;
-                U.s = hs + v / units_rt;
-                r = v - (U.s - hs) * units_rt;
-                Fx = F;
-                blob = P.w_routed + (size_t)s_slot_exp[U.s] * eb;
-            }
-            U.fg = r / (2 * nchH);
-            const int rem = r - U.fg * 2 * nchH;
-            U.mat = rem / nchH;
-            U.kc = rem - U.mat * nchH;
-            U.rows = blob + (size_t)U.mat * Fx * rowH + (size_t)U.fg * 16 * rowH;
-            return U;
-        };
-        // unit order: wave 0 of every workgroup first, then wave 1, ...
-        int u = wave * G + blockIdx.x;
-        const int ustep = G * DEC_WAVES;
-        Chunk c;
-        if (u < n_units) {
-            const Unit U = unit_of(u);
-            chunk_load(c, U.rows, (int)rowH, U.kc * segH, segH, lane);
+    // ======================= Phase B: gate/up tasks =======================
+    bool first_task = true;
+    for (int task = blockIdx.x; task < n_tasks; task += G) {
+        int s, tl;
+        if (task < tasks_sh) {
+            s = 0;
+            tl = task;
+        } else {
+            const int v = task - tasks_sh, si = v / tasks_rt;
+            s = hs + si;
+            tl = v - si * tasks_rt;
         }
-        for (; u < n_units; u += ustep) {
-            const Unit U = unit_of(u);
+        const int n_tok = s_slot_cnt[s];
+        const bool shared_slot = s_slot_exp[s] < 0;
+        const int mrow = n_lane < n_tok ? n_lane : 0;  // A row of this lane (rows past n_tok: any valid row)
+        const int tok = shared_slot ? mrow : s_sorted[s_slot_start[s] + mrow] / k;
+        float4v accr[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        for (int rho = 0; rho < rounds; ++rho) {
+            const int ui = rho * 8 + wave;
+            const int kc = (ui % upt) % nchH;
+            if (first_task && rho == 0) TRACEW(1);
             __builtin_amdgcn_wave_barrier();
-            chunk_store_lds(c, s_chunk, segH, lane);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // the registers are free again: the next unit's chunk streams in
-            // while this one computes
-            const int un = u + ustep;
-            if (un < n_units) {
-                const Unit N = unit_of(un);
-                chunk_load(c, N.rows, (int)rowH, N.kc * segH, segH, lane);
+            chunk_store(c, s_chunk, mapH);
+            wave_lds_handoff();
+            // the registers are free again: the next unit's chunk streams in while this one computes
+            int nt = task, nr = rho + 1;
+            if (nr == rounds) {
+                nt += G;
+                nr = 0;
             }
-
-            const int n_tok = s_slot_cnt[U.s];
-            const bool shared_slot = s_slot_exp[U.s] < 0;
-            const bool a_valid = n_lane < n_tok;
-            int tok = 0;
-            if (a_valid) tok = shared_slot ? n_lane : s_sorted[s_slot_start[U.s] + n_lane] / k;
-            const uint8_t *a_base = s_xa + (((size_t)tok * nkbH + U.kc * cbH) * 4 + g_lane) * 16;
-            float4v acc = {0.f, 0.f, 0.f, 0.f};
-            chunk_mma<BITS, XPARTS>(acc, s_chunk, segH, cbH, n_lane, g_lane, a_base, 64, T * nkbH * 64, a_valid);
-
-            // publish the partial sums (back in the units of x), laid out in the
-            // down projection's k order so the consumer reads whole groups
-            const float av[4] = {acc.x, acc.y, acc.z, acc.w};
-            const int f = U.fg * 16 + n_lane;
+            if (nt < n_tasks) chunk_load(c, unit_rows(nt, nr), mapH);
+            const uint8_t *ab = s_xa + (size_t)tok * P.x_rs + (size_t)(kc * cbH) * 64 + g_lane * 16;
+            chunk_mma<BITS, XPARTS>(accr[rho], s_chunk, rsH, cbH, n_lane, g_lane, ab, 64, T * P.x_rs);
+        }
+        if (first_task) TRACEW(2);
+        // unit partials (token m, feature n) into this wave's LDS buffer: round rho at [rho][m][n]
+        float *sp = (float *)s_chunk;
+#pragma unroll
+        for (int rho = 0; rho < 2; ++rho) {
+            if (rho < rounds) {
+                sp[rho * 256 + (4 * g_lane + 0) * 16 + n_lane] = accr[rho].x;
+                sp[rho * 256 + (4 * g_lane + 1) * 16 + n_lane] = accr[rho].y;
+                sp[rho * 256 + (4 * g_lane + 2) * 16 + n_lane] = accr[rho].z;
+                sp[rho * 256 + (4 * g_lane + 3) * 16 + n_lane] = accr[rho].w;
+            }
+        }
+        __syncthreads();
+        // h = silu(g) * u per (feature group, token, feature): K chunks summed in
+        // order 0, 1, ...; back in the units of x; stored in the down
+        // projection's k order
+        const int per_fl = n_tok * 16;
+        for (int i = tid; i < nfgT * per_fl; i += DEC_THREADS) {
+            const int fl = i / per_fl, rem = i - fl * per_fl;
+            const int m = rem >> 4, n = rem & 15;
+            float gs = 0.0f, us = 0.0f;
+            for (int kc = 0; kc < nchH; ++kc) {
+                const int ug = fl * upt + kc, uu = ug + nchH;
+                gs += *(const float *)(smem + P.lds_chunk + (ug & 7) * P.chunk_stride + ((ug >> 3) * 256 + m * 16 + n) * 4);
+                us += *(const float *)(smem + P.lds_chunk + (uu & 7) * P.chunk_stride + ((uu >> 3) * 256 + m * 16 + n) * 4);
+            }
+            const int tk = shared_slot ? m : s_sorted[s_slot_start[s] + m] / k;
+            const float ti = s_tinv[tk];
+            const float gv = gs * ti, uv = us * ti;
+            const float h = gv / (1.0f + expf(-gv)) * uv;
+            const int f = (tl * nfgT + fl) * 16 + n;
             int pg, pe;
             group_slot_of(BITS, f & 31, pg, pe);
             const int fo = (f >> 5) * 32 + pg * 8 + pe;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = 4 * g_lane + r;
-                if (m < n_tok) {
-                    const int tk = shared_slot ? m : s_sorted[s_slot_start[U.s] + m] / k;
-                    const int row = shared_slot ? TK + m : s_slot_start[U.s] + m;
-                    st_dev(P.gu_part + (size_t)row * P.part_stride + (size_t)(U.mat * nchH + U.kc) * fstride + fo,
-                           av[r] * s_tinv[tk]);
-                }
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            wait_all_mem();  // this wave's partial stores are complete before the count goes up
-            __builtin_amdgcn_wave_barrier();
-            if (lane == 0) add_dev(&P.gu_count[U.s], 1u);
+            const int row = shared_slot ? TK + m : s_slot_start[s] + m;
+            st_dev(P.hbuf + (size_t)row * P.h_stride + fo, h);
         }
+        wait_all_mem();   // this thread's h stores are complete ...
+        __syncthreads();  // ... for every thread, before the task is counted
+        if (tid == 0) add_dev(&P.gu_count[s * DEC_CSTRIDE], 1u);
+        if (first_task) TRACEW(3);
+        first_task = false;
     }
     TRACE(3);
 
     // ======================= Phase C: down + weighted write + combine =======================
+    // Down tiles (slot, 128 output rows) continue the round robin of the
+    // gate/up tasks over the workgroups: tile i is work item n_tasks + i.
     const int tiles_per_slot = H / DEC_DN_ROWS;
     const int n_tiles = n_slots * tiles_per_slot;
-    const int t0 = (int)(((long long)blockIdx.x * n_tiles) / G);
-    const int t1 = (int)(((long long)(blockIdx.x + 1) * n_tiles) / G);
-    int cur_slot = -1;
-    for (int ti = t0; ti < t1; ++ti) {
+    const int first_tile = (int)(((long long)blockIdx.x - n_tasks % G + G) % G);
+    int cur_slot = -1, map_fx = -1;
+    ChunkMap mapF;
+    for (int ti = first_tile; ti < n_tiles; ti += G) {
         const int s = ti / tiles_per_slot, rg = ti - s * tiles_per_slot;
         const bool shared_slot = (s_slot_exp[s] < 0);
         const int Fx = shared_slot ? Fs : F;
         const uint8_t *blob = shared_slot ? P.w_shared : P.w_routed + (size_t)s_slot_exp[s] * eb;
         const int nkbF = Fx >> 5;
-        const int cbF = chunk_blocks(nkbF), nchF = nkbF / cbF, segF = cbF * bb;
-        const size_t rowF = (size_t)nkbF * bb;
+        const int cbF = decode_f_chunk_blocks(nkbF), nchF = nkbF / cbF, segF = cbF * bb;
+        const int rowF = nkbF * bb;
+        const int rsF = decode_chunk_rstride(segF);
+        if (Fx != map_fx) {
+            chunk_map(mapF, segF, rowF, lane);
+            map_fx = Fx;
+        }
         const uint8_t *rows_d = blob + (size_t)2 * Fx * rowH + (size_t)(rg * DEC_DN_ROWS + wave * 16) * rowF;
         const int n_tok = s_slot_cnt[s];
 
-        Chunk c;
-        chunk_load(c, rows_d, (int)rowF, 0, segF, lane);  // prefetch before the wait
+        Chunk cd;
+        chunk_load(cd, rows_d, mapF);  // prefetch before the wait
 
         if (s != cur_slot) {
-            __syncthreads();  // previous tile's readers of s_xa are done
-            if (ti == t0) TRACE(4);
+            if (tid < T) s_xmax[tid] = 0u;
+            __syncthreads();  // previous tile's readers of the staged h are done
+            if (ti == first_tile) TRACE(4);
             if (tid == 0) {
-                const uint32_t need = (uint32_t)((Fx >> 4) * 2 * nchH);
+                const uint32_t need = (uint32_t)(Fx / (16 * nfgT));
                 uint32_t spins = 0;
-                while (ld_dev_u32(&P.gu_count[s]) < need) {
-                    __builtin_amdgcn_s_sleep(1);
+                while (ld_dev_u32(&P.gu_count[s * DEC_CSTRIDE]) < need) {
+                    __builtin_amdgcn_s_sleep(2);
                     if (++spins > DEC_SPIN_LIMIT || (ld_dev_u32(P.err) & 1u)) {
                         atomicOr(P.err, 1u);
                         break;
                     }
                 }
             }
-            if (ti == t0) TRACE(5);
             __syncthreads();
-            // h = silu(g) * u from the fixed-order sum of the partials; staged in
-            // LDS as fp16 hi + lo of h * 2^sc_t (per-token power of two)
+            if (ti == first_tile) TRACE(5);
+            // stage h * 2^sc_m (per-row power of two) as fp16 hi + lo: row m at
+            // m*h_rs, k-group gi (8 values) at gi*32 (hi 16 B, lo 16 B)
             const int row0 = shared_slot ? TK : s_slot_start[s];
-            const int ngrp = Fx >> 3;  // groups of 8 values (one k-group of one block)
-            for (int r = wave; r < n_tok; r += DEC_WAVES) {
-                const float *pr = P.gu_part + (size_t)(row0 + r) * P.part_stride;
-                float hv[2][8];
-                float mx = 0.0f;
+            const int ngrp = Fx >> 3;
+            const int nit = n_tok * ngrp;
+            float hv[4][8];
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int gi = lane + 64 * q;
-                    if (gi < ngrp) {
-                        float gs[8], us[8];
-                        const float *pg0 = pr + gi * 8;
-                        const float *pu0 = pr + (size_t)nchH * fstride + gi * 8;
+            for (int q = 0; q < 4; ++q) {
+                const int it = tid + DEC_THREADS * q;
+                if (it < nit) {
+                    const int m = it / ngrp, gi = it - m * ngrp;
+                    const float *src = P.hbuf + (size_t)(row0 + m) * P.h_stride + gi * 8;
+                    float mx = 0.0f;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            gs[e] = ld_dev(pg0 + e);
-                            us[e] = ld_dev(pu0 + e);
-                        }
-                        for (int kc = 1; kc < nchH; ++kc) {  // fixed order: chunk 0, 1, ...
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                gs[e] += ld_dev(pg0 + (size_t)kc * fstride + e);
-                                us[e] += ld_dev(pu0 + (size_t)kc * fstride + e);
-                            }
-                        }
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const float h = gs[e] / (1.0f + expf(-gs[e])) * us[e];
-                            hv[q][e] = h;
-                            mx = fmaxf(mx, fabsf(h));
-                        }
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        const uint64_t two = ld_dev_u64(src + 2 * e2);
+                        hv[q][2 * e2] = __builtin_bit_cast(float, (uint32_t)two);
+                        hv[q][2 * e2 + 1] = __builtin_bit_cast(float, (uint32_t)(two >> 32));
+                        mx = fmaxf(mx, fmaxf(fabsf(hv[q][2 * e2]), fabsf(hv[q][2 * e2 + 1])));
                     }
-                }
-                mx = __builtin_bit_cast(float, wave_max_u32(__builtin_bit_cast(uint32_t, mx)));
-                int ex = 0;
-                if (mx > 0.0f) frexpf(mx, &ex);
-                const int sc = mx > 0.0f ? 14 - ex : 0;
-                const float scale = __builtin_bit_cast(float, (uint32_t)(127 + sc) << 23);
-                if (lane == 0) s_hinv[r] = __builtin_bit_cast(float, (uint32_t)(127 - sc) << 23);
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const int gi = lane + 64 * q;
-                    if (gi < ngrp) {
-                        uint32_t h4[4], l4[4];
-#pragma unroll
-                        for (int e2 = 0; e2 < 4; ++e2) {
-                            const float v0 = hv[q][2 * e2] * scale, v1 = hv[q][2 * e2 + 1] * scale;
-                            const _Float16 a0 = (_Float16)v0, a1 = (_Float16)v1;
-                            h4[e2] = __builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
-                            l4[e2] = f2h_bits(v0 - (float)a0) | ((uint32_t)f2h_bits(v1 - (float)a1) << 16);
-                        }
-                        uint8_t *dst = s_xa + (size_t)r * (Fx * 4) + (size_t)gi * 32;
-                        *(u32x4 *)dst = u32x4{h4[0], h4[1], h4[2], h4[3]};
-                        *(u32x4 *)(dst + 16) = u32x4{l4[0], l4[1], l4[2], l4[3]};
-                    }
+                    atomicMax(&s_xmax[m], __builtin_bit_cast(uint32_t, mx));
                 }
             }
             __syncthreads();
-            if (ti == t0) TRACE(6);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int it = tid + DEC_THREADS * q;
+                if (it < nit) {
+                    const int m = it / ngrp, gi = it - m * ngrp;
+                    const float mx = __builtin_bit_cast(float, s_xmax[m]);
+                    int ex = 0;
+                    if (mx > 0.0f) frexpf(mx, &ex);
+                    const int sc = mx > 0.0f ? 14 - ex : 0;
+                    const float scale = __builtin_bit_cast(float, (uint32_t)(127 + sc) << 23);
+                    if (gi == 0) s_hinv[m] = __builtin_bit_cast(float, (uint32_t)(127 - sc) << 23);
+                    uint32_t h4[4], l4[4];
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        const float v0 = hv[q][2 * e2] * scale, v1 = hv[q][2 * e2 + 1] * scale;
+                        const _Float16 a0 = (_Float16)v0, a1 = (_Float16)v1;
+                        h4[e2] = __builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
+                        l4[e2] = f2h_bits(v0 - (float)a0) | ((uint32_t)f2h_bits(v1 - (float)a1) << 16);
+                    }
+                    uint8_t *dst = s_xa + (size_t)m * P.h_rs + (size_t)gi * 32;
+                    *(u32x4 *)dst = u32x4{h4[0], h4[1], h4[2], h4[3]};
+                    *(u32x4 *)(dst + 16) = u32x4{l4[0], l4[1], l4[2], l4[3]};
+                }
+            }
+            __syncthreads();
+            if (ti == first_tile) TRACE(6);
             cur_slot = s;
         }
 
         float4v acc = {0.f, 0.f, 0.f, 0.f};
-        const bool a_valid = n_lane < n_tok;
-        const uint8_t *a_base = s_xa + (size_t)n_lane * (Fx * 4) + g_lane * 32;
+        const uint8_t *ab = s_xa + (size_t)(n_lane < n_tok ? n_lane : 0) * P.h_rs + g_lane * 32;
         for (int ci = 0; ci < nchF; ++ci) {
             __builtin_amdgcn_wave_barrier();
-            chunk_store_lds(c, s_chunk, segF, lane);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (ci + 1 < nchF) chunk_load(c, rows_d, (int)rowF, (ci + 1) * segF, segF, lane);
-            chunk_mma<BITS, 2>(acc, s_chunk, segF, cbF, n_lane, g_lane, a_base + (size_t)ci * cbF * 128, 128, 16,
-                               a_valid);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
+            chunk_store(cd, s_chunk, mapF);
+            wave_lds_handoff();
+            if (ci + 1 < nchF) chunk_load(cd, rows_d + (size_t)(ci + 1) * segF, mapF);
+            chunk_mma<BITS, 2>(acc, s_chunk, rsF, cbF, n_lane, g_lane, ab + (size_t)ci * cbF * 128, 128, 16);
+            wave_lds_handoff();
         }
-        // o = acc * 2^-sc_t; weighted write per pair
+        // o = acc * 2^-sc_m; weighted write per pair
         {
             const int hrow = rg * DEC_DN_ROWS + wave * 16 + n_lane;
             const float ov[4] = {acc.x, acc.y, acc.z, acc.w};
@@ -702,24 +827,26 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
                 }
             }
         }
-        if (ti == t0) TRACE(7);
+        if (ti == first_tile) TRACE(7);
         wait_all_mem();   // every wave's output stores are complete ...
         __syncthreads();  // ... before the workgroup counts this tile
         if (tid == 0) {
             int do_combine = 0;
             if (P.mode & DEC_MODE_COMBINE) {
-                const uint32_t old = add_dev(&P.slice_count[rg], 1u);
+                const uint32_t old = add_dev(&P.slice_count[rg * DEC_CSTRIDE], 1u);
                 do_combine = (old == (uint32_t)(n_slots - 1));
             }
-            const uint32_t dn = add_dev(&P.dn_count[s], 1u);
+            const uint32_t dn = add_dev(&P.dn_count[s * DEC_CSTRIDE], 1u);
             if (dn == (uint32_t)(tiles_per_slot - 1)) {
-                store_dev_u32(&P.gu_count[s], 0u);
-                store_dev_u32(&P.dn_count[s], 0u);
+                // every tile of this slot has passed its wait: the counters can return to zero
+                store_dev_u32(&P.gu_count[s * DEC_CSTRIDE], 0u);
+                store_dev_u32(&P.dn_count[s * DEC_CSTRIDE], 0u);
             }
             s_misc[1] = do_combine;
         }
         __syncthreads();
         if (s_misc[1]) {
+            // the last slot of this 128-row slice: y = ((w0 o0 + w1 o1) + ...) + shared
             for (int i = tid; i < T * DEC_DN_ROWS; i += DEC_THREADS) {
                 const int t = i / DEC_DN_ROWS, hrow = rg * DEC_DN_ROWS + (i - t * DEC_DN_ROWS);
                 float acc2 = ld_dev(&P.out_pairs[((size_t)t * k) * H + hrow]);
@@ -728,7 +855,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
                 P.y[(size_t)t * H + hrow] = acc2;
             }
             __syncthreads();
-            if (tid == 0) store_dev_u32(&P.slice_count[rg], 0u);
+            if (tid == 0) store_dev_u32(&P.slice_count[rg * DEC_CSTRIDE], 0u);
         }
     }
     TRACE(8);
@@ -772,7 +899,6 @@ hipError_t decode_set_lds(int bits, int x_f32, int lds) {
     return x_f32 ? set_lds_t<3, 2>(lds) : set_lds_t<3, 1>(lds);
 }
 
-int decode_chunk_blocks(int nkb) { return chunk_blocks(nkb); }
 
 #ifdef MOE_PHASE_TRACE
 extern "C" int moe_trace_set(void *buf) {

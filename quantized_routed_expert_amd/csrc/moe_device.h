@@ -180,6 +180,10 @@ __device__ __forceinline__ void st_dev(float *p, float v) {
 __device__ __forceinline__ float ld_dev(const float *p) {
     return __builtin_bit_cast(float, __hip_atomic_load((const uint32_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
+// two floats, 8-byte aligned
+__device__ __forceinline__ uint64_t ld_dev_u64(const float *p) {
+    return __hip_atomic_load((const uint64_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ uint32_t ld_dev_u32(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

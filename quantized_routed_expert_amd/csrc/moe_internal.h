@@ -18,13 +18,42 @@ constexpr int DEC_MAX_E_FUSED = 1024;        // router fused into the kernel up 
 constexpr int DEC_MAX_F = 1024;              // expert FFN width handled by the fused decode launch
 constexpr int DEC_X_BLOCKS_PER_THREAD = 4;   // activation blocks staged per thread (bf16; 2 for fp32)
 constexpr uint32_t DEC_SPIN_LIMIT = 1u << 20;  // bounded waits: a wait that runs out sets err bit 0
+constexpr int DEC_CSTRIDE = 64;              // 32-bit words between counters (one 256-byte line each)
 #define MOE_MAX_EXPERTS_DEV 4096
 #define MOE_DECODE_ROWS_DEV 16
+constexpr int DEC_MAX_SLOTS = MOE_DECODE_ROWS_DEV * 32 + 1;  // T*k pairs (k <= 32) + the shared expert
+constexpr int DEC_MAX_SLICES = 65536 / DEC_DN_ROWS;
 
 // bits of DecodeParams::mode
 constexpr int DEC_MODE_ROUTE = 1;    // route + group from logits (else grouping is given)
 constexpr int DEC_MODE_COMBINE = 2;  // sum per-pair rows + shared into y
 constexpr int DEC_MODE_SHARED = 4;   // a shared expert is present
+
+// Quant blocks per streamed gate/up chunk for a row of nkb blocks: the K
+// chunks of a row number 1, 2, 4 or 8 (so the units of a 16-feature group
+// fill a workgroup's 8 waves exactly), each chunk an even number of blocks
+// (operands are read two blocks at a time) and at most DEC_CB_MAX.  0: no
+// such split (the fused decode launch does not take the shape).
+__host__ __device__ inline int decode_h_chunk_blocks(int nkb) {
+    for (int nch = 1; nch <= 8; nch <<= 1) {
+        if (nkb % nch) continue;
+        const int cb = nkb / nch;
+        if (cb <= DEC_CB_MAX && (cb & 1) == 0) return cb;
+    }
+    return 0;
+}
+
+// Quant blocks per streamed down chunk (F is a multiple of 256: nkb % 8 == 0).
+__host__ __device__ inline int decode_f_chunk_blocks(int nkb) {
+    return (nkb % 32 == 0) ? 32 : (nkb % 24 == 0) ? 24 : (nkb % 16 == 0) ? 16 : 8;
+}
+
+// LDS bytes between the 16 rows of a staged chunk: a whole number of 16-byte
+// granules, made odd so that the 16 rows start in 16 different bank groups.
+__host__ __device__ inline int decode_chunk_rstride(int seg_bytes) {
+    const int gr = (seg_bytes + 15) >> 4;
+    return 16 * (gr | 1);
+}
 
 struct DecodeParams {
     const void *x;             // [T][H] fp32 or bf16
@@ -40,15 +69,16 @@ struct DecodeParams {
     float *out_shared;         // [T][H]
     int32_t *topk_idx_out;     // may be null
     float *topk_w_out;         // may be null
-    float *gu_part;            // [(T*k + T)][2][nch][Fmax] fp32 partial gate/up sums per K chunk
-    uint32_t *gu_count;        // [max_slots]
-    uint32_t *dn_count;        // [max_slots]
-    uint32_t *slice_count;     // [H / DEC_DN_ROWS]
-    uint32_t *err;             // error word (bit 0: a wait hit its spin limit)
+    float *hbuf;               // [(T*k + T)][Fmax] fp32 SwiGLU outputs, in the down projection's k order
+    uint32_t *gu_count;        // [DEC_MAX_SLOTS * DEC_CSTRIDE]: finished gate/up tasks per slot
+    uint32_t *dn_count;        // [DEC_MAX_SLOTS * DEC_CSTRIDE]: finished down tiles per slot
+    uint32_t *slice_count;     // [DEC_MAX_SLICES * DEC_CSTRIDE]: finished slots per 128-row slice
+    uint32_t *err;             // error word (bit 0: a wait hit its spin limit; bit 1: bad given grouping)
     int T, E, k, H, F, Fs;     // Fs = shared ffn (0 = none)
     int bits, x_f32, mode, max_slots;
-    int part_stride;           // floats per gu_part row = 2 * nch * Fmax
-    int nch;                   // K chunks of the gate/up rows
+    int h_stride;              // floats per hbuf row (Fmax)
+    int cbH;                   // quant blocks per gate/up chunk
+    int x_rs, h_rs;            // LDS bytes per token row: activations (one part), staged h (hi + lo)
     // dynamic LDS layout (byte offsets)
     int lds_idx, lds_w, lds_sorted, lds_hist, lds_slot_start, lds_slot_exp, lds_slot_cnt,
         lds_tinv, lds_hinv, lds_xmax, lds_misc, lds_xa, lds_chunk, chunk_stride, lds_total;
