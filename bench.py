@@ -56,6 +56,43 @@ def distinct_experts(logits: np.ndarray, k: int) -> int:
     return int(np.unique(order).size)
 
 
+def source_digest() -> str:
+    """sha256 over the HIP sources and the ABI header: identifies the kernel
+    build that a stored counter summary belongs to."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_routed_expert_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "include", "moe.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter
+    reads for a plain copy of known size), or None when there is no summary for
+    this workload or the kernel sources have changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic.{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("source_digest") != source_digest():
+        return None
+    try:
+        return round(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 def layer_flops(cfg, T: int) -> tuple[float, float]:
     """(gate/up FLOPs, down FLOPs) of one layer: 2*H*F per matrix per routed
     row, for T*k routed rows plus T shared rows."""
@@ -73,6 +110,8 @@ def main():
     ap.add_argument("--layers", type=int, default=48)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the layer's kernels run on one device); --gpus {args.gpus} "
@@ -81,6 +120,17 @@ def main():
 
     import torch
     from quantized_routed_expert_amd import moe, synth
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                          "copies": 5}), flush=True)
+        return
 
     cname, T = WORKLOADS[args.workload]
     cfg = synth.CONFIGS[cname]
@@ -154,9 +204,10 @@ def main():
     us_layer = ms_step * 1000.0 / L
     log(f"pass {ms_step:.4f} ms, {us_layer:.2f} us/layer")
 
-    # ---- dominant kernel's own duration: events on its stream around each launch
-    # (decode: the single fused kernel of each layer; prefill: the whole layer's
-    # launches, of which the gate/up GEMM is the largest)
+    # ---- dominant kernel's own duration.  Decode: the layer is one kernel
+    # launch, so the timed region (events on the kernel's stream) over its K*L
+    # launches is that kernel's average duration plus the graph's launch gap.
+    # Prefill: events on the stream around each layer's launches.
     reps = 3
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L * reps)]
     with torch.cuda.stream(stream):
@@ -180,10 +231,12 @@ def main():
 
     if path == moe.PATH_DECODE:
         metric_value, unit = gbs, "GB/s"
+        kern_us = us_layer
         ach = (total_bytes / L) / (kern_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "k_decode_layer", "bytes_per_launch": round(total_bytes / L)}
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
+                "kernel": "k_decode_layer", "bytes_per_launch": round(total_bytes / L),
+                "launch_us": round(kern_us, 3)}
         dtype = "f16"  # MFMA inputs (exact integer codes, power-of-two-scaled activations), fp32 accumulate
     else:
         metric_value, unit = toks, "tok/s"
@@ -204,17 +257,18 @@ def main():
         rows_done = 0
         cpu_bytes = 0.0
         if path == moe.PATH_DECODE:
-            for li in host_keep:
+            # the layers of the pass in order, cycling, until the time budget is spent
+            while time.time() - t_start < args.cpu_seconds:
+                li = host_keep[n_layers % len(host_keep)]
                 orc.layer_forward(li.x, li.x_code, li.logits, cfg.top_k, cfg.bits, cfg.ffn, li.routed, li.shared,
                                   s_ffn=cfg.shared_ffn or None)
+                cpu_bytes += bytes_layer[n_layers % len(host_keep)]
                 n_layers += 1
-                cpu_bytes += bytes_layer[n_layers - 1]
-                if time.time() - t_start > args.cpu_seconds:
-                    break
             dt = time.time() - t_start
             cpu = {"value": round(cpu_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                   "sample": f"{n_layers} of the {L} layers, all {T} row(s), single-threaded C oracle "
-                             f"({dt:.1f} s); {dt / n_layers * 1e6:.0f} us/layer"}
+                   "sample": f"{n_layers} layer evaluations (the pass's {len(host_keep)} layers in order, "
+                             f"cycling), all {T} row(s), single-threaded C oracle ({dt:.1f} s); "
+                             f"{dt / n_layers * 1e6:.0f} us/layer"}
         else:
             li = host_keep[0]
             step = 16
