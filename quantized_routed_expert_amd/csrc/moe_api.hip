@@ -65,7 +65,7 @@ int dev_info(DevInfo &out) {
 // ----------------------------------------------------------------------------
 struct Layout {
     size_t counters = 0, n_counters = 0;       // decode: gu[MS] dn[MS] slice[H/128] err[4]
-    size_t harr = 0, out_pairs = 0, out_shared = 0;
+    size_t harr = 0, oll = 0, out_pairs = 0, out_shared = 0;
     size_t idx = 0, w = 0, offsets = 0, pairs = 0, active = 0, chunk_counts = 0;
     size_t slot_exp = 0, slot_row0 = 0, slot_cnt = 0, slot_hrow0 = 0, prefix_gu = 0, prefix_dn = 0;
     size_t hbuf = 0;
@@ -77,7 +77,7 @@ struct Layout {
 // layout, so a workspace that is zero before its first use stays valid for
 // calls of any shape and path (each call returns the counters to zero).  Each
 // counter has a 256-byte line of its own.
-constexpr size_t COUNTER_WORDS = (size_t)(2 * DEC_MAX_SLOTS + DEC_MAX_SLICES + 1) * DEC_CSTRIDE;
+constexpr size_t COUNTER_WORDS = (size_t)(2 * DEC_MAX_SLOTS + DEC_MAX_SLICES + 3) * DEC_CSTRIDE;
 Layout make_layout(int T, int E, int k, int H, int F, int Fs, int path) {
     Layout L;
     size_t off = 0;
@@ -102,7 +102,8 @@ Layout make_layout(int T, int E, int k, int H, int F, int Fs, int path) {
     L.out_pairs = take(TK * H * 4);
     L.out_shared = take((size_t)T * H * 4);
     if (path == MOE_PATH_DECODE) {
-        L.harr = take((TK + T) * (size_t)Fmax * 4);  // SwiGLU outputs per pair row (+ shared rows)
+        L.harr = take((TK + T) * (size_t)Fmax * 8);  // tagged SwiGLU outputs per pair row (+ shared rows)
+        L.oll = take((TK + T) * (size_t)H * 8);      // tagged weighted pair rows (+ shared rows)
     } else {
         L.slot_exp = take((size_t)(E + 1) * 4);
         L.slot_row0 = take((size_t)(E + 1) * 4);
@@ -162,7 +163,7 @@ int decode_lds_layout(DecodeParams &P, int xparts) {
     };
     P.lds_idx = take(TK * 4);
     P.lds_w = take(TK * 4);
-    P.lds_sorted = take(TK * 4);
+    P.lds_sorted = take((TK + P.E) * 4);  // sorted pairs, then (fused routing) each expert's first position
     P.lds_hist = take((P.E + 1) * 4);
     P.lds_slot_start = take(P.max_slots * 4);
     P.lds_slot_exp = take(P.max_slots * 4);
@@ -308,12 +309,15 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
     P.out_shared = at<float>(ws, L.out_shared);
     P.topk_idx_out = tidx;
     P.topk_w_out = tw;
-    P.hbuf = at<float>(ws, L.harr);
+    P.hll = at<uint64_t>(ws, L.harr);
+    P.oll = at<uint64_t>(ws, L.oll);
     uint32_t *cnt = at<uint32_t>(ws, L.counters);
     P.gu_count = cnt;
     P.dn_count = cnt + (size_t)DEC_MAX_SLOTS * DEC_CSTRIDE;
     P.slice_count = cnt + (size_t)2 * DEC_MAX_SLOTS * DEC_CSTRIDE;
     P.err = cnt + (size_t)(2 * DEC_MAX_SLOTS + DEC_MAX_SLICES) * DEC_CSTRIDE;
+    P.epoch = P.err + DEC_CSTRIDE;
+    P.done = P.err + 2 * DEC_CSTRIDE;
     P.T = T;
     P.E = E;
     P.k = k;

@@ -43,20 +43,25 @@
 namespace moe {
 
 #ifdef MOE_PHASE_TRACE
-// Phase timestamps (100 MHz device clock) per workgroup, for analysis builds only.
+// Phase timestamps (100 MHz device clock) per workgroup, for analysis builds
+// only.  The buffer pointer is read once at kernel start (TRACE_INIT), so a
+// trace point adds no global load (and no wait on outstanding loads).
 __device__ uint64_t *g_trace = nullptr;
+#define TRACE_INIT volatile uint64_t *const trace_buf = g_trace
 #define TRACE(slot)                                                                                        \
     do {                                                                                                   \
-        if (g_trace && threadIdx.x == 0) g_trace[blockIdx.x * 64 + (slot)] = __builtin_amdgcn_s_memrealtime(); \
+        if (trace_buf && threadIdx.x == 0) trace_buf[blockIdx.x * 128 + (slot)] = __builtin_amdgcn_s_memrealtime(); \
     } while (0)
-// per wave (after this wave's outstanding memory operations)
+// per wave (no wait of its own)
 #define TRACEW(slot)                                                                                        \
     do {                                                                                                    \
-        __builtin_amdgcn_s_waitcnt(0);                                                                      \
-        if (g_trace && (threadIdx.x & 63) == 0)                                                             \
-            g_trace[blockIdx.x * 64 + 16 + (threadIdx.x >> 6) * 6 + (slot)] = __builtin_amdgcn_s_memrealtime(); \
+        if (trace_buf && (threadIdx.x & 63) == 0)                                                           \
+            trace_buf[blockIdx.x * 128 + 32 + (threadIdx.x >> 6) * 12 + (slot)] = __builtin_amdgcn_s_memrealtime(); \
     } while (0)
 #else
+#define TRACE_INIT \
+    do {           \
+    } while (0)
 #define TRACE(slot) \
     do {            \
     } while (0)
@@ -79,6 +84,18 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
+
+// Inclusive prefix sum over the 64 lanes (row shifts within rows of 16, then
+// row broadcasts across rows).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+    return v;
+}
 
 // Router for one row by one wave (E <= 64 * EPL): k rounds of a wave-wide
 // argmax, an equal logit going to the lower expert id; softmax over the k.
@@ -401,21 +418,53 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         return blob + (size_t)mat * Fx * rowH + (size_t)(tl * nfgT + fl) * 16 * rowH + (size_t)kc * segH;
     };
 
+    TRACE_INIT;
     TRACE(0);
-    // A first unit of the shared expert depends on no routing: it starts streaming now.
+    // Routing: row t by wave DEC_WAVES-1 - t % DEC_WAVES.  For small windows
+    // those waves hold no activation blocks, and a routing wave issues its
+    // logits load before any other: waits on loads are in issue order, so
+    // the routing waits for the logits only.
+    // The call's tag is the first load of every wave; it is read into a scalar
+    // register after the routing barrier, when it has landed: waits on loads
+    // are in issue order, so reading it later would wait for every weight
+    // load issued in between.
+    const uint32_t tag_v = ld_dev_u32(P.epoch);
+    const bool route_mode = (P.mode & DEC_MODE_ROUTE) != 0;
+    const int route_w = DEC_WAVES - 1 - wave;
+    const bool routes = route_mode && route_w < T;
+
+    // A first unit of the shared expert depends on no routing: it starts
+    // streaming now (in a routing wave, right after its routing).
     Chunk c;
     bool pref = false;
-    if ((int)blockIdx.x < tasks_sh) {
+    const bool shared_first = (int)blockIdx.x < tasks_sh;
+    if (shared_first && !routes) {
         TRACEW(0);
         chunk_load(c, unit_rows(blockIdx.x, 0), mapH);
         pref = true;
     }
 
-    // ======================= Phase A: activations, routing, grouping =======================
+    // ======================= Phase A: routing, activations, grouping =======================
     for (int i = tid; i < T; i += DEC_THREADS) s_xmax[i] = 0u;
-    if (P.mode & DEC_MODE_ROUTE)
-        for (int e = tid; e <= E; e += DEC_THREADS) s_hist[e] = 0;
-    __syncthreads();
+    if (route_mode)
+        for (int e = tid; e <= E; e += DEC_THREADS) s_hist[e] = 0;  // token masks
+    TRACEW(6);
+    if (routes) {
+        const int epl = (E + 63) >> 6;
+        for (int t = route_w; t < T; t += DEC_WAVES) {
+            const float *row = P.logits + (size_t)t * E;
+            if (epl <= 2) route_row<2>(row, E, k, s_idx + t * k, s_w + t * k, lane);
+            else if (epl <= 4) route_row<4>(row, E, k, s_idx + t * k, s_w + t * k, lane);
+            else if (epl <= 8) route_row<8>(row, E, k, s_idx + t * k, s_w + t * k, lane);
+            else route_row<16>(row, E, k, s_idx + t * k, s_w + t * k, lane);
+        }
+        TRACEW(7);
+        if (shared_first) {
+            chunk_load(c, unit_rows(blockIdx.x, 0), mapH);
+            pref = true;
+        }
+    }
+    TRACE(1);
 
     // activation blocks: thread owns blocks tid + 512 q (token t, block b)
     constexpr int QX = XPARTS == 1 ? DEC_X_BLOCKS_PER_THREAD : DEC_X_BLOCKS_PER_THREAD / 2;
@@ -431,76 +480,44 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             for (int v = 0; v < NV; ++v) xr[q][v] = src[v];
         }
     }
-    // routing of the rows owned by this wave (overlaps the activation loads)
-    if (P.mode & DEC_MODE_ROUTE) {
-        const int epl = (E + 63) >> 6;
-        for (int t = wave; t < T; t += DEC_WAVES) {
-            const float *row = P.logits + (size_t)t * E;
-            if (epl <= 2) route_row<2>(row, E, k, s_idx + t * k, s_w + t * k, lane);
-            else if (epl <= 4) route_row<4>(row, E, k, s_idx + t * k, s_w + t * k, lane);
-            else if (epl <= 8) route_row<8>(row, E, k, s_idx + t * k, s_w + t * k, lane);
-            else route_row<16>(row, E, k, s_idx + t * k, s_w + t * k, lane);
-        }
-    }
-    // per-token max |x|
-#pragma unroll
-    for (int q = 0; q < QX; ++q) {
-        const int j = tid + DEC_THREADS * q;
-        if (j < nxb) {
-            float mx = 0.0f;
-#pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const uint32_t w4[4] = {xr[q][v].x, xr[q][v].y, xr[q][v].z, xr[q][v].w};
-#pragma unroll
-                for (int c2 = 0; c2 < 4; ++c2) {
-                    if (XPARTS == 1) {
-                        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w4[c2] << 16)));
-                        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w4[c2] & 0xFFFF0000u)));
-                    } else {
-                        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w4[c2])));
-                    }
-                }
-            }
-            atomicMax(&s_xmax[j / nkbH], __builtin_bit_cast(uint32_t, mx));
-        }
-    }
-    TRACE(1);
-    __syncthreads();
+    __syncthreads();  // routing complete
+    const uint32_t tag = decode_tag(__builtin_amdgcn_readfirstlane(tag_v));  // this call's tag (see DecodeParams)
+    TRACE(9);
 
-    // grouping: histogram, scan (wave 0), stable placement
-    if (P.mode & DEC_MODE_ROUTE) {
-        for (int p = tid; p < TK; p += DEC_THREADS) atomicAdd(&s_hist[s_idx[p]], 1);
+    // grouping of the pairs by expert: slots in ascending expert id, pairs of
+    // a slot in (token, slot) order.  A token's k experts are distinct, so an
+    // expert's pairs are identified by a mask of its tokens: the pair of
+    // token t sits at the expert's start + the number of earlier tokens.
+    if (route_mode) {
+        uint32_t *s_tmask = (uint32_t *)s_hist;  // [E] tokens that chose expert e
+        int *s_start = s_sorted + TK;            // [E] first position of expert e
+        for (int p = tid; p < TK; p += DEC_THREADS) atomicOr(&s_tmask[s_idx[p]], 1u << (p / k));
         __syncthreads();
         if (wave == 0) {
-            // exclusive scan of (count | active flag << 16) over E <= 1024 experts
+            // exclusive scan of (count | active flag << 16) over the experts
             const int per = (E + 63) / 64;
             const int base = lane * per;
             int sum = 0;
             for (int i = 0; i < per; ++i) {
                 const int e = base + i;
                 if (e < E) {
-                    const int cnt = s_hist[e];
+                    const int cnt = __popc(s_tmask[e]);
                     sum += cnt | ((cnt > 0) << 16);
                 }
             }
-            int incl = sum;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int o = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += o;
-            }
+            const int incl = wave_incl_scan(sum);
             int run = incl - sum;
             for (int i = 0; i < per; ++i) {
                 const int e = base + i;
                 if (e < E) {
-                    const int cnt = s_hist[e];
+                    const int cnt = __popc(s_tmask[e]);
                     const int off = run & 0xFFFF, act = run >> 16;
                     if (cnt > 0) {
                         s_slot_exp[hs + act] = e;
                         s_slot_start[hs + act] = off;
                         s_slot_cnt[hs + act] = cnt;
                     }
-                    s_hist[e] = off;  // becomes the expert's first position
+                    s_start[e] = off;
                     run += cnt | ((cnt > 0) << 16);
                 }
             }
@@ -508,10 +525,8 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         }
         __syncthreads();
         for (int p = tid; p < TK; p += DEC_THREADS) {
-            const int e = s_idx[p];
-            int rank = 0;
-            for (int q = 0; q < p; ++q) rank += (s_idx[q] == e);
-            s_sorted[s_hist[e] + rank] = p;
+            const int e = s_idx[p], t = p / k;
+            s_sorted[s_start[e] + __popc(s_tmask[e] & ((1u << t) - 1u))] = p;
         }
         if (blockIdx.x == 0) {
             for (int p = tid; p < TK; p += DEC_THREADS) {
@@ -566,13 +581,85 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         s_slot_cnt[0] = T;
     }
     __syncthreads();  // slot tables complete
+    TRACE(13);
     const int n_slots = s_misc[0];
     const int n_tasks = tasks_sh + (n_slots - hs) * tasks_rt;
-    if (!pref && (int)blockIdx.x < n_tasks) {
-        TRACEW(0);
-        chunk_load(c, unit_rows(blockIdx.x, 0), mapH);
+
+    // Down tiles (slot, 128 output rows) continue the round robin of the
+    // gate/up tasks over the workgroups: tile i is work item n_tasks + i.
+    const int tiles_per_slot = H / DEC_DN_ROWS;
+    const int n_tiles = n_slots * tiles_per_slot;
+    const int first_tile = (int)(((long long)blockIdx.x - n_tasks % G + G) % G);
+    struct Tile {
+        const uint8_t *rows;  // this wave's 16 down rows
+        int s, rg, Fx, cbF, nchF, segF, rowF;
+        bool shared;
+    };
+    auto tile_of = [&](int ti) {
+        Tile t;
+        t.s = ti / tiles_per_slot;
+        t.rg = ti - t.s * tiles_per_slot;
+        t.shared = s_slot_exp[t.s] < 0;
+        t.Fx = t.shared ? Fs : F;
+        const uint8_t *blob = t.shared ? P.w_shared : P.w_routed + (size_t)s_slot_exp[t.s] * eb;
+        const int nkbF = t.Fx >> 5;
+        t.cbF = decode_f_chunk_blocks(nkbF);
+        t.nchF = nkbF / t.cbF;
+        t.segF = t.cbF * bb;
+        t.rowF = nkbF * bb;
+        t.rows = blob + (size_t)2 * t.Fx * rowH + (size_t)(t.rg * DEC_DN_ROWS + wave * 16) * t.rowF;
+        return t;
+    };
+    // The first down chunk streams in as soon as the registers are free: here
+    // for a workgroup without gate/up work, else during its last gate/up unit.
+    ChunkMap mapF;
+    int map_fx = -1;
+    bool c_holds_tile = false;
+    auto prefetch_first_tile = [&]() {
+        if (first_tile < n_tiles) {
+            const Tile t = tile_of(first_tile);
+            chunk_map(mapF, t.segF, t.rowF, lane);
+            map_fx = t.Fx;
+            chunk_load(c, t.rows, mapF);
+            c_holds_tile = true;
+        }
+    };
+    // per-token max |x|, before this wave issues any weight load after its
+    // activation loads (so the wait covers the activations only)
+#pragma unroll
+    for (int q = 0; q < QX; ++q) {
+        const int j = tid + DEC_THREADS * q;
+        if (j < nxb) {
+            float mx = 0.0f;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const uint32_t w4[4] = {xr[q][v].x, xr[q][v].y, xr[q][v].z, xr[q][v].w};
+#pragma unroll
+                for (int c2 = 0; c2 < 4; ++c2) {
+                    if (XPARTS == 1) {
+                        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w4[c2] << 16)));
+                        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w4[c2] & 0xFFFF0000u)));
+                    } else {
+                        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w4[c2])));
+                    }
+                }
+            }
+            atomicMax(&s_xmax[j / nkbH], __builtin_bit_cast(uint32_t, mx));
+        }
+    }
+    TRACEW(8);
+    if (!pref) {
+        if ((int)blockIdx.x < n_tasks) {
+            TRACEW(0);
+            chunk_load(c, unit_rows(blockIdx.x, 0), mapH);
+        } else {
+            prefetch_first_tile();
+        }
     }
 
+    TRACEW(9);
+    __syncthreads();
+    TRACE(14);
     // activations to fp16 (hi [+ lo]) of x * 2^sc_t in the format's k order:
     // part p, token t, block b, k-group g at p*T*x_rs + t*x_rs + (4b+g)*16
 #pragma unroll
@@ -643,9 +730,9 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         for (int rho = 0; rho < rounds; ++rho) {
             const int ui = rho * 8 + wave;
             const int kc = (ui % upt) % nchH;
-            if (first_task && rho == 0) TRACEW(1);
             __builtin_amdgcn_wave_barrier();
             chunk_store(c, s_chunk, mapH);
+            if (first_task && rho == 0) TRACEW(1);
             wave_lds_handoff();
             // the registers are free again: the next unit's chunk streams in while this one computes
             int nt = task, nr = rho + 1;
@@ -654,8 +741,11 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
                 nr = 0;
             }
             if (nt < n_tasks) chunk_load(c, unit_rows(nt, nr), mapH);
+            else prefetch_first_tile();
             const uint8_t *ab = s_xa + (size_t)tok * P.x_rs + (size_t)(kc * cbH) * 64 + g_lane * 16;
+            if (first_task && rho == 0) TRACEW(10);
             chunk_mma<BITS, XPARTS>(accr[rho], s_chunk, rsH, cbH, n_lane, g_lane, ab, 64, T * P.x_rs);
+            if (first_task && rho == 0) TRACEW(11);
         }
         if (first_task) TRACEW(2);
         // unit partials (token m, feature n) into this wave's LDS buffer: round rho at [rho][m][n]
@@ -670,9 +760,11 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             }
         }
         __syncthreads();
-        // h = silu(g) * u per (feature group, token, feature): K chunks summed in
-        // order 0, 1, ...; back in the units of x; stored in the down
-        // projection's k order
+        if (first_task) TRACEW(3);
+        // h = silu(g) * u per (feature group, token, feature): K chunks summed
+        // in order 0, 1, ...; back in the units of x; stored as tagged words in
+        // the down projection's k order.  The count goes up without waiting for
+        // the stores: a reader checks each word's tag.
         const int per_fl = n_tok * 16;
         for (int i = tid; i < nfgT * per_fl; i += DEC_THREADS) {
             const int fl = i / per_fl, rem = i - fl * per_fl;
@@ -692,42 +784,30 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             group_slot_of(BITS, f & 31, pg, pe);
             const int fo = (f >> 5) * 32 + pg * 8 + pe;
             const int row = shared_slot ? TK + m : s_slot_start[s] + m;
-            st_dev(P.hbuf + (size_t)row * P.h_stride + fo, h);
+            st_tagged(P.hll + (size_t)row * P.h_stride + fo, h, tag);
         }
-        wait_all_mem();   // this thread's h stores are complete ...
-        __syncthreads();  // ... for every thread, before the task is counted
+        __syncthreads();  // the unit partials have been read: the buffers are free again
         if (tid == 0) add_dev(&P.gu_count[s * DEC_CSTRIDE], 1u);
-        if (first_task) TRACEW(3);
+        if (first_task) TRACEW(4);
         first_task = false;
     }
     TRACE(3);
 
     // ======================= Phase C: down + weighted write + combine =======================
-    // Down tiles (slot, 128 output rows) continue the round robin of the
-    // gate/up tasks over the workgroups: tile i is work item n_tasks + i.
-    const int tiles_per_slot = H / DEC_DN_ROWS;
-    const int n_tiles = n_slots * tiles_per_slot;
-    const int first_tile = (int)(((long long)blockIdx.x - n_tasks % G + G) % G);
-    int cur_slot = -1, map_fx = -1;
-    ChunkMap mapF;
+    int cur_slot = -1;
     for (int ti = first_tile; ti < n_tiles; ti += G) {
-        const int s = ti / tiles_per_slot, rg = ti - s * tiles_per_slot;
-        const bool shared_slot = (s_slot_exp[s] < 0);
-        const int Fx = shared_slot ? Fs : F;
-        const uint8_t *blob = shared_slot ? P.w_shared : P.w_routed + (size_t)s_slot_exp[s] * eb;
-        const int nkbF = Fx >> 5;
-        const int cbF = decode_f_chunk_blocks(nkbF), nchF = nkbF / cbF, segF = cbF * bb;
-        const int rowF = nkbF * bb;
+        const Tile tl = tile_of(ti);
+        const int s = tl.s, rg = tl.rg, Fx = tl.Fx;
+        const bool shared_slot = tl.shared;
+        const int cbF = tl.cbF, nchF = tl.nchF, segF = tl.segF;
         const int rsF = decode_chunk_rstride(segF);
+        const uint8_t *rows_d = tl.rows;
         if (Fx != map_fx) {
-            chunk_map(mapF, segF, rowF, lane);
+            chunk_map(mapF, segF, tl.rowF, lane);
             map_fx = Fx;
         }
-        const uint8_t *rows_d = blob + (size_t)2 * Fx * rowH + (size_t)(rg * DEC_DN_ROWS + wave * 16) * rowF;
         const int n_tok = s_slot_cnt[s];
-
-        Chunk cd;
-        chunk_load(cd, rows_d, mapF);  // prefetch before the wait
+        if (!(ti == first_tile && c_holds_tile)) chunk_load(c, rows_d, mapF);  // prefetch before the wait
 
         if (s != cur_slot) {
             if (tid < T) s_xmax[tid] = 0u;
@@ -757,14 +837,27 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
                 const int it = tid + DEC_THREADS * q;
                 if (it < nit) {
                     const int m = it / ngrp, gi = it - m * ngrp;
-                    const float *src = P.hbuf + (size_t)(row0 + m) * P.h_stride + gi * 8;
+                    const uint64_t *src = P.hll + (size_t)(row0 + m) * P.h_stride + gi * 8;
+                    uint64_t wd[8];
+                    for (uint32_t spins = 0;; ++spins) {  // until every word carries this call's tag
+                        bool ok = true;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            wd[e] = ld_dev_u64(src + e);
+                            ok = ok && (uint32_t)(wd[e] >> 32) == tag;
+                        }
+                        if (ok) break;
+                        if (spins > DEC_SPIN_LIMIT) {
+                            atomicOr(P.err, 1u);
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
+                    }
                     float mx = 0.0f;
 #pragma unroll
-                    for (int e2 = 0; e2 < 4; ++e2) {
-                        const uint64_t two = ld_dev_u64(src + 2 * e2);
-                        hv[q][2 * e2] = __builtin_bit_cast(float, (uint32_t)two);
-                        hv[q][2 * e2 + 1] = __builtin_bit_cast(float, (uint32_t)(two >> 32));
-                        mx = fmaxf(mx, fmaxf(fabsf(hv[q][2 * e2]), fabsf(hv[q][2 * e2 + 1])));
+                    for (int e = 0; e < 8; ++e) {
+                        hv[q][e] = __builtin_bit_cast(float, (uint32_t)wd[e]);
+                        mx = fmaxf(mx, fabsf(hv[q][e]));
                     }
                     atomicMax(&s_xmax[m], __builtin_bit_cast(uint32_t, mx));
                 }
@@ -803,9 +896,10 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         const uint8_t *ab = s_xa + (size_t)(n_lane < n_tok ? n_lane : 0) * P.h_rs + g_lane * 32;
         for (int ci = 0; ci < nchF; ++ci) {
             __builtin_amdgcn_wave_barrier();
-            chunk_store(cd, s_chunk, mapF);
+            chunk_store(c, s_chunk, mapF);
+            if (ti == first_tile && ci == 0) TRACEW(5);
             wave_lds_handoff();
-            if (ci + 1 < nchF) chunk_load(cd, rows_d + (size_t)(ci + 1) * segF, mapF);
+            if (ci + 1 < nchF) chunk_load(c, rows_d + (size_t)(ci + 1) * segF, mapF);
             chunk_mma<BITS, 2>(acc, s_chunk, rsF, cbF, n_lane, g_lane, ab + (size_t)ci * cbF * 128, 128, 16);
             wave_lds_handoff();
         }
@@ -819,46 +913,92 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
                 if (m < n_tok) {
                     const float o = ov[r] * s_hinv[m];
                     if (shared_slot) {
-                        st_dev(&P.out_shared[(size_t)m * H + hrow], o);
+                        st_tagged(P.oll + (size_t)(TK + m) * H + hrow, o, tag);
                     } else {
                         const int p = s_sorted[s_slot_start[s] + m];
-                        st_dev(&P.out_pairs[(size_t)p * H + hrow], s_w[p] * o);
+                        if (P.mode & DEC_MODE_COMBINE) st_tagged(P.oll + (size_t)p * H + hrow, s_w[p] * o, tag);
+                        else P.out_pairs[(size_t)p * H + hrow] = s_w[p] * o;  // read after the launch only
                     }
                 }
             }
         }
         if (ti == first_tile) TRACE(7);
-        wait_all_mem();   // every wave's output stores are complete ...
-        __syncthreads();  // ... before the workgroup counts this tile
+        __syncthreads();  // every wave's output stores are issued before the workgroup counts this tile
         if (tid == 0) {
-            int do_combine = 0;
-            if (P.mode & DEC_MODE_COMBINE) {
-                const uint32_t old = add_dev(&P.slice_count[rg * DEC_CSTRIDE], 1u);
-                do_combine = (old == (uint32_t)(n_slots - 1));
-            }
+            // both counts in flight together
+            const uint32_t old = add_dev(&P.slice_count[rg * DEC_CSTRIDE], 1u);
             const uint32_t dn = add_dev(&P.dn_count[s * DEC_CSTRIDE], 1u);
             if (dn == (uint32_t)(tiles_per_slot - 1)) {
                 // every tile of this slot has passed its wait: the counters can return to zero
                 store_dev_u32(&P.gu_count[s * DEC_CSTRIDE], 0u);
                 store_dev_u32(&P.dn_count[s * DEC_CSTRIDE], 0u);
             }
-            s_misc[1] = do_combine;
+            const bool last = old == (uint32_t)(n_slots - 1);
+            if (last) store_dev_u32(&P.slice_count[rg * DEC_CSTRIDE], 0u);
+            s_misc[1] = last && (P.mode & DEC_MODE_COMBINE);
         }
         __syncthreads();
         if (s_misc[1]) {
             // the last slot of this 128-row slice: y = ((w0 o0 + w1 o1) + ...) + shared
-            for (int i = tid; i < T * DEC_DN_ROWS; i += DEC_THREADS) {
-                const int t = i / DEC_DN_ROWS, hrow = rg * DEC_DN_ROWS + (i - t * DEC_DN_ROWS);
-                float acc2 = ld_dev(&P.out_pairs[((size_t)t * k) * H + hrow]);
-                for (int j = 1; j < k; ++j) acc2 += ld_dev(&P.out_pairs[((size_t)t * k + j) * H + hrow]);
-                if (has_shared) acc2 += ld_dev(&P.out_shared[(size_t)t * H + hrow]);
-                P.y[(size_t)t * H + hrow] = acc2;
+            // every (term, output) word of the slice is loaded with the loads in
+            // flight together, checked for this call's tag and parked in LDS
+            // (the staged h and the chunk buffers are free here), then each
+            // output is summed in the fixed order; in batches of outputs that fit
+            const int nterm = k + hs;
+            const int nout = T * DEC_DN_ROWS;
+            float *s_terms = (float *)(smem + P.lds_xa);
+            const int ob = min(nout, ((P.lds_total - P.lds_xa) >> 2) / nterm);
+            for (int o0 = 0; o0 < nout; o0 += ob) {
+                const int nb = min(ob, nout - o0);
+                const int nw = nterm * nb;
+                for (int i0 = 0; i0 < nw; i0 += 4 * DEC_THREADS) {
+                    uint64_t wd[4];
+                    const uint64_t *src[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int i = i0 + q * DEC_THREADS + tid;
+                        const int j = i / nb, o = o0 + (i - j * nb);
+                        const int t = o / DEC_DN_ROWS, hrow = rg * DEC_DN_ROWS + (o - t * DEC_DN_ROWS);
+                        src[q] = P.oll + (size_t)(j < k ? t * k + j : TK + t) * H + hrow;
+                        wd[q] = i < nw ? ld_dev_u64(src[q]) : 0;
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int i = i0 + q * DEC_THREADS + tid;
+                        if (i < nw) {
+                            for (uint32_t spins = 0; (uint32_t)(wd[q] >> 32) != tag; ++spins) {
+                                if (spins > DEC_SPIN_LIMIT) {
+                                    atomicOr(P.err, 1u);
+                                    break;
+                                }
+                                __builtin_amdgcn_s_sleep(1);
+                                wd[q] = ld_dev_u64(src[q]);
+                            }
+                            s_terms[i] = __builtin_bit_cast(float, (uint32_t)wd[q]);
+                        }
+                    }
+                }
+                __syncthreads();
+                for (int ol = tid; ol < nb; ol += DEC_THREADS) {
+                    const int o = o0 + ol;
+                    const int t = o / DEC_DN_ROWS, hrow = rg * DEC_DN_ROWS + (o - t * DEC_DN_ROWS);
+                    float acc2 = s_terms[ol];
+                    for (int j = 1; j < nterm; ++j) acc2 += s_terms[j * nb + ol];  // ((w0 o0 + w1 o1) + ...) + shared
+                    P.y[(size_t)t * H + hrow] = acc2;
+                }
+                __syncthreads();  // the terms are read before the next batch or tile reuses the LDS
             }
-            __syncthreads();
-            if (tid == 0) store_dev_u32(&P.slice_count[rg * DEC_CSTRIDE], 0u);
+            cur_slot = -1;  // the staged h was overwritten
         }
     }
     TRACE(8);
+    // the last workgroup to finish moves the workspace on to the next call's tag
+    if (tid == 0) {
+        if (add_dev(P.done, 1u) == (uint32_t)(G - 1)) {
+            store_dev_u32(P.done, 0u);
+            store_dev_u32(P.epoch, ld_dev_u32(P.epoch) + 1u);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -69,6 +69,8 @@ __device__ __forceinline__ uint32_t pk_fma_h2(uint32_t v, uint32_t scale, uint32
 // mantissa bits of 0x6400 builds it without a conversion instruction.
 #define FP16_MAGIC 0x64006400u
 
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) { return (a & m) | c; }
+
 // 4-bit: q = bytes qs[4g..4g+3] of one block -> 8 exact fp16 values (code - 8)
 // in the order of pos_in_block(4, g, .).
 __device__ __forceinline__ half8 unpack4(uint32_t q) {
@@ -77,10 +79,10 @@ __device__ __forceinline__ half8 unpack4(uint32_t q) {
     const uint32_t o_lo = H2(0xE408, 0xE408);       // -1032
     const uint32_t o_hi = H2(0xD480, 0xD480);       // -72
     uint32_t q8 = q >> 8;
-    uint32_t v0 = (q & 0x000F000Fu) | FP16_MAGIC;   // 1024 + c
-    uint32_t v1 = (q & 0x00F000F0u) | FP16_MAGIC;   // 1024 + 16 c
-    uint32_t v2 = (q8 & 0x000F000Fu) | FP16_MAGIC;
-    uint32_t v3 = (q8 & 0x00F000F0u) | FP16_MAGIC;
+    uint32_t v0 = and_or(q, 0x000F000Fu, FP16_MAGIC);   // 1024 + c
+    uint32_t v1 = and_or(q, 0x00F000F0u, FP16_MAGIC);   // 1024 + 16 c
+    uint32_t v2 = and_or(q8, 0x000F000Fu, FP16_MAGIC);
+    uint32_t v3 = and_or(q8, 0x00F000F0u, FP16_MAGIC);
     u32x4 r;
     r.x = pk_fma_h2(v0, one, o_lo);
     r.y = pk_fma_h2(v1, s16, o_hi);
@@ -98,10 +100,10 @@ __device__ __forceinline__ void unpack3(uint32_t p0, uint32_t p1, uint32_t th, h
     const uint32_t sA = H2(0x3C00, 0x2C00), oA = H2(0xE404, 0xD440);  // (1, 1/16), (-1028, -68)
     const uint32_t sB = H2(0x3400, 0x2400), oB = H2(0xDC10, 0xCD00);  // (1/4, 1/64), (-260, -20)
     u32x4 a;
-    a.x = pk_fma_h2((p0 & 0x00300003u) | FP16_MAGIC, sA, oA);
-    a.y = pk_fma_h2((p0 & 0x00C0000Cu) | FP16_MAGIC, sB, oB);
-    a.z = pk_fma_h2((p1 & 0x00300003u) | FP16_MAGIC, sA, oA);
-    a.w = pk_fma_h2((p1 & 0x00C0000Cu) | FP16_MAGIC, sB, oB);
+    a.x = pk_fma_h2(and_or(p0, 0x00300003u, FP16_MAGIC), sA, oA);
+    a.y = pk_fma_h2(and_or(p0, 0x00C0000Cu, FP16_MAGIC), sB, oB);
+    a.z = pk_fma_h2(and_or(p1, 0x00300003u, FP16_MAGIC), sA, oA);
+    a.w = pk_fma_h2(and_or(p1, 0x00C0000Cu, FP16_MAGIC), sB, oB);
     lo = __builtin_bit_cast(half8, a);
     // third bits: positions 0, 8, 1, 9 (and +16) of th
     const uint32_t s0 = H2(0x4400, 0x4400), o0 = H2(0xEC00, 0xEC00);  // 4, -4096
@@ -109,10 +111,10 @@ __device__ __forceinline__ void unpack3(uint32_t p0, uint32_t p1, uint32_t th, h
     const uint32_t s1 = H2(0x4000, 0x4000), o1 = H2(0xE800, 0xE800);  // 2, -2048
     const uint32_t s9 = H2(0x2000, 0x2000), o9 = H2(0xC800, 0xC800);  // 1/128, -8
     u32x4 b;
-    b.x = pk_fma_h2((th & 0x00010001u) | FP16_MAGIC, s0, o0);
-    b.y = pk_fma_h2((th & 0x01000100u) | FP16_MAGIC, s8, o8);
-    b.z = pk_fma_h2((th & 0x00020002u) | FP16_MAGIC, s1, o1);
-    b.w = pk_fma_h2((th & 0x02000200u) | FP16_MAGIC, s9, o9);
+    b.x = pk_fma_h2(and_or(th, 0x00010001u, FP16_MAGIC), s0, o0);
+    b.y = pk_fma_h2(and_or(th, 0x01000100u, FP16_MAGIC), s8, o8);
+    b.z = pk_fma_h2(and_or(th, 0x00020002u, FP16_MAGIC), s1, o1);
+    b.w = pk_fma_h2(and_or(th, 0x02000200u, FP16_MAGIC), s9, o9);
     hb = __builtin_bit_cast(half8, b);
 }
 
@@ -180,9 +182,14 @@ __device__ __forceinline__ void st_dev(float *p, float v) {
 __device__ __forceinline__ float ld_dev(const float *p) {
     return __builtin_bit_cast(float, __hip_atomic_load((const uint32_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
-// two floats, 8-byte aligned
-__device__ __forceinline__ uint64_t ld_dev_u64(const float *p) {
-    return __hip_atomic_load((const uint64_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// tagged words: fp32 value in the low half, a tag in the high half, read and
+// written as one 64-bit access
+__device__ __forceinline__ uint64_t ld_dev_u64(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_tagged(uint64_t *p, float v, uint32_t tag) {
+    __hip_atomic_store(p, (uint64_t)__builtin_bit_cast(uint32_t, v) | ((uint64_t)tag << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t ld_dev_u32(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -20,7 +20,7 @@ constexpr int DEC_X_BLOCKS_PER_THREAD = 4;   // activation blocks staged per thr
 constexpr uint32_t DEC_SPIN_LIMIT = 1u << 20;  // bounded waits: a wait that runs out sets err bit 0
 constexpr int DEC_CSTRIDE = 64;              // 32-bit words between counters (one 256-byte line each)
 #define MOE_MAX_EXPERTS_DEV 4096
-#define MOE_DECODE_ROWS_DEV 16
+#define MOE_DECODE_ROWS_DEV 16  // <= 32: the fused grouping keeps a 32-bit token mask per expert
 constexpr int DEC_MAX_SLOTS = MOE_DECODE_ROWS_DEV * 32 + 1;  // T*k pairs (k <= 32) + the shared expert
 constexpr int DEC_MAX_SLICES = 65536 / DEC_DN_ROWS;
 
@@ -55,6 +55,14 @@ __host__ __device__ inline int decode_chunk_rstride(int seg_bytes) {
     return 16 * (gr | 1);
 }
 
+// The tag of the call that follows `completed` calls on a workspace: a
+// bijection of the count (so consecutive calls never share a tag), never 0
+// (the value a zeroed workspace holds).
+__host__ __device__ inline uint32_t decode_tag(uint32_t completed) {
+    const uint32_t t = ((completed + 1u) * 0x9E3779B1u) ^ 0xA5A5A5A5u;
+    return t ? t : 0x5A5A5A5Au;
+}
+
 struct DecodeParams {
     const void *x;             // [T][H] fp32 or bf16
     const float *logits;       // [T][E] (ROUTE mode)
@@ -69,11 +77,18 @@ struct DecodeParams {
     float *out_shared;         // [T][H]
     int32_t *topk_idx_out;     // may be null
     float *topk_w_out;         // may be null
-    float *hbuf;               // [(T*k + T)][Fmax] fp32 SwiGLU outputs, in the down projection's k order
+    // Data handed between workgroups is written as 64-bit words (fp32 value in
+    // the low half, the call's tag in the high half), so a reader can tell a
+    // word of this call from an older one and the writer never has to wait for
+    // its stores to complete.
+    uint64_t *hll;             // [(T*k + T)][Fmax] SwiGLU outputs, in the down projection's k order
+    uint64_t *oll;             // [(T*k + T)][H] weighted pair rows, then shared rows (COMBINE mode)
     uint32_t *gu_count;        // [DEC_MAX_SLOTS * DEC_CSTRIDE]: finished gate/up tasks per slot
     uint32_t *dn_count;        // [DEC_MAX_SLOTS * DEC_CSTRIDE]: finished down tiles per slot
     uint32_t *slice_count;     // [DEC_MAX_SLICES * DEC_CSTRIDE]: finished slots per 128-row slice
     uint32_t *err;             // error word (bit 0: a wait hit its spin limit; bit 1: bad given grouping)
+    uint32_t *epoch;           // calls completed on this workspace (the tag source)
+    uint32_t *done;            // workgroups of this call that have finished
     int T, E, k, H, F, Fs;     // Fs = shared ffn (0 = none)
     int bits, x_f32, mode, max_slots;
     int h_stride;              // floats per hbuf row (Fmax)
