@@ -150,6 +150,64 @@ int resolve_path(int path, int T) {
 
 inline hipStream_t S(int64_t s) { return (hipStream_t)(intptr_t)s; }
 
+// ceil(2^32 / d) for d >= 2 (n / d == umulhi(n, magic) for n < 2^20); 0 for d = 1
+uint32_t magic_div(uint32_t d) { return d < 2 ? 0u : (uint32_t)((((uint64_t)1 << 32) + d - 1) / d); }
+int ilog2(int v) {
+    int r = 0;
+    while ((1 << r) < v) ++r;
+    return r;
+}
+
+// Geometry of the fused decode launch (see DecodeParams); needs T, E, k, H,
+// F, Fs, bits.
+void decode_geometry(DecodeParams &P) {
+    const int bb = P.bits == 4 ? 18 : 14;
+    P.nkbH = P.H / 32;
+    P.cbH = decode_h_chunk_blocks(P.nkbH);
+    const int nchH = P.nkbH / P.cbH;
+    P.segH = P.cbH * bb;
+    P.rowH = P.nkbH * bb;
+    P.rsH = decode_chunk_rstride(P.segH);
+    P.perH = P.segH / 16;
+    P.invH = 65536u / (uint32_t)P.perH + 1u;
+    P.lg_nchH = ilog2(nchH);
+    const int upt = 2 * nchH;
+    P.lg_upt = ilog2(upt);
+    const int nfgT = upt >= 8 ? 1 : 8 / upt;
+    P.lg_nfgT = ilog2(nfgT);
+    P.rounds = upt > 8 ? upt / 8 : 1;
+    P.tasks_sh = P.Fs / (16 * nfgT);
+    P.tasks_rt = P.F / (16 * nfgT);
+    P.m_tasks_rt = magic_div(P.tasks_rt);
+    P.tps = P.H / DEC_DN_ROWS;
+    P.m_tps = magic_div(P.tps);
+    for (int i = 0; i < 2; ++i) {
+        const int fx = i == 0 ? P.F : (P.Fs ? P.Fs : P.F);
+        const int nkb = fx / 32;
+        P.fx[i] = fx;
+        P.cbF[i] = decode_f_chunk_blocks(nkb);
+        P.nchF[i] = nkb / P.cbF[i];
+        P.segF[i] = P.cbF[i] * bb;
+        P.rowF[i] = nkb * bb;
+        P.rsF[i] = decode_chunk_rstride(P.segF[i]);
+        P.perF[i] = P.segF[i] / 16;
+        P.invF[i] = 65536u / (uint32_t)P.perF[i] + 1u;
+        P.m_ngrp[i] = magic_div(fx / 8);
+    }
+    P.m_k = magic_div(P.k);
+    P.xgrp = P.H / 8;
+    P.m_xgrp = magic_div(P.xgrp);
+    // routing by ranks when every thread compares few keys: threads per logit
+    // = 512 / (T*E), a power of two from 1 to 16
+    const long long nkeys = (long long)P.T * P.E;
+    int tpi = 1;
+    while (tpi < 16 && nkeys * tpi * 2 <= DEC_THREADS) tpi *= 2;
+    const long long cmp = (nkeys + DEC_THREADS / tpi - 1) / (DEC_THREADS / tpi) * ((P.E + tpi - 1) / tpi);
+    P.route_rank = nkeys <= DEC_RANK_MAX_KEYS && cmp <= DEC_RANK_MAX_CMP && P.E % (4 * tpi) == 0;
+    P.lg_tpi = ilog2(tpi);
+    P.m_E = magic_div(P.E);
+}
+
 // Fill the decode kernel's LDS layout; returns the byte total.
 int decode_lds_layout(DecodeParams &P, int xparts) {
     const int TK = P.T * P.k;
@@ -188,6 +246,9 @@ int decode_lds_layout(DecodeParams &P, int xparts) {
         cmax = cs > cmax ? cs : cmax;
     }
     cmax = cmax > 2048 ? cmax : 2048;
+    // (phase A also keeps the rank keys and the selected logits there)
+    const int rank_bytes = (P.T * P.E + TK) * 4;
+    if (DEC_WAVES * cmax < rank_bytes) cmax = (rank_bytes + DEC_WAVES - 1) / DEC_WAVES;
     P.chunk_stride = (int)align_up((size_t)cmax, 16);
     P.lds_chunk = take(DEC_WAVES * P.chunk_stride);
     P.lds_total = off;
@@ -203,8 +264,8 @@ int launch_err(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 constexpr int DEC_LDS_BUDGET = 160 * 1024;
 bool decode_fits(int T, int E, int k, int H, int F, int Fs, int bits, int x_dtype) {
     const int xf = x_dtype == MOE_DTYPE_F32;
-    const int per = xf ? DEC_X_BLOCKS_PER_THREAD / 2 : DEC_X_BLOCKS_PER_THREAD;
-    if ((long long)T * (H / 32) > (long long)per * DEC_THREADS) return false;
+    const int per = xf ? DEC_XG_F32 : DEC_XG_BF16;
+    if ((long long)T * (H / 8) > (long long)per * DEC_THREADS) return false;
     if (F > DEC_MAX_F || Fs > DEC_MAX_F) return false;
     if (decode_h_chunk_blocks(H / 32) == 0) return false;
     DecodeParams P;
@@ -216,8 +277,8 @@ bool decode_fits(int T, int E, int k, int H, int F, int Fs, int bits, int x_dtyp
     P.F = F;
     P.Fs = Fs;
     P.bits = bits;
-    P.cbH = decode_h_chunk_blocks(H / 32);
     P.max_slots = ((T * k < E) ? T * k : E) + 1;
+    decode_geometry(P);
     return decode_lds_layout(P, xf ? 2 : 1) <= DEC_LDS_BUDGET;
 }
 
@@ -329,7 +390,7 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
     P.mode = mode | (shared ? DEC_MODE_SHARED : 0);
     P.max_slots = ((T * k < E) ? T * k : E) + 1;  // LDS slot tables (counters use the fixed stride)
     P.h_stride = P.F > P.Fs ? P.F : P.Fs;
-    P.cbH = decode_h_chunk_blocks(P.H / 32);
+    decode_geometry(P);
     const int lds = decode_lds_layout(P, x_f32 ? 2 : 1);
     if (lds > dv.lds_max) return MOE_ERR_UNSUPPORTED;
     static std::mutex mu;

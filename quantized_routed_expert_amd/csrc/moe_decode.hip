@@ -37,6 +37,8 @@
 // Data crossing workgroups (partials, pair rows) uses device-coherent accesses
 // and per-wave store completion instead of agent-scope fences, which on this
 // chip would write back or invalidate a whole XCD's L2.
+#include <type_traits>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -99,14 +101,22 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 
 // Router for one row by one wave (E <= 64 * EPL): k rounds of a wave-wide
 // argmax, an equal logit going to the lower expert id; softmax over the k.
+// The logits load (route_keys) is separate from the selection (route_pick),
+// so a wave can issue other loads in between.
 template <int EPL>
-__device__ void route_row(const float *row, int E, int k, int *out_idx, float *out_w, int lane) {
-    uint32_t key[EPL];
+__device__ __forceinline__ void route_keys(const float *row, int E, int lane, uint32_t (&key)[EPL]) {
+    float v[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + 64 * i;
-        key[i] = e < E ? float_key(row[e]) : 0u;  // finite values have keys > 0
+        v[i] = row[e < E ? e : 0];  // every lane loads (in bounds), so the loads issue as one sequence
     }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) key[i] = lane + 64 * i < E ? float_key(v[i]) : 0u;  // finite values: keys > 0
+}
+
+template <int EPL>
+__device__ __forceinline__ void route_pick(uint32_t (&key)[EPL], int k, int *out_idx, float *out_w, int lane) {
     float mine = 0.0f;
     int mine_id = 0;
     for (int j = 0; j < k; ++j) {
@@ -150,37 +160,38 @@ __device__ void route_row(const float *row, int E, int k, int *out_idx, float *o
 // ---------------------------------------------------------------------------
 // Chunk streaming: 16 consecutive rows x cb blocks of one matrix, read with
 // 16-byte loads (consecutive lanes on consecutive bytes of a row) and staged
-// in a wave-private LDS buffer whose rows are decode_chunk_rstride() apart.
+// in a wave-private LDS buffer whose rows are rs bytes apart.
 // ---------------------------------------------------------------------------
 struct Chunk {
     u32x4 r[DEC_MAX_LD];
 };
 
 // Per-lane byte offsets of a chunk's pieces: in global memory (from the first
-// row's segment start) and in the LDS buffer (-1: no piece for this lane).
+// row's segment start) and in the LDS buffer (-1: no piece for this lane; its
+// load re-reads the lane's first piece, so every lane issues the same fixed
+// sequence of loads and the waits on them can be counted).
 struct ChunkMap {
     int g[DEC_MAX_LD];
     int l[DEC_MAX_LD];
 };
 
-__device__ __forceinline__ void chunk_map(ChunkMap &m, int seg, int row_bytes, int lane) {
-    const int per_row = seg >> 4;  // 16-byte pieces per row segment (<= 36)
-    const int rs = decode_chunk_rstride(seg);
-    const uint32_t inv = 65536u / (uint32_t)per_row + 1u;  // j / per_row exactly for j < 1024, per_row <= 42
+// per_row: 16-byte pieces per row segment (7..36); inv = 65536 / per_row + 1
+// (j / per_row exactly for the j < 576 used here); rs: LDS row stride.
+__device__ __forceinline__ void chunk_map(ChunkMap &m, int per_row, uint32_t inv, int rs, int row_bytes, int lane) {
 #pragma unroll
     for (int u = 0; u < DEC_MAX_LD; ++u) {
         const int j = lane + 64 * u;
         const int r = (int)(((uint32_t)j * inv) >> 16);
         const int col = j - r * per_row;
-        m.g[u] = r * row_bytes + col * 16;
-        m.l[u] = j < 16 * per_row ? r * rs + col * 16 : -1;
+        const bool ok = j < 16 * per_row;
+        m.g[u] = ok ? r * row_bytes + col * 16 : m.g[0];
+        m.l[u] = ok ? r * rs + col * 16 : -1;
     }
 }
 
 __device__ __forceinline__ void chunk_load(Chunk &c, const uint8_t *base, const ChunkMap &m) {
 #pragma unroll
-    for (int u = 0; u < DEC_MAX_LD; ++u)
-        if (m.l[u] >= 0) c.r[u] = *(const u32x4 *)(base + m.g[u]);
+    for (int u = 0; u < DEC_MAX_LD; ++u) c.r[u] = *(const u32x4 *)(base + m.g[u]);
 }
 
 __device__ __forceinline__ void chunk_store(const Chunk &c, uint8_t *buf, const ChunkMap &m) {
@@ -347,6 +358,75 @@ __device__ __forceinline__ void chunk_mma(float4v &acc, const uint8_t *buf, int 
     }
 }
 
+// ---------------------------------------------------------------------------
+// Activation k-groups: the 8 values of (token t, block b, k-group g) that one
+// MFMA lane of k-group g feeds, i.e. the block's weights at pos_in_block(g, e)
+// e = 0..7.  4-bit: elements 4g+0..3 and 16+4g+0..3 (two loads); 3-bit:
+// elements 2g+{0,1} + {0, 8, 16, 24} (four loads).  The value of slot e is
+// loaded value xslot(e) of the group.
+// ---------------------------------------------------------------------------
+template <int BITS>
+__host__ __device__ constexpr int xslot(int e) {
+    // pos_in_block(BITS, 0, e) -> its index among the loaded elements
+    return BITS == 4 ? (pos_in_block(4, 0, e) < 16 ? pos_in_block(4, 0, e) : pos_in_block(4, 0, e) - 12)
+                     : 2 * (pos_in_block(3, 0, e) >> 3) + (pos_in_block(3, 0, e) & 1);
+}
+
+template <int BITS, int XPARTS>
+struct XGroup {
+    uint32_t w[4 * XPARTS];  // bf16: 8 values in 4 dwords; fp32: 8 dwords
+    // row: the token's activations; base: element index 4g (4-bit) or 2g (3-bit) of block b
+    __device__ __forceinline__ void load(const void *row, int base) {
+        if constexpr (BITS == 4) {
+            if constexpr (XPARTS == 1) {
+                const uint2 a = *(const uint2 *)((const uint16_t *)row + base);
+                const uint2 b = *(const uint2 *)((const uint16_t *)row + base + 16);
+                w[0] = a.x; w[1] = a.y; w[2] = b.x; w[3] = b.y;
+            } else {
+                const u32x4 a = *(const u32x4 *)((const float *)row + base);
+                const u32x4 b = *(const u32x4 *)((const float *)row + base + 16);
+                w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+                w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+            }
+        } else {
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                if constexpr (XPARTS == 1) {
+                    w[f] = *(const uint32_t *)((const uint16_t *)row + base + 8 * f);
+                } else {
+                    const uint2 a = *(const uint2 *)((const float *)row + base + 8 * f);
+                    w[2 * f] = a.x;
+                    w[2 * f + 1] = a.y;
+                }
+            }
+        }
+    }
+    // loaded value s (0..7) as fp32
+    __device__ __forceinline__ float val(int s) const {
+        if constexpr (XPARTS == 1) return __builtin_bit_cast(float, (w[s >> 1] >> (16 * (s & 1))) << 16);
+        else return __builtin_bit_cast(float, w[s]);
+    }
+    __device__ __forceinline__ float absmax() const {
+        float m = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) m = fmaxf(m, fabsf(val(s)));
+        return m;
+    }
+    // fp16 hi [and lo] of value * scale in slot order e = 0..7
+    __device__ __forceinline__ void convert(float scale, u32x4 &hi, u32x4 &lo) const {
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            const float v0 = val(xslot<BITS>(2 * e2)) * scale, v1 = val(xslot<BITS>(2 * e2 + 1)) * scale;
+            const _Float16 a0 = (_Float16)v0, a1 = (_Float16)v1;
+            h[e2] = __builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
+            l[e2] = f2h_bits(v0 - (float)a0) | ((uint32_t)f2h_bits(v1 - (float)a1) << 16);
+        }
+        hi = u32x4{h[0], h[1], h[2], h[3]};
+        lo = u32x4{l[0], l[1], l[2], l[3]};
+    }
+};
+
 __device__ __forceinline__ void wave_lds_handoff() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -380,109 +460,198 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
     uint8_t *s_xa = smem + P.lds_xa;
     uint8_t *s_chunk = smem + P.lds_chunk + wave * P.chunk_stride;
 
-    // ---- gate/up geometry: a unit is 16 feature rows x one K chunk of one
-    // matrix (one wave); a task is the 8 (or 16) units that complete whole
-    // 16-feature groups (one workgroup)
+    // ---- gate/up geometry (host-computed): a unit is 16 feature rows x one K
+    // chunk of one matrix (one wave); a task is the 8 (or 16) units that
+    // complete whole 16-feature groups (one workgroup)
     constexpr int bb = BITS == 4 ? 18 : 14;
-    const int nkbH = H >> 5;
-    const int cbH = P.cbH, nchH = nkbH / cbH, segH = cbH * bb;
-    const int rowH = nkbH * bb;
-    const int rsH = decode_chunk_rstride(segH);
+    const int cbH = P.cbH, segH = P.segH, rowH = P.rowH, rsH = P.rsH;
+    const int lg_nchH = P.lg_nchH, lg_upt = P.lg_upt, lg_nfgT = P.lg_nfgT, rounds = P.rounds;
+    const int nchH = 1 << lg_nchH, upt = 1 << lg_upt, nfgT = 1 << lg_nfgT;
     const int F = P.F, Fs = has_shared ? P.Fs : 0;
     const size_t eb = (size_t)3 * F * rowH;  // routed expert blob bytes
-    const int upt = 2 * nchH;                 // units per 16-feature group: (gate, up) x K chunks
-    const int nfgT = upt >= 8 ? 1 : 8 / upt;  // 16-feature groups per task
-    const int rounds = upt > 8 ? upt / 8 : 1;
-    const int tasks_sh = Fs / (16 * nfgT), tasks_rt = F / (16 * nfgT);
+    const int tasks_sh = has_shared ? P.tasks_sh : 0, tasks_rt = P.tasks_rt;
     const int n_lane = lane & 15, g_lane = lane >> 4;
 
+    // token of pair p (p / k; the reciprocal does not cover k = 1)
+    auto div_k = [&](int p) { return k == 1 ? p : (int)__umulhi((uint32_t)p, P.m_k); };
     ChunkMap mapH;
-    chunk_map(mapH, segH, rowH, lane);
-    // this wave's chunk of unit (task, round)
-    auto unit_rows = [&](int task, int rho) -> const uint8_t * {
-        int Fx, tl;
-        const uint8_t *blob;
+    chunk_map(mapH, P.perH, P.invH, rsH, rowH, lane);
+    // task -> (slot, index of the task within its slot)
+    auto task_slot = [&](int task, int &tl) {
         if (task < tasks_sh) {
             tl = task;
-            Fx = Fs;
-            blob = P.w_shared;
-        } else {
-            const int v = task - tasks_sh, si = v / tasks_rt;
-            tl = v - si * tasks_rt;
-            Fx = F;
-            blob = P.w_routed + (size_t)s_slot_exp[hs + si] * eb;
+            return 0;
         }
+        const int v = task - tasks_sh, si = (int)__umulhi((uint32_t)v, P.m_tasks_rt);
+        tl = v - si * tasks_rt;
+        return hs + si;
+    };
+    // this wave's chunk of unit (task, round)
+    auto unit_rows = [&](int task, int rho) -> const uint8_t * {
+        int tl;
+        const int s = task_slot(task, tl);
+        const bool sh = task < tasks_sh;
+        const int Fx = sh ? Fs : F;
+        const uint8_t *blob = sh ? P.w_shared : P.w_routed + (size_t)s_slot_exp[s] * eb;
         const int ui = rho * 8 + wave;
-        const int fl = ui / upt, rem = ui - fl * upt;
-        const int mat = rem / nchH, kc = rem - mat * nchH;
-        return blob + (size_t)mat * Fx * rowH + (size_t)(tl * nfgT + fl) * 16 * rowH + (size_t)kc * segH;
+        const int fl = ui >> lg_upt, rem = ui & (upt - 1);
+        const int mat = rem >> lg_nchH, kc = rem & (nchH - 1);
+        return blob + (size_t)mat * Fx * rowH + (size_t)((tl << lg_nfgT) + fl) * 16 * rowH + (size_t)kc * segH;
     };
 
     TRACE_INIT;
     TRACE(0);
-    // Routing: row t by wave DEC_WAVES-1 - t % DEC_WAVES.  For small windows
-    // those waves hold no activation blocks, and a routing wave issues its
-    // logits load before any other: waits on loads are in issue order, so
-    // the routing waits for the logits only.
-    // The call's tag is the first load of every wave; it is read into a scalar
-    // register after the routing barrier, when it has landed: waits on loads
-    // are in issue order, so reading it later would wait for every weight
-    // load issued in between.
+    // ======================= Phase A: routing, activations, grouping =======================
+    // Waits on loads are in issue order, so each wave issues first what it
+    // needs first: the call's tag (see DecodeParams), then (routing waves) the
+    // logits, then the activation groups, then the first weight chunk.
     const uint32_t tag_v = ld_dev_u32(P.epoch);
     const bool route_mode = (P.mode & DEC_MODE_ROUTE) != 0;
-    const int route_w = DEC_WAVES - 1 - wave;
+    const int route_w = DEC_WAVES - 1 - wave;  // routing: row t by wave DEC_WAVES-1 - t % DEC_WAVES
     const bool routes = route_mode && route_w < T;
-
-    // A first unit of the shared expert depends on no routing: it starts
-    // streaming now (in a routing wave, right after its routing).
-    Chunk c;
-    bool pref = false;
-    const bool shared_first = (int)blockIdx.x < tasks_sh;
-    if (shared_first && !routes) {
-        TRACEW(0);
-        chunk_load(c, unit_rows(blockIdx.x, 0), mapH);
-        pref = true;
-    }
-
-    // ======================= Phase A: routing, activations, grouping =======================
     for (int i = tid; i < T; i += DEC_THREADS) s_xmax[i] = 0u;
     if (route_mode)
         for (int e = tid; e <= E; e += DEC_THREADS) s_hist[e] = 0;  // token masks
-    TRACEW(6);
-    if (routes) {
-        const int epl = (E + 63) >> 6;
-        for (int t = route_w; t < T; t += DEC_WAVES) {
-            const float *row = P.logits + (size_t)t * E;
-            if (epl <= 2) route_row<2>(row, E, k, s_idx + t * k, s_w + t * k, lane);
-            else if (epl <= 4) route_row<4>(row, E, k, s_idx + t * k, s_w + t * k, lane);
-            else if (epl <= 8) route_row<8>(row, E, k, s_idx + t * k, s_w + t * k, lane);
-            else route_row<16>(row, E, k, s_idx + t * k, s_w + t * k, lane);
-        }
-        TRACEW(7);
-        if (shared_first) {
-            chunk_load(c, unit_rows(blockIdx.x, 0), mapH);
-            pref = true;
-        }
-    }
-    TRACE(1);
+    __syncthreads();
 
-    // activation blocks: thread owns blocks tid + 512 q (token t, block b)
-    constexpr int QX = XPARTS == 1 ? DEC_X_BLOCKS_PER_THREAD : DEC_X_BLOCKS_PER_THREAD / 2;
-    constexpr int NV = XPARTS == 1 ? 4 : 8;  // 16-byte pieces per block (bf16: 64 B, fp32: 128 B)
-    u32x4 xr[QX][NV];
-    const int nxb = T * nkbH;
+    // activation k-groups of this thread: group ((tid - 64) mod 512) + 512 q,
+    // so a one-row window leaves waves 0 and 7 (grouping, routing) without any
+    constexpr int XG = XPARTS == 1 ? DEC_XG_BF16 : DEC_XG_F32;
+    const int ngrp_x = T * P.xgrp;
+    const int nq = (ngrp_x + DEC_THREADS - 1) / DEC_THREADS;
+    XGroup<BITS, XPARTS> xg[XG];
+    int xg_t[XG], xg_pos[XG];  // token, (4b + g) of each group (-1: none)
+    auto issue_x = [&]() {
 #pragma unroll
-    for (int q = 0; q < QX; ++q) {
-        const int j = tid + DEC_THREADS * q;
-        if (j < nxb) {
-            const u32x4 *src = (const u32x4 *)((const uint8_t *)P.x + (size_t)j * 32 * (XPARTS == 1 ? 2 : 4));
-#pragma unroll
-            for (int v = 0; v < NV; ++v) xr[q][v] = src[v];
+        for (int q = 0; q < XG; ++q) {
+            if (q < nq) {
+                const int grp = ((tid + DEC_THREADS - 64) & (DEC_THREADS - 1)) + DEC_THREADS * q;
+                const bool ok = grp < ngrp_x;
+                const int gc = ok ? grp : 0;  // (an in-bounds load for lanes without a group)
+                const int t = (int)__umulhi((uint32_t)gc, P.m_xgrp);
+                const int rem = gc - t * P.xgrp;  // 4 b + g
+                const int base = (rem >> 2) * 32 + (BITS == 4 ? 4 : 2) * (rem & 3);
+                xg[q].load((const uint8_t *)P.x + (size_t)t * H * (XPARTS == 1 ? 2 : 4), base);
+                xg_t[q] = ok ? t : -1;
+                xg_pos[q] = rem;
+            }
         }
+    };
+
+    Chunk c;
+    bool pref = false;
+    const bool shared_first = (int)blockIdx.x < tasks_sh;  // its first unit depends on no routing
+    // routing by ranks (small T*E): every thread takes part; the keys and the
+    // selected logits sit in the chunk buffers, unused until the gate/up phase
+    const bool rank_mode = route_mode && P.route_rank;
+    const int nkeys = T * E;
+    uint32_t *s_keys = (uint32_t *)(smem + P.lds_chunk);
+    float *s_lg = (float *)(smem + P.lds_chunk + (size_t)nkeys * 4);
+    TRACEW(6);
+    if (rank_mode) {
+        constexpr int NL = DEC_RANK_MAX_KEYS / DEC_THREADS;
+        const int nl = (nkeys + DEC_THREADS - 1) / DEC_THREADS;
+        float lv[NL];
+#pragma unroll
+        for (int r = 0; r < NL; ++r)
+            if (r < nl) lv[r] = P.logits[tid + DEC_THREADS * r < nkeys ? tid + DEC_THREADS * r : 0];
+        issue_x();
+#pragma unroll
+        for (int r = 0; r < NL; ++r)
+            if (r < nl && tid + DEC_THREADS * r < nkeys) s_keys[tid + DEC_THREADS * r] = float_key(lv[r]);
+    } else if (routes) {
+        const int epl = (E + 63) >> 6;
+        auto route_wave = [&](auto epl_c) {
+            constexpr int EPL = decltype(epl_c)::value;
+            uint32_t key[EPL];
+            route_keys<EPL>(P.logits + (size_t)route_w * E, E, lane, key);
+            issue_x();
+            route_pick<EPL>(key, k, s_idx + route_w * k, s_w + route_w * k, lane);
+            for (int t = route_w + DEC_WAVES; t < T; t += DEC_WAVES) {
+                route_keys<EPL>(P.logits + (size_t)t * E, E, lane, key);
+                route_pick<EPL>(key, k, s_idx + t * k, s_w + t * k, lane);
+            }
+        };
+        if (epl <= 2) route_wave(std::integral_constant<int, 2>{});
+        else if (epl <= 4) route_wave(std::integral_constant<int, 4>{});
+        else if (epl <= 8) route_wave(std::integral_constant<int, 8>{});
+        else route_wave(std::integral_constant<int, 16>{});
+        TRACEW(7);
+    } else {
+        issue_x();
     }
-    __syncthreads();  // routing complete
+    if (shared_first) {
+        chunk_load(c, unit_rows(blockIdx.x, 0), mapH);
+        pref = true;
+    }
+    // per-token max |x| (the wait covers the tag, logits and activation loads)
+#pragma unroll
+    for (int q = 0; q < XG; ++q)
+        if (q < nq && xg_t[q] >= 0) atomicMax(&s_xmax[xg_t[q]], __builtin_bit_cast(uint32_t, xg[q].absmax()));
+    TRACEW(8);
+    __syncthreads();  // routing and the token maxima complete
     const uint32_t tag = decode_tag(__builtin_amdgcn_readfirstlane(tag_v));  // this call's tag (see DecodeParams)
     TRACE(9);
+    if (rank_mode) {
+        // rank of logit (t, e) in its row: keys above it, plus equal keys of a
+        // lower id (so an equal logit goes to the lower id); 2^lg_tpi threads
+        // per logit, each over a contiguous part of the row, summed by DPP
+        const int lg_tpi = P.lg_tpi, tpi = 1 << lg_tpi;
+        const int per = E >> lg_tpi, sub = tid & (tpi - 1), j0 = sub * per;
+        for (int item = tid >> lg_tpi; item < nkeys; item += DEC_THREADS >> lg_tpi) {
+            const int t = (int)__umulhi((uint32_t)item, P.m_E), e = item - t * E;
+            const uint32_t key = s_keys[item];
+            const uint32_t *row = s_keys + t * E + j0;
+            int cnt = 0;
+            for (int j = 0; j < per; j += 4) {
+                const u32x4 kv = *(const u32x4 *)(row + j);
+                const int jj = j0 + j;
+                cnt += (kv.x > key) + (kv.y > key) + (kv.z > key) + (kv.w > key);
+                cnt += (kv.x == key && jj < e) + (kv.y == key && jj + 1 < e) + (kv.z == key && jj + 2 < e) +
+                       (kv.w == key && jj + 3 < e);
+            }
+            if (tpi >= 2) cnt += __builtin_amdgcn_update_dpp(0, cnt, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+            if (tpi >= 4) cnt += __builtin_amdgcn_update_dpp(0, cnt, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+            if (tpi >= 8) cnt += __builtin_amdgcn_update_dpp(0, cnt, 0x141, 0xF, 0xF, false);  // row_half_mirror
+            if (tpi >= 16) cnt += __builtin_amdgcn_update_dpp(0, cnt, 0x140, 0xF, 0xF, false); // row_mirror
+            if (sub == 0 && cnt < k) {
+                s_idx[t * k + cnt] = e;
+                s_lg[t * k + cnt] = __builtin_bit_cast(float, (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+            }
+        }
+        __syncthreads();
+        // softmax over the k selected logits of the row (sum in slot order)
+        for (int p = tid; p < TK; p += DEC_THREADS) {
+            const int t = div_k(p);
+            const float *lr = s_lg + t * k;
+            const float l0 = lr[0];
+            float sum = 0.0f;
+            for (int j = 0; j < k; ++j) sum += expf(lr[j] - l0);
+            s_w[p] = expf(s_lg[p] - l0) / sum;
+        }
+    }
+
+    // Activations to fp16 (hi [+ lo]) of x * 2^sc_t in the format's k order:
+    // part p, token t, block b, k-group g at p*T*x_rs + t*x_rs + (4b+g)*16.
+    auto stage_x = [&]() {
+#pragma unroll
+        for (int q = 0; q < XG; ++q) {
+            if (q < nq && xg_t[q] >= 0) {
+                const int t = xg_t[q];
+                const float mx = __builtin_bit_cast(float, s_xmax[t]);
+                int ex = 0;
+                if (mx > 0.0f) frexpf(mx, &ex);
+                const int sc = mx > 0.0f ? 14 - ex : 0;  // max * 2^sc in [2^13, 2^14)
+                const float scale = __builtin_bit_cast(float, (uint32_t)(127 + sc) << 23);  // 2^sc, exact
+                if (xg_pos[q] == 0) s_tinv[t] = __builtin_bit_cast(float, (uint32_t)(127 - sc) << 23);
+                u32x4 hi, lo;
+                xg[q].convert(scale, hi, lo);
+                uint8_t *dst = s_xa + (size_t)t * P.x_rs + (size_t)xg_pos[q] * 16;
+                *(u32x4 *)dst = hi;
+                if (XPARTS == 2) *(u32x4 *)(dst + (size_t)T * P.x_rs) = lo;
+            }
+        }
+    };
 
     // grouping of the pairs by expert: slots in ascending expert id, pairs of
     // a slot in (token, slot) order.  A token's k experts are distinct, so an
@@ -491,7 +660,8 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
     if (route_mode) {
         uint32_t *s_tmask = (uint32_t *)s_hist;  // [E] tokens that chose expert e
         int *s_start = s_sorted + TK;            // [E] first position of expert e
-        for (int p = tid; p < TK; p += DEC_THREADS) atomicOr(&s_tmask[s_idx[p]], 1u << (p / k));
+        for (int p = tid; p < TK; p += DEC_THREADS)
+            atomicOr(&s_tmask[s_idx[p]], 1u << div_k(p));
         __syncthreads();
         if (wave == 0) {
             // exclusive scan of (count | active flag << 16) over the experts
@@ -523,9 +693,10 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             }
             if (lane == 63) s_misc[0] = hs + (incl >> 16);  // number of slots
         }
+        stage_x();  // (wave 0 after its scan; it holds groups only for windows of 2+ rows)
         __syncthreads();
         for (int p = tid; p < TK; p += DEC_THREADS) {
-            const int e = s_idx[p], t = p / k;
+            const int e = s_idx[p], t = div_k(p);
             s_sorted[s_start[e] + __popc(s_tmask[e] & ((1u << t) - 1u))] = p;
         }
         if (blockIdx.x == 0) {
@@ -546,6 +717,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             }
             s_misc[0] = hs + na;
         }
+        stage_x();
         __syncthreads();
         const int na = s_misc[0] - hs;
         for (int a = tid; a < na; a += DEC_THREADS) {
@@ -580,33 +752,38 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         s_slot_start[0] = 0;
         s_slot_cnt[0] = T;
     }
-    __syncthreads();  // slot tables complete
+    __syncthreads();  // slot tables and staged activations complete
     TRACE(13);
     const int n_slots = s_misc[0];
     const int n_tasks = tasks_sh + (n_slots - hs) * tasks_rt;
 
     // Down tiles (slot, 128 output rows) continue the round robin of the
     // gate/up tasks over the workgroups: tile i is work item n_tasks + i.
-    const int tiles_per_slot = H / DEC_DN_ROWS;
+    const int tiles_per_slot = P.tps;
     const int n_tiles = n_slots * tiles_per_slot;
     const int first_tile = (int)(((long long)blockIdx.x - n_tasks % G + G) % G);
     struct Tile {
         const uint8_t *rows;  // this wave's 16 down rows
-        int s, rg, Fx, cbF, nchF, segF, rowF;
+        int s, rg, Fx, cbF, nchF, segF, rowF, rsF, perF;
+        uint32_t invF, m_ngrp;
         bool shared;
     };
     auto tile_of = [&](int ti) {
         Tile t;
-        t.s = ti / tiles_per_slot;
+        t.s = (int)__umulhi((uint32_t)ti, P.m_tps);
         t.rg = ti - t.s * tiles_per_slot;
         t.shared = s_slot_exp[t.s] < 0;
-        t.Fx = t.shared ? Fs : F;
+        const int i = t.shared ? 1 : 0;
+        t.Fx = i ? P.fx[1] : P.fx[0];
+        t.cbF = i ? P.cbF[1] : P.cbF[0];
+        t.nchF = i ? P.nchF[1] : P.nchF[0];
+        t.segF = i ? P.segF[1] : P.segF[0];
+        t.rowF = i ? P.rowF[1] : P.rowF[0];
+        t.rsF = i ? P.rsF[1] : P.rsF[0];
+        t.perF = i ? P.perF[1] : P.perF[0];
+        t.invF = i ? P.invF[1] : P.invF[0];
+        t.m_ngrp = i ? P.m_ngrp[1] : P.m_ngrp[0];
         const uint8_t *blob = t.shared ? P.w_shared : P.w_routed + (size_t)s_slot_exp[t.s] * eb;
-        const int nkbF = t.Fx >> 5;
-        t.cbF = decode_f_chunk_blocks(nkbF);
-        t.nchF = nkbF / t.cbF;
-        t.segF = t.cbF * bb;
-        t.rowF = nkbF * bb;
         t.rows = blob + (size_t)2 * t.Fx * rowH + (size_t)(t.rg * DEC_DN_ROWS + wave * 16) * t.rowF;
         return t;
     };
@@ -618,118 +795,32 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
     auto prefetch_first_tile = [&]() {
         if (first_tile < n_tiles) {
             const Tile t = tile_of(first_tile);
-            chunk_map(mapF, t.segF, t.rowF, lane);
+            chunk_map(mapF, t.perF, t.invF, t.rsF, t.rowF, lane);
             map_fx = t.Fx;
             chunk_load(c, t.rows, mapF);
             c_holds_tile = true;
         }
     };
-    // per-token max |x|, before this wave issues any weight load after its
-    // activation loads (so the wait covers the activations only)
-#pragma unroll
-    for (int q = 0; q < QX; ++q) {
-        const int j = tid + DEC_THREADS * q;
-        if (j < nxb) {
-            float mx = 0.0f;
-#pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const uint32_t w4[4] = {xr[q][v].x, xr[q][v].y, xr[q][v].z, xr[q][v].w};
-#pragma unroll
-                for (int c2 = 0; c2 < 4; ++c2) {
-                    if (XPARTS == 1) {
-                        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w4[c2] << 16)));
-                        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w4[c2] & 0xFFFF0000u)));
-                    } else {
-                        mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, w4[c2])));
-                    }
-                }
-            }
-            atomicMax(&s_xmax[j / nkbH], __builtin_bit_cast(uint32_t, mx));
-        }
-    }
-    TRACEW(8);
     if (!pref) {
-        if ((int)blockIdx.x < n_tasks) {
-            TRACEW(0);
-            chunk_load(c, unit_rows(blockIdx.x, 0), mapH);
-        } else {
-            prefetch_first_tile();
-        }
+        TRACEW(0);
+        if ((int)blockIdx.x < n_tasks) chunk_load(c, unit_rows(blockIdx.x, 0), mapH);
+        else prefetch_first_tile();
     }
-
     TRACEW(9);
-    __syncthreads();
-    TRACE(14);
-    // activations to fp16 (hi [+ lo]) of x * 2^sc_t in the format's k order:
-    // part p, token t, block b, k-group g at p*T*x_rs + t*x_rs + (4b+g)*16
-#pragma unroll
-    for (int q = 0; q < QX; ++q) {
-        const int j = tid + DEC_THREADS * q;
-        if (j < nxb) {
-            const int t = j / nkbH, b = j - t * nkbH;
-            const float mx = __builtin_bit_cast(float, s_xmax[t]);
-            int ex = 0;
-            if (mx > 0.0f) frexpf(mx, &ex);
-            const int sc = mx > 0.0f ? 14 - ex : 0;  // max * 2^sc in [2^13, 2^14)
-            const float scale = __builtin_bit_cast(float, (uint32_t)(127 + sc) << 23);  // 2^sc, exact
-            if (b == 0) s_tinv[t] = __builtin_bit_cast(float, (uint32_t)(127 - sc) << 23);
-            uint32_t w[NV * 4];
-#pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                w[4 * v] = xr[q][v].x;
-                w[4 * v + 1] = xr[q][v].y;
-                w[4 * v + 2] = xr[q][v].z;
-                w[4 * v + 3] = xr[q][v].w;
-            }
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                uint32_t hv[4], lv[4];
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    uint16_t hb2[2], lb2[2];
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        const int pos = pos_in_block(BITS, g, 2 * e2 + h2);
-                        float xv;
-                        if (XPARTS == 1) xv = __builtin_bit_cast(float, (w[pos >> 1] >> (16 * (pos & 1))) << 16);
-                        else xv = __builtin_bit_cast(float, w[pos]);
-                        xv *= scale;
-                        const _Float16 hh = (_Float16)xv;
-                        hb2[h2] = __builtin_bit_cast(uint16_t, hh);
-                        lb2[h2] = f2h_bits(xv - (float)hh);
-                    }
-                    hv[e2] = hb2[0] | ((uint32_t)hb2[1] << 16);
-                    lv[e2] = lb2[0] | ((uint32_t)lb2[1] << 16);
-                }
-                uint8_t *dst = s_xa + (size_t)t * P.x_rs + (size_t)(4 * b + g) * 16;
-                *(u32x4 *)dst = u32x4{hv[0], hv[1], hv[2], hv[3]};
-                if (XPARTS == 2) *(u32x4 *)(dst + (size_t)T * P.x_rs) = u32x4{lv[0], lv[1], lv[2], lv[3]};
-            }
-        }
-    }
-    __syncthreads();
     TRACE(2);
 
     // ======================= Phase B: gate/up tasks =======================
     bool first_task = true;
     for (int task = blockIdx.x; task < n_tasks; task += G) {
-        int s, tl;
-        if (task < tasks_sh) {
-            s = 0;
-            tl = task;
-        } else {
-            const int v = task - tasks_sh, si = v / tasks_rt;
-            s = hs + si;
-            tl = v - si * tasks_rt;
-        }
+        int tl;
+        const int s = task_slot(task, tl);
         const int n_tok = s_slot_cnt[s];
         const bool shared_slot = s_slot_exp[s] < 0;
         const int mrow = n_lane < n_tok ? n_lane : 0;  // A row of this lane (rows past n_tok: any valid row)
-        const int tok = shared_slot ? mrow : s_sorted[s_slot_start[s] + mrow] / k;
+        const int tok = shared_slot ? mrow : div_k(s_sorted[s_slot_start[s] + mrow]);
         float4v accr[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         for (int rho = 0; rho < rounds; ++rho) {
-            const int ui = rho * 8 + wave;
-            const int kc = (ui % upt) % nchH;
+            const int kc = (rho * 8 + wave) & (nchH - 1);
             __builtin_amdgcn_wave_barrier();
             chunk_store(c, s_chunk, mapH);
             if (first_task && rho == 0) TRACEW(1);
@@ -765,21 +856,20 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         // in order 0, 1, ...; back in the units of x; stored as tagged words in
         // the down projection's k order.  The count goes up without waiting for
         // the stores: a reader checks each word's tag.
-        const int per_fl = n_tok * 16;
-        for (int i = tid; i < nfgT * per_fl; i += DEC_THREADS) {
-            const int fl = i / per_fl, rem = i - fl * per_fl;
-            const int m = rem >> 4, n = rem & 15;
+        for (int i = tid; i < nfgT * 256; i += DEC_THREADS) {
+            const int fl = i >> 8, m = (i >> 4) & 15, n = i & 15;
+            if (m >= n_tok) continue;
             float gs = 0.0f, us = 0.0f;
             for (int kc = 0; kc < nchH; ++kc) {
                 const int ug = fl * upt + kc, uu = ug + nchH;
                 gs += *(const float *)(smem + P.lds_chunk + (ug & 7) * P.chunk_stride + ((ug >> 3) * 256 + m * 16 + n) * 4);
                 us += *(const float *)(smem + P.lds_chunk + (uu & 7) * P.chunk_stride + ((uu >> 3) * 256 + m * 16 + n) * 4);
             }
-            const int tk = shared_slot ? m : s_sorted[s_slot_start[s] + m] / k;
+            const int tk = shared_slot ? m : div_k(s_sorted[s_slot_start[s] + m]);
             const float ti = s_tinv[tk];
             const float gv = gs * ti, uv = us * ti;
             const float h = gv / (1.0f + expf(-gv)) * uv;
-            const int f = (tl * nfgT + fl) * 16 + n;
+            const int f = ((tl << lg_nfgT) + fl) * 16 + n;
             int pg, pe;
             group_slot_of(BITS, f & 31, pg, pe);
             const int fo = (f >> 5) * 32 + pg * 8 + pe;
@@ -799,11 +889,10 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         const Tile tl = tile_of(ti);
         const int s = tl.s, rg = tl.rg, Fx = tl.Fx;
         const bool shared_slot = tl.shared;
-        const int cbF = tl.cbF, nchF = tl.nchF, segF = tl.segF;
-        const int rsF = decode_chunk_rstride(segF);
+        const int cbF = tl.cbF, nchF = tl.nchF, segF = tl.segF, rsF = tl.rsF;
         const uint8_t *rows_d = tl.rows;
         if (Fx != map_fx) {
-            chunk_map(mapF, segF, tl.rowF, lane);
+            chunk_map(mapF, tl.perF, tl.invF, rsF, tl.rowF, lane);
             map_fx = Fx;
         }
         const int n_tok = s_slot_cnt[s];
@@ -814,7 +903,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             __syncthreads();  // previous tile's readers of the staged h are done
             if (ti == first_tile) TRACE(4);
             if (tid == 0) {
-                const uint32_t need = (uint32_t)(Fx / (16 * nfgT));
+                const uint32_t need = (uint32_t)(Fx >> (4 + lg_nfgT));
                 uint32_t spins = 0;
                 while (ld_dev_u32(&P.gu_count[s * DEC_CSTRIDE]) < need) {
                     __builtin_amdgcn_s_sleep(2);
@@ -836,7 +925,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             for (int q = 0; q < 4; ++q) {
                 const int it = tid + DEC_THREADS * q;
                 if (it < nit) {
-                    const int m = it / ngrp, gi = it - m * ngrp;
+                    const int m = (int)__umulhi((uint32_t)it, tl.m_ngrp), gi = it - m * ngrp;
                     const uint64_t *src = P.hll + (size_t)(row0 + m) * P.h_stride + gi * 8;
                     uint64_t wd[8];
                     for (uint32_t spins = 0;; ++spins) {  // until every word carries this call's tag
@@ -867,7 +956,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             for (int q = 0; q < 4; ++q) {
                 const int it = tid + DEC_THREADS * q;
                 if (it < nit) {
-                    const int m = it / ngrp, gi = it - m * ngrp;
+                    const int m = (int)__umulhi((uint32_t)it, tl.m_ngrp), gi = it - m * ngrp;
                     const float mx = __builtin_bit_cast(float, s_xmax[m]);
                     int ex = 0;
                     if (mx > 0.0f) frexpf(mx, &ex);

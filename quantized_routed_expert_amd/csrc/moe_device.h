@@ -31,7 +31,7 @@ __device__ __forceinline__ int block_bytes(int bits) { return bits == 4 ? 18 : 1
 // pos_in_block(bits, g, e): which of the block's 32 weights is the e-th value
 // a lane of k-group g feeds.  Used to lay activations out to match.
 // ---------------------------------------------------------------------------
-__host__ __device__ __forceinline__ int pos_in_block(int bits, int g, int e) {
+__host__ __device__ constexpr int pos_in_block(int bits, int g, int e) {
     if (bits == 4) {
         // e: 0:(4g) 1:(4g+2) 2:(16+4g) 3:(16+4g+2) 4:(4g+1) 5:(4g+3) 6:(16+4g+1) 7:(16+4g+3)
         int r = ((e >> 2) & 1) + ((e & 1) << 1);

@@ -16,9 +16,12 @@ constexpr int DEC_CB_MAX = 32;               // quant blocks per row in one stre
 constexpr int DEC_MAX_LD = 9;                // 16-byte loads per lane per chunk (16 rows x 32 x 18 B)
 constexpr int DEC_MAX_E_FUSED = 1024;        // router fused into the kernel up to this many experts
 constexpr int DEC_MAX_F = 1024;              // expert FFN width handled by the fused decode launch
-constexpr int DEC_X_BLOCKS_PER_THREAD = 4;   // activation blocks staged per thread (bf16; 2 for fp32)
+constexpr int DEC_XG_BF16 = 8;              // activation k-groups (8 values) loaded per thread: bf16
+constexpr int DEC_XG_F32 = 4;               // ... fp32
 constexpr uint32_t DEC_SPIN_LIMIT = 1u << 20;  // bounded waits: a wait that runs out sets err bit 0
 constexpr int DEC_CSTRIDE = 64;              // 32-bit words between counters (one 256-byte line each)
+constexpr int DEC_RANK_MAX_KEYS = 2048;      // routing by ranks: T*E up to this ...
+constexpr int DEC_RANK_MAX_CMP = 64;         // ... and at most this many comparisons per thread
 #define MOE_MAX_EXPERTS_DEV 4096
 #define MOE_DECODE_ROWS_DEV 16  // <= 32: the fused grouping keeps a 32-bit token mask per expert
 constexpr int DEC_MAX_SLOTS = MOE_DECODE_ROWS_DEV * 32 + 1;  // T*k pairs (k <= 32) + the shared expert
@@ -31,14 +34,15 @@ constexpr int DEC_MODE_SHARED = 4;   // a shared expert is present
 
 // Quant blocks per streamed gate/up chunk for a row of nkb blocks: the K
 // chunks of a row number 1, 2, 4 or 8 (so the units of a 16-feature group
-// fill a workgroup's 8 waves exactly), each chunk an even number of blocks
-// (operands are read two blocks at a time) and at most DEC_CB_MAX.  0: no
-// such split (the fused decode launch does not take the shape).
+// fill a workgroup's 8 waves exactly, in one or two rounds), each chunk a
+// multiple of 8 blocks (so chunk segments start 16-byte aligned in both
+// formats) and at most DEC_CB_MAX.  0: no such split (the fused decode launch
+// does not take the shape).
 __host__ __device__ inline int decode_h_chunk_blocks(int nkb) {
     for (int nch = 1; nch <= 8; nch <<= 1) {
         if (nkb % nch) continue;
         const int cb = nkb / nch;
-        if (cb <= DEC_CB_MAX && (cb & 1) == 0) return cb;
+        if (cb <= DEC_CB_MAX && cb % 8 == 0) return cb;
     }
     return 0;
 }
@@ -91,9 +95,27 @@ struct DecodeParams {
     uint32_t *done;            // workgroups of this call that have finished
     int T, E, k, H, F, Fs;     // Fs = shared ffn (0 = none)
     int bits, x_f32, mode, max_slots;
-    int h_stride;              // floats per hbuf row (Fmax)
-    int cbH;                   // quant blocks per gate/up chunk
+    int h_stride;              // words per hll row (Fmax)
     int x_rs, h_rs;            // LDS bytes per token row: activations (one part), staged h (hi + lo)
+    // geometry, computed on the host (divisions by values that are not powers
+    // of two use m_* = ceil(2^32 / d): n / d = umulhi(n, m_d) for n < 2^20)
+    int nkbH, cbH, segH, rowH, rsH, perH;  // gate/up rows: blocks, blocks per chunk, chunk bytes per row,
+                                           // row bytes, LDS row stride, 16-byte pieces per chunk row
+    uint32_t invH;                         // 65536 / perH + 1
+    int lg_nchH, lg_upt, lg_nfgT, rounds;  // K chunks, units per 16-feature group, groups per task (log2)
+    int tasks_sh, tasks_rt;                // gate/up tasks of the shared expert / of a routed expert
+    uint32_t m_tasks_rt;
+    int tps;                               // down tiles per slot (H / 128)
+    uint32_t m_tps;
+    // down geometry per kind of slot: [0] routed (F), [1] shared (Fs)
+    int fx[2], cbF[2], nchF[2], segF[2], rowF[2], rsF[2], perF[2];
+    uint32_t invF[2], m_ngrp[2];           // m_ngrp: 1 / (fx / 8)
+    uint32_t m_k;                          // 1 / k
+    int xgrp;                              // activation k-groups per token (H / 8)
+    uint32_t m_xgrp;
+    // routing by ranks (all threads; small T*E): lg_tpi = log2 threads per logit
+    int route_rank, lg_tpi;
+    uint32_t m_E;
     // dynamic LDS layout (byte offsets)
     int lds_idx, lds_w, lds_sorted, lds_hist, lds_slot_start, lds_slot_exp, lds_slot_cnt,
         lds_tinv, lds_hinv, lds_xmax, lds_misc, lds_xa, lds_chunk, chunk_stride, lds_total;
