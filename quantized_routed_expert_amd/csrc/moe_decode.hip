@@ -115,46 +115,66 @@ __device__ __forceinline__ void route_keys(const float *row, int E, int lane, ui
     for (int i = 0; i < EPL; ++i) key[i] = lane + 64 * i < E ? float_key(v[i]) : 0u;  // finite values: keys > 0
 }
 
+// One selection round: the largest key (an equal key goes to the lower
+// expert id), removed from the keys; returns the expert id, sets its key.
+template <int EPL>
+__device__ __forceinline__ int route_round(uint32_t (&key)[EPL], uint32_t &m, int lane) {
+    uint32_t bk = 0;
+    int bi = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+        if (key[i] > bk) {  // strict: the lowest i wins among equal keys
+            bk = key[i];
+            bi = i;
+        }
+    m = wave_max_u32(bk);
+    const uint64_t tied = __ballot(bk == m);
+    int e;
+    if (__popcll(tied) == 1) {
+        const int wl = __ffsll((unsigned long long)tied) - 1;
+        e = wl + 64 * __builtin_amdgcn_readlane(bi, wl);
+    } else {
+        e = (int)wave_min_u32(bk == m ? (uint32_t)(lane + 64 * bi) : 0xFFFFFFFFu);
+    }
+    if ((e & 63) == lane) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (i == (e >> 6)) key[i] = 0u;
+    }
+    return e;
+}
+
+__device__ __forceinline__ float key_value(uint32_t m) {
+    return __builtin_bit_cast(float, (m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
+}
+
+// softmax over the k selected logits of one row (lane j < k holds slot j),
+// the sum taken in slot order 0, 1, ..., k-1 like every other routing path,
+// so a row's weights do not depend on which path routed it
+__device__ __forceinline__ void route_write(float mine, int mine_id, int k, int *out_idx, float *out_w, int lane) {
+    const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mine)));
+    const float ex = lane < k ? expf(mine - l0) : 0.0f;
+    float s = 0.0f;
+    for (int j = 0; j < k; ++j) s += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), j));
+    if (lane < k) {
+        out_idx[lane] = mine_id;
+        out_w[lane] = ex / s;
+    }
+}
+
 template <int EPL>
 __device__ __forceinline__ void route_pick(uint32_t (&key)[EPL], int k, int *out_idx, float *out_w, int lane) {
     float mine = 0.0f;
     int mine_id = 0;
     for (int j = 0; j < k; ++j) {
-        uint32_t bk = 0;
-        int bi = 0;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            if (key[i] > bk) {  // strict: the lowest i wins among equal keys
-                bk = key[i];
-                bi = i;
-            }
-        const uint32_t m = wave_max_u32(bk);
-        const uint64_t tied = __ballot(bk == m);
-        int e;
-        if (__popcll(tied) == 1) {
-            const int wl = __ffsll((unsigned long long)tied) - 1;
-            e = wl + 64 * __builtin_amdgcn_readlane(bi, wl);
-        } else {
-            e = (int)wave_min_u32(bk == m ? (uint32_t)(lane + 64 * bi) : 0xFFFFFFFFu);
-        }
-        if ((e & 63) == lane) {
-#pragma unroll
-            for (int i = 0; i < EPL; ++i)
-                if (i == (e >> 6)) key[i] = 0u;
-        }
-        const uint32_t u = (m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m;
+        uint32_t m;
+        const int e = route_round<EPL>(key, m, lane);
         if (lane == j) {
-            mine = __builtin_bit_cast(float, u);
+            mine = key_value(m);
             mine_id = e;
         }
     }
-    const float l0 = __shfl(mine, 0, 64);
-    const float ex = lane < k ? expf(mine - l0) : 0.0f;
-    const float s = wave_sum_f(ex);
-    if (lane < k) {
-        out_idx[lane] = mine_id;
-        out_w[lane] = ex / s;
-    }
+    route_write(mine, mine_id, k, out_idx, out_w, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -584,10 +604,21 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         chunk_load(c, unit_rows(blockIdx.x, 0), mapH);
         pref = true;
     }
-    // per-token max |x| (the wait covers the tag, logits and activation loads)
+    // per-token max |x| (the wait covers the tag, logits and activation
+    // loads); reduced over the wave first when all its lanes hold one token
+    const bool wave_tok = (P.xgrp & 63) == 0;
 #pragma unroll
-    for (int q = 0; q < XG; ++q)
-        if (q < nq && xg_t[q] >= 0) atomicMax(&s_xmax[xg_t[q]], __builtin_bit_cast(uint32_t, xg[q].absmax()));
+    for (int q = 0; q < XG; ++q) {
+        if (q < nq) {
+            const uint32_t mb = xg_t[q] >= 0 ? __builtin_bit_cast(uint32_t, xg[q].absmax()) : 0u;
+            if (wave_tok) {
+                const uint32_t wm = wave_max_u32(mb);
+                if (lane == 0 && xg_t[q] >= 0) atomicMax(&s_xmax[xg_t[q]], wm);
+            } else if (xg_t[q] >= 0) {
+                atomicMax(&s_xmax[xg_t[q]], mb);
+            }
+        }
+    }
     TRACEW(8);
     __syncthreads();  // routing and the token maxima complete
     const uint32_t tag = decode_tag(__builtin_amdgcn_readfirstlane(tag_v));  // this call's tag (see DecodeParams)

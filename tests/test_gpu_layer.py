@@ -138,13 +138,17 @@ def test_run_twice_bitwise():
 
 
 def test_batch_invariance_decode():
-    """A row's output is bitwise the same alone as inside a 16-row window."""
+    """A row's output and routing weights are bitwise the same alone as inside
+    a 16-row window (the two take different routing code: per-row waves for
+    the window, all-thread ranks for the single row)."""
     print("[layer] batch invariance", flush=True)
     li = layer_inputs("mtp16", 16)
-    y16 = DevLayer(li).forward(D)[0]
-    for t in (0, 5, 15):
+    y16, i16, w16 = DevLayer(li).forward(D)
+    for t in range(16):
         one = dataclasses.replace(li, T=1, x=li.x[t:t + 1].copy(), logits=li.logits[t:t + 1].copy())
-        y1 = DevLayer(one).forward(D)[0]
+        y1, i1, w1 = DevLayer(one).forward(D)
+        assert np.array_equal(i1[0], i16[t]), t
+        assert np.array_equal(w1[0], w16[t]), t
         assert np.array_equal(y1[0], y16[t]), t
 
 
