@@ -30,10 +30,17 @@
  *             weight = d * (code - 4).
  * A matrix [rows][cols] is stored row by row, cols/32 blocks per row, with
  * no padding.  One expert's blob is gate [F][H] | up [F][H] | down [H][F]
- * (gate, up and down concatenated per expert, thread §三: the blob fed to the
- * kernel without conversion); experts follow each other with no padding.
- * The nibble order and the whole 3-bit layout are readings of points the
- * pages leave open.
+ * (gate, up and down concatenated per expert, thread §三); experts follow
+ * each other with no padding.  This is MOE_LAYOUT_ROWS.  The nibble order
+ * and the whole 3-bit layout are readings of points the pages leave open.
+ *
+ * The compute calls read MOE_LAYOUT_PREPARED, written once per weight set by
+ * moe_prepare_qweights: the same blocks and sizes, gate and up unchanged,
+ * the down projection's blocks reordered column-block-major (block (h, c) of
+ * down, row h, FFN columns 32c..32c+31, at index c*H + h), so a 32-column
+ * slice of down for all H rows is one contiguous run.  (The thread feeds its
+ * blob to the kernel without conversion; this library converts once at load
+ * time instead, so a decode split over FFN slices streams contiguous bytes.)
  *
  * Conventions for every call:
  *  - Pointers marked (device) point to GPU memory on the current HIP device;
@@ -64,7 +71,7 @@ extern "C" {
 
 #define MOE_OK 0
 #define MOE_ERR_INVALID_ARG (-1)  /* null pointer, negative or inconsistent size */
-#define MOE_ERR_UNSUPPORTED (-2)  /* bits not 3/4, H or F not a multiple of 256, ... */
+#define MOE_ERR_UNSUPPORTED (-2)  /* bits not 3/4, H or F not a multiple of 256, weights not prepared, ... */
 #define MOE_ERR_WORKSPACE (-3)    /* workspace smaller than moe_workspace_bytes */
 #define MOE_ERR_LAUNCH (-4)       /* a kernel launch failed */
 #define MOE_ERR_DEVICE (-5)       /* no usable gfx950 device / device query failed */
@@ -87,6 +94,10 @@ extern "C" {
 #define MOE_MAX_EXPERTS 4096
 #define MOE_MAX_TOPK 32
 
+/* block orders of a weight set (see "Weight format" above) */
+#define MOE_LAYOUT_ROWS 0      /* every matrix row by row, as stored on the pages */
+#define MOE_LAYOUT_PREPARED 1  /* down column-block-major: what the compute calls read */
+
 /* Quantized expert weights (host struct; `data` is a device pointer). */
 typedef struct moe_qweights {
     const void *data;   /* (device) n_experts blobs back to back, see above */
@@ -94,6 +105,7 @@ typedef struct moe_qweights {
     int32_t n_experts;  /* routed: E; shared: 1 */
     int32_t hidden;     /* H, multiple of 256 */
     int32_t ffn;        /* F, multiple of 256 */
+    int32_t layout;     /* MOE_LAYOUT_*; the compute calls take MOE_LAYOUT_PREPARED only */
 } moe_qweights;
 
 /* Library version (major*100 + minor). */
@@ -112,6 +124,18 @@ int64_t moe_expert_bytes(int32_t bits, int32_t hidden, int32_t ffn);
  * shapes.  Pure host function. */
 int64_t moe_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t hidden, int32_t ffn,
                             int32_t shared_ffn, int32_t path);
+
+/*
+ * Weight preparation (once per weight set, before any compute call).  src
+ * (host struct) describes weights in MOE_LAYOUT_ROWS; dst (device) receives
+ * the same n_experts blobs in MOE_LAYOUT_PREPARED (src->n_experts *
+ * moe_expert_bytes(...) bytes; describe it with layout = MOE_LAYOUT_PREPARED
+ * afterwards).  src and dst must not overlap, and src must stay valid until
+ * the copy, enqueued on `stream`, has run.  Errors: MOE_ERR_INVALID_ARG for
+ * a null pointer, overlapping buffers or src->layout != MOE_LAYOUT_ROWS,
+ * MOE_ERR_UNSUPPORTED for bits or shapes the compute calls do not take.
+ */
+int moe_prepare_qweights(const moe_qweights *src, void *dst, int64_t stream);
 
 /*
  * Router (step 1).  logits (device) fp32 [T][E]; writes topk_idx (device)

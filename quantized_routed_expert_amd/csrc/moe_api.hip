@@ -26,6 +26,7 @@ namespace moe {
 hipError_t prefill_plan_launch(const PlanParams &P, hipStream_t st);
 hipError_t prefill_gemm_launch(int mode, int bits, const GemmParams &P, int grid, hipStream_t st);
 hipError_t prefill_combine_launch(const CombineParams &P, hipStream_t st);
+hipError_t prepare_launch(const uint8_t *src, uint8_t *dst, const PrepareParams &P, hipStream_t st);
 }  // namespace moe
 
 using namespace moe;
@@ -136,6 +137,7 @@ int check_shape(int32_t T, int32_t E, int32_t k, int32_t H, int32_t F) {
 int check_weights(const moe_qweights *w, int H, int n_experts) {
     if (!w || !w->data) return MOE_ERR_INVALID_ARG;
     if (w->bits != 3 && w->bits != 4) return MOE_ERR_UNSUPPORTED;
+    if (w->layout != MOE_LAYOUT_PREPARED) return MOE_ERR_UNSUPPORTED;
     if (w->hidden != H) return MOE_ERR_INVALID_ARG;
     if (n_experts >= 0 && w->n_experts != n_experts) return MOE_ERR_INVALID_ARG;
     if (w->ffn <= 0) return MOE_ERR_INVALID_ARG;
@@ -187,10 +189,12 @@ void decode_geometry(DecodeParams &P) {
         P.fx[i] = fx;
         P.cbF[i] = decode_f_chunk_blocks(nkb);
         P.nchF[i] = nkb / P.cbF[i];
-        P.segF[i] = P.cbF[i] * bb;
-        P.rowF[i] = nkb * bb;
-        P.rsF[i] = decode_chunk_rstride(P.segF[i]);
-        P.perF[i] = P.segF[i] / 16;
+        // down is column-block-major: a chunk is cbF runs of 16 rows x bb
+        // bytes (one run per 32-column block), H*bb bytes apart
+        P.segF[i] = P.cbF[i] * P.H * bb;  // bytes from one chunk to the next
+        P.rowF[i] = P.H * bb;             // bytes between the runs of a chunk
+        P.rsF[i] = decode_chunk_rstride(16 * bb);
+        P.perF[i] = bb;                   // 16-byte pieces per run
         P.invF[i] = 65536u / (uint32_t)P.perF[i] + 1u;
         P.m_ngrp[i] = magic_div(fx / 8);
     }
@@ -239,10 +243,10 @@ int decode_lds_layout(DecodeParams &P, int xparts) {
     P.lds_xa = take(xa_bytes > ha_bytes ? xa_bytes : ha_bytes);
     // wave-private chunk buffers (also the gate/up unit partials: 2 x 16 x 16 floats)
     int cmax = 16 * decode_chunk_rstride(P.cbH * bb);
-    const int cf = 16 * decode_chunk_rstride(decode_f_chunk_blocks(P.F / 32) * bb);
+    const int cf = decode_f_chunk_blocks(P.F / 32) * decode_chunk_rstride(16 * bb);
     cmax = cf > cmax ? cf : cmax;
     if (P.Fs) {
-        const int cs = 16 * decode_chunk_rstride(decode_f_chunk_blocks(P.Fs / 32) * bb);
+        const int cs = decode_f_chunk_blocks(P.Fs / 32) * decode_chunk_rstride(16 * bb);
         cmax = cs > cmax ? cs : cmax;
     }
     cmax = cmax > 2048 ? cmax : 2048;
@@ -320,6 +324,29 @@ int64_t moe_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t hidden, int
         n = n > n2 ? n : n2;
     }
     return (int64_t)n;
+}
+
+int moe_prepare_qweights(const moe_qweights *src, void *dst, int64_t stream) {
+    if (!src || !src->data || !dst) return MOE_ERR_INVALID_ARG;
+    if (src->layout != MOE_LAYOUT_ROWS) return MOE_ERR_INVALID_ARG;
+    if (src->bits != 3 && src->bits != 4) return MOE_ERR_UNSUPPORTED;
+    if (src->n_experts <= 0 || src->hidden <= 0 || src->ffn <= 0) return MOE_ERR_INVALID_ARG;
+    if (src->n_experts > MOE_MAX_EXPERTS || src->hidden % 256 || src->ffn % 256 || src->hidden > 65536 ||
+        src->ffn > 65536)
+        return MOE_ERR_UNSUPPORTED;
+    const int64_t eb = moe_expert_bytes(src->bits, src->hidden, src->ffn);
+    const uintptr_t s0 = (uintptr_t)src->data, d0 = (uintptr_t)dst;
+    const uintptr_t n = (uintptr_t)eb * (uintptr_t)src->n_experts;
+    if (s0 < d0 + n && d0 < s0 + n) return MOE_ERR_INVALID_ARG;  // overlap
+    const int bb = src->bits == 4 ? 18 : 14;
+    PrepareParams P;
+    P.expert_bytes = (size_t)eb;
+    P.gu_bytes = (size_t)2 * src->ffn * (src->hidden / 32) * bb;
+    P.n_experts = src->n_experts;
+    P.H = src->hidden;
+    P.nc = src->ffn / 32;
+    P.bb = bb;
+    return launch_err(prepare_launch((const uint8_t *)src->data, (uint8_t *)dst, P, S(stream)));
 }
 
 int moe_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *topk_idx, float *topk_w,

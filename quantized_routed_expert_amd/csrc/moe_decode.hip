@@ -195,15 +195,17 @@ struct ChunkMap {
     int l[DEC_MAX_LD];
 };
 
-// per_row: 16-byte pieces per row segment (7..36); inv = 65536 / per_row + 1
-// (j / per_row exactly for the j < 576 used here); rs: LDS row stride.
-__device__ __forceinline__ void chunk_map(ChunkMap &m, int per_row, uint32_t inv, int rs, int row_bytes, int lane) {
+// A chunk is nrows runs of per_row 16-byte pieces (7..36), row_bytes apart in
+// global memory and rs apart in LDS; inv = 65536 / per_row + 1 (j / per_row
+// exactly for the j < 576 used here).
+__device__ __forceinline__ void chunk_map(ChunkMap &m, int nrows, int per_row, uint32_t inv, int rs, int row_bytes,
+                                          int lane) {
 #pragma unroll
     for (int u = 0; u < DEC_MAX_LD; ++u) {
         const int j = lane + 64 * u;
         const int r = (int)(((uint32_t)j * inv) >> 16);
         const int col = j - r * per_row;
-        const bool ok = j < 16 * per_row;
+        const bool ok = j < nrows * per_row;
         m.g[u] = ok ? r * row_bytes + col * 16 : m.g[0];
         m.l[u] = ok ? r * rs + col * 16 : -1;
     }
@@ -379,6 +381,95 @@ __device__ __forceinline__ void chunk_mma(float4v &acc, const uint8_t *buf, int 
 }
 
 // ---------------------------------------------------------------------------
+// Down chunks (column-block-major weights): block j of row n sits at
+// j*rs + n*bb, 4-byte aligned for even n and 2 bytes past that for odd n, so
+// each read takes the dword below and shifts by the byte offset (0 or 2),
+// which makes the instruction stream the same for both parities.
+// ---------------------------------------------------------------------------
+template <int BITS>
+struct DnBlk;
+
+template <>
+struct DnBlk<4> {
+    uint32_t dw, lo, hi;
+    half8 a[2];
+    __device__ __forceinline__ void load(const uint8_t *buf, int a0, int qa, const uint8_t *ab) {
+        dw = lds_u32(buf + (a0 & ~3));  // scale
+        lo = lds_u32(buf + qa);         // code bytes 4g.. of the block, from the dword at or below
+        hi = lds_u32(buf + qa + 4);
+        a[0] = *(const half8 *)ab;
+        a[1] = *(const half8 *)(ab + 16);
+    }
+    __device__ __forceinline__ BVal<4> get(uint32_t sh_d, uint32_t sh_c) const {
+        BVal<4> v;
+        v.b = unpack4(__builtin_amdgcn_alignbyte(hi, lo, sh_c));
+        v.d = half_bits_to_float(dw >> sh_d);
+        return v;
+    }
+};
+
+template <>
+struct DnBlk<3> {
+    uint32_t dw, ql, h0, h1;
+    half8 a[2];
+    __device__ __forceinline__ void load(const uint8_t *buf, int a0, int qa, const uint8_t *ab) {
+        dw = lds_u32(buf + (a0 & ~3));         // scale
+        ql = lds_u32(buf + qa);                // low-part bytes 2g, 2g+1 of the block
+        const int r = (a0 + 10) & ~3;          // third bits: block bytes 10..13
+        h0 = lds_u32(buf + r);
+        h1 = lds_u32(buf + r + 4);
+        a[0] = *(const half8 *)ab;
+        a[1] = *(const half8 *)(ab + 16);
+    }
+    // sh_d: scale shift (bits); sh_q: byte of low-part byte 2g in ql; sh_h: byte shift of the third bits
+    __device__ __forceinline__ BVal<3> get(uint32_t sh_d, uint32_t sh_q, uint32_t sh_h, int g) const {
+        BVal<3> v;
+        v.d = half_bits_to_float(dw >> sh_d);
+        const uint32_t qh = __builtin_amdgcn_alignbyte(h1, h0, sh_h);
+        const uint32_t sel0 = 0x0C000C00u | (sh_q << 16) | sh_q;
+        const uint32_t p0 = __builtin_amdgcn_perm(ql, ql, sel0);
+        const uint32_t p1 = __builtin_amdgcn_perm(ql, ql, sel0 + 0x00010001u);
+        unpack3(p0, p1, qh >> (2 * g), v.lo, v.hb);
+        return v;
+    }
+};
+
+// acc += sum over the chunk's cb blocks (cb even) of d_j * (h . codes_j) for
+// weight row n; A operands (staged h, two fp16 parts 16 bytes apart) at
+// ab + j*128.  Two operand sets: block j+1's reads in flight while j computes.
+template <int BITS>
+__device__ __forceinline__ void dn_chunk_mma(float4v &acc, const uint8_t *buf, int rs, int cb, int n, int g,
+                                             const uint8_t *ab) {
+    constexpr int bb = BITS == 4 ? 18 : 14;
+    const int a0 = n * bb;                                   // block 0 of row n
+    const uint32_t par = (uint32_t)(n & 1);                  // a0 mod 4 = 2 * par
+    const uint32_t sh_d = 16u * par;
+    const int q = a0 + 2 + (BITS == 4 ? 4 : 2) * g;          // first code / low-part byte of this lane
+    const int qa = q & ~3;
+    const uint32_t sh_c = (uint32_t)(q & 3);
+    const uint32_t sh_h = (uint32_t)((a0 + 10) & 3);
+    auto step = [&](const DnBlk<BITS> &b) {
+        BVal<BITS> v;
+        if constexpr (BITS == 4) v = b.get(sh_d, sh_c);
+        else v = b.get(sh_d, sh_c, sh_h, g);
+        const float4v d = block_dot<BITS, 2>(v, b.a);
+        acc.x = fmaf(v.d, d.x, acc.x);
+        acc.y = fmaf(v.d, d.y, acc.y);
+        acc.z = fmaf(v.d, d.z, acc.z);
+        acc.w = fmaf(v.d, d.w, acc.w);
+    };
+    DnBlk<BITS> ba, bq;
+    ba.load(buf, a0, qa, ab);
+    for (int j = 0; j < cb; j += 2) {
+        bq.load(buf + (j + 1) * rs, a0, qa, ab + (j + 1) * 128);
+        step(ba);
+        const int jn = j + 2 < cb ? j + 2 : 0;  // (last round: unused re-read)
+        ba.load(buf + jn * rs, a0, qa, ab + jn * 128);
+        step(bq);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Activation k-groups: the 8 values of (token t, block b, k-group g) that one
 // MFMA lane of k-group g feeds, i.e. the block's weights at pos_in_block(g, e)
 // e = 0..7.  4-bit: elements 4g+0..3 and 16+4g+0..3 (two loads); 3-bit:
@@ -495,7 +586,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
     // token of pair p (p / k; the reciprocal does not cover k = 1)
     auto div_k = [&](int p) { return k == 1 ? p : (int)__umulhi((uint32_t)p, P.m_k); };
     ChunkMap mapH;
-    chunk_map(mapH, P.perH, P.invH, rsH, rowH, lane);
+    chunk_map(mapH, 16, P.perH, P.invH, rsH, rowH, lane);
     // task -> (slot, index of the task within its slot)
     auto task_slot = [&](int task, int &tl) {
         if (task < tasks_sh) {
@@ -815,7 +906,8 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         t.invF = i ? P.invF[1] : P.invF[0];
         t.m_ngrp = i ? P.m_ngrp[1] : P.m_ngrp[0];
         const uint8_t *blob = t.shared ? P.w_shared : P.w_routed + (size_t)s_slot_exp[t.s] * eb;
-        t.rows = blob + (size_t)2 * t.Fx * rowH + (size_t)(t.rg * DEC_DN_ROWS + wave * 16) * t.rowF;
+        // column-block-major down: this wave's 16 rows of column block 0
+        t.rows = blob + (size_t)2 * t.Fx * rowH + (size_t)(t.rg * DEC_DN_ROWS + wave * 16) * bb;
         return t;
     };
     // The first down chunk streams in as soon as the registers are free: here
@@ -826,7 +918,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
     auto prefetch_first_tile = [&]() {
         if (first_tile < n_tiles) {
             const Tile t = tile_of(first_tile);
-            chunk_map(mapF, t.perF, t.invF, t.rsF, t.rowF, lane);
+            chunk_map(mapF, t.cbF, t.perF, t.invF, t.rsF, t.rowF, lane);
             map_fx = t.Fx;
             chunk_load(c, t.rows, mapF);
             c_holds_tile = true;
@@ -923,7 +1015,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         const int cbF = tl.cbF, nchF = tl.nchF, segF = tl.segF, rsF = tl.rsF;
         const uint8_t *rows_d = tl.rows;
         if (Fx != map_fx) {
-            chunk_map(mapF, tl.perF, tl.invF, rsF, tl.rowF, lane);
+            chunk_map(mapF, cbF, tl.perF, tl.invF, rsF, tl.rowF, lane);
             map_fx = Fx;
         }
         const int n_tok = s_slot_cnt[s];
@@ -1020,7 +1112,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             if (ti == first_tile && ci == 0) TRACEW(5);
             wave_lds_handoff();
             if (ci + 1 < nchF) chunk_load(c, rows_d + (size_t)(ci + 1) * segF, mapF);
-            chunk_mma<BITS, 2>(acc, s_chunk, rsF, cbF, n_lane, g_lane, ab + (size_t)ci * cbF * 128, 128, 16);
+            dn_chunk_mma<BITS>(acc, s_chunk, rsF, cbF, n_lane, g_lane, ab + (size_t)ci * cbF * 128);
             wave_lds_handoff();
         }
         // o = acc * 2^-sc_m; weighted write per pair

@@ -107,7 +107,10 @@ struct DecodeParams {
     uint32_t m_tasks_rt;
     int tps;                               // down tiles per slot (H / 128)
     uint32_t m_tps;
-    // down geometry per kind of slot: [0] routed (F), [1] shared (Fs)
+    // down geometry per kind of slot: [0] routed (F), [1] shared (Fs).  Down
+    // is column-block-major, so a wave's chunk (16 rows x cbF blocks) is cbF
+    // runs of 16*bb bytes: segF = bytes between chunks, rowF = between runs,
+    // rsF = LDS bytes between runs, perF = 16-byte pieces per run
     int fx[2], cbF[2], nchF[2], segF[2], rowF[2], rsF[2], perF[2];
     uint32_t invF[2], m_ngrp[2];           // m_ngrp: 1 / (fx / 8)
     uint32_t m_k;                          // 1 / k
@@ -173,6 +176,13 @@ struct CombineParams {
     const float *out_pairs, *out_shared;
     float *y;
     int T, k, H;
+};
+
+// Weight preparation (row-by-row block order -> down column-block-major).
+struct PrepareParams {
+    size_t expert_bytes;  // one blob
+    size_t gu_bytes;      // gate + up bytes of one blob (2 * F * H/32 * bb)
+    int n_experts, H, nc, bb;  // nc = F / 32 (down blocks per row), bb = bytes per block
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }

@@ -160,7 +160,6 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_gemm(GemmParams P) {
         const int mt = local % mtiles, nt = local / mtiles;
         const int r0 = mt * PF_MT;
         const int nrows = min(PF_MT, cnt - r0);
-        const size_t rowF = (size_t)(Fx >> 5) * bb;
         const uint8_t *blob = shared_slot ? P.w_shared : P.w_routed + (size_t)e * 3 * Fx * rowH;
         const uint8_t *wrows;
         size_t wrow_bytes;
@@ -170,8 +169,9 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_gemm(GemmParams P) {
             wrow_bytes = rowH;
             K = P.H;
         } else {
-            wrows = blob + (size_t)2 * Fx * rowH + (size_t)nt * PF_NF * rowF;
-            wrow_bytes = rowF;
+            // down, column-block-major: block (h, c) at (c * H + h) * bb
+            wrows = blob + (size_t)2 * Fx * rowH + (size_t)nt * PF_NF * bb;
+            wrow_bytes = bb;
             K = Fx;
         }
         __syncthreads();
@@ -264,10 +264,10 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_gemm(GemmParams P) {
                 if (MODE == 0) {
                     const int half = row / PF_NF;  // 0 gate, 1 up
                     src = wrows + (size_t)half * Fx * rowH + (size_t)(row - half * PF_NF) * wrow_bytes;
+                    src += (size_t)(ks * PF_KSB + blk) * bb;
                 } else {
-                    src = wrows + (size_t)row * wrow_bytes;
+                    src = wrows + (size_t)row * wrow_bytes + (size_t)(ks * PF_KSB + blk) * P.H * bb;
                 }
-                src += (size_t)(ks * PF_KSB + blk) * bb;
                 uint16_t codes[32];
                 float d = dequant_block_bf16<BITS>(src, codes);
                 sS[blk][row] = d;

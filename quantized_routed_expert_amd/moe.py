@@ -26,9 +26,10 @@ MOE_ERR_DEVICE = -5
 DTYPE_F32, DTYPE_BF16 = 0, 1
 PATH_AUTO, PATH_DECODE, PATH_PREFILL = 0, 1, 2
 DECODE_MAX_ROWS = 16
+LAYOUT_ROWS, LAYOUT_PREPARED = 0, 1
 
 EXPORTS = ["moe_version", "moe_status_string", "moe_expert_bytes", "moe_workspace_bytes",
-           "moe_route", "moe_group", "moe_expert_ffn", "moe_layer_forward"]
+           "moe_prepare_qweights", "moe_route", "moe_group", "moe_expert_ffn", "moe_layer_forward"]
 
 
 class MoeError(RuntimeError):
@@ -40,7 +41,7 @@ class MoeError(RuntimeError):
 class QWeights(ctypes.Structure):
     """moe_qweights: device pointer + format and shape of a set of experts."""
     _fields_ = [("data", ctypes.c_void_p), ("bits", ctypes.c_int32), ("n_experts", ctypes.c_int32),
-                ("hidden", ctypes.c_int32), ("ffn", ctypes.c_int32)]
+                ("hidden", ctypes.c_int32), ("ffn", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -61,6 +62,8 @@ def lib():
         L.moe_expert_bytes.argtypes = [i32, i32, i32]
         L.moe_workspace_bytes.restype = i64
         L.moe_workspace_bytes.argtypes = [i32] * 7
+        L.moe_prepare_qweights.restype = ctypes.c_int
+        L.moe_prepare_qweights.argtypes = [ctypes.POINTER(QWeights), vp, i64]
         L.moe_route.restype = ctypes.c_int
         L.moe_route.argtypes = [vp, i32, i32, i32, vp, vp, i64]
         L.moe_group.restype = ctypes.c_int
@@ -106,9 +109,21 @@ def _xcode(x: torch.Tensor) -> int:
     raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
 
 
-def qweights(data: torch.Tensor, bits: int, n_experts: int, hidden: int, ffn: int) -> QWeights:
-    """Describe a uint8 device tensor holding n_experts expert blobs."""
-    return QWeights(ctypes.c_void_p(data.data_ptr()), bits, n_experts, hidden, ffn)
+def qweights(data: torch.Tensor, bits: int, n_experts: int, hidden: int, ffn: int, layout: int) -> QWeights:
+    """Describe a uint8 device tensor holding n_experts expert blobs in the
+    given block order (LAYOUT_ROWS or LAYOUT_PREPARED)."""
+    return QWeights(ctypes.c_void_p(data.data_ptr()), bits, n_experts, hidden, ffn, layout)
+
+
+def prepare_qweights(data: torch.Tensor, bits: int, n_experts: int, hidden: int, ffn: int, out=None,
+                     stream=None):
+    """Blobs in the pages' row-by-row order (uint8 device tensor) -> a new
+    tensor in the order the compute calls read; returns (tensor, QWeights)."""
+    if out is None:
+        out = torch.empty_like(data)
+    src = QWeights(ctypes.c_void_p(data.data_ptr()), bits, n_experts, hidden, ffn, LAYOUT_ROWS)
+    _check(lib().moe_prepare_qweights(ctypes.byref(src), _ptr(out), _stream(stream)), "moe_prepare_qweights")
+    return out, qweights(out, bits, n_experts, hidden, ffn, LAYOUT_PREPARED)
 
 
 def expert_bytes(bits: int, hidden: int, ffn: int) -> int:

@@ -27,13 +27,14 @@ class DevLayer:
         self.T = li.T
         self.x = x_to_dev(li.x, cfg.x_dtype)
         self.logits = torch.from_numpy(li.logits).to(DEV)
-        self.routed_t = torch.from_numpy(li.routed).to(DEV)
-        self.routed = moe.qweights(self.routed_t, cfg.bits, cfg.n_experts, cfg.hidden, cfg.ffn)
+        # the pages' block order on the host, converted once on the device
+        self.routed_t, self.routed = moe.prepare_qweights(torch.from_numpy(li.routed).to(DEV), cfg.bits,
+                                                          cfg.n_experts, cfg.hidden, cfg.ffn)
         self.shared_t = None
         self.shared = None
         if li.shared is not None:
-            self.shared_t = torch.from_numpy(li.shared).to(DEV)
-            self.shared = moe.qweights(self.shared_t, cfg.bits, 1, cfg.hidden, cfg.shared_ffn)
+            self.shared_t, self.shared = moe.prepare_qweights(torch.from_numpy(li.shared).to(DEV), cfg.bits, 1,
+                                                              cfg.hidden, cfg.shared_ffn)
 
     def forward(self, path=moe.PATH_AUTO, ws=None, want_routing=True):
         cfg = self.cfg

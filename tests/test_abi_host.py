@@ -77,12 +77,14 @@ def test_rejects_before_launch(L):
     assert L.moe_group(fake, 4, 8, 2, fake, None, fake, fake, 1 << 20, 0) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_group(fake, 4, 8, 2, fake, fake, fake, fake, 0, 0) == moe.MOE_ERR_WORKSPACE
 
-    w = moe.QWeights(fake, 4, 8, 256, 512)
-    bad_bits = moe.QWeights(fake, 5, 8, 256, 512)
-    bad_h = moe.QWeights(fake, 4, 8, 200, 512)
-    bad_sh = moe.QWeights(fake, 4, 2, 256, 512)   # shared must hold one expert
-    nodata = moe.QWeights(None, 4, 8, 256, 512)
-    sh = moe.QWeights(fake, 4, 1, 256, 512)
+    P = moe.LAYOUT_PREPARED
+    w = moe.QWeights(fake, 4, 8, 256, 512, P)
+    bad_bits = moe.QWeights(fake, 5, 8, 256, 512, P)
+    bad_h = moe.QWeights(fake, 4, 8, 200, 512, P)
+    bad_sh = moe.QWeights(fake, 4, 2, 256, 512, P)   # shared must hold one expert
+    nodata = moe.QWeights(None, 4, 8, 256, 512, P)
+    rows = moe.QWeights(fake, 4, 8, 256, 512, moe.LAYOUT_ROWS)  # not converted
+    sh = moe.QWeights(fake, 4, 1, 256, 512, P)
     big = 1 << 30
 
     def lf(x=fake, dt=0, lg=fake, T=4, k=2, r=w, s=sh, y=fake, path=0, ws=fake, wsb=big):
@@ -99,13 +101,15 @@ def test_rejects_before_launch(L):
     assert lf(r=bad_h) == moe.MOE_ERR_INVALID_ARG        # hidden differs from the shared expert's
     assert lf(r=bad_h, s=None) == moe.MOE_ERR_UNSUPPORTED  # hidden not a multiple of 256
     assert lf(r=nodata) == moe.MOE_ERR_INVALID_ARG
+    assert lf(r=rows) == moe.MOE_ERR_UNSUPPORTED
+    assert lf(s=moe.QWeights(fake, 4, 1, 256, 512, moe.LAYOUT_ROWS)) == moe.MOE_ERR_UNSUPPORTED
     assert lf(s=bad_sh) == moe.MOE_ERR_INVALID_ARG
     assert lf(k=9) == moe.MOE_ERR_UNSUPPORTED
     assert lf(T=-1) == moe.MOE_ERR_INVALID_ARG
     assert lf(wsb=16) == moe.MOE_ERR_WORKSPACE
     assert lf(T=17, path=moe.PATH_DECODE) == moe.MOE_ERR_UNSUPPORTED
     # mixed bit widths cannot take the fused decode launch when forced
-    assert lf(s=moe.QWeights(fake, 3, 1, 256, 512), path=moe.PATH_DECODE) == moe.MOE_ERR_UNSUPPORTED
+    assert lf(s=moe.QWeights(fake, 3, 1, 256, 512, P), path=moe.PATH_DECODE) == moe.MOE_ERR_UNSUPPORTED
     # T == 0 is a valid empty call: nothing is launched
     assert lf(T=0) == moe.MOE_OK
 
@@ -116,6 +120,31 @@ def test_rejects_before_launch(L):
     assert ef(off=None) == moe.MOE_ERR_INVALID_ARG
     assert ef(out=None) == moe.MOE_ERR_INVALID_ARG
     assert ef(ww=bad_bits) == moe.MOE_ERR_UNSUPPORTED
+    assert ef(ww=rows) == moe.MOE_ERR_UNSUPPORTED
     assert ef(T=17, path=moe.PATH_DECODE) == moe.MOE_ERR_UNSUPPORTED
     assert ef(wsb=0) == moe.MOE_ERR_WORKSPACE
     assert ef(T=0) == moe.MOE_OK
+
+
+def test_prepare_rejects_before_launch(L):
+    """moe_prepare_qweights validates on the host: null pointers, a source not
+    in the row-by-row order, overlapping buffers, unsupported formats."""
+    from quantized_routed_expert_amd import moe
+    fake = ctypes.c_void_p(0x1000)
+    eb = moe.expert_bytes(4, 256, 512)
+    src = moe.QWeights(fake, 4, 8, 256, 512, moe.LAYOUT_ROWS)
+    pf = L.moe_prepare_qweights
+    assert pf(None, ctypes.c_void_p(0x10000000), 0) == moe.MOE_ERR_INVALID_ARG
+    assert pf(ctypes.byref(src), None, 0) == moe.MOE_ERR_INVALID_ARG
+    assert pf(ctypes.byref(moe.QWeights(None, 4, 8, 256, 512, 0)), ctypes.c_void_p(0x10000000), 0) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert pf(ctypes.byref(moe.QWeights(fake, 4, 8, 256, 512, moe.LAYOUT_PREPARED)),
+              ctypes.c_void_p(0x10000000), 0) == moe.MOE_ERR_INVALID_ARG
+    # dst starting inside src, and src starting inside dst
+    assert pf(ctypes.byref(src), ctypes.c_void_p(0x1000 + eb), 0) == moe.MOE_ERR_INVALID_ARG
+    assert pf(ctypes.byref(moe.QWeights(ctypes.c_void_p(0x1000 + 64), 4, 8, 256, 512, 0)), fake, 0) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert pf(ctypes.byref(moe.QWeights(fake, 5, 8, 256, 512, 0)), ctypes.c_void_p(0x10000000), 0) == \
+        moe.MOE_ERR_UNSUPPORTED
+    assert pf(ctypes.byref(moe.QWeights(fake, 4, 8, 200, 512, 0)), ctypes.c_void_p(0x10000000), 0) == \
+        moe.MOE_ERR_UNSUPPORTED

@@ -178,8 +178,8 @@ def test_expert_ffn(orc, name, T, path):
     ref = orc.expert_ffn(li.x, li.x_code, cfg.top_k, cfg.bits, cfg.n_experts, cfg.hidden, cfg.ffn,
                          li.routed, ro, rp, ra, rw)
     x = x_to_dev(li.x, cfg.x_dtype)
-    routed_t = torch.from_numpy(li.routed).to(DEV)
-    qw = moe.qweights(routed_t, cfg.bits, cfg.n_experts, cfg.hidden, cfg.ffn)
+    routed_t, qw = moe.prepare_qweights(torch.from_numpy(li.routed).to(DEV), cfg.bits, cfg.n_experts, cfg.hidden,
+                                        cfg.ffn)
     off = torch.from_numpy(ro).to(DEV)
     pairs = torch.from_numpy(np.ascontiguousarray(rp)).to(DEV)
     act = torch.from_numpy(ra).to(DEV)
@@ -206,8 +206,30 @@ def test_negative_control_corrupted_expert(orc):
     assert rel_err(y0, yr) <= TOL
     e = int(ir[0, 0])
     eb = cfg.expert_bytes
-    # a down-projection block of the top expert: scale byte (high) of block 0, row 0
+    # a down-projection block of the top expert: scale byte (high) of block 0,
+    # row 0 (the first down block in either block order)
     off = e * eb + 2 * cfg.ffn * (cfg.hidden // 32) * cfg.block_bytes + 1
     dl.routed_t[off] ^= 0x40
     y1 = dl.forward(D)[0]
     assert rel_err(y1, yr) > TOL
+
+
+# ---- weight preparation ---------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "e512"])
+def test_prepare_qweights_order(name):
+    """moe_prepare_qweights is a pure reordering: gate and up byte for byte,
+    down block (h, c) moved to index c*H + h (checked against a numpy
+    transpose of the blocks; both formats)."""
+    print(f"[prepare] {name}", flush=True)
+    cfg = synth.CONFIGS[name]
+    li = layer_inputs(name, 1)
+    n = 3
+    raw = np.ascontiguousarray(li.routed[: n * cfg.expert_bytes])
+    dev, _ = moe.prepare_qweights(torch.from_numpy(raw).to(DEV), cfg.bits, n, cfg.hidden, cfg.ffn)
+    got = dev.cpu().numpy().reshape(n, -1)
+    H, F, bb = cfg.hidden, cfg.ffn, cfg.block_bytes
+    gu = 2 * F * (H // 32) * bb
+    exp = raw.reshape(n, -1).copy()
+    exp[:, gu:] = exp[:, gu:].reshape(n, H, F // 32, bb).transpose(0, 2, 1, 3).reshape(n, -1)
+    assert np.array_equal(got, exp)
