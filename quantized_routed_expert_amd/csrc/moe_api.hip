@@ -18,6 +18,8 @@ namespace moe {
 hipError_t decode_launch(const DecodeParams &P, int grid, hipStream_t st);
 int decode_occupancy(int bits, int x_f32, int lds);
 hipError_t decode_set_lds(int bits, int x_f32, int lds);
+hipError_t split_launch(const SplitParams &P, int grid, hipStream_t st);
+hipError_t split_set_lds(int bits, int T, int xf, int lds);
 hipError_t route_launch(const RouteParams &P, hipStream_t st);
 hipError_t group_launch(const GroupParams &P, hipStream_t st);
 }  // namespace moe
@@ -65,8 +67,8 @@ int dev_info(DevInfo &out) {
 // Workspace layout
 // ----------------------------------------------------------------------------
 struct Layout {
-    size_t counters = 0, n_counters = 0;       // decode: gu[MS] dn[MS] slice[H/128] err[4]
-    size_t harr = 0, oll = 0, out_pairs = 0, out_shared = 0;
+    size_t counters = 0, n_counters = 0;       // decode: gu[MS] dn[MS] slice[H/128] err epoch done items
+    size_t harr = 0, oll = 0, part = 0, out_pairs = 0, out_shared = 0;
     size_t idx = 0, w = 0, offsets = 0, pairs = 0, active = 0, chunk_counts = 0;
     size_t slot_exp = 0, slot_row0 = 0, slot_cnt = 0, slot_hrow0 = 0, prefix_gu = 0, prefix_dn = 0;
     size_t hbuf = 0;
@@ -78,7 +80,7 @@ struct Layout {
 // layout, so a workspace that is zero before its first use stays valid for
 // calls of any shape and path (each call returns the counters to zero).  Each
 // counter has a 256-byte line of its own.
-constexpr size_t COUNTER_WORDS = (size_t)(2 * DEC_MAX_SLOTS + DEC_MAX_SLICES + 3) * DEC_CSTRIDE;
+constexpr size_t COUNTER_WORDS = (size_t)(2 * DEC_MAX_SLOTS + DEC_MAX_SLICES + 4) * DEC_CSTRIDE;
 Layout make_layout(int T, int E, int k, int H, int F, int Fs, int path) {
     Layout L;
     size_t off = 0;
@@ -105,6 +107,11 @@ Layout make_layout(int T, int E, int k, int H, int F, int Fs, int path) {
     if (path == MOE_PATH_DECODE) {
         L.harr = take((TK + T) * (size_t)Fmax * 8);  // tagged SwiGLU outputs per pair row (+ shared rows)
         L.oll = take((TK + T) * (size_t)H * 8);      // tagged weighted pair rows (+ shared rows)
+        // tagged partial rows per (pair, 32-column slice) of the column-split
+        // launch, sized for its largest window so that a workspace sized for
+        // T rows also serves every smaller window
+        const size_t Ts = T < SPL_MAX_T ? (size_t)T : (size_t)SPL_MAX_T;
+        L.part = take((Ts * k + Ts) * (size_t)(Fmax / 32) * H * 8);
     } else {
         L.slot_exp = take((size_t)(E + 1) * 4);
         L.slot_row0 = take((size_t)(E + 1) * 4);
@@ -286,6 +293,52 @@ bool decode_fits(int T, int E, int k, int H, int F, int Fs, int bits, int x_dtyp
     return decode_lds_layout(P, xf ? 2 : 1) <= DEC_LDS_BUDGET;
 }
 
+// ---- column-split decode launch (windows of one or two rows) ----
+int split_xpd(int bits) { return bits == 4 ? 36 : 80; }
+
+int split_lds_layout(SplitParams &P) {
+    const int bb = P.bits == 4 ? 18 : 14, xpd = split_xpd(P.bits);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t a = off;
+        off = align_up(off + bytes, 16);
+        return (int)a;
+    };
+    P.lds_small = take(sizeof(SplitSmall));
+    P.lds_wt = take((size_t)3 * P.H * bb);
+    P.lds_a = take((size_t)P.T * P.H * 2);
+    P.lds_S = take((size_t)P.T * (P.H / 32) * 4);
+    P.lds_xd = take((size_t)P.T * (P.H / 64) * xpd * 4);
+    P.lds_gu = take((size_t)P.T * 64 * 4);
+    P.lds_ah = take((size_t)P.T * 32 * 2);
+    P.lds_hd = take((size_t)P.T * xpd * 4);
+    P.lds_total = (int)off;
+    return P.lds_total;
+}
+
+// Reduction outputs per workgroup for a grid of G.
+int split_units(int T, int k, int H, int combine, int G) {
+    const long long n = combine ? (long long)T * H : (long long)T * k * H;
+    return (int)((n + G - 1) / G);
+}
+
+bool split_fits(int T, int E, int k, int H, int F, int Fs, int bits, int G) {
+    (void)E;
+    if (T < 1 || T > SPL_MAX_T || k > 32) return false;
+    if (H != 256 && H != 512 && H != 1024 && H != 2048) return false;
+    if (F > 4096 || Fs > 4096) return false;
+    SplitParams P;
+    memset(&P, 0, sizeof(P));
+    P.T = T;
+    P.H = H;
+    P.bits = bits;
+    if (split_lds_layout(P) > DEC_LDS_BUDGET) return false;
+    // the reduction stages (outputs x terms) floats in the item weight area
+    const int units = split_units(T, k, H, 0, G) > split_units(T, k, H, 1, G) ? split_units(T, k, H, 0, G)
+                                                                                : split_units(T, k, H, 1, G);
+    return (long long)units * (k + 1) * 4 <= (long long)3 * H * (bits == 4 ? 18 : 14);
+}
+
 }  // namespace
 
 extern "C" {
@@ -382,6 +435,60 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
     DevInfo dv;
     int rc = dev_info(dv);
     if (rc) return rc;
+    const int Fs_ = shared ? shared->ffn : 0;
+    if (split_fits(T, E, k, routed->hidden, routed->ffn, Fs_, routed->bits, dv.cus)) {
+        SplitParams S_;
+        memset(&S_, 0, sizeof(S_));
+        S_.x = x;
+        S_.logits = logits;
+        S_.g_offsets = g_off;
+        S_.g_pairs = g_pairs;
+        S_.g_active = g_act;
+        S_.g_pair_w = g_pw;
+        S_.w_routed = (const uint8_t *)routed->data;
+        S_.w_shared = shared ? (const uint8_t *)shared->data : nullptr;
+        S_.y = y;
+        S_.out_pairs = out_pairs;
+        S_.out_shared = at<float>(ws, L.out_shared);
+        S_.topk_idx_out = tidx;
+        S_.topk_w_out = tw;
+        S_.part = at<uint64_t>(ws, L.part);
+        uint32_t *cnt = at<uint32_t>(ws, L.counters);
+        S_.err = cnt + (size_t)(2 * DEC_MAX_SLOTS + DEC_MAX_SLICES) * DEC_CSTRIDE;
+        S_.epoch = S_.err + DEC_CSTRIDE;
+        S_.done = S_.err + 2 * DEC_CSTRIDE;
+        S_.items_done = S_.err + 3 * DEC_CSTRIDE;
+        S_.T = T;
+        S_.E = E;
+        S_.k = k;
+        S_.H = routed->hidden;
+        S_.F = routed->ffn;
+        S_.Fs = Fs_;
+        S_.bits = routed->bits;
+        S_.mode = mode | (shared ? DEC_MODE_SHARED : 0);
+        S_.x_f32 = x_f32;
+        S_.nc = S_.F / 32;
+        S_.ncs = Fs_ / 32;
+        S_.ncmax = S_.nc > S_.ncs ? S_.nc : S_.ncs;
+        S_.m_nc = magic_div(S_.nc);
+        S_.rowH = (S_.H / 32) * (S_.bits == 4 ? 18 : 14);
+        S_.lg_qpr = ilog2(S_.H / 256);
+        const int grid = dv.cus;  // one workgroup per CU, all resident
+        S_.units = split_units(T, k, S_.H, (mode & DEC_MODE_COMBINE) ? 1 : 0, grid);
+        const int lds = split_lds_layout(S_);
+        if (lds > dv.lds_max) return MOE_ERR_UNSUPPORTED;
+        static std::mutex smu;
+        static int s_lds_set[2][2][2] = {};
+        {
+            std::lock_guard<std::mutex> lk(smu);
+            int &cur = s_lds_set[S_.bits == 4][T - 1][x_f32 ? 1 : 0];
+            if (lds > cur) {
+                if (split_set_lds(S_.bits, T, x_f32, lds) != hipSuccess) return MOE_ERR_LAUNCH;
+                cur = lds;
+            }
+        }
+        return launch_err(split_launch(S_, grid, st));
+    }
     DecodeParams P;
     memset(&P, 0, sizeof(P));
     P.x = x;
@@ -496,7 +603,8 @@ int moe_expert_ffn(const void *x, int32_t x_dtype, int32_t T, const moe_qweights
     if (rc) return rc;
     int p = resolve_path(path, T);
     if (p == MOE_PATH_DECODE &&
-        (T > MOE_DECODE_MAX_ROWS || !decode_fits(T, w->n_experts, k, w->hidden, w->ffn, 0, w->bits, x_dtype))) {
+        (T > MOE_DECODE_MAX_ROWS || !(split_fits(T, w->n_experts, k, w->hidden, w->ffn, 0, w->bits, 256) ||
+                                      decode_fits(T, w->n_experts, k, w->hidden, w->ffn, 0, w->bits, x_dtype)))) {
         if (path == MOE_PATH_DECODE) return MOE_ERR_UNSUPPORTED;
         p = MOE_PATH_PREFILL;
     }
@@ -535,7 +643,8 @@ int moe_layer_forward(const void *x, int32_t x_dtype, const float *logits, int32
     int p = resolve_path(path, T);
     const bool same_bits = !shared || shared->bits == routed->bits;
     if (p == MOE_PATH_DECODE && (T > MOE_DECODE_MAX_ROWS || !same_bits ||
-                                 !decode_fits(T, E, k, H, routed->ffn, Fs, routed->bits, x_dtype))) {
+                                 !(split_fits(T, E, k, H, routed->ffn, Fs, routed->bits, 256) ||
+                                   decode_fits(T, E, k, H, routed->ffn, Fs, routed->bits, x_dtype)))) {
         if (path == MOE_PATH_DECODE) return MOE_ERR_UNSUPPORTED;
         p = MOE_PATH_PREFILL;
     }

@@ -203,53 +203,110 @@ __device__ __forceinline__ void store_dev_u32(uint32_t *p, uint32_t v) {
 // all of this wave's memory operations have completed
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
-// Router for one logits row by one wave: the k largest logits (an equal logit
-// goes to the lower expert id; the comparison is on the fp32 values, -0 == +0)
-// and the softmax over those k, lane j < k writing entry j.  EPL = logits per
-// lane (E <= 64 * EPL).  k rounds of a wave-wide max over 64-bit keys
-// (orderable value << 32 | inverted id).
+// ---------------------------------------------------------------------------
+// Wave reductions on DPP (gfx9 row broadcasts); result valid in every lane.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
+
+// Inclusive prefix sum over the 64 lanes (row shifts within rows of 16, then
+// row broadcasts across rows).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+    return v;
+}
+
+// Router for one row by one wave (E <= 64 * EPL): k rounds of a wave-wide
+// argmax, an equal logit going to the lower expert id; softmax over the k.
+// The logits load (route_keys) is separate from the selection (route_pick),
+// so a wave can issue other loads in between.
 template <int EPL>
-__device__ void wave_topk_row(const float *row, int E, int k, int *out_idx, float *out_w, int lane) {
+__device__ __forceinline__ void route_keys(const float *row, int E, int lane, uint32_t (&key)[EPL]) {
     float v[EPL];
-    uint64_t avail = 0;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-        int e = lane + 64 * i;
-        v[i] = 0.0f;
-        if (e < E) {
-            v[i] = row[e];
-            avail |= 1ull << i;
-        }
+        const int e = lane + 64 * i;
+        v[i] = row[e < E ? e : 0];  // every lane loads (in bounds), so the loads issue as one sequence
     }
-    float mine = 0.0f;
-    int mine_id = 0;
-    for (int j = 0; j < k; ++j) {
-        uint64_t best = 0;
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            if ((avail >> i) & 1ull) {
-                uint64_t key = ((uint64_t)float_key(v[i]) << 32) |
-                               (uint32_t)(0xFFFFFFFFu - (uint32_t)(lane + 64 * i));
-                best = key > best ? key : best;
-            }
+    for (int i = 0; i < EPL; ++i) key[i] = lane + 64 * i < E ? float_key(v[i]) : 0u;  // finite values: keys > 0
+}
+
+// One selection round: the largest key (an equal key goes to the lower
+// expert id), removed from the keys; returns the expert id, sets its key.
+template <int EPL>
+__device__ __forceinline__ int route_round(uint32_t (&key)[EPL], uint32_t &m, int lane) {
+    uint32_t bk = 0;
+    int bi = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+        if (key[i] > bk) {  // strict: the lowest i wins among equal keys
+            bk = key[i];
+            bi = i;
         }
-        uint64_t win = wave_max_u64(best);
-        int e = (int)(0xFFFFFFFFu - (uint32_t)win);
-        uint32_t kh = (uint32_t)(win >> 32);
-        uint32_t u = (kh & 0x80000000u) ? (kh & 0x7FFFFFFFu) : ~kh;
-        if ((e & 63) == lane) avail &= ~(1ull << (e >> 6));
-        if (lane == j) {
-            mine = __builtin_bit_cast(float, u);
-            mine_id = e;
-        }
+    m = wave_max_u32(bk);
+    const uint64_t tied = __ballot(bk == m);
+    int e;
+    if (__popcll(tied) == 1) {
+        const int wl = __ffsll((unsigned long long)tied) - 1;
+        e = wl + 64 * __builtin_amdgcn_readlane(bi, wl);
+    } else {
+        e = (int)wave_min_u32(bk == m ? (uint32_t)(lane + 64 * bi) : 0xFFFFFFFFu);
     }
-    float l0 = __shfl(mine, 0, 64);
-    float ex = lane < k ? expf(mine - l0) : 0.0f;
-    float s = wave_sum_f(ex);
+    if ((e & 63) == lane) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (i == (e >> 6)) key[i] = 0u;
+    }
+    return e;
+}
+
+__device__ __forceinline__ float key_value(uint32_t m) {
+    return __builtin_bit_cast(float, (m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
+}
+
+// softmax over the k selected logits of one row (lane j < k holds slot j),
+// the sum taken in slot order 0, 1, ..., k-1 like every other routing path,
+// so a row's weights do not depend on which path routed it
+__device__ __forceinline__ void route_write(float mine, int mine_id, int k, int *out_idx, float *out_w, int lane) {
+    const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mine)));
+    const float ex = lane < k ? expf(mine - l0) : 0.0f;
+    float s = 0.0f;
+    for (int j = 0; j < k; ++j) s += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), j));
     if (lane < k) {
         out_idx[lane] = mine_id;
         out_w[lane] = ex / s;
     }
 }
+
+template <int EPL>
+__device__ __forceinline__ void route_pick(uint32_t (&key)[EPL], int k, int *out_idx, float *out_w, int lane) {
+    float mine = 0.0f;
+    int mine_id = 0;
+    for (int j = 0; j < k; ++j) {
+        uint32_t m;
+        const int e = route_round<EPL>(key, m, lane);
+        if (lane == j) {
+            mine = key_value(m);
+            mine_id = e;
+        }
+    }
+    route_write(mine, mine_id, k, out_idx, out_w, lane);
+}
+
 
 }  // namespace moe

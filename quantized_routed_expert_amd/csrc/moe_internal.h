@@ -125,6 +125,53 @@ struct DecodeParams {
 };
 
 // ---------------------------------------------------------------------------
+// Column-split decode launch (windows of one or two rows): each workgroup item
+// is (expert, 32-column slice of its FFN): gate/up rows of the slice, SwiGLU
+// and the slice's partial down projection, reduced over the slices at the end.
+// ---------------------------------------------------------------------------
+constexpr int SPL_MAX_T = 2;
+constexpr int SPL_MAX_SLOTS = SPL_MAX_T * 32 + 1;  // T*k pairs (k <= 32) + the shared expert
+
+struct SplitSmall {  // fixed part of the launch's LDS
+    int idx[SPL_MAX_T * 32];
+    float w[SPL_MAX_T * 32];
+    int slot_exp[SPL_MAX_SLOTS];
+    int slot_pair[SPL_MAX_SLOTS][SPL_MAX_T];  // pair id of each row in the slot, -1: none
+    int plist[SPL_MAX_SLOTS * SPL_MAX_T];     // pairs present (output rows of the per-pair mode)
+    uint32_t xmax[SPL_MAX_T];
+    float tinv[SPL_MAX_T], hinv[SPL_MAX_T];
+    int Sh[SPL_MAX_T];
+    int n_slots, n_pl, pad[2];
+};
+
+struct SplitParams {
+    const void *x;             // [T][H] fp32 or bf16
+    const float *logits;       // [T][E] (ROUTE mode)
+    const int32_t *g_offsets;  // given grouping (not ROUTE mode)
+    const int32_t *g_pairs;
+    const int32_t *g_active;
+    const float *g_pair_w;     // may be null: weight 1
+    const uint8_t *w_routed;   // E prepared expert blobs
+    const uint8_t *w_shared;   // 1 prepared blob or null
+    float *y;                  // [T][H] (COMBINE mode)
+    float *out_pairs;          // [T*k][H]
+    float *out_shared;         // [T][H]
+    int32_t *topk_idx_out;     // may be null
+    float *topk_w_out;         // may be null
+    uint64_t *part;            // [T*k + T][ncmax][H] tagged partial down rows per (pair, slice)
+    uint32_t *items_done;      // finished items of this call (a hint: readers check tags)
+    uint32_t *err, *epoch, *done;
+    int T, E, k, H, F, Fs, bits, mode, x_f32;
+    int nc, ncs, ncmax;        // 32-column slices of F and Fs; the partial buffer's stride
+    uint32_t m_nc;             // ceil(2^32 / nc) (0 when nc = 1)
+    int rowH;                  // bytes of one gate/up row
+    int lg_qpr;                // log2 of the 4-pair pieces per gate/up row (H / 256)
+    int units;                 // reduction outputs per workgroup
+    // LDS byte offsets
+    int lds_small, lds_wt, lds_a, lds_S, lds_xd, lds_gu, lds_ah, lds_hd, lds_total;
+};
+
+// ---------------------------------------------------------------------------
 // Prefill / general path.
 // ---------------------------------------------------------------------------
 constexpr int GRP_CHUNK_TOKENS = 64;  // tokens per grouping chunk

@@ -27,7 +27,9 @@ __global__ __launch_bounds__(256) void k_route(RouteParams P) {
     __shared__ int s_idx[4][MOE_TOPK_MAX_LDS];
     __shared__ float s_w[4][MOE_TOPK_MAX_LDS];
     const int wv = threadIdx.x >> 6;
-    wave_topk_row<EPL>(P.logits + (size_t)t * P.E, P.E, P.k, s_idx[wv], s_w[wv], lane);
+    uint32_t key[EPL];
+    route_keys<EPL>(P.logits + (size_t)t * P.E, P.E, lane, key);
+    route_pick<EPL>(key, P.k, s_idx[wv], s_w[wv], lane);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");

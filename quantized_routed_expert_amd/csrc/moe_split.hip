@@ -1,0 +1,747 @@
+// moe_split.hip -- the routed-expert layer for decode windows of one or two
+// rows, in one launch, split over 32-column slices of every expert's FFN.
+//
+// With one or two rows the matrix cores would idle on 15 of their 16 rows,
+// and the layer is a stream of quantized bytes: per row and weight it needs
+// one multiply-add.  So this launch does integer dot products on the vector
+// units instead (v_dot8_i32_i4: eight signed 4-bit products per instruction):
+//  - activations x (and later h) are scaled per row by a power of two so the
+//    largest |value| lies in [2^13, 2^14), rounded to integers (15 bits; the
+//    relative rounding error is below 2^-14 of the row's largest value), and
+//    cut into four signed radix-16 digits;
+//  - 4-bit codes become signed nibbles (code - 8) with one xor; 3-bit codes
+//    split into their two low bits and their third bit, each a nibble, with
+//    (code - 4) * a = low * a + third * 4a - 4a;
+//  - a block's integer dot product is exact (it fits fp32's 24-bit
+//    significand) and is scaled by the block's fp16 scale in fp32, the same
+//    rounding point as the dequantized fp32 dot product of the pages.
+//
+// Work items: (expert, 32-column slice c of its FFN).  An item needs the 32
+// gate rows and 32 up rows of the slice and column block c of down (the
+// prepared down layout stores that column block contiguously): 3 * H * B
+// bytes, copied straight into LDS with direct-to-LDS loads.  The workgroup
+// computes the slice's gate and up values, SwiGLU, and the slice's share of
+// the down projection for all H output rows, and stores it as tagged words
+// (value + call tag).  After all items, every workgroup sums a range of
+// outputs over the slices (slice order fixed) and the k experts (top-k order)
+// plus the shared expert: the same fixed order as the other launches, and no
+// floating-point atomics.  Grouping (forum thread "把 Strata 搬上 SGLang 引擎
+// 的嘗試", §二, the expert-scoped layout): only the experts some row routes
+// to are read, each once per window.
+#include <type_traits>
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int SPL_THREADS = 512;
+constexpr int SPL_WAVES = SPL_THREADS / 64;
+
+// ---------------------------------------------------------------------------
+// Layouts for the integer dot products.  A "pair" is 64 consecutive k of a
+// gate/up row (two blocks), or the same block of two consecutive down rows.
+// Nibble-dwords: the 32-bit words whose eight nibbles multiply eight
+// activation digits.  4-bit: the pair's 9 dwords (36 bytes) themselves;
+// nibbles of scale bytes meet zero digits.  3-bit (28 bytes, 7 dwords): the
+// low-bit fields of dwords 0, 1, 2, 4, 5 masked two ways (10 nibble-dwords)
+// and each block's third-bit word spread four ways (8 nibble-dwords).
+// ---------------------------------------------------------------------------
+template <int BITS>
+struct SFmt;
+template <>
+struct SFmt<4> {
+    static constexpr int bb = 18;   // bytes per block
+    static constexpr int pb = 36;   // bytes per pair
+    static constexpr int pw = 9;    // dwords per pair
+    static constexpr int nnd = 9;   // nibble-dwords per pair
+    static constexpr int xpd = 36;  // digit dwords per pair: [digit 4][nibble-dword 9]
+};
+template <>
+struct SFmt<3> {
+    static constexpr int bb = 14;
+    static constexpr int pb = 28;
+    static constexpr int pw = 7;
+    static constexpr int nnd = 18;
+    static constexpr int xpd = 80;  // [low fields 10][digit 4], then [third bits 8][digit 5]
+};
+
+// k (0..63 within the pair) that nibble i of nibble-dword nd multiplies, or -1.
+template <int BITS>
+__device__ __forceinline__ int nibble_k(int nd, int i) {
+    const int h = i & 1;
+    if constexpr (BITS == 4) {
+        // byte 2+j of a block: code j (low nibble), code j+16 (high nibble)
+        const int beta = 4 * nd + (i >> 1);
+        if (beta >= 2 && beta <= 17) return beta - 2 + 16 * h;
+        if (beta >= 20 && beta <= 35) return 32 + beta - 20 + 16 * h;
+        return -1;  // a scale byte
+    } else {
+        if (nd < 10) {
+            // low parts: byte 2+j of a block holds the two low bits of codes
+            // j, j+8, j+16, j+24 (fields 0..3); mask a keeps fields 0 and 2 as
+            // the low and high nibble of the byte, mask b (after >> 2) fields 1, 3
+            const int w = nd >> 1;
+            const int beta = 4 * w + (w >= 3 ? 4 : 0) + (i >> 1);  // dwords 0, 1, 2, 4, 5
+            int B, j;
+            if (beta >= 2 && beta <= 9) {
+                B = 0;
+                j = beta - 2;
+            } else if (beta >= 16 && beta <= 23) {
+                B = 1;
+                j = beta - 16;
+            } else {
+                return -1;  // scale or third-bit bytes
+            }
+            const int f = (nd & 1) ? (h ? 3 : 1) : (h ? 2 : 0);
+            return 32 * B + j + 8 * f;
+        } else {
+            // third bits: word bit q is code q's; spread s takes bits 4m + s
+            const int u = nd - 10, B = u >> 2, s = u & 3;
+            return 32 * B + 4 * i + s;
+        }
+    }
+}
+
+// Digit dwords of nibble-dword nd from integer activations src[k & kmask]
+// (kmask 63: a pair of blocks of one row; 31: one block read by two rows).
+template <int BITS>
+__device__ __forceinline__ void build_digits(const int16_t *src, int kmask, int nd, uint32_t *dst) {
+    const bool third = BITS == 3 && nd >= 10;
+    uint32_t D[5] = {0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int kk = nibble_k<BITS>(nd, i);
+        int v = kk >= 0 ? (int)src[kk & kmask] : 0;
+        if (third) v *= 4;
+#pragma unroll
+        for (int j = 0; j < 5; ++j) {  // signed radix-16 digits in [-8, 7]
+            const int n = ((v + 8) & 15) - 8;
+            D[j] |= (uint32_t)(n & 15) << (4 * i);
+            v = (v - n) >> 4;
+        }
+    }
+    if constexpr (BITS == 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[j * 9 + nd] = D[j];
+    } else {
+        if (!third) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[nd * 4 + j] = D[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 5; ++j) dst[40 + (nd - 10) * 5 + j] = D[j];
+        }
+    }
+}
+
+__device__ __forceinline__ int sdot8(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot8((int)a, (int)b, c, false);
+}
+// a0 + 16 a1 + 256 a2 + ...
+template <int N>
+__device__ __forceinline__ int radix16(const int (&a)[N]) {
+    int v = a[N - 1];
+#pragma unroll
+    for (int j = N - 2; j >= 0; --j) v = (v << 4) + a[j];
+    return v;
+}
+
+// Weights of one pair, unpacked once for all rows.
+template <int BITS>
+struct SPair;
+
+template <>
+struct SPair<4> {
+    uint32_t wx[9];
+    float d0, d1;
+    __device__ __forceinline__ void set(const uint32_t (&w)[9]) {
+#pragma unroll
+        for (int q = 0; q < 9; ++q) wx[q] = w[q] ^ 0x88888888u;  // nibble c -> signed c - 8
+        d0 = half_bits_to_float(w[0] & 0xFFFFu);
+        d1 = half_bits_to_float(w[4] >> 16);
+    }
+    // exact integer dot products of block 0 and block 1 with a row's digits xd
+    __device__ __forceinline__ void blocks(const uint32_t *xd, int, int, int &A0, int &A1) const {
+        int a0[4], a1[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int s0 = 0, s1 = 0;
+#pragma unroll
+            for (int q = 0; q < 5; ++q) s0 = sdot8(wx[q], xd[j * 9 + q], s0);
+#pragma unroll
+            for (int q = 5; q < 9; ++q) s1 = sdot8(wx[q], xd[j * 9 + q], s1);
+            a0[j] = s0;
+            a1[j] = s1;
+        }
+        A0 = radix16(a0);
+        A1 = radix16(a1);
+    }
+};
+
+template <>
+struct SPair<3> {
+    uint32_t N[10], M[8];
+    float d0, d1;
+    __device__ __forceinline__ void set(const uint32_t (&w)[7]) {
+        const uint32_t lw[5] = {w[0], w[1], w[2], w[4], w[5]};
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            N[2 * i] = lw[i] & 0x33333333u;
+            N[2 * i + 1] = (lw[i] >> 2) & 0x33333333u;
+        }
+        const uint32_t h0 = __builtin_amdgcn_alignbyte(w[3], w[2], 2u);  // block 0 bytes 10..13
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            M[s] = (h0 >> s) & 0x11111111u;
+            M[4 + s] = (w[6] >> s) & 0x11111111u;
+        }
+        d0 = half_bits_to_float(w[0] & 0xFFFFu);
+        d1 = half_bits_to_float(w[3] >> 16);
+    }
+    // S0, S1: the row's sums of the activations over block 0 / 1 (the -4a term)
+    __device__ __forceinline__ void blocks(const uint32_t *xd, int S0, int S1, int &A0, int &A1) const {
+        int a0[5], a1[5];
+#pragma unroll
+        for (int j = 0; j < 5; ++j) {
+            int s0 = j == 0 ? -4 * S0 : 0, s1 = j == 0 ? -4 * S1 : 0;
+            if (j < 4) {
+#pragma unroll
+                for (int nd = 0; nd < 6; ++nd) s0 = sdot8(N[nd], xd[nd * 4 + j], s0);
+#pragma unroll
+                for (int nd = 6; nd < 10; ++nd) s1 = sdot8(N[nd], xd[nd * 4 + j], s1);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) s0 = sdot8(M[u], xd[40 + u * 5 + j], s0);
+#pragma unroll
+            for (int u = 4; u < 8; ++u) s1 = sdot8(M[u], xd[40 + u * 5 + j], s1);
+            a0[j] = s0;
+            a1[j] = s1;
+        }
+        A0 = radix16(a0);
+        A1 = radix16(a1);
+    }
+};
+
+template <int N>
+__device__ __forceinline__ void lds_read_dwords(const uint8_t *p, uint32_t (&w)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) w[i] = *(const uint32_t *)(p + 4 * i);
+}
+// 16-byte aligned
+template <int N>
+__device__ __forceinline__ void lds_read_b128(const uint8_t *p, uint32_t (&w)[N]) {
+    static_assert(N % 4 == 0, "whole 16-byte reads");
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+        const u32x4 v = *(const u32x4 *)(p + 16 * i);
+        w[4 * i] = v.x;
+        w[4 * i + 1] = v.y;
+        w[4 * i + 2] = v.z;
+        w[4 * i + 3] = v.w;
+    }
+}
+
+// One 16-byte piece per lane from global memory straight into LDS at
+// lds_wave + 16 * lane (lds_wave the same for the whole wave).
+__device__ __forceinline__ void lds_dma16(const void *g, uint8_t *lds_wave) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds_wave, 16, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// The kernel
+// ---------------------------------------------------------------------------
+template <int BITS, int T_, int XF32>
+__global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
+    using F_ = SFmt<BITS>;
+    constexpr int bb = F_::bb, pb = F_::pb, xpd = F_::xpd;
+    extern __shared__ __align__(16) uint8_t smem[];
+    SplitSmall &sm = *(SplitSmall *)(smem + P.lds_small);
+    uint8_t *s_wt = smem + P.lds_wt;                    // item weights: gate rows | up rows | down column
+    int16_t *s_a = (int16_t *)(smem + P.lds_a);         // [T][H] integer activations
+    int *s_S = (int *)(smem + P.lds_S);                 // [T][H/32] block sums (3-bit)
+    uint32_t *s_xd = (uint32_t *)(smem + P.lds_xd);     // [T][H/64][xpd] activation digits
+    float *s_gu = (float *)(smem + P.lds_gu);           // [T][64] gate then up values of the slice
+    int16_t *s_ah = (int16_t *)(smem + P.lds_ah);       // [T][32] integer h of the slice
+    uint32_t *s_hd = (uint32_t *)(smem + P.lds_hd);     // [T][xpd] h digits
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = gridDim.x;
+    const int k = P.k, E = P.E, H = P.H;
+    const int TK = T_ * k;
+    const bool has_shared = (P.mode & DEC_MODE_SHARED) != 0;
+    const int hs = has_shared ? 1 : 0;
+    const bool route_mode = (P.mode & DEC_MODE_ROUTE) != 0;
+    const int nc = P.nc, ncs = has_shared ? P.ncs : 0;
+    const int RB = H * bb;              // bytes of each item region
+    const int np = RB >> 4;             // 16-byte pieces per region
+    const int npairs = H >> 6;          // pairs per gate/up row
+    const size_t eb = (size_t)3 * P.F * P.rowH;
+
+    // ---- item -> (slot, column slice) and its three regions in global memory
+    auto item_slot = [&](int it, int &c) {
+        if (it < ncs) {
+            c = it;
+            return 0;
+        }
+        const int j = it - ncs;
+        const int s = nc == 1 ? j : (int)__umulhi((uint32_t)j, P.m_nc);
+        c = j - s * nc;
+        return hs + s;
+    };
+    auto issue_item = [&](int it, int parts) {  // parts: 1 gate/up, 2 down
+        int c;
+        const int s = item_slot(it, c);
+        const bool sh = s < hs;
+        const int Fx = sh ? P.Fs : P.F;
+        const uint8_t *blob = sh ? P.w_shared : P.w_routed + (size_t)sm.slot_exp[s] * eb;
+        const uint8_t *g0 = blob + (size_t)c * 32 * P.rowH;                // gate rows 32c..
+        const uint8_t *u0 = blob + (size_t)(Fx + c * 32) * P.rowH;         // up rows 32c..
+        const uint8_t *d0 = blob + (size_t)2 * Fx * P.rowH + (size_t)c * RB;  // down column block c
+        const int p0 = (parts & 1) ? 0 : 2 * np, p1 = (parts & 2) ? 3 * np : 2 * np;
+        for (int cb = p0 + wave * 64; cb < p1; cb += SPL_THREADS) {
+            const int pc = cb + lane;
+            if (pc < p1) {
+                const int r = pc < np ? 0 : pc < 2 * np ? 1 : 2;
+                const uint8_t *src = (r == 0 ? g0 : r == 1 ? u0 : d0) + (size_t)(pc - r * np) * 16;
+                lds_dma16(src, s_wt + (size_t)cb * 16);
+            }
+        }
+    };
+
+    // ======================= Phase A: routing, activations, slots =======================
+    const uint32_t tag_v = ld_dev_u32(P.epoch);
+    if (tid < T_) sm.xmax[tid] = 0u;
+    // the shared expert's items need no routing: their weights stream in now
+    if ((int)blockIdx.x < ncs) issue_item(blockIdx.x, 3);
+    __syncthreads();
+
+    // activations: thread tid holds elements 8 tid .. 8 tid + 7 of [T][H]
+    const int nx = T_ * H;
+    const bool has_x = 8 * tid < nx;
+    const int xt = has_x ? (8 * tid) / H : 0, xk = has_x ? 8 * tid - xt * H : 0;
+    float xv[8];
+    auto load_x = [&]() {
+        const int e0 = has_x ? 8 * tid : 0;
+        if constexpr (XF32) {
+            const u32x4 a = *(const u32x4 *)((const float *)P.x + e0);
+            const u32x4 b = *(const u32x4 *)((const float *)P.x + e0 + 4);
+            const uint32_t wv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xv[i] = __builtin_bit_cast(float, wv[i]);
+        } else {
+            const u32x4 a = *(const u32x4 *)((const uint16_t *)P.x + e0);
+            const uint32_t wv[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xv[2 * i] = __builtin_bit_cast(float, wv[i] << 16);
+                xv[2 * i + 1] = __builtin_bit_cast(float, wv[i] & 0xFFFF0000u);
+            }
+        }
+    };
+    if (route_mode && wave < T_) {
+        // routing of row `wave` by this wave: logits first, then its activations
+        const int epl = (E + 63) >> 6;
+        auto route_wave = [&](auto epl_c) {
+            constexpr int EPL = decltype(epl_c)::value;
+            uint32_t key[EPL];
+            route_keys<EPL>(P.logits + (size_t)wave * E, E, lane, key);
+            load_x();
+            route_pick<EPL>(key, k, sm.idx + wave * k, sm.w + wave * k, lane);
+        };
+        if (epl <= 2) route_wave(std::integral_constant<int, 2>{});
+        else if (epl <= 4) route_wave(std::integral_constant<int, 4>{});
+        else if (epl <= 8) route_wave(std::integral_constant<int, 8>{});
+        else route_wave(std::integral_constant<int, 16>{});
+    } else {
+        load_x();
+    }
+    {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(xv[i]));
+        const uint32_t mb = has_x ? __builtin_bit_cast(uint32_t, m) : 0u;
+        if ((H & 511) == 0) {  // a wave's 512 elements lie in one row
+            const uint32_t wm = wave_max_u32(mb);
+            if (lane == 0 && has_x) atomicMax(&sm.xmax[xt], wm);
+        } else if (has_x) {
+            atomicMax(&sm.xmax[xt], mb);
+        }
+    }
+    __syncthreads();  // routing and the row maxima complete
+    const uint32_t tag = decode_tag(__builtin_amdgcn_readfirstlane(tag_v));
+
+    // integer activations a = rint(x * 2^sc), max |x| * 2^sc in [2^13, 2^14)
+    {
+        const float mx = __builtin_bit_cast(float, sm.xmax[xt]);
+        int ex = 0;
+        if (mx > 0.0f) frexpf(mx, &ex);
+        const int sc = mx > 0.0f ? 14 - ex : 0;
+        const float scale = __builtin_bit_cast(float, (uint32_t)(127 + sc) << 23);
+        int ai[8], bs = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            ai[i] = (int)rintf(xv[i] * scale);
+            bs += ai[i];
+        }
+        if (has_x) {
+            const u32x4 pk = {(uint32_t)(ai[0] & 0xFFFF) | ((uint32_t)ai[1] << 16),
+                              (uint32_t)(ai[2] & 0xFFFF) | ((uint32_t)ai[3] << 16),
+                              (uint32_t)(ai[4] & 0xFFFF) | ((uint32_t)ai[5] << 16),
+                              (uint32_t)(ai[6] & 0xFFFF) | ((uint32_t)ai[7] << 16)};
+            *(u32x4 *)(s_a + xt * H + xk) = pk;
+            if (xk == 0) sm.tinv[xt] = __builtin_bit_cast(float, (uint32_t)(127 - sc) << 23);
+        }
+        if (BITS == 3) {
+            // block sums: the four threads of a block are consecutive lanes
+            bs += __builtin_amdgcn_update_dpp(0, bs, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+            bs += __builtin_amdgcn_update_dpp(0, bs, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+            if (has_x && (tid & 3) == 0) s_S[xt * (H >> 5) + (xk >> 5)] = bs;
+        }
+    }
+
+    // slots: the shared expert (slot 0 when present), then the routed experts
+    // in order of first use (row 0's top-k order, then row 1's new ones)
+    if (wave == 0) {
+        if (route_mode) {
+            const int p = lane;
+            const bool valid = p < TK;
+            const int e = valid ? sm.idx[p] : -1;
+            const int t = p >= k ? 1 : 0;
+            bool owner = valid;
+            if (valid && t == 1)
+                for (int q = 0; q < k; ++q) owner = owner && sm.idx[q] != e;
+            const uint64_t om = __ballot(owner);
+            const int slot = hs + __popcll(om & ((1ull << lane) - 1ull));
+            if (owner) {
+                sm.slot_exp[slot] = e;
+                sm.slot_pair[slot][t] = p;
+                if (T_ == 2) sm.slot_pair[slot][1 - t] = -1;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (valid && !owner) {  // row 1's pick of an expert row 0 also chose
+                int q = 0;
+                for (int qq = 0; qq < k; ++qq)
+                    if (sm.idx[qq] == e) q = qq;
+                sm.slot_pair[hs + __popcll(om & ((1ull << q) - 1ull))][1] = p;
+            }
+            if (lane == 0) sm.n_slots = hs + __popcll(om);
+        } else {
+            // a grouping given by the caller, sanitized so that bad entries
+            // give a wrong answer (and err bit 1) but never an access out of bounds
+            int na = P.g_active[0];
+            const int lim = min(E, TK);
+            if (na < 0 || na > lim) {
+                if (lane == 0) atomicOr(P.err, 2u);
+                na = na < 0 ? 0 : lim;
+            }
+            for (int a = lane; a < na; a += 64) {
+                int e = P.g_active[1 + a];
+                int st = 0, cnt = 0;
+                if (e >= 0 && e < E) {
+                    st = P.g_offsets[e];
+                    cnt = P.g_offsets[e + 1] - st;
+                }
+                if (e < 0 || e >= E || st < 0 || cnt < 0 || cnt > T_ || st + cnt > TK) {
+                    atomicOr(P.err, 2u);
+                    e = (e >= 0 && e < E) ? e : 0;
+                    cnt = 0;
+                }
+                sm.slot_exp[hs + a] = e;
+                int pr[SPL_MAX_T] = {-1, -1};
+                for (int q = 0; q < cnt; ++q) {
+                    int p = P.g_pairs[st + q];
+                    if (p < 0 || p >= TK) {
+                        atomicOr(P.err, 2u);
+                        continue;
+                    }
+                    pr[p >= k ? 1 : 0] = p;
+                }
+#pragma unroll
+                for (int t = 0; t < T_; ++t) sm.slot_pair[hs + a][t] = pr[t];
+            }
+            for (int p = lane; p < TK; p += 64) sm.w[p] = P.g_pair_w ? P.g_pair_w[p] : 1.0f;
+            if (lane == 0) sm.n_slots = hs + na;
+        }
+        if (lane == 0 && has_shared) {
+            sm.slot_exp[0] = -1;
+#pragma unroll
+            for (int t = 0; t < T_; ++t) sm.slot_pair[0][t] = TK + t;
+        }
+        if (!(P.mode & DEC_MODE_COMBINE)) {
+            // the pairs present, for the per-pair outputs
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (lane == 0) {
+                int n = 0;
+                for (int s = 0; s < sm.n_slots; ++s)
+                    for (int t = 0; t < T_; ++t)
+                        if (sm.slot_pair[s][t] >= 0) sm.plist[n++] = sm.slot_pair[s][t];
+                sm.n_pl = n;
+            }
+        }
+    }
+    if (blockIdx.x == 0 && route_mode && wave == 1) {
+        for (int p = lane; p < TK; p += 64) {
+            if (P.topk_idx_out) P.topk_idx_out[p] = sm.idx[p];
+            if (P.topk_w_out) P.topk_w_out[p] = sm.w[p];
+        }
+    }
+    __syncthreads();  // slots, integer activations, block sums
+    const int n_slots = sm.n_slots;
+    const int n_items = ncs + (n_slots - hs) * nc;
+    int it = blockIdx.x;
+    if (it < n_items && it >= ncs) issue_item(it, 3);
+
+    // activation digits: (row, pair, nibble-dword) tasks
+    {
+        const int ntask = T_ * npairs * F_::nnd;
+        for (int q = tid; q < ntask; q += SPL_THREADS) {
+            const int t = q / (npairs * F_::nnd);
+            const int r = q - t * npairs * F_::nnd;
+            const int pr = r / F_::nnd, nd = r - pr * F_::nnd;
+            build_digits<BITS>(s_a + t * H + pr * 64, 63, nd, s_xd + ((size_t)t * npairs + pr) * xpd);
+        }
+    }
+
+    // ======================= Phase B: items =======================
+    const int lg_qpr = P.lg_qpr, qpr = 1 << lg_qpr;
+    const int gu_tasks = 64 << lg_qpr;
+    int my_items = 0;
+    for (; it < n_items; it += G) {
+        int c;
+        const int s = item_slot(it, c);
+        wait_all_mem();   // this thread's part of the item's weights is in LDS
+        __syncthreads();  // ... and everyone's (also: digits of the first item)
+
+        // gate/up: task (row r of the 64, piece m of 4 pairs)
+        bool row_in[T_];
+#pragma unroll
+        for (int t = 0; t < T_; ++t) row_in[t] = sm.slot_pair[s][t] >= 0;
+        if (tid < gu_tasks) {
+            const int r = tid >> lg_qpr, m = tid & (qpr - 1);
+            float acc[T_];
+#pragma unroll
+            for (int t = 0; t < T_; ++t) acc[t] = 0.0f;
+            const uint8_t *wr = s_wt + (size_t)r * P.rowH + (size_t)m * 4 * pb;
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                const int pr = 4 * m + pp;
+                uint32_t w[F_::pw];
+                lds_read_dwords<F_::pw>(wr + pp * pb, w);
+                SPair<BITS> sp;
+                sp.set(w);
+#pragma unroll
+                for (int t = 0; t < T_; ++t) {
+                    if (!row_in[t]) continue;  // (uniform over the workgroup)
+                    uint32_t xd[xpd];
+                    lds_read_b128<xpd>((const uint8_t *)(s_xd + ((size_t)t * npairs + pr) * xpd), xd);
+                    const int S0 = BITS == 3 ? s_S[t * (H >> 5) + 2 * pr] : 0;
+                    const int S1 = BITS == 3 ? s_S[t * (H >> 5) + 2 * pr + 1] : 0;
+                    int A0, A1;
+                    sp.blocks(xd, S0, S1, A0, A1);
+                    acc[t] = fmaf(sp.d0, (float)A0, acc[t]);
+                    acc[t] = fmaf(sp.d1, (float)A1, acc[t]);
+                }
+            }
+            // sum over the row's pieces (consecutive lanes; a fixed tree)
+#pragma unroll
+            for (int t = 0; t < T_; ++t) {
+                float v = acc[t];
+                if (qpr >= 2) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+                if (qpr >= 4) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+                if (qpr >= 8) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+                if (m == 0) s_gu[t * 64 + r] = v;
+            }
+        }
+        __syncthreads();  // gate/up values; the gate/up regions are free
+        const int nxt = it + G;
+        if (nxt < n_items) issue_item(nxt, 1);
+
+        // SwiGLU and the h digits: wave t for row t
+        if (wave < T_) {
+            const int t = wave;
+            float h = 0.0f;
+            if (lane < 32) {
+                const float ti = sm.tinv[t];
+                const float g = s_gu[t * 64 + lane] * ti, u = s_gu[t * 64 + 32 + lane] * ti;
+                h = g / (1.0f + expf(-g)) * u;
+            }
+            const float mx = __builtin_bit_cast(float, wave_max_u32(__builtin_bit_cast(uint32_t, fabsf(h))));
+            int ex = 0;
+            if (mx > 0.0f) frexpf(mx, &ex);
+            const int sc = mx > 0.0f ? 14 - ex : 0;
+            const int ah = (int)rintf(h * __builtin_bit_cast(float, (uint32_t)(127 + sc) << 23));
+            if (lane < 32) s_ah[t * 32 + lane] = (int16_t)ah;
+            if (BITS == 3) {
+                int sum = ah;
+#pragma unroll
+                for (int off = 16; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+                if (lane == 0) sm.Sh[t] = sum;
+            }
+            if (lane == 0) sm.hinv[t] = __builtin_bit_cast(float, (uint32_t)(127 - sc) << 23);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (lane < F_::nnd) build_digits<BITS>(s_ah + t * 32, 31, lane, s_hd + t * xpd);
+        }
+        __syncthreads();  // h digits
+
+        // down: row pairs (2 rp, 2 rp + 1) of column block c; partial rows stored tagged
+        {
+            const uint8_t *dcol = s_wt + 2 * (size_t)RB;
+            int pid[T_];
+            float hinv[T_];
+            int Sh[T_];
+#pragma unroll
+            for (int t = 0; t < T_; ++t) {
+                pid[t] = sm.slot_pair[s][t];
+                hinv[t] = sm.hinv[t];
+                Sh[t] = BITS == 3 ? sm.Sh[t] : 0;
+            }
+            uint32_t hd[T_][xpd];
+#pragma unroll
+            for (int t = 0; t < T_; ++t) lds_read_b128<xpd>((const uint8_t *)(s_hd + t * xpd), hd[t]);
+            for (int rp = tid; rp < (H >> 1); rp += SPL_THREADS) {
+                uint32_t w[F_::pw];
+                lds_read_dwords<F_::pw>(dcol + (size_t)rp * pb, w);
+                SPair<BITS> sp;
+                sp.set(w);
+#pragma unroll
+                for (int t = 0; t < T_; ++t) {
+                    if (pid[t] < 0) continue;
+                    // the pair's two blocks are the rows 2rp and 2rp + 1
+                    int A0, A1;
+                    sp.blocks(hd[t], Sh[t], Sh[t], A0, A1);
+                    uint64_t *dst = P.part + ((size_t)pid[t] * P.ncmax + c) * H + 2 * rp;
+                    st_tagged(dst, sp.d0 * (float)A0 * hinv[t], tag);
+                    st_tagged(dst + 1, sp.d1 * (float)A1 * hinv[t], tag);
+                }
+            }
+        }
+        ++my_items;
+        __syncthreads();  // the down column is free
+        if (nxt < n_items) issue_item(nxt, 2);
+    }
+
+    // ======================= Phase C: sums over the slices =======================
+    __syncthreads();  // every thread's partial stores are issued
+    if (tid == 0) {
+        if (my_items) add_dev(P.items_done, (uint32_t)my_items);
+        uint32_t spins = 0;
+        while (ld_dev_u32(P.items_done) < (uint32_t)n_items) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins > DEC_SPIN_LIMIT || (ld_dev_u32(P.err) & 1u)) {
+                atomicOr(P.err, 1u);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    // outputs: COMBINE: (row t, output h) -> y; else (present pair, output h)
+    const bool combine = (P.mode & DEC_MODE_COMBINE) != 0;
+    const int n_out = combine ? T_ * H : sm.n_pl * H;
+    const int u0 = blockIdx.x * P.units;
+    const int nu = max(0, min(P.units, n_out - u0));
+    const int nterm = combine ? k + hs : 1;
+    float *s_red = (float *)s_wt;  // [units][nterm]
+    for (int q = tid; q < nu * nterm; q += SPL_THREADS) {
+        const int ul = q / nterm, j = q - ul * nterm;
+        const int u = u0 + ul;
+        const int t = u / H, row = u - t * H;
+        int p;
+        float wgt;
+        if (combine) {
+            p = j < k ? t * k + j : TK + t;
+            wgt = j < k ? sm.w[p] : 1.0f;
+        } else {
+            p = sm.plist[t];
+            wgt = p < TK ? sm.w[p] : 1.0f;
+        }
+        const int ncx = p >= TK ? ncs : nc;
+        const uint64_t *src = P.part + (size_t)p * P.ncmax * H + row;
+        float sum = 0.0f;
+        for (int c0 = 0; c0 < ncx; c0 += 8) {
+            uint64_t wd[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) wd[i] = c0 + i < ncx ? ld_dev_u64(src + (size_t)(c0 + i) * H) : 0ull;
+            for (uint32_t spins = 0;; ++spins) {
+                bool ok = true;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) ok = ok && (c0 + i >= ncx || (uint32_t)(wd[i] >> 32) == tag);
+                if (ok) break;
+                if (spins > DEC_SPIN_LIMIT) {
+                    atomicOr(P.err, 1u);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (c0 + i < ncx && (uint32_t)(wd[i] >> 32) != tag) wd[i] = ld_dev_u64(src + (size_t)(c0 + i) * H);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (c0 + i < ncx) sum += __builtin_bit_cast(float, (uint32_t)wd[i]);
+        }
+        s_red[q] = wgt * sum;
+        if (!combine) {
+            if (p < TK) P.out_pairs[(size_t)p * H + row] = wgt * sum;
+            else P.out_shared[(size_t)(p - TK) * H + row] = sum;
+        }
+    }
+    if (combine) {
+        __syncthreads();
+        for (int ul = tid; ul < nu; ul += SPL_THREADS) {
+            const int u = u0 + ul;
+            float v = s_red[ul * nterm];
+            for (int j = 1; j < nterm; ++j) v += s_red[ul * nterm + j];
+            P.y[u] = v;
+        }
+    }
+
+    // ---- end of call: the last workgroup returns the counters to zero and
+    // advances the epoch (the next call's tag)
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t old = add_dev(P.done, 1u);
+        if (old == (uint32_t)(G - 1)) {
+            store_dev_u32(P.items_done, 0u);
+            store_dev_u32(P.done, 0u);
+            store_dev_u32(P.epoch, ld_dev_u32(P.epoch) + 1u);
+        }
+    }
+}
+
+template <int BITS, int T_, int XF32>
+static hipError_t split_launch_t(const SplitParams &P, int grid, hipStream_t st) {
+    hipLaunchKernelGGL((k_split_layer<BITS, T_, XF32>), dim3(grid), dim3(SPL_THREADS), P.lds_total, st, P);
+    return hipGetLastError();
+}
+
+template <int BITS, int T_, int XF32>
+static hipError_t split_attr_t(int lds) {
+    return hipFuncSetAttribute((const void *)k_split_layer<BITS, T_, XF32>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+}
+
+#define SPLIT_DISPATCH(FN, ...)                                                   \
+    do {                                                                          \
+        if (bits == 4) {                                                          \
+            if (T == 1) return xf ? FN<4, 1, 1>(__VA_ARGS__) : FN<4, 1, 0>(__VA_ARGS__); \
+            return xf ? FN<4, 2, 1>(__VA_ARGS__) : FN<4, 2, 0>(__VA_ARGS__);     \
+        }                                                                         \
+        if (T == 1) return xf ? FN<3, 1, 1>(__VA_ARGS__) : FN<3, 1, 0>(__VA_ARGS__); \
+        return xf ? FN<3, 2, 1>(__VA_ARGS__) : FN<3, 2, 0>(__VA_ARGS__);         \
+    } while (0)
+
+hipError_t split_launch(const SplitParams &P, int grid, hipStream_t st) {
+    const int bits = P.bits, T = P.T, xf = P.x_f32;
+    SPLIT_DISPATCH(split_launch_t, P, grid, st);
+}
+
+hipError_t split_set_lds(int bits, int T, int xf, int lds) { SPLIT_DISPATCH(split_attr_t, lds); }
+
+}  // namespace moe

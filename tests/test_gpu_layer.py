@@ -112,6 +112,41 @@ def test_edge_cases(orc):
     _check(orc, li, P)
 
 
+@pytest.mark.parametrize("T", [1, 2])
+def test_split_launch_shapes(orc, T):
+    """Windows of one or two rows take the column-split launch (integer dot
+    products): both weight formats, fp32 and bf16 activations, every hidden
+    size it takes (256 .. 2048), with and without a shared expert (of another
+    width), k = E, E = k = 1, tied logits, zero and large activations."""
+    cases = [
+        ("tiny", _cfg("tiny", name="sp_tiny")),                                   # H 256, fp32 x, 4-bit
+        ("h512", _cfg("decode", name="sp_h512", n_experts=16, hidden=512, ffn=256, shared_ffn=1024)),
+        ("h1024_3b", _cfg("e512", name="sp_h1024", n_experts=40, hidden=1024, ffn=768, shared_ffn=0)),
+        ("kE", _cfg("tiny", name="sp_kE", n_experts=6, top_k=6)),
+        ("e1", _cfg("tiny", name="sp_e1", n_experts=1, top_k=1)),
+        ("k32", _cfg("e512", name="sp_k32", n_experts=64, top_k=32, hidden=256, ffn=256, shared_ffn=256)),
+    ]
+    for tag, cfg in cases:
+        print(f"[split] {tag} T={T}", flush=True)
+        _check(orc, synth.layer_inputs(cfg, T=T, threads=2), D)
+    print(f"[split] tied logits T={T}", flush=True)
+    li = synth.layer_inputs(_cfg("e512", name="sp_tie", n_experts=64, hidden=512, ffn=256, shared_ffn=256),
+                            T=T, threads=2)
+    li = dataclasses.replace(li, logits=np.zeros_like(li.logits))
+    _check(orc, li, D)
+    print(f"[split] zero activations T={T}", flush=True)
+    y = DevLayer(dataclasses.replace(li, x=np.zeros_like(li.x))).forward(D)[0]
+    assert np.all(y == 0.0)
+    print(f"[split] large activations T={T}", flush=True)
+    li = synth.layer_inputs(_cfg("decode", name="sp_big", n_experts=16, hidden=512, ffn=256, shared_ffn=256),
+                            T=T, threads=2)
+    xb = (synth.bf16_bits_to_f32(li.x) * 3000.0).astype(np.float32)
+    _check(orc, dataclasses.replace(li, x=synth.f32_to_bf16_bits(xb)), D)
+    print(f"[split] real workloads T={T}", flush=True)
+    _check(orc, layer_inputs("decode", T), D)
+    _check(orc, layer_inputs("e512", T), D)
+
+
 def test_decode_matches_prefill(orc):
     """The two kernel families agree with each other on the same inputs."""
     print("[layer] decode vs prefill kernels", flush=True)
@@ -126,7 +161,7 @@ def test_decode_matches_prefill(orc):
 
 def test_run_twice_bitwise():
     print("[layer] run twice", flush=True)
-    for name, T, path in [("mtp16", 16, D), ("e512", 4, D), ("prefill", 512, P)]:
+    for name, T, path in [("mtp16", 16, D), ("e512", 4, D), ("decode", 1, D), ("e512", 2, D), ("prefill", 512, P)]:
         li = layer_inputs(name, T) if T == synth.CONFIGS[name].rows[0] else synth.layer_inputs(
             synth.CONFIGS[name], T=T)
         dl = DevLayer(li)
@@ -138,18 +173,33 @@ def test_run_twice_bitwise():
 
 
 def test_batch_invariance_decode():
-    """A row's output and routing weights are bitwise the same alone as inside
-    a 16-row window (the two take different routing code: per-row waves for
-    the window, all-thread ranks for the single row)."""
+    """A row's routing is bitwise the same in any window; its output is
+    bitwise the same in any window served by the same launch: the 16-row
+    window against 4-row windows (matrix-core launch), and 2-row windows
+    against single rows (column-split launch), both weight formats."""
     print("[layer] batch invariance", flush=True)
     li = layer_inputs("mtp16", 16)
     y16, i16, w16 = DevLayer(li).forward(D)
+    for t0 in (0, 4, 12):
+        sub = dataclasses.replace(li, T=4, x=li.x[t0:t0 + 4].copy(), logits=li.logits[t0:t0 + 4].copy())
+        y4, i4, w4 = DevLayer(sub).forward(D)
+        assert np.array_equal(i4, i16[t0:t0 + 4]), t0
+        assert np.array_equal(w4, w16[t0:t0 + 4]), t0
+        assert np.array_equal(y4, y16[t0:t0 + 4]), t0
     for t in range(16):
         one = dataclasses.replace(li, T=1, x=li.x[t:t + 1].copy(), logits=li.logits[t:t + 1].copy())
-        y1, i1, w1 = DevLayer(one).forward(D)
+        _, i1, w1 = DevLayer(one).forward(D)
         assert np.array_equal(i1[0], i16[t]), t
         assert np.array_equal(w1[0], w16[t]), t
-        assert np.array_equal(y1[0], y16[t]), t
+    for name in ("decode", "e512"):
+        li2 = layer_inputs(name, 2)
+        y2, i2, w2 = DevLayer(li2).forward(D)
+        for t in range(2):
+            one = dataclasses.replace(li2, T=1, x=li2.x[t:t + 1].copy(), logits=li2.logits[t:t + 1].copy())
+            y1, i1, w1 = DevLayer(one).forward(D)
+            assert np.array_equal(i1[0], i2[t]), (name, t)
+            assert np.array_equal(w1[0], w2[t]), (name, t)
+            assert np.array_equal(y1[0], y2[t]), (name, t)
 
 
 def test_workspace_reuse_across_shapes(orc):
@@ -158,7 +208,7 @@ def test_workspace_reuse_across_shapes(orc):
     print("[layer] workspace reuse", flush=True)
     cfg = synth.CONFIGS["e512"]
     ws = moe.workspace(16, cfg.n_experts, cfg.top_k, cfg.hidden, cfg.ffn, cfg.shared_ffn, D)
-    for T in (4, 1, 16, 3, 4):
+    for T in (4, 1, 16, 2, 3, 1, 4):
         li = synth.layer_inputs(cfg, T=T, layer=T)
         y, idx, _ = DevLayer(li).forward(D, ws=ws)
         yr, ir, _ = oracle_forward(orc, li)
@@ -168,7 +218,8 @@ def test_workspace_reuse_across_shapes(orc):
 
 # ---- the expert FFN entry point on a given grouping -------------------------------
 
-@pytest.mark.parametrize("name,T,path", [("tiny", 4, D), ("mtp16", 16, D), ("e512", 4, P), ("tiny", 40, P)])
+@pytest.mark.parametrize("name,T,path", [("tiny", 4, D), ("mtp16", 16, D), ("e512", 4, P), ("tiny", 40, P),
+                                         ("decode", 1, D), ("e512", 2, D), ("tiny", 2, D)])
 def test_expert_ffn(orc, name, T, path):
     print(f"[expert_ffn] {name} T={T} path={path}", flush=True)
     cfg = synth.CONFIGS[name]
