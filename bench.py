@@ -234,11 +234,16 @@ def main():
         metric_value, unit = gbs, "GB/s"
         kern_us = us_layer
         ach = (total_bytes / L) / (kern_us * 1e-6) / 1e9
+        # windows of one or two rows take the column-split launch (integer
+        # nibble dot products), larger windows the matrix-core launch
+        split = T <= 2
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
-                "kernel": "k_decode_layer", "bytes_per_launch": round(total_bytes / L),
+                "kernel": "k_split_layer" if split else "k_decode_layer", "bytes_per_launch": round(total_bytes / L),
                 "launch_us": round(kern_us, 3)}
-        dtype = "f16"  # MFMA inputs (exact integer codes, power-of-two-scaled activations), fp32 accumulate
+        # split: signed 4-bit products (codes x 16-bit activation digits), int32
+        # block sums, fp32 scale and accumulate; matrix-core: f16 MFMA, fp32 accumulate
+        dtype = "i4" if split else "f16"
     else:
         metric_value, unit = toks, "tok/s"
         ach = (fl_gu + fl_dn) / (kern_us * 1e-6) / 1e12

@@ -80,7 +80,8 @@ struct Layout {
 // layout, so a workspace that is zero before its first use stays valid for
 // calls of any shape and path (each call returns the counters to zero).  Each
 // counter has a 256-byte line of its own.
-constexpr size_t COUNTER_WORDS = (size_t)(2 * DEC_MAX_SLOTS + DEC_MAX_SLICES + 4) * DEC_CSTRIDE;
+// after the slot and slice counters: err, epoch, done shards, done top
+constexpr size_t COUNTER_WORDS = (size_t)(2 * DEC_MAX_SLOTS + DEC_MAX_SLICES + 2 + CNT_SHARDS + 1) * DEC_CSTRIDE;
 Layout make_layout(int T, int E, int k, int H, int F, int Fs, int path) {
     Layout L;
     size_t off = 0;
@@ -294,10 +295,10 @@ bool decode_fits(int T, int E, int k, int H, int F, int Fs, int bits, int x_dtyp
 }
 
 // ---- column-split decode launch (windows of one or two rows) ----
-int split_xpd(int bits) { return bits == 4 ? 36 : 80; }
+int split_xps(int bits) { return bits == 4 ? 36 : 84; }  // digit dwords per pair slot in LDS
 
 int split_lds_layout(SplitParams &P) {
-    const int bb = P.bits == 4 ? 18 : 14, xpd = split_xpd(P.bits);
+    const int bb = P.bits == 4 ? 18 : 14, xps = split_xps(P.bits);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t a = off;
@@ -308,21 +309,21 @@ int split_lds_layout(SplitParams &P) {
     P.lds_wt = take((size_t)3 * P.H * bb);
     P.lds_a = take((size_t)P.T * P.H * 2);
     P.lds_S = take((size_t)P.T * (P.H / 32) * 4);
-    P.lds_xd = take((size_t)P.T * (P.H / 64) * xpd * 4);
+    P.lds_xd = take((size_t)P.T * (P.H / 64) * xps * 4);
     P.lds_gu = take((size_t)P.T * 64 * 4);
     P.lds_ah = take((size_t)P.T * 32 * 2);
-    P.lds_hd = take((size_t)P.T * xpd * 4);
+    P.lds_hd = take((size_t)P.T * xps * 4);
     P.lds_total = (int)off;
     return P.lds_total;
 }
 
-// Reduction outputs per workgroup for a grid of G.
+// Reduction outputs per workgroup for a grid of G (whole chunks of 8).
 int split_units(int T, int k, int H, int combine, int G) {
     const long long n = combine ? (long long)T * H : (long long)T * k * H;
-    return (int)((n + G - 1) / G);
+    return (int)(((n + G - 1) / G + 7) / 8 * 8);
 }
 
-bool split_fits(int T, int E, int k, int H, int F, int Fs, int bits, int G) {
+bool split_fits(int T, int E, int k, int H, int F, int Fs, int bits, int combine, int G) {
     (void)E;
     if (T < 1 || T > SPL_MAX_T || k > 32) return false;
     if (H != 256 && H != 512 && H != 1024 && H != 2048) return false;
@@ -333,10 +334,11 @@ bool split_fits(int T, int E, int k, int H, int F, int Fs, int bits, int G) {
     P.H = H;
     P.bits = bits;
     if (split_lds_layout(P) > DEC_LDS_BUDGET) return false;
-    // the reduction stages (outputs x terms) floats in the item weight area
-    const int units = split_units(T, k, H, 0, G) > split_units(T, k, H, 1, G) ? split_units(T, k, H, 0, G)
-                                                                                : split_units(T, k, H, 1, G);
-    return (long long)units * (k + 1) * 4 <= (long long)3 * H * (bits == 4 ? 18 : 14);
+    // the reduction stages (outputs x terms x (slices + 1)) floats in the item weight area
+    const int units = split_units(T, k, H, combine, G);
+    const int nterm = combine ? k + 1 : 1;
+    const int ncmax = (F > Fs ? F : Fs) / 32;
+    return (long long)units * nterm * (ncmax + 1) * 4 <= (long long)3 * H * (bits == 4 ? 18 : 14);
 }
 
 }  // namespace
@@ -436,7 +438,8 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
     int rc = dev_info(dv);
     if (rc) return rc;
     const int Fs_ = shared ? shared->ffn : 0;
-    if (split_fits(T, E, k, routed->hidden, routed->ffn, Fs_, routed->bits, dv.cus)) {
+    if (split_fits(T, E, k, routed->hidden, routed->ffn, Fs_, routed->bits, (mode & DEC_MODE_COMBINE) ? 1 : 0,
+                   dv.cus)) {
         SplitParams S_;
         memset(&S_, 0, sizeof(S_));
         S_.x = x;
@@ -457,7 +460,7 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
         S_.err = cnt + (size_t)(2 * DEC_MAX_SLOTS + DEC_MAX_SLICES) * DEC_CSTRIDE;
         S_.epoch = S_.err + DEC_CSTRIDE;
         S_.done = S_.err + 2 * DEC_CSTRIDE;
-        S_.items_done = S_.err + 3 * DEC_CSTRIDE;
+        S_.done_top = S_.done + CNT_SHARDS * DEC_CSTRIDE;
         S_.T = T;
         S_.E = E;
         S_.k = k;
@@ -472,7 +475,11 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
         S_.ncmax = S_.nc > S_.ncs ? S_.nc : S_.ncs;
         S_.m_nc = magic_div(S_.nc);
         S_.rowH = (S_.H / 32) * (S_.bits == 4 ? 18 : 14);
-        S_.lg_qpr = ilog2(S_.H / 256);
+        {
+            const int npairs = S_.H / 64, tpr = npairs < 16 ? npairs : 16;
+            S_.lg_tpr = ilog2(tpr);
+            S_.lg_ppt = ilog2(npairs / tpr);
+        }
         const int grid = dv.cus;  // one workgroup per CU, all resident
         S_.units = split_units(T, k, S_.H, (mode & DEC_MODE_COMBINE) ? 1 : 0, grid);
         const int lds = split_lds_layout(S_);
@@ -513,6 +520,7 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
     P.err = cnt + (size_t)(2 * DEC_MAX_SLOTS + DEC_MAX_SLICES) * DEC_CSTRIDE;
     P.epoch = P.err + DEC_CSTRIDE;
     P.done = P.err + 2 * DEC_CSTRIDE;
+    P.done_top = P.done + CNT_SHARDS * DEC_CSTRIDE;
     P.T = T;
     P.E = E;
     P.k = k;
@@ -603,7 +611,7 @@ int moe_expert_ffn(const void *x, int32_t x_dtype, int32_t T, const moe_qweights
     if (rc) return rc;
     int p = resolve_path(path, T);
     if (p == MOE_PATH_DECODE &&
-        (T > MOE_DECODE_MAX_ROWS || !(split_fits(T, w->n_experts, k, w->hidden, w->ffn, 0, w->bits, 256) ||
+        (T > MOE_DECODE_MAX_ROWS || !(split_fits(T, w->n_experts, k, w->hidden, w->ffn, 0, w->bits, 0, 256) ||
                                       decode_fits(T, w->n_experts, k, w->hidden, w->ffn, 0, w->bits, x_dtype)))) {
         if (path == MOE_PATH_DECODE) return MOE_ERR_UNSUPPORTED;
         p = MOE_PATH_PREFILL;
@@ -643,7 +651,7 @@ int moe_layer_forward(const void *x, int32_t x_dtype, const float *logits, int32
     int p = resolve_path(path, T);
     const bool same_bits = !shared || shared->bits == routed->bits;
     if (p == MOE_PATH_DECODE && (T > MOE_DECODE_MAX_ROWS || !same_bits ||
-                                 !(split_fits(T, E, k, H, routed->ffn, Fs, routed->bits, 256) ||
+                                 !(split_fits(T, E, k, H, routed->ffn, Fs, routed->bits, 1, 256) ||
                                    decode_fits(T, E, k, H, routed->ffn, Fs, routed->bits, x_dtype)))) {
         if (path == MOE_PATH_DECODE) return MOE_ERR_UNSUPPORTED;
         p = MOE_PATH_PREFILL;

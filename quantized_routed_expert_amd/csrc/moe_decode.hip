@@ -1101,8 +1101,8 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
     TRACE(8);
     // the last workgroup to finish moves the workspace on to the next call's tag
     if (tid == 0) {
-        if (add_dev(P.done, 1u) == (uint32_t)(G - 1)) {
-            store_dev_u32(P.done, 0u);
+        if (last_workgroup(P.done, P.done_top, blockIdx.x, G, DEC_CSTRIDE)) {
+            store_dev_u32(P.done_top, 0u);
             store_dev_u32(P.epoch, ld_dev_u32(P.epoch) + 1u);
         }
     }

@@ -15,6 +15,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include "moe_internal.h"
 
 namespace moe {
 
@@ -202,6 +203,23 @@ __device__ __forceinline__ void store_dev_u32(uint32_t *p, uint32_t v) {
 }
 // all of this wave's memory operations have completed
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Counters that every workgroup of a grid updates are split into CNT_SHARDS
+// shards (one 256-byte line each, `stride` words apart): atomics to one
+// address are performed one after another, so a single counter hit by every
+// workgroup of a 256-workgroup grid would serialize all of them.
+// Counts workgroup b as finished; true for exactly one workgroup of the grid,
+// the last.  shards[b % 16] counts its workgroups, the workgroup completing a
+// shard returns it to zero and counts the shard in *top; the caller that gets
+// true must return *top to zero.
+__device__ __forceinline__ bool last_workgroup(uint32_t *shards, uint32_t *top, int b, int G, int stride) {
+    const int sh = b & (CNT_SHARDS - 1);
+    const uint32_t in_shard = (uint32_t)((G - sh + CNT_SHARDS - 1) / CNT_SHARDS);
+    const uint32_t n_shards = (uint32_t)(G < CNT_SHARDS ? G : CNT_SHARDS);
+    if (add_dev(shards + sh * stride, 1u) != in_shard - 1u) return false;
+    store_dev_u32(shards + sh * stride, 0u);
+    return add_dev(top, 1u) == n_shards - 1u;
+}
 
 // ---------------------------------------------------------------------------
 // Wave reductions on DPP (gfx9 row broadcasts); result valid in every lane.

@@ -20,6 +20,7 @@ constexpr int DEC_XG_BF16 = 8;              // activation k-groups (8 values) lo
 constexpr int DEC_XG_F32 = 4;               // ... fp32
 constexpr uint32_t DEC_SPIN_LIMIT = 1u << 20;  // bounded waits: a wait that runs out sets err bit 0
 constexpr int DEC_CSTRIDE = 64;              // 32-bit words between counters (one 256-byte line each)
+constexpr int CNT_SHARDS = 16;               // shards of a counter that every workgroup updates
 constexpr int DEC_RANK_MAX_KEYS = 2048;      // routing by ranks: T*E up to this ...
 constexpr int DEC_RANK_MAX_CMP = 64;         // ... and at most this many comparisons per thread
 #define MOE_MAX_EXPERTS_DEV 4096
@@ -92,7 +93,7 @@ struct DecodeParams {
     uint32_t *slice_count;     // [DEC_MAX_SLICES * DEC_CSTRIDE]: finished slots per 128-row slice
     uint32_t *err;             // error word (bit 0: a wait hit its spin limit; bit 1: bad given grouping)
     uint32_t *epoch;           // calls completed on this workspace (the tag source)
-    uint32_t *done;            // workgroups of this call that have finished
+    uint32_t *done, *done_top; // finished workgroups of this call: 16 shards, then shards completed
     int T, E, k, H, F, Fs;     // Fs = shared ffn (0 = none)
     int bits, x_f32, mode, max_slots;
     int h_stride;              // words per hll row (Fmax)
@@ -138,7 +139,7 @@ struct SplitSmall {  // fixed part of the launch's LDS
     int slot_exp[SPL_MAX_SLOTS];
     int slot_pair[SPL_MAX_SLOTS][SPL_MAX_T];  // pair id of each row in the slot, -1: none
     int plist[SPL_MAX_SLOTS * SPL_MAX_T];     // pairs present (output rows of the per-pair mode)
-    uint32_t xmax[SPL_MAX_T];
+    uint32_t wmax[8][SPL_MAX_T];  // per wave and row: largest |x| (as bits)
     float tinv[SPL_MAX_T], hinv[SPL_MAX_T];
     int Sh[SPL_MAX_T];
     int n_slots, n_pl, pad[2];
@@ -159,13 +160,12 @@ struct SplitParams {
     int32_t *topk_idx_out;     // may be null
     float *topk_w_out;         // may be null
     uint64_t *part;            // [T*k + T][ncmax][H] tagged partial down rows per (pair, slice)
-    uint32_t *items_done;      // finished items of this call (a hint: readers check tags)
-    uint32_t *err, *epoch, *done;
+    uint32_t *err, *epoch, *done, *done_top;
     int T, E, k, H, F, Fs, bits, mode, x_f32;
     int nc, ncs, ncmax;        // 32-column slices of F and Fs; the partial buffer's stride
     uint32_t m_nc;             // ceil(2^32 / nc) (0 when nc = 1)
     int rowH;                  // bytes of one gate/up row
-    int lg_qpr;                // log2 of the 4-pair pieces per gate/up row (H / 256)
+    int lg_tpr, lg_ppt;        // gate/up rows: log2 threads per row (<= 16), log2 pairs per thread (<= 2)
     int units;                 // reduction outputs per workgroup
     // LDS byte offsets
     int lds_small, lds_wt, lds_a, lds_S, lds_xd, lds_gu, lds_ah, lds_hd, lds_total;

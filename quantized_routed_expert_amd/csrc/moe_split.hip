@@ -38,6 +38,26 @@ namespace moe {
 constexpr int SPL_THREADS = 512;
 constexpr int SPL_WAVES = SPL_THREADS / 64;
 
+#ifdef MOE_PHASE_TRACE
+// Phase timestamps (100 MHz device clock) per workgroup, analysis builds only.
+__device__ uint64_t *g_trace_split = nullptr;
+#define STRACE_INIT volatile uint64_t *const strace_buf = g_trace_split
+#define STRACE(slot)                                                                                              \
+    do {                                                                                                          \
+        if (strace_buf && threadIdx.x == 0) strace_buf[blockIdx.x * 32 + (slot)] = __builtin_amdgcn_s_memrealtime(); \
+    } while (0)
+extern "C" int moe_trace_split_set(void *buf) {
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_trace_split), &buf, sizeof(buf)) == hipSuccess ? 0 : -1;
+}
+#else
+#define STRACE_INIT \
+    do {            \
+    } while (0)
+#define STRACE(slot) \
+    do {             \
+    } while (0)
+#endif
+
 // ---------------------------------------------------------------------------
 // Layouts for the integer dot products.  A "pair" is 64 consecutive k of a
 // gate/up row (two blocks), or the same block of two consecutive down rows.
@@ -56,6 +76,7 @@ struct SFmt<4> {
     static constexpr int pw = 9;    // dwords per pair
     static constexpr int nnd = 9;   // nibble-dwords per pair
     static constexpr int xpd = 36;  // digit dwords per pair: [digit 4][nibble-dword 9]
+    static constexpr int xps = 36;  // their stride in LDS
 };
 template <>
 struct SFmt<3> {
@@ -64,6 +85,7 @@ struct SFmt<3> {
     static constexpr int pw = 7;
     static constexpr int nnd = 18;
     static constexpr int xpd = 80;  // [low fields 10][digit 4], then [third bits 8][digit 5]
+    static constexpr int xps = 84;  // their stride in LDS (84 mod 64 banks spreads 8 pieces' reads)
 };
 
 // k (0..63 within the pair) that nibble i of nibble-dword nd multiplies, or -1.
@@ -105,6 +127,10 @@ __device__ __forceinline__ int nibble_k(int nd, int i) {
 
 // Digit dwords of nibble-dword nd from integer activations src[k & kmask]
 // (kmask 63: a pair of blocks of one row; 31: one block read by two rows).
+// Signed radix-16 digits n_j in [-8, 7] of v: with C = 8 * (1 + 16 + 16^2 +
+// ...), v + C = sum (n_j + 8) 16^j, so nibble j of v + C is n_j + 8 and
+// n_j as a 4-bit two's complement nibble is that nibble xor 8.  A missing
+// value (v = 0) gives zero digits.
 template <int BITS>
 __device__ __forceinline__ void build_digits(const int16_t *src, int kmask, int nd, uint32_t *dst) {
     const bool third = BITS == 3 && nd >= 10;
@@ -113,14 +139,13 @@ __device__ __forceinline__ void build_digits(const int16_t *src, int kmask, int 
     for (int i = 0; i < 8; ++i) {
         const int kk = nibble_k<BITS>(nd, i);
         int v = kk >= 0 ? (int)src[kk & kmask] : 0;
-        if (third) v *= 4;
+        // |v| <= 2^14, |4v| <= 2^16: four or five digits
+        const uint32_t u = third ? (uint32_t)(4 * v + 0x88888) : (uint32_t)(v + 0x8888);
 #pragma unroll
-        for (int j = 0; j < 5; ++j) {  // signed radix-16 digits in [-8, 7]
-            const int n = ((v + 8) & 15) - 8;
-            D[j] |= (uint32_t)(n & 15) << (4 * i);
-            v = (v - n) >> 4;
-        }
+        for (int j = 0; j < 5; ++j) D[j] |= ((u >> (4 * j)) & 15u) << (4 * i);
     }
+#pragma unroll
+    for (int j = 0; j < 5; ++j) D[j] ^= 0x88888888u;
     if constexpr (BITS == 4) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) dst[j * 9 + nd] = D[j];
@@ -254,13 +279,16 @@ __device__ __forceinline__ void lds_dma16(const void *g, uint8_t *lds_wave) {
 template <int BITS, int T_, int XF32>
 __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     using F_ = SFmt<BITS>;
-    constexpr int bb = F_::bb, pb = F_::pb, xpd = F_::xpd;
+    constexpr int bb = F_::bb, pb = F_::pb, xpd = F_::xpd, xps = F_::xps;
     extern __shared__ __align__(16) uint8_t smem[];
     SplitSmall &sm = *(SplitSmall *)(smem + P.lds_small);
     uint8_t *s_wt = smem + P.lds_wt;                    // item weights: gate rows | up rows | down column
     int16_t *s_a = (int16_t *)(smem + P.lds_a);         // [T][H] integer activations
     int *s_S = (int *)(smem + P.lds_S);                 // [T][H/32] block sums (3-bit)
-    uint32_t *s_xd = (uint32_t *)(smem + P.lds_xd);     // [T][H/64][xpd] activation digits
+    // [T][H/64 pair slots][xps] activation digits; pair 4m + j of a row sits in
+    // slot j * (H/256) + m, so the pieces m = 0, 1, ... that the lanes of a
+    // wave read together are xps dwords apart (distinct LDS banks)
+    uint32_t *s_xd = (uint32_t *)(smem + P.lds_xd);
     float *s_gu = (float *)(smem + P.lds_gu);           // [T][64] gate then up values of the slice
     int16_t *s_ah = (int16_t *)(smem + P.lds_ah);       // [T][32] integer h of the slice
     uint32_t *s_hd = (uint32_t *)(smem + P.lds_hd);     // [T][xpd] h digits
@@ -276,6 +304,8 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     const int RB = H * bb;              // bytes of each item region
     const int np = RB >> 4;             // 16-byte pieces per region
     const int npairs = H >> 6;          // pairs per gate/up row
+    // gate/up tasks: tpr threads per row, ppt consecutive pairs each
+    const int lg_tpr = P.lg_tpr, tpr = 1 << lg_tpr, lg_ppt = P.lg_ppt, ppt = 1 << lg_ppt;
     const size_t eb = (size_t)3 * P.F * P.rowH;
 
     // ---- item -> (slot, column slice) and its three regions in global memory
@@ -289,32 +319,55 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
         c = j - s * nc;
         return hs + s;
     };
-    auto issue_item = [&](int it, int parts) {  // parts: 1 gate/up, 2 down
+    // An item's three regions (gate rows, up rows, down column block; np
+    // 16-byte pieces each) are loaded into registers, NPER pieces per thread
+    // per region (pieces past np re-read piece 0 and are not staged), so
+    // every thread issues the same loads in the order they are needed: the
+    // wait for the gate rows leaves the up and down loads in flight.
+    constexpr int NPER = BITS == 4 ? 5 : 4;  // ceil(np / 512) at H = 2048
+    u32x4 rg[NPER], ru[NPER], rd[NPER];
+    auto issue_item_e = [&](int c, int e) {  // e: the routed expert, -1: the shared one
+        const bool sh = e < 0;
+        const int Fx = sh ? P.Fs : P.F;
+        const uint8_t *blob = sh ? P.w_shared : P.w_routed + (size_t)e * eb;
+        const uint8_t *g0 = blob + (size_t)c * 32 * P.rowH;                   // gate rows 32c..
+        const uint8_t *u0 = blob + (size_t)(Fx + c * 32) * P.rowH;            // up rows 32c..
+        const uint8_t *d0 = blob + (size_t)2 * Fx * P.rowH + (size_t)c * RB;  // down column block c
+#pragma unroll
+        for (int i = 0; i < NPER; ++i) {
+            const int pc = tid + i * SPL_THREADS, q = pc < np ? pc : 0;
+            rg[i] = *(const u32x4 *)(g0 + (size_t)q * 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // (keep the issue order: gate, up, down)
+#pragma unroll
+        for (int i = 0; i < NPER; ++i) {
+            const int pc = tid + i * SPL_THREADS, q = pc < np ? pc : 0;
+            ru[i] = *(const u32x4 *)(u0 + (size_t)q * 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NPER; ++i) {
+            const int pc = tid + i * SPL_THREADS, q = pc < np ? pc : 0;
+            rd[i] = *(const u32x4 *)(d0 + (size_t)q * 16);
+        }
+    };
+    auto issue_item = [&](int it) {
         int c;
         const int s = item_slot(it, c);
-        const bool sh = s < hs;
-        const int Fx = sh ? P.Fs : P.F;
-        const uint8_t *blob = sh ? P.w_shared : P.w_routed + (size_t)sm.slot_exp[s] * eb;
-        const uint8_t *g0 = blob + (size_t)c * 32 * P.rowH;                // gate rows 32c..
-        const uint8_t *u0 = blob + (size_t)(Fx + c * 32) * P.rowH;         // up rows 32c..
-        const uint8_t *d0 = blob + (size_t)2 * Fx * P.rowH + (size_t)c * RB;  // down column block c
-        const int p0 = (parts & 1) ? 0 : 2 * np, p1 = (parts & 2) ? 3 * np : 2 * np;
-        for (int cb = p0 + wave * 64; cb < p1; cb += SPL_THREADS) {
-            const int pc = cb + lane;
-            if (pc < p1) {
-                const int r = pc < np ? 0 : pc < 2 * np ? 1 : 2;
-                const uint8_t *src = (r == 0 ? g0 : r == 1 ? u0 : d0) + (size_t)(pc - r * np) * 16;
-                lds_dma16(src, s_wt + (size_t)cb * 16);
-            }
+        issue_item_e(c, s < hs ? -1 : sm.slot_exp[s]);
+    };
+    auto stage = [&](const u32x4 (&r)[NPER], uint8_t *dst) {
+#pragma unroll
+        for (int i = 0; i < NPER; ++i) {
+            const int pc = tid + i * SPL_THREADS;
+            if (pc < np) *(u32x4 *)(dst + (size_t)pc * 16) = r[i];
         }
     };
 
     // ======================= Phase A: routing, activations, slots =======================
+    STRACE_INIT;
+    STRACE(0);
     const uint32_t tag_v = ld_dev_u32(P.epoch);
-    if (tid < T_) sm.xmax[tid] = 0u;
-    // the shared expert's items need no routing: their weights stream in now
-    if ((int)blockIdx.x < ncs) issue_item(blockIdx.x, 3);
-    __syncthreads();
 
     // activations: thread tid holds elements 8 tid .. 8 tid + 7 of [T][H]
     const int nx = T_ * H;
@@ -347,7 +400,9 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
             uint32_t key[EPL];
             route_keys<EPL>(P.logits + (size_t)wave * E, E, lane, key);
             load_x();
+            STRACE(10);
             route_pick<EPL>(key, k, sm.idx + wave * k, sm.w + wave * k, lane);
+            STRACE(11);
         };
         if (epl <= 2) route_wave(std::integral_constant<int, 2>{});
         else if (epl <= 4) route_wave(std::integral_constant<int, 4>{});
@@ -357,23 +412,40 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
         load_x();
     }
     {
+        // per wave and row: the largest |x|
         float m = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(xv[i]));
         const uint32_t mb = has_x ? __builtin_bit_cast(uint32_t, m) : 0u;
-        if ((H & 511) == 0) {  // a wave's 512 elements lie in one row
-            const uint32_t wm = wave_max_u32(mb);
-            if (lane == 0 && has_x) atomicMax(&sm.xmax[xt], wm);
-        } else if (has_x) {
-            atomicMax(&sm.xmax[xt], mb);
+#pragma unroll
+        for (int t = 0; t < T_; ++t) {
+            const uint32_t wm = wave_max_u32(xt == t ? mb : 0u);
+            if (lane == 0) sm.wmax[wave][t] = wm;
         }
     }
+    // the shared expert's items need no routing: their weights stream in now
+    if ((int)blockIdx.x < ncs) issue_item_e(blockIdx.x, -1);
     __syncthreads();  // routing and the row maxima complete
+    STRACE(1);
     const uint32_t tag = decode_tag(__builtin_amdgcn_readfirstlane(tag_v));
+    // a one-row window: its first routed item is known from the routing alone
+    // (slot hs + j is the row's j-th expert)
+    int it = blockIdx.x;
+    const bool early = T_ == 1 && route_mode;
+    if (early) {
+        const int n_items1 = ncs + k * nc;
+        if (it < n_items1 && it >= ncs) {
+            const int j = it - ncs, sl = nc == 1 ? j : (int)__umulhi((uint32_t)j, P.m_nc);
+            issue_item_e(j - sl * nc, sm.idx[sl]);
+        }
+    }
 
     // integer activations a = rint(x * 2^sc), max |x| * 2^sc in [2^13, 2^14)
     {
-        const float mx = __builtin_bit_cast(float, sm.xmax[xt]);
+        uint32_t mxb = 0u;
+#pragma unroll
+        for (int w = 0; w < SPL_WAVES; ++w) mxb = max(mxb, sm.wmax[w][xt]);
+        const float mx = __builtin_bit_cast(float, mxb);
         int ex = 0;
         if (mx > 0.0f) frexpf(mx, &ex);
         const int sc = mx > 0.0f ? 14 - ex : 0;
@@ -491,10 +563,10 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
         }
     }
     __syncthreads();  // slots, integer activations, block sums
+    STRACE(2);
     const int n_slots = sm.n_slots;
     const int n_items = ncs + (n_slots - hs) * nc;
-    int it = blockIdx.x;
-    if (it < n_items && it >= ncs) issue_item(it, 3);
+    if (!early && it < n_items && it >= ncs) issue_item(it);
 
     // activation digits: (row, pair, nibble-dword) tasks
     {
@@ -503,63 +575,72 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
             const int t = q / (npairs * F_::nnd);
             const int r = q - t * npairs * F_::nnd;
             const int pr = r / F_::nnd, nd = r - pr * F_::nnd;
-            build_digits<BITS>(s_a + t * H + pr * 64, 63, nd, s_xd + ((size_t)t * npairs + pr) * xpd);
+            const int slot = (pr & (ppt - 1)) * tpr + (pr >> lg_ppt);
+            build_digits<BITS>(s_a + t * H + pr * 64, 63, nd, s_xd + ((size_t)t * npairs + slot) * xps);
         }
     }
 
     // ======================= Phase B: items =======================
-    const int lg_qpr = P.lg_qpr, qpr = 1 << lg_qpr;
-    const int gu_tasks = 64 << lg_qpr;
-    int my_items = 0;
+    int my_items = 0;  // (for the trace points)
     for (; it < n_items; it += G) {
         int c;
         const int s = item_slot(it, c);
-        wait_all_mem();   // this thread's part of the item's weights is in LDS
-        __syncthreads();  // ... and everyone's (also: digits of the first item)
-
-        // gate/up: task (row r of the 64, piece m of 4 pairs)
+        if (my_items > 0) issue_item(it);
         bool row_in[T_];
 #pragma unroll
         for (int t = 0; t < T_; ++t) row_in[t] = sm.slot_pair[s][t] >= 0;
-        if (tid < gu_tasks) {
-            const int r = tid >> lg_qpr, m = tid & (qpr - 1);
-            float acc[T_];
+
+        // gate rows, then up rows: task (row r of the 32, piece `sub` of ppt
+        // pairs); the up rows still stream in while the gate rows compute
+        auto half_rows = [&](const uint8_t *wreg, int base_row) {
+            const int r = tid >> lg_tpr, sub = tid & (tpr - 1);
+            if (r < 32) {
+                float acc[T_];
 #pragma unroll
-            for (int t = 0; t < T_; ++t) acc[t] = 0.0f;
-            const uint8_t *wr = s_wt + (size_t)r * P.rowH + (size_t)m * 4 * pb;
+                for (int t = 0; t < T_; ++t) acc[t] = 0.0f;
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-                const int pr = 4 * m + pp;
-                uint32_t w[F_::pw];
-                lds_read_dwords<F_::pw>(wr + pp * pb, w);
-                SPair<BITS> sp;
-                sp.set(w);
+                for (int pp = 0; pp < 2; ++pp) {
+                    if (pp < ppt) {
+                        const int pr = sub * ppt + pp, slot = pp * tpr + sub;
+                        uint32_t w[F_::pw];
+                        lds_read_dwords<F_::pw>(wreg + (size_t)r * P.rowH + (size_t)pr * pb, w);
+                        SPair<BITS> sp;
+                        sp.set(w);
+#pragma unroll
+                        for (int t = 0; t < T_; ++t) {
+                            if (!row_in[t]) continue;  // (uniform over the workgroup)
+                            uint32_t xd[xpd];
+                            lds_read_b128<xpd>((const uint8_t *)(s_xd + ((size_t)t * npairs + slot) * xps), xd);
+                            const int S0 = BITS == 3 ? s_S[t * (H >> 5) + 2 * pr] : 0;
+                            const int S1 = BITS == 3 ? s_S[t * (H >> 5) + 2 * pr + 1] : 0;
+                            int A0, A1;
+                            sp.blocks(xd, S0, S1, A0, A1);
+                            acc[t] = fmaf(sp.d0, (float)A0, acc[t]);
+                            acc[t] = fmaf(sp.d1, (float)A1, acc[t]);
+                        }
+                    }
+                }
+                // sum over the row's tpr pieces (consecutive lanes; a fixed tree)
 #pragma unroll
                 for (int t = 0; t < T_; ++t) {
-                    if (!row_in[t]) continue;  // (uniform over the workgroup)
-                    uint32_t xd[xpd];
-                    lds_read_b128<xpd>((const uint8_t *)(s_xd + ((size_t)t * npairs + pr) * xpd), xd);
-                    const int S0 = BITS == 3 ? s_S[t * (H >> 5) + 2 * pr] : 0;
-                    const int S1 = BITS == 3 ? s_S[t * (H >> 5) + 2 * pr + 1] : 0;
-                    int A0, A1;
-                    sp.blocks(xd, S0, S1, A0, A1);
-                    acc[t] = fmaf(sp.d0, (float)A0, acc[t]);
-                    acc[t] = fmaf(sp.d1, (float)A1, acc[t]);
+                    float v = acc[t];
+                    if (tpr >= 2) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+                    if (tpr >= 4) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+                    if (tpr >= 8) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+                    if (tpr >= 16) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+                    if (sub == 0) s_gu[t * 64 + base_row + r] = v;
                 }
             }
-            // sum over the row's pieces (consecutive lanes; a fixed tree)
-#pragma unroll
-            for (int t = 0; t < T_; ++t) {
-                float v = acc[t];
-                if (qpr >= 2) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-                if (qpr >= 4) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-                if (qpr >= 8) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
-                if (m == 0) s_gu[t * 64 + r] = v;
-            }
-        }
-        __syncthreads();  // gate/up values; the gate/up regions are free
-        const int nxt = it + G;
-        if (nxt < n_items) issue_item(nxt, 1);
+        };
+        stage(rg, s_wt);
+        __syncthreads();  // gate rows staged (and, first time, the activation digits)
+        if (my_items == 0) STRACE(3);
+        half_rows(s_wt, 0);
+        stage(ru, s_wt + RB);
+        __syncthreads();  // up rows staged
+        half_rows(s_wt + RB, 32);
+        __syncthreads();  // gate/up values
+        if (my_items == 0) STRACE(4);
 
         // SwiGLU and the h digits: wave t for row t
         if (wave < T_) {
@@ -586,9 +667,11 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (lane < F_::nnd) build_digits<BITS>(s_ah + t * 32, 31, lane, s_hd + t * xpd);
+            if (lane < F_::nnd) build_digits<BITS>(s_ah + t * 32, 31, lane, s_hd + t * xps);
         }
-        __syncthreads();  // h digits
+        stage(rd, s_wt + 2 * (size_t)RB);
+        __syncthreads();  // h digits, down column staged
+        if (my_items == 0) STRACE(5);
 
         // down: row pairs (2 rp, 2 rp + 1) of column block c; partial rows stored tagged
         {
@@ -604,7 +687,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
             }
             uint32_t hd[T_][xpd];
 #pragma unroll
-            for (int t = 0; t < T_; ++t) lds_read_b128<xpd>((const uint8_t *)(s_hd + t * xpd), hd[t]);
+            for (int t = 0; t < T_; ++t) lds_read_b128<xpd>((const uint8_t *)(s_hd + t * xps), hd[t]);
             for (int rp = tid; rp < (H >> 1); rp += SPL_THREADS) {
                 uint32_t w[F_::pw];
                 lds_read_dwords<F_::pw>(dcol + (size_t)rp * pb, w);
@@ -616,44 +699,37 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
                     // the pair's two blocks are the rows 2rp and 2rp + 1
                     int A0, A1;
                     sp.blocks(hd[t], Sh[t], Sh[t], A0, A1);
-                    uint64_t *dst = P.part + ((size_t)pid[t] * P.ncmax + c) * H + 2 * rp;
+                    // partial layout [pair][row / 8][slice][row % 8]: rows 2rp, 2rp+1 adjacent
+                    uint64_t *dst = P.part + (((size_t)pid[t] * (H >> 3) + (rp >> 2)) * P.ncmax + c) * 8 + 2 * (rp & 3);
                     st_tagged(dst, sp.d0 * (float)A0 * hinv[t], tag);
                     st_tagged(dst + 1, sp.d1 * (float)A1 * hinv[t], tag);
                 }
             }
         }
+        if (my_items == 0) STRACE(6);
         ++my_items;
-        __syncthreads();  // the down column is free
-        if (nxt < n_items) issue_item(nxt, 2);
+        __syncthreads();  // the staged regions are free
     }
 
     // ======================= Phase C: sums over the slices =======================
     __syncthreads();  // every thread's partial stores are issued
-    if (tid == 0) {
-        if (my_items) add_dev(P.items_done, (uint32_t)my_items);
-        uint32_t spins = 0;
-        while (ld_dev_u32(P.items_done) < (uint32_t)n_items) {
-            __builtin_amdgcn_s_sleep(2);
-            if (++spins > DEC_SPIN_LIMIT || (ld_dev_u32(P.err) & 1u)) {
-                atomicOr(P.err, 1u);
-                break;
-            }
-        }
-    }
-    __syncthreads();
+    STRACE(7);
     // outputs: COMBINE: (row t, output h) -> y; else (present pair, output h)
     const bool combine = (P.mode & DEC_MODE_COMBINE) != 0;
     const int n_out = combine ? T_ * H : sm.n_pl * H;
     const int u0 = blockIdx.x * P.units;
     const int nu = max(0, min(P.units, n_out - u0));
     const int nterm = combine ? k + hs : 1;
-    float *s_red = (float *)s_wt;  // [units][nterm]
-    for (int q = tid; q < nu * nterm; q += SPL_THREADS) {
-        const int ul = q / nterm, j = q - ul * nterm;
-        const int u = u0 + ul;
-        const int t = u / H, row = u - t * H;
-        int p;
-        float wgt;
+    const int ncm = P.ncmax;
+    // units come in chunks of 8 outputs (8 consecutive rows of one pair or
+    // row), which is how the partials are laid out: a term of a chunk is
+    // ncx * 8 consecutive words
+    const int nchk = nu >> 3;
+    float *s_val = (float *)s_wt;                         // [chunk][term][slice][8]
+    float *s_red = s_val + (size_t)nchk * nterm * ncm * 8;  // [unit][term]
+    auto term = [&](int g, int j, int &p, float &wgt, int &rowc) {  // chunk g, term j
+        const int u = u0 + 8 * g, t = u / H;
+        rowc = (u - t * H) >> 3;
         if (combine) {
             p = j < k ? t * k + j : TK + t;
             wgt = j < k ? sm.w[p] : 1.0f;
@@ -661,57 +737,97 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
             p = sm.plist[t];
             wgt = p < TK ? sm.w[p] : 1.0f;
         }
-        const int ncx = p >= TK ? ncs : nc;
-        const uint64_t *src = P.part + (size_t)p * P.ncmax * H + row;
-        float sum = 0.0f;
-        for (int c0 = 0; c0 < ncx; c0 += 8) {
-            uint64_t wd[8];
+    };
+    {
+        // every word in flight at once (consecutive threads on consecutive
+        // words), words not yet written by this call read again
+        const int per_term = ncm * 8, nw = nchk * nterm * per_term;
+        for (int q0 = tid; q0 < nw; q0 += 4 * SPL_THREADS) {
+            uint64_t wd[4];
+            const uint64_t *src[4];
+            bool need[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) wd[i] = c0 + i < ncx ? ld_dev_u64(src + (size_t)(c0 + i) * H) : 0ull;
+            for (int i = 0; i < 4; ++i) {
+                const int q = q0 + i * SPL_THREADS;
+                const int r = q % per_term, gj = q / per_term;
+                const int g = gj / nterm, j = gj - g * nterm;
+                int p = 0, rowc = 0;
+                float wgt;
+                if (q < nw) term(g, j, p, wgt, rowc);
+                need[i] = q < nw && (r >> 3) < (p >= TK ? ncs : nc);
+                src[i] = P.part + ((size_t)p * (H >> 3) + rowc) * per_term + (need[i] ? r : 0);
+                wd[i] = need[i] ? ld_dev_u64(src[i]) : 0ull;
+            }
             for (uint32_t spins = 0;; ++spins) {
                 bool ok = true;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) ok = ok && (c0 + i >= ncx || (uint32_t)(wd[i] >> 32) == tag);
+                for (int i = 0; i < 4; ++i) ok = ok && (!need[i] || (uint32_t)(wd[i] >> 32) == tag);
                 if (ok) break;
                 if (spins > DEC_SPIN_LIMIT) {
                     atomicOr(P.err, 1u);
                     break;
                 }
-                __builtin_amdgcn_s_sleep(1);
+                __builtin_amdgcn_s_sleep(4);
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    if (c0 + i < ncx && (uint32_t)(wd[i] >> 32) != tag) wd[i] = ld_dev_u64(src + (size_t)(c0 + i) * H);
+                for (int i = 0; i < 4; ++i)
+                    if (need[i] && (uint32_t)(wd[i] >> 32) != tag) wd[i] = ld_dev_u64(src[i]);
             }
 #pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (q0 + i * SPL_THREADS < nw) s_val[q0 + i * SPL_THREADS] = __builtin_bit_cast(float, (uint32_t)wd[i]);
+        }
+    }
+    __syncthreads();
+    // per (output, term): the sum over the slices in slice order, times the router weight
+    for (int q = tid; q < nu * nterm; q += SPL_THREADS) {
+        const int ul = q / nterm, j = q - ul * nterm;
+        const int g = ul >> 3, rr = ul & 7;
+        int p, rowc;
+        float wgt;
+        term(g, j, p, wgt, rowc);
+        const int ncx = p >= TK ? ncs : nc;
+        const float *v = s_val + ((size_t)g * nterm + j) * ncm * 8 + rr;
+        float sum = 0.0f;
+        for (int c0 = 0; c0 < ncx; c0 += 8) {  // eight reads in flight, added in order
+            float vv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vv[i] = c0 + i < ncx ? v[(c0 + i) * 8] : 0.0f;
+#pragma unroll
             for (int i = 0; i < 8; ++i)
-                if (c0 + i < ncx) sum += __builtin_bit_cast(float, (uint32_t)wd[i]);
+                if (c0 + i < ncx) sum += vv[i];
         }
         s_red[q] = wgt * sum;
         if (!combine) {
+            const int u = u0 + ul, t = u / H, row = u - t * H;
             if (p < TK) P.out_pairs[(size_t)p * H + row] = wgt * sum;
             else P.out_shared[(size_t)(p - TK) * H + row] = sum;
         }
     }
+    STRACE(8);
     if (combine) {
         __syncthreads();
         for (int ul = tid; ul < nu; ul += SPL_THREADS) {
-            const int u = u0 + ul;
-            float v = s_red[ul * nterm];
-            for (int j = 1; j < nterm; ++j) v += s_red[ul * nterm + j];
-            P.y[u] = v;
+            const float *r = s_red + ul * nterm;
+            float v = r[0];
+            for (int j0 = 1; j0 < nterm; j0 += 8) {  // eight reads in flight, added in order
+                float vv[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) vv[i] = j0 + i < nterm ? r[j0 + i] : 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (j0 + i < nterm) v += vv[i];
+            }
+            P.y[u0 + ul] = v;
         }
     }
 
     // ---- end of call: the last workgroup returns the counters to zero and
     // advances the epoch (the next call's tag)
     __syncthreads();
-    if (tid == 0) {
-        const uint32_t old = add_dev(P.done, 1u);
-        if (old == (uint32_t)(G - 1)) {
-            store_dev_u32(P.items_done, 0u);
-            store_dev_u32(P.done, 0u);
-            store_dev_u32(P.epoch, ld_dev_u32(P.epoch) + 1u);
-        }
+    STRACE(9);
+    if (tid == 0 && last_workgroup(P.done, P.done_top, blockIdx.x, G, DEC_CSTRIDE)) {
+        store_dev_u32(P.done_top, 0u);
+        store_dev_u32(P.epoch, ld_dev_u32(P.epoch) + 1u);
     }
 }
 
