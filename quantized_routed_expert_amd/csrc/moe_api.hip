@@ -67,7 +67,7 @@ int dev_info(DevInfo &out) {
 // Workspace layout
 // ----------------------------------------------------------------------------
 struct Layout {
-    size_t counters = 0, n_counters = 0;       // decode: gu[MS] dn[MS] slice[H/128] err epoch done items
+    size_t counters = 0, n_counters = 0;       // decode: gu[MS] dn[MS] slice[H/128] err epoch[EPOCH_SLOTS]
     size_t harr = 0, oll = 0, part = 0, out_pairs = 0, out_shared = 0;
     size_t idx = 0, w = 0, offsets = 0, pairs = 0, active = 0, chunk_counts = 0;
     size_t slot_exp = 0, slot_row0 = 0, slot_cnt = 0, slot_hrow0 = 0, prefix_gu = 0, prefix_dn = 0;
@@ -80,8 +80,9 @@ struct Layout {
 // layout, so a workspace that is zero before its first use stays valid for
 // calls of any shape and path (each call returns the counters to zero).  Each
 // counter has a 256-byte line of its own.
-// after the slot and slice counters: err, epoch, done shards, done top
-constexpr size_t COUNTER_WORDS = (size_t)(2 * DEC_MAX_SLOTS + DEC_MAX_SLICES + 2 + CNT_SHARDS + 1) * DEC_CSTRIDE;
+// after the slot and slice counters: the error word (a line of its own),
+// then the per-workgroup epochs
+constexpr size_t COUNTER_WORDS = (size_t)(2 * DEC_MAX_SLOTS + DEC_MAX_SLICES + 1) * DEC_CSTRIDE + EPOCH_SLOTS;
 Layout make_layout(int T, int E, int k, int H, int F, int Fs, int path) {
     Layout L;
     size_t off = 0;
@@ -459,8 +460,6 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
         uint32_t *cnt = at<uint32_t>(ws, L.counters);
         S_.err = cnt + (size_t)(2 * DEC_MAX_SLOTS + DEC_MAX_SLICES) * DEC_CSTRIDE;
         S_.epoch = S_.err + DEC_CSTRIDE;
-        S_.done = S_.err + 2 * DEC_CSTRIDE;
-        S_.done_top = S_.done + CNT_SHARDS * DEC_CSTRIDE;
         S_.T = T;
         S_.E = E;
         S_.k = k;
@@ -481,6 +480,7 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
             S_.lg_ppt = ilog2(npairs / tpr);
         }
         const int grid = dv.cus;  // one workgroup per CU, all resident
+        if (grid > EPOCH_SLOTS) return MOE_ERR_UNSUPPORTED;
         S_.units = split_units(T, k, S_.H, (mode & DEC_MODE_COMBINE) ? 1 : 0, grid);
         const int lds = split_lds_layout(S_);
         if (lds > dv.lds_max) return MOE_ERR_UNSUPPORTED;
@@ -519,8 +519,6 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
     P.slice_count = cnt + (size_t)2 * DEC_MAX_SLOTS * DEC_CSTRIDE;
     P.err = cnt + (size_t)(2 * DEC_MAX_SLOTS + DEC_MAX_SLICES) * DEC_CSTRIDE;
     P.epoch = P.err + DEC_CSTRIDE;
-    P.done = P.err + 2 * DEC_CSTRIDE;
-    P.done_top = P.done + CNT_SHARDS * DEC_CSTRIDE;
     P.T = T;
     P.E = E;
     P.k = k;
@@ -551,6 +549,7 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
     // persistent grid: every workgroup resident (the down tiles wait on
     // counters written by other workgroups' gate/up items)
     const int grid = dv.cus * occ;
+    if (grid > EPOCH_SLOTS) return MOE_ERR_UNSUPPORTED;
     return launch_err(decode_launch(P, grid, st));
 }
 

@@ -511,7 +511,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
     // Waits on loads are in issue order, so each wave issues first what it
     // needs first: the call's tag (see DecodeParams), then (routing waves) the
     // logits, then the activation groups, then the first weight chunk.
-    const uint32_t tag_v = ld_dev_u32(P.epoch);
+    const uint32_t tag_v = epoch_read(P.epoch);
     const bool route_mode = (P.mode & DEC_MODE_ROUTE) != 0;
     const int route_w = DEC_WAVES - 1 - wave;  // routing: row t by wave DEC_WAVES-1 - t % DEC_WAVES
     const bool routes = route_mode && route_w < T;
@@ -1099,13 +1099,8 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         }
     }
     TRACE(8);
-    // the last workgroup to finish moves the workspace on to the next call's tag
-    if (tid == 0) {
-        if (last_workgroup(P.done, P.done_top, blockIdx.x, G, DEC_CSTRIDE)) {
-            store_dev_u32(P.done_top, 0u);
-            store_dev_u32(P.epoch, ld_dev_u32(P.epoch) + 1u);
-        }
-    }
+    // the workspace moves on to the next call's tag
+    if (tid == 0) epoch_advance(P.epoch, __builtin_amdgcn_readfirstlane(tag_v));
 }
 
 // ---------------------------------------------------------------------------

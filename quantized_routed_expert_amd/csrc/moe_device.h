@@ -204,21 +204,16 @@ __device__ __forceinline__ void store_dev_u32(uint32_t *p, uint32_t v) {
 // all of this wave's memory operations have completed
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
-// Counters that every workgroup of a grid updates are split into CNT_SHARDS
-// shards (one 256-byte line each, `stride` words apart): atomics to one
-// address are performed one after another, so a single counter hit by every
-// workgroup of a 256-workgroup grid would serialize all of them.
-// Counts workgroup b as finished; true for exactly one workgroup of the grid,
-// the last.  shards[b % 16] counts its workgroups, the workgroup completing a
-// shard returns it to zero and counts the shard in *top; the caller that gets
-// true must return *top to zero.
-__device__ __forceinline__ bool last_workgroup(uint32_t *shards, uint32_t *top, int b, int G, int stride) {
-    const int sh = b & (CNT_SHARDS - 1);
-    const uint32_t in_shard = (uint32_t)((G - sh + CNT_SHARDS - 1) / CNT_SHARDS);
-    const uint32_t n_shards = (uint32_t)(G < CNT_SHARDS ? G : CNT_SHARDS);
-    if (add_dev(shards + sh * stride, 1u) != in_shard - 1u) return false;
-    store_dev_u32(shards + sh * stride, 0u);
-    return add_dev(top, 1u) == n_shards - 1u;
+// The call's tag source without a grid-wide counter: EPOCH_SLOTS words, all
+// equal to the number of calls made on the workspace.  Workgroup b reads
+// word b at its start and, at its end, writes the next value into every word
+// i with i % G == b: each word is written by exactly one workgroup of a call
+// (so no workgroup overwrites a word another one has yet to read), and after
+// the call every word holds the next value whatever the grid size G (<=
+// EPOCH_SLOTS), so launches of any grid sharing the workspace stay in step.
+__device__ __forceinline__ uint32_t epoch_read(const uint32_t *epoch) { return ld_dev_u32(epoch + blockIdx.x); }
+__device__ __forceinline__ void epoch_advance(uint32_t *epoch, uint32_t e) {
+    for (int i = blockIdx.x; i < EPOCH_SLOTS; i += gridDim.x) store_dev_u32(epoch + i, e + 1u);
 }
 
 // ---------------------------------------------------------------------------

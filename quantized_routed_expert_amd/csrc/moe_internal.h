@@ -20,7 +20,7 @@ constexpr int DEC_XG_BF16 = 8;              // activation k-groups (8 values) lo
 constexpr int DEC_XG_F32 = 4;               // ... fp32
 constexpr uint32_t DEC_SPIN_LIMIT = 1u << 20;  // bounded waits: a wait that runs out sets err bit 0
 constexpr int DEC_CSTRIDE = 64;              // 32-bit words between counters (one 256-byte line each)
-constexpr int CNT_SHARDS = 16;               // shards of a counter that every workgroup updates
+constexpr int EPOCH_SLOTS = 1024;            // per-workgroup copies of the call count (grids of <= 1024)
 constexpr int DEC_RANK_MAX_KEYS = 2048;      // routing by ranks: T*E up to this ...
 constexpr int DEC_RANK_MAX_CMP = 64;         // ... and at most this many comparisons per thread
 #define MOE_MAX_EXPERTS_DEV 4096
@@ -92,8 +92,7 @@ struct DecodeParams {
     uint32_t *dn_count;        // [DEC_MAX_SLOTS * DEC_CSTRIDE]: finished down tiles per slot
     uint32_t *slice_count;     // [DEC_MAX_SLICES * DEC_CSTRIDE]: finished slots per 128-row slice
     uint32_t *err;             // error word (bit 0: a wait hit its spin limit; bit 1: bad given grouping)
-    uint32_t *epoch;           // calls completed on this workspace (the tag source)
-    uint32_t *done, *done_top; // finished workgroups of this call: 16 shards, then shards completed
+    uint32_t *epoch;           // [EPOCH_SLOTS] calls completed on this workspace (the tag source)
     int T, E, k, H, F, Fs;     // Fs = shared ffn (0 = none)
     int bits, x_f32, mode, max_slots;
     int h_stride;              // words per hll row (Fmax)
@@ -160,7 +159,7 @@ struct SplitParams {
     int32_t *topk_idx_out;     // may be null
     float *topk_w_out;         // may be null
     uint64_t *part;            // [T*k + T][ncmax][H] tagged partial down rows per (pair, slice)
-    uint32_t *err, *epoch, *done, *done_top;
+    uint32_t *err, *epoch;     // error word; [EPOCH_SLOTS] calls completed (the tag source)
     int T, E, k, H, F, Fs, bits, mode, x_f32;
     int nc, ncs, ncmax;        // 32-column slices of F and Fs; the partial buffer's stride
     uint32_t m_nc;             // ceil(2^32 / nc) (0 when nc = 1)

@@ -367,7 +367,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     // ======================= Phase A: routing, activations, slots =======================
     STRACE_INIT;
     STRACE(0);
-    const uint32_t tag_v = ld_dev_u32(P.epoch);
+    const uint32_t tag_v = epoch_read(P.epoch);
 
     // activations: thread tid holds elements 8 tid .. 8 tid + 7 of [T][H]
     const int nx = T_ * H;
@@ -821,14 +821,9 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
         }
     }
 
-    // ---- end of call: the last workgroup returns the counters to zero and
-    // advances the epoch (the next call's tag)
-    __syncthreads();
+    // ---- end of call: the workspace moves on to the next call's tag
     STRACE(9);
-    if (tid == 0 && last_workgroup(P.done, P.done_top, blockIdx.x, G, DEC_CSTRIDE)) {
-        store_dev_u32(P.done_top, 0u);
-        store_dev_u32(P.epoch, ld_dev_u32(P.epoch) + 1u);
-    }
+    if (tid == 0) epoch_advance(P.epoch, __builtin_amdgcn_readfirstlane(tag_v));
 }
 
 template <int BITS, int T_, int XF32>
