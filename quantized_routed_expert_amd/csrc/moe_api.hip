@@ -308,7 +308,7 @@ int split_lds_layout(SplitParams &P) {
     };
     P.lds_small = take(sizeof(SplitSmall));
     P.lds_wt = take((size_t)3 * P.H * bb);
-    P.lds_a = take((size_t)P.T * P.H * 2);
+    P.lds_a = P.lds_wt;  // the integer activations live in the item weight area until the items start
     P.lds_S = take((size_t)P.T * (P.H / 32) * 4);
     P.lds_xd = take((size_t)P.T * (P.H / 64) * xps * 4);
     P.lds_gu = take((size_t)P.T * 64 * 4);
@@ -326,7 +326,7 @@ int split_units(int T, int k, int H, int combine, int G) {
 
 bool split_fits(int T, int E, int k, int H, int F, int Fs, int bits, int combine, int G) {
     (void)E;
-    if (T < 1 || T > SPL_MAX_T || k > 32) return false;
+    if (T < 1 || T > SPL_MAX_T || k > 32 || T * k > 64) return false;
     if (H != 256 && H != 512 && H != 1024 && H != 2048) return false;
     if (F > 4096 || Fs > 4096) return false;
     SplitParams P;
@@ -474,18 +474,14 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
         S_.ncmax = S_.nc > S_.ncs ? S_.nc : S_.ncs;
         S_.m_nc = magic_div(S_.nc);
         S_.rowH = (S_.H / 32) * (S_.bits == 4 ? 18 : 14);
-        {
-            const int npairs = S_.H / 64, tpr = npairs < 16 ? npairs : 16;
-            S_.lg_tpr = ilog2(tpr);
-            S_.lg_ppt = ilog2(npairs / tpr);
-        }
+        S_.lg_qpr = ilog2(S_.H / 256);
         const int grid = dv.cus;  // one workgroup per CU, all resident
         if (grid > EPOCH_SLOTS) return MOE_ERR_UNSUPPORTED;
         S_.units = split_units(T, k, S_.H, (mode & DEC_MODE_COMBINE) ? 1 : 0, grid);
         const int lds = split_lds_layout(S_);
         if (lds > dv.lds_max) return MOE_ERR_UNSUPPORTED;
         static std::mutex smu;
-        static int s_lds_set[2][2][2] = {};
+        static int s_lds_set[2][SPL_MAX_T][2] = {};
         {
             std::lock_guard<std::mutex> lk(smu);
             int &cur = s_lds_set[S_.bits == 4][T - 1][x_f32 ? 1 : 0];

@@ -433,11 +433,6 @@ struct XGroup {
     }
 };
 
-__device__ __forceinline__ void wave_lds_handoff() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // ---------------------------------------------------------------------------
 // The kernel

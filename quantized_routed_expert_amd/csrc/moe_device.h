@@ -201,6 +201,13 @@ __device__ __forceinline__ uint32_t add_dev(uint32_t *p, uint32_t v) {
 __device__ __forceinline__ void store_dev_u32(uint32_t *p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// LDS written by some lanes of a wave, then read by other lanes of it
+__device__ __forceinline__ void wave_lds_handoff() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // all of this wave's memory operations have completed
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 

@@ -125,11 +125,11 @@ struct DecodeParams {
 };
 
 // ---------------------------------------------------------------------------
-// Column-split decode launch (windows of one or two rows): each workgroup item
+// Column-split decode launch (windows of one to four rows): each workgroup item
 // is (expert, 32-column slice of its FFN): gate/up rows of the slice, SwiGLU
 // and the slice's partial down projection, reduced over the slices at the end.
 // ---------------------------------------------------------------------------
-constexpr int SPL_MAX_T = 2;
+constexpr int SPL_MAX_T = 4;
 constexpr int SPL_MAX_SLOTS = SPL_MAX_T * 32 + 1;  // T*k pairs (k <= 32) + the shared expert
 
 struct SplitSmall {  // fixed part of the launch's LDS
@@ -164,7 +164,7 @@ struct SplitParams {
     int nc, ncs, ncmax;        // 32-column slices of F and Fs; the partial buffer's stride
     uint32_t m_nc;             // ceil(2^32 / nc) (0 when nc = 1)
     int rowH;                  // bytes of one gate/up row
-    int lg_tpr, lg_ppt;        // gate/up rows: log2 threads per row (<= 16), log2 pairs per thread (<= 2)
+    int lg_qpr;                // log2 of the 4-pair pieces per gate/up row (H / 256)
     int units;                 // reduction outputs per workgroup
     // LDS byte offsets
     int lds_small, lds_wt, lds_a, lds_S, lds_xd, lds_gu, lds_ah, lds_hd, lds_total;

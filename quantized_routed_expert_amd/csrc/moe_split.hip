@@ -276,14 +276,15 @@ __device__ __forceinline__ void lds_dma16(const void *g, uint8_t *lds_wave) {
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
-template <int BITS, int T_, int XF32>
+template <int BITS, int TM, int XF32>
 __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     using F_ = SFmt<BITS>;
     constexpr int bb = F_::bb, pb = F_::pb, xpd = F_::xpd, xps = F_::xps;
     extern __shared__ __align__(16) uint8_t smem[];
     SplitSmall &sm = *(SplitSmall *)(smem + P.lds_small);
     uint8_t *s_wt = smem + P.lds_wt;                    // item weights: gate rows | up rows | down column
-    int16_t *s_a = (int16_t *)(smem + P.lds_a);         // [T][H] integer activations
+    int16_t *s_a = (int16_t *)(smem + P.lds_wt);        // [T][H] integer activations (in the item
+                                                        // weight area, unused until the items)
     int *s_S = (int *)(smem + P.lds_S);                 // [T][H/32] block sums (3-bit)
     // [T][H/64 pair slots][xps] activation digits; pair 4m + j of a row sits in
     // slot j * (H/256) + m, so the pieces m = 0, 1, ... that the lanes of a
@@ -296,7 +297,8 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = gridDim.x;
     const int k = P.k, E = P.E, H = P.H;
-    const int TK = T_ * k;
+    const int T = P.T;  // rows of the window, 1 <= T <= TM
+    const int TK = T * k;
     const bool has_shared = (P.mode & DEC_MODE_SHARED) != 0;
     const int hs = has_shared ? 1 : 0;
     const bool route_mode = (P.mode & DEC_MODE_ROUTE) != 0;
@@ -304,8 +306,8 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     const int RB = H * bb;              // bytes of each item region
     const int np = RB >> 4;             // 16-byte pieces per region
     const int npairs = H >> 6;          // pairs per gate/up row
-    // gate/up tasks: tpr threads per row, ppt consecutive pairs each
-    const int lg_tpr = P.lg_tpr, tpr = 1 << lg_tpr, lg_ppt = P.lg_ppt, ppt = 1 << lg_ppt;
+    // gate/up tasks: qpr pieces of 4 consecutive pairs per row (H / 256)
+    const int lg_qpr = P.lg_qpr, qpr = 1 << lg_qpr;
     const size_t eb = (size_t)3 * P.F * P.rowH;
 
     // ---- item -> (slot, column slice) and its three regions in global memory
@@ -319,49 +321,47 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
         c = j - s * nc;
         return hs + s;
     };
-    // An item's three regions (gate rows, up rows, down column block; np
-    // 16-byte pieces each) are loaded into registers, NPER pieces per thread
-    // per region (pieces past np re-read piece 0 and are not staged), so
-    // every thread issues the same loads in the order they are needed: the
-    // wait for the gate rows leaves the up and down loads in flight.
-    constexpr int NPER = BITS == 4 ? 5 : 4;  // ceil(np / 512) at H = 2048
-    u32x4 rg[NPER], ru[NPER], rd[NPER];
-    auto issue_item_e = [&](int c, int e) {  // e: the routed expert, -1: the shared one
+    // Each wave owns a share of an item end to end: 8 of its 64 gate/up rows
+    // (waves 0-3 gate rows 8w.., waves 4-7 up rows) and H/8 of its down rows.
+    // It loads that share into registers (NGU + ND 16-byte pieces per lane;
+    // pieces past the share re-read its first piece and are not staged),
+    // stages it through its own part of LDS and computes from it: no other
+    // wave's data is waited for until the gate/up values are complete, so a
+    // wave computes as soon as its own bytes arrive.  Loads complete in issue
+    // order: gate/up rows first, then down rows.
+    constexpr int NGU = BITS == 4 ? 9 : 7;  // ceil(8 rows * rowH / 16 / 64) at H = 2048
+    constexpr int ND = BITS == 4 ? 5 : 4;   // ceil(H/8 rows * bb / 16 / 64) at H = 2048
+    const int npw = (8 * P.rowH) >> 4;      // pieces of a wave's 8 gate/up rows
+    const int npd = (H * bb) >> 7;          // pieces of a wave's H/8 down rows
+    u32x4 rw[NGU], rdn[ND];
+    // parts: 1 this wave's gate/up rows, 2 its down rows; e: the routed expert, -1: the shared one
+    auto issue_item_e = [&](int c, int e, int parts) {
         const bool sh = e < 0;
         const int Fx = sh ? P.Fs : P.F;
         const uint8_t *blob = sh ? P.w_shared : P.w_routed + (size_t)e * eb;
-        const uint8_t *g0 = blob + (size_t)c * 32 * P.rowH;                   // gate rows 32c..
-        const uint8_t *u0 = blob + (size_t)(Fx + c * 32) * P.rowH;            // up rows 32c..
-        const uint8_t *d0 = blob + (size_t)2 * Fx * P.rowH + (size_t)c * RB;  // down column block c
+        if (parts & 1) {
+            const int row0 = wave < 4 ? 32 * c + 8 * wave : Fx + 32 * c + 8 * (wave - 4);
+            const uint8_t *g0 = blob + (size_t)row0 * P.rowH;
 #pragma unroll
-        for (int i = 0; i < NPER; ++i) {
-            const int pc = tid + i * SPL_THREADS, q = pc < np ? pc : 0;
-            rg[i] = *(const u32x4 *)(g0 + (size_t)q * 16);
+            for (int i = 0; i < NGU; ++i) {
+                const int pc = lane + 64 * i, q = pc < npw ? pc : 0;
+                rw[i] = *(const u32x4 *)(g0 + (size_t)q * 16);
+            }
         }
-        __builtin_amdgcn_sched_barrier(0);  // (keep the issue order: gate, up, down)
+        __builtin_amdgcn_sched_barrier(0);  // (keep the issue order)
+        if (parts & 2) {
+            const uint8_t *d0 = blob + (size_t)2 * Fx * P.rowH + (size_t)c * RB + (size_t)wave * (H >> 3) * bb;
 #pragma unroll
-        for (int i = 0; i < NPER; ++i) {
-            const int pc = tid + i * SPL_THREADS, q = pc < np ? pc : 0;
-            ru[i] = *(const u32x4 *)(u0 + (size_t)q * 16);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < NPER; ++i) {
-            const int pc = tid + i * SPL_THREADS, q = pc < np ? pc : 0;
-            rd[i] = *(const u32x4 *)(d0 + (size_t)q * 16);
+            for (int i = 0; i < ND; ++i) {
+                const int pc = lane + 64 * i, q = pc < npd ? pc : 0;
+                rdn[i] = *(const u32x4 *)(d0 + (size_t)q * 16);
+            }
         }
     };
-    auto issue_item = [&](int it) {
+    auto issue_item = [&](int it, int parts) {
         int c;
         const int s = item_slot(it, c);
-        issue_item_e(c, s < hs ? -1 : sm.slot_exp[s]);
-    };
-    auto stage = [&](const u32x4 (&r)[NPER], uint8_t *dst) {
-#pragma unroll
-        for (int i = 0; i < NPER; ++i) {
-            const int pc = tid + i * SPL_THREADS;
-            if (pc < np) *(u32x4 *)(dst + (size_t)pc * 16) = r[i];
-        }
+        issue_item_e(c, s < hs ? -1 : sm.slot_exp[s], parts);
     };
 
     // ======================= Phase A: routing, activations, slots =======================
@@ -369,30 +369,42 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     STRACE(0);
     const uint32_t tag_v = epoch_read(P.epoch);
 
-    // activations: thread tid holds elements 8 tid .. 8 tid + 7 of [T][H]
-    const int nx = T_ * H;
-    const bool has_x = 8 * tid < nx;
-    const int xt = has_x ? (8 * tid) / H : 0, xk = has_x ? 8 * tid - xt * H : 0;
-    float xv[8];
+    // activations: thread tid holds the groups of 8 elements g = tid + 512 r
+    // of [T][H] (r < XR)
+    constexpr int XR = TM > 2 ? 2 : 1;  // (T * H / 8 <= 512 * XR for H <= 2048)
+    const int nx = T * H;
+    bool has_x[XR];
+    int xt[XR], xk[XR];
+    float xv[XR][8];
+#pragma unroll
+    for (int r = 0; r < XR; ++r) {
+        const int e0 = 8 * (tid + SPL_THREADS * r);
+        has_x[r] = e0 < nx;
+        xt[r] = has_x[r] ? e0 / H : 0;
+        xk[r] = has_x[r] ? e0 - xt[r] * H : 0;
+    }
     auto load_x = [&]() {
-        const int e0 = has_x ? 8 * tid : 0;
-        if constexpr (XF32) {
-            const u32x4 a = *(const u32x4 *)((const float *)P.x + e0);
-            const u32x4 b = *(const u32x4 *)((const float *)P.x + e0 + 4);
-            const uint32_t wv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-            for (int i = 0; i < 8; ++i) xv[i] = __builtin_bit_cast(float, wv[i]);
-        } else {
-            const u32x4 a = *(const u32x4 *)((const uint16_t *)P.x + e0);
-            const uint32_t wv[4] = {a.x, a.y, a.z, a.w};
+        for (int r = 0; r < XR; ++r) {
+            const int e0 = has_x[r] ? 8 * (tid + SPL_THREADS * r) : 0;
+            if constexpr (XF32) {
+                const u32x4 a = *(const u32x4 *)((const float *)P.x + e0);
+                const u32x4 b = *(const u32x4 *)((const float *)P.x + e0 + 4);
+                const uint32_t wv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                xv[2 * i] = __builtin_bit_cast(float, wv[i] << 16);
-                xv[2 * i + 1] = __builtin_bit_cast(float, wv[i] & 0xFFFF0000u);
+                for (int i = 0; i < 8; ++i) xv[r][i] = __builtin_bit_cast(float, wv[i]);
+            } else {
+                const u32x4 a = *(const u32x4 *)((const uint16_t *)P.x + e0);
+                const uint32_t wv[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    xv[r][2 * i] = __builtin_bit_cast(float, wv[i] << 16);
+                    xv[r][2 * i + 1] = __builtin_bit_cast(float, wv[i] & 0xFFFF0000u);
+                }
             }
         }
     };
-    if (route_mode && wave < T_) {
+    if (route_mode && wave < T) {
         // routing of row `wave` by this wave: logits first, then its activations
         const int epl = (E + 63) >> 6;
         auto route_wave = [&](auto epl_c) {
@@ -413,38 +425,46 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     }
     {
         // per wave and row: the largest |x|
-        float m = 0.0f;
+        uint32_t mb[XR];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(xv[i]));
-        const uint32_t mb = has_x ? __builtin_bit_cast(uint32_t, m) : 0u;
+        for (int r = 0; r < XR; ++r) {
+            float m = 0.0f;
 #pragma unroll
-        for (int t = 0; t < T_; ++t) {
-            const uint32_t wm = wave_max_u32(xt == t ? mb : 0u);
+            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(xv[r][i]));
+            mb[r] = has_x[r] ? __builtin_bit_cast(uint32_t, m) : 0u;
+        }
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            uint32_t v = 0u;
+#pragma unroll
+            for (int r = 0; r < XR; ++r) v = max(v, xt[r] == t ? mb[r] : 0u);
+            const uint32_t wm = wave_max_u32(v);
             if (lane == 0) sm.wmax[wave][t] = wm;
         }
     }
     // the shared expert's items need no routing: their weights stream in now
-    if ((int)blockIdx.x < ncs) issue_item_e(blockIdx.x, -1);
+    if ((int)blockIdx.x < ncs) issue_item_e(blockIdx.x, -1, 3);
     __syncthreads();  // routing and the row maxima complete
     STRACE(1);
     const uint32_t tag = decode_tag(__builtin_amdgcn_readfirstlane(tag_v));
     // a one-row window: its first routed item is known from the routing alone
     // (slot hs + j is the row's j-th expert)
     int it = blockIdx.x;
-    const bool early = T_ == 1 && route_mode;
+    const bool early = T == 1 && route_mode;
     if (early) {
         const int n_items1 = ncs + k * nc;
         if (it < n_items1 && it >= ncs) {
             const int j = it - ncs, sl = nc == 1 ? j : (int)__umulhi((uint32_t)j, P.m_nc);
-            issue_item_e(j - sl * nc, sm.idx[sl]);
+            issue_item_e(j - sl * nc, sm.idx[sl], 3);
         }
     }
 
     // integer activations a = rint(x * 2^sc), max |x| * 2^sc in [2^13, 2^14)
-    {
+#pragma unroll
+    for (int r = 0; r < XR; ++r) {
         uint32_t mxb = 0u;
 #pragma unroll
-        for (int w = 0; w < SPL_WAVES; ++w) mxb = max(mxb, sm.wmax[w][xt]);
+        for (int w = 0; w < SPL_WAVES; ++w) mxb = max(mxb, sm.wmax[w][xt[r]]);
         const float mx = __builtin_bit_cast(float, mxb);
         int ex = 0;
         if (mx > 0.0f) frexpf(mx, &ex);
@@ -453,52 +473,53 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
         int ai[8], bs = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            ai[i] = (int)rintf(xv[i] * scale);
+            ai[i] = (int)rintf(xv[r][i] * scale);
             bs += ai[i];
         }
-        if (has_x) {
+        if (has_x[r]) {
             const u32x4 pk = {(uint32_t)(ai[0] & 0xFFFF) | ((uint32_t)ai[1] << 16),
                               (uint32_t)(ai[2] & 0xFFFF) | ((uint32_t)ai[3] << 16),
                               (uint32_t)(ai[4] & 0xFFFF) | ((uint32_t)ai[5] << 16),
                               (uint32_t)(ai[6] & 0xFFFF) | ((uint32_t)ai[7] << 16)};
-            *(u32x4 *)(s_a + xt * H + xk) = pk;
-            if (xk == 0) sm.tinv[xt] = __builtin_bit_cast(float, (uint32_t)(127 - sc) << 23);
+            *(u32x4 *)(s_a + xt[r] * H + xk[r]) = pk;
+            if (xk[r] == 0) sm.tinv[xt[r]] = __builtin_bit_cast(float, (uint32_t)(127 - sc) << 23);
         }
         if (BITS == 3) {
             // block sums: the four threads of a block are consecutive lanes
             bs += __builtin_amdgcn_update_dpp(0, bs, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
             bs += __builtin_amdgcn_update_dpp(0, bs, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
-            if (has_x && (tid & 3) == 0) s_S[xt * (H >> 5) + (xk >> 5)] = bs;
+            if (has_x[r] && (tid & 3) == 0) s_S[xt[r] * (H >> 5) + (xk[r] >> 5)] = bs;
         }
     }
 
     // slots: the shared expert (slot 0 when present), then the routed experts
-    // in order of first use (row 0's top-k order, then row 1's new ones)
+    // in order of first use (row 0's top-k order, then each later row's new
+    // ones); pick p = t*k + j (T*k <= 64: one lane each)
     if (wave == 0) {
         if (route_mode) {
             const int p = lane;
             const bool valid = p < TK;
             const int e = valid ? sm.idx[p] : -1;
-            const int t = p >= k ? 1 : 0;
-            bool owner = valid;
-            if (valid && t == 1)
-                for (int q = 0; q < k; ++q) owner = owner && sm.idx[q] != e;
+            int t = 0;
+            while (t + 1 < T && (t + 1) * k <= p) ++t;
+            // the first pick of this expert (a row's own picks are distinct)
+            int first = p;
+            if (valid)
+                for (int q = t * k - 1; q >= 0; --q)
+                    if (sm.idx[q] == e) first = q;
+            const bool owner = valid && first == p;
             const uint64_t om = __ballot(owner);
-            const int slot = hs + __popcll(om & ((1ull << lane) - 1ull));
             if (owner) {
+                const int slot = hs + __popcll(om & ((1ull << lane) - 1ull));
                 sm.slot_exp[slot] = e;
-                sm.slot_pair[slot][t] = p;
-                if (T_ == 2) sm.slot_pair[slot][1 - t] = -1;
+#pragma unroll
+                for (int tt = 0; tt < TM; ++tt) sm.slot_pair[slot][tt] = tt == t ? p : -1;
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (valid && !owner) {  // row 1's pick of an expert row 0 also chose
-                int q = 0;
-                for (int qq = 0; qq < k; ++qq)
-                    if (sm.idx[qq] == e) q = qq;
-                sm.slot_pair[hs + __popcll(om & ((1ull << q) - 1ull))][1] = p;
-            }
+            if (valid && !owner)  // a later row's pick of an expert an earlier row chose
+                sm.slot_pair[hs + __popcll(om & ((1ull << first) - 1ull))][t] = p;
             if (lane == 0) sm.n_slots = hs + __popcll(om);
         } else {
             // a grouping given by the caller, sanitized so that bad entries
@@ -516,23 +537,29 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
                     st = P.g_offsets[e];
                     cnt = P.g_offsets[e + 1] - st;
                 }
-                if (e < 0 || e >= E || st < 0 || cnt < 0 || cnt > T_ || st + cnt > TK) {
+                if (e < 0 || e >= E || st < 0 || cnt < 0 || cnt > T || st + cnt > TK) {
                     atomicOr(P.err, 2u);
                     e = (e >= 0 && e < E) ? e : 0;
                     cnt = 0;
                 }
                 sm.slot_exp[hs + a] = e;
-                int pr[SPL_MAX_T] = {-1, -1};
+                int pr[TM];
+#pragma unroll
+                for (int t = 0; t < TM; ++t) pr[t] = -1;
                 for (int q = 0; q < cnt; ++q) {
                     int p = P.g_pairs[st + q];
                     if (p < 0 || p >= TK) {
                         atomicOr(P.err, 2u);
                         continue;
                     }
-                    pr[p >= k ? 1 : 0] = p;
+                    int t = 0;
+                    while (t + 1 < T && (t + 1) * k <= p) ++t;
+#pragma unroll
+                    for (int tt = 0; tt < TM; ++tt)
+                        if (tt == t) pr[tt] = p;
                 }
 #pragma unroll
-                for (int t = 0; t < T_; ++t) sm.slot_pair[hs + a][t] = pr[t];
+                for (int t = 0; t < TM; ++t) sm.slot_pair[hs + a][t] = pr[t];
             }
             for (int p = lane; p < TK; p += 64) sm.w[p] = P.g_pair_w ? P.g_pair_w[p] : 1.0f;
             if (lane == 0) sm.n_slots = hs + na;
@@ -540,7 +567,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
         if (lane == 0 && has_shared) {
             sm.slot_exp[0] = -1;
 #pragma unroll
-            for (int t = 0; t < T_; ++t) sm.slot_pair[0][t] = TK + t;
+            for (int t = 0; t < TM; ++t) sm.slot_pair[0][t] = t < T ? TK + t : -1;
         }
         if (!(P.mode & DEC_MODE_COMBINE)) {
             // the pairs present, for the per-pair outputs
@@ -550,7 +577,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
             if (lane == 0) {
                 int n = 0;
                 for (int s = 0; s < sm.n_slots; ++s)
-                    for (int t = 0; t < T_; ++t)
+                    for (int t = 0; t < TM; ++t)
                         if (sm.slot_pair[s][t] >= 0) sm.plist[n++] = sm.slot_pair[s][t];
                 sm.n_pl = n;
             }
@@ -566,84 +593,87 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     STRACE(2);
     const int n_slots = sm.n_slots;
     const int n_items = ncs + (n_slots - hs) * nc;
-    if (!early && it < n_items && it >= ncs) issue_item(it);
+    if (!early && it < n_items && it >= ncs) issue_item(it, 3);
 
     // activation digits: (row, pair, nibble-dword) tasks
     {
-        const int ntask = T_ * npairs * F_::nnd;
+        const int ntask = T * npairs * F_::nnd;
         for (int q = tid; q < ntask; q += SPL_THREADS) {
             const int t = q / (npairs * F_::nnd);
             const int r = q - t * npairs * F_::nnd;
             const int pr = r / F_::nnd, nd = r - pr * F_::nnd;
-            const int slot = (pr & (ppt - 1)) * tpr + (pr >> lg_ppt);
+            const int slot = (pr & 3) * qpr + (pr >> 2);
             build_digits<BITS>(s_a + t * H + pr * 64, 63, nd, s_xd + ((size_t)t * npairs + slot) * xps);
         }
     }
 
+    __syncthreads();  // activation digits complete
     // ======================= Phase B: items =======================
     int my_items = 0;  // (for the trace points)
     for (; it < n_items; it += G) {
         int c;
         const int s = item_slot(it, c);
-        if (my_items > 0) issue_item(it);
-        bool row_in[T_];
+        const int nxt = it + G;  // (its loads go out while this item computes)
+        bool row_in[TM];
 #pragma unroll
-        for (int t = 0; t < T_; ++t) row_in[t] = sm.slot_pair[s][t] >= 0;
+        for (int t = 0; t < TM; ++t) row_in[t] = sm.slot_pair[s][t] >= 0;
 
-        // gate rows, then up rows: task (row r of the 32, piece `sub` of ppt
-        // pairs); the up rows still stream in while the gate rows compute
-        auto half_rows = [&](const uint8_t *wreg, int base_row) {
-            const int r = tid >> lg_tpr, sub = tid & (tpr - 1);
-            if (r < 32) {
-                float acc[T_];
+        // gate/up: this wave's 8 rows; lane (row, piece m of 4 pairs)
+        {
+            uint8_t *wr = s_wt + (size_t)wave * 8 * P.rowH;
 #pragma unroll
-                for (int t = 0; t < T_; ++t) acc[t] = 0.0f;
+            for (int i = 0; i < NGU; ++i) {
+                const int pc = lane + 64 * i;
+                if (pc < npw) *(u32x4 *)(wr + (size_t)pc * 16) = rw[i];
+            }
+            wave_lds_handoff();
+            if (my_items == 0) STRACE(3);
+            if (nxt < n_items) issue_item(nxt, 1);
+            const int r = lane >> lg_qpr, m = lane & (qpr - 1);
+            if (r < 8) {
+                float acc[TM];
 #pragma unroll
-                for (int pp = 0; pp < 2; ++pp) {
-                    if (pp < ppt) {
-                        const int pr = sub * ppt + pp, slot = pp * tpr + sub;
-                        uint32_t w[F_::pw];
-                        lds_read_dwords<F_::pw>(wreg + (size_t)r * P.rowH + (size_t)pr * pb, w);
-                        SPair<BITS> sp;
-                        sp.set(w);
+                for (int t = 0; t < TM; ++t) acc[t] = 0.0f;
+                // the piece's 4 pairs (144 or 112 bytes, 16-byte aligned)
+                uint32_t wq[4 * F_::pw];
+                lds_read_b128<4 * F_::pw>(wr + (size_t)r * P.rowH + (size_t)m * 4 * pb, wq);
 #pragma unroll
-                        for (int t = 0; t < T_; ++t) {
-                            if (!row_in[t]) continue;  // (uniform over the workgroup)
-                            uint32_t xd[xpd];
-                            lds_read_b128<xpd>((const uint8_t *)(s_xd + ((size_t)t * npairs + slot) * xps), xd);
-                            const int S0 = BITS == 3 ? s_S[t * (H >> 5) + 2 * pr] : 0;
-                            const int S1 = BITS == 3 ? s_S[t * (H >> 5) + 2 * pr + 1] : 0;
-                            int A0, A1;
-                            sp.blocks(xd, S0, S1, A0, A1);
-                            acc[t] = fmaf(sp.d0, (float)A0, acc[t]);
-                            acc[t] = fmaf(sp.d1, (float)A1, acc[t]);
-                        }
+                for (int pp = 0; pp < 4; ++pp) {
+                    const int pr = 4 * m + pp, slot = pp * qpr + m;
+                    uint32_t w[F_::pw];
+#pragma unroll
+                    for (int i = 0; i < F_::pw; ++i) w[i] = wq[pp * F_::pw + i];
+                    SPair<BITS> sp;
+                    sp.set(w);
+#pragma unroll
+                    for (int t = 0; t < TM; ++t) {
+                        if (!row_in[t]) continue;  // (uniform over the workgroup)
+                        uint32_t xd[xpd];
+                        lds_read_b128<xpd>((const uint8_t *)(s_xd + ((size_t)t * npairs + slot) * xps), xd);
+                        const int S0 = BITS == 3 ? s_S[t * (H >> 5) + 2 * pr] : 0;
+                        const int S1 = BITS == 3 ? s_S[t * (H >> 5) + 2 * pr + 1] : 0;
+                        int A0, A1;
+                        sp.blocks(xd, S0, S1, A0, A1);
+                        acc[t] = fmaf(sp.d0, (float)A0, acc[t]);
+                        acc[t] = fmaf(sp.d1, (float)A1, acc[t]);
                     }
                 }
-                // sum over the row's tpr pieces (consecutive lanes; a fixed tree)
+                // sum over the row's qpr pieces (consecutive lanes; a fixed tree)
 #pragma unroll
-                for (int t = 0; t < T_; ++t) {
+                for (int t = 0; t < TM; ++t) {
                     float v = acc[t];
-                    if (tpr >= 2) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-                    if (tpr >= 4) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-                    if (tpr >= 8) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
-                    if (tpr >= 16) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
-                    if (sub == 0) s_gu[t * 64 + base_row + r] = v;
+                    if (qpr >= 2) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+                    if (qpr >= 4) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+                    if (qpr >= 8) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+                    if (m == 0) s_gu[t * 64 + 8 * wave + r] = v;
                 }
             }
-        };
-        stage(rg, s_wt);
-        __syncthreads();  // gate rows staged (and, first time, the activation digits)
-        if (my_items == 0) STRACE(3);
-        half_rows(s_wt, 0);
-        stage(ru, s_wt + RB);
-        __syncthreads();  // up rows staged
-        half_rows(s_wt + RB, 32);
+        }
         __syncthreads();  // gate/up values
         if (my_items == 0) STRACE(4);
 
         // SwiGLU and the h digits: wave t for row t
-        if (wave < T_) {
+        if (wave < T) {
             const int t = wave;
             float h = 0.0f;
             if (lane < 32) {
@@ -669,36 +699,53 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             if (lane < F_::nnd) build_digits<BITS>(s_ah + t * 32, 31, lane, s_hd + t * xps);
         }
-        stage(rd, s_wt + 2 * (size_t)RB);
-        __syncthreads();  // h digits, down column staged
+        __syncthreads();  // h digits
         if (my_items == 0) STRACE(5);
 
-        // down: row pairs (2 rp, 2 rp + 1) of column block c; partial rows stored tagged
+        // down: this wave's H/8 rows of column block c, as row pairs (2 rp, 2 rp + 1);
+        // partial rows stored tagged
         {
-            const uint8_t *dcol = s_wt + 2 * (size_t)RB;
-            int pid[T_];
-            float hinv[T_];
-            int Sh[T_];
+            uint8_t *dw = s_wt + 2 * (size_t)RB + (size_t)wave * (H >> 3) * bb;
 #pragma unroll
-            for (int t = 0; t < T_; ++t) {
+            for (int i = 0; i < ND; ++i) {
+                const int pc = lane + 64 * i;
+                if (pc < npd) *(u32x4 *)(dw + (size_t)pc * 16) = rdn[i];
+            }
+            wave_lds_handoff();
+            if (nxt < n_items) issue_item(nxt, 2);
+            const uint8_t *dcol = s_wt + 2 * (size_t)RB;
+            int pid[TM];
+            float hinv[TM];
+            int Sh[TM];
+#pragma unroll
+            for (int t = 0; t < TM; ++t) {
                 pid[t] = sm.slot_pair[s][t];
                 hinv[t] = sm.hinv[t];
                 Sh[t] = BITS == 3 ? sm.Sh[t] : 0;
             }
-            uint32_t hd[T_][xpd];
+            // h digits in registers for one or two rows; re-read (LDS broadcast) for more
+            constexpr int HR = TM <= 2 ? TM : 1;
+            uint32_t hd[HR][xpd];
+            if constexpr (TM <= 2) {
 #pragma unroll
-            for (int t = 0; t < T_; ++t) lds_read_b128<xpd>((const uint8_t *)(s_hd + t * xps), hd[t]);
-            for (int rp = tid; rp < (H >> 1); rp += SPL_THREADS) {
+                for (int t = 0; t < TM; ++t) lds_read_b128<xpd>((const uint8_t *)(s_hd + t * xps), hd[t]);
+            }
+            for (int rp = wave * (H >> 4) + lane; rp < (wave + 1) * (H >> 4); rp += 64) {
                 uint32_t w[F_::pw];
                 lds_read_dwords<F_::pw>(dcol + (size_t)rp * pb, w);
                 SPair<BITS> sp;
                 sp.set(w);
 #pragma unroll
-                for (int t = 0; t < T_; ++t) {
+                for (int t = 0; t < TM; ++t) {
                     if (pid[t] < 0) continue;
                     // the pair's two blocks are the rows 2rp and 2rp + 1
                     int A0, A1;
-                    sp.blocks(hd[t], Sh[t], Sh[t], A0, A1);
+                    if constexpr (TM <= 2) {
+                        sp.blocks(hd[t], Sh[t], Sh[t], A0, A1);
+                    } else {
+                        lds_read_b128<xpd>((const uint8_t *)(s_hd + t * xps), hd[0]);
+                        sp.blocks(hd[0], Sh[t], Sh[t], A0, A1);
+                    }
                     // partial layout [pair][row / 8][slice][row % 8]: rows 2rp, 2rp+1 adjacent
                     uint64_t *dst = P.part + (((size_t)pid[t] * (H >> 3) + (rp >> 2)) * P.ncmax + c) * 8 + 2 * (rp & 3);
                     st_tagged(dst, sp.d0 * (float)A0 * hinv[t], tag);
@@ -708,7 +755,9 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
         }
         if (my_items == 0) STRACE(6);
         ++my_items;
-        __syncthreads();  // the staged regions are free
+        // (no barrier: every wave reuses only its own staging area; the shared
+        // gate/up values and h digits are next written after a barrier that
+        // every wave reaches only once its down rows are done)
     }
 
     // ======================= Phase C: sums over the slices =======================
@@ -716,7 +765,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     STRACE(7);
     // outputs: COMBINE: (row t, output h) -> y; else (present pair, output h)
     const bool combine = (P.mode & DEC_MODE_COMBINE) != 0;
-    const int n_out = combine ? T_ * H : sm.n_pl * H;
+    const int n_out = combine ? T * H : sm.n_pl * H;
     const int u0 = blockIdx.x * P.units;
     const int nu = max(0, min(P.units, n_out - u0));
     const int nterm = combine ? k + hs : 1;
@@ -826,26 +875,29 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     if (tid == 0) epoch_advance(P.epoch, __builtin_amdgcn_readfirstlane(tag_v));
 }
 
-template <int BITS, int T_, int XF32>
+template <int BITS, int TM, int XF32>
 static hipError_t split_launch_t(const SplitParams &P, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((k_split_layer<BITS, T_, XF32>), dim3(grid), dim3(SPL_THREADS), P.lds_total, st, P);
+    hipLaunchKernelGGL((k_split_layer<BITS, TM, XF32>), dim3(grid), dim3(SPL_THREADS), P.lds_total, st, P);
     return hipGetLastError();
 }
 
-template <int BITS, int T_, int XF32>
+template <int BITS, int TM, int XF32>
 static hipError_t split_attr_t(int lds) {
-    return hipFuncSetAttribute((const void *)k_split_layer<BITS, T_, XF32>,
+    return hipFuncSetAttribute((const void *)k_split_layer<BITS, TM, XF32>,
                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
 }
 
-#define SPLIT_DISPATCH(FN, ...)                                                   \
-    do {                                                                          \
-        if (bits == 4) {                                                          \
-            if (T == 1) return xf ? FN<4, 1, 1>(__VA_ARGS__) : FN<4, 1, 0>(__VA_ARGS__); \
-            return xf ? FN<4, 2, 1>(__VA_ARGS__) : FN<4, 2, 0>(__VA_ARGS__);     \
-        }                                                                         \
-        if (T == 1) return xf ? FN<3, 1, 1>(__VA_ARGS__) : FN<3, 1, 0>(__VA_ARGS__); \
-        return xf ? FN<3, 2, 1>(__VA_ARGS__) : FN<3, 2, 0>(__VA_ARGS__);         \
+// compile-time row maximum TM: 1, 2 or 4
+#define SPLIT_DISPATCH_B(FN, B, ...)                                                      \
+    do {                                                                                  \
+        if (T == 1) return xf ? FN<B, 1, 1>(__VA_ARGS__) : FN<B, 1, 0>(__VA_ARGS__);     \
+        if (T == 2) return xf ? FN<B, 2, 1>(__VA_ARGS__) : FN<B, 2, 0>(__VA_ARGS__);     \
+        return xf ? FN<B, 4, 1>(__VA_ARGS__) : FN<B, 4, 0>(__VA_ARGS__);                 \
+    } while (0)
+#define SPLIT_DISPATCH(FN, ...)                            \
+    do {                                                   \
+        if (bits == 4) SPLIT_DISPATCH_B(FN, 4, __VA_ARGS__); \
+        SPLIT_DISPATCH_B(FN, 3, __VA_ARGS__);              \
     } while (0)
 
 hipError_t split_launch(const SplitParams &P, int grid, hipStream_t st) {

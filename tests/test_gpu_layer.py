@@ -112,9 +112,9 @@ def test_edge_cases(orc):
     _check(orc, li, P)
 
 
-@pytest.mark.parametrize("T", [1, 2])
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
 def test_split_launch_shapes(orc, T):
-    """Windows of one or two rows take the column-split launch (integer dot
+    """Windows of one to four rows take the column-split launch (integer dot
     products): both weight formats, fp32 and bf16 activations, every hidden
     size it takes (256 .. 2048), with and without a shared expert (of another
     width), k = E, E = k = 1, tied logits, zero and large activations."""
@@ -161,7 +161,8 @@ def test_decode_matches_prefill(orc):
 
 def test_run_twice_bitwise():
     print("[layer] run twice", flush=True)
-    for name, T, path in [("mtp16", 16, D), ("e512", 4, D), ("decode", 1, D), ("e512", 2, D), ("prefill", 512, P)]:
+    for name, T, path in [("mtp16", 16, D), ("e512", 4, D), ("decode", 1, D), ("e512", 2, D), ("tiny", 3, D),
+                          ("prefill", 512, P)]:
         li = layer_inputs(name, T) if T == synth.CONFIGS[name].rows[0] else synth.layer_inputs(
             synth.CONFIGS[name], T=T)
         dl = DevLayer(li)
@@ -175,31 +176,35 @@ def test_run_twice_bitwise():
 def test_batch_invariance_decode():
     """A row's routing is bitwise the same in any window; its output is
     bitwise the same in any window served by the same launch: the 16-row
-    window against 4-row windows (matrix-core launch), and 2-row windows
-    against single rows (column-split launch), both weight formats."""
+    window against 8-row windows (matrix-core launch, 5-16 rows), and 4-row
+    and 2-row windows against single rows (column-split launch, 1-4 rows),
+    both weight formats."""
     print("[layer] batch invariance", flush=True)
     li = layer_inputs("mtp16", 16)
     y16, i16, w16 = DevLayer(li).forward(D)
-    for t0 in (0, 4, 12):
-        sub = dataclasses.replace(li, T=4, x=li.x[t0:t0 + 4].copy(), logits=li.logits[t0:t0 + 4].copy())
-        y4, i4, w4 = DevLayer(sub).forward(D)
-        assert np.array_equal(i4, i16[t0:t0 + 4]), t0
-        assert np.array_equal(w4, w16[t0:t0 + 4]), t0
-        assert np.array_equal(y4, y16[t0:t0 + 4]), t0
+    for t0 in (0, 8):
+        sub = dataclasses.replace(li, T=8, x=li.x[t0:t0 + 8].copy(), logits=li.logits[t0:t0 + 8].copy())
+        y8, i8, w8 = DevLayer(sub).forward(D)
+        assert np.array_equal(i8, i16[t0:t0 + 8]), t0
+        assert np.array_equal(w8, w16[t0:t0 + 8]), t0
+        assert np.array_equal(y8, y16[t0:t0 + 8]), t0
     for t in range(16):
         one = dataclasses.replace(li, T=1, x=li.x[t:t + 1].copy(), logits=li.logits[t:t + 1].copy())
         _, i1, w1 = DevLayer(one).forward(D)
         assert np.array_equal(i1[0], i16[t]), t
         assert np.array_equal(w1[0], w16[t]), t
     for name in ("decode", "e512"):
-        li2 = layer_inputs(name, 2)
-        y2, i2, w2 = DevLayer(li2).forward(D)
-        for t in range(2):
-            one = dataclasses.replace(li2, T=1, x=li2.x[t:t + 1].copy(), logits=li2.logits[t:t + 1].copy())
+        li4 = layer_inputs(name, 4)
+        y4, i4, w4 = DevLayer(li4).forward(D)
+        sub = dataclasses.replace(li4, T=2, x=li4.x[1:3].copy(), logits=li4.logits[1:3].copy())
+        y2, _, _ = DevLayer(sub).forward(D)
+        assert np.array_equal(y2, y4[1:3]), name
+        for t in range(4):
+            one = dataclasses.replace(li4, T=1, x=li4.x[t:t + 1].copy(), logits=li4.logits[t:t + 1].copy())
             y1, i1, w1 = DevLayer(one).forward(D)
-            assert np.array_equal(i1[0], i2[t]), (name, t)
-            assert np.array_equal(w1[0], w2[t]), (name, t)
-            assert np.array_equal(y1[0], y2[t]), (name, t)
+            assert np.array_equal(i1[0], i4[t]), (name, t)
+            assert np.array_equal(w1[0], w4[t]), (name, t)
+            assert np.array_equal(y1[0], y4[t]), (name, t)
 
 
 def test_workspace_reuse_across_shapes(orc):
@@ -219,7 +224,7 @@ def test_workspace_reuse_across_shapes(orc):
 # ---- the expert FFN entry point on a given grouping -------------------------------
 
 @pytest.mark.parametrize("name,T,path", [("tiny", 4, D), ("mtp16", 16, D), ("e512", 4, P), ("tiny", 40, P),
-                                         ("decode", 1, D), ("e512", 2, D), ("tiny", 2, D)])
+                                         ("decode", 1, D), ("e512", 2, D), ("tiny", 2, D), ("e512", 4, D)])
 def test_expert_ffn(orc, name, T, path):
     print(f"[expert_ffn] {name} T={T} path={path}", flush=True)
     cfg = synth.CONFIGS[name]
