@@ -234,9 +234,9 @@ def main():
         metric_value, unit = gbs, "GB/s"
         kern_us = us_layer
         ach = (total_bytes / L) / (kern_us * 1e-6) / 1e9
-        # windows of one or two rows take the column-split launch (integer
-        # nibble dot products), larger windows the matrix-core launch
-        split = T <= 2
+        # windows of one to four rows (T * k <= 64) take the column-split
+        # launch (integer nibble dot products), larger windows the matrix-core launch
+        split = T <= 4 and T * cfg.top_k <= 64
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
                 "kernel": "k_split_layer" if split else "k_decode_layer", "bytes_per_launch": round(total_bytes / L),
