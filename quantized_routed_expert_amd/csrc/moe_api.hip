@@ -26,7 +26,7 @@ hipError_t group_launch(const GroupParams &P, hipStream_t st);
 
 namespace moe {
 hipError_t prefill_plan_launch(const PlanParams &P, hipStream_t st);
-hipError_t prefill_gemm_launch(int mode, int bits, const GemmParams &P, int grid, hipStream_t st);
+hipError_t prefill_gemm_launch(int mode, int bits, const GemmParams &P, int cus, hipStream_t st);
 hipError_t prefill_combine_launch(const CombineParams &P, hipStream_t st);
 hipError_t prepare_launch(const uint8_t *src, uint8_t *dst, const PrepareParams &P, hipStream_t st);
 }  // namespace moe
@@ -580,12 +580,11 @@ int prefill_gemms(const void *x, int x_f32, int T, int E, int k, const moe_qweig
     G.Fs = Fs;
     G.h_stride = Fmax;
     G.x_f32 = x_f32;
-    const int grid = dv.cus * 4;
     G.prefix = at<int32_t>(ws, L.prefix_gu);
-    hipError_t e = prefill_gemm_launch(0, routed->bits, G, grid, st);
+    hipError_t e = prefill_gemm_launch(0, routed->bits, G, dv.cus, st);
     if (e != hipSuccess) return MOE_ERR_LAUNCH;
     G.prefix = at<int32_t>(ws, L.prefix_dn);
-    e = prefill_gemm_launch(1, routed->bits, G, grid, st);
+    e = prefill_gemm_launch(1, routed->bits, G, dv.cus, st);
     return launch_err(e);
 }
 

@@ -13,16 +13,18 @@
 //   k_prefill_plan   one workgroup: active experts (+ the shared expert as a
 //                    group of every row) ordered by decreasing row count, and
 //                    the prefix sums of their tile counts.
-//   k_prefill_gemm   persistent grouped GEMM, 64 rows x 64 outputs per tile.
-//                    The quantized weight tile is dequantized into LDS as bf16
-//                    holding the exact integer codes; the activations (bf16,
-//                    exact) are gathered into LDS by the group's row list;
-//                    v_mfma_f32_16x16x32_bf16 covers one 32-wide quant block,
-//                    and the fp16 block scale multiplies that block's fp32
-//                    partial.  Gate/up tiles compute both projections for the
-//                    same 64 features and apply SwiGLU in fp32 (h stored as
-//                    fp32); down tiles split h into bf16 hi + lo (two MFMAs)
-//                    and write w * o per (token, slot) pair.
+//   k_prefill_gemm   persistent grouped GEMM, tiles of 16, 32 or 64 rows (by
+//                    the group's size) x 64 outputs.  Each wave dequantizes
+//                    the weight fragments of its own MFMAs in registers, as
+//                    bf16 holding the exact integer codes minus the bias; the
+//                    activations (bf16, exact) are gathered into LDS by the
+//                    group's row list; v_mfma_f32_16x16x32_bf16 covers one
+//                    32-wide quant block, and the fp16 block scale multiplies
+//                    that block's fp32 partial.  Gate/up tiles compute both
+//                    projections for the same 64 features and apply SwiGLU in
+//                    fp32, storing h as bf16 hi + lo (h = hi + lo to 16 bits);
+//                    down tiles run both parts through the MFMA and write
+//                    w * o per (token, slot) pair.
 //   k_prefill_combine  y_t = (((w_t0 o_t0 + w_t1 o_t1) + ...) + s_t) in slot
 //                    order, one thread per output element.
 #include "moe_device.h"
@@ -30,17 +32,22 @@
 
 namespace moe {
 
-constexpr int PF_MT = 64;      // rows per tile
-constexpr int PF_NF = 64;      // output features per tile
-constexpr int PF_KSB = 2;      // quant blocks per K step
-constexpr int PF_THREADS = 256;
+constexpr int PF_KSB = 2;        // quant blocks per K step
+constexpr int PF_THREADS = 512;  // eight waves
+constexpr int PF_NF_GU = 128;    // features per gate/up tile (8 waves x 16)
+constexpr int PF_NF_DN = 256;    // outputs per down tile (8 waves x 2 x 16)
+
+// 16-row m-tiles per tile for a group of cnt rows: tiles of 16, 32 or 64 rows,
+// so a small group does not pay for MFMAs over empty rows.
+__device__ __forceinline__ int pf_mtl(int cnt) { return cnt <= 16 ? 1 : (cnt <= 32 ? 2 : 4); }
 
 __global__ __launch_bounds__(1024) void k_prefill_plan(PlanParams P) {
     extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ int s_sg[1024], s_sd[1024];
     const int tid = threadIdx.x;
     const int na = P.active[0];
     const int ns = na + (P.has_shared ? 1 : 0);
-    uint64_t *keys = (uint64_t *)smem;            // [ns]
+    uint64_t *keys = (uint64_t *)smem;                  // [ns]
     int *tg = (int *)(smem + 8 * (size_t)(P.E + 1));   // [ns] gate/up tiles per sorted slot
     int *td = tg + (P.E + 1);                          // [ns]
     // key: row count (desc), then expert id (asc; the shared expert is id -1 -> first)
@@ -66,21 +73,40 @@ __global__ __launch_bounds__(1024) void k_prefill_plan(PlanParams P) {
         P.slot_cnt[rank] = cnt;
         P.slot_row0[rank] = e < 0 ? 0 : P.offsets[e];
         P.slot_hrow0[rank] = e < 0 ? P.T * P.k : P.offsets[e];
-        int mt = (cnt + PF_MT - 1) / PF_MT;
-        tg[rank] = mt * ((e < 0 ? P.Fs : P.F) / PF_NF);
-        td[rank] = mt * (P.H / PF_NF);
+        const int mt = (cnt + 16 * pf_mtl(cnt) - 1) / (16 * pf_mtl(cnt));
+        tg[rank] = mt * ((e < 0 ? P.Fs : P.F) / PF_NF_GU);
+        td[rank] = mt * (P.H / PF_NF_DN);
     }
     __syncthreads();
-    if (tid == 0) {
-        int a = 0, b = 0;
-        for (int i = 0; i < ns; ++i) {
-            P.prefix_gu[i] = a;
-            P.prefix_dn[i] = b;
-            a += tg[i];
-            b += td[i];
-        }
-        P.prefix_gu[ns] = a;
-        P.prefix_dn[ns] = b;
+    // tile prefix sums: thread i owns a run of consecutive slots
+    const int per = (ns + 1023) / 1024;
+    const int i0 = min(ns, tid * per), i1 = min(ns, i0 + per);
+    int sg = 0, sd = 0;
+    for (int i = i0; i < i1; ++i) {
+        sg += tg[i];
+        sd += td[i];
+    }
+    s_sg[tid] = sg;
+    s_sd[tid] = sd;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int a = tid >= off ? s_sg[tid - off] : 0;
+        const int b = tid >= off ? s_sd[tid - off] : 0;
+        __syncthreads();
+        s_sg[tid] += a;
+        s_sd[tid] += b;
+        __syncthreads();
+    }
+    int a = s_sg[tid] - sg, b = s_sd[tid] - sd;
+    for (int i = i0; i < i1; ++i) {
+        P.prefix_gu[i] = a;
+        P.prefix_dn[i] = b;
+        a += tg[i];
+        b += td[i];
+    }
+    if (tid == 1023) {
+        P.prefix_gu[ns] = s_sg[1023];
+        P.prefix_dn[ns] = s_sd[1023];
         P.prefix_gu[P.E + 2] = ns;  // number of slots, for the GEMM kernels
         P.prefix_dn[P.E + 2] = ns;
     }
@@ -92,54 +118,346 @@ __device__ __forceinline__ uint16_t f2bf_bits(float f) {
     return (uint16_t)(u >> 16);
 }
 
-// Dequantize one quant block (32 weights) to exact bf16 codes (code - bias),
-// natural order; returns the scale.  Reads exactly the block's bytes.
-template <int BITS>
-__device__ __forceinline__ float dequant_block_bf16(const uint8_t *blk, uint16_t *out32) {
-    const uint16_t *h = (const uint16_t *)blk;  // blocks are 2-byte aligned
-    float d = half_bits_to_float(h[0]);
-    if constexpr (BITS == 4) {
-        uint16_t w[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = h[1 + i];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            uint32_t byte = (w[i >> 1] >> (8 * (i & 1))) & 0xFFu;
-            out32[i] = f2bf_bits((float)((int)(byte & 15u) - 8));
-            out32[i + 16] = f2bf_bits((float)((int)(byte >> 4) - 8));
-        }
-    } else {
-        uint16_t w[6];
-#pragma unroll
-        for (int i = 0; i < 6; ++i) w[i] = h[1 + i];
-        uint32_t qh = (uint32_t)w[4] | ((uint32_t)w[5] << 16);
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            uint32_t byte = (w[(i & 7) >> 1] >> (8 * (i & 1))) & 0xFFu;
-            int lo = (int)((byte >> (2 * (i >> 3))) & 3u);
-            int hb = (int)((qh >> i) & 1u);
-            out32[i] = f2bf_bits((float)((lo | (hb << 2)) - 4));
-        }
-    }
-    return d;
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));  // 4-byte aligned 16-byte load
+
+// ---------------------------------------------------------------------------
+// In-register dequantization of one k-group (8 consecutive weights 8g..8g+7 of
+// a 32-weight block) into 8 bf16 values that hold the integer codes minus the
+// format's bias exactly (scale applied later to the fp32 MFMA result).
+// ---------------------------------------------------------------------------
+
+// 3-bit: weight i of a block = low part (field i/8 of low-part byte i%8) plus
+// 4 * third bit i, minus 4.  The 3-bit codes of four weights are assembled
+// one per byte, then each byte indexes two 8-entry byte tables (the high and
+// the low byte of bf16(code - 4)) with v_perm_b32, and two more byte
+// permutes interleave them into bf16 pairs.
+__device__ __forceinline__ u32x4 deq3_group(uint32_t qs0, uint32_t qs1, uint32_t qh, uint32_t g) {
+    const uint32_t sh = 2u * g;
+    const uint32_t l0 = (qs0 >> sh) & 0x03030303u;
+    const uint32_t l1 = (qs1 >> sh) & 0x03030303u;
+    const uint32_t t0 = (qh >> (8u * g)) & 15u;
+    const uint32_t t1 = (qh >> (8u * g + 4u)) & 15u;
+    // bit j of t -> bit 2 of byte j: t * (4 + 2^9 + 2^16 + 2^23), the other
+    // partial products land on bits the mask drops (no carries: all distinct)
+    const uint32_t c0 = and_or(__umul24(t0, 0x810204u), 0x04040404u, l0);
+    const uint32_t c1 = and_or(__umul24(t1, 0x810204u), 0x04040404u, l1);
+    // bf16(c - 4), c = 0..7: C080 C040 C000 BF80 0000 3F80 4000 4040
+    const uint32_t hi_lo = 0xBFC0C0C0u, hi_hi = 0x40403F00u;  // high bytes, codes 0-3 / 4-7
+    const uint32_t lo_lo = 0x80004080u, lo_hi = 0x40008000u;  // low bytes
+    const uint32_t h0 = __builtin_amdgcn_perm(hi_hi, hi_lo, c0), b0 = __builtin_amdgcn_perm(lo_hi, lo_lo, c0);
+    const uint32_t h1 = __builtin_amdgcn_perm(hi_hi, hi_lo, c1), b1 = __builtin_amdgcn_perm(lo_hi, lo_lo, c1);
+    u32x4 r;
+    r.x = __builtin_amdgcn_perm(h0, b0, 0x05010400u);  // (low, high) byte of weights 0, 1
+    r.y = __builtin_amdgcn_perm(h0, b0, 0x07030602u);  // weights 2, 3
+    r.z = __builtin_amdgcn_perm(h1, b1, 0x05010400u);
+    r.w = __builtin_amdgcn_perm(h1, b1, 0x07030602u);
+    return r;
 }
 
-// MODE 0: gate/up + SwiGLU -> hout.  MODE 1: down -> weighted pair rows.
+// 4-bit: weight i < 16 = low nibble of code byte i, weight i+16 = its high
+// nibble, minus 8.  qa/qb: code dwords of the group's eight bytes, ns: nibble
+// shift.  xor 0x8 turns c into the 4-bit two's complement of c - 8.
+__device__ __forceinline__ u32x4 deq4_group(uint32_t qa, uint32_t qb, uint32_t ns) {
+    qa ^= 0x88888888u;
+    qb ^= 0x88888888u;
+    uint32_t f[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[j] = __builtin_bit_cast(uint32_t, (float)(int)__builtin_amdgcn_sbfe((int)qa, 8u * j + ns, 4u));
+        f[4 + j] = __builtin_bit_cast(uint32_t, (float)(int)__builtin_amdgcn_sbfe((int)qb, 8u * j + ns, 4u));
+    }
+    u32x4 r;  // small integers: bf16 = the fp32 high half, exactly
+    r.x = __builtin_amdgcn_perm(f[1], f[0], 0x07060302u);
+    r.y = __builtin_amdgcn_perm(f[3], f[2], 0x07060302u);
+    r.z = __builtin_amdgcn_perm(f[5], f[4], 0x07060302u);
+    r.w = __builtin_amdgcn_perm(f[7], f[6], 0x07060302u);
+    return r;
+}
+
+// Raw dwords of weight blocks as loaded from HBM, and the block fields.
+//   MODE 0 (gate/up): NW = one pair of consecutive blocks of one weight row
+//     (3-bit: 28 bytes = 7 dwords; 4-bit: 36 bytes = 9 dwords).
+//   MODE 1 (down, column-block-major): one block of an even or odd row, the
+//     row pair's dwords from the block's first one (3-bit: 4, 4-bit: 5).
+template <int BITS>
+struct BFields {
+    uint32_t d;      // fp16 scale bits (low half)
+    uint32_t q[BITS == 4 ? 4 : 3];  // 4-bit: code dwords; 3-bit: low parts (2), third bits
+};
+
+// Fields of one block from a run of dwords: `odd` = the block starts 2 bytes
+// into dword o (scale in its high half, then aligned code dwords); otherwise
+// it starts at dword 0 and every field is two bytes into a dword.
+template <int BITS>
+__device__ __forceinline__ BFields<BITS> block_fields(const uint32_t *w, bool odd, int o) {
+    BFields<BITS> f;
+    constexpr int NQ = BITS == 4 ? 4 : 3;
+    if (!odd) {
+        f.d = w[0];
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) f.q[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], 16u);
+    } else {
+        f.d = w[o] >> 16;
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) f.q[i] = w[o + 1 + i];
+    }
+    return f;
+}
+
+template <int BITS>
+__device__ __forceinline__ u32x4 deq_group(const BFields<BITS> &f, uint32_t g) {
+    if constexpr (BITS == 3) {
+        return deq3_group(f.q[0], f.q[1], f.q[2], g);
+    } else {
+        const bool odd = g & 1u;
+        return deq4_group(odd ? f.q[2] : f.q[0], odd ? f.q[3] : f.q[1], 4u * (g >> 1));
+    }
+}
+
+template <int MODE, int BITS, int XP>
+struct GemmSmem {
+    uint16_t a[2][XP][4][PF_KSB][4][16][8];  // A, double-buffered: [buf][part][m-tile][block][k-group][row][8]
+    int pair[64];                            // pair id of each tile row (down tiles)
+};
+
+struct TileInfo {
+    int slot, cnt, nt, r0, nrows, Fx;
+    bool shared_slot;
+    const uint8_t *blob;
+};
+
+template <int MODE, int BITS, int XP, int MTL>
+__device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BITS, XP> &sm, const TileInfo &ti) {
+    constexpr int NPASS = MODE == 0 ? 2 : 1;       // gate + up / down
+    constexpr int NTW = MODE == 0 ? 1 : 2;         // 16-column n-tiles per wave
+    constexpr int NFT = MODE == 0 ? PF_NF_GU : PF_NF_DN;
+    constexpr int NB = NPASS * NTW;                // weight fragments per lane per block
+    constexpr int bb = BITS == 4 ? 18 : 14;
+    // gate/up: dwords of one block pair; down: dwords per block
+    constexpr int NW = MODE == 0 ? (BITS == 4 ? 9 : 7) : (BITS == 4 ? 5 : 4);
+    constexpr int NRAW = MODE == 0 ? NPASS : NTW * PF_KSB;  // raw runs per lane per K step
+    constexpr bool XF32 = MODE == 0 && XP == 2;              // fp32 activations, split into bf16 hi + lo
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n_lane = lane & 15;
+    const uint32_t g_lane = (uint32_t)(lane >> 4);
+    const size_t rowH = (size_t)(P.H >> 5) * bb;
+    const int hs = P.h_stride;  // h row: hi plane [0, hs), lo plane [hs, 2 hs) (u16)
+    // A staging: one chunk per thread = (m-tile, block, k-group, row) of 8 K-elements
+    const int a_n = tid & 15, a_g = (tid >> 4) & 3, a_blk = (tid >> 6) & 1, a_m = tid >> 7;
+    const int K = MODE == 0 ? P.H : ti.Fx;
+    const int nks = K / (32 * PF_KSB);
+
+    const int a_r = 16 * a_m + a_n;
+    const bool a_st = a_m < MTL;
+    const bool a_ld = a_st && a_r < ti.nrows;
+    size_t a_off = 0;
+    if (a_ld) {
+        if (MODE == 0) {
+            int t;
+            if (ti.shared_slot) t = ti.r0 + a_r;
+            else t = P.pairs[P.slot_row0[ti.slot] + ti.r0 + a_r] / P.k;
+            a_off = (size_t)t * P.H + 32 * a_blk + 8 * a_g;
+        } else {
+            a_off = (size_t)(P.slot_hrow0[ti.slot] + ti.r0 + a_r) * (2 * hs) + 32 * a_blk + 8 * a_g;
+        }
+    }
+    u32x4 ra[2];
+    auto load_a = [&](int ks) {
+        ra[0] = u32x4{0u, 0u, 0u, 0u};
+        ra[1] = u32x4{0u, 0u, 0u, 0u};
+        if (a_ld) {
+            const size_t o = a_off + (size_t)ks * (32 * PF_KSB);
+            if (MODE == 0 && !XF32) {
+                ra[0] = *(const u32x4 *)((const uint16_t *)P.x + o);
+            } else if (XF32) {
+                const u32x4 *src = (const u32x4 *)((const float *)P.x + o);
+                ra[0] = src[0];
+                ra[1] = src[1];
+            } else {
+                const uint16_t *hb16 = (const uint16_t *)P.hbuf;
+                ra[0] = *(const u32x4 *)(hb16 + o);
+                ra[1] = *(const u32x4 *)(hb16 + o + hs);
+            }
+        }
+    };
+    auto store_a = [&](int buf) {
+        if (!a_st) return;
+        if (XF32) {
+            uint32_t hv[4], lv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float v0 = __builtin_bit_cast(float, i < 2 ? ra[0][2 * i] : ra[1][2 * i - 4]);
+                const float v1 = __builtin_bit_cast(float, i < 2 ? ra[0][2 * i + 1] : ra[1][2 * i - 3]);
+                const uint16_t h0 = f2bf_bits(v0), h1 = f2bf_bits(v1);
+                const uint16_t l0 = f2bf_bits(v0 - bf16_bits_to_float(h0));
+                const uint16_t l1 = f2bf_bits(v1 - bf16_bits_to_float(h1));
+                hv[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                lv[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+            }
+            *(u32x4 *)&sm.a[buf][0][a_m][a_blk][a_g][a_n][0] = u32x4{hv[0], hv[1], hv[2], hv[3]};
+            *(u32x4 *)&sm.a[buf][XP - 1][a_m][a_blk][a_g][a_n][0] = u32x4{lv[0], lv[1], lv[2], lv[3]};
+        } else {
+            *(u32x4 *)&sm.a[buf][0][a_m][a_blk][a_g][a_n][0] = ra[0];
+            if (XP == 2) *(u32x4 *)&sm.a[buf][XP - 1][a_m][a_blk][a_g][a_n][0] = ra[1];
+        }
+    };
+
+    // ---- weight sources of this lane ----
+    const uint8_t *wsrc[NRAW];
+    size_t wstep;  // bytes per K step
+    if (MODE == 0) {
+        const uint8_t *g_row = ti.blob + (size_t)(ti.nt * NFT + wave * 16 + n_lane) * rowH;
+        wsrc[0] = g_row;
+        if (NPASS == 2) wsrc[NPASS - 1] = g_row + (size_t)ti.Fx * rowH;  // up row
+        wstep = (size_t)PF_KSB * bb;
+    } else {
+        // wave w, n-tile t: rows nt*256 + 32 w + 2 n + t (t = row parity); the
+        // pair (2i, 2i+1) of block c sits at (c*H + 2i)*bb, the odd row's
+        // block 12 (3-bit) / 16 (4-bit) bytes after a dword boundary - 2
+        const int hp = ti.nt * NFT + 32 * wave + 2 * n_lane;
+        const uint8_t *dn = ti.blob + (size_t)2 * ti.Fx * rowH + (size_t)hp * bb;
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+#pragma unroll
+            for (int b = 0; b < PF_KSB; ++b)
+                wsrc[t * PF_KSB + b] = dn + (size_t)b * P.H * bb + (BITS == 4 ? 16 : 12) * t;
+        wstep = (size_t)PF_KSB * P.H * bb;
+    }
+    uint32_t rw[NRAW][NW];
+    auto load_w = [&](int ks, uint32_t (&dst)[NRAW][NW]) {
+#pragma unroll
+        for (int b = 0; b < NRAW; ++b) {
+            const uint32_t *s = (const uint32_t *)(wsrc[b] + (size_t)ks * wstep);
+            const u32x4 v = *(const u32x4a4 *)s;
+            dst[b][0] = v.x;
+            dst[b][1] = v.y;
+            dst[b][2] = v.z;
+            dst[b][3] = v.w;
+            if constexpr (NW == 5) {
+                dst[b][4] = s[4];
+            } else if constexpr (NW == 7) {
+                dst[b][4] = s[4];
+                dst[b][5] = s[5];
+                dst[b][6] = s[6];
+            } else if constexpr (NW == 9) {
+                const u32x4 u = *(const u32x4a4 *)(s + 4);
+                dst[b][4] = u.x;
+                dst[b][5] = u.y;
+                dst[b][6] = u.z;
+                dst[b][7] = u.w;
+                dst[b][8] = s[8];
+            }
+        }
+    };
+
+    float4v acc[NB][MTL];
+#pragma unroll
+    for (int a = 0; a < NB; ++a)
+#pragma unroll
+        for (int m = 0; m < MTL; ++m) acc[a][m] = float4v{0.f, 0.f, 0.f, 0.f};
+
+    load_a(0);
+    load_w(0, rw);
+    store_a(0);
+    __syncthreads();
+    for (int ks = 0; ks < nks; ++ks) {
+        const int cur = ks & 1;
+        const bool more = ks + 1 < nks;
+        uint32_t rn[NRAW][NW];
+        if (more) {
+            load_a(ks + 1);
+            load_w(ks + 1, rn);
+        }
+#pragma unroll
+        for (int blk = 0; blk < PF_KSB; ++blk) {
+            bf16x8 av[MTL][XP];
+#pragma unroll
+            for (int m = 0; m < MTL; ++m)
+#pragma unroll
+                for (int x = 0; x < XP; ++x) av[m][x] = *(const bf16x8 *)&sm.a[cur][x][m][blk][g_lane][n_lane][0];
+#pragma unroll
+            for (int f = 0; f < NB; ++f) {
+                // fragment f: gate/up pass f, or down n-tile f (row parity f)
+                BFields<BITS> fl;
+                if (MODE == 0) fl = block_fields<BITS>(rw[f], blk == 1, BITS == 4 ? 4 : 3);
+                else fl = block_fields<BITS>(rw[f * PF_KSB + blk], f == 1, 0);
+                const bf16x8 bq = __builtin_bit_cast(bf16x8, deq_group<BITS>(fl, g_lane));
+                const float d = half_bits_to_float(fl.d);
+                // the m-tiles' MFMAs issue back to back, then their scaling
+                float4v dd[MTL];
+#pragma unroll
+                for (int m = 0; m < MTL; ++m) {
+                    const float4v z = {0.f, 0.f, 0.f, 0.f};
+                    dd[m] = mfma16bf(av[m][0], bq, z);
+                    if (XP == 2) dd[m] = mfma16bf(av[m][XP - 1], bq, dd[m]);
+                }
+#pragma unroll
+                for (int m = 0; m < MTL; ++m) {
+                    acc[f][m].x = fmaf(d, dd[m].x, acc[f][m].x);
+                    acc[f][m].y = fmaf(d, dd[m].y, acc[f][m].y);
+                    acc[f][m].z = fmaf(d, dd[m].z, acc[f][m].z);
+                    acc[f][m].w = fmaf(d, dd[m].w, acc[f][m].w);
+                }
+            }
+        }
+        if (more) {
+            store_a(cur ^ 1);
+#pragma unroll
+            for (int b = 0; b < NRAW; ++b)
+#pragma unroll
+                for (int i = 0; i < NW; ++i) rw[b][i] = rn[b][i];
+        }
+        __syncthreads();
+    }
+    // ---- epilogue ----
+#pragma unroll
+    for (int m = 0; m < MTL; ++m) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rr = m * 16 + 4 * (int)g_lane + r;
+            if (rr >= ti.nrows) continue;
+            if (MODE == 0) {
+                const int col = ti.nt * NFT + wave * 16 + n_lane;  // feature
+                const float g = acc[0][m][r], u = acc[NPASS - 1][m][r];
+                const float h = g / (1.0f + expf(-g)) * u;
+                const uint16_t hh = f2bf_bits(h);
+                const uint16_t hl = f2bf_bits(h - bf16_bits_to_float(hh));
+                uint16_t *dst = (uint16_t *)P.hout + (size_t)(P.slot_hrow0[ti.slot] + ti.r0 + rr) * (2 * hs) + col;
+                dst[0] = hh;
+                dst[hs] = hl;
+            } else {
+                const int pr = sm.pair[rr];
+                const float wgt = (ti.shared_slot || !P.pair_w) ? 1.0f : P.pair_w[pr];
+                float *orow = ti.shared_slot ? P.out_shared + (size_t)(ti.r0 + rr) * P.H
+                                             : P.out_pairs + (size_t)pr * P.H;
+#pragma unroll
+                for (int t = 0; t < NTW; ++t)
+                    orow[ti.nt * NFT + 32 * wave + 2 * n_lane + t] = wgt * acc[t][m][r];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM: persistent workgroups walk the tile list (slots by decreasing
+// row count; within a slot, m-tiles of one 64-output n-tile are consecutive).
+// Tile: 16*mtl rows (mtl = 1, 2, 4 by the group's size) x 128 features
+// (gate/up) or 256 outputs (down), K in steps of two quant blocks.  Eight
+// waves; wave w owns 16 features (gate/up: the gate and the up row of each)
+// or 32 output rows (down) and dequantizes exactly the B fragments of its
+// own MFMAs in registers: lane (n, g) holds k-group g of
+// weight row n, as v_mfma_f32_16x16x32_bf16 expects.  A (activations, or h
+// as bf16 hi + lo) goes through LDS, double-buffered: one barrier per K step,
+// and the next step's A and weight loads are in flight during this step's
+// math.
+// ---------------------------------------------------------------------------
 template <int MODE, int BITS, int XP>
 __global__ __launch_bounds__(PF_THREADS) void k_prefill_gemm(GemmParams P) {
-    constexpr int NB = MODE == 0 ? 2 * PF_NF : PF_NF;  // weight rows staged
-    constexpr int NT_B = NB / 16;
-    __shared__ __align__(16) uint16_t sA[XP][4][PF_KSB][4][16][8];
-    __shared__ __align__(16) uint16_t sB[NT_B][PF_KSB][4][16][8];
-    __shared__ float sS[PF_KSB][NB];
-    __shared__ int s_tok[PF_MT];
-    __shared__ int s_pair[PF_MT];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n_lane = lane & 15, g_lane = lane >> 4;
+    __shared__ __align__(16) GemmSmem<MODE, BITS, XP> sm;
+    constexpr int bb = BITS == 4 ? 18 : 14;
+    const int tid = threadIdx.x;
     const int ns = P.prefix[P.E + 2];
     const int total = P.prefix[ns];
-    const int bb = BITS == 4 ? 18 : 14;
     const size_t rowH = (size_t)(P.H >> 5) * bb;
 
     for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
@@ -150,187 +468,31 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_gemm(GemmParams P) {
             if (P.prefix[mid] <= tile) lo = mid;
             else hi = mid - 1;
         }
-        const int slot = lo;
-        const int e = P.slot_exp[slot];
-        const int cnt = P.slot_cnt[slot];
-        const bool shared_slot = e < 0;
-        const int Fx = shared_slot ? P.Fs : P.F;
-        const int mtiles = (cnt + PF_MT - 1) / PF_MT;
-        const int local = tile - P.prefix[slot];
-        const int mt = local % mtiles, nt = local / mtiles;
-        const int r0 = mt * PF_MT;
-        const int nrows = min(PF_MT, cnt - r0);
-        const uint8_t *blob = shared_slot ? P.w_shared : P.w_routed + (size_t)e * 3 * Fx * rowH;
-        const uint8_t *wrows;
-        size_t wrow_bytes;
-        int K;
-        if (MODE == 0) {
-            wrows = blob + (size_t)nt * PF_NF * rowH;  // gate rows; up rows at + Fx*rowH
-            wrow_bytes = rowH;
-            K = P.H;
-        } else {
-            // down, column-block-major: block (h, c) at (c * H + h) * bb
-            wrows = blob + (size_t)2 * Fx * rowH + (size_t)nt * PF_NF * bb;
-            wrow_bytes = bb;
-            K = Fx;
-        }
-        __syncthreads();
-        if (tid < PF_MT) {
-            int r = r0 + tid;
-            int tok = 0, pr = -1;
-            if (tid < nrows) {
-                if (shared_slot) tok = r;
-                else {
-                    pr = P.pairs[P.slot_row0[slot] + r];
-                    tok = pr / P.k;
-                }
-            }
-            s_tok[tid] = tok;
-            s_pair[tid] = pr;
-        }
-        __syncthreads();
+        TileInfo ti;
+        ti.slot = lo;
+        const int e = P.slot_exp[lo];
+        ti.cnt = P.slot_cnt[lo];
+        ti.shared_slot = e < 0;
+        ti.Fx = ti.shared_slot ? P.Fs : P.F;
+        const int mtl = pf_mtl(ti.cnt);
+        const int MT = 16 * mtl;
+        const int mtiles = (ti.cnt + MT - 1) / MT;
+        const int local = tile - P.prefix[lo];
+        const int mt = local % mtiles;
+        ti.nt = local / mtiles;
+        ti.r0 = mt * MT;
+        ti.nrows = min(MT, ti.cnt - ti.r0);
+        ti.blob = ti.shared_slot ? P.w_shared : P.w_routed + (size_t)e * 3 * ti.Fx * rowH;
 
-        float4v acc[2][4];
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) acc[a][m] = float4v{0.f, 0.f, 0.f, 0.f};
-
-        const int nks = (K >> 5) / PF_KSB;
-        for (int ks = 0; ks < nks; ++ks) {
-            // ---- stage A: 64 rows x 64 K ----
-            {
-                const int r = tid >> 2, q = tid & 3;  // q: 16 K-elements
-                const int blk = q >> 1, g0 = (q & 1) * 2;
-                const int k0 = ks * 64 + q * 16;
-                uint16_t hv[16], lv[16];
-                if (r < nrows) {
-                    if (MODE == 0) {
-                        const int t = s_tok[r];
-                        if (P.x_f32) {
-                            const float *xr = (const float *)P.x + (size_t)t * P.H + k0;
-#pragma unroll
-                            for (int i = 0; i < 16; ++i) {
-                                float v = xr[i];
-                                hv[i] = f2bf_bits(v);
-                                lv[i] = f2bf_bits(v - bf16_bits_to_float(hv[i]));
-                            }
-                        } else {
-                            const u32x4 *xr = (const u32x4 *)((const uint16_t *)P.x + (size_t)t * P.H + k0);
-                            u32x4 v0 = xr[0], v1 = xr[1];
-                            uint32_t wv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-                            for (int i = 0; i < 8; ++i) {
-                                hv[2 * i] = (uint16_t)(wv[i] & 0xFFFFu);
-                                hv[2 * i + 1] = (uint16_t)(wv[i] >> 16);
-                                lv[2 * i] = 0;
-                                lv[2 * i + 1] = 0;
-                            }
-                        }
-                    } else {
-                        const float *hr = P.hbuf + (size_t)(P.slot_hrow0[slot] + r0 + r) * P.h_stride + k0;
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            float v = hr[i];
-                            hv[i] = f2bf_bits(v);
-                            lv[i] = f2bf_bits(v - bf16_bits_to_float(hv[i]));
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) hv[i] = lv[i] = 0;
-                }
-#pragma unroll
-                for (int gg = 0; gg < 2; ++gg) {
-                    u32x4 h4, l4;
-                    h4.x = hv[8 * gg] | ((uint32_t)hv[8 * gg + 1] << 16);
-                    h4.y = hv[8 * gg + 2] | ((uint32_t)hv[8 * gg + 3] << 16);
-                    h4.z = hv[8 * gg + 4] | ((uint32_t)hv[8 * gg + 5] << 16);
-                    h4.w = hv[8 * gg + 6] | ((uint32_t)hv[8 * gg + 7] << 16);
-                    *(u32x4 *)&sA[0][r >> 4][blk][g0 + gg][r & 15][0] = h4;
-                    if (XP == 2) {
-                        l4.x = lv[8 * gg] | ((uint32_t)lv[8 * gg + 1] << 16);
-                        l4.y = lv[8 * gg + 2] | ((uint32_t)lv[8 * gg + 3] << 16);
-                        l4.z = lv[8 * gg + 4] | ((uint32_t)lv[8 * gg + 5] << 16);
-                        l4.w = lv[8 * gg + 6] | ((uint32_t)lv[8 * gg + 7] << 16);
-                        *(u32x4 *)&sA[XP - 1][r >> 4][blk][g0 + gg][r & 15][0] = l4;
-                    }
-                }
-            }
-            // ---- stage B: NB weight rows x 2 blocks, exact bf16 codes ----
-            if (tid < NB * PF_KSB) {
-                const int row = tid >> 1, blk = tid & 1;
-                const uint8_t *src;
-                if (MODE == 0) {
-                    const int half = row / PF_NF;  // 0 gate, 1 up
-                    src = wrows + (size_t)half * Fx * rowH + (size_t)(row - half * PF_NF) * wrow_bytes;
-                    src += (size_t)(ks * PF_KSB + blk) * bb;
-                } else {
-                    src = wrows + (size_t)row * wrow_bytes + (size_t)(ks * PF_KSB + blk) * P.H * bb;
-                }
-                uint16_t codes[32];
-                float d = dequant_block_bf16<BITS>(src, codes);
-                sS[blk][row] = d;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    u32x4 c4;
-                    c4.x = codes[8 * g] | ((uint32_t)codes[8 * g + 1] << 16);
-                    c4.y = codes[8 * g + 2] | ((uint32_t)codes[8 * g + 3] << 16);
-                    c4.z = codes[8 * g + 4] | ((uint32_t)codes[8 * g + 5] << 16);
-                    c4.w = codes[8 * g + 6] | ((uint32_t)codes[8 * g + 7] << 16);
-                    *(u32x4 *)&sB[row >> 4][blk][g][row & 15][0] = c4;
-                }
-            }
-            __syncthreads();
-            // ---- MFMA ----
-#pragma unroll
-            for (int blk = 0; blk < PF_KSB; ++blk) {
-                constexpr int NPASS = MODE == 0 ? 2 : 1;
-#pragma unroll
-                for (int pss = 0; pss < NPASS; ++pss) {
-                    const int ntb = MODE == 0 ? (pss * 4 + wave) : wave;  // B n-tile
-                    const bf16x8 b = *(const bf16x8 *)&sB[ntb][blk][g_lane][n_lane][0];
-                    const float d = sS[blk][ntb * 16 + n_lane];
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        float4v z = {0.f, 0.f, 0.f, 0.f};
-                        float4v dd = mfma16bf(*(const bf16x8 *)&sA[0][m][blk][g_lane][n_lane][0], b, z);
-                        if (XP == 2) dd = mfma16bf(*(const bf16x8 *)&sA[XP - 1][m][blk][g_lane][n_lane][0], b, dd);
-                        acc[pss][m].x = fmaf(d, dd.x, acc[pss][m].x);
-                        acc[pss][m].y = fmaf(d, dd.y, acc[pss][m].y);
-                        acc[pss][m].z = fmaf(d, dd.z, acc[pss][m].z);
-                        acc[pss][m].w = fmaf(d, dd.w, acc[pss][m].w);
-                    }
-                }
-            }
-            __syncthreads();
+        __syncthreads();  // the previous tile's epilogue is done with sm.pair
+        if (tid < 64) {
+            int pr = -1;
+            if (tid < ti.nrows && !ti.shared_slot) pr = P.pairs[P.slot_row0[ti.slot] + ti.r0 + tid];
+            sm.pair[tid] = pr;
         }
-        // ---- epilogue ----
-        const int col = nt * PF_NF + wave * 16 + n_lane;  // feature (MODE 0) / output row (MODE 1)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            float gv[4] = {acc[0][m].x, acc[0][m].y, acc[0][m].z, acc[0][m].w};
-            float uv[4] = {acc[1][m].x, acc[1][m].y, acc[1][m].z, acc[1][m].w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int rr = m * 16 + 4 * g_lane + r;
-                if (rr < nrows) {
-                    if (MODE == 0) {
-                        float g = gv[r], u = uv[r];
-                        float h = g / (1.0f + expf(-g)) * u;
-                        P.hout[(size_t)(P.slot_hrow0[slot] + r0 + rr) * P.h_stride + col] = h;
-                    } else {
-                        if (shared_slot) {
-                            P.out_shared[(size_t)(r0 + rr) * P.H + col] = gv[r];
-                        } else {
-                            const int pr = s_pair[rr];
-                            const float wgt = P.pair_w ? P.pair_w[pr] : 1.0f;
-                            P.out_pairs[(size_t)pr * P.H + col] = wgt * gv[r];
-                        }
-                    }
-                }
-            }
-        }
+        if (mtl == 4) gemm_tile<MODE, BITS, XP, 4>(P, sm, ti);
+        else if (mtl == 2) gemm_tile<MODE, BITS, XP, 2>(P, sm, ti);
+        else gemm_tile<MODE, BITS, XP, 1>(P, sm, ti);
     }
 }
 
@@ -359,21 +521,28 @@ hipError_t prefill_plan_launch(const PlanParams &P, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Persistent grid: every workgroup resident (cus x workgroups per CU).
 template <int MODE, int BITS, int XP>
-static void gemm_t(const GemmParams &P, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((k_prefill_gemm<MODE, BITS, XP>), dim3(grid), dim3(PF_THREADS), 0, st, P);
+static hipError_t gemm_t(const GemmParams &P, int cus, hipStream_t st) {
+    static int occ = 0;
+    if (occ == 0) {
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void *)k_prefill_gemm<MODE, BITS, XP>,
+                                                                     PF_THREADS, 0);
+        if (e != hipSuccess) return e;
+        if (occ < 1) occ = 1;
+    }
+    hipLaunchKernelGGL((k_prefill_gemm<MODE, BITS, XP>), dim3(cus * occ), dim3(PF_THREADS), 0, st, P);
+    return hipGetLastError();
 }
 
-hipError_t prefill_gemm_launch(int mode, int bits, const GemmParams &P, int grid, hipStream_t st) {
+hipError_t prefill_gemm_launch(int mode, int bits, const GemmParams &P, int cus, hipStream_t st) {
     const int xp = (mode == 1 || P.x_f32) ? 2 : 1;
     if (mode == 0) {
-        if (bits == 4) xp == 2 ? gemm_t<0, 4, 2>(P, grid, st) : gemm_t<0, 4, 1>(P, grid, st);
-        else xp == 2 ? gemm_t<0, 3, 2>(P, grid, st) : gemm_t<0, 3, 1>(P, grid, st);
-    } else {
-        if (bits == 4) gemm_t<1, 4, 2>(P, grid, st);
-        else gemm_t<1, 3, 2>(P, grid, st);
+        if (bits == 4) return xp == 2 ? gemm_t<0, 4, 2>(P, cus, st) : gemm_t<0, 4, 1>(P, cus, st);
+        return xp == 2 ? gemm_t<0, 3, 2>(P, cus, st) : gemm_t<0, 3, 1>(P, cus, st);
     }
-    return hipGetLastError();
+    if (bits == 4) return gemm_t<1, 4, 2>(P, cus, st);
+    return gemm_t<1, 3, 2>(P, cus, st);
 }
 
 hipError_t prefill_combine_launch(const CombineParams &P, hipStream_t st) {
