@@ -261,8 +261,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BI
             a_off = (size_t)(P.slot_hrow0[ti.slot] + ti.r0 + a_r) * (2 * hs) + 32 * a_blk + 8 * a_g;
         }
     }
-    u32x4 ra[2];
-    auto load_a = [&](int ks) {
+    constexpr int PD = MODE == 0 ? 3 : 2;  // K steps in flight: step s loads at the end of step s - PD
+    auto load_a = [&](int ks, u32x4 (&ra)[2]) {
         ra[0] = u32x4{0u, 0u, 0u, 0u};
         ra[1] = u32x4{0u, 0u, 0u, 0u};
         if (a_ld) {
@@ -280,7 +280,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BI
             }
         }
     };
-    auto store_a = [&](int buf) {
+    auto store_a = [&](int buf, const u32x4 (&ra)[2]) {
         if (!a_st) return;
         if (XF32) {
             uint32_t hv[4], lv[4];
@@ -302,32 +302,32 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BI
         }
     };
 
-    // ---- weight sources of this lane ----
-    const uint8_t *wsrc[NRAW];
+    // ---- weight sources of this lane: byte offsets from the tile's blob ----
+    uint32_t woff[NRAW];
     size_t wstep;  // bytes per K step
     if (MODE == 0) {
-        const uint8_t *g_row = ti.blob + (size_t)(ti.nt * NFT + wave * 16 + n_lane) * rowH;
-        wsrc[0] = g_row;
-        if (NPASS == 2) wsrc[NPASS - 1] = g_row + (size_t)ti.Fx * rowH;  // up row
+        const uint32_t g_row = (uint32_t)((ti.nt * NFT + wave * 16 + n_lane) * rowH);
+        woff[0] = g_row;
+        if (NPASS == 2) woff[NPASS - 1] = g_row + (uint32_t)(ti.Fx * rowH);  // up row
         wstep = (size_t)PF_KSB * bb;
     } else {
         // wave w, n-tile t: rows nt*256 + 32 w + 2 n + t (t = row parity); the
-        // pair (2i, 2i+1) of block c sits at (c*H + 2i)*bb, the odd row's
-        // block 12 (3-bit) / 16 (4-bit) bytes after a dword boundary - 2
+        // pair (2i, 2i+1) of block c sits at (c*H + 2i)*bb, and the odd row's
+        // block starts 2 bytes into the pair's dword 3 (3-bit) / 4 (4-bit)
         const int hp = ti.nt * NFT + 32 * wave + 2 * n_lane;
-        const uint8_t *dn = ti.blob + (size_t)2 * ti.Fx * rowH + (size_t)hp * bb;
+        const uint32_t dn = (uint32_t)(2 * ti.Fx * rowH + (size_t)hp * bb);
 #pragma unroll
         for (int t = 0; t < NTW; ++t)
 #pragma unroll
             for (int b = 0; b < PF_KSB; ++b)
-                wsrc[t * PF_KSB + b] = dn + (size_t)b * P.H * bb + (BITS == 4 ? 16 : 12) * t;
+                woff[t * PF_KSB + b] = dn + (uint32_t)(b * P.H * bb) + (BITS == 4 ? 16 : 12) * t;
         wstep = (size_t)PF_KSB * P.H * bb;
     }
-    uint32_t rw[NRAW][NW];
     auto load_w = [&](int ks, uint32_t (&dst)[NRAW][NW]) {
+        const uint8_t *base = ti.blob + (size_t)ks * wstep;
 #pragma unroll
         for (int b = 0; b < NRAW; ++b) {
-            const uint32_t *s = (const uint32_t *)(wsrc[b] + (size_t)ks * wstep);
+            const uint32_t *s = (const uint32_t *)(base + woff[b]);
             const u32x4 v = *(const u32x4a4 *)s;
             dst[b][0] = v.x;
             dst[b][1] = v.y;
@@ -356,18 +356,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BI
 #pragma unroll
         for (int m = 0; m < MTL; ++m) acc[a][m] = float4v{0.f, 0.f, 0.f, 0.f};
 
-    load_a(0);
-    load_w(0, rw);
-    store_a(0);
-    __syncthreads();
-    for (int ks = 0; ks < nks; ++ks) {
-        const int cur = ks & 1;
-        const bool more = ks + 1 < nks;
-        uint32_t rn[NRAW][NW];
-        if (more) {
-            load_a(ks + 1);
-            load_w(ks + 1, rn);
-        }
+    auto compute = [&](int cur, const uint32_t (&rw)[NRAW][NW]) {
 #pragma unroll
         for (int blk = 0; blk < PF_KSB; ++blk) {
             bf16x8 av[MTL][XP];
@@ -400,14 +389,34 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BI
                 }
             }
         }
-        if (more) {
-            store_a(cur ^ 1);
+    };
+
+    // ring of PD steps in registers (static slots: the step loop is unrolled by PD)
+    uint32_t rw[PD][NRAW][NW];
+    u32x4 ra[PD][2];
 #pragma unroll
-            for (int b = 0; b < NRAW; ++b)
-#pragma unroll
-                for (int i = 0; i < NW; ++i) rw[b][i] = rn[b][i];
+    for (int u = 0; u < PD; ++u) {
+        if (u < nks) {
+            load_a(u, ra[u]);
+            load_w(u, rw[u]);
         }
-        __syncthreads();
+    }
+    store_a(0, ra[0]);
+    __syncthreads();
+    for (int k0 = 0; k0 < nks; k0 += PD) {
+#pragma unroll
+        for (int u = 0; u < PD; ++u) {
+            const int ks = k0 + u;
+            if (ks < nks) {
+                compute(ks & 1, rw[u]);
+                if (ks + 1 < nks) store_a((ks + 1) & 1, ra[(u + 1) % PD]);
+                if (ks + PD < nks) {
+                    load_a(ks + PD, ra[u]);
+                    load_w(ks + PD, rw[u]);
+                }
+                __syncthreads();
+            }
+        }
     }
     // ---- epilogue ----
 #pragma unroll
@@ -419,7 +428,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BI
             if (MODE == 0) {
                 const int col = ti.nt * NFT + wave * 16 + n_lane;  // feature
                 const float g = acc[0][m][r], u = acc[NPASS - 1][m][r];
-                const float h = g / (1.0f + expf(-g)) * u;
+                const float h = g * u * __frcp_rn(1.0f + __expf(-g));
                 const uint16_t hh = f2bf_bits(h);
                 const uint16_t hl = f2bf_bits(h - bf16_bits_to_float(hh));
                 uint16_t *dst = (uint16_t *)P.hout + (size_t)(P.slot_hrow0[ti.slot] + ti.r0 + rr) * (2 * hs) + col;
@@ -496,15 +505,28 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_gemm(GemmParams P) {
     }
 }
 
+// Four consecutive outputs per thread (H is a multiple of 256).
 __global__ __launch_bounds__(256) void k_prefill_combine(CombineParams P) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= (size_t)P.T * P.H) return;
     const size_t t = i / P.H, h = i - t * P.H;
     const float *src = P.out_pairs + t * P.k * P.H + h;
-    float acc = src[0];
-    for (int j = 1; j < P.k; ++j) acc += src[(size_t)j * P.H];
-    if (P.out_shared) acc += P.out_shared[i];
-    P.y[i] = acc;
+    float4v acc = *(const float4v *)src;
+    for (int j = 1; j < P.k; ++j) {
+        const float4v v = *(const float4v *)(src + (size_t)j * P.H);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    if (P.out_shared) {
+        const float4v s = *(const float4v *)(P.out_shared + i);
+        acc.x += s.x;
+        acc.y += s.y;
+        acc.z += s.z;
+        acc.w += s.w;
+    }
+    *(float4v *)(P.y + i) = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -548,7 +570,7 @@ hipError_t prefill_gemm_launch(int mode, int bits, const GemmParams &P, int cus,
 hipError_t prefill_combine_launch(const CombineParams &P, hipStream_t st) {
     const size_t n = (size_t)P.T * P.H;
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_prefill_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, P);
+    hipLaunchKernelGGL(k_prefill_combine, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, st, P);
     return hipGetLastError();
 }
 

@@ -63,20 +63,15 @@ __global__ __launch_bounds__(1024) void k_group_scan(GroupParams P) {
     __shared__ int s_act[1024];
     const int tid = threadIdx.x;
     const int E = P.E, per = (E + 1023) / 1024;
-    // per expert: exclusive running sum over chunks; total
+    const int nc = P.nchunks;
+    // per expert: total over chunks (independent loads)
     int tot[MOE_SCAN_PER_MAX];
     int my = 0, myact = 0;
     for (int i = 0; i < per; ++i) {
-        int e = tid * per + i;
+        const int e = tid * per + i;
         int run = 0;
-        if (e < E) {
-            for (int c = 0; c < P.nchunks; ++c) {
-                uint32_t *cc = P.chunk_counts + (size_t)c * E + e;
-                int v = (int)*cc;
-                *cc = (uint32_t)run;
-                run += v;
-            }
-        }
+        if (e < E)
+            for (int c = 0; c < nc; ++c) run += (int)P.chunk_counts[(size_t)c * E + e];
         tot[i] = run;
         my += run;
         myact += (run > 0);
@@ -95,13 +90,25 @@ __global__ __launch_bounds__(1024) void k_group_scan(GroupParams P) {
     }
     int base = s_part[tid] - my, abase = s_act[tid] - myact;
     for (int i = 0; i < per; ++i) {
-        int e = tid * per + i;
-        if (e < E) {
-            P.offsets[e] = base;
-            for (int c = 0; c < P.nchunks; ++c) P.chunk_counts[(size_t)c * E + e] += (uint32_t)base;
-            if (tot[i] > 0) P.active[1 + abase++] = e;
-            base += tot[i];
+        const int e = tid * per + i;
+        if (e >= E) break;
+        P.offsets[e] = base;
+        // chunk c's first position: base + pairs of e in chunks before c
+        // (eight counts read before any is overwritten)
+        int run = base;
+        for (int c0 = 0; c0 < nc; c0 += 8) {
+            uint32_t v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                v[j] = c0 + j < nc ? P.chunk_counts[(size_t)(c0 + j) * E + e] : 0u;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (c0 + j < nc) P.chunk_counts[(size_t)(c0 + j) * E + e] = (uint32_t)run;
+                run += (int)v[j];
+            }
         }
+        if (tot[i] > 0) P.active[1 + abase++] = e;
+        base += tot[i];
     }
     if (tid == 1023) {
         P.offsets[E] = s_part[1023];
@@ -109,32 +116,38 @@ __global__ __launch_bounds__(1024) void k_group_scan(GroupParams P) {
     }
 }
 
-// Each chunk places its pairs in (token, slot) order.
+// Each chunk places its pairs in (token, slot) order, 64 pairs at a time:
+// a pair's position is its expert's running count in the chunk plus the
+// number of earlier pairs of the same expert among the 64.  The chunk's
+// expert ids are read into LDS first (one round of loads).
 __global__ __launch_bounds__(64) void k_group_place(GroupParams P) {
     extern __shared__ __align__(16) uint8_t smem[];
-    uint32_t *cnt = (uint32_t *)smem;
+    uint32_t *cnt = (uint32_t *)smem;              // [E]
+    int *ids = (int *)(smem + 4 * (size_t)P.E);     // [GRP_CHUNK_TOKENS * k]
     const int c = blockIdx.x, lane = threadIdx.x;
+    const int64_t p0 = (int64_t)c * GRP_CHUNK_TOKENS * P.k;
+    const int64_t p1 = min((int64_t)(c + 1) * GRP_CHUNK_TOKENS * P.k, (int64_t)P.T * P.k);
+    const int n = (int)(p1 - p0);
     for (int e = lane; e < P.E; e += 64) cnt[e] = P.chunk_counts[(size_t)c * P.E + e];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    for (int i = lane; i < n; i += 64) {
+        const int e = P.idx[p0 + i];
+        ids[i] = (unsigned)e < (unsigned)P.E ? e : -1;  // ids outside [0, E) are not placed
+    }
     __syncthreads();
-    const int t0 = c * GRP_CHUNK_TOKENS, t1 = min(t0 + GRP_CHUNK_TOKENS, P.T);
-    const int k = P.k;
-    for (int t = t0; t < t1; ++t) {
-        int e = lane < k ? P.idx[(size_t)t * k + lane] : -1;
-        if ((unsigned)e >= (unsigned)P.E) e = -1;  // ids outside [0, E) are not placed
-        // slots of this token earlier in the row that name the same expert
-        int dup = 0, later = 0;
-        for (int j = 0; j < k; ++j) {
-            int ej = __shfl(e, j, 64);
+    for (int b = 0; b < n; b += 64) {
+        const int e = b + lane < n ? ids[b + lane] : -1;
+        int dup = 0;
+        bool later = false;
+        for (int j = 0; j < 64; ++j) {
+            const int ej = __builtin_amdgcn_readlane(e, j);
             dup += (j < lane) && (ej == e);
-            later += (j > lane) && (ej == e);
+            later |= (j > lane) && (ej == e);
         }
-        uint32_t base = 0;
-        if (e >= 0) base = cnt[e];
+        const uint32_t base = e >= 0 ? cnt[e] : 0u;
         __syncthreads();
         if (e >= 0) {
-            P.pairs[base + dup] = t * k + lane;
-            if (later == 0) cnt[e] = base + dup + 1;
+            P.pairs[base + dup] = (int32_t)(p0 + b + lane);
+            if (!later) cnt[e] = base + dup + 1;
         }
         __syncthreads();
     }
@@ -158,7 +171,8 @@ hipError_t group_launch(const GroupParams &P, hipStream_t st) {
     const size_t lds = (size_t)P.E * 4;
     if (P.nchunks > 0) hipLaunchKernelGGL(k_group_count, dim3(P.nchunks), dim3(256), lds, st, P);
     hipLaunchKernelGGL(k_group_scan, dim3(1), dim3(1024), 0, st, P);
-    if (P.nchunks > 0) hipLaunchKernelGGL(k_group_place, dim3(P.nchunks), dim3(64), lds, st, P);
+    const size_t lds_place = lds + (size_t)GRP_CHUNK_TOKENS * P.k * 4;
+    if (P.nchunks > 0) hipLaunchKernelGGL(k_group_place, dim3(P.nchunks), dim3(64), lds_place, st, P);
     return hipGetLastError();
 }
 
