@@ -233,9 +233,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BI
     constexpr int NFT = MODE == 0 ? PF_NF_GU : PF_NF_DN;
     constexpr int NB = NPASS * NTW;                // weight fragments per lane per block
     constexpr int bb = BITS == 4 ? 18 : 14;
-    // gate/up: dwords of one block pair; down: dwords per block
-    constexpr int NW = MODE == 0 ? (BITS == 4 ? 9 : 7) : (BITS == 4 ? 5 : 4);
-    constexpr int NRAW = MODE == 0 ? NPASS : NTW * PF_KSB;  // raw runs per lane per K step
+    // dwords of one block pair: gate/up, two consecutive blocks of a row;
+    // down, one block of the rows 2i (n-tile 0) and 2i+1 (n-tile 1)
+    constexpr int NW = BITS == 4 ? 9 : 7;
+    constexpr int NRAW = MODE == 0 ? NPASS : PF_KSB;  // pairs per lane per K step
     constexpr bool XF32 = MODE == 0 && XP == 2;              // fp32 activations, split into bf16 hi + lo
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n_lane = lane & 15;
@@ -261,7 +262,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BI
             a_off = (size_t)(P.slot_hrow0[ti.slot] + ti.r0 + a_r) * (2 * hs) + 32 * a_blk + 8 * a_g;
         }
     }
-    constexpr int PD = MODE == 0 ? 3 : 2;  // K steps in flight: step s loads at the end of step s - PD
+    constexpr int PD = (MODE == 1 && BITS == 4) ? 2 : 3;  // K steps in flight: step s loads at the end of step s - PD
     auto load_a = [&](int ks, u32x4 (&ra)[2]) {
         ra[0] = u32x4{0u, 0u, 0u, 0u};
         ra[1] = u32x4{0u, 0u, 0u, 0u};
@@ -312,15 +313,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BI
         wstep = (size_t)PF_KSB * bb;
     } else {
         // wave w, n-tile t: rows nt*256 + 32 w + 2 n + t (t = row parity); the
-        // pair (2i, 2i+1) of block c sits at (c*H + 2i)*bb, and the odd row's
-        // block starts 2 bytes into the pair's dword 3 (3-bit) / 4 (4-bit)
+        // pair (2i, 2i+1) of block c sits at (c*H + 2i)*bb
         const int hp = ti.nt * NFT + 32 * wave + 2 * n_lane;
         const uint32_t dn = (uint32_t)(2 * ti.Fx * rowH + (size_t)hp * bb);
 #pragma unroll
-        for (int t = 0; t < NTW; ++t)
-#pragma unroll
-            for (int b = 0; b < PF_KSB; ++b)
-                woff[t * PF_KSB + b] = dn + (uint32_t)(b * P.H * bb) + (BITS == 4 ? 16 : 12) * t;
+        for (int b = 0; b < PF_KSB; ++b) woff[b] = dn + (uint32_t)(b * P.H * bb);
         wstep = (size_t)PF_KSB * P.H * bb;
     }
     auto load_w = [&](int ks, uint32_t (&dst)[NRAW][NW]) {
@@ -333,9 +330,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BI
             dst[b][1] = v.y;
             dst[b][2] = v.z;
             dst[b][3] = v.w;
-            if constexpr (NW == 5) {
-                dst[b][4] = s[4];
-            } else if constexpr (NW == 7) {
+            if constexpr (NW == 7) {
                 dst[b][4] = s[4];
                 dst[b][5] = s[5];
                 dst[b][6] = s[6];
@@ -369,7 +364,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BI
                 // fragment f: gate/up pass f, or down n-tile f (row parity f)
                 BFields<BITS> fl;
                 if (MODE == 0) fl = block_fields<BITS>(rw[f], blk == 1, BITS == 4 ? 4 : 3);
-                else fl = block_fields<BITS>(rw[f * PF_KSB + blk], f == 1, 0);
+                else fl = block_fields<BITS>(rw[blk], f == 1, BITS == 4 ? 4 : 3);
                 const bf16x8 bq = __builtin_bit_cast(bf16x8, deq_group<BITS>(fl, g_lane));
                 const float d = half_bits_to_float(fl.d);
                 // the m-tiles' MFMAs issue back to back, then their scaling
