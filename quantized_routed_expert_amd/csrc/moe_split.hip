@@ -1,7 +1,8 @@
-// moe_split.hip -- the routed-expert layer for decode windows of one or two
-// rows, in one launch, split over 32-column slices of every expert's FFN.
+// moe_split.hip -- the routed-expert layer for decode windows of one to four
+// rows (at most 64 (row, expert) pairs), in one launch, split over 32-column
+// slices of every expert's FFN.
 //
-// With one or two rows the matrix cores would idle on 15 of their 16 rows,
+// With so few rows the matrix cores would idle on most of their 16 rows,
 // and the layer is a stream of quantized bytes: per row and weight it needs
 // one multiply-add.  So this launch does integer dot products on the vector
 // units instead (v_dot8_i32_i4: eight signed 4-bit products per instruction):
@@ -19,8 +20,10 @@
 // Work items: (expert, 32-column slice c of its FFN).  An item needs the 32
 // gate rows and 32 up rows of the slice and column block c of down (the
 // prepared down layout stores that column block contiguously): 3 * H * B
-// bytes, copied straight into LDS with direct-to-LDS loads.  The workgroup
-// computes the slice's gate and up values, SwiGLU, and the slice's share of
+// bytes.  Each wave loads its own share of an item into registers, stages it
+// in its own part of LDS and computes from it; the next item's loads are in
+// flight during the current one.  The workgroup computes the slice's gate and
+// up values, SwiGLU, and the slice's share of
 // the down projection for all H output rows, and stores it as tagged words
 // (value + call tag).  After all items, every workgroup sums a range of
 // outputs over the slices (slice order fixed) and the k experts (top-k order)
