@@ -11,8 +11,9 @@
 //
 // Kernels:
 //   k_prefill_plan   one workgroup: active experts (+ the shared expert as a
-//                    group of every row) ordered by decreasing row count, and
-//                    the prefix sums of their tile counts.
+//                    group of every row) ordered by decreasing size class
+//                    (floor(log2(rows)); ties in expert order), and the prefix
+//                    sums of their tile counts.
 //   k_prefill_gemm   persistent grouped GEMM, tiles of 16, 32 or 64 rows (by
 //                    the group's size) x 64 outputs.  Each wave dequantizes
 //                    the weight fragments of its own MFMAs in registers, as
@@ -50,9 +51,7 @@ __global__ __launch_bounds__(1024) void k_prefill_plan(PlanParams P) {
     uint64_t *keys = (uint64_t *)smem;                  // [ns]
     int *tg = (int *)(smem + 8 * (size_t)(P.E + 1));   // [ns] gate/up tiles per sorted slot
     int *td = tg + (P.E + 1);                          // [ns]
-    // key: row count (desc), then expert id (asc; the shared expert is id -1 -> first)
-    for (int i = tid; i < ns; i += 1024) {
-        int e, cnt;
+    auto slot_of = [&](int i, int &e, int &cnt) {
         if (P.has_shared && i == na) {
             e = -1;
             cnt = P.T;
@@ -60,15 +59,8 @@ __global__ __launch_bounds__(1024) void k_prefill_plan(PlanParams P) {
             e = P.active[1 + i];
             cnt = P.offsets[e + 1] - P.offsets[e];
         }
-        keys[i] = ((uint64_t)(uint32_t)cnt << 32) | (uint32_t)(0x7FFFFFFF - (e + 1));
-    }
-    __syncthreads();
-    for (int i = tid; i < ns; i += 1024) {
-        uint64_t ki = keys[i];
-        int rank = 0;
-        for (int j = 0; j < ns; ++j) rank += keys[j] > ki;
-        int e = 0x7FFFFFFF - (int)(uint32_t)ki - 1;
-        int cnt = (int)(ki >> 32);
+    };
+    auto place = [&](int rank, int e, int cnt) {
         P.slot_exp[rank] = e;
         P.slot_cnt[rank] = cnt;
         P.slot_row0[rank] = e < 0 ? 0 : P.offsets[e];
@@ -76,6 +68,60 @@ __global__ __launch_bounds__(1024) void k_prefill_plan(PlanParams P) {
         const int mt = (cnt + 16 * pf_mtl(cnt) - 1) / (16 * pf_mtl(cnt));
         tg[rank] = mt * ((e < 0 ? P.Fs : P.F) / PF_NF_GU);
         td[rank] = mt * (P.H / PF_NF_DN);
+    };
+    if (ns <= 1024) {
+        // order: size class floor(log2(rows)) descending, then the active list's
+        // order (expert id; the shared expert, a group of every row, after the
+        // routed ones of its class).  Rank = slots of larger classes + earlier
+        // slots of the same class (ballots per class within a wave, then the
+        // earlier waves' counts).
+        __shared__ int s_wcnt[16][32];
+        const int lane = tid & 63, wv = tid >> 6;
+        int e = 0, cnt = 0, cls = -1;
+        if (tid < ns) {
+            slot_of(tid, e, cnt);
+            cls = 31 - __builtin_clz((unsigned)cnt);
+        }
+        int within = 0;
+        for (int v = 0; v < 32; ++v) {
+            const uint64_t m = __ballot(cls == v);
+            if (cls == v) within = __popcll(m & ((1ull << lane) - 1ull));
+            if (lane == 0) s_wcnt[wv][v] = __popcll(m);
+        }
+        __syncthreads();
+        // per class: the earlier waves' counts (in place), then the slots of the
+        // larger classes (one wave, a suffix sum over the 32 classes)
+        __shared__ int s_above[32];
+        if (tid < 32) {
+            int run = 0;
+            for (int w = 0; w < 16; ++w) {
+                const int c = s_wcnt[w][tid];
+                s_wcnt[w][tid] = run;
+                run += c;
+            }
+            int above = 0;
+            for (int v = 0; v < 32; ++v) {  // every lane takes part in every shuffle
+                const int r = __shfl(run, v, 64);
+                above += v > tid ? r : 0;
+            }
+            s_above[tid] = above;
+        }
+        __syncthreads();
+        if (tid < ns) place(s_above[cls] + s_wcnt[wv][cls] + within, e, cnt);
+    } else {
+        // key: row count (desc), then expert id (asc; the shared expert is id -1 -> first)
+        for (int i = tid; i < ns; i += 1024) {
+            int e, cnt;
+            slot_of(i, e, cnt);
+            keys[i] = ((uint64_t)(uint32_t)cnt << 32) | (uint32_t)(0x7FFFFFFF - (e + 1));
+        }
+        __syncthreads();
+        for (int i = tid; i < ns; i += 1024) {
+            const uint64_t ki = keys[i];
+            int rank = 0;
+            for (int j = 0; j < ns; ++j) rank += keys[j] > ki;
+            place(rank, 0x7FFFFFFF - (int)(uint32_t)ki - 1, (int)(ki >> 32));
+        }
     }
     __syncthreads();
     // tile prefix sums: thread i owns a run of consecutive slots

@@ -116,26 +116,31 @@ __global__ __launch_bounds__(1024) void k_group_scan(GroupParams P) {
     }
 }
 
-// Each chunk places its pairs in (token, slot) order, 64 pairs at a time:
-// a pair's position is its expert's running count in the chunk plus the
-// number of earlier pairs of the same expert among the 64.  The chunk's
-// expert ids are read into LDS first (one round of loads).
-__global__ __launch_bounds__(64) void k_group_place(GroupParams P) {
+// Each chunk places its pairs in (token, slot) order, 256 pairs per round,
+// 64 per wave.  A pair's position is its expert's count before the round,
+// plus the pairs of that expert in the earlier waves' batches of the round,
+// plus the earlier ones in its own batch.  The chunk's expert ids are read
+// into LDS first (one round of loads), padded with -1 to whole rounds.
+constexpr int GRP_PLACE_THREADS = 256;
+
+__global__ __launch_bounds__(GRP_PLACE_THREADS) void k_group_place(GroupParams P) {
     extern __shared__ __align__(16) uint8_t smem[];
-    uint32_t *cnt = (uint32_t *)smem;              // [E]
-    int *ids = (int *)(smem + 4 * (size_t)P.E);     // [GRP_CHUNK_TOKENS * k]
-    const int c = blockIdx.x, lane = threadIdx.x;
+    uint32_t *cnt = (uint32_t *)smem;               // [E]
+    int *ids = (int *)(smem + ((4 * (size_t)P.E + 15) & ~(size_t)15));  // [chunk pairs rounded up to 256]
+    const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t p0 = (int64_t)c * GRP_CHUNK_TOKENS * P.k;
     const int64_t p1 = min((int64_t)(c + 1) * GRP_CHUNK_TOKENS * P.k, (int64_t)P.T * P.k);
     const int n = (int)(p1 - p0);
-    for (int e = lane; e < P.E; e += 64) cnt[e] = P.chunk_counts[(size_t)c * P.E + e];
-    for (int i = lane; i < n; i += 64) {
-        const int e = P.idx[p0 + i];
+    const int n_pad = (n + GRP_PLACE_THREADS - 1) / GRP_PLACE_THREADS * GRP_PLACE_THREADS;
+    for (int e = tid; e < P.E; e += GRP_PLACE_THREADS) cnt[e] = P.chunk_counts[(size_t)c * P.E + e];
+    for (int i = tid; i < n_pad; i += GRP_PLACE_THREADS) {
+        const int e = i < n ? P.idx[p0 + i] : -1;
         ids[i] = (unsigned)e < (unsigned)P.E ? e : -1;  // ids outside [0, E) are not placed
     }
     __syncthreads();
-    for (int b = 0; b < n; b += 64) {
-        const int e = b + lane < n ? ids[b + lane] : -1;
+    for (int b = 0; b < n; b += GRP_PLACE_THREADS) {
+        const int i = b + 64 * wave + lane;
+        const int e = ids[i];
         int dup = 0;
         bool later = false;
         for (int j = 0; j < 64; ++j) {
@@ -143,11 +148,19 @@ __global__ __launch_bounds__(64) void k_group_place(GroupParams P) {
             dup += (j < lane) && (ej == e);
             later |= (j > lane) && (ej == e);
         }
+        int prior = 0;
+        for (int w2 = 0; w2 < wave; ++w2) {
+            const u32x4 *row = (const u32x4 *)(ids + b + 64 * w2);
+            for (int j = 0; j < 16; ++j) {
+                const u32x4 v = row[j];
+                prior += ((int)v.x == e) + ((int)v.y == e) + ((int)v.z == e) + ((int)v.w == e);
+            }
+        }
         const uint32_t base = e >= 0 ? cnt[e] : 0u;
         __syncthreads();
         if (e >= 0) {
-            P.pairs[base + dup] = (int32_t)(p0 + b + lane);
-            if (!later) cnt[e] = base + dup + 1;
+            P.pairs[base + prior + dup] = (int32_t)(p0 + i);
+            if (!later) atomicAdd(&cnt[e], (uint32_t)(dup + 1));  // this batch's pairs of e (a sum: any order)
         }
         __syncthreads();
     }
@@ -171,8 +184,11 @@ hipError_t group_launch(const GroupParams &P, hipStream_t st) {
     const size_t lds = (size_t)P.E * 4;
     if (P.nchunks > 0) hipLaunchKernelGGL(k_group_count, dim3(P.nchunks), dim3(256), lds, st, P);
     hipLaunchKernelGGL(k_group_scan, dim3(1), dim3(1024), 0, st, P);
-    const size_t lds_place = lds + (size_t)GRP_CHUNK_TOKENS * P.k * 4;
-    if (P.nchunks > 0) hipLaunchKernelGGL(k_group_place, dim3(P.nchunks), dim3(64), lds_place, st, P);
+    const size_t per_chunk = ((size_t)GRP_CHUNK_TOKENS * P.k + GRP_PLACE_THREADS - 1) / GRP_PLACE_THREADS *
+                             GRP_PLACE_THREADS;
+    const size_t lds_place = ((lds + 15) & ~(size_t)15) + per_chunk * 4;
+    if (P.nchunks > 0)
+        hipLaunchKernelGGL(k_group_place, dim3(P.nchunks), dim3(GRP_PLACE_THREADS), lds_place, st, P);
     return hipGetLastError();
 }
 

@@ -289,3 +289,40 @@ def test_prepare_qweights_order(name):
     exp = raw.reshape(n, -1).copy()
     exp[:, gu:] = exp[:, gu:].reshape(n, H, F // 32, bb).transpose(0, 2, 1, 3).reshape(n, -1)
     assert np.array_equal(got, exp)
+
+
+# ---- prefill tile heights: groups at every 16/32/64-row boundary ------------------
+
+@pytest.mark.parametrize("bits,x_dtype", [(3, "bf16"), (4, "f32")])
+def test_prefill_group_size_boundaries(orc, bits, x_dtype):
+    """moe_expert_ffn on the prefill path with a hand-made grouping (top-1):
+    group sizes straddle the 16-, 32- and 64-row tile heights and need several
+    64-row tiles, so every tile height, ragged last tiles and multi-tile
+    groups are compared element by element with the oracle."""
+    counts = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 129]
+    E = len(counts) + 1  # one expert with no rows
+    print(f"[prefill groups] bits={bits} x={x_dtype} counts={counts}", flush=True)
+    cfg = synth.scaled_config(synth.CONFIGS["prefill"], name=f"pf_groups{bits}", bits=bits, x_dtype=x_dtype,
+                              hidden=512, n_experts=E, ffn=256, shared_ffn=0, top_k=1)
+    T = sum(counts)
+    li = synth.layer_inputs(cfg, T=T)
+    ids = np.concatenate([np.full(c, e + 1, dtype=np.int32) for e, c in enumerate(counts)])
+    rng = np.random.default_rng(7)
+    idx = rng.permutation(ids).reshape(T, 1).astype(np.int32)
+    ro, rp, ra = orc.group(idx, E)
+    assert [int(ro[e + 1] - ro[e]) for e in range(E)] == [0] + counts
+    rw = rng.uniform(0.25, 1.0, T).astype(np.float64)
+    ref = orc.expert_ffn(li.x, li.x_code, 1, bits, E, cfg.hidden, cfg.ffn, li.routed, ro, rp, ra, rw)
+    x = x_to_dev(li.x, cfg.x_dtype)
+    routed_t, qw = moe.prepare_qweights(torch.from_numpy(li.routed).to(DEV), bits, E, cfg.hidden, cfg.ffn)
+    out = torch.full((T, cfg.hidden), float("nan"), device=DEV)
+    ws = moe.workspace(T, E, 1, cfg.hidden, cfg.ffn, 0, P)
+    moe.expert_ffn(x, qw, torch.from_numpy(ro).to(DEV), torch.from_numpy(np.ascontiguousarray(rp)).to(DEV),
+                   torch.from_numpy(ra).to(DEV), 1, out, ws, pair_w=torch.from_numpy(rw.astype(np.float32)).to(DEV),
+                   path=P)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    e = rel_err(got, ref)
+    print(f"    rel err {e:.3e}", flush=True)
+    assert e <= TOL
