@@ -248,7 +248,7 @@ def main():
         metric_value, unit = toks, "tok/s"
         ach = (fl_gu + fl_dn) / (kern_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(args.workload),
                 "kernel": "layer (route, group, plan, gate/up GEMM, down GEMM, combine)",
                 "flops_per_launch": fl_gu + fl_dn}
         dtype = "bf16"
