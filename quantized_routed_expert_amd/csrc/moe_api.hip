@@ -295,7 +295,7 @@ bool decode_fits(int T, int E, int k, int H, int F, int Fs, int bits, int x_dtyp
     return decode_lds_layout(P, xf ? 2 : 1) <= DEC_LDS_BUDGET;
 }
 
-// ---- column-split decode launch (windows of one or two rows) ----
+// ---- column-split decode launch (windows of one to four rows, T*k <= 64) ----
 int split_xps(int bits) { return bits == 4 ? 36 : 84; }  // digit dwords per pair slot in LDS
 
 int split_lds_layout(SplitParams &P) {

@@ -15,19 +15,20 @@
 //                    (floor(log2(rows)); ties in expert order), and the prefix
 //                    sums of their tile counts.
 //   k_prefill_gemm   persistent grouped GEMM, tiles of 16, 32 or 64 rows (by
-//                    the group's size) x 64 outputs.  Each wave dequantizes
-//                    the weight fragments of its own MFMAs in registers, as
-//                    bf16 holding the exact integer codes minus the bias; the
-//                    activations (bf16, exact) are gathered into LDS by the
-//                    group's row list; v_mfma_f32_16x16x32_bf16 covers one
-//                    32-wide quant block, and the fp16 block scale multiplies
-//                    that block's fp32 partial.  Gate/up tiles compute both
-//                    projections for the same 64 features and apply SwiGLU in
-//                    fp32, storing h as bf16 hi + lo (h = hi + lo to 16 bits);
-//                    down tiles run both parts through the MFMA and write
-//                    w * o per (token, slot) pair.
+//                    the group's size) x 128 features (gate/up) or 256
+//                    outputs (down).  Each wave dequantizes the weight
+//                    fragments of its own MFMAs in registers, as bf16 holding
+//                    the exact integer codes minus the bias; the activations
+//                    (bf16, exact) are gathered into LDS by the group's row
+//                    list; v_mfma_f32_16x16x32_bf16 covers one 32-wide quant
+//                    block, and the fp16 block scale multiplies that block's
+//                    fp32 partial.  Gate/up tiles compute both projections for
+//                    the same 128 features and apply SwiGLU in fp32, storing h
+//                    as bf16 hi + lo (h = hi + lo to 16 bits); down tiles run
+//                    both parts through the MFMA and write w * o per (token,
+//                    slot) pair.
 //   k_prefill_combine  y_t = (((w_t0 o_t0 + w_t1 o_t1) + ...) + s_t) in slot
-//                    order, one thread per output element.
+//                    order, four consecutive outputs per thread.
 #include "moe_device.h"
 #include "moe_internal.h"
 

@@ -270,12 +270,6 @@ __device__ __forceinline__ void lds_read_b128(const uint8_t *p, uint32_t (&w)[N]
     }
 }
 
-// One 16-byte piece per lane from global memory straight into LDS at
-// lds_wave + 16 * lane (lds_wave the same for the whole wave).
-__device__ __forceinline__ void lds_dma16(const void *g, uint8_t *lds_wave) {
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)lds_wave, 16, 0, 0);
-}
-
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
