@@ -34,6 +34,23 @@
 
 namespace moe {
 
+#ifdef MOE_PHASE_TRACE
+// Per-tile timestamps (100 MHz device clock), analysis builds only: word
+// [mode][tile][4] = start, end, m-tiles, workgroup.
+__device__ uint64_t *g_trace_pf = nullptr;
+extern "C" int moe_trace_prefill_set(void *buf) {
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_trace_pf), &buf, sizeof(buf)) == hipSuccess ? 0 : -1;
+}
+#define PTRACE(i, v)                                          \
+    do {                                                      \
+        if (g_trace_pf && threadIdx.x == 0) g_trace_pf[i] = (v); \
+    } while (0)
+#else
+#define PTRACE(i, v) \
+    do {             \
+    } while (0)
+#endif
+
 constexpr int PF_KSB = 2;        // quant blocks per K step
 constexpr int PF_THREADS = 512;  // eight waves
 constexpr int PF_NF_GU = 128;    // features per gate/up tile (8 waves x 16)
@@ -268,9 +285,11 @@ struct GemmSmem {
 };
 
 struct TileInfo {
-    int slot, cnt, nt, r0, nrows, Fx;
+    int slot, cnt, nt, r0, nrows, Fx, hrow0, mtl;
     bool shared_slot;
     const uint8_t *blob;
+    int a_pair;  // this thread's A row: its pair id (gate/up gather), -1 when none
+    int pr64;    // thread tid < 64: pair id of tile row tid, -1 when none
 };
 
 template <int MODE, int BITS, int XP, int MTL>
@@ -301,12 +320,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BI
     size_t a_off = 0;
     if (a_ld) {
         if (MODE == 0) {
-            int t;
-            if (ti.shared_slot) t = ti.r0 + a_r;
-            else t = P.pairs[P.slot_row0[ti.slot] + ti.r0 + a_r] / P.k;
+            const int t = ti.shared_slot ? ti.r0 + a_r : ti.a_pair / P.k;
             a_off = (size_t)t * P.H + 32 * a_blk + 8 * a_g;
         } else {
-            a_off = (size_t)(P.slot_hrow0[ti.slot] + ti.r0 + a_r) * (2 * hs) + 32 * a_blk + 8 * a_g;
+            a_off = (size_t)(ti.hrow0 + ti.r0 + a_r) * (2 * hs) + 32 * a_blk + 8 * a_g;
         }
     }
     constexpr int PD = (MODE == 1 && BITS == 4) ? 2 : 3;  // K steps in flight: step s loads at the end of step s - PD
@@ -473,7 +490,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BI
                 const float h = g * u * __frcp_rn(1.0f + __expf(-g));
                 const uint16_t hh = f2bf_bits(h);
                 const uint16_t hl = f2bf_bits(h - bf16_bits_to_float(hh));
-                uint16_t *dst = (uint16_t *)P.hout + (size_t)(P.slot_hrow0[ti.slot] + ti.r0 + rr) * (2 * hs) + col;
+                uint16_t *dst = (uint16_t *)P.hout + (size_t)(ti.hrow0 + ti.r0 + rr) * (2 * hs) + col;
                 dst[0] = hh;
                 dst[hs] = hl;
             } else {
@@ -505,45 +522,71 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BI
 template <int MODE, int BITS, int XP>
 __global__ __launch_bounds__(PF_THREADS) void k_prefill_gemm(GemmParams P) {
     __shared__ __align__(16) GemmSmem<MODE, BITS, XP> sm;
+    // the slot plan, read once: prefix[ns + 1], then per slot exp, cnt, row0, hrow0
+    extern __shared__ __align__(16) int s_plan[];
     constexpr int bb = BITS == 4 ? 18 : 14;
     const int tid = threadIdx.x;
     const int ns = P.prefix[P.E + 2];
     const int total = P.prefix[ns];
     const size_t rowH = (size_t)(P.H >> 5) * bb;
+    int *s_prefix = s_plan, *s_exp = s_plan + ns + 1, *s_cnt = s_exp + ns, *s_row0 = s_cnt + ns,
+        *s_hrow0 = s_row0 + ns;
+    for (int i = tid; i <= ns; i += PF_THREADS) s_prefix[i] = P.prefix[i];
+    for (int i = tid; i < ns; i += PF_THREADS) {
+        s_exp[i] = P.slot_exp[i];
+        s_cnt[i] = P.slot_cnt[i];
+        s_row0[i] = P.slot_row0[i];
+        s_hrow0[i] = P.slot_hrow0[i];
+    }
+    __syncthreads();
 
-    for (int tile = blockIdx.x; tile < total; tile += gridDim.x) {
-        // slot: largest i with prefix[i] <= tile
-        int lo = 0, hi = ns - 1;
+    // tile -> slot and rows, from LDS; the rows' pair ids are global loads,
+    // issued one tile ahead
+    auto tile_info = [&](int tile, TileInfo &ti) {
+        int lo = 0, hi = ns - 1;  // slot: largest i with prefix[i] <= tile
         while (lo < hi) {
-            int mid = (lo + hi + 1) >> 1;
-            if (P.prefix[mid] <= tile) lo = mid;
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_prefix[mid] <= tile) lo = mid;
             else hi = mid - 1;
         }
-        TileInfo ti;
         ti.slot = lo;
-        const int e = P.slot_exp[lo];
-        ti.cnt = P.slot_cnt[lo];
+        const int e = s_exp[lo];
+        ti.cnt = s_cnt[lo];
         ti.shared_slot = e < 0;
         ti.Fx = ti.shared_slot ? P.Fs : P.F;
-        const int mtl = pf_mtl(ti.cnt);
-        const int MT = 16 * mtl;
+        ti.hrow0 = s_hrow0[lo];
+        ti.mtl = pf_mtl(ti.cnt);
+        const int MT = 16 * ti.mtl;
         const int mtiles = (ti.cnt + MT - 1) / MT;
-        const int local = tile - P.prefix[lo];
+        const int local = tile - s_prefix[lo];
         const int mt = local % mtiles;
         ti.nt = local / mtiles;
         ti.r0 = mt * MT;
         ti.nrows = min(MT, ti.cnt - ti.r0);
         ti.blob = ti.shared_slot ? P.w_shared : P.w_routed + (size_t)e * 3 * ti.Fx * rowH;
+        const int row0 = s_row0[lo] + ti.r0;
+        const int a_r = 16 * (tid >> 7) + (tid & 15);  // this thread's A row (see gemm_tile)
+        ti.a_pair = (MODE == 0 && !ti.shared_slot && (tid >> 7) < ti.mtl && a_r < ti.nrows) ? P.pairs[row0 + a_r] : -1;
+        ti.pr64 = (tid < 64 && tid < ti.nrows && !ti.shared_slot) ? P.pairs[row0 + tid] : -1;
+    };
 
+    int tile = blockIdx.x;
+    TileInfo cur;
+    if (tile < total) tile_info(tile, cur);
+    for (; tile < total; tile += gridDim.x) {
+        TileInfo nxt;
+        const bool more = tile + (int)gridDim.x < total;
+        if (more) tile_info(tile + gridDim.x, nxt);
         __syncthreads();  // the previous tile's epilogue is done with sm.pair
-        if (tid < 64) {
-            int pr = -1;
-            if (tid < ti.nrows && !ti.shared_slot) pr = P.pairs[P.slot_row0[ti.slot] + ti.r0 + tid];
-            sm.pair[tid] = pr;
-        }
-        if (mtl == 4) gemm_tile<MODE, BITS, XP, 4>(P, sm, ti);
-        else if (mtl == 2) gemm_tile<MODE, BITS, XP, 2>(P, sm, ti);
-        else gemm_tile<MODE, BITS, XP, 1>(P, sm, ti);
+        if (tid < 64) sm.pair[tid] = cur.pr64;
+        PTRACE(((size_t)MODE << 20) + 4 * (size_t)tile, __builtin_amdgcn_s_memrealtime());
+        if (cur.mtl == 4) gemm_tile<MODE, BITS, XP, 4>(P, sm, cur);
+        else if (cur.mtl == 2) gemm_tile<MODE, BITS, XP, 2>(P, sm, cur);
+        else gemm_tile<MODE, BITS, XP, 1>(P, sm, cur);
+        PTRACE(((size_t)MODE << 20) + 4 * (size_t)tile + 1, __builtin_amdgcn_s_memrealtime());
+        PTRACE(((size_t)MODE << 20) + 4 * (size_t)tile + 2, (uint64_t)cur.mtl);
+        PTRACE(((size_t)MODE << 20) + 4 * (size_t)tile + 3, (uint64_t)blockIdx.x);
+        if (more) cur = nxt;
     }
 }
 
@@ -588,14 +631,20 @@ hipError_t prefill_plan_launch(const PlanParams &P, hipStream_t st) {
 // Persistent grid: every workgroup resident (cus x workgroups per CU).
 template <int MODE, int BITS, int XP>
 static hipError_t gemm_t(const GemmParams &P, int cus, hipStream_t st) {
+    // dynamic LDS: the slot plan (prefix[ns + 1] + 4 arrays of ns), ns <= E + 1
+    const size_t plan_bytes = (size_t)(5 * (P.E + 1) + 1) * 4;
     static int occ = 0;
     if (occ == 0) {
-        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void *)k_prefill_gemm<MODE, BITS, XP>,
-                                                                     PF_THREADS, 0);
+        hipError_t e = hipFuncSetAttribute((const void *)k_prefill_gemm<MODE, BITS, XP>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (5 * (MOE_MAX_EXPERTS_DEV + 1) + 1) * 4);
+        if (e != hipSuccess) return e;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void *)k_prefill_gemm<MODE, BITS, XP>, PF_THREADS,
+                                                         (5 * (MOE_MAX_EXPERTS_DEV + 1) + 1) * 4);
         if (e != hipSuccess) return e;
         if (occ < 1) occ = 1;
     }
-    hipLaunchKernelGGL((k_prefill_gemm<MODE, BITS, XP>), dim3(cus * occ), dim3(PF_THREADS), 0, st, P);
+    hipLaunchKernelGGL((k_prefill_gemm<MODE, BITS, XP>), dim3(cus * occ), dim3(PF_THREADS), plan_bytes, st, P);
     return hipGetLastError();
 }
 
