@@ -293,7 +293,7 @@ def test_prepare_qweights_order(name):
 
 # ---- prefill tile heights: groups at every 16/32/64-row boundary ------------------
 
-@pytest.mark.parametrize("bits,x_dtype", [(3, "bf16"), (4, "f32")])
+@pytest.mark.parametrize("bits,x_dtype", [(3, "bf16"), (4, "f32"), (3, "f32"), (4, "bf16")])
 def test_prefill_group_size_boundaries(orc, bits, x_dtype):
     """moe_expert_ffn on the prefill path with a hand-made grouping (top-1):
     group sizes straddle the 16-, 32- and 64-row tile heights and need several
@@ -326,3 +326,12 @@ def test_prefill_group_size_boundaries(orc, bits, x_dtype):
     e = rel_err(got, ref)
     print(f"    rel err {e:.3e}", flush=True)
     assert e <= TOL
+
+
+def test_prefill_many_experts(orc):
+    """More than 1024 groups in one chunk (1,071 active experts + the shared
+    one): the plan's general ranking and the GEMMs' slot plan at its largest."""
+    print("[layer] prefill E=1100 T=512", flush=True)
+    cfg = _cfg("e512", name="pf_e1100", n_experts=1100, hidden=256, ffn=256, shared_ffn=256, top_k=8)
+    li = synth.layer_inputs(cfg, T=512, threads=4)
+    _check(orc, li, P)
