@@ -126,16 +126,9 @@ __device__ __forceinline__ uint32_t lds_u32(const uint8_t *p) { return *(const u
 // row stride the 16 rows x 4 k-groups of one read fall in distinct banks.
 // ---------------------------------------------------------------------------
 template <int BITS>
-struct BVal;
-template <>
-struct BVal<4> {
-    half8 b;
-    float d;
-};
-template <>
-struct BVal<3> {
-    half8 lo, hb;
-    float d;
+struct BVal {
+    half8 b;  // exact fp16 codes minus the bias
+    float d;  // block scale
 };
 
 // A operands of blocks b, b+1.  Rows past the window's tokens read a valid
@@ -181,41 +174,28 @@ struct Pair<4, NP> {
 };
 
 // 3-bit pair: block b = bytes 0..13 (scale 0-1, low parts 2..9, third bits
-// 10..13), block b+1 = 14..27.
+// 10..13), block b+1 = 14..27 (scale, low parts 16..23, third bits 24..27).
 template <int NP>
 struct Pair<3, NP> {
-    uint32_t d0, d2, d3, d6, qb, qb1;
+    uint32_t w[7];
     half8 a[2][NP];
     __device__ __forceinline__ void load(const uint8_t *buf, int ro, int p, int g, const uint8_t *ab, int a_stride,
                                          int part_off) {
         const int o = ro + 28 * p;
-        d0 = lds_u32(buf + o);
-        d3 = lds_u32(buf + o + 12);
-        d2 = lds_u32(buf + o + 8);
-        d6 = lds_u32(buf + o + 24);
-        qb = lds_u32(buf + o + 4 * ((g + 1) >> 1));  // holds low-part bytes 2+2g, 3+2g
-        qb1 = lds_u32(buf + o + 16 + 4 * (g >> 1));  // holds low-part bytes 16+2g, 17+2g
+#pragma unroll
+        for (int i = 0; i < 7; ++i) w[i] = lds_u32(buf + o + 4 * i);
         load_a<NP>(a, ab, 2 * p, a_stride, part_off);
     }
     __device__ __forceinline__ BVal<3> get(int i, int g) const {
         BVal<3> v;
-        uint32_t qw, qh, sh;
         if (i == 0) {
-            qw = qb;
-            sh = (g & 1) ? 0u : 2u;
-            qh = __builtin_amdgcn_alignbyte(d3, d2, 2u);  // bytes 10..13
-            v.d = half_bits_to_float(d0);
+            v.b = unpack3(__builtin_amdgcn_alignbyte(w[1], w[0], 2u), __builtin_amdgcn_alignbyte(w[2], w[1], 2u),
+                          __builtin_amdgcn_alignbyte(w[3], w[2], 2u), (uint32_t)g);
+            v.d = half_bits_to_float(w[0]);
         } else {
-            qw = qb1;
-            sh = (g & 1) ? 2u : 0u;
-            qh = d6;  // bytes 24..27
-            v.d = half_bits_to_float(d3 >> 16);
+            v.b = unpack3(w[4], w[5], w[6], (uint32_t)g);
+            v.d = half_bits_to_float(w[3] >> 16);
         }
-        // low-part bytes 2g and 2g+1 of the block, each replicated into bytes 0 and 2
-        const uint32_t sel0 = 0x0C000C00u | (sh << 16) | sh;
-        const uint32_t p0 = __builtin_amdgcn_perm(qw, qw, sel0);
-        const uint32_t p1 = __builtin_amdgcn_perm(qw, qw, sel0 + 0x00010001u);
-        unpack3(p0, p1, qh >> (2 * g), v.lo, v.hb);
         return v;
     }
 };
@@ -224,18 +204,8 @@ struct Pair<3, NP> {
 template <int BITS, int NP>
 __device__ __forceinline__ float4v block_dot(const BVal<BITS> &v, const half8 *a) {
     const float4v z = {0.f, 0.f, 0.f, 0.f};
-    float4v dd;
-    if constexpr (BITS == 4) {
-        dd = mfma16(a[0], v.b, z);
-        if constexpr (NP == 2) dd = mfma16(a[1], v.b, dd);
-    } else {
-        dd = mfma16(a[0], v.lo, z);
-        dd = mfma16(a[0], v.hb, dd);
-        if constexpr (NP == 2) {
-            dd = mfma16(a[1], v.lo, dd);
-            dd = mfma16(a[1], v.hb, dd);
-        }
-    }
+    float4v dd = mfma16(a[0], v.b, z);
+    if constexpr (NP == 2) dd = mfma16(a[1], v.b, dd);
     return dd;
 }
 
@@ -305,26 +275,24 @@ struct DnBlk<4> {
 
 template <>
 struct DnBlk<3> {
-    uint32_t dw, ql, h0, h1;
+    uint32_t dw, r0, r1, r2, r3;
     half8 a[2];
+    // qa: the dword at or below the block's first low-part byte
     __device__ __forceinline__ void load(const uint8_t *buf, int a0, int qa, const uint8_t *ab) {
-        dw = lds_u32(buf + (a0 & ~3));         // scale
-        ql = lds_u32(buf + qa);                // low-part bytes 2g, 2g+1 of the block
-        const int r = (a0 + 10) & ~3;          // third bits: block bytes 10..13
-        h0 = lds_u32(buf + r);
-        h1 = lds_u32(buf + r + 4);
+        dw = lds_u32(buf + (a0 & ~3));       // scale
+        r0 = lds_u32(buf + qa);              // low parts and third bits from the dwords at qa ..
+        r1 = lds_u32(buf + qa + 4);
+        r2 = lds_u32(buf + qa + 8);
+        r3 = lds_u32(buf + (a0 & ~3) + 12);  // (odd rows: the last dword is r2 and r3 goes unused)
         a[0] = *(const half8 *)ab;
         a[1] = *(const half8 *)(ab + 16);
     }
-    // sh_d: scale shift (bits); sh_q: byte of low-part byte 2g in ql; sh_h: byte shift of the third bits
-    __device__ __forceinline__ BVal<3> get(uint32_t sh_d, uint32_t sh_q, uint32_t sh_h, int g) const {
+    // sh_d: scale shift (bits); sh_c: byte offset of the low parts in r0
+    __device__ __forceinline__ BVal<3> get(uint32_t sh_d, uint32_t sh_c, int g) const {
         BVal<3> v;
         v.d = half_bits_to_float(dw >> sh_d);
-        const uint32_t qh = __builtin_amdgcn_alignbyte(h1, h0, sh_h);
-        const uint32_t sel0 = 0x0C000C00u | (sh_q << 16) | sh_q;
-        const uint32_t p0 = __builtin_amdgcn_perm(ql, ql, sel0);
-        const uint32_t p1 = __builtin_amdgcn_perm(ql, ql, sel0 + 0x00010001u);
-        unpack3(p0, p1, qh >> (2 * g), v.lo, v.hb);
+        v.b = unpack3(__builtin_amdgcn_alignbyte(r1, r0, sh_c), __builtin_amdgcn_alignbyte(r2, r1, sh_c),
+                      __builtin_amdgcn_alignbyte(r3, r2, sh_c), (uint32_t)g);
         return v;
     }
 };
@@ -339,14 +307,13 @@ __device__ __forceinline__ void dn_chunk_mma(float4v &acc, const uint8_t *buf, i
     const int a0 = n * bb;                                   // block 0 of row n
     const uint32_t par = (uint32_t)(n & 1);                  // a0 mod 4 = 2 * par
     const uint32_t sh_d = 16u * par;
-    const int q = a0 + 2 + (BITS == 4 ? 4 : 2) * g;          // first code / low-part byte of this lane
+    const int q = a0 + 2 + (BITS == 4 ? 4 * g : 0);          // first code / low-part byte of this lane
     const int qa = q & ~3;
     const uint32_t sh_c = (uint32_t)(q & 3);
-    const uint32_t sh_h = (uint32_t)((a0 + 10) & 3);
     auto step = [&](const DnBlk<BITS> &b) {
         BVal<BITS> v;
         if constexpr (BITS == 4) v = b.get(sh_d, sh_c);
-        else v = b.get(sh_d, sh_c, sh_h, g);
+        else v = b.get(sh_d, sh_c, g);
         const float4v d = block_dot<BITS, 2>(v, b.a);
         acc.x = fmaf(v.d, d.x, acc.x);
         acc.y = fmaf(v.d, d.y, acc.y);
@@ -368,20 +335,20 @@ __device__ __forceinline__ void dn_chunk_mma(float4v &acc, const uint8_t *buf, i
 // Activation k-groups: the 8 values of (token t, block b, k-group g) that one
 // MFMA lane of k-group g feeds, i.e. the block's weights at pos_in_block(g, e)
 // e = 0..7.  4-bit: elements 4g+0..3 and 16+4g+0..3 (two loads); 3-bit:
-// elements 2g+{0,1} + {0, 8, 16, 24} (four loads).  The value of slot e is
-// loaded value xslot(e) of the group.
+// elements 8g+0..7 (one load).  The value of slot e is loaded value xslot(e)
+// of the group.
 // ---------------------------------------------------------------------------
 template <int BITS>
 __host__ __device__ constexpr int xslot(int e) {
     // pos_in_block(BITS, 0, e) -> its index among the loaded elements
     return BITS == 4 ? (pos_in_block(4, 0, e) < 16 ? pos_in_block(4, 0, e) : pos_in_block(4, 0, e) - 12)
-                     : 2 * (pos_in_block(3, 0, e) >> 3) + (pos_in_block(3, 0, e) & 1);
+                     : pos_in_block(3, 0, e);
 }
 
 template <int BITS, int XPARTS>
 struct XGroup {
     uint32_t w[4 * XPARTS];  // bf16: 8 values in 4 dwords; fp32: 8 dwords
-    // row: the token's activations; base: element index 4g (4-bit) or 2g (3-bit) of block b
+    // row: the token's activations; base: element index 4g (4-bit) or 8g (3-bit) of block b
     __device__ __forceinline__ void load(const void *row, int base) {
         if constexpr (BITS == 4) {
             if constexpr (XPARTS == 1) {
@@ -395,15 +362,14 @@ struct XGroup {
                 w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
             }
         } else {
-#pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                if constexpr (XPARTS == 1) {
-                    w[f] = *(const uint32_t *)((const uint16_t *)row + base + 8 * f);
-                } else {
-                    const uint2 a = *(const uint2 *)((const float *)row + base + 8 * f);
-                    w[2 * f] = a.x;
-                    w[2 * f + 1] = a.y;
-                }
+            if constexpr (XPARTS == 1) {
+                const u32x4 a = *(const u32x4 *)((const uint16_t *)row + base);
+                w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+            } else {
+                const u32x4 a = *(const u32x4 *)((const float *)row + base);
+                const u32x4 b = *(const u32x4 *)((const float *)row + base + 4);
+                w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+                w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
             }
         }
     }
@@ -531,7 +497,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
                 const int gc = ok ? grp : 0;  // (an in-bounds load for lanes without a group)
                 const int t = (int)__umulhi((uint32_t)gc, P.m_xgrp);
                 const int rem = gc - t * P.xgrp;  // 4 b + g
-                const int base = (rem >> 2) * 32 + (BITS == 4 ? 4 : 2) * (rem & 3);
+                const int base = (rem >> 2) * 32 + (BITS == 4 ? 4 : 8) * (rem & 3);
                 xg[q].load((const uint8_t *)P.x + (size_t)t * H * (XPARTS == 1 ? 2 : 4), base);
                 xg_t[q] = ok ? t : -1;
                 xg_pos[q] = rem;

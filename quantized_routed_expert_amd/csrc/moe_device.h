@@ -38,9 +38,8 @@ __host__ __device__ constexpr int pos_in_block(int bits, int g, int e) {
         int r = ((e >> 2) & 1) + ((e & 1) << 1);
         return 4 * g + r + ((e >> 1) & 1) * 16;
     } else {
-        // e: 0:(2g) 1:(2g+16) 2:(2g+8) 3:(2g+24) 4:(2g+1) 5:(2g+17) 6:(2g+9) 7:(2g+25)
-        int f = ((e & 1) << 1) | ((e >> 1) & 1);  // 2-bit field index 0..3
-        return 2 * g + ((e >> 2) & 1) + 8 * f;
+        // natural order: weights 8g .. 8g+7 (the 2-bit field g of all eight low-part bytes)
+        return 8 * g + e;
     }
 }
 
@@ -51,9 +50,8 @@ __host__ __device__ __forceinline__ void group_slot_of(int bits, int i, int &g, 
         g = (i & 15) >> 2;
         e = ((r & 1) << 2) | (hi << 1) | (r >> 1);
     } else {
-        int f8 = i >> 3;
-        g = (i & 7) >> 1;
-        e = ((i & 1) << 2) | ((f8 & 1) << 1) | (f8 >> 1);
+        g = i >> 3;
+        e = i & 7;
     }
 }
 
@@ -92,31 +90,30 @@ __device__ __forceinline__ half8 unpack4(uint32_t q) {
     return __builtin_bit_cast(half8, r);
 }
 
-// 3-bit: two fp16 operands whose MFMA products add up to (code - 4):
-//   lo = (2-bit low part - 4), hb = 4 * third bit, both exact, in the order of
-//   pos_in_block(3, g, .).  p0/p1: ql[2g] / ql[2g+1] replicated into bytes 0
-//   and 2 (other bytes zero); th = qh >> 2g.
-__device__ __forceinline__ void unpack3(uint32_t p0, uint32_t p1, uint32_t th, half8 &lo, half8 &hb) {
-    // low parts: field f of byte j in the lower half, field f+2 in the upper half
-    const uint32_t sA = H2(0x3C00, 0x2C00), oA = H2(0xE404, 0xD440);  // (1, 1/16), (-1028, -68)
-    const uint32_t sB = H2(0x3400, 0x2400), oB = H2(0xDC10, 0xCD00);  // (1/4, 1/64), (-260, -20)
-    u32x4 a;
-    a.x = pk_fma_h2(and_or(p0, 0x00300003u, FP16_MAGIC), sA, oA);
-    a.y = pk_fma_h2(and_or(p0, 0x00C0000Cu, FP16_MAGIC), sB, oB);
-    a.z = pk_fma_h2(and_or(p1, 0x00300003u, FP16_MAGIC), sA, oA);
-    a.w = pk_fma_h2(and_or(p1, 0x00C0000Cu, FP16_MAGIC), sB, oB);
-    lo = __builtin_bit_cast(half8, a);
-    // third bits: positions 0, 8, 1, 9 (and +16) of th
-    const uint32_t s0 = H2(0x4400, 0x4400), o0 = H2(0xEC00, 0xEC00);  // 4, -4096
-    const uint32_t s8 = H2(0x2400, 0x2400), o8 = H2(0xCC00, 0xCC00);  // 1/64, -16
-    const uint32_t s1 = H2(0x4000, 0x4000), o1 = H2(0xE800, 0xE800);  // 2, -2048
-    const uint32_t s9 = H2(0x2000, 0x2000), o9 = H2(0xC800, 0xC800);  // 1/128, -8
-    u32x4 b;
-    b.x = pk_fma_h2(and_or(th, 0x00010001u, FP16_MAGIC), s0, o0);
-    b.y = pk_fma_h2(and_or(th, 0x01000100u, FP16_MAGIC), s8, o8);
-    b.z = pk_fma_h2(and_or(th, 0x00020002u, FP16_MAGIC), s1, o1);
-    b.w = pk_fma_h2(and_or(th, 0x02000200u, FP16_MAGIC), s9, o9);
-    hb = __builtin_bit_cast(half8, b);
+// 3-bit: weights 8g .. 8g+7 of one block -> 8 exact fp16 values (code - 4), in
+// that order.  qs0 / qs1: low-part bytes 0..3 / 4..7 of the block, qh: its
+// third-bit word.  The codes are assembled one per byte, then looked up in a
+// byte table: fp16(c - 4) has a zero low byte for c = 0..7.
+__device__ __forceinline__ half8 unpack3(uint32_t qs0, uint32_t qs1, uint32_t qh, uint32_t g) {
+    const uint32_t l0 = (qs0 >> (2u * g)) & 0x03030303u;  // low parts, one per byte
+    const uint32_t l1 = (qs1 >> (2u * g)) & 0x03030303u;
+    const uint32_t t0 = (qh >> (8u * g)) & 15u;            // third bits of weights 8g .. 8g+3
+    const uint32_t t1 = (qh >> (8u * g + 4u)) & 15u;
+    // bit j of t -> bit 2 of byte j: t * (4 + 2^9 + 2^16 + 2^23); the other
+    // partial products land on bits the mask drops (all distinct: no carries)
+    const uint32_t c0 = and_or(__umul24(t0, 0x810204u), 0x04040404u, l0);
+    const uint32_t c1 = and_or(__umul24(t1, 0x810204u), 0x04040404u, l1);
+    // high bytes of fp16(c - 4), c = 0..7: C4 C2 C0 BC 00 3C 40 42
+    const uint32_t tab_lo = 0xBCC0C2C4u, tab_hi = 0x42403C00u;
+    const uint32_t h0 = __builtin_amdgcn_perm(tab_hi, tab_lo, c0);
+    const uint32_t h1 = __builtin_amdgcn_perm(tab_hi, tab_lo, c1);
+    // (zero, high byte) pairs: selector byte 0x0C is the constant zero
+    u32x4 r;
+    r.x = __builtin_amdgcn_perm(h0, h0, 0x050C040Cu);  // weights 0, 1
+    r.y = __builtin_amdgcn_perm(h0, h0, 0x070C060Cu);  // weights 2, 3
+    r.z = __builtin_amdgcn_perm(h1, h1, 0x050C040Cu);
+    r.w = __builtin_amdgcn_perm(h1, h1, 0x070C060Cu);
+    return __builtin_bit_cast(half8, r);
 }
 
 __device__ __forceinline__ float4v mfma16(half8 a, half8 b, float4v c) {
