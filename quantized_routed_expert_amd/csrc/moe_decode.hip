@@ -814,7 +814,12 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             else prefetch_first_tile();
             const uint8_t *ab = s_xa + (size_t)tok * P.x_rs + (size_t)(kc * cbH) * 64 + g_lane * 16;
             if (first_task && rho == 0) TRACEW(10);
-            chunk_mma<BITS, XPARTS>(accr[rho], s_chunk, rsH, cbH, n_lane, g_lane, ab, 64, T * P.x_rs);
+            // (a register array indexed by rho would be read and written through
+            // select chains over all its elements)
+            float4v acc = {0.f, 0.f, 0.f, 0.f};
+            chunk_mma<BITS, XPARTS>(acc, s_chunk, rsH, cbH, n_lane, g_lane, ab, 64, T * P.x_rs);
+            if (rho == 0) accr[0] = acc;
+            else accr[1] = acc;
             if (first_task && rho == 0) TRACEW(11);
         }
         if (first_task) TRACEW(2);
@@ -863,8 +868,101 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
     TRACE(3);
 
     // ======================= Phase C: down + weighted write + combine =======================
+    // Combine items follow the down tiles in the same round robin (so they go
+    // to the workgroups with one tile fewer): item ci = part ci % DEC_COMB_PARTS
+    // of 128-row slice ci / DEC_COMB_PARTS, i.e. DEC_DN_ROWS / DEC_COMB_PARTS
+    // rows of y for every token: ((w0 o0 + w1 o1) + ...) + shared.  It waits
+    // for the slice's count of finished slots, loads every (term, output) word
+    // of its rows (DEC_COMB_LOADS per thread in flight together), checks each
+    // for this call's tag and parks it in LDS (the staged h and the chunk
+    // buffers are free: these items come after the workgroup's tiles), then
+    // sums each output in the fixed order.  The last part of a slice returns
+    // the slice's counters to zero.
+    constexpr int CROWS = DEC_DN_ROWS / DEC_COMB_PARTS;
+    const int n_comb = (P.mode & DEC_MODE_COMBINE) ? tiles_per_slot * DEC_COMB_PARTS : 0;
+    auto combine_part = [&](int ci) {
+        const int crg = ci / DEC_COMB_PARTS, row0 = crg * DEC_DN_ROWS + (ci - crg * DEC_COMB_PARTS) * CROWS;
+        uint32_t *cnt = &P.slice_count[crg * DEC_CSTRIDE];
+        if (tid == 0) {
+            uint32_t spins = 0;
+            while (ld_dev_u32(cnt) < (uint32_t)n_slots) {
+                __builtin_amdgcn_s_sleep(2);
+                if (++spins > DEC_SPIN_LIMIT || (ld_dev_u32(P.err) & 1u)) {
+                    atomicOr(P.err, 1u);
+                    break;
+                }
+            }
+        }
+        __syncthreads();
+        const int nterm = k + hs;
+        const int nout = T * CROWS;
+        float *s_terms = (float *)(smem + P.lds_xa);
+        const int ob = min(nout, ((P.lds_total - P.lds_xa) >> 2) / nterm);
+        for (int o0 = 0; o0 < nout; o0 += ob) {
+            const int nb = min(ob, nout - o0);
+            const int nw = nterm * nb;
+            auto src_of = [&](int i) {
+                const int j = i / nb, o = o0 + (i - j * nb);
+                const int t = o / CROWS;
+                return P.oll + (size_t)(j < k ? t * k + j : TK + t) * H + row0 + (o - t * CROWS);
+            };
+            for (int i0 = 0; i0 < nw; i0 += DEC_COMB_LOADS * DEC_THREADS) {
+                uint64_t wd[DEC_COMB_LOADS];
+#pragma unroll
+                for (int q = 0; q < DEC_COMB_LOADS; ++q) {
+                    const int i = i0 + q * DEC_THREADS + tid;
+                    wd[q] = i < nw ? ld_dev_u64(src_of(i)) : 0;
+                }
+#pragma unroll
+                for (int q = 0; q < DEC_COMB_LOADS; ++q) {
+                    const int i = i0 + q * DEC_THREADS + tid;
+                    if (i < nw) {
+                        for (uint32_t spins = 0; (uint32_t)(wd[q] >> 32) != tag; ++spins) {
+                            if (spins > DEC_SPIN_LIMIT) {
+                                atomicOr(P.err, 1u);
+                                break;
+                            }
+                            __builtin_amdgcn_s_sleep(1);
+                            wd[q] = ld_dev_u64(src_of(i));
+                        }
+                        s_terms[i] = __builtin_bit_cast(float, (uint32_t)wd[q]);
+                    }
+                }
+            }
+            __syncthreads();
+            for (int ol = tid; ol < nb; ol += DEC_THREADS) {
+                const int o = o0 + ol;
+                const int t = o / CROWS;
+                float acc2 = s_terms[ol];
+                for (int j = 1; j < nterm; ++j) acc2 += s_terms[j * nb + ol];  // ((w0 o0 + w1 o1) + ...) + shared
+                P.y[(size_t)t * H + row0 + (o - t * CROWS)] = acc2;
+            }
+            __syncthreads();  // the terms are read before the next batch or item reuses the LDS
+        }
+        if (tid == 0 && add_dev(cnt + 1, 1u) == (uint32_t)(DEC_COMB_PARTS - 1)) {
+            store_dev_u32(cnt, 0u);
+            store_dev_u32(cnt + 1, 0u);
+        }
+    };
+    // Thread 0 counts each finished tile and acts on the returned count of its
+    // slot one tile later, so that the round trip overlaps the next tile.
+    uint32_t p_dn = 0;
+    int p_s = -1;
+    auto settle = [&]() {
+        if (p_s >= 0 && p_dn == (uint32_t)(tiles_per_slot - 1)) {
+            // every tile of this slot has passed its wait: the counters can return to zero
+            store_dev_u32(&P.gu_count[p_s * DEC_CSTRIDE], 0u);
+            store_dev_u32(&P.dn_count[p_s * DEC_CSTRIDE], 0u);
+        }
+        p_s = -1;
+    };
     int cur_slot = -1;
-    for (int ti = first_tile; ti < n_tiles; ti += G) {
+    bool c_next = c_holds_tile;  // c holds this tile's first chunk (loaded during the previous work item)
+    for (int ti = first_tile; ti < n_tiles + n_comb; ti += G) {
+        if (ti >= n_tiles) {
+            combine_part(ti - n_tiles);
+            continue;
+        }
         const Tile tl = tile_of(ti);
         const int s = tl.s, rg = tl.rg, Fx = tl.Fx;
         const bool shared_slot = tl.shared;
@@ -875,7 +973,8 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             map_fx = Fx;
         }
         const int n_tok = s_slot_cnt[s];
-        if (!(ti == first_tile && c_holds_tile)) chunk_load(c, rows_d, mapF);  // prefetch before the wait
+        if (!c_next) chunk_load(c, rows_d, mapF);  // before the wait
+        c_next = false;
 
         if (s != cur_slot) {
             if (tid < T) s_xmax[tid] = 0u;
@@ -899,32 +998,42 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             const int row0 = shared_slot ? TK : s_slot_start[s];
             const int ngrp = Fx >> 3;
             const int nit = n_tok * ngrp;
+            // every item's words are loaded before any is checked (one round trip)
             float hv[4][8];
+            uint64_t wd[4][8];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int it = tid + DEC_THREADS * q;
                 if (it < nit) {
                     const int m = (int)__umulhi((uint32_t)it, tl.m_ngrp), gi = it - m * ngrp;
                     const uint64_t *src = P.hll + (size_t)(row0 + m) * P.h_stride + gi * 8;
-                    uint64_t wd[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) wd[q][e] = ld_dev_u64(src + e);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int it = tid + DEC_THREADS * q;
+                if (it < nit) {
+                    const int m = (int)__umulhi((uint32_t)it, tl.m_ngrp), gi = it - m * ngrp;
+                    const uint64_t *src = P.hll + (size_t)(row0 + m) * P.h_stride + gi * 8;
                     for (uint32_t spins = 0;; ++spins) {  // until every word carries this call's tag
                         bool ok = true;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            wd[e] = ld_dev_u64(src + e);
-                            ok = ok && (uint32_t)(wd[e] >> 32) == tag;
-                        }
+                        for (int e = 0; e < 8; ++e) ok = ok && (uint32_t)(wd[q][e] >> 32) == tag;
                         if (ok) break;
                         if (spins > DEC_SPIN_LIMIT) {
                             atomicOr(P.err, 1u);
                             break;
                         }
                         __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) wd[q][e] = ld_dev_u64(src + e);
                     }
                     float mx = 0.0f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        hv[q][e] = __builtin_bit_cast(float, (uint32_t)wd[e]);
+                        hv[q][e] = __builtin_bit_cast(float, (uint32_t)wd[q][e]);
                         mx = fmaxf(mx, fabsf(hv[q][e]));
                     }
                     atomicMax(&s_xmax[m], __builtin_bit_cast(uint32_t, mx));
@@ -967,7 +1076,17 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             chunk_store(c, s_chunk, mapF);
             if (ti == first_tile && ci == 0) TRACEW(5);
             wave_lds_handoff();
-            if (ci + 1 < nchF) chunk_load(c, rows_d + (size_t)(ci + 1) * segF, mapF);
+            if (ci + 1 < nchF) {
+                chunk_load(c, rows_d + (size_t)(ci + 1) * segF, mapF);
+            } else if (ti + G < n_tiles) {
+                // the next tile's first chunk streams in while this one computes
+                // (same chunk geometry only: the map is per FFN width)
+                const Tile tn = tile_of(ti + G);
+                if (tn.Fx == map_fx) {
+                    chunk_load(c, tn.rows, mapF);
+                    c_next = true;
+                }
+            }
             dn_chunk_mma<BITS>(acc, s_chunk, rsF, cbF, n_lane, g_lane, ab + (size_t)ci * cbF * 128);
             wave_lds_handoff();
         }
@@ -993,72 +1112,13 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         if (ti == first_tile) TRACE(7);
         __syncthreads();  // every wave's output stores are issued before the workgroup counts this tile
         if (tid == 0) {
-            // both counts in flight together
-            const uint32_t old = add_dev(&P.slice_count[rg * DEC_CSTRIDE], 1u);
-            const uint32_t dn = add_dev(&P.dn_count[s * DEC_CSTRIDE], 1u);
-            if (dn == (uint32_t)(tiles_per_slot - 1)) {
-                // every tile of this slot has passed its wait: the counters can return to zero
-                store_dev_u32(&P.gu_count[s * DEC_CSTRIDE], 0u);
-                store_dev_u32(&P.dn_count[s * DEC_CSTRIDE], 0u);
-            }
-            const bool last = old == (uint32_t)(n_slots - 1);
-            if (last) store_dev_u32(&P.slice_count[rg * DEC_CSTRIDE], 0u);
-            s_misc[1] = last && (P.mode & DEC_MODE_COMBINE);
-        }
-        __syncthreads();
-        if (s_misc[1]) {
-            // the last slot of this 128-row slice: y = ((w0 o0 + w1 o1) + ...) + shared
-            // every (term, output) word of the slice is loaded with the loads in
-            // flight together, checked for this call's tag and parked in LDS
-            // (the staged h and the chunk buffers are free here), then each
-            // output is summed in the fixed order; in batches of outputs that fit
-            const int nterm = k + hs;
-            const int nout = T * DEC_DN_ROWS;
-            float *s_terms = (float *)(smem + P.lds_xa);
-            const int ob = min(nout, ((P.lds_total - P.lds_xa) >> 2) / nterm);
-            for (int o0 = 0; o0 < nout; o0 += ob) {
-                const int nb = min(ob, nout - o0);
-                const int nw = nterm * nb;
-                for (int i0 = 0; i0 < nw; i0 += 4 * DEC_THREADS) {
-                    uint64_t wd[4];
-                    const uint64_t *src[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int i = i0 + q * DEC_THREADS + tid;
-                        const int j = i / nb, o = o0 + (i - j * nb);
-                        const int t = o / DEC_DN_ROWS, hrow = rg * DEC_DN_ROWS + (o - t * DEC_DN_ROWS);
-                        src[q] = P.oll + (size_t)(j < k ? t * k + j : TK + t) * H + hrow;
-                        wd[q] = i < nw ? ld_dev_u64(src[q]) : 0;
-                    }
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int i = i0 + q * DEC_THREADS + tid;
-                        if (i < nw) {
-                            for (uint32_t spins = 0; (uint32_t)(wd[q] >> 32) != tag; ++spins) {
-                                if (spins > DEC_SPIN_LIMIT) {
-                                    atomicOr(P.err, 1u);
-                                    break;
-                                }
-                                __builtin_amdgcn_s_sleep(1);
-                                wd[q] = ld_dev_u64(src[q]);
-                            }
-                            s_terms[i] = __builtin_bit_cast(float, (uint32_t)wd[q]);
-                        }
-                    }
-                }
-                __syncthreads();
-                for (int ol = tid; ol < nb; ol += DEC_THREADS) {
-                    const int o = o0 + ol;
-                    const int t = o / DEC_DN_ROWS, hrow = rg * DEC_DN_ROWS + (o - t * DEC_DN_ROWS);
-                    float acc2 = s_terms[ol];
-                    for (int j = 1; j < nterm; ++j) acc2 += s_terms[j * nb + ol];  // ((w0 o0 + w1 o1) + ...) + shared
-                    P.y[(size_t)t * H + hrow] = acc2;
-                }
-                __syncthreads();  // the terms are read before the next batch or tile reuses the LDS
-            }
-            cur_slot = -1;  // the staged h was overwritten
+            settle();  // the previous tile's count has long arrived
+            if (P.mode & DEC_MODE_COMBINE) add_dev(&P.slice_count[rg * DEC_CSTRIDE], 1u);
+            p_dn = add_dev(&P.dn_count[s * DEC_CSTRIDE], 1u);
+            p_s = s;
         }
     }
+    if (tid == 0) settle();  // the last tile's count
     TRACE(8);
     // the workspace moves on to the next call's tag
     if (tid == 0) epoch_advance(P.epoch, __builtin_amdgcn_readfirstlane(tag_v));

@@ -19,6 +19,8 @@ constexpr int DEC_MAX_F = 1024;              // expert FFN width handled by the 
 constexpr int DEC_XG_BF16 = 8;              // activation k-groups (8 values) loaded per thread: bf16
 constexpr int DEC_XG_F32 = 4;               // ... fp32
 constexpr uint32_t DEC_SPIN_LIMIT = 1u << 20;  // bounded waits: a wait that runs out sets err bit 0
+constexpr int DEC_COMB_LOADS = 8;           // combine: loads in flight per thread
+constexpr int DEC_COMB_PARTS = 8;           // combine items per 128-row slice
 constexpr int DEC_CSTRIDE = 64;              // 32-bit words between counters (one 256-byte line each)
 constexpr int EPOCH_SLOTS = 1024;            // per-workgroup copies of the call count (grids of <= 1024)
 constexpr int DEC_RANK_MAX_KEYS = 2048;      // routing by ranks: T*E up to this ...
