@@ -476,10 +476,6 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
     const bool route_mode = (P.mode & DEC_MODE_ROUTE) != 0;
     const int route_w = DEC_WAVES - 1 - wave;  // routing: row t by wave DEC_WAVES-1 - t % DEC_WAVES
     const bool routes = route_mode && route_w < T;
-    for (int i = tid; i < T; i += DEC_THREADS) s_xmax[i] = 0u;
-    if (route_mode)
-        for (int e = tid; e <= E; e += DEC_THREADS) s_hist[e] = 0;  // token masks
-    __syncthreads();
 
     // activation k-groups of this thread: group ((tid - 64) mod 512) + 512 q,
     // so a one-row window leaves waves 0 and 7 (grouping, routing) without any
@@ -530,11 +526,20 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         const int epl = (E + 63) >> 6;
         auto route_wave = [&](auto epl_c) {
             constexpr int EPL = decltype(epl_c)::value;
+            // both rows' logits (windows of up to 16 rows) in flight together
+            const int t2 = route_w + DEC_WAVES;
+            float v1[EPL], v2[EPL];
             uint32_t key[EPL];
-            route_keys<EPL>(P.logits + (size_t)route_w * E, E, lane, key);
+            route_load<EPL>(P.logits + (size_t)route_w * E, E, lane, v1);
+            if (t2 < T) route_load<EPL>(P.logits + (size_t)t2 * E, E, lane, v2);
             issue_x();
+            route_keys_of<EPL>(v1, E, lane, key);
             route_pick<EPL>(key, k, s_idx + route_w * k, s_w + route_w * k, lane);
-            for (int t = route_w + DEC_WAVES; t < T; t += DEC_WAVES) {
+            if (t2 < T) {
+                route_keys_of<EPL>(v2, E, lane, key);
+                route_pick<EPL>(key, k, s_idx + t2 * k, s_w + t2 * k, lane);
+            }
+            for (int t = t2 + DEC_WAVES; t < T; t += DEC_WAVES) {
                 route_keys<EPL>(P.logits + (size_t)t * E, E, lane, key);
                 route_pick<EPL>(key, k, s_idx + t * k, s_w + t * k, lane);
             }
@@ -551,6 +556,11 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         chunk_load(c, unit_rows(blockIdx.x, 0), mapH);
         pref = true;
     }
+    // (cleared only now: the loads above go out first)
+    for (int i = tid; i < T; i += DEC_THREADS) s_xmax[i] = 0u;
+    if (route_mode)
+        for (int e = tid; e <= E; e += DEC_THREADS) s_hist[e] = 0;  // token masks
+    __syncthreads();
     // per-token max |x| (the wait covers the tag, logits and activation
     // loads); reduced over the wave first when all its lanes hold one token
     const bool wave_tok = (P.xgrp & 63) == 0;

@@ -251,16 +251,26 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // argmax, an equal logit going to the lower expert id; softmax over the k.
 // The logits load (route_keys) is separate from the selection (route_pick),
 // so a wave can issue other loads in between.
+// route_load + route_keys_of: the raw logits loads and their keys apart, so a
+// wave can issue several rows' loads before it waits for the first.
 template <int EPL>
-__device__ __forceinline__ void route_keys(const float *row, int E, int lane, uint32_t (&key)[EPL]) {
-    float v[EPL];
+__device__ __forceinline__ void route_load(const float *row, int E, int lane, float (&v)[EPL]) {
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + 64 * i;
         v[i] = row[e < E ? e : 0];  // every lane loads (in bounds), so the loads issue as one sequence
     }
+}
+template <int EPL>
+__device__ __forceinline__ void route_keys_of(const float (&v)[EPL], int E, int lane, uint32_t (&key)[EPL]) {
 #pragma unroll
     for (int i = 0; i < EPL; ++i) key[i] = lane + 64 * i < E ? float_key(v[i]) : 0u;  // finite values: keys > 0
+}
+template <int EPL>
+__device__ __forceinline__ void route_keys(const float *row, int E, int lane, uint32_t (&key)[EPL]) {
+    float v[EPL];
+    route_load<EPL>(row, E, lane, v);
+    route_keys_of<EPL>(v, E, lane, key);
 }
 
 // One selection round: the largest key (an equal key goes to the lower
