@@ -209,27 +209,34 @@ __device__ __forceinline__ float4v block_dot(const BVal<BITS> &v, const half8 *a
     return dd;
 }
 
-// acc += d0 * dot(block 0) then d1 * dot(block 1): both blocks' MFMAs issue
-// before either result is scaled.
+// The products of one pair of blocks, before their scales are applied.
+struct PairDot {
+    float4v d0, d1;
+    float s0, s1;
+};
 template <int BITS, int NP>
-__device__ __forceinline__ void pair_mma(float4v &acc, const Pair<BITS, NP> &pr, int g) {
+__device__ __forceinline__ PairDot pair_dot(const Pair<BITS, NP> &pr, int g) {
     const BVal<BITS> v0 = pr.get(0, g), v1 = pr.get(1, g);
-    const float4v d0 = block_dot<BITS, NP>(v0, pr.a[0]);
-    const float4v d1 = block_dot<BITS, NP>(v1, pr.a[1]);
-    acc.x = fmaf(v0.d, d0.x, acc.x);
-    acc.y = fmaf(v0.d, d0.y, acc.y);
-    acc.z = fmaf(v0.d, d0.z, acc.z);
-    acc.w = fmaf(v0.d, d0.w, acc.w);
-    acc.x = fmaf(v1.d, d1.x, acc.x);
-    acc.y = fmaf(v1.d, d1.y, acc.y);
-    acc.z = fmaf(v1.d, d1.z, acc.z);
-    acc.w = fmaf(v1.d, d1.w, acc.w);
+    return PairDot{block_dot<BITS, NP>(v0, pr.a[0]), block_dot<BITS, NP>(v1, pr.a[1]), v0.d, v1.d};
+}
+// acc += s0 * d0 then s1 * d1 (the block order of the sum)
+__device__ __forceinline__ void pair_apply(float4v &acc, const PairDot &q) {
+    acc.x = fmaf(q.s0, q.d0.x, acc.x);
+    acc.y = fmaf(q.s0, q.d0.y, acc.y);
+    acc.z = fmaf(q.s0, q.d0.z, acc.z);
+    acc.w = fmaf(q.s0, q.d0.w, acc.w);
+    acc.x = fmaf(q.s1, q.d1.x, acc.x);
+    acc.y = fmaf(q.s1, q.d1.y, acc.y);
+    acc.z = fmaf(q.s1, q.d1.z, acc.z);
+    acc.w = fmaf(q.s1, q.d1.w, acc.w);
 }
 
 // Multiply-accumulate a staged chunk of cb blocks (cb a multiple of 4) into
 // acc: two operand sets, the reads of one pair in flight while the other
-// pair computes.  A operands: ab points at this lane's first block, a_stride
-// bytes between blocks, part_off bytes between the NP parts.
+// pair computes, and each pair's scaled products added one pair later, after
+// the next pair's MFMAs have issued (the blocks are still summed in order).
+// A operands: ab points at this lane's first block, a_stride bytes between
+// blocks, part_off bytes between the NP parts.
 template <int BITS, int NP>
 __device__ __forceinline__ void chunk_mma(float4v &acc, const uint8_t *buf, int rs, int cb, int n, int g,
                                           const uint8_t *ab, int a_stride, int part_off) {
@@ -237,12 +244,21 @@ __device__ __forceinline__ void chunk_mma(float4v &acc, const uint8_t *buf, int 
     const int np = cb >> 1;
     Pair<BITS, NP> pa, pb;
     pa.load(buf, ro, 0, g, ab, a_stride, part_off);
-    for (int p = 0; p < np; p += 2) {
-        pb.load(buf, ro, p + 1, g, ab, a_stride, part_off);
-        pair_mma<BITS, NP>(acc, pa, g);
+    pb.load(buf, ro, 1, g, ab, a_stride, part_off);
+    PairDot qa = pair_dot<BITS, NP>(pa, g);                        // pair 0
+    pa.load(buf, ro, 2 < np ? 2 : 0, g, ab, a_stride, part_off);  // (np = 2: unused re-read)
+    PairDot qb = pair_dot<BITS, NP>(pb, g);                        // pair 1
+    pair_apply(acc, qa);
+    pb.load(buf, ro, 3 < np ? 3 : 0, g, ab, a_stride, part_off);
+    for (int p = 2; p < np; p += 2) {
+        qa = pair_dot<BITS, NP>(pa, g);  // pair p
+        pair_apply(acc, qb);             // pair p - 1
         pa.load(buf, ro, p + 2 < np ? p + 2 : 0, g, ab, a_stride, part_off);  // (last round: unused re-read)
-        pair_mma<BITS, NP>(acc, pb, g);
+        qb = pair_dot<BITS, NP>(pb, g);  // pair p + 1
+        pair_apply(acc, qa);             // pair p
+        pb.load(buf, ro, p + 3 < np ? p + 3 : 0, g, ab, a_stride, part_off);
     }
+    pair_apply(acc, qb);  // pair np - 1
 }
 
 // ---------------------------------------------------------------------------
