@@ -15,25 +15,29 @@
 //     wave reductions on DPP).  Grouping is a counting sort in LDS.  The
 //     activations are stored in LDS as fp16 in each format's k order with a
 //     per-token power-of-two scale (exact), so any bf16/fp32 range fits fp16.
-//  B. gate/up units: (expert, 16 output rows, gate or up, one K chunk of up
-//     to 32 quant blocks), a few KB each, spread over every wave of the grid.
-//     A wave streams its unit's quantized rows from HBM with 16-byte loads
-//     (the next unit's chunk in flight while the current one computes),
-//     passes them through a wave-private LDS buffer into the MFMA lane
-//     layout, unpacks exact fp16 codes and runs v_mfma_f32_16x16x32_f16 with
-//     the expert's (<= 16) rows as the M dimension: every weight byte is read
-//     once per window for all rows that share the expert (the read-once-per-
-//     window rule of Strata "Several requests at once", opening section).  The
-//     fp16 block scale multiplies each block's fp32 partial.  A unit publishes
-//     its fp32 partial sums and counts itself done for its expert.
-//  C. down tiles: (expert, 128 output rows) per workgroup.  The tile prefetches
-//     its weights, waits for its expert's units, sums the partials in a fixed
-//     order, applies SwiGLU in fp32 and stages h in LDS as fp16 hi + lo (about
-//     22 bits) with a per-token power-of-two scale, streams the down rows and
-//     writes w * o per (token, slot) pair.  The workgroup that completes the
-//     last expert of a 128-row slice sums that slice in the fixed slot order
-//     into y (deterministic; no floating-point atomics).
-//
+//  B. gate/up tasks.  A unit is (expert, 16 feature rows, gate or up, one K
+//     chunk of up to 32 quant blocks), one wave's work; a task is the units
+//     that complete whole 16-feature groups, one workgroup's.  A wave streams
+//     its unit's quantized rows from HBM with 16-byte loads (the next unit's
+//     chunk in flight while the current one computes), passes them through a
+//     wave-private LDS buffer into the MFMA lane layout, unpacks exact fp16
+//     codes and runs v_mfma_f32_16x16x32_f16 with the expert's (<= 16) rows
+//     as the M dimension: every weight byte is read once per window for all
+//     rows that share the expert (the read-once-per-window rule of Strata
+//     "Several requests at once", opening section).  The fp16 block scale
+//     multiplies each block's fp32 partial.  The workgroup sums its units'
+//     partials in LDS in a fixed order, applies SwiGLU in fp32, writes h as
+//     tagged words and counts the task done for its expert.
+//  C. down tiles (expert, 128 output rows), then combine items, continuing the
+//     same round robin.  A tile's first weight chunk streams in during the
+//     previous work item; the tile waits for its expert's tasks, stages h in
+//     LDS as fp16 hi + lo (about 22 bits) with a per-token power-of-two
+//     scale, streams the down rows and writes w * o per (token, slot) pair.
+//     A combine item is 16 rows of one 128-row slice of y for every token:
+//     it waits for the slice's count of finished experts and sums each
+//     output in the fixed slot order (deterministic; no floating-point
+//     atomics).
+
 // Data crossing workgroups (partials, pair rows) uses device-coherent accesses
 // and per-wave store completion instead of agent-scope fences, which on this
 // chip would write back or invalidate a whole XCD's L2.
