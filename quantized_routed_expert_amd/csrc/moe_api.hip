@@ -296,7 +296,7 @@ bool decode_fits(int T, int E, int k, int H, int F, int Fs, int bits, int x_dtyp
 }
 
 // ---- column-split decode launch (windows of one to four rows, T*k <= 64) ----
-int split_xps(int bits) { return bits == 4 ? 36 : 84; }  // digit dwords per pair slot in LDS
+int split_xps(int /*bits*/) { return 36; }  // digit dwords per pair slot in LDS (both formats)
 
 int split_lds_layout(SplitParams &P) {
     const int bb = P.bits == 4 ? 18 : 14, xps = split_xps(P.bits);

@@ -10,9 +10,9 @@
 //    largest |value| lies in [2^13, 2^14), rounded to integers (15 bits; the
 //    relative rounding error is below 2^-14 of the row's largest value), and
 //    cut into four signed radix-16 digits;
-//  - 4-bit codes become signed nibbles (code - 8) with one xor; 3-bit codes
-//    split into their two low bits and their third bit, each a nibble, with
-//    (code - 4) * a = low * a + third * 4a - 4a;
+//  - 4-bit codes become signed nibbles (code - 8) with one xor; a 3-bit code
+//    (0..7) is itself a nibble, with (code - 4) * a = code * a - 4a (the
+//    block's sum of a is staged with the digits);
 //  - a block's integer dot product is exact (it fits fp32's 24-bit
 //    significand) and is scaled by the block's fp16 scale in fp32, the same
 //    rounding point as the dequantized fp32 dot product of the pages.
@@ -67,8 +67,9 @@ extern "C" int moe_trace_split_set(void *buf) {
 // Nibble-dwords: the 32-bit words whose eight nibbles multiply eight
 // activation digits.  4-bit: the pair's 9 dwords (36 bytes) themselves;
 // nibbles of scale bytes meet zero digits.  3-bit (28 bytes, 7 dwords): the
-// low-bit fields of dwords 0, 1, 2, 4, 5 masked two ways (10 nibble-dwords)
-// and each block's third-bit word spread four ways (8 nibble-dwords).
+// whole codes, 8 per nibble-dword (8 nibble-dwords): per block, each of its
+// two low-part dwords masked two ways (fields 0 and 2 of a byte, or 1 and 3)
+// with the matching third bits spread in.
 // ---------------------------------------------------------------------------
 template <int BITS>
 struct SFmt;
@@ -86,9 +87,9 @@ struct SFmt<3> {
     static constexpr int bb = 14;
     static constexpr int pb = 28;
     static constexpr int pw = 7;
-    static constexpr int nnd = 18;
-    static constexpr int xpd = 80;  // [low fields 10][digit 4], then [third bits 8][digit 5]
-    static constexpr int xps = 84;  // their stride in LDS (84 mod 64 banks spreads 8 pieces' reads)
+    static constexpr int nnd = 8;
+    static constexpr int xpd = 32;  // digit dwords per pair: [digit 4][nibble-dword 8]
+    static constexpr int xps = 36;  // their stride in LDS (36 mod 64 banks spreads 8 pieces' reads)
 };
 
 // k (0..63 within the pair) that nibble i of nibble-dword nd multiplies, or -1.
@@ -102,29 +103,12 @@ __device__ __forceinline__ int nibble_k(int nd, int i) {
         if (beta >= 20 && beta <= 35) return 32 + beta - 20 + 16 * h;
         return -1;  // a scale byte
     } else {
-        if (nd < 10) {
-            // low parts: byte 2+j of a block holds the two low bits of codes
-            // j, j+8, j+16, j+24 (fields 0..3); mask a keeps fields 0 and 2 as
-            // the low and high nibble of the byte, mask b (after >> 2) fields 1, 3
-            const int w = nd >> 1;
-            const int beta = 4 * w + (w >= 3 ? 4 : 0) + (i >> 1);  // dwords 0, 1, 2, 4, 5
-            int B, j;
-            if (beta >= 2 && beta <= 9) {
-                B = 0;
-                j = beta - 2;
-            } else if (beta >= 16 && beta <= 23) {
-                B = 1;
-                j = beta - 16;
-            } else {
-                return -1;  // scale or third-bit bytes
-            }
-            const int f = (nd & 1) ? (h ? 3 : 1) : (h ? 2 : 0);
-            return 32 * B + j + 8 * f;
-        } else {
-            // third bits: word bit q is code q's; spread s takes bits 4m + s
-            const int u = nd - 10, B = u >> 2, s = u & 3;
-            return 32 * B + 4 * i + s;
-        }
+        // nibble-dword 4B + m of block B: byte j of the block's low-part dword
+        // m >> 1 (bytes 4 (m >> 1) + j) holds the low bits of codes
+        // 4 (m >> 1) + j + 8 f in its fields f = 0..3; mask m & 1 = 0 keeps
+        // fields 0 and 2 (low and high nibble), 1 fields 1 and 3
+        const int B = nd >> 2, m = nd & 3;
+        return 32 * B + 8 * (m & 1) + 4 * (m >> 1) + (i >> 1) + 16 * (i & 1);
     }
 }
 
@@ -136,31 +120,17 @@ __device__ __forceinline__ int nibble_k(int nd, int i) {
 // value (v = 0) gives zero digits.
 template <int BITS>
 __device__ __forceinline__ void build_digits(const int16_t *src, int kmask, int nd, uint32_t *dst) {
-    const bool third = BITS == 3 && nd >= 10;
-    uint32_t D[5] = {0u, 0u, 0u, 0u, 0u};
+    uint32_t D[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int kk = nibble_k<BITS>(nd, i);
         int v = kk >= 0 ? (int)src[kk & kmask] : 0;
-        // |v| <= 2^14, |4v| <= 2^16: four or five digits
-        const uint32_t u = third ? (uint32_t)(4 * v + 0x88888) : (uint32_t)(v + 0x8888);
+        const uint32_t u = (uint32_t)(v + 0x8888);  // |v| <= 2^14: four digits
 #pragma unroll
-        for (int j = 0; j < 5; ++j) D[j] |= ((u >> (4 * j)) & 15u) << (4 * i);
+        for (int j = 0; j < 4; ++j) D[j] |= ((u >> (4 * j)) & 15u) << (4 * i);
     }
 #pragma unroll
-    for (int j = 0; j < 5; ++j) D[j] ^= 0x88888888u;
-    if constexpr (BITS == 4) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) dst[j * 9 + nd] = D[j];
-    } else {
-        if (!third) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) dst[nd * 4 + j] = D[j];
-        } else {
-#pragma unroll
-            for (int j = 0; j < 5; ++j) dst[40 + (nd - 10) * 5 + j] = D[j];
-        }
-    }
+    for (int j = 0; j < 4; ++j) dst[j * SFmt<BITS>::nnd + nd] = D[j] ^ 0x88888888u;
 }
 
 __device__ __forceinline__ int sdot8(uint32_t a, uint32_t b, int c) {
@@ -209,40 +179,38 @@ struct SPair<4> {
 
 template <>
 struct SPair<3> {
-    uint32_t N[10], M[8];
+    uint32_t C[8];  // the 64 codes, 8 per nibble-dword (order of nibble_k<3>)
     float d0, d1;
     __device__ __forceinline__ void set(const uint32_t (&w)[7]) {
-        const uint32_t lw[5] = {w[0], w[1], w[2], w[4], w[5]};
+        // block 0: bytes 0..13 (low parts 2..9, third bits 10..13); block 1: 14..27
+        const uint32_t L[2][2] = {{__builtin_amdgcn_alignbyte(w[1], w[0], 2u), __builtin_amdgcn_alignbyte(w[2], w[1], 2u)},
+                                  {w[4], w[5]}};
+        const uint32_t Q[2] = {__builtin_amdgcn_alignbyte(w[3], w[2], 2u), w[6]};
+        // bit q of t -> bit 2 of byte q: t * (4 + 2^9 + 2^16 + 2^23), the other
+        // partial products land on bits the mask drops (all distinct: no carries)
+        auto spread = [](uint32_t t) { return __umul24(t, 0x810204u) & 0x04040404u; };
 #pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            N[2 * i] = lw[i] & 0x33333333u;
-            N[2 * i + 1] = (lw[i] >> 2) & 0x33333333u;
-        }
-        const uint32_t h0 = __builtin_amdgcn_alignbyte(w[3], w[2], 2u);  // block 0 bytes 10..13
+        for (int B = 0; B < 2; ++B)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            M[s] = (h0 >> s) & 0x11111111u;
-            M[4 + s] = (w[6] >> s) & 0x11111111u;
-        }
+            for (int m = 0; m < 4; ++m) {
+                const int c0 = 8 * (m & 1) + 4 * (m >> 1);  // code of byte 0's low nibble
+                const uint32_t n = ((m & 1) ? L[B][m >> 1] >> 2 : L[B][m >> 1]) & 0x33333333u;
+                const uint32_t tl = spread((Q[B] >> c0) & 15u), th = spread((Q[B] >> (c0 + 16)) & 15u);
+                C[4 * B + m] = n | tl | (th << 4);
+            }
         d0 = half_bits_to_float(w[0] & 0xFFFFu);
         d1 = half_bits_to_float(w[3] >> 16);
     }
     // S0, S1: the row's sums of the activations over block 0 / 1 (the -4a term)
     __device__ __forceinline__ void blocks(const uint32_t *xd, int S0, int S1, int &A0, int &A1) const {
-        int a0[5], a1[5];
+        int a0[4], a1[4];
 #pragma unroll
-        for (int j = 0; j < 5; ++j) {
+        for (int j = 0; j < 4; ++j) {
             int s0 = j == 0 ? -4 * S0 : 0, s1 = j == 0 ? -4 * S1 : 0;
-            if (j < 4) {
 #pragma unroll
-                for (int nd = 0; nd < 6; ++nd) s0 = sdot8(N[nd], xd[nd * 4 + j], s0);
+            for (int q = 0; q < 4; ++q) s0 = sdot8(C[q], xd[j * 8 + q], s0);
 #pragma unroll
-                for (int nd = 6; nd < 10; ++nd) s1 = sdot8(N[nd], xd[nd * 4 + j], s1);
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) s0 = sdot8(M[u], xd[40 + u * 5 + j], s0);
-#pragma unroll
-            for (int u = 4; u < 8; ++u) s1 = sdot8(M[u], xd[40 + u * 5 + j], s1);
+            for (int q = 4; q < 8; ++q) s1 = sdot8(C[q], xd[j * 8 + q], s1);
             a0[j] = s0;
             a1[j] = s1;
         }

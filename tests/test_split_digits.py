@@ -3,8 +3,9 @@
 The launch (csrc/moe_split.hip) multiplies weight bytes, read as 32-bit words
 of eight nibbles, by words of signed radix-16 activation digits with
 v_dot8_i32_i4.  This test models those layouts in Python -- which k each
-nibble of each word multiplies, how the digits are cut, how 3-bit codes are
-split into their low bits and their third bit -- and checks that the sums
+nibble of each word multiplies, how the digits are cut, how a 3-bit code is
+assembled as one nibble from its low bits and its third bit (with the -4a
+term taken from the block's sum of a) -- and checks that the sums
 are the exact integer dot products sum (code - bias) * a of each block, for
 both formats, for a pair of blocks of one row (gate/up) and for the same
 block of two rows (down), including the extreme activations +-2^14.  A wrong
@@ -24,45 +25,27 @@ def nibble_k(bits, nd, i):
         if 20 <= beta <= 35:
             return 32 + beta - 20 + 16 * h
         return -1
-    if nd < 10:
-        w = nd >> 1
-        beta = 4 * w + (4 if w >= 3 else 0) + (i >> 1)
-        if 2 <= beta <= 9:
-            B, j = 0, beta - 2
-        elif 16 <= beta <= 23:
-            B, j = 1, beta - 16
-        else:
-            return -1
-        f = (3 if h else 1) if (nd & 1) else (2 if h else 0)
-        return 32 * B + j + 8 * f
-    u = nd - 10
-    return 32 * (u >> 2) + 4 * i + (u & 3)
+    # 3-bit: nibble-dword 4B + m holds codes 8 (m & 1) + 4 (m >> 1) + j (+16 in
+    # the high nibble) of block B, byte j
+    B, m = nd >> 2, nd & 3
+    return 32 * B + 8 * (m & 1) + 4 * (m >> 1) + (i >> 1) + 16 * h
 
 
 def digit_words(bits, a, kmask):
-    """The digit words of one pair: 4-bit [digit][word]; 3-bit [low word][digit] then [third word][digit]."""
-    nnd = 9 if bits == 4 else 18
-    out = [0] * (36 if bits == 4 else 80)
+    """The digit words of one pair, [digit][word]."""
+    nnd = 9 if bits == 4 else 8
+    out = [0] * (4 * nnd)
     for nd in range(nnd):
-        third = bits == 3 and nd >= 10
-        D = [0] * 5
+        D = [0] * 4
         for i in range(8):
             kk = nibble_k(bits, nd, i)
             v = int(a[kk & kmask]) if kk >= 0 else 0
-            u = 4 * v + 0x88888 if third else v + 0x8888
-            assert 0 <= u < (1 << 20)
-            for j in range(5):
+            u = v + 0x8888
+            assert 0 <= u < (1 << 16)
+            for j in range(4):
                 D[j] |= ((u >> (4 * j)) & 15) << (4 * i)
-        D = [d ^ 0x88888888 for d in D]
-        if bits == 4:
-            for j in range(4):
-                out[j * 9 + nd] = D[j]
-        elif not third:
-            for j in range(4):
-                out[nd * 4 + j] = D[j]
-        else:
-            for j in range(5):
-                out[40 + (nd - 10) * 5 + j] = D[j]
+        for j in range(4):
+            out[j * nnd + nd] = D[j] ^ 0x88888888
     return out
 
 
@@ -95,23 +78,22 @@ def block_sums(bits, pair_bytes, xd, S0, S1):
             for q in range(5, 9):
                 a1[j] = sdot8(wx[q], xd[j * 9 + q], a1[j])
         return radix16(a0), radix16(a1)
-    lw = [w[0], w[1], w[2], w[4], w[5]]
-    N = []
-    for x in lw:
-        N += [x & 0x33333333, (x >> 2) & 0x33333333]
-    h0 = (((w[3] << 32) | w[2]) >> 16) & 0xFFFFFFFF
-    M = [(h0 >> s) & 0x11111111 for s in range(4)] + [(w[6] >> s) & 0x11111111 for s in range(4)]
-    a0, a1 = [-4 * S0, 0, 0, 0, 0], [-4 * S1, 0, 0, 0, 0]
-    for j in range(5):
-        if j < 4:
-            for nd in range(6):
-                a0[j] = sdot8(N[nd], xd[nd * 4 + j], a0[j])
-            for nd in range(6, 10):
-                a1[j] = sdot8(N[nd], xd[nd * 4 + j], a1[j])
-        for u in range(4):
-            a0[j] = sdot8(M[u], xd[40 + u * 5 + j], a0[j])
-        for u in range(4, 8):
-            a1[j] = sdot8(M[u], xd[40 + u * 5 + j], a1[j])
+    align = lambda hi, lo: (((hi << 32) | lo) >> 16) & 0xFFFFFFFF
+    L = [[align(w[1], w[0]), align(w[2], w[1])], [w[4], w[5]]]
+    Q = [align(w[3], w[2]), w[6]]
+    spread = lambda t: ((t & 0xFFFFFF) * 0x810204) & 0x04040404
+    C = []
+    for B in range(2):
+        for m in range(4):
+            c0 = 8 * (m & 1) + 4 * (m >> 1)
+            n = ((L[B][m >> 1] >> 2) if m & 1 else L[B][m >> 1]) & 0x33333333
+            C.append(n | spread((Q[B] >> c0) & 15) | (spread((Q[B] >> (c0 + 16)) & 15) << 4))
+    a0, a1 = [-4 * S0, 0, 0, 0], [-4 * S1, 0, 0, 0]
+    for j in range(4):
+        for q in range(4):
+            a0[j] = sdot8(C[q], xd[j * 8 + q], a0[j])
+        for q in range(4, 8):
+            a1[j] = sdot8(C[q], xd[j * 8 + q], a1[j])
     return radix16(a0), radix16(a1)
 
 
