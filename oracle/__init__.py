@@ -22,10 +22,13 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
-def build(out_path: str | None = None, extra_flags: list[str] | None = None) -> str:
-    """Compile oracle.c with gcc -O2 into a shared library; returns its path."""
+def build(out_path: str | None = None, extra_flags: list[str] | None = None, openmp: bool = True) -> str:
+    """Compile oracle.c with gcc -O2 (and OpenMP over rows unless openmp is
+    False) into a shared library; returns its path."""
     out = out_path or _LIB_PATH
     cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", out, _SRC, "-lm"]
+    if openmp:
+        cmd[1:1] = ["-fopenmp"]
     if extra_flags:
         cmd[1:1] = extra_flags
     subprocess.run(cmd, check=True)
@@ -37,12 +40,16 @@ def _bind(lib):
     f64p = ctypes.POINTER(ctypes.c_double)
     u8p = ctypes.c_void_p
     lib.orc_version.restype = ctypes.c_int
+    lib.orc_set_threads.restype = ctypes.c_int
+    lib.orc_set_threads.argtypes = [ctypes.c_int]
     lib.orc_half_to_double.restype = ctypes.c_double
     lib.orc_half_to_double.argtypes = [ctypes.c_uint16]
     lib.orc_bf16_to_double.restype = ctypes.c_double
     lib.orc_bf16_to_double.argtypes = [ctypes.c_uint16]
     lib.orc_block_bytes.restype = ctypes.c_int
     lib.orc_block_bytes.argtypes = [ctypes.c_int]
+    lib.orc_format_bits.restype = ctypes.c_int
+    lib.orc_format_bits.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.orc_expert_bytes.restype = ctypes.c_int64
     lib.orc_expert_bytes.argtypes = [ctypes.c_int] * 3
     lib.orc_dequant_block.restype = None
@@ -97,6 +104,11 @@ class Oracle:
     def __init__(self, lib=None):
         self.lib = lib or load()
 
+    def set_threads(self, n: int = 0) -> int:
+        """Threads for the loops over rows (n <= 0 keeps the current count);
+        returns the count in use (1 for a serial build)."""
+        return self.lib.orc_set_threads(int(n))
+
     # -- scalar formats ---------------------------------------------------
     def half_to_double(self, h: int) -> float:
         return self.lib.orc_half_to_double(int(h))
@@ -108,8 +120,12 @@ class Oracle:
     def block_bytes(self, bits: int) -> int:
         return self.lib.orc_block_bytes(bits)
 
-    def expert_bytes(self, bits: int, hidden: int, ffn: int) -> int:
-        return self.lib.orc_expert_bytes(bits, hidden, ffn)
+    def format_bits(self, fmt: int, down: bool) -> int:
+        """Bit width of the gate/up (down=False) or down projection of a format code."""
+        return self.lib.orc_format_bits(fmt, 1 if down else 0)
+
+    def expert_bytes(self, fmt: int, hidden: int, ffn: int) -> int:
+        return self.lib.orc_expert_bytes(fmt, hidden, ffn)
 
     def dequant_block(self, bits: int, blk: bytes | np.ndarray) -> np.ndarray:
         b = np.ascontiguousarray(np.frombuffer(bytes(blk), dtype=np.uint8))
@@ -126,14 +142,15 @@ class Oracle:
         assert rc == 0
         return out
 
-    def dequant_expert(self, bits: int, blob: np.ndarray, hidden: int, ffn: int):
-        """(gate [F,H], up [F,H], down [H,F]) of one expert blob."""
+    def dequant_expert(self, fmt: int, blob: np.ndarray, hidden: int, ffn: int):
+        """(gate [F,H], up [F,H], down [H,F]) of one expert blob of format fmt."""
         blob = np.ascontiguousarray(blob, dtype=np.uint8)
-        mb = hidden * (ffn // 32) * self.block_bytes(bits)
-        assert blob.size == 3 * mb
-        g = self.dequant_matrix(bits, blob[:mb], ffn, hidden)
-        u = self.dequant_matrix(bits, blob[mb:2 * mb], ffn, hidden)
-        d = self.dequant_matrix(bits, blob[2 * mb:], hidden, ffn)
+        bg, bd = self.format_bits(fmt, False), self.format_bits(fmt, True)
+        mb = hidden * (ffn // 32) * self.block_bytes(bg)
+        assert blob.size == self.expert_bytes(fmt, hidden, ffn)
+        g = self.dequant_matrix(bg, blob[:mb], ffn, hidden)
+        u = self.dequant_matrix(bg, blob[mb:2 * mb], ffn, hidden)
+        d = self.dequant_matrix(bd, blob[2 * mb:], hidden, ffn)
         return g, u, d
 
     # -- router and grouping ------------------------------------------------
@@ -161,7 +178,7 @@ class Oracle:
         return offsets, pairs[:T * k], active
 
     # -- FFN and layer --------------------------------------------------------
-    def expert_ffn(self, x: np.ndarray, x_dtype: int, k: int, bits: int, E: int, hidden: int,
+    def expert_ffn(self, x: np.ndarray, x_dtype: int, k: int, fmt: int, E: int, hidden: int,
                    ffn: int, blobs: np.ndarray, offsets, pairs, active, pair_w=None):
         x = np.ascontiguousarray(x)
         T = x.shape[0]
@@ -173,7 +190,7 @@ class Oracle:
         pw = None
         if pair_w is not None:
             pw = np.ascontiguousarray(pair_w, dtype=np.float64).reshape(-1)
-        rc = self.lib.orc_expert_ffn(_ptr(x), x_dtype, T, k, bits, E, hidden, ffn, _ptr(blobs),
+        rc = self.lib.orc_expert_ffn(_ptr(x), x_dtype, T, k, fmt, E, hidden, ffn, _ptr(blobs),
                                      _ptr(offsets, ctypes.c_int32), _ptr(pairs, ctypes.c_int32),
                                      _ptr(active, ctypes.c_int32),
                                      _ptr(pw) if pw is not None else None,
@@ -182,16 +199,18 @@ class Oracle:
             raise ValueError(f"orc_expert_ffn rc={rc}")
         return out
 
-    def layer_forward(self, x: np.ndarray, x_dtype: int, logits: np.ndarray, k: int, bits: int,
+    def layer_forward(self, x: np.ndarray, x_dtype: int, logits: np.ndarray, k: int, fmt: int,
                       ffn: int, routed: np.ndarray, shared: np.ndarray | None = None,
-                      s_bits: int | None = None, s_ffn: int | None = None, rows=None):
-        """Returns (y [n_rows, H] float64, idx [T,k] int32, w [T,k] float64)."""
+                      s_fmt: int | None = None, s_ffn: int | None = None, rows=None):
+        """fmt / s_fmt: format codes of the routed / shared experts (a bit
+        width 3 or 4, or gate/up bits | down bits << 8).
+        Returns (y [n_rows, H] float64, idx [T,k] int32, w [T,k] float64)."""
         x = np.ascontiguousarray(x)
         logits = np.ascontiguousarray(logits, dtype=np.float32)
         T, E = logits.shape
         H = x.shape[1]
         routed = np.ascontiguousarray(routed, dtype=np.uint8)
-        s_bits = bits if s_bits is None else s_bits
+        s_fmt = fmt if s_fmt is None else s_fmt
         s_ffn = ffn if s_ffn is None else s_ffn
         sh = None if shared is None else np.ascontiguousarray(shared, dtype=np.uint8)
         rws = None
@@ -202,8 +221,8 @@ class Oracle:
         y = np.zeros((nr, H), dtype=np.float64)
         idx = np.zeros((T, k), dtype=np.int32)
         w = np.zeros((T, k), dtype=np.float64)
-        rc = self.lib.orc_layer_forward(_ptr(x), x_dtype, _ptr(logits), T, E, k, H, bits, ffn,
-                                        _ptr(routed), s_bits, s_ffn,
+        rc = self.lib.orc_layer_forward(_ptr(x), x_dtype, _ptr(logits), T, E, k, H, fmt, ffn,
+                                        _ptr(routed), s_fmt, s_ffn,
                                         _ptr(sh) if sh is not None else None, nr,
                                         _ptr(rws) if rws is not None else None,
                                         _ptr(y, ctypes.c_double), _ptr(idx, ctypes.c_int32),

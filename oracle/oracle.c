@@ -41,12 +41,32 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORC_OK 0
 #define ORC_ERR_ARG (-1)
 #define ORC_ERR_MEM (-2)
 
 int orc_version(void) { return 1; }
+
+/*
+ * Threads.  Built with OpenMP, the loops over rows (tokens, or the pairs of
+ * one expert) and over matrix rows in the dequantization run in parallel.
+ * Every row's arithmetic is the same sequence of operations as in the serial
+ * build (each row is computed start to end by one thread), so the results
+ * are bitwise those of the serial build whatever the thread count.
+ */
+int orc_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
 
 /* ------------------------------------------------------------------ */
 /* Scalar formats                                                       */
@@ -86,11 +106,27 @@ int orc_block_bytes(int bits) {
     return -1;
 }
 
-int64_t orc_expert_bytes(int bits, int hidden, int ffn) {
-    int bb = orc_block_bytes(bits);
-    if (bb < 0 || hidden <= 0 || ffn <= 0 || hidden % 32 || ffn % 32) return -1;
+/*
+ * A weight format: the bit width of the gate and up projections in bits
+ * 0..7, that of the down projection in bits 8..15, 0 there meaning the same
+ * width as gate/up (so a plain 3 or 4 is a uniform format).  The thread's §三
+ * decode table pairs each gate/up format with a down format of its own (a
+ * 2- or 3-bit gate/up with a 4-bit down); here the same per-projection choice
+ * is made between the 3- and 4-bit blocks above.  -1 for anything else.
+ */
+int orc_format_bits(int fmt, int down) {
+    int gu = fmt & 0xFF, dn = (fmt >> 8) & 0xFF;
+    if (fmt < 0 || (fmt >> 16) != 0) return -1;
+    if (dn == 0) dn = gu;
+    if (orc_block_bytes(gu) < 0 || orc_block_bytes(dn) < 0) return -1;
+    return down ? dn : gu;
+}
+
+int64_t orc_expert_bytes(int fmt, int hidden, int ffn) {
+    int bg = orc_format_bits(fmt, 0), bd = orc_format_bits(fmt, 1);
+    if (bg < 0 || bd < 0 || hidden <= 0 || ffn <= 0 || hidden % 32 || ffn % 32) return -1;
     /* gate [ffn][hidden] + up [ffn][hidden] + down [hidden][ffn] */
-    return (int64_t)3 * hidden * (ffn / 32) * bb;
+    return (int64_t)hidden * (ffn / 32) * (2 * orc_block_bytes(bg) + orc_block_bytes(bd));
 }
 
 /*
@@ -128,6 +164,7 @@ int orc_dequant_matrix(int bits, const uint8_t *m, int rows, int cols, double *o
     int bb = orc_block_bytes(bits);
     int r, b;
     if (bb < 0 || cols % 32) return ORC_ERR_ARG;
+#pragma omp parallel for private(b) schedule(static)
     for (r = 0; r < rows; ++r)
         for (b = 0; b < cols / 32; ++b)
             orc_dequant_block(bits, m + ((int64_t)r * (cols / 32) + b) * bb,
@@ -221,17 +258,18 @@ typedef struct {
     int H, F;
 } orc_expert;
 
-static int orc_load_expert(int bits, const uint8_t *blob, int H, int F, orc_expert *ex) {
-    int64_t mat = (int64_t)H * (F / 32) * orc_block_bytes(bits); /* bytes per matrix */
+static int orc_load_expert(int fmt, const uint8_t *blob, int H, int F, orc_expert *ex) {
+    int bg = orc_format_bits(fmt, 0), bd = orc_format_bits(fmt, 1);
+    int64_t mat = (int64_t)H * (F / 32) * orc_block_bytes(bg); /* bytes of the gate (and the up) matrix */
     ex->H = H;
     ex->F = F;
     ex->gate = (double *)malloc(sizeof(double) * (size_t)H * F);
     ex->up = (double *)malloc(sizeof(double) * (size_t)H * F);
     ex->down = (double *)malloc(sizeof(double) * (size_t)H * F);
     if (!ex->gate || !ex->up || !ex->down) return ORC_ERR_MEM;
-    orc_dequant_matrix(bits, blob, F, H, ex->gate);
-    orc_dequant_matrix(bits, blob + mat, F, H, ex->up);
-    orc_dequant_matrix(bits, blob + 2 * mat, H, F, ex->down);
+    orc_dequant_matrix(bg, blob, F, H, ex->gate);
+    orc_dequant_matrix(bg, blob + mat, F, H, ex->up);
+    orc_dequant_matrix(bd, blob + 2 * mat, H, F, ex->down);
     return ORC_OK;
 }
 
@@ -281,39 +319,42 @@ static void orc_load_x_row(const void *x, int x_dtype, int H, int t, double *out
  * active expert e.  pair_w == NULL means weight 1.  Rows of out_pairs for
  * pairs not listed are left untouched.
  */
-int orc_expert_ffn(const void *x, int x_dtype, int T, int k, int bits, int E, int H, int F,
+int orc_expert_ffn(const void *x, int x_dtype, int T, int k, int fmt, int E, int H, int F,
                    const uint8_t *blobs, const int32_t *offsets, const int32_t *pairs,
                    const int32_t *active, const double *pair_w, double *out_pairs) {
-    int64_t eb = orc_expert_bytes(bits, H, F);
-    double *xr, *hid, *o;
+    int64_t eb = orc_expert_bytes(fmt, H, F);
     int a, rc = ORC_OK;
     if (eb < 0 || T < 0 || k <= 0 || E <= 0 || (x_dtype != 0 && x_dtype != 1)) return ORC_ERR_ARG;
-    xr = (double *)malloc(sizeof(double) * (size_t)H);
-    hid = (double *)malloc(sizeof(double) * (size_t)F);
-    o = (double *)malloc(sizeof(double) * (size_t)H);
-    if (!xr || !hid || !o) { rc = ORC_ERR_MEM; goto done; }
     for (a = 0; a < active[0]; ++a) {
         int e = active[1 + a], q, h;
         orc_expert ex;
         if (e < 0 || e >= E) { rc = ORC_ERR_ARG; goto done; }
-        if (orc_load_expert(bits, blobs + (int64_t)e * eb, H, F, &ex) != ORC_OK) {
+        if (orc_load_expert(fmt, blobs + (int64_t)e * eb, H, F, &ex) != ORC_OK) {
             orc_free_expert(&ex);
             rc = ORC_ERR_MEM;
             goto done;
         }
-        for (q = offsets[e]; q < offsets[e + 1]; ++q) {
-            int p = pairs[q];
-            double wp = pair_w ? pair_w[p] : 1.0;
-            orc_load_x_row(x, x_dtype, H, p / k, xr);
-            orc_ffn_row(&ex, xr, hid, o);
-            for (h = 0; h < H; ++h) out_pairs[(int64_t)p * H + h] = wp * o[h];
+#pragma omp parallel private(q, h)
+        {
+            double *xr_t = (double *)malloc(sizeof(double) * (size_t)H);
+            double *hid_t = (double *)malloc(sizeof(double) * (size_t)F);
+            double *o_t = (double *)malloc(sizeof(double) * (size_t)H);
+            if (!xr_t || !hid_t || !o_t) abort();
+#pragma omp for schedule(dynamic, 1)
+            for (q = offsets[e]; q < offsets[e + 1]; ++q) {
+                int p = pairs[q];
+                double wp = pair_w ? pair_w[p] : 1.0;
+                orc_load_x_row(x, x_dtype, H, p / k, xr_t);
+                orc_ffn_row(&ex, xr_t, hid_t, o_t);
+                for (h = 0; h < H; ++h) out_pairs[(int64_t)p * H + h] = wp * o_t[h];
+            }
+            free(xr_t);
+            free(hid_t);
+            free(o_t);
         }
         orc_free_expert(&ex);
     }
 done:
-    free(xr);
-    free(hid);
-    free(o);
     return rc;
 }
 
@@ -326,24 +367,21 @@ done:
  * Combine order per token: (((w_0 o_0 + w_1 o_1) + ...) + w_{k-1} o_{k-1}) + s.
  */
 int orc_layer_forward(const void *x, int x_dtype, const float *logits, int T, int E, int k,
-                      int H, int bits, int F, const uint8_t *routed, int s_bits, int s_F,
+                      int H, int fmt, int F, const uint8_t *routed, int s_fmt, int s_F,
                       const uint8_t *shared, int n_rows, const int32_t *rows, double *y,
                       int32_t *idx, double *w) {
-    int64_t eb = orc_expert_bytes(bits, H, F), n = (int64_t)T * k;
+    int64_t eb = orc_expert_bytes(fmt, H, F), n = (int64_t)T * k;
     int32_t *offsets = NULL, *pairs = NULL, *active = NULL, *row_of = NULL;
-    double *pair_o = NULL, *xr = NULL, *hid = NULL, *o = NULL;
+    double *pair_o = NULL;
     int rc = ORC_OK, nr = rows ? n_rows : T, i, a, h;
     if (eb < 0 || T < 0 || E <= 0 || k <= 0 || k > E || (x_dtype != 0 && x_dtype != 1)) return ORC_ERR_ARG;
-    if (shared && orc_expert_bytes(s_bits, H, s_F) < 0) return ORC_ERR_ARG;
+    if (shared && orc_expert_bytes(s_fmt, H, s_F) < 0) return ORC_ERR_ARG;
     offsets = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E + 1));
     pairs = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n ? n : 1));
     active = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E + 1));
     row_of = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T ? T : 1));
     pair_o = (double *)calloc((size_t)nr * k * H + 1, sizeof(double));
-    xr = (double *)malloc(sizeof(double) * (size_t)H);
-    hid = (double *)malloc(sizeof(double) * (size_t)(F > s_F ? F : s_F));
-    o = (double *)malloc(sizeof(double) * (size_t)H);
-    if (!offsets || !pairs || !active || !row_of || !pair_o || !xr || !hid || !o) { rc = ORC_ERR_MEM; goto done; }
+    if (!offsets || !pairs || !active || !row_of || !pair_o) { rc = ORC_ERR_MEM; goto done; }
 
     rc = orc_route(logits, T, E, k, idx, w);
     if (rc) goto done;
@@ -365,22 +403,34 @@ int orc_layer_forward(const void *x, int x_dtype, const float *logits, int T, in
         for (q = offsets[e]; q < offsets[e + 1]; ++q)
             if (row_of[pairs[q] / k] >= 0) need = 1;
         if (!need) continue;
-        if (orc_load_expert(bits, routed + (int64_t)e * eb, H, F, &ex) != ORC_OK) {
+        if (orc_load_expert(fmt, routed + (int64_t)e * eb, H, F, &ex) != ORC_OK) {
             orc_free_expert(&ex);
             rc = ORC_ERR_MEM;
             goto done;
         }
-        for (q = offsets[e]; q < offsets[e + 1]; ++q) {
-            int p = pairs[q], t = p / k, j = p % k;
-            if (row_of[t] < 0) continue;
-            orc_load_x_row(x, x_dtype, H, t, xr);
-            orc_ffn_row(&ex, xr, hid, o);
-            for (h = 0; h < H; ++h) pair_o[((int64_t)row_of[t] * k + j) * H + h] = o[h];
+#pragma omp parallel private(q, h)
+        {
+            double *xr_t = (double *)malloc(sizeof(double) * (size_t)H);
+            double *hid_t = (double *)malloc(sizeof(double) * (size_t)F);
+            double *o_t = (double *)malloc(sizeof(double) * (size_t)H);
+            if (!xr_t || !hid_t || !o_t) abort();
+#pragma omp for schedule(dynamic, 1)
+            for (q = offsets[e]; q < offsets[e + 1]; ++q) {
+                int p = pairs[q], t = p / k, j = p % k;
+                if (row_of[t] < 0) continue;
+                orc_load_x_row(x, x_dtype, H, t, xr_t);
+                orc_ffn_row(&ex, xr_t, hid_t, o_t);
+                for (h = 0; h < H; ++h) pair_o[((int64_t)row_of[t] * k + j) * H + h] = o_t[h];
+            }
+            free(xr_t);
+            free(hid_t);
+            free(o_t);
         }
         orc_free_expert(&ex);
     }
 
     /* combine in slot order, then the shared expert */
+#pragma omp parallel for private(h) schedule(static)
     for (i = 0; i < nr; ++i) {
         int t = rows ? rows[i] : i, j;
         for (h = 0; h < H; ++h) {
@@ -391,16 +441,27 @@ int orc_layer_forward(const void *x, int x_dtype, const float *logits, int T, in
     }
     if (shared) {
         orc_expert sx;
-        if (orc_load_expert(s_bits, shared, H, s_F, &sx) != ORC_OK) {
+        if (orc_load_expert(s_fmt, shared, H, s_F, &sx) != ORC_OK) {
             orc_free_expert(&sx);
             rc = ORC_ERR_MEM;
             goto done;
         }
-        for (i = 0; i < nr; ++i) {
-            int t = rows ? rows[i] : i;
-            orc_load_x_row(x, x_dtype, H, t, xr);
-            orc_ffn_row(&sx, xr, hid, o);
-            for (h = 0; h < H; ++h) y[(int64_t)i * H + h] += o[h];
+#pragma omp parallel private(i, h)
+        {
+            double *xr_t = (double *)malloc(sizeof(double) * (size_t)H);
+            double *hid_t = (double *)malloc(sizeof(double) * (size_t)s_F);
+            double *o_t = (double *)malloc(sizeof(double) * (size_t)H);
+            if (!xr_t || !hid_t || !o_t) abort();
+#pragma omp for schedule(dynamic, 1)
+            for (i = 0; i < nr; ++i) {
+                int t = rows ? rows[i] : i;
+                orc_load_x_row(x, x_dtype, H, t, xr_t);
+                orc_ffn_row(&sx, xr_t, hid_t, o_t);
+                for (h = 0; h < H; ++h) y[(int64_t)i * H + h] += o_t[h];
+            }
+            free(xr_t);
+            free(hid_t);
+            free(o_t);
         }
         orc_free_expert(&sx);
     }
@@ -410,8 +471,5 @@ done:
     free(active);
     free(row_of);
     free(pair_o);
-    free(xr);
-    free(hid);
-    free(o);
     return rc;
 }

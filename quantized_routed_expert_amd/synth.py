@@ -18,6 +18,7 @@ the HIP kernels):
     little-endian word whose bit i is code i's third bit; weight = d*(code-4).
   * A matrix [rows][cols] is stored row by row, cols/32 blocks per row; an
     expert is gate [F][H] | up [F][H] | down [H][F]; experts back to back.
+    Gate and up share one bit width, down may have another (``down_bits``).
 
 The 4-bit block of 32 values in 18 bytes is the one the forum thread "把
 Strata 搬上 SGLang 引擎 的嘗試" names in §四; the nibble order and the whole
@@ -50,10 +51,20 @@ class Config:
     logits: tuple       # ("normal", sigma) or ("zipf", s)
     layers: int
     weight_cid: int = 0  # seed namespace of the weights (0 = cid)
+    down_bits: int = 0   # bit width of the down projection (0 = bits, the gate/up width)
 
     @property
     def wcid(self) -> int:
         return self.weight_cid or self.cid
+
+    @property
+    def dbits(self) -> int:
+        return self.down_bits or self.bits
+
+    @property
+    def fmt(self) -> int:
+        """Format code: gate/up bits in the low byte, down bits in the next (0 = the same)."""
+        return format_code(self.bits, self.down_bits)
 
     @property
     def block_bytes(self) -> int:
@@ -61,11 +72,11 @@ class Config:
 
     @property
     def expert_bytes(self) -> int:
-        return expert_bytes(self.bits, self.hidden, self.ffn)
+        return expert_bytes(self.bits, self.hidden, self.ffn, self.down_bits)
 
     @property
     def shared_bytes(self) -> int:
-        return expert_bytes(self.bits, self.hidden, self.shared_ffn) if self.shared_ffn else 0
+        return expert_bytes(self.bits, self.hidden, self.shared_ffn, self.down_bits) if self.shared_ffn else 0
 
 
 CONFIGS = {
@@ -87,8 +98,12 @@ def block_bytes(bits: int) -> int:
     return {4: 18, 3: 14}[bits]
 
 
-def expert_bytes(bits: int, hidden: int, ffn: int) -> int:
-    return 3 * hidden * (ffn // 32) * block_bytes(bits)
+def format_code(bits: int, down_bits: int = 0) -> int:
+    return bits | ((down_bits if down_bits and down_bits != bits else 0) << 8)
+
+
+def expert_bytes(bits: int, hidden: int, ffn: int, down_bits: int = 0) -> int:
+    return hidden * (ffn // 32) * (2 * block_bytes(bits) + block_bytes(down_bits or bits))
 
 
 def rng(*key: int) -> np.random.Generator:
@@ -158,12 +173,87 @@ def quantize(w: np.ndarray, bits: int) -> np.ndarray:
     return pack_codes(codes, d16, bits)
 
 
-def expert_blob(rg: np.random.Generator, hidden: int, ffn: int, bits: int, std: float = 0.02) -> np.ndarray:
-    """One expert: N(0, std) gate [F,H], up [F,H], down [H,F], quantized."""
+def quantize_torch(w, bits: int):
+    """The encoder of ``quantize`` in torch, on w's device (any device): the
+    same steps in the same fp32/fp16 arithmetic, so the same bytes for the
+    same w.  w: float32 tensor [..., cols] (cols % 32 == 0) -> uint8 tensor
+    [nblk * block_bytes], blocks in row-major order."""
+    import torch
+    w = w.contiguous().to(torch.float32)
+    qmax = (1 << (bits - 1)) - 1
+    bias = 1 << (bits - 1)
+    blk = w.reshape(-1, 32)
+    nblk = blk.shape[0]
+    amax = blk.abs().amax(dim=1)
+    d16 = (amax / torch.tensor(float(qmax), dtype=torch.float32, device=w.device)).to(torch.float16)
+    d32 = d16.to(torch.float32)
+    safe = torch.where(d32 > 0, d32, torch.ones_like(d32))
+    q = torch.round(blk / safe[:, None])  # round half to even, as np.rint
+    q.clamp_(-qmax, qmax)
+    q[d32 == 0] = 0
+    codes = (q + bias).to(torch.uint8)
+    out = torch.empty((nblk, block_bytes(bits)), dtype=torch.uint8, device=w.device)
+    dv = d16.view(torch.int16).to(torch.int32)
+    out[:, 0] = (dv & 0xFF).to(torch.uint8)
+    out[:, 1] = ((dv >> 8) & 0xFF).to(torch.uint8)
+    if bits == 4:
+        out[:, 2:18] = (codes[:, :16] & 0x0F) | ((codes[:, 16:] & 0x0F) << 4)
+    elif bits == 3:
+        lo = codes & 3
+        ql = torch.zeros((nblk, 8), dtype=torch.uint8, device=w.device)
+        for f in range(4):
+            ql |= lo[:, 8 * f:8 * f + 8] << (2 * f)
+        out[:, 2:10] = ql
+        hb = ((codes >> 2) & 1).to(torch.int64)
+        word = (hb << torch.arange(32, device=w.device, dtype=torch.int64)).sum(dim=1)
+        for j in range(4):
+            out[:, 10 + j] = ((word >> (8 * j)) & 0xFF).to(torch.uint8)
+    else:
+        raise ValueError(bits)
+    return out.reshape(-1)
+
+
+def _torch_seed(*key: int) -> int:
+    return int(np.random.SeedSequence([int(k) for k in key]).generate_state(1, dtype=np.uint64)[0] >> 1)
+
+
+def routed_weights_torch(cfg: Config, layer: int, device, base_seed: int = 0, chunk: int = 32,
+                         std: float = 0.02):
+    """All routed experts of one layer generated and quantized on `device`
+    (the benchmark's fast path for 48 layers of hundreds of experts): the
+    same recipe as ``routed_weights`` (N(0, std) gate, up, down per expert,
+    quantized per block of 32), drawn from torch's generator seeded per
+    (config, layer, expert, base_seed), so other values than the numpy
+    generator gives.  Returns a uint8 tensor [E * expert_bytes] on `device`."""
+    import torch
+    H, F, E, bits = cfg.hidden, cfg.ffn, cfg.n_experts, cfg.bits
+    eb = cfg.expert_bytes
+    mb = H * (F // 32) * block_bytes(bits)  # bytes of the gate (and the up) matrix
+    out = torch.empty(E * eb, dtype=torch.uint8, device=device)
+    gen = torch.Generator(device=device)
+    for e0 in range(0, E, chunk):
+        n = min(chunk, E - e0)
+        gu = torch.empty((n, 2, F, H), device=device, dtype=torch.float32)
+        dn = torch.empty((n, H, F), device=device, dtype=torch.float32)
+        for i in range(n):
+            gen.manual_seed(_torch_seed(cfg.wcid, layer, TID_ROUTED, base_seed, e0 + i, 1))
+            gu[i].normal_(0.0, std, generator=gen)
+            dn[i].normal_(0.0, std, generator=gen)
+        view = out[e0 * eb:(e0 + n) * eb].view(n, eb)
+        view[:, :2 * mb] = quantize_torch(gu, bits).view(n, 2 * mb)
+        view[:, 2 * mb:] = quantize_torch(dn, cfg.dbits).view(n, eb - 2 * mb)
+        del gu, dn
+    return out
+
+
+def expert_blob(rg: np.random.Generator, hidden: int, ffn: int, bits: int, std: float = 0.02,
+                down_bits: int = 0) -> np.ndarray:
+    """One expert: N(0, std) gate [F,H], up [F,H] (bits), down [H,F]
+    (down_bits, 0 = bits), quantized."""
     g = rg.standard_normal((ffn, hidden), dtype=np.float32) * np.float32(std)
     u = rg.standard_normal((ffn, hidden), dtype=np.float32) * np.float32(std)
     d = rg.standard_normal((hidden, ffn), dtype=np.float32) * np.float32(std)
-    return np.concatenate([quantize(g, bits), quantize(u, bits), quantize(d, bits)])
+    return np.concatenate([quantize(g, bits), quantize(u, bits), quantize(d, down_bits or bits)])
 
 
 def _threads(n: int | None) -> int:
@@ -180,7 +270,7 @@ def routed_weights(cfg: Config, layer: int, base_seed: int = 0, threads: int | N
 
     def one(e):
         buf[e * eb:(e + 1) * eb] = expert_blob(rng(cfg.wcid, layer, TID_ROUTED, base_seed, e),
-                                               cfg.hidden, cfg.ffn, cfg.bits)
+                                               cfg.hidden, cfg.ffn, cfg.bits, down_bits=cfg.down_bits)
 
     with ThreadPoolExecutor(_threads(threads)) as ex:
         list(ex.map(one, range(cfg.n_experts)))
@@ -190,7 +280,8 @@ def routed_weights(cfg: Config, layer: int, base_seed: int = 0, threads: int | N
 def shared_weights(cfg: Config, layer: int, base_seed: int = 0) -> np.ndarray | None:
     if not cfg.shared_ffn:
         return None
-    return expert_blob(rng(cfg.wcid, layer, TID_SHARED, base_seed), cfg.hidden, cfg.shared_ffn, cfg.bits)
+    return expert_blob(rng(cfg.wcid, layer, TID_SHARED, base_seed), cfg.hidden, cfg.shared_ffn, cfg.bits,
+                       down_bits=cfg.down_bits)
 
 
 # --------------------------------------------------------------------------

@@ -41,12 +41,15 @@ def dequant_matrix(raw, bits, rows, cols):
     return dequant_blocks(raw, bits).reshape(rows, cols)
 
 
-def dequant_expert(blob, bits, H, F):
-    B = {4: 18, 3: 14}[bits]
-    mb = H * (F // 32) * B
+def dequant_expert(blob, bits, H, F, down_bits=None):
+    """gate, up ([F,H], `bits`) and down ([H,F], `down_bits`, default `bits`)."""
+    db = bits if down_bits is None else down_bits
+    mg = H * (F // 32) * {4: 18, 3: 14}[bits]
+    md = H * (F // 32) * {4: 18, 3: 14}[db]
     blob = np.asarray(blob, dtype=np.uint8)
-    return (dequant_matrix(blob[:mb], bits, F, H), dequant_matrix(blob[mb:2 * mb], bits, F, H),
-            dequant_matrix(blob[2 * mb:3 * mb], bits, H, F))
+    assert blob.size == 2 * mg + md
+    return (dequant_matrix(blob[:mg], bits, F, H), dequant_matrix(blob[mg:2 * mg], bits, F, H),
+            dequant_matrix(blob[2 * mg:], db, H, F))
 
 
 def swiglu_mlp(X, Wg, Wu, Wd):
@@ -61,9 +64,12 @@ def x_to_f64(x, x_code):
     return np.asarray(x, dtype=np.float64) if x_code == 0 else bf16_bits_to_f64(x)
 
 
-def dense_masked_layer(x, x_code, logits, k, bits, H, F, routed, shared=None, s_bits=None, s_F=None):
+def dense_masked_layer(x, x_code, logits, k, bits, H, F, routed, shared=None, s_bits=None, s_F=None,
+                       down_bits=None):
     """Every expert on every row, weighted by a [T,E] mask that is the softmax
-    of the k selected logits and zero elsewhere; plus the shared expert."""
+    of the k selected logits and zero elsewhere; plus the shared expert.
+    bits: gate/up width, down_bits: down width (default bits), for the routed
+    and the shared experts alike."""
     X = x_to_f64(x, x_code)
     L = np.asarray(logits, dtype=np.float32)
     T, E = L.shape
@@ -73,16 +79,17 @@ def dense_masked_layer(x, x_code, logits, k, bits, H, F, routed, shared=None, s_
         sel = L[t, order[t]].astype(np.float64)
         ex = np.exp(sel - sel.max())
         M[t, order[t]] = ex / ex.sum()
-    eb = 3 * H * (F // 32) * {4: 18, 3: 14}[bits]
+    db = bits if down_bits is None else down_bits
+    eb = H * (F // 32) * (2 * {4: 18, 3: 14}[bits] + {4: 18, 3: 14}[db])
     Y = np.zeros((T, H))
     for e in range(E):
         if not M[:, e].any():
             continue
-        Wg, Wu, Wd = dequant_expert(routed[e * eb:(e + 1) * eb], bits, H, F)
+        Wg, Wu, Wd = dequant_expert(routed[e * eb:(e + 1) * eb], bits, H, F, db)
         Y += M[:, e:e + 1] * swiglu_mlp(X, Wg, Wu, Wd)
     if shared is not None:
         sb = bits if s_bits is None else s_bits
         sF = F if s_F is None else s_F
-        Wg, Wu, Wd = dequant_expert(shared, sb, H, sF)
+        Wg, Wu, Wd = dequant_expert(shared, sb, H, sF, db)
         Y += swiglu_mlp(X, Wg, Wu, Wd)
     return Y, order.astype(np.int32), M

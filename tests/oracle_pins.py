@@ -6,6 +6,8 @@ force or an invariant.  The same functions run against deliberately broken
 builds of oracle.c (tests/test_oracle_negative.py): every planted mistake
 must trip at least one pin.
 """
+import dataclasses
+
 import numpy as np
 
 import npref
@@ -147,6 +149,46 @@ def pin_expert_bytes(o):
     assert o.expert_bytes(3, 2048, 512) == 1376256
     assert o.expert_bytes(5, 256, 512) == -1
     assert o.expert_bytes(4, 250, 512) == -1
+    # per-projection widths: H*F/32 * (2*B_gate/up + B_down)
+    assert o.expert_bytes(3 | (4 << 8), 2048, 512) == 2048 * 16 * (2 * 14 + 18) == 1507328
+    assert o.expert_bytes(4 | (3 << 8), 2048, 768) == 2048 * 24 * (2 * 18 + 14) == 2457600
+    assert o.expert_bytes(3 | (3 << 8), 2048, 512) == o.expert_bytes(3, 2048, 512)
+    assert o.expert_bytes(3 | (5 << 8), 2048, 512) == -1
+    assert o.expert_bytes(3 | (4 << 16), 2048, 512) == -1
+
+
+def pin_format_bits(o):
+    assert (o.format_bits(3, False), o.format_bits(3, True)) == (3, 3)
+    assert (o.format_bits(4, False), o.format_bits(4, True)) == (4, 4)
+    assert (o.format_bits(3 | (4 << 8), False), o.format_bits(3 | (4 << 8), True)) == (3, 4)
+    assert (o.format_bits(4 | (3 << 8), False), o.format_bits(4 | (3 << 8), True)) == (4, 3)
+    assert o.format_bits(2, False) == -1 and o.format_bits(4 | (2 << 8), True) == -1
+
+
+def pin_mixed_expert_indexing(o):
+    """A blob with gate/up in one width and down in the other: every block's
+    scale names its (matrix, row, block) and every code is bias + 1, so each
+    dequantized weight is its block's scale; the three matrices must come back
+    at their own offsets, in their own widths."""
+    H, F = 64, 96
+    for bg, bd in ((3, 4), (4, 3)):
+        mats, exp = [], []
+        for m, (rows, cols, bits) in enumerate(((F, H, bg), (F, H, bg), (H, F, bd))):
+            nb = cols // 32
+            d = np.array([(m + 1) * 256 + r * 4 + b for r in range(rows) for b in range(nb)], dtype=np.float64)
+            d16 = (d / 4096.0).astype(np.float16)  # exact: 11-bit integers over a power of two
+            assert np.array_equal(d16.astype(np.float64), d / 4096.0)
+            codes = np.full((rows * nb, 32), (1 << (bits - 1)) + 1, dtype=np.uint8)
+            mats.append(synth.pack_codes(codes, d16, bits))
+            exp.append(np.repeat((d / 4096.0).reshape(rows, nb), 32, axis=1))
+        blob = np.concatenate(mats)
+        fmt = bg | (bd << 8)
+        assert blob.size == o.expert_bytes(fmt, H, F)
+        got = o.dequant_expert(fmt, blob, H, F)
+        for g, e in zip(got, exp):
+            assert np.array_equal(g, e), (bg, bd)
+        for g, e in zip(npref.dequant_expert(blob, bg, H, F, bd), exp):
+            assert np.array_equal(g, e)
 
 
 # ----------------------------------------------------------------------------
@@ -235,18 +277,20 @@ def small_cfg(bits, x_dtype, E=12, H=64, F=96, k=3, Fs=64, logits=("normal", 1.0
 
 
 def pin_layer_dense(o):
-    """Oracle layer == dense-with-mask brute force (all experts on all rows)."""
-    for bits, xd, Fs in [(4, "f32", 64), (3, "bf16", 96), (4, "bf16", 0), (3, "f32", 32)]:
-        cfg = small_cfg(bits, xd, Fs=Fs)
+    """Oracle layer == dense-with-mask brute force (all experts on all rows),
+    uniform and per-projection formats."""
+    for bits, db, xd, Fs in [(4, 0, "f32", 64), (3, 0, "bf16", 96), (4, 0, "bf16", 0), (3, 0, "f32", 32),
+                             (3, 4, "bf16", 64), (4, 3, "f32", 96)]:
+        cfg = dataclasses.replace(small_cfg(bits, xd, Fs=Fs), down_bits=db)
         li = synth.layer_inputs(cfg, T=7, threads=1)
-        y, idx, w = o.layer_forward(li.x, li.x_code, li.logits, cfg.top_k, bits, cfg.ffn,
+        y, idx, w = o.layer_forward(li.x, li.x_code, li.logits, cfg.top_k, cfg.fmt, cfg.ffn,
                                     li.routed, li.shared, s_ffn=Fs or None)
         yr, ir, M = npref.dense_masked_layer(li.x, li.x_code, li.logits, cfg.top_k, bits,
                                              cfg.hidden, cfg.ffn, li.routed, li.shared,
-                                             s_F=Fs or None)
+                                             s_F=Fs or None, down_bits=cfg.dbits)
         assert np.array_equal(idx, ir)
         rms = np.sqrt(np.mean(yr ** 2))
-        assert np.max(np.abs(y - yr)) <= 1e-12 * rms, (bits, xd, np.max(np.abs(y - yr)) / rms)
+        assert np.max(np.abs(y - yr)) <= 1e-12 * rms, (bits, db, xd, np.max(np.abs(y - yr)) / rms)
 
 
 def pin_layer_single_expert(o):
@@ -321,6 +365,7 @@ def pin_expert_ffn_matches_layer(o):
 
 
 ALL_PINS = [pin_half, pin_bf16, pin_blocks, pin_encoder_roundtrip, pin_matrix_indexing,
-            pin_numpy_dequant_agrees, pin_expert_bytes, pin_route_bruteforce, pin_route_ties,
+            pin_numpy_dequant_agrees, pin_expert_bytes, pin_format_bits, pin_mixed_expert_indexing,
+            pin_route_bruteforce, pin_route_ties,
             pin_route_special, pin_group, pin_layer_dense, pin_layer_single_expert,
             pin_layer_zeros, pin_layer_invariances, pin_expert_ffn_matches_layer]

@@ -30,8 +30,12 @@ MUTATIONS = [
     ("down_input_reversed", "acc += dr[f] * hid[f];", "acc += dr[f] * hid[F - 1 - f];"),
     ("shared_expert_dropped", "    if (shared) {\n        orc_expert sx;", "    if (0) {\n        orc_expert sx;"),
     ("combine_drops_last_slot", "for (j = 1; j < k; ++j) acc += w", "for (j = 1; j < k - 1; ++j) acc += w"),
-    ("gate_up_swapped", "orc_dequant_matrix(bits, blob, F, H, ex->gate);",
-     "orc_dequant_matrix(bits, blob, F, H, ex->up);"),
+    ("gate_up_swapped", "orc_dequant_matrix(bg, blob, F, H, ex->gate);",
+     "orc_dequant_matrix(bg, blob, F, H, ex->up);"),
+    ("down_read_in_gate_up_format", "orc_dequant_matrix(bd, blob + 2 * mat, H, F, ex->down);",
+     "orc_dequant_matrix(bg, blob + 2 * mat, H, F, ex->down);"),
+    ("format_down_width_ignored", "    if (dn == 0) dn = gu;", "    dn = gu;"),
+    ("expert_bytes_uniform", "(2 * orc_block_bytes(bg) + orc_block_bytes(bd))", "(3 * orc_block_bytes(bg))"),
 ]
 
 
@@ -48,8 +52,8 @@ def test_planted_mistake_is_caught(tmpdir_mod, name, old, new):
     assert src.count(old) == 1, f"mutation anchor not unique for {name}"
     mut = src.replace(old, new)
     if name == "gate_up_swapped":  # load up into gate's slot too, so up reads gate's bytes
-        mut = mut.replace("orc_dequant_matrix(bits, blob + mat, F, H, ex->up);",
-                          "orc_dequant_matrix(bits, blob + mat, F, H, ex->gate);")
+        mut = mut.replace("orc_dequant_matrix(bg, blob + mat, F, H, ex->up);",
+                          "orc_dequant_matrix(bg, blob + mat, F, H, ex->gate);")
     c_path = os.path.join(tmpdir_mod, f"{name}.c")
     so_path = os.path.join(tmpdir_mod, f"lib{name}.so")
     open(c_path, "w").write(mut)
