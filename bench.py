@@ -5,17 +5,21 @@ activations and router logits, all resident in HBM), captured in a HIP graph
 and replayed; every step runs the whole hot path (routing, grouping, expert
 FFNs, shared expert, combine).
 
-    python bench.py [--workload decode|mtp16|e512|e512x4|prefill|tiny] [--steps K] [--warmup W]
+    python bench.py [--workload all|decode|tiny|mtp16|e512|e512x4|prefill] [--steps K] [--warmup W]
 
-Prints one JSON line.  The default workload is the decode layer (one row per
-window, 128 experts, top-8 + shared expert, 4-bit, hidden 2048, FFN 768).
-`value` is the effective expert-weight bandwidth (distinct experts touched per
-layer, plus the shared expert, each blob's bytes counted once) over the
-whole pass; for the prefill workload it is tokens/s.  `roofline` rates the
-dominant kernel against MI355X's HBM (8 TB/s) or bf16 MFMA (2.5 PFLOP/s)
-peak from its own duration, timed with HIP events recorded on its stream
-around each launch.  `cpu_baseline` is the CPU oracle timed on a bounded
-sample of the same workload on this host.
+The default runs every workload (the five configurations; the
+large-expert-count decode at 1 and 4 rows) and prints ONE JSON line.  Its
+top-level fields are the decode workload's (one row per window, 128 experts,
+top-8 + shared expert, 4-bit, hidden 2048, FFN 768); `workloads` lists every
+workload with its us/layer, tokens/s, expert-weight GB/s, roofline fraction,
+counter traffic and CPU baseline.  `value` is the effective expert-weight
+bandwidth (distinct experts touched per layer, plus the shared expert, each
+blob's bytes counted once) over the whole pass; for the prefill workload it
+is tokens/s.  `roofline` rates the dominant kernel against MI355X's HBM
+(8 TB/s) or bf16 MFMA (2.5 PFLOP/s) peak from its own duration, timed with
+HIP events recorded on its stream.  `cpu_baseline` is the CPU oracle timed
+on a bounded sample of the same workload on this host, on all cores (OpenMP
+over rows) and on one.
 """
 from __future__ import annotations
 
@@ -33,11 +37,12 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+METRIC = "MoE layer us + expert-weight GB/s at 1-16 decode rows; prefill tok/s"
 
+# name: (config, rows); the order of the default run (the headline first)
 WORKLOADS = {
-    # name: (config, rows)
-    "tiny": ("tiny", 4),
     "decode": ("decode", 1),
+    "tiny": ("tiny", 4),
     "mtp16": ("mtp16", 16),
     "e512": ("e512", 1),
     "e512x4": ("e512", 4),
@@ -101,74 +106,140 @@ def layer_flops(cfg, T: int) -> tuple[float, float]:
     return 2 * (routed + shared), routed + shared
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
-    ap.add_argument("--layers", type=int, default=48)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle sample")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="only run a plain device copy of MIB MiB five times (reference for HBM byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (the layer's kernels run on one device); --gpus {args.gpus} "
-              f"is not supported", file=sys.stderr)
-        sys.exit(2)
+def host_info() -> dict:
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"nproc": usable, "cpu_count": os.cpu_count(), "cpu_model": model,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
 
+
+class WeightCache:
+    """Prepared weight sets on the device, shared by the workloads that read
+    the same layer weights (e512, e512x4 and prefill), freed when no later
+    workload needs them."""
+
+    def __init__(self, dev, layers: int):
+        self.dev = dev
+        self.layers = layers
+        self.sets = {}
+
+    def get(self, cfg):
+        import torch
+        from quantized_routed_expert_amd import moe, synth
+        key = (cfg.wcid, cfg.bits, cfg.hidden, cfg.ffn, cfg.n_experts, cfg.shared_ffn)
+        if key in self.sets:
+            return self.sets[key]
+        t0 = time.time()
+        out = []
+        for l in range(self.layers):
+            raw = synth.routed_weights_torch(cfg, l, self.dev)
+            routed_t, routed = moe.prepare_qweights(raw, cfg.bits, cfg.n_experts, cfg.hidden, cfg.ffn)
+            sh = synth.shared_weights(cfg, l)
+            shared_raw = torch.from_numpy(sh).to(self.dev) if sh is not None else None
+            shared_t, shared = (moe.prepare_qweights(shared_raw, cfg.bits, 1, cfg.hidden, cfg.shared_ffn)
+                                if sh is not None else (None, None))
+            # the pages' block order of a few layers stays on the host for the oracle
+            host = (raw.cpu().numpy(), sh) if l < 4 else None
+            del raw, shared_raw
+            out.append({"routed_t": routed_t, "routed": routed, "shared_t": shared_t, "shared": shared,
+                        "host": host})
+        torch.cuda.synchronize()
+        log(f"weights of {cfg.name}-shaped layers: {self.layers} layers generated and prepared on the device "
+            f"({time.time() - t0:.1f} s)")
+        self.sets[key] = out
+        return out
+
+    def drop_unless(self, cfgs_left):
+        import torch
+        keep = {(c.wcid, c.bits, c.hidden, c.ffn, c.n_experts, c.shared_ffn) for c in cfgs_left}
+        for key in list(self.sets):
+            if key not in keep:
+                del self.sets[key]
+        torch.cuda.empty_cache()
+
+
+def cpu_baseline(orc, cfg, T, wsets, xs, logits, bytes_layer, seconds, path_decode, L):
+    """The oracle on a bounded sample of the workload, on all cores (OpenMP
+    over rows) and on one; returns the cpu_baseline object."""
+    nthreads = orc.set_threads(0)
+    res = {}
+    for leg, nt in (("all_cores", nthreads), ("one_core", 1)):
+        orc.set_threads(nt)
+        t_start = time.time()
+        if path_decode:
+            n_layers, cpu_bytes = 0, 0.0
+            while time.time() - t_start < seconds or n_layers == 0:
+                l = n_layers % min(4, L)
+                routed, shared = wsets[l]["host"]
+                orc.layer_forward(xs[l], 0 if cfg.x_dtype == "f32" else 1, logits[l], cfg.top_k, cfg.fmt,
+                                  cfg.ffn, routed, shared, s_ffn=cfg.shared_ffn or None)
+                cpu_bytes += bytes_layer[l]
+                n_layers += 1
+            dt = time.time() - t_start
+            res[leg] = {"value": round(cpu_bytes / dt / 1e9, 4), "unit": "GB/s", "threads": nt,
+                        "us_per_layer": round(dt / n_layers * 1e6, 1),
+                        "sample": f"{n_layers} layer evaluations of {T} row(s) (layers 0-3 of the pass, "
+                                  f"cycling), {dt:.1f} s"}
+        else:
+            routed, shared = wsets[0]["host"]
+            step = 16 if nt == 1 else 256
+            rows_done = 0
+            while (time.time() - t_start < seconds or rows_done == 0) and rows_done < T:
+                rows = np.arange(rows_done, min(rows_done + step, T), dtype=np.int32)
+                orc.layer_forward(xs[0], 0 if cfg.x_dtype == "f32" else 1, logits[0], cfg.top_k, cfg.fmt,
+                                  cfg.ffn, routed, shared,
+                                  s_ffn=cfg.shared_ffn or None, rows=rows)
+                rows_done += rows.size
+            dt = time.time() - t_start
+            res[leg] = {"value": round(rows_done / dt / L, 4), "unit": "tok/s", "threads": nt,
+                        "sample": f"{rows_done} of the {T} chunk rows of layer 0 (routing of all rows), "
+                                  f"{dt:.1f} s, scaled to a {L}-layer pass"}
+    orc.set_threads(nthreads)
+    main = res["all_cores"]
+    return {"value": main["value"], "unit": main["unit"], "cores": nthreads, "kind": "oracle",
+            "sample": main["sample"] + "; C oracle, OpenMP over rows", "one_core": res["one_core"],
+            **host_info()}
+
+
+def run_workload(name, args, wcache, orc):
     import torch
     from quantized_routed_expert_amd import moe, synth
 
-    if args.calibrate_copy:
-        n = args.calibrate_copy << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibration": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
-                          "copies": 5}), flush=True)
-        return
-
-    cname, T = WORKLOADS[args.workload]
+    cname, T = WORKLOADS[name]
     cfg = synth.CONFIGS[cname]
     L = args.layers
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
+    dev = wcache.dev
     path = moe.PATH_DECODE if T <= moe.DECODE_MAX_ROWS else moe.PATH_PREFILL
 
-    # ---- inputs: 48 independent layers, resident in HBM ----------------------
-    t0 = time.time()
-    layers = []
-    host_keep = []  # a few layers kept on the host for the oracle sample
+    # ---- inputs: L independent layers, resident in HBM ------------------------
+    wsets = wcache.get(cfg)
+    xs, lgs, layers, bytes_layer = [], [], [], []
     eb = cfg.expert_bytes
-    bytes_layer = []
     for l in range(L):
-        li = synth.layer_inputs(cfg, layer=l, T=T)
-        d = {
-            "x": (torch.from_numpy(li.x.view(np.int16)).view(torch.bfloat16) if cfg.x_dtype == "bf16"
-                  else torch.from_numpy(li.x)).to(dev),
-            "logits": torch.from_numpy(li.logits).to(dev),
-        }
-        # weights converted once to the order the kernels read (outside the timed region)
-        d["routed_t"], d["routed"] = moe.prepare_qweights(torch.from_numpy(li.routed).to(dev), cfg.bits,
-                                                          cfg.n_experts, cfg.hidden, cfg.ffn)
-        d["shared_t"], d["shared"] = (moe.prepare_qweights(torch.from_numpy(li.shared).to(dev), cfg.bits, 1,
-                                                           cfg.hidden, cfg.shared_ffn)
-                                      if li.shared is not None else (None, None))
+        x = synth.activations(cfg, l, T)
+        lg = synth.logits(cfg, l, T)
+        xs.append(x)
+        lgs.append(lg)
+        d = dict(wsets[l])
+        d["x"] = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if cfg.x_dtype == "bf16"
+                  else torch.from_numpy(x)).to(dev)
+        d["logits"] = torch.from_numpy(lg).to(dev)
         d["y"] = torch.empty((T, cfg.hidden), dtype=torch.float32, device=dev)
-        nd = distinct_experts(li.logits, cfg.top_k)
-        bytes_layer.append(nd * eb + cfg.shared_bytes)
+        bytes_layer.append(distinct_experts(lg, cfg.top_k) * eb + cfg.shared_bytes)
         layers.append(d)
-        if len(host_keep) < 48:
-            host_keep.append(li)
-        if l % 8 == 7 or l == L - 1:
-            log(f"generated and uploaded {l + 1}/{L} layers ({time.time() - t0:.0f} s)")
     torch.cuda.synchronize()
     ws = moe.workspace(T, cfg.n_experts, cfg.top_k, cfg.hidden, cfg.ffn, cfg.shared_ffn, path)
-
     stream = torch.cuda.Stream()
 
     def one_pass(s):
@@ -181,6 +252,7 @@ def main():
         for _ in range(max(args.warmup, 1)):
             one_pass(stream)
     torch.cuda.synchronize()
+    assert moe.workspace_error(ws) == 0, "device error word set during warmup"
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
         with torch.cuda.graph(graph, stream=stream):
@@ -189,9 +261,8 @@ def main():
     for _ in range(max(args.warmup, 1)):
         graph.replay()
     torch.cuda.synchronize()
-    log("warmup done")
 
-    # ---- timed region: K replays of the 48-layer pass ---------------------------
+    # ---- timed region: K replays of the L-layer pass ----------------------------
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -203,116 +274,145 @@ def main():
     torch.cuda.synchronize()
     ms_step = ev0.elapsed_time(ev1) / args.steps
     us_layer = ms_step * 1000.0 / L
-    log(f"pass {ms_step:.4f} ms, {us_layer:.2f} us/layer")
-
-    # ---- dominant kernel's own duration.  Decode: the layer is one kernel
-    # launch, so the timed region (events on the kernel's stream) over its K*L
-    # launches is that kernel's average duration plus the graph's launch gap.
-    # Prefill: events on the stream around each layer's launches.
-    reps = 3
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L * reps)]
-    with torch.cuda.stream(stream):
-        i = 0
-        for _ in range(reps):
-            for d in layers:
-                evs[i][0].record(stream)
-                moe.layer_forward(d["x"], d["logits"], cfg.top_k, d["routed"], d["shared"], d["y"], ws,
-                                  path=path, stream=stream)
-                evs[i][1].record(stream)
-                i += 1
-    torch.cuda.synchronize()
-    per_launch_us = np.array([a.elapsed_time(b) * 1000.0 for a, b in evs])
-    kern_us = float(np.mean(per_launch_us))
-    log(f"per-launch (event-bracketed) {kern_us:.2f} us")
+    err = moe.workspace_error(ws)
+    assert err == 0, f"device error word {err} after the timed region"
+    log(f"{name}: pass {ms_step:.4f} ms, {us_layer:.2f} us/layer")
 
     total_bytes = float(np.sum(bytes_layer))
     gbs = total_bytes / (ms_step * 1e-3) / 1e9
-    toks = T * 1000.0 / ms_step  # tokens per second through a 48-layer MoE stack
+    toks = T * 1000.0 / ms_step  # tokens per second through an L-layer MoE stack
     fl_gu, fl_dn = layer_flops(cfg, T)
+    desc = (f"{name}: H={cfg.hidden} E={cfg.n_experts} F={cfg.ffn} top-{cfg.top_k} + shared F={cfg.shared_ffn}, "
+            f"{cfg.bits}-bit block-32, T={T} rows, {L} layers")
 
     if path == moe.PATH_DECODE:
         metric_value, unit = gbs, "GB/s"
+        # the layer is one kernel launch: the timed region (events on the
+        # kernel's stream) over its K*L launches is that kernel's average
+        # duration plus the graph's launch gap
         kern_us = us_layer
         ach = (total_bytes / L) / (kern_us * 1e-6) / 1e9
         # windows of one to four rows (T * k <= 64) take the column-split
         # launch (integer nibble dot products), larger windows the matrix-core launch
         split = T <= 4 and T * cfg.top_k <= 64
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload),
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name),
                 "kernel": "k_split_layer" if split else "k_decode_layer", "bytes_per_launch": round(total_bytes / L),
                 "launch_us": round(kern_us, 3)}
-        # split: signed 4-bit products (codes x 16-bit activation digits), int32
-        # block sums, fp32 scale and accumulate; matrix-core: f16 MFMA, fp32 accumulate
+        # split: signed 4-bit products (codes x 15-bit integer activations cut
+        # into signed radix-16 digits), int32 block sums, fp32 scale and
+        # accumulate; matrix-core: f16 MFMA on exact codes and hi+lo activations
         dtype = "i4" if split else "f16"
     else:
         metric_value, unit = toks, "tok/s"
+        # events on the stream around each layer's launches (route, group,
+        # plan, both GEMMs, combine)
+        reps = 2
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(L * reps)]
+        with torch.cuda.stream(stream):
+            i = 0
+            for _ in range(reps):
+                for d in layers:
+                    evs[i][0].record(stream)
+                    moe.layer_forward(d["x"], d["logits"], cfg.top_k, d["routed"], d["shared"], d["y"], ws,
+                                      path=path, stream=stream)
+                    evs[i][1].record(stream)
+                    i += 1
+        torch.cuda.synchronize()
+        kern_us = float(np.mean([a.elapsed_time(b) * 1000.0 for a, b in evs]))
         ach = (fl_gu + fl_dn) / (kern_us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(args.workload),
+                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(name),
                 "kernel": "layer (route, group, plan, gate/up GEMM, down GEMM, combine)",
-                "flops_per_launch": fl_gu + fl_dn}
+                "flops_per_launch": fl_gu + fl_dn, "launch_us": round(kern_us, 3),
+                "hbm_frac_of_weights": round((total_bytes / L) / (kern_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         dtype = "bf16"
 
-    # ---- CPU baseline: the oracle on a bounded sample ------------------------------
     cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(orc, cfg, T, wsets, xs, lgs, bytes_layer, args.cpu_seconds,
+                           path == moe.PATH_DECODE, L)
+        log(f"{name}: cpu baseline {cpu['value']} {cpu['unit']} on {cpu['cores']} threads, "
+            f"{cpu['one_core']['value']} on one")
+
+    return {
+        "workload": name,
+        "metric_value": round(metric_value, 3), "unit": unit, "ms_per_step": round(ms_step, 5), "dtype": dtype,
+        "config": {"workload": desc, "rows": T, "layers": L,
+                   "path": "decode" if path == moe.PATH_DECODE else "prefill",
+                   "us_per_layer": round(us_layer, 3), "tokens_per_s": round(toks, 1),
+                   "expert_weight_GBps": round(gbs, 1),
+                   "mean_distinct_experts": round(float(np.mean([b - cfg.shared_bytes for b in bytes_layer]) / eb),
+                                                  2),
+                   "useful_TFLOPs": round((fl_gu + fl_dn) / (us_layer * 1e-6) / 1e12, 3)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="all", choices=["all"] + list(WORKLOADS))
+    ap.add_argument("--layers", type=int, default=48)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=6.0, help="budget of each oracle leg per workload")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the layer's kernels run on one device); --gpus {args.gpus} "
+              f"is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                          "copies": 5}), flush=True)
+        return
+
+    from quantized_routed_expert_amd import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    names = list(WORKLOADS) if args.workload == "all" else [args.workload]
+    orc = None
     if not args.no_cpu_baseline:
         import oracle
         orc = oracle.Oracle()
-        t_start = time.time()
-        n_layers = 0
-        rows_done = 0
-        cpu_bytes = 0.0
-        if path == moe.PATH_DECODE:
-            # the layers of the pass in order, cycling, until the time budget is spent
-            while time.time() - t_start < args.cpu_seconds:
-                li = host_keep[n_layers % len(host_keep)]
-                orc.layer_forward(li.x, li.x_code, li.logits, cfg.top_k, cfg.bits, cfg.ffn, li.routed, li.shared,
-                                  s_ffn=cfg.shared_ffn or None)
-                cpu_bytes += bytes_layer[n_layers % len(host_keep)]
-                n_layers += 1
-            dt = time.time() - t_start
-            cpu = {"value": round(cpu_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                   "sample": f"{n_layers} layer evaluations (the pass's {len(host_keep)} layers in order, "
-                             f"cycling), all {T} row(s), single-threaded C oracle ({dt:.1f} s); "
-                             f"{dt / n_layers * 1e6:.0f} us/layer"}
-        else:
-            li = host_keep[0]
-            step = 16
-            while time.time() - t_start < args.cpu_seconds and rows_done < T:
-                rows = np.arange(rows_done, min(rows_done + step, T), dtype=np.int32)
-                orc.layer_forward(li.x, li.x_code, li.logits, cfg.top_k, cfg.bits, cfg.ffn, li.routed, li.shared,
-                                  s_ffn=cfg.shared_ffn or None, rows=rows)
-                rows_done += rows.size
-            dt = time.time() - t_start
-            cpu = {"value": round(rows_done / dt / L, 4), "unit": "tok/s", "cores": 1, "kind": "oracle",
-                   "sample": f"{rows_done} of the {T} chunk rows of layer 0 (routing of all rows), "
-                             f"single-threaded C oracle ({dt:.1f} s), scaled to a {L}-layer pass"}
-        log(f"cpu baseline {cpu['value']} {cpu['unit']}")
+    wcache = WeightCache(dev, args.layers)
+    results = []
+    for i, name in enumerate(names):
+        results.append(run_workload(name, args, wcache, orc))
+        wcache.drop_unless([synth.CONFIGS[WORKLOADS[n][0]] for n in names[i + 1:]])
 
+    head = results[0]
     out = {
-        "metric": "MoE layer us + expert-weight GB/s at 1-16 decode rows; prefill tok/s",
-        "value": round(metric_value, 3),
-        "unit": unit,
+        "metric": METRIC,
+        "value": head["metric_value"],
+        "unit": head["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        "dtype": head["dtype"],
         "data": "synthetic (seeded; weights N(0,0.02) block-quantized, activations N(0,1), logits per recipe)",
-        "config": {
-            "workload": f"{args.workload}: H={cfg.hidden} E={cfg.n_experts} F={cfg.ffn} top-{cfg.top_k}"
-                        f" + shared F={cfg.shared_ffn}, {cfg.bits}-bit block-32, T={T} rows, {L} layers",
-            "rows": T, "layers": L, "path": "decode" if path == moe.PATH_DECODE else "prefill",
-            "us_per_layer": round(us_layer, 3),
-            "tokens_per_s": round(toks, 1),
-            "expert_weight_GBps": round(gbs, 1),
-            "mean_distinct_experts": round(float(np.mean([b - cfg.shared_bytes for b in bytes_layer]) / eb), 2),
-        },
-        "roofline": roof,
-        "cpu_baseline": cpu,
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "cpu_baseline": head["cpu_baseline"],
+        "workloads": [{k: v for k, v in r.items()} for r in results],
     }
     print(json.dumps(out), flush=True)
 

@@ -59,6 +59,14 @@
  *    at zero again, so a workspace can be reused by later calls (and graph
  *    replays) without clearing.  Two calls that run at the same time must
  *    not share a workspace.
+ *  - Co-residency.  The decode path (MOE_PATH_DECODE, and AUTO for T <= 16)
+ *    is one launch whose workgroups hand partial results to each other; it
+ *    launches as many workgroups as the device holds at once and assumes
+ *    that all of them are resident together.  Every wait in it is bounded:
+ *    if other work on the device keeps some workgroup from starting, the
+ *    waits run out, the call ends with wrong outputs and the workspace's
+ *    error word records it (moe_workspace_error).  Run decode calls without
+ *    other kernels competing for the device when the outputs matter.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -138,6 +146,19 @@ int64_t moe_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t hidden, int
 int moe_prepare_qweights(const moe_qweights *src, void *dst, int64_t stream);
 
 /*
+ * Device-side errors of the calls that used a workspace.  Synchronizes
+ * `stream`, copies the workspace's error word to *err_out (host) and, if
+ * clear != 0, sets it back to zero.  Bits: 1 = a bounded wait of a decode
+ * launch ran out (see "Co-residency" above; that call's outputs are wrong);
+ * 2 = moe_expert_ffn on the decode path was given a malformed grouping
+ * (its outputs are wrong; no access went out of bounds).  0 after correct
+ * calls.  The bits stay set until cleared; a later call is not affected by
+ * an earlier call's timeout.  Unlike the compute calls, this one waits for
+ * the stream and must not be called during graph capture.
+ */
+int moe_workspace_error(void *ws, int64_t ws_bytes, uint32_t *err_out, int32_t clear, int64_t stream);
+
+/*
  * Router (step 1).  logits (device) fp32 [T][E]; writes topk_idx (device)
  * int32 [T][k] and topk_w (device) fp32 [T][k].  Per token the k experts are
  * listed by decreasing logit, an equal logit going to the lower expert id
@@ -180,18 +201,31 @@ int moe_expert_ffn(const void *x, int32_t x_dtype, int32_t T, const moe_qweights
 /*
  * The whole layer (steps 1-4).  x (device) [T][H] fp32 or bf16; logits
  * (device) fp32 [T][E] with E = routed->n_experts; shared (host struct, may
- * be NULL) with n_experts = 1 and the same hidden.  Writes y (device) fp32
+ * be NULL) with n_experts = 1, the same hidden and the same bits as the
+ * routed experts (its ffn may differ; other bits: MOE_ERR_UNSUPPORTED,
+ * since every launch reads it as one more slot of the routed format).
+ * Writes y (device) fp32
  * [T][H]:
  *     y_t = (((w_t0 o_t0 + w_t1 o_t1) + ...) + w_t,k-1 o_t,k-1) + s_t
  * with o_tj the output of token t's j-th expert, w_tj its router weight and
  * s_t the shared expert's output, summed in that fixed order (the result
  * does not depend on launch geometry or timing).  topk_idx_out / topk_w_out
  * (device, may be NULL) receive the routing ([T][k] int32 / fp32).
+ *
+ * heat (device, may be NULL): int32 [E] routing heat of this layer.  The call
+ * adds to heat[e] the number of its (token, slot) pairs routed to expert e
+ * (the counts of step 2; they sum to T*k), so a caller keeping one [E] row
+ * per layer accumulates the per-(layer, expert) heat over calls (Strata
+ * "Several requests at once (batch slots)", section "The VRAM expert tier
+ * keeps adapting in batch windows"; extended-strata-moe "Reference",
+ * section "The adaptive cache": a heat per layer and expert).  Integer
+ * atomic adds, so the counts are exact whatever the order; calls running
+ * at the same time may share the buffer.
  */
 int moe_layer_forward(const void *x, int32_t x_dtype, const float *logits, int32_t T,
                       int32_t k, const moe_qweights *routed, const moe_qweights *shared,
-                      float *y, int32_t *topk_idx_out, float *topk_w_out, int32_t path,
-                      void *ws, int64_t ws_bytes, int64_t stream);
+                      float *y, int32_t *topk_idx_out, float *topk_w_out, int32_t *heat,
+                      int32_t path, void *ws, int64_t ws_bytes, int64_t stream);
 
 #ifdef __cplusplus
 }

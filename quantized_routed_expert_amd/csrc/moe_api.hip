@@ -83,6 +83,8 @@ struct Layout {
 // after the slot and slice counters: the error word (a line of its own),
 // then the per-workgroup epochs
 constexpr size_t COUNTER_WORDS = (size_t)(2 * DEC_MAX_SLOTS + DEC_MAX_SLICES + 1) * DEC_CSTRIDE + EPOCH_SLOTS;
+// byte offset of the error word (and, after it, the tag of the last call whose wait ran out)
+constexpr size_t ERR_OFFSET = (size_t)(2 * DEC_MAX_SLOTS + DEC_MAX_SLICES) * DEC_CSTRIDE * 4;
 Layout make_layout(int T, int E, int k, int H, int F, int Fs, int path) {
     Layout L;
     size_t off = 0;
@@ -239,8 +241,8 @@ int decode_lds_layout(DecodeParams &P, int xparts) {
     P.lds_slot_start = take(P.max_slots * 4);
     P.lds_slot_exp = take(P.max_slots * 4);
     P.lds_slot_cnt = take(P.max_slots * 4);
-    P.lds_tinv = take(P.T * 4);
-    P.lds_hinv = take(P.T * 4);
+    P.lds_tsc = take(P.T * 4);
+    P.lds_hsc = take(P.T * 4);
     P.lds_xmax = take(P.T * 4);
     P.lds_misc = take(64);
     // activations (one 16-byte pad per token row keeps the 16 rows of an
@@ -405,6 +407,21 @@ int moe_prepare_qweights(const moe_qweights *src, void *dst, int64_t stream) {
     return launch_err(prepare_launch((const uint8_t *)src->data, (uint8_t *)dst, P, S(stream)));
 }
 
+int moe_workspace_error(void *ws, int64_t ws_bytes, uint32_t *err_out, int32_t clear, int64_t stream) {
+    if (!ws || !err_out) return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < (int64_t)(ERR_OFFSET + 8)) return MOE_ERR_WORKSPACE;
+    uint8_t *w = (uint8_t *)ws + ERR_OFFSET;
+    uint32_t v = 0;
+    if (hipMemcpyAsync(&v, w, 4, hipMemcpyDeviceToHost, S(stream)) != hipSuccess) return MOE_ERR_LAUNCH;
+    if (hipStreamSynchronize(S(stream)) != hipSuccess) return MOE_ERR_LAUNCH;
+    if (clear) {
+        if (hipMemsetAsync(w, 0, 8, S(stream)) != hipSuccess) return MOE_ERR_LAUNCH;
+        if (hipStreamSynchronize(S(stream)) != hipSuccess) return MOE_ERR_LAUNCH;
+    }
+    *err_out = v;
+    return MOE_OK;
+}
+
 int moe_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *topk_idx, float *topk_w,
               int64_t stream) {
     int rc = check_shape(T, E, k, 256, 256);
@@ -422,7 +439,7 @@ int moe_group(const int32_t *topk_idx, int32_t T, int32_t E, int32_t k, int32_t 
     if (rc) return rc;
     Layout L = make_layout(T, E, k, 256, 256, 0, MOE_PATH_PREFILL);
     if (ws_bytes < (int64_t)(L.chunk_counts + (size_t)L.nchunks * E * 4)) return MOE_ERR_WORKSPACE;
-    GroupParams G{topk_idx, T, E, k, L.nchunks, at<uint32_t>(ws, L.chunk_counts), offsets, pairs, active};
+    GroupParams G{topk_idx, T, E, k, L.nchunks, at<uint32_t>(ws, L.chunk_counts), offsets, pairs, active, nullptr};
     return launch_err(group_launch(G, S(stream)));
 }
 
@@ -433,8 +450,8 @@ namespace {
 // Fused decode launch (routing in-kernel when logits != nullptr).
 int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_off, const int32_t *g_pairs,
                const int32_t *g_act, const float *g_pw, int T, int E, int k, const moe_qweights *routed,
-               const moe_qweights *shared, float *y, float *out_pairs, int32_t *tidx, float *tw, const Layout &L,
-               void *ws, int mode, hipStream_t st) {
+               const moe_qweights *shared, float *y, float *out_pairs, int32_t *tidx, float *tw, int32_t *heat,
+               const Layout &L, void *ws, int mode, hipStream_t st) {
     DevInfo dv;
     int rc = dev_info(dv);
     if (rc) return rc;
@@ -456,6 +473,7 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
         S_.out_shared = at<float>(ws, L.out_shared);
         S_.topk_idx_out = tidx;
         S_.topk_w_out = tw;
+        S_.heat = heat;
         S_.part = at<uint64_t>(ws, L.part);
         uint32_t *cnt = at<uint32_t>(ws, L.counters);
         S_.err = cnt + (size_t)(2 * DEC_MAX_SLOTS + DEC_MAX_SLICES) * DEC_CSTRIDE;
@@ -507,6 +525,7 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
     P.out_shared = at<float>(ws, L.out_shared);
     P.topk_idx_out = tidx;
     P.topk_w_out = tw;
+    P.heat = heat;
     P.hll = at<uint64_t>(ws, L.harr);
     P.oll = at<uint64_t>(ws, L.oll);
     uint32_t *cnt = at<uint32_t>(ws, L.counters);
@@ -616,7 +635,7 @@ int moe_expert_ffn(const void *x, int32_t x_dtype, int32_t T, const moe_qweights
     const int xf = x_dtype == MOE_DTYPE_F32;
     if (p == MOE_PATH_DECODE)
         return run_decode(x, xf, nullptr, offsets, pairs, active, pair_w, T, w->n_experts, k, w, nullptr, nullptr,
-                          out_pairs, nullptr, nullptr, L, ws, 0, S(stream));
+                          out_pairs, nullptr, nullptr, nullptr, L, ws, 0, S(stream));
     PlanParams PP{offsets, active, T, w->n_experts, k, 0, w->ffn, 0, w->hidden,
                   at<int32_t>(ws, L.slot_exp), at<int32_t>(ws, L.slot_row0), at<int32_t>(ws, L.slot_cnt),
                   at<int32_t>(ws, L.slot_hrow0), at<int32_t>(ws, L.prefix_gu), at<int32_t>(ws, L.prefix_dn)};
@@ -627,7 +646,8 @@ int moe_expert_ffn(const void *x, int32_t x_dtype, int32_t T, const moe_qweights
 
 int moe_layer_forward(const void *x, int32_t x_dtype, const float *logits, int32_t T, int32_t k,
                       const moe_qweights *routed, const moe_qweights *shared, float *y, int32_t *topk_idx_out,
-                      float *topk_w_out, int32_t path, void *ws, int64_t ws_bytes, int64_t stream) {
+                      float *topk_w_out, int32_t *heat, int32_t path, void *ws, int64_t ws_bytes,
+                      int64_t stream) {
     if (!routed) return MOE_ERR_INVALID_ARG;
     if (T != 0 && (!x || !logits || !y || !ws)) return MOE_ERR_INVALID_ARG;
     if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
@@ -641,10 +661,12 @@ int moe_layer_forward(const void *x, int32_t x_dtype, const float *logits, int32
     const int E = routed->n_experts, H = routed->hidden;
     rc = check_shape(T, E, k, H, routed->ffn);
     if (rc) return rc;
+    // every launch reads the shared expert as one more slot in the routed
+    // experts' format
+    if (shared && shared->bits != routed->bits) return MOE_ERR_UNSUPPORTED;
     const int Fs = shared ? shared->ffn : 0;
     int p = resolve_path(path, T);
-    const bool same_bits = !shared || shared->bits == routed->bits;
-    if (p == MOE_PATH_DECODE && (T > MOE_DECODE_MAX_ROWS || !same_bits ||
+    if (p == MOE_PATH_DECODE && (T > MOE_DECODE_MAX_ROWS ||
                                  !(split_fits(T, E, k, H, routed->ffn, Fs, routed->bits, 1, 256) ||
                                    decode_fits(T, E, k, H, routed->ffn, Fs, routed->bits, x_dtype)))) {
         if (path == MOE_PATH_DECODE) return MOE_ERR_UNSUPPORTED;
@@ -660,22 +682,22 @@ int moe_layer_forward(const void *x, int32_t x_dtype, const float *logits, int32
     if (p == MOE_PATH_DECODE) {
         if (E <= DEC_MAX_E_FUSED)
             return run_decode(x, xf, logits, nullptr, nullptr, nullptr, nullptr, T, E, k, routed, shared, y,
-                              at<float>(ws, L.out_pairs), topk_idx_out, topk_w_out, L, ws,
+                              at<float>(ws, L.out_pairs), topk_idx_out, topk_w_out, heat, L, ws,
                               DEC_MODE_ROUTE | DEC_MODE_COMBINE, st);
         RouteParams R{logits, T, E, k, idx, wts};
         if (route_launch(R, st) != hipSuccess) return MOE_ERR_LAUNCH;
         GroupParams G{idx, T, E, k, L.nchunks, at<uint32_t>(ws, L.chunk_counts), at<int32_t>(ws, L.offsets),
-                      at<int32_t>(ws, L.pairs), at<int32_t>(ws, L.active)};
+                      at<int32_t>(ws, L.pairs), at<int32_t>(ws, L.active), heat};
         if (group_launch(G, st) != hipSuccess) return MOE_ERR_LAUNCH;
         return run_decode(x, xf, nullptr, at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.pairs),
                           at<int32_t>(ws, L.active), wts, T, E, k, routed, shared, y, at<float>(ws, L.out_pairs),
-                          nullptr, nullptr, L, ws, DEC_MODE_COMBINE, st);
+                          nullptr, nullptr, nullptr, L, ws, DEC_MODE_COMBINE, st);
     }
     // prefill: route, group, plan, gate/up GEMM, down GEMM, combine
     RouteParams R{logits, T, E, k, idx, wts};
     if (route_launch(R, st) != hipSuccess) return MOE_ERR_LAUNCH;
     GroupParams G{idx, T, E, k, L.nchunks, at<uint32_t>(ws, L.chunk_counts), at<int32_t>(ws, L.offsets),
-                  at<int32_t>(ws, L.pairs), at<int32_t>(ws, L.active)};
+                  at<int32_t>(ws, L.pairs), at<int32_t>(ws, L.active), heat};
     if (group_launch(G, st) != hipSuccess) return MOE_ERR_LAUNCH;
     PlanParams PP{at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.active), T, E, k, shared ? 1 : 0, routed->ffn,
                   Fs, H, at<int32_t>(ws, L.slot_exp), at<int32_t>(ws, L.slot_row0), at<int32_t>(ws, L.slot_cnt),

@@ -404,12 +404,13 @@ struct XGroup {
         for (int s = 0; s < 8; ++s) m = fmaxf(m, fabsf(val(s)));
         return m;
     }
-    // fp16 hi [and lo] of value * scale in slot order e = 0..7
-    __device__ __forceinline__ void convert(float scale, u32x4 &hi, u32x4 &lo) const {
+    // fp16 hi [and lo] of value * 2^sc in slot order e = 0..7 (ldexp: exact
+    // for any sc, also where 2^sc itself is not a normal float)
+    __device__ __forceinline__ void convert(int sc, u32x4 &hi, u32x4 &lo) const {
         uint32_t h[4], l[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-            const float v0 = val(xslot<BITS>(2 * e2)) * scale, v1 = val(xslot<BITS>(2 * e2 + 1)) * scale;
+            const float v0 = ldexpf(val(xslot<BITS>(2 * e2)), sc), v1 = ldexpf(val(xslot<BITS>(2 * e2 + 1)), sc);
             const _Float16 a0 = (_Float16)v0, a1 = (_Float16)v1;
             h[e2] = __builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
             l[e2] = f2h_bits(v0 - (float)a0) | ((uint32_t)f2h_bits(v1 - (float)a1) << 16);
@@ -440,8 +441,8 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
     int *s_slot_start = (int *)(smem + P.lds_slot_start);
     int *s_slot_exp = (int *)(smem + P.lds_slot_exp);
     int *s_slot_cnt = (int *)(smem + P.lds_slot_cnt);
-    float *s_tinv = (float *)(smem + P.lds_tinv);
-    float *s_hinv = (float *)(smem + P.lds_hinv);
+    int *s_tsc = (int *)(smem + P.lds_tsc);  // per token: the power of two sc of its staged activations
+    int *s_hsc = (int *)(smem + P.lds_hsc);  // per row of a down tile: that of its staged h
     uint32_t *s_xmax = (uint32_t *)(smem + P.lds_xmax);
     int *s_misc = (int *)(smem + P.lds_misc);
     uint8_t *s_xa = smem + P.lds_xa;
@@ -650,10 +651,9 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
                 int ex = 0;
                 if (mx > 0.0f) frexpf(mx, &ex);
                 const int sc = mx > 0.0f ? 14 - ex : 0;  // max * 2^sc in [2^13, 2^14)
-                const float scale = __builtin_bit_cast(float, (uint32_t)(127 + sc) << 23);  // 2^sc, exact
-                if (xg_pos[q] == 0) s_tinv[t] = __builtin_bit_cast(float, (uint32_t)(127 - sc) << 23);
+                if (xg_pos[q] == 0) s_tsc[t] = sc;
                 u32x4 hi, lo;
-                xg[q].convert(scale, hi, lo);
+                xg[q].convert(sc, hi, lo);
                 uint8_t *dst = s_xa + (size_t)t * P.x_rs + (size_t)xg_pos[q] * 16;
                 *(u32x4 *)dst = hi;
                 if (XPARTS == 2) *(u32x4 *)(dst + (size_t)T * P.x_rs) = lo;
@@ -711,6 +711,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             for (int p = tid; p < TK; p += DEC_THREADS) {
                 if (P.topk_idx_out) P.topk_idx_out[p] = s_idx[p];
                 if (P.topk_w_out) P.topk_w_out[p] = s_w[p];
+                if (P.heat) atomicAdd(&P.heat[s_idx[p]], 1);  // routing heat (integer adds: any order)
             }
         }
     } else {
@@ -880,8 +881,8 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
                 us += *(const float *)(smem + P.lds_chunk + (uu & 7) * P.chunk_stride + ((uu >> 3) * 256 + m * 16 + n) * 4);
             }
             const int tk = shared_slot ? m : div_k(s_sorted[s_slot_start[s] + m]);
-            const float ti = s_tinv[tk];
-            const float gv = gs * ti, uv = us * ti;
+            const int tsc = s_tsc[tk];
+            const float gv = ldexpf(gs, -tsc), uv = ldexpf(us, -tsc);
             const float h = gv / (1.0f + expf(-gv)) * uv;
             const int f = ((tl << lg_nfgT) + fl) * 16 + n;
             int pg, pe;
@@ -917,8 +918,8 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             uint32_t spins = 0;
             while (ld_dev_u32(cnt) < (uint32_t)n_slots) {
                 __builtin_amdgcn_s_sleep(2);
-                if (++spins > DEC_SPIN_LIMIT || (ld_dev_u32(P.err) & 1u)) {
-                    atomicOr(P.err, 1u);
+                if (++spins > DEC_SPIN_LIMIT || call_timed_out(P.err, tag)) {
+                    note_timeout(P.err, tag);
                     break;
                 }
             }
@@ -949,7 +950,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
                     if (i < nw) {
                         for (uint32_t spins = 0; (uint32_t)(wd[q] >> 32) != tag; ++spins) {
                             if (spins > DEC_SPIN_LIMIT) {
-                                atomicOr(P.err, 1u);
+                                note_timeout(P.err, tag);
                                 break;
                             }
                             __builtin_amdgcn_s_sleep(1);
@@ -1015,8 +1016,8 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
                 uint32_t spins = 0;
                 while (ld_dev_u32(&P.gu_count[s * DEC_CSTRIDE]) < need) {
                     __builtin_amdgcn_s_sleep(2);
-                    if (++spins > DEC_SPIN_LIMIT || (ld_dev_u32(P.err) & 1u)) {
-                        atomicOr(P.err, 1u);
+                    if (++spins > DEC_SPIN_LIMIT || call_timed_out(P.err, tag)) {
+                        note_timeout(P.err, tag);
                         break;
                     }
                 }
@@ -1053,7 +1054,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
                         for (int e = 0; e < 8; ++e) ok = ok && (uint32_t)(wd[q][e] >> 32) == tag;
                         if (ok) break;
                         if (spins > DEC_SPIN_LIMIT) {
-                            atomicOr(P.err, 1u);
+                            note_timeout(P.err, tag);
                             break;
                         }
                         __builtin_amdgcn_s_sleep(1);
@@ -1079,12 +1080,11 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
                     int ex = 0;
                     if (mx > 0.0f) frexpf(mx, &ex);
                     const int sc = mx > 0.0f ? 14 - ex : 0;
-                    const float scale = __builtin_bit_cast(float, (uint32_t)(127 + sc) << 23);
-                    if (gi == 0) s_hinv[m] = __builtin_bit_cast(float, (uint32_t)(127 - sc) << 23);
+                    if (gi == 0) s_hsc[m] = sc;
                     uint32_t h4[4], l4[4];
 #pragma unroll
                     for (int e2 = 0; e2 < 4; ++e2) {
-                        const float v0 = hv[q][2 * e2] * scale, v1 = hv[q][2 * e2 + 1] * scale;
+                        const float v0 = ldexpf(hv[q][2 * e2], sc), v1 = ldexpf(hv[q][2 * e2 + 1], sc);
                         const _Float16 a0 = (_Float16)v0, a1 = (_Float16)v1;
                         h4[e2] = __builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
                         l4[e2] = f2h_bits(v0 - (float)a0) | ((uint32_t)f2h_bits(v1 - (float)a1) << 16);
@@ -1128,7 +1128,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             for (int r = 0; r < 4; ++r) {
                 const int m = 4 * g_lane + r;
                 if (m < n_tok) {
-                    const float o = ov[r] * s_hinv[m];
+                    const float o = ldexpf(ov[r], -s_hsc[m]);
                     if (shared_slot) {
                         st_tagged(P.oll + (size_t)(TK + m) * H + hrow, o, tag);
                     } else {

@@ -198,6 +198,18 @@ __device__ __forceinline__ uint32_t add_dev(uint32_t *p, uint32_t v) {
 __device__ __forceinline__ void store_dev_u32(uint32_t *p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// The error word of a workspace (see DecodeParams::err): bit 0 = a bounded
+// wait ran out, bit 1 = a given grouping was malformed; the bits stay set
+// until the host clears them.  The word after it holds the tag of the last
+// call whose wait ran out: that call's other waits end at once, while later
+// calls (other tags) wait normally.
+__device__ __forceinline__ void note_timeout(uint32_t *err, uint32_t tag) {
+    atomicOr(err, 1u);
+    store_dev_u32(err + 1, tag);
+}
+__device__ __forceinline__ bool call_timed_out(const uint32_t *err, uint32_t tag) {
+    return ld_dev_u32(err + 1) == tag;
+}
 // LDS written by some lanes of a wave, then read by other lanes of it
 __device__ __forceinline__ void wave_lds_handoff() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -84,6 +84,7 @@ struct DecodeParams {
     float *out_shared;         // [T][H]
     int32_t *topk_idx_out;     // may be null
     float *topk_w_out;         // may be null
+    int32_t *heat;             // [E] routing heat, += pairs per expert (ROUTE mode; may be null)
     // Data handed between workgroups is written as 64-bit words (fp32 value in
     // the low half, the call's tag in the high half), so a reader can tell a
     // word of this call from an older one and the writer never has to wait for
@@ -93,7 +94,8 @@ struct DecodeParams {
     uint32_t *gu_count;        // [DEC_MAX_SLOTS * DEC_CSTRIDE]: finished gate/up tasks per slot
     uint32_t *dn_count;        // [DEC_MAX_SLOTS * DEC_CSTRIDE]: finished down tiles per slot
     uint32_t *slice_count;     // [DEC_MAX_SLICES * DEC_CSTRIDE]: finished slots per 128-row slice
-    uint32_t *err;             // error word (bit 0: a wait hit its spin limit; bit 1: bad given grouping)
+    uint32_t *err;             // error word (bit 0: a wait hit its spin limit; bit 1: bad given grouping);
+                               // err[1]: tag of the last call whose wait ran out
     uint32_t *epoch;           // [EPOCH_SLOTS] calls completed on this workspace (the tag source)
     int T, E, k, H, F, Fs;     // Fs = shared ffn (0 = none)
     int bits, x_f32, mode, max_slots;
@@ -123,7 +125,7 @@ struct DecodeParams {
     uint32_t m_E;
     // dynamic LDS layout (byte offsets)
     int lds_idx, lds_w, lds_sorted, lds_hist, lds_slot_start, lds_slot_exp, lds_slot_cnt,
-        lds_tinv, lds_hinv, lds_xmax, lds_misc, lds_xa, lds_chunk, chunk_stride, lds_total;
+        lds_tsc, lds_hsc, lds_xmax, lds_misc, lds_xa, lds_chunk, chunk_stride, lds_total;
 };
 
 // ---------------------------------------------------------------------------
@@ -141,7 +143,7 @@ struct SplitSmall {  // fixed part of the launch's LDS
     int slot_pair[SPL_MAX_SLOTS][SPL_MAX_T];  // pair id of each row in the slot, -1: none
     int plist[SPL_MAX_SLOTS * SPL_MAX_T];     // pairs present (output rows of the per-pair mode)
     uint32_t wmax[8][SPL_MAX_T];  // per wave and row: largest |x| (as bits)
-    float tinv[SPL_MAX_T], hinv[SPL_MAX_T];
+    int tsc[SPL_MAX_T], hsc[SPL_MAX_T];  // per row: the powers of two sc of its integer x and h
     int Sh[SPL_MAX_T];
     int n_slots, n_pl, pad[2];
 };
@@ -160,8 +162,9 @@ struct SplitParams {
     float *out_shared;         // [T][H]
     int32_t *topk_idx_out;     // may be null
     float *topk_w_out;         // may be null
+    int32_t *heat;             // [E] routing heat, += pairs per expert (ROUTE mode; may be null)
     uint64_t *part;            // [T*k + T][ncmax][H] tagged partial down rows per (pair, slice)
-    uint32_t *err, *epoch;     // error word; [EPOCH_SLOTS] calls completed (the tag source)
+    uint32_t *err, *epoch;     // error word (as DecodeParams::err); [EPOCH_SLOTS] calls completed (the tag source)
     int T, E, k, H, F, Fs, bits, mode, x_f32;
     int nc, ncs, ncmax;        // 32-column slices of F and Fs; the partial buffer's stride
     uint32_t m_nc;             // ceil(2^32 / nc) (0 when nc = 1)
@@ -193,6 +196,7 @@ struct GroupParams {
     int32_t *offsets;        // [E+1]
     int32_t *pairs;          // [T*k]
     int32_t *active;         // [E+1]
+    int32_t *heat;           // [E] routing heat, += pairs per expert (may be null)
 };
 
 struct PlanParams {
@@ -218,6 +222,8 @@ struct GemmParams {
     float *out_shared;      // [T][H]
     const int32_t *slot_exp, *slot_row0, *slot_cnt, *slot_hrow0, *prefix;  // prefix[E+2] = #slots
     int T, E, k, H, F, Fs, h_stride, x_f32;
+    int rowG;               // bytes of one gate/up row (H/32 blocks of the gate/up format)
+    size_t eb;              // bytes of one routed expert blob
 };
 
 struct CombineParams {

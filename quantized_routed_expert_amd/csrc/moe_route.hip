@@ -107,7 +107,11 @@ __global__ __launch_bounds__(1024) void k_group_scan(GroupParams P) {
                 run += (int)v[j];
             }
         }
-        if (tot[i] > 0) P.active[1 + abase++] = e;
+        if (tot[i] > 0) {
+            P.active[1 + abase++] = e;
+            // routing heat: this call's pairs of e (integer adds: any order)
+            if (P.heat) atomicAdd(&P.heat[e], tot[i]);
+        }
         base += tot[i];
     }
     if (tid == 1023) {

@@ -433,12 +433,12 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
         const float mx = __builtin_bit_cast(float, mxb);
         int ex = 0;
         if (mx > 0.0f) frexpf(mx, &ex);
+        // (ldexp: exact for any sc, also where 2^sc is not a normal float)
         const int sc = mx > 0.0f ? 14 - ex : 0;
-        const float scale = __builtin_bit_cast(float, (uint32_t)(127 + sc) << 23);
         int ai[8], bs = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            ai[i] = (int)rintf(xv[r][i] * scale);
+            ai[i] = (int)rintf(ldexpf(xv[r][i], sc));
             bs += ai[i];
         }
         if (has_x[r]) {
@@ -447,7 +447,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
                               (uint32_t)(ai[4] & 0xFFFF) | ((uint32_t)ai[5] << 16),
                               (uint32_t)(ai[6] & 0xFFFF) | ((uint32_t)ai[7] << 16)};
             *(u32x4 *)(s_a + xt[r] * H + xk[r]) = pk;
-            if (xk[r] == 0) sm.tinv[xt[r]] = __builtin_bit_cast(float, (uint32_t)(127 - sc) << 23);
+            if (xk[r] == 0) sm.tsc[xt[r]] = sc;
         }
         if (BITS == 3) {
             // block sums: the four threads of a block are consecutive lanes
@@ -552,6 +552,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
         for (int p = lane; p < TK; p += 64) {
             if (P.topk_idx_out) P.topk_idx_out[p] = sm.idx[p];
             if (P.topk_w_out) P.topk_w_out[p] = sm.w[p];
+            if (P.heat) atomicAdd(&P.heat[sm.idx[p]], 1);  // routing heat (integer adds: any order)
         }
     }
     __syncthreads();  // slots, integer activations, block sums
@@ -642,15 +643,15 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
             const int t = wave;
             float h = 0.0f;
             if (lane < 32) {
-                const float ti = sm.tinv[t];
-                const float g = s_gu[t * 64 + lane] * ti, u = s_gu[t * 64 + 32 + lane] * ti;
+                const int tsc = sm.tsc[t];
+                const float g = ldexpf(s_gu[t * 64 + lane], -tsc), u = ldexpf(s_gu[t * 64 + 32 + lane], -tsc);
                 h = g / (1.0f + expf(-g)) * u;
             }
             const float mx = __builtin_bit_cast(float, wave_max_u32(__builtin_bit_cast(uint32_t, fabsf(h))));
             int ex = 0;
             if (mx > 0.0f) frexpf(mx, &ex);
             const int sc = mx > 0.0f ? 14 - ex : 0;
-            const int ah = (int)rintf(h * __builtin_bit_cast(float, (uint32_t)(127 + sc) << 23));
+            const int ah = (int)rintf(ldexpf(h, sc));
             if (lane < 32) s_ah[t * 32 + lane] = (int16_t)ah;
             if (BITS == 3) {
                 int sum = ah;
@@ -658,7 +659,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
                 for (int off = 16; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
                 if (lane == 0) sm.Sh[t] = sum;
             }
-            if (lane == 0) sm.hinv[t] = __builtin_bit_cast(float, (uint32_t)(127 - sc) << 23);
+            if (lane == 0) sm.hsc[t] = sc;
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -680,12 +681,12 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
             if (nxt < n_items) issue_item(nxt, 2);
             const uint8_t *dcol = s_wt + 2 * (size_t)RB;
             int pid[TM];
-            float hinv[TM];
+            int hsc[TM];
             int Sh[TM];
 #pragma unroll
             for (int t = 0; t < TM; ++t) {
                 pid[t] = sm.slot_pair[s][t];
-                hinv[t] = sm.hinv[t];
+                hsc[t] = sm.hsc[t];
                 Sh[t] = BITS == 3 ? sm.Sh[t] : 0;
             }
             // h digits in registers for one or two rows; re-read (LDS broadcast) for more
@@ -713,8 +714,8 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
                     }
                     // partial layout [pair][row / 8][slice][row % 8]: rows 2rp, 2rp+1 adjacent
                     uint64_t *dst = P.part + (((size_t)pid[t] * (H >> 3) + (rp >> 2)) * P.ncmax + c) * 8 + 2 * (rp & 3);
-                    st_tagged(dst, sp.d0 * (float)A0 * hinv[t], tag);
-                    st_tagged(dst + 1, sp.d1 * (float)A1 * hinv[t], tag);
+                    st_tagged(dst, ldexpf(sp.d0 * (float)A0, -hsc[t]), tag);
+                    st_tagged(dst + 1, ldexpf(sp.d1 * (float)A1, -hsc[t]), tag);
                 }
             }
         }
@@ -778,7 +779,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
                 for (int i = 0; i < 4; ++i) ok = ok && (!need[i] || (uint32_t)(wd[i] >> 32) == tag);
                 if (ok) break;
                 if (spins > DEC_SPIN_LIMIT) {
-                    atomicOr(P.err, 1u);
+                    note_timeout(P.err, tag);
                     break;
                 }
                 __builtin_amdgcn_s_sleep(4);

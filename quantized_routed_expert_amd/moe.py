@@ -29,7 +29,12 @@ DECODE_MAX_ROWS = 16
 LAYOUT_ROWS, LAYOUT_PREPARED = 0, 1
 
 EXPORTS = ["moe_version", "moe_status_string", "moe_expert_bytes", "moe_workspace_bytes",
-           "moe_prepare_qweights", "moe_route", "moe_group", "moe_expert_ffn", "moe_layer_forward"]
+           "moe_prepare_qweights", "moe_workspace_error", "moe_route", "moe_group", "moe_expert_ffn",
+           "moe_layer_forward"]
+
+# bits of the workspace error word (moe_workspace_error)
+ERR_WAIT_TIMEOUT = 1
+ERR_BAD_GROUPING = 2
 
 
 class MoeError(RuntimeError):
@@ -64,6 +69,8 @@ def lib():
         L.moe_workspace_bytes.argtypes = [i32] * 7
         L.moe_prepare_qweights.restype = ctypes.c_int
         L.moe_prepare_qweights.argtypes = [ctypes.POINTER(QWeights), vp, i64]
+        L.moe_workspace_error.restype = ctypes.c_int
+        L.moe_workspace_error.argtypes = [vp, i64, ctypes.POINTER(ctypes.c_uint32), i32, i64]
         L.moe_route.restype = ctypes.c_int
         L.moe_route.argtypes = [vp, i32, i32, i32, vp, vp, i64]
         L.moe_group.restype = ctypes.c_int
@@ -73,7 +80,7 @@ def lib():
                                      vp, i64, i64]
         L.moe_layer_forward.restype = ctypes.c_int
         L.moe_layer_forward.argtypes = [vp, i32, vp, i32, i32, ctypes.POINTER(QWeights),
-                                        ctypes.POINTER(QWeights), vp, vp, vp, i32, vp, i64, i64]
+                                        ctypes.POINTER(QWeights), vp, vp, vp, vp, i32, vp, i64, i64]
         _lib = L
     return _lib
 
@@ -144,6 +151,15 @@ def workspace(T, E, k, hidden, ffn, shared_ffn=0, path=PATH_AUTO, device="cuda")
                        device=device)
 
 
+def workspace_error(ws: torch.Tensor, clear: bool = True, stream=None) -> int:
+    """The workspace's device error word (0 after correct calls); waits for
+    the stream and, with clear, resets the word."""
+    v = ctypes.c_uint32(0)
+    _check(lib().moe_workspace_error(_ptr(ws), ws.numel(), ctypes.byref(v), 1 if clear else 0, _stream(stream)),
+           "moe_workspace_error")
+    return int(v.value)
+
+
 def route(logits: torch.Tensor, k: int, topk_idx=None, topk_w=None, stream=None):
     T, E = logits.shape
     if topk_idx is None:
@@ -177,10 +193,13 @@ def expert_ffn(x: torch.Tensor, w: QWeights, offsets, pairs, active, k: int, out
 
 def layer_forward(x: torch.Tensor, logits: torch.Tensor, k: int, routed: QWeights, shared: QWeights | None,
                   y: torch.Tensor, ws: torch.Tensor, topk_idx=None, topk_w=None, path: int = PATH_AUTO,
-                  stream=None):
+                  stream=None, heat=None):
+    """heat: optional int32 [E] device tensor; the call adds its per-expert
+    pair counts to it (routing heat)."""
     T = x.shape[0]
     _check(lib().moe_layer_forward(_ptr(x), _xcode(x), _ptr(logits), T, k, ctypes.byref(routed),
                                    ctypes.byref(shared) if shared is not None else None, _ptr(y),
-                                   _ptr(topk_idx), _ptr(topk_w), path, _ptr(ws), ws.numel(), _stream(stream)),
+                                   _ptr(topk_idx), _ptr(topk_w), _ptr(heat), path, _ptr(ws), ws.numel(),
+                                   _stream(stream)),
            "moe_layer_forward")
     return y

@@ -46,6 +46,7 @@ class DevLayer:
         w = torch.full((T, k), float("nan"), dtype=torch.float32, device=DEV) if want_routing else None
         moe.layer_forward(self.x, self.logits, k, self.routed, self.shared, y, ws, idx, w, path=path)
         torch.cuda.synchronize()
+        assert moe.workspace_error(ws) == 0, "device error word set"
         return (y.cpu().numpy(), None if idx is None else idx.cpu().numpy(),
                 None if w is None else w.cpu().numpy())
 
@@ -57,7 +58,7 @@ def layer_inputs(name: str, T: int, layer: int = 0, seed: int = 0):
 
 def oracle_forward(orc, li: synth.LayerInputs, rows=None):
     cfg = li.cfg
-    return orc.layer_forward(li.x, li.x_code, li.logits, cfg.top_k, cfg.bits, cfg.ffn, li.routed, li.shared,
+    return orc.layer_forward(li.x, li.x_code, li.logits, cfg.top_k, cfg.fmt, cfg.ffn, li.routed, li.shared,
                              s_ffn=cfg.shared_ffn or None, rows=rows)
 
 

@@ -89,7 +89,7 @@ def test_rejects_before_launch(L):
 
     def lf(x=fake, dt=0, lg=fake, T=4, k=2, r=w, s=sh, y=fake, path=0, ws=fake, wsb=big):
         return L.moe_layer_forward(x, dt, lg, T, k, ctypes.byref(r), ctypes.byref(s) if s else None, y, None,
-                                   None, path, ws, wsb, 0)
+                                   None, None, path, ws, wsb, 0)
 
     assert lf(x=None) == moe.MOE_ERR_INVALID_ARG
     assert lf(lg=None) == moe.MOE_ERR_INVALID_ARG
@@ -108,8 +108,12 @@ def test_rejects_before_launch(L):
     assert lf(T=-1) == moe.MOE_ERR_INVALID_ARG
     assert lf(wsb=16) == moe.MOE_ERR_WORKSPACE
     assert lf(T=17, path=moe.PATH_DECODE) == moe.MOE_ERR_UNSUPPORTED
-    # mixed bit widths cannot take the fused decode launch when forced
-    assert lf(s=moe.QWeights(fake, 3, 1, 256, 512, P), path=moe.PATH_DECODE) == moe.MOE_ERR_UNSUPPORTED
+    # a shared expert whose bit width differs from the routed experts' is
+    # refused on every path (each launch reads it in the routed format)
+    for path in (moe.PATH_AUTO, moe.PATH_DECODE, moe.PATH_PREFILL):
+        assert lf(s=moe.QWeights(fake, 3, 1, 256, 512, P), path=path) == moe.MOE_ERR_UNSUPPORTED
+        assert lf(r=moe.QWeights(fake, 3, 8, 256, 512, P), path=path) == moe.MOE_ERR_UNSUPPORTED
+        assert lf(T=40, s=moe.QWeights(fake, 3, 1, 256, 512, P), path=path) == moe.MOE_ERR_UNSUPPORTED
     # T == 0 is a valid empty call: nothing is launched
     assert lf(T=0) == moe.MOE_OK
 
@@ -124,6 +128,17 @@ def test_rejects_before_launch(L):
     assert ef(T=17, path=moe.PATH_DECODE) == moe.MOE_ERR_UNSUPPORTED
     assert ef(wsb=0) == moe.MOE_ERR_WORKSPACE
     assert ef(T=0) == moe.MOE_OK
+
+
+def test_workspace_error_rejects(L):
+    """The error query checks its arguments before touching the device."""
+    from quantized_routed_expert_amd import moe
+    fake = ctypes.c_void_p(0x1000)
+    v = ctypes.c_uint32(7)
+    assert L.moe_workspace_error(None, 1 << 20, ctypes.byref(v), 1, 0) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_workspace_error(fake, 1 << 20, None, 1, 0) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_workspace_error(fake, 64, ctypes.byref(v), 1, 0) == moe.MOE_ERR_WORKSPACE
+    assert v.value == 7  # untouched on error
 
 
 def test_prepare_rejects_before_launch(L):

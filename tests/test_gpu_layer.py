@@ -43,13 +43,14 @@ def test_workload_full(orc, name, T, path):
     _check(orc, layer_inputs(name, T), path)
 
 
-def test_prefill_chunk_sampled(orc):
-    """The 2048-token chunk in the launch configuration the benchmark times;
-    rows sampled (first, last, spread) because the oracle is slow."""
-    print("[layer] prefill T=2048 sampled rows", flush=True)
-    li = layer_inputs("prefill", 2048)
-    rows = np.array([0, 1, 17, 63, 64, 511, 1024, 1500, 2000, 2046, 2047], dtype=np.int32)
-    _check(orc, li, P, rows=rows)
+@pytest.mark.parametrize("layer", [0, 31])
+def test_prefill_chunk_full(orc, layer):
+    """The whole 2048-token chunk (512 experts, top-10, Zipf routing) in the
+    launch configuration the benchmark times, every row and output compared
+    with the oracle (OpenMP over rows)."""
+    print(f"[layer] prefill T=2048 layer={layer}, all rows (oracle on {orc.set_threads(0)} threads)", flush=True)
+    li = synth.layer_inputs(synth.CONFIGS["prefill"], layer=layer, T=2048)
+    _check(orc, li, P)
 
 
 def test_mtp16_other_layers(orc):
