@@ -227,6 +227,28 @@ int moe_layer_forward(const void *x, int32_t x_dtype, const float *logits, int32
                       float *y, int32_t *topk_idx_out, float *topk_w_out, int32_t *heat,
                       int32_t path, void *ws, int64_t ws_bytes, int64_t stream);
 
+/*
+ * moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Arguments and results are those of
+ * moe_layer_forward; the scratch is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES, one per device, held until the process ends
+ * and found once per device (hipGetSymbolAddress on the first call made
+ * with that device current).  The call allocates and frees nothing.
+ * Limit: a call whose workspace (moe_workspace_bytes for its shapes and
+ * path) exceeds MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_WORKSPACE and
+ * launches nothing; every decode window of the five reference shapes fits
+ * (at most about 24 MiB), a 2048-token prefill chunk does not.  Every call
+ * on a device shares that device's array: calls that overlap in time on one
+ * device (other streams, other threads) race and give wrong results; calls
+ * in one stream's order are safe.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+int moe_layer_forward_noalloc(const void *x, int32_t x_dtype, const float *logits, int32_t T,
+                              int32_t k, const moe_qweights *routed, const moe_qweights *shared,
+                              float *y, int32_t *topk_idx_out, float *topk_w_out, int32_t *heat,
+                              int32_t path, int64_t stream);
+
 #ifdef __cplusplus
 }
 #endif

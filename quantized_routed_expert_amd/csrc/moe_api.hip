@@ -711,3 +711,42 @@ int moe_layer_forward(const void *x, int32_t x_dtype, const float *logits, int32
 }
 
 }  // extern "C"
+
+// ----------------------------------------------------------------------------
+// The layer without a caller workspace: its scratch is this array, one copy
+// per device, held until the process ends.  Like every object of static
+// storage duration it starts zeroed, which is what the workspace protocol
+// needs before a first call; every call leaves its counters at zero again.
+// In host code `scratch` names a host-side stand-in: the device address is
+// taken with hipGetSymbolAddress, once per device, and only that is used.
+// ----------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+void *g_scratch_dev[64];  // per device: the device address of `scratch`
+
+int scratch_address(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_DEVICE;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_DEVICE;
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return MOE_OK;
+}
+}  // namespace
+
+extern "C" int moe_layer_forward_noalloc(const void *x, int32_t x_dtype, const float *logits, int32_t T, int32_t k,
+                                         const moe_qweights *routed, const moe_qweights *shared, float *y,
+                                         int32_t *topk_idx_out, float *topk_w_out, int32_t *heat, int32_t path,
+                                         int64_t stream) {
+    void *ws = nullptr;
+    const int rc = scratch_address(&ws);
+    if (rc) return rc;
+    // a call whose workspace would exceed the array is refused (MOE_ERR_WORKSPACE) before any launch
+    return moe_layer_forward(x, x_dtype, logits, T, k, routed, shared, y, topk_idx_out, topk_w_out, heat, path, ws,
+                             (int64_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
+}

@@ -30,7 +30,8 @@ LAYOUT_ROWS, LAYOUT_PREPARED = 0, 1
 
 EXPORTS = ["moe_version", "moe_status_string", "moe_expert_bytes", "moe_workspace_bytes",
            "moe_prepare_qweights", "moe_workspace_error", "moe_route", "moe_group", "moe_expert_ffn",
-           "moe_layer_forward"]
+           "moe_layer_forward", "moe_layer_forward_noalloc"]
+NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 
 # bits of the workspace error word (moe_workspace_error)
 ERR_WAIT_TIMEOUT = 1
@@ -81,6 +82,9 @@ def lib():
         L.moe_layer_forward.restype = ctypes.c_int
         L.moe_layer_forward.argtypes = [vp, i32, vp, i32, i32, ctypes.POINTER(QWeights),
                                         ctypes.POINTER(QWeights), vp, vp, vp, vp, i32, vp, i64, i64]
+        L.moe_layer_forward_noalloc.restype = ctypes.c_int
+        L.moe_layer_forward_noalloc.argtypes = [vp, i32, vp, i32, i32, ctypes.POINTER(QWeights),
+                                                ctypes.POINTER(QWeights), vp, vp, vp, vp, i32, i64]
         _lib = L
     return _lib
 
@@ -202,4 +206,17 @@ def layer_forward(x: torch.Tensor, logits: torch.Tensor, k: int, routed: QWeight
                                    _ptr(topk_idx), _ptr(topk_w), _ptr(heat), path, _ptr(ws), ws.numel(),
                                    _stream(stream)),
            "moe_layer_forward")
+    return y
+
+
+def layer_forward_noalloc(x: torch.Tensor, logits: torch.Tensor, k: int, routed: QWeights,
+                          shared: QWeights | None, y: torch.Tensor, topk_idx=None, topk_w=None,
+                          path: int = PATH_AUTO, stream=None, heat=None):
+    """moe_layer_forward_noalloc: the layer with the library's static device
+    scratch instead of a workspace (nothing is allocated)."""
+    T = x.shape[0]
+    _check(lib().moe_layer_forward_noalloc(_ptr(x), _xcode(x), _ptr(logits), T, k, ctypes.byref(routed),
+                                           ctypes.byref(shared) if shared is not None else None, _ptr(y),
+                                           _ptr(topk_idx), _ptr(topk_w), _ptr(heat), path, _stream(stream)),
+           "moe_layer_forward_noalloc")
     return y
