@@ -144,10 +144,12 @@ class WeightCache:
         out = []
         for l in range(self.layers):
             raw = synth.routed_weights_torch(cfg, l, self.dev)
-            routed_t, routed = moe.prepare_qweights(raw, cfg.bits, cfg.n_experts, cfg.hidden, cfg.ffn)
+            routed_t, routed = moe.prepare_qweights(raw, cfg.bits, cfg.n_experts, cfg.hidden, cfg.ffn,
+                                                    down_bits=cfg.down_bits)
             sh = synth.shared_weights(cfg, l)
             shared_raw = torch.from_numpy(sh).to(self.dev) if sh is not None else None
-            shared_t, shared = (moe.prepare_qweights(shared_raw, cfg.bits, 1, cfg.hidden, cfg.shared_ffn)
+            shared_t, shared = (moe.prepare_qweights(shared_raw, cfg.bits, 1, cfg.hidden, cfg.shared_ffn,
+                                                     down_bits=cfg.down_bits)
                                 if sh is not None else (None, None))
             # the pages' block order of a few layers stays on the host for the oracle
             host = (raw.cpu().numpy(), sh) if l < 4 else None

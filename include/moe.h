@@ -33,6 +33,9 @@
  * (gate, up and down concatenated per expert, thread §三); experts follow
  * each other with no padding.  This is MOE_LAYOUT_ROWS.  The nibble order
  * and the whole 3-bit layout are readings of points the pages leave open.
+ * Gate and up share one bit width (`bits`); down may have its own
+ * (`down_bits`), as the thread's §三 decode table pairs each gate/up format
+ * with a down format (a 2- or 3-bit gate/up with a 4-bit down).
  *
  * The compute calls read MOE_LAYOUT_PREPARED, written once per weight set by
  * moe_prepare_qweights: the same blocks and sizes, gate and up unchanged,
@@ -109,11 +112,12 @@ extern "C" {
 /* Quantized expert weights (host struct; `data` is a device pointer). */
 typedef struct moe_qweights {
     const void *data;   /* (device) n_experts blobs back to back, see above */
-    int32_t bits;       /* 3 or 4 */
+    int32_t bits;       /* 3 or 4: the gate and up projections */
     int32_t n_experts;  /* routed: E; shared: 1 */
     int32_t hidden;     /* H, multiple of 256 */
     int32_t ffn;        /* F, multiple of 256 */
     int32_t layout;     /* MOE_LAYOUT_*; the compute calls take MOE_LAYOUT_PREPARED only */
+    int32_t down_bits;  /* 3 or 4: the down projection; 0 = the same as bits */
 } moe_qweights;
 
 /* Library version (major*100 + minor). */
@@ -122,9 +126,10 @@ int moe_version(void);
 /* Text for a status code; never NULL. */
 const char *moe_status_string(int status);
 
-/* Bytes of one expert blob: 3 * hidden * ffn/32 * (18 or 14); -1 if the
- * arguments are not a valid shape (pure host function). */
-int64_t moe_expert_bytes(int32_t bits, int32_t hidden, int32_t ffn);
+/* Bytes of one expert blob: hidden * ffn/32 * (2 * B(bits) + B(down_bits)),
+ * B = 18 (4-bit) or 14 (3-bit) bytes per block, down_bits 0 = bits; -1 if
+ * the arguments are not a valid format and shape (pure host function). */
+int64_t moe_expert_bytes(int32_t bits, int32_t down_bits, int32_t hidden, int32_t ffn);
 
 /* Workspace bytes needed by moe_layer_forward / moe_expert_ffn for these
  * shapes on `path` (AUTO resolves as the calls do).  shared_ffn = 0 when
@@ -201,9 +206,10 @@ int moe_expert_ffn(const void *x, int32_t x_dtype, int32_t T, const moe_qweights
 /*
  * The whole layer (steps 1-4).  x (device) [T][H] fp32 or bf16; logits
  * (device) fp32 [T][E] with E = routed->n_experts; shared (host struct, may
- * be NULL) with n_experts = 1, the same hidden and the same bits as the
- * routed experts (its ffn may differ; other bits: MOE_ERR_UNSUPPORTED,
- * since every launch reads it as one more slot of the routed format).
+ * be NULL) with n_experts = 1, the same hidden and the same bits and
+ * down_bits as the routed experts (its ffn may differ; other widths:
+ * MOE_ERR_UNSUPPORTED, since every launch reads it as one more slot of the
+ * routed format).
  * Writes y (device) fp32
  * [T][H]:
  *     y_t = (((w_t0 o_t0 + w_t1 o_t1) + ...) + w_t,k-1 o_t,k-1) + s_t

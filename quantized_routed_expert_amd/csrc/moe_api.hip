@@ -16,10 +16,10 @@
 
 namespace moe {
 hipError_t decode_launch(const DecodeParams &P, int grid, hipStream_t st);
-int decode_occupancy(int bits, int x_f32, int lds);
-hipError_t decode_set_lds(int bits, int x_f32, int lds);
+int decode_occupancy(int bg, int bd, int x_f32, int lds);
+hipError_t decode_set_lds(int bg, int bd, int x_f32, int lds);
 hipError_t split_launch(const SplitParams &P, int grid, hipStream_t st);
-hipError_t split_set_lds(int bits, int T, int xf, int lds);
+hipError_t split_set_lds(int bg, int bd, int T, int xf, int lds);
 hipError_t route_launch(const RouteParams &P, hipStream_t st);
 hipError_t group_launch(const GroupParams &P, hipStream_t st);
 }  // namespace moe
@@ -145,9 +145,17 @@ int check_shape(int32_t T, int32_t E, int32_t k, int32_t H, int32_t F) {
     return MOE_OK;
 }
 
+int down_bits_of(const moe_qweights *w) { return w->down_bits ? w->down_bits : w->bits; }
+int block_bytes_of(int bits) { return bits == 4 ? 18 : 14; }
+// bytes of one expert blob: gate and up [F][H] in `bits`, down [H][F] in `dbits`
+size_t expert_bytes_of(int bits, int dbits, int H, int F) {
+    return (size_t)H * (F / 32) * (2 * block_bytes_of(bits) + block_bytes_of(dbits));
+}
+
 int check_weights(const moe_qweights *w, int H, int n_experts) {
     if (!w || !w->data) return MOE_ERR_INVALID_ARG;
     if (w->bits != 3 && w->bits != 4) return MOE_ERR_UNSUPPORTED;
+    if (w->down_bits != 0 && w->down_bits != 3 && w->down_bits != 4) return MOE_ERR_UNSUPPORTED;
     if (w->layout != MOE_LAYOUT_PREPARED) return MOE_ERR_UNSUPPORTED;
     if (w->hidden != H) return MOE_ERR_INVALID_ARG;
     if (n_experts >= 0 && w->n_experts != n_experts) return MOE_ERR_INVALID_ARG;
@@ -174,7 +182,8 @@ int ilog2(int v) {
 // Geometry of the fused decode launch (see DecodeParams); needs T, E, k, H,
 // F, Fs, bits.
 void decode_geometry(DecodeParams &P) {
-    const int bb = P.bits == 4 ? 18 : 14;
+    const int bb = block_bytes_of(P.bits);    // gate/up blocks
+    const int bbd = block_bytes_of(P.dbits);  // down blocks
     P.nkbH = P.H / 32;
     P.cbH = decode_h_chunk_blocks(P.nkbH);
     const int nchH = P.nkbH / P.cbH;
@@ -200,12 +209,12 @@ void decode_geometry(DecodeParams &P) {
         P.fx[i] = fx;
         P.cbF[i] = decode_f_chunk_blocks(nkb);
         P.nchF[i] = nkb / P.cbF[i];
-        // down is column-block-major: a chunk is cbF runs of 16 rows x bb
-        // bytes (one run per 32-column block), H*bb bytes apart
-        P.segF[i] = P.cbF[i] * P.H * bb;  // bytes from one chunk to the next
-        P.rowF[i] = P.H * bb;             // bytes between the runs of a chunk
-        P.rsF[i] = decode_chunk_rstride(16 * bb);
-        P.perF[i] = bb;                   // 16-byte pieces per run
+        // down is column-block-major: a chunk is cbF runs of 16 rows x bbd
+        // bytes (one run per 32-column block), H*bbd bytes apart
+        P.segF[i] = P.cbF[i] * P.H * bbd;  // bytes from one chunk to the next
+        P.rowF[i] = P.H * bbd;             // bytes between the runs of a chunk
+        P.rsF[i] = decode_chunk_rstride(16 * bbd);
+        P.perF[i] = bbd;                   // 16-byte pieces per run
         P.invF[i] = 65536u / (uint32_t)P.perF[i] + 1u;
         P.m_ngrp[i] = magic_div(fx / 8);
     }
@@ -227,7 +236,7 @@ void decode_geometry(DecodeParams &P) {
 int decode_lds_layout(DecodeParams &P, int xparts) {
     const int TK = P.T * P.k;
     const int Fmax = P.F > P.Fs ? P.F : P.Fs;
-    const int bb = P.bits == 4 ? 18 : 14;
+    const int bb = block_bytes_of(P.bits), bbd = block_bytes_of(P.dbits);
     int off = 0;
     auto take = [&](int bytes) {
         int a = off;
@@ -254,10 +263,10 @@ int decode_lds_layout(DecodeParams &P, int xparts) {
     P.lds_xa = take(xa_bytes > ha_bytes ? xa_bytes : ha_bytes);
     // wave-private chunk buffers (also the gate/up unit partials: 2 x 16 x 16 floats)
     int cmax = 16 * decode_chunk_rstride(P.cbH * bb);
-    const int cf = decode_f_chunk_blocks(P.F / 32) * decode_chunk_rstride(16 * bb);
+    const int cf = decode_f_chunk_blocks(P.F / 32) * decode_chunk_rstride(16 * bbd);
     cmax = cf > cmax ? cf : cmax;
     if (P.Fs) {
-        const int cs = decode_f_chunk_blocks(P.Fs / 32) * decode_chunk_rstride(16 * bb);
+        const int cs = decode_f_chunk_blocks(P.Fs / 32) * decode_chunk_rstride(16 * bbd);
         cmax = cs > cmax ? cs : cmax;
     }
     cmax = cmax > 2048 ? cmax : 2048;
@@ -277,7 +286,7 @@ int launch_err(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 // width is at most DEC_MAX_F, the gate/up rows split into 1, 2, 4 or 8 K
 // chunks, and the LDS layout fits one workgroup per CU.
 constexpr int DEC_LDS_BUDGET = 160 * 1024;
-bool decode_fits(int T, int E, int k, int H, int F, int Fs, int bits, int x_dtype) {
+bool decode_fits(int T, int E, int k, int H, int F, int Fs, int bits, int dbits, int x_dtype) {
     const int xf = x_dtype == MOE_DTYPE_F32;
     const int per = xf ? DEC_XG_F32 : DEC_XG_BF16;
     if ((long long)T * (H / 8) > (long long)per * DEC_THREADS) return false;
@@ -292,6 +301,7 @@ bool decode_fits(int T, int E, int k, int H, int F, int Fs, int bits, int x_dtyp
     P.F = F;
     P.Fs = Fs;
     P.bits = bits;
+    P.dbits = dbits;
     P.max_slots = ((T * k < E) ? T * k : E) + 1;
     decode_geometry(P);
     return decode_lds_layout(P, xf ? 2 : 1) <= DEC_LDS_BUDGET;
@@ -301,7 +311,7 @@ bool decode_fits(int T, int E, int k, int H, int F, int Fs, int bits, int x_dtyp
 int split_xps(int /*bits*/) { return 36; }  // digit dwords per pair slot in LDS (both formats)
 
 int split_lds_layout(SplitParams &P) {
-    const int bb = P.bits == 4 ? 18 : 14, xps = split_xps(P.bits);
+    const int bb = block_bytes_of(P.bits), bbd = block_bytes_of(P.dbits), xps = split_xps(P.bits);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t a = off;
@@ -309,7 +319,7 @@ int split_lds_layout(SplitParams &P) {
         return (int)a;
     };
     P.lds_small = take(sizeof(SplitSmall));
-    P.lds_wt = take((size_t)3 * P.H * bb);
+    P.lds_wt = take((size_t)P.H * (2 * bb + bbd));  // an item's gate rows, up rows and down column block
     P.lds_a = P.lds_wt;  // the integer activations live in the item weight area until the items start
     P.lds_S = take((size_t)P.T * (P.H / 32) * 4);
     P.lds_xd = take((size_t)P.T * (P.H / 64) * xps * 4);
@@ -326,7 +336,7 @@ int split_units(int T, int k, int H, int combine, int G) {
     return (int)(((n + G - 1) / G + 7) / 8 * 8);
 }
 
-bool split_fits(int T, int E, int k, int H, int F, int Fs, int bits, int combine, int G) {
+bool split_fits(int T, int E, int k, int H, int F, int Fs, int bits, int dbits, int combine, int G) {
     (void)E;
     if (T < 1 || T > SPL_MAX_T || k > 32 || T * k > 64) return false;
     if (H != 256 && H != 512 && H != 1024 && H != 2048) return false;
@@ -336,12 +346,13 @@ bool split_fits(int T, int E, int k, int H, int F, int Fs, int bits, int combine
     P.T = T;
     P.H = H;
     P.bits = bits;
+    P.dbits = dbits;
     if (split_lds_layout(P) > DEC_LDS_BUDGET) return false;
     // the reduction stages (outputs x terms x (slices + 1)) floats in the item weight area
     const int units = split_units(T, k, H, combine, G);
     const int nterm = combine ? k + 1 : 1;
     const int ncmax = (F > Fs ? F : Fs) / 32;
-    return (long long)units * nterm * (ncmax + 1) * 4 <= (long long)3 * H * (bits == 4 ? 18 : 14);
+    return (long long)units * nterm * (ncmax + 1) * 4 <= (long long)H * (2 * block_bytes_of(bits) + block_bytes_of(dbits));
 }
 
 }  // namespace
@@ -362,9 +373,10 @@ const char *moe_status_string(int status) {
     }
 }
 
-int64_t moe_expert_bytes(int32_t bits, int32_t hidden, int32_t ffn) {
-    if ((bits != 3 && bits != 4) || hidden <= 0 || ffn <= 0 || hidden % 32 || ffn % 32) return -1;
-    return (int64_t)3 * hidden * (ffn / 32) * (bits == 4 ? 18 : 14);
+int64_t moe_expert_bytes(int32_t bits, int32_t down_bits, int32_t hidden, int32_t ffn) {
+    if ((bits != 3 && bits != 4) || (down_bits != 0 && down_bits != 3 && down_bits != 4)) return -1;
+    if (hidden <= 0 || ffn <= 0 || hidden % 32 || ffn % 32) return -1;
+    return (int64_t)expert_bytes_of(bits, down_bits ? down_bits : bits, hidden, ffn);
 }
 
 int64_t moe_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t hidden, int32_t ffn,
@@ -388,22 +400,22 @@ int moe_prepare_qweights(const moe_qweights *src, void *dst, int64_t stream) {
     if (!src || !src->data || !dst) return MOE_ERR_INVALID_ARG;
     if (src->layout != MOE_LAYOUT_ROWS) return MOE_ERR_INVALID_ARG;
     if (src->bits != 3 && src->bits != 4) return MOE_ERR_UNSUPPORTED;
+    if (src->down_bits != 0 && src->down_bits != 3 && src->down_bits != 4) return MOE_ERR_UNSUPPORTED;
     if (src->n_experts <= 0 || src->hidden <= 0 || src->ffn <= 0) return MOE_ERR_INVALID_ARG;
     if (src->n_experts > MOE_MAX_EXPERTS || src->hidden % 256 || src->ffn % 256 || src->hidden > 65536 ||
         src->ffn > 65536)
         return MOE_ERR_UNSUPPORTED;
-    const int64_t eb = moe_expert_bytes(src->bits, src->hidden, src->ffn);
+    const int64_t eb = (int64_t)expert_bytes_of(src->bits, down_bits_of(src), src->hidden, src->ffn);
     const uintptr_t s0 = (uintptr_t)src->data, d0 = (uintptr_t)dst;
     const uintptr_t n = (uintptr_t)eb * (uintptr_t)src->n_experts;
     if (s0 < d0 + n && d0 < s0 + n) return MOE_ERR_INVALID_ARG;  // overlap
-    const int bb = src->bits == 4 ? 18 : 14;
     PrepareParams P;
     P.expert_bytes = (size_t)eb;
-    P.gu_bytes = (size_t)2 * src->ffn * (src->hidden / 32) * bb;
+    P.gu_bytes = (size_t)2 * src->ffn * (src->hidden / 32) * block_bytes_of(src->bits);
     P.n_experts = src->n_experts;
     P.H = src->hidden;
     P.nc = src->ffn / 32;
-    P.bb = bb;
+    P.bb = block_bytes_of(down_bits_of(src));  // the down blocks are what moves
     return launch_err(prepare_launch((const uint8_t *)src->data, (uint8_t *)dst, P, S(stream)));
 }
 
@@ -456,7 +468,8 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
     int rc = dev_info(dv);
     if (rc) return rc;
     const int Fs_ = shared ? shared->ffn : 0;
-    if (split_fits(T, E, k, routed->hidden, routed->ffn, Fs_, routed->bits, (mode & DEC_MODE_COMBINE) ? 1 : 0,
+    const int dbits = down_bits_of(routed);
+    if (split_fits(T, E, k, routed->hidden, routed->ffn, Fs_, routed->bits, dbits, (mode & DEC_MODE_COMBINE) ? 1 : 0,
                    dv.cus)) {
         SplitParams S_;
         memset(&S_, 0, sizeof(S_));
@@ -485,13 +498,15 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
         S_.F = routed->ffn;
         S_.Fs = Fs_;
         S_.bits = routed->bits;
+        S_.dbits = dbits;
+        S_.eb = expert_bytes_of(routed->bits, dbits, routed->hidden, routed->ffn);
         S_.mode = mode | (shared ? DEC_MODE_SHARED : 0);
         S_.x_f32 = x_f32;
         S_.nc = S_.F / 32;
         S_.ncs = Fs_ / 32;
         S_.ncmax = S_.nc > S_.ncs ? S_.nc : S_.ncs;
         S_.m_nc = magic_div(S_.nc);
-        S_.rowH = (S_.H / 32) * (S_.bits == 4 ? 18 : 14);
+        S_.rowH = (S_.H / 32) * block_bytes_of(S_.bits);
         S_.lg_qpr = ilog2(S_.H / 256);
         const int grid = dv.cus;  // one workgroup per CU, all resident
         if (grid > EPOCH_SLOTS) return MOE_ERR_UNSUPPORTED;
@@ -499,12 +514,12 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
         const int lds = split_lds_layout(S_);
         if (lds > dv.lds_max) return MOE_ERR_UNSUPPORTED;
         static std::mutex smu;
-        static int s_lds_set[2][SPL_MAX_T][2] = {};
+        static int s_lds_set[2][2][SPL_MAX_T][2] = {};
         {
             std::lock_guard<std::mutex> lk(smu);
-            int &cur = s_lds_set[S_.bits == 4][T - 1][x_f32 ? 1 : 0];
+            int &cur = s_lds_set[S_.bits == 4][dbits == 4][T - 1][x_f32 ? 1 : 0];
             if (lds > cur) {
-                if (split_set_lds(S_.bits, T, x_f32, lds) != hipSuccess) return MOE_ERR_LAUNCH;
+                if (split_set_lds(S_.bits, dbits, T, x_f32, lds) != hipSuccess) return MOE_ERR_LAUNCH;
                 cur = lds;
             }
         }
@@ -541,6 +556,8 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
     P.F = routed->ffn;
     P.Fs = shared ? shared->ffn : 0;
     P.bits = routed->bits;
+    P.dbits = dbits;
+    P.eb = expert_bytes_of(routed->bits, dbits, routed->hidden, routed->ffn);
     P.x_f32 = x_f32;
     P.mode = mode | (shared ? DEC_MODE_SHARED : 0);
     P.max_slots = ((T * k < E) ? T * k : E) + 1;  // LDS slot tables (counters use the fixed stride)
@@ -549,16 +566,16 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
     const int lds = decode_lds_layout(P, x_f32 ? 2 : 1);
     if (lds > dv.lds_max) return MOE_ERR_UNSUPPORTED;
     static std::mutex mu;
-    static int lds_set[2][2] = {{0, 0}, {0, 0}};
+    static int lds_set[2][2][2] = {};
     int occ;
     {
         std::lock_guard<std::mutex> lk(mu);
-        int &cur = lds_set[P.bits == 4][x_f32 ? 1 : 0];
+        int &cur = lds_set[P.bits == 4][dbits == 4][x_f32 ? 1 : 0];
         if (lds > cur) {
-            if (decode_set_lds(P.bits, x_f32, lds) != hipSuccess) return MOE_ERR_LAUNCH;
+            if (decode_set_lds(P.bits, dbits, x_f32, lds) != hipSuccess) return MOE_ERR_LAUNCH;
             cur = lds;
         }
-        occ = decode_occupancy(P.bits, x_f32, lds);
+        occ = decode_occupancy(P.bits, dbits, x_f32, lds);
     }
     if (occ <= 0) return MOE_ERR_UNSUPPORTED;
     // persistent grid: every workgroup resident (the down tiles wait on
@@ -599,11 +616,14 @@ int prefill_gemms(const void *x, int x_f32, int T, int E, int k, const moe_qweig
     G.Fs = Fs;
     G.h_stride = Fmax;
     G.x_f32 = x_f32;
+    const int dbits = down_bits_of(routed);
+    G.rowG = (G.H / 32) * block_bytes_of(routed->bits);
+    G.eb = expert_bytes_of(routed->bits, dbits, routed->hidden, routed->ffn);
     G.prefix = at<int32_t>(ws, L.prefix_gu);
-    hipError_t e = prefill_gemm_launch(0, routed->bits, G, dv.cus, st);
+    hipError_t e = prefill_gemm_launch(0, routed->bits, G, dv.cus, st);  // gate/up in their format
     if (e != hipSuccess) return MOE_ERR_LAUNCH;
     G.prefix = at<int32_t>(ws, L.prefix_dn);
-    e = prefill_gemm_launch(1, routed->bits, G, dv.cus, st);
+    e = prefill_gemm_launch(1, dbits, G, dv.cus, st);  // down in its own
     return launch_err(e);
 }
 
@@ -624,8 +644,9 @@ int moe_expert_ffn(const void *x, int32_t x_dtype, int32_t T, const moe_qweights
     if (rc) return rc;
     int p = resolve_path(path, T);
     if (p == MOE_PATH_DECODE &&
-        (T > MOE_DECODE_MAX_ROWS || !(split_fits(T, w->n_experts, k, w->hidden, w->ffn, 0, w->bits, 0, 256) ||
-                                      decode_fits(T, w->n_experts, k, w->hidden, w->ffn, 0, w->bits, x_dtype)))) {
+        (T > MOE_DECODE_MAX_ROWS ||
+         !(split_fits(T, w->n_experts, k, w->hidden, w->ffn, 0, w->bits, down_bits_of(w), 0, 256) ||
+           decode_fits(T, w->n_experts, k, w->hidden, w->ffn, 0, w->bits, down_bits_of(w), x_dtype)))) {
         if (path == MOE_PATH_DECODE) return MOE_ERR_UNSUPPORTED;
         p = MOE_PATH_PREFILL;
     }
@@ -663,12 +684,14 @@ int moe_layer_forward(const void *x, int32_t x_dtype, const float *logits, int32
     if (rc) return rc;
     // every launch reads the shared expert as one more slot in the routed
     // experts' format
-    if (shared && shared->bits != routed->bits) return MOE_ERR_UNSUPPORTED;
+    if (shared && (shared->bits != routed->bits || down_bits_of(shared) != down_bits_of(routed)))
+        return MOE_ERR_UNSUPPORTED;
     const int Fs = shared ? shared->ffn : 0;
     int p = resolve_path(path, T);
     if (p == MOE_PATH_DECODE && (T > MOE_DECODE_MAX_ROWS ||
-                                 !(split_fits(T, E, k, H, routed->ffn, Fs, routed->bits, 1, 256) ||
-                                   decode_fits(T, E, k, H, routed->ffn, Fs, routed->bits, x_dtype)))) {
+                                 !(split_fits(T, E, k, H, routed->ffn, Fs, routed->bits, down_bits_of(routed), 1, 256) ||
+                                   decode_fits(T, E, k, H, routed->ffn, Fs, routed->bits, down_bits_of(routed),
+                                               x_dtype)))) {
         if (path == MOE_PATH_DECODE) return MOE_ERR_UNSUPPORTED;
         p = MOE_PATH_PREFILL;
     }

@@ -424,7 +424,9 @@ struct XGroup {
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
-template <int BITS, int XPARTS>
+// BG: bit width of the gate and up projections, BD: of the down projection
+// (per-projection formats, as the thread's §三 decode table pairs them).
+template <int BG, int BD, int XPARTS>
 __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -451,12 +453,12 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
     // ---- gate/up geometry (host-computed): a unit is 16 feature rows x one K
     // chunk of one matrix (one wave); a task is the 8 (or 16) units that
     // complete whole 16-feature groups (one workgroup)
-    constexpr int bb = BITS == 4 ? 18 : 14;
+    constexpr int bbD = BD == 4 ? 18 : 14;  // bytes of a down block
     const int cbH = P.cbH, segH = P.segH, rowH = P.rowH, rsH = P.rsH;
     const int lg_nchH = P.lg_nchH, lg_upt = P.lg_upt, lg_nfgT = P.lg_nfgT, rounds = P.rounds;
     const int nchH = 1 << lg_nchH, upt = 1 << lg_upt, nfgT = 1 << lg_nfgT;
     const int F = P.F, Fs = has_shared ? P.Fs : 0;
-    const size_t eb = (size_t)3 * F * rowH;  // routed expert blob bytes
+    const size_t eb = P.eb;  // routed expert blob bytes
     const int tasks_sh = has_shared ? P.tasks_sh : 0, tasks_rt = P.tasks_rt;
     const int n_lane = lane & 15, g_lane = lane >> 4;
 
@@ -503,7 +505,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
     constexpr int XG = XPARTS == 1 ? DEC_XG_BF16 : DEC_XG_F32;
     const int ngrp_x = T * P.xgrp;
     const int nq = (ngrp_x + DEC_THREADS - 1) / DEC_THREADS;
-    XGroup<BITS, XPARTS> xg[XG];
+    XGroup<BG, XPARTS> xg[XG];
     int xg_t[XG], xg_pos[XG];  // token, (4b + g) of each group (-1: none)
     auto issue_x = [&]() {
 #pragma unroll
@@ -514,7 +516,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
                 const int gc = ok ? grp : 0;  // (an in-bounds load for lanes without a group)
                 const int t = (int)__umulhi((uint32_t)gc, P.m_xgrp);
                 const int rem = gc - t * P.xgrp;  // 4 b + g
-                const int base = (rem >> 2) * 32 + (BITS == 4 ? 4 : 8) * (rem & 3);
+                const int base = (rem >> 2) * 32 + (BG == 4 ? 4 : 8) * (rem & 3);
                 xg[q].load((const uint8_t *)P.x + (size_t)t * H * (XPARTS == 1 ? 2 : 4), base);
                 xg_t[q] = ok ? t : -1;
                 xg_pos[q] = rem;
@@ -794,7 +796,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
         t.m_ngrp = i ? P.m_ngrp[1] : P.m_ngrp[0];
         const uint8_t *blob = t.shared ? P.w_shared : P.w_routed + (size_t)s_slot_exp[t.s] * eb;
         // column-block-major down: this wave's 16 rows of column block 0
-        t.rows = blob + (size_t)2 * t.Fx * rowH + (size_t)(t.rg * DEC_DN_ROWS + wave * 16) * bb;
+        t.rows = blob + (size_t)2 * t.Fx * rowH + (size_t)(t.rg * DEC_DN_ROWS + wave * 16) * bbD;
         return t;
     };
     // The first down chunk streams in as soon as the registers are free: here
@@ -848,7 +850,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             // (a register array indexed by rho would be read and written through
             // select chains over all its elements)
             float4v acc = {0.f, 0.f, 0.f, 0.f};
-            chunk_mma<BITS, XPARTS>(acc, s_chunk, rsH, cbH, n_lane, g_lane, ab, 64, T * P.x_rs);
+            chunk_mma<BG, XPARTS>(acc, s_chunk, rsH, cbH, n_lane, g_lane, ab, 64, T * P.x_rs);
             if (rho == 0) accr[0] = acc;
             else accr[1] = acc;
             if (first_task && rho == 0) TRACEW(11);
@@ -886,7 +888,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             const float h = gv / (1.0f + expf(-gv)) * uv;
             const int f = ((tl << lg_nfgT) + fl) * 16 + n;
             int pg, pe;
-            group_slot_of(BITS, f & 31, pg, pe);
+            group_slot_of(BD, f & 31, pg, pe);
             const int fo = (f >> 5) * 32 + pg * 8 + pe;
             const int row = shared_slot ? TK + m : s_slot_start[s] + m;
             st_tagged(P.hll + (size_t)row * P.h_stride + fo, h, tag);
@@ -1117,7 +1119,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
                     c_next = true;
                 }
             }
-            dn_chunk_mma<BITS>(acc, s_chunk, rsF, cbF, n_lane, g_lane, ab + (size_t)ci * cbF * 128);
+            dn_chunk_mma<BD>(acc, s_chunk, rsF, cbF, n_lane, g_lane, ab + (size_t)ci * cbF * 128);
             wave_lds_handoff();
         }
         // o = acc * 2^-sc_m; weighted write per pair
@@ -1157,41 +1159,46 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
 // ---------------------------------------------------------------------------
 // Host-side launcher (called from the C ABI layer)
 // ---------------------------------------------------------------------------
-template <int BITS, int XPARTS>
+template <int BG, int BD, int XPARTS>
 static hipError_t launch_t(const DecodeParams &P, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((k_decode_layer<BITS, XPARTS>), dim3(grid), dim3(DEC_THREADS), P.lds_total, st, P);
+    hipLaunchKernelGGL((k_decode_layer<BG, BD, XPARTS>), dim3(grid), dim3(DEC_THREADS), P.lds_total, st, P);
     return hipGetLastError();
 }
 
-template <int BITS, int XPARTS>
-static int occupancy_t(int lds) {
+template <int BG, int BD, int XPARTS>
+static hipError_t occupancy_t(int lds, int *nb) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(nb, k_decode_layer<BG, BD, XPARTS>, DEC_THREADS, lds);
+}
+
+template <int BG, int BD, int XPARTS>
+static hipError_t set_lds_t(int lds) {
+    return hipFuncSetAttribute((const void *)k_decode_layer<BG, BD, XPARTS>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+}
+
+// compile-time formats (gate/up bits, down bits) and activation parts (1: bf16, 2: fp32)
+#define DECODE_DISPATCH_F(FN, BG, BD, ...) \
+    return xf ? FN<BG, BD, 2>(__VA_ARGS__) : FN<BG, BD, 1>(__VA_ARGS__)
+#define DECODE_DISPATCH(FN, ...)                                             \
+    do {                                                                     \
+        if (bg == 4 && bd == 4) DECODE_DISPATCH_F(FN, 4, 4, __VA_ARGS__);    \
+        if (bg == 3 && bd == 4) DECODE_DISPATCH_F(FN, 3, 4, __VA_ARGS__);    \
+        if (bg == 4 && bd == 3) DECODE_DISPATCH_F(FN, 4, 3, __VA_ARGS__);    \
+        DECODE_DISPATCH_F(FN, 3, 3, __VA_ARGS__);                            \
+    } while (0)
+
+hipError_t decode_launch(const DecodeParams &P, int grid, hipStream_t st) {
+    const int bg = P.bits, bd = P.dbits, xf = P.x_f32;
+    DECODE_DISPATCH(launch_t, P, grid, st);
+}
+
+int decode_occupancy(int bg, int bd, int xf, int lds) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_decode_layer<BITS, XPARTS>, DEC_THREADS, lds) != hipSuccess)
-        return 0;
+    if ([&]() -> hipError_t { DECODE_DISPATCH(occupancy_t, lds, &nb); }() != hipSuccess) return 0;
     return nb;
 }
 
-template <int BITS, int XPARTS>
-static hipError_t set_lds_t(int lds) {
-    return hipFuncSetAttribute((const void *)k_decode_layer<BITS, XPARTS>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               lds);
-}
-
-hipError_t decode_launch(const DecodeParams &P, int grid, hipStream_t st) {
-    if (P.bits == 4) return P.x_f32 ? launch_t<4, 2>(P, grid, st) : launch_t<4, 1>(P, grid, st);
-    return P.x_f32 ? launch_t<3, 2>(P, grid, st) : launch_t<3, 1>(P, grid, st);
-}
-
-int decode_occupancy(int bits, int x_f32, int lds) {
-    if (bits == 4) return x_f32 ? occupancy_t<4, 2>(lds) : occupancy_t<4, 1>(lds);
-    return x_f32 ? occupancy_t<3, 2>(lds) : occupancy_t<3, 1>(lds);
-}
-
-hipError_t decode_set_lds(int bits, int x_f32, int lds) {
-    if (bits == 4) return x_f32 ? set_lds_t<4, 2>(lds) : set_lds_t<4, 1>(lds);
-    return x_f32 ? set_lds_t<3, 2>(lds) : set_lds_t<3, 1>(lds);
-}
-
+hipError_t decode_set_lds(int bg, int bd, int xf, int lds) { DECODE_DISPATCH(set_lds_t, lds); }
 
 #ifdef MOE_PHASE_TRACE
 extern "C" int moe_trace_set(void *buf) {

@@ -98,7 +98,9 @@ struct DecodeParams {
                                // err[1]: tag of the last call whose wait ran out
     uint32_t *epoch;           // [EPOCH_SLOTS] calls completed on this workspace (the tag source)
     int T, E, k, H, F, Fs;     // Fs = shared ffn (0 = none)
-    int bits, x_f32, mode, max_slots;
+    int bits, x_f32, mode, max_slots;  // bits: gate and up projections
+    int dbits;                 // bit width of the down projection
+    size_t eb;                 // bytes of one routed expert blob
     int h_stride;              // words per hll row (Fmax)
     int x_rs, h_rs;            // LDS bytes per token row: activations (one part), staged h (hi + lo)
     // geometry, computed on the host (divisions by values that are not powers
@@ -166,9 +168,11 @@ struct SplitParams {
     uint64_t *part;            // [T*k + T][ncmax][H] tagged partial down rows per (pair, slice)
     uint32_t *err, *epoch;     // error word (as DecodeParams::err); [EPOCH_SLOTS] calls completed (the tag source)
     int T, E, k, H, F, Fs, bits, mode, x_f32;
+    int dbits;                 // bit width of the down projection (bits: gate and up)
+    size_t eb;                 // bytes of one routed expert blob
     int nc, ncs, ncmax;        // 32-column slices of F and Fs; the partial buffer's stride
     uint32_t m_nc;             // ceil(2^32 / nc) (0 when nc = 1)
-    int rowH;                  // bytes of one gate/up row
+    int rowH;                  // bytes of one gate/up row (H/32 blocks of the gate/up format)
     int lg_qpr;                // log2 of the 4-pair pieces per gate/up row (H / 256)
     int units;                 // reduction outputs per workgroup
     // LDS byte offsets

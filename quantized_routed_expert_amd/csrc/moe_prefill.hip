@@ -307,7 +307,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BI
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n_lane = lane & 15;
     const uint32_t g_lane = (uint32_t)(lane >> 4);
-    const size_t rowH = (size_t)(P.H >> 5) * bb;
+    const size_t rowH = (size_t)P.rowG;  // bytes of a gate/up row (the gate/up format's blocks)
     const int hs = P.h_stride;  // h row: hi plane [0, hs), lo plane [hs, 2 hs) (u16)
     // A staging: one chunk per thread = (m-tile, block, k-group, row) of 8 K-elements
     const int a_n = tid & 15, a_g = (tid >> 4) & 3, a_blk = (tid >> 6) & 1, a_m = tid >> 7;
@@ -524,11 +524,9 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_gemm(GemmParams P) {
     __shared__ __align__(16) GemmSmem<MODE, BITS, XP> sm;
     // the slot plan, read once: prefix[ns + 1], then per slot exp, cnt, row0, hrow0
     extern __shared__ __align__(16) int s_plan[];
-    constexpr int bb = BITS == 4 ? 18 : 14;
     const int tid = threadIdx.x;
     const int ns = P.prefix[P.E + 2];
     const int total = P.prefix[ns];
-    const size_t rowH = (size_t)(P.H >> 5) * bb;
     int *s_prefix = s_plan, *s_exp = s_plan + ns + 1, *s_cnt = s_exp + ns, *s_row0 = s_cnt + ns,
         *s_hrow0 = s_row0 + ns;
     for (int i = tid; i <= ns; i += PF_THREADS) s_prefix[i] = P.prefix[i];
@@ -563,7 +561,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_gemm(GemmParams P) {
         ti.nt = local / mtiles;
         ti.r0 = mt * MT;
         ti.nrows = min(MT, ti.cnt - ti.r0);
-        ti.blob = ti.shared_slot ? P.w_shared : P.w_routed + (size_t)e * 3 * ti.Fx * rowH;
+        ti.blob = ti.shared_slot ? P.w_shared : P.w_routed + (size_t)e * P.eb;
         const int row0 = s_row0[lo] + ti.r0;
         const int a_r = 16 * (tid >> 7) + (tid & 15);  // this thread's A row (see gemm_tile)
         ti.a_pair = (MODE == 0 && !ti.shared_slot && (tid >> 7) < ti.mtl && a_r < ti.nrows) ? P.pairs[row0 + a_r] : -1;

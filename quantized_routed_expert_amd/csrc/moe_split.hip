@@ -241,10 +241,14 @@ __device__ __forceinline__ void lds_read_b128(const uint8_t *p, uint32_t (&w)[N]
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
-template <int BITS, int TM, int XF32>
+// BG: bit width of the gate and up projections, BD: of the down projection
+// (per-projection formats, as the thread's §三 decode table pairs them).
+template <int BG, int BD, int TM, int XF32>
 __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
-    using F_ = SFmt<BITS>;
-    constexpr int bb = F_::bb, pb = F_::pb, xpd = F_::xpd, xps = F_::xps;
+    using FG = SFmt<BG>;  // gate/up blocks and the activation digits
+    using FD = SFmt<BD>;  // down blocks and the h digits
+    constexpr int xps = FG::xps;
+    static_assert(FG::xps == FD::xps, "one LDS stride for both digit layouts");
     extern __shared__ __align__(16) uint8_t smem[];
     SplitSmall &sm = *(SplitSmall *)(smem + P.lds_small);
     uint8_t *s_wt = smem + P.lds_wt;                    // item weights: gate rows | up rows | down column
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     uint32_t *s_xd = (uint32_t *)(smem + P.lds_xd);
     float *s_gu = (float *)(smem + P.lds_gu);           // [T][64] gate then up values of the slice
     int16_t *s_ah = (int16_t *)(smem + P.lds_ah);       // [T][32] integer h of the slice
-    uint32_t *s_hd = (uint32_t *)(smem + P.lds_hd);     // [T][xpd] h digits
+    uint32_t *s_hd = (uint32_t *)(smem + P.lds_hd);     // [T][xps] h digits
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = gridDim.x;
@@ -268,12 +272,12 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     const int hs = has_shared ? 1 : 0;
     const bool route_mode = (P.mode & DEC_MODE_ROUTE) != 0;
     const int nc = P.nc, ncs = has_shared ? P.ncs : 0;
-    const int RB = H * bb;              // bytes of each item region
-    const int np = RB >> 4;             // 16-byte pieces per region
+    const int RG = H * FG::bb;          // bytes of an item's gate (and its up) rows: 32 rows of H/32 blocks
+    const int RD = H * FD::bb;          // bytes of an item's down column block: H blocks
     const int npairs = H >> 6;          // pairs per gate/up row
     // gate/up tasks: qpr pieces of 4 consecutive pairs per row (H / 256)
     const int lg_qpr = P.lg_qpr, qpr = 1 << lg_qpr;
-    const size_t eb = (size_t)3 * P.F * P.rowH;
+    const size_t eb = P.eb;             // bytes of a routed expert blob
 
     // ---- item -> (slot, column slice) and its three regions in global memory
     auto item_slot = [&](int it, int &c) {
@@ -294,10 +298,10 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     // wave's data is waited for until the gate/up values are complete, so a
     // wave computes as soon as its own bytes arrive.  Loads complete in issue
     // order: gate/up rows first, then down rows.
-    constexpr int NGU = BITS == 4 ? 9 : 7;  // ceil(8 rows * rowH / 16 / 64) at H = 2048
-    constexpr int ND = BITS == 4 ? 5 : 4;   // ceil(H/8 rows * bb / 16 / 64) at H = 2048
+    constexpr int NGU = BG == 4 ? 9 : 7;    // ceil(8 rows * rowH / 16 / 64) at H = 2048
+    constexpr int ND = BD == 4 ? 5 : 4;     // ceil(H/8 rows * bb / 16 / 64) at H = 2048
     const int npw = (8 * P.rowH) >> 4;      // pieces of a wave's 8 gate/up rows
-    const int npd = (H * bb) >> 7;          // pieces of a wave's H/8 down rows
+    const int npd = (H * FD::bb) >> 7;      // pieces of a wave's H/8 down rows
     u32x4 rw[NGU], rdn[ND];
     // parts: 1 this wave's gate/up rows, 2 its down rows; e: the routed expert, -1: the shared one
     auto issue_item_e = [&](int c, int e, int parts) {
@@ -315,7 +319,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
         }
         __builtin_amdgcn_sched_barrier(0);  // (keep the issue order)
         if (parts & 2) {
-            const uint8_t *d0 = blob + (size_t)2 * Fx * P.rowH + (size_t)c * RB + (size_t)wave * (H >> 3) * bb;
+            const uint8_t *d0 = blob + (size_t)2 * Fx * P.rowH + (size_t)c * RD + (size_t)wave * (H >> 3) * FD::bb;
 #pragma unroll
             for (int i = 0; i < ND; ++i) {
                 const int pc = lane + 64 * i, q = pc < npd ? pc : 0;
@@ -449,7 +453,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
             *(u32x4 *)(s_a + xt[r] * H + xk[r]) = pk;
             if (xk[r] == 0) sm.tsc[xt[r]] = sc;
         }
-        if (BITS == 3) {
+        if (BG == 3) {
             // block sums: the four threads of a block are consecutive lanes
             bs += __builtin_amdgcn_update_dpp(0, bs, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
             bs += __builtin_amdgcn_update_dpp(0, bs, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
@@ -563,13 +567,13 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
 
     // activation digits: (row, pair, nibble-dword) tasks
     {
-        const int ntask = T * npairs * F_::nnd;
+        const int ntask = T * npairs * FG::nnd;
         for (int q = tid; q < ntask; q += SPL_THREADS) {
-            const int t = q / (npairs * F_::nnd);
-            const int r = q - t * npairs * F_::nnd;
-            const int pr = r / F_::nnd, nd = r - pr * F_::nnd;
+            const int t = q / (npairs * FG::nnd);
+            const int r = q - t * npairs * FG::nnd;
+            const int pr = r / FG::nnd, nd = r - pr * FG::nnd;
             const int slot = (pr & 3) * qpr + (pr >> 2);
-            build_digits<BITS>(s_a + t * H + pr * 64, 63, nd, s_xd + ((size_t)t * npairs + slot) * xps);
+            build_digits<BG>(s_a + t * H + pr * 64, 63, nd, s_xd + ((size_t)t * npairs + slot) * xps);
         }
     }
 
@@ -601,23 +605,23 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
 #pragma unroll
                 for (int t = 0; t < TM; ++t) acc[t] = 0.0f;
                 // the piece's 4 pairs (144 or 112 bytes, 16-byte aligned)
-                uint32_t wq[4 * F_::pw];
-                lds_read_b128<4 * F_::pw>(wr + (size_t)r * P.rowH + (size_t)m * 4 * pb, wq);
+                uint32_t wq[4 * FG::pw];
+                lds_read_b128<4 * FG::pw>(wr + (size_t)r * P.rowH + (size_t)m * 4 * FG::pb, wq);
 #pragma unroll
                 for (int pp = 0; pp < 4; ++pp) {
                     const int pr = 4 * m + pp, slot = pp * qpr + m;
-                    uint32_t w[F_::pw];
+                    uint32_t w[FG::pw];
 #pragma unroll
-                    for (int i = 0; i < F_::pw; ++i) w[i] = wq[pp * F_::pw + i];
-                    SPair<BITS> sp;
+                    for (int i = 0; i < FG::pw; ++i) w[i] = wq[pp * FG::pw + i];
+                    SPair<BG> sp;
                     sp.set(w);
 #pragma unroll
                     for (int t = 0; t < TM; ++t) {
                         if (!row_in[t]) continue;  // (uniform over the workgroup)
-                        uint32_t xd[xpd];
-                        lds_read_b128<xpd>((const uint8_t *)(s_xd + ((size_t)t * npairs + slot) * xps), xd);
-                        const int S0 = BITS == 3 ? s_S[t * (H >> 5) + 2 * pr] : 0;
-                        const int S1 = BITS == 3 ? s_S[t * (H >> 5) + 2 * pr + 1] : 0;
+                        uint32_t xd[FG::xpd];
+                        lds_read_b128<FG::xpd>((const uint8_t *)(s_xd + ((size_t)t * npairs + slot) * xps), xd);
+                        const int S0 = BG == 3 ? s_S[t * (H >> 5) + 2 * pr] : 0;
+                        const int S1 = BG == 3 ? s_S[t * (H >> 5) + 2 * pr + 1] : 0;
                         int A0, A1;
                         sp.blocks(xd, S0, S1, A0, A1);
                         acc[t] = fmaf(sp.d0, (float)A0, acc[t]);
@@ -653,7 +657,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
             const int sc = mx > 0.0f ? 14 - ex : 0;
             const int ah = (int)rintf(ldexpf(h, sc));
             if (lane < 32) s_ah[t * 32 + lane] = (int16_t)ah;
-            if (BITS == 3) {
+            if (BD == 3) {
                 int sum = ah;
 #pragma unroll
                 for (int off = 16; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
@@ -663,7 +667,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (lane < F_::nnd) build_digits<BITS>(s_ah + t * 32, 31, lane, s_hd + t * xps);
+            if (lane < FD::nnd) build_digits<BD>(s_ah + t * 32, 31, lane, s_hd + t * xps);
         }
         __syncthreads();  // h digits
         if (my_items == 0) STRACE(5);
@@ -671,7 +675,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
         // down: this wave's H/8 rows of column block c, as row pairs (2 rp, 2 rp + 1);
         // partial rows stored tagged
         {
-            uint8_t *dw = s_wt + 2 * (size_t)RB + (size_t)wave * (H >> 3) * bb;
+            uint8_t *dw = s_wt + 2 * (size_t)RG + (size_t)wave * (H >> 3) * FD::bb;
 #pragma unroll
             for (int i = 0; i < ND; ++i) {
                 const int pc = lane + 64 * i;
@@ -679,7 +683,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
             }
             wave_lds_handoff();
             if (nxt < n_items) issue_item(nxt, 2);
-            const uint8_t *dcol = s_wt + 2 * (size_t)RB;
+            const uint8_t *dcol = s_wt + 2 * (size_t)RG;
             int pid[TM];
             int hsc[TM];
             int Sh[TM];
@@ -687,19 +691,19 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
             for (int t = 0; t < TM; ++t) {
                 pid[t] = sm.slot_pair[s][t];
                 hsc[t] = sm.hsc[t];
-                Sh[t] = BITS == 3 ? sm.Sh[t] : 0;
+                Sh[t] = BD == 3 ? sm.Sh[t] : 0;
             }
             // h digits in registers for one or two rows; re-read (LDS broadcast) for more
             constexpr int HR = TM <= 2 ? TM : 1;
-            uint32_t hd[HR][xpd];
+            uint32_t hd[HR][FD::xpd];
             if constexpr (TM <= 2) {
 #pragma unroll
-                for (int t = 0; t < TM; ++t) lds_read_b128<xpd>((const uint8_t *)(s_hd + t * xps), hd[t]);
+                for (int t = 0; t < TM; ++t) lds_read_b128<FD::xpd>((const uint8_t *)(s_hd + t * xps), hd[t]);
             }
             for (int rp = wave * (H >> 4) + lane; rp < (wave + 1) * (H >> 4); rp += 64) {
-                uint32_t w[F_::pw];
-                lds_read_dwords<F_::pw>(dcol + (size_t)rp * pb, w);
-                SPair<BITS> sp;
+                uint32_t w[FD::pw];
+                lds_read_dwords<FD::pw>(dcol + (size_t)rp * FD::pb, w);
+                SPair<BD> sp;
                 sp.set(w);
 #pragma unroll
                 for (int t = 0; t < TM; ++t) {
@@ -709,7 +713,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
                     if constexpr (TM <= 2) {
                         sp.blocks(hd[t], Sh[t], Sh[t], A0, A1);
                     } else {
-                        lds_read_b128<xpd>((const uint8_t *)(s_hd + t * xps), hd[0]);
+                        lds_read_b128<FD::xpd>((const uint8_t *)(s_hd + t * xps), hd[0]);
                         sp.blocks(hd[0], Sh[t], Sh[t], A0, A1);
                     }
                     // partial layout [pair][row / 8][slice][row % 8]: rows 2rp, 2rp+1 adjacent
@@ -841,36 +845,38 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     if (tid == 0) epoch_advance(P.epoch, __builtin_amdgcn_readfirstlane(tag_v));
 }
 
-template <int BITS, int TM, int XF32>
+template <int BG, int BD, int TM, int XF32>
 static hipError_t split_launch_t(const SplitParams &P, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((k_split_layer<BITS, TM, XF32>), dim3(grid), dim3(SPL_THREADS), P.lds_total, st, P);
+    hipLaunchKernelGGL((k_split_layer<BG, BD, TM, XF32>), dim3(grid), dim3(SPL_THREADS), P.lds_total, st, P);
     return hipGetLastError();
 }
 
-template <int BITS, int TM, int XF32>
+template <int BG, int BD, int TM, int XF32>
 static hipError_t split_attr_t(int lds) {
-    return hipFuncSetAttribute((const void *)k_split_layer<BITS, TM, XF32>,
+    return hipFuncSetAttribute((const void *)k_split_layer<BG, BD, TM, XF32>,
                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
 }
 
-// compile-time row maximum TM: 1, 2 or 4
-#define SPLIT_DISPATCH_B(FN, B, ...)                                                      \
-    do {                                                                                  \
-        if (T == 1) return xf ? FN<B, 1, 1>(__VA_ARGS__) : FN<B, 1, 0>(__VA_ARGS__);     \
-        if (T == 2) return xf ? FN<B, 2, 1>(__VA_ARGS__) : FN<B, 2, 0>(__VA_ARGS__);     \
-        return xf ? FN<B, 4, 1>(__VA_ARGS__) : FN<B, 4, 0>(__VA_ARGS__);                 \
+// compile-time formats (gate/up bits, down bits) and row maximum TM: 1, 2 or 4
+#define SPLIT_DISPATCH_T(FN, BG, BD, ...)                                                        \
+    do {                                                                                         \
+        if (T == 1) return xf ? FN<BG, BD, 1, 1>(__VA_ARGS__) : FN<BG, BD, 1, 0>(__VA_ARGS__);   \
+        if (T == 2) return xf ? FN<BG, BD, 2, 1>(__VA_ARGS__) : FN<BG, BD, 2, 0>(__VA_ARGS__);   \
+        return xf ? FN<BG, BD, 4, 1>(__VA_ARGS__) : FN<BG, BD, 4, 0>(__VA_ARGS__);               \
     } while (0)
-#define SPLIT_DISPATCH(FN, ...)                            \
-    do {                                                   \
-        if (bits == 4) SPLIT_DISPATCH_B(FN, 4, __VA_ARGS__); \
-        SPLIT_DISPATCH_B(FN, 3, __VA_ARGS__);              \
+#define SPLIT_DISPATCH(FN, ...)                                           \
+    do {                                                                  \
+        if (bg == 4 && bd == 4) SPLIT_DISPATCH_T(FN, 4, 4, __VA_ARGS__);  \
+        if (bg == 3 && bd == 4) SPLIT_DISPATCH_T(FN, 3, 4, __VA_ARGS__);  \
+        if (bg == 4 && bd == 3) SPLIT_DISPATCH_T(FN, 4, 3, __VA_ARGS__);  \
+        SPLIT_DISPATCH_T(FN, 3, 3, __VA_ARGS__);                          \
     } while (0)
 
 hipError_t split_launch(const SplitParams &P, int grid, hipStream_t st) {
-    const int bits = P.bits, T = P.T, xf = P.x_f32;
+    const int bg = P.bits, bd = P.dbits, T = P.T, xf = P.x_f32;
     SPLIT_DISPATCH(split_launch_t, P, grid, st);
 }
 
-hipError_t split_set_lds(int bits, int T, int xf, int lds) { SPLIT_DISPATCH(split_attr_t, lds); }
+hipError_t split_set_lds(int bg, int bd, int T, int xf, int lds) { SPLIT_DISPATCH(split_attr_t, lds); }
 
 }  // namespace moe

@@ -47,7 +47,8 @@ class MoeError(RuntimeError):
 class QWeights(ctypes.Structure):
     """moe_qweights: device pointer + format and shape of a set of experts."""
     _fields_ = [("data", ctypes.c_void_p), ("bits", ctypes.c_int32), ("n_experts", ctypes.c_int32),
-                ("hidden", ctypes.c_int32), ("ffn", ctypes.c_int32), ("layout", ctypes.c_int32)]
+                ("hidden", ctypes.c_int32), ("ffn", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("down_bits", ctypes.c_int32)]
 
 
 _lib = None
@@ -65,7 +66,7 @@ def lib():
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_expert_bytes.restype = i64
-        L.moe_expert_bytes.argtypes = [i32, i32, i32]
+        L.moe_expert_bytes.argtypes = [i32, i32, i32, i32]
         L.moe_workspace_bytes.restype = i64
         L.moe_workspace_bytes.argtypes = [i32] * 7
         L.moe_prepare_qweights.restype = ctypes.c_int
@@ -120,25 +121,27 @@ def _xcode(x: torch.Tensor) -> int:
     raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
 
 
-def qweights(data: torch.Tensor, bits: int, n_experts: int, hidden: int, ffn: int, layout: int) -> QWeights:
+def qweights(data: torch.Tensor, bits: int, n_experts: int, hidden: int, ffn: int, layout: int,
+             down_bits: int = 0) -> QWeights:
     """Describe a uint8 device tensor holding n_experts expert blobs in the
-    given block order (LAYOUT_ROWS or LAYOUT_PREPARED)."""
-    return QWeights(ctypes.c_void_p(data.data_ptr()), bits, n_experts, hidden, ffn, layout)
+    given block order (LAYOUT_ROWS or LAYOUT_PREPARED); gate/up in `bits`,
+    down in `down_bits` (0: the same)."""
+    return QWeights(ctypes.c_void_p(data.data_ptr()), bits, n_experts, hidden, ffn, layout, down_bits)
 
 
 def prepare_qweights(data: torch.Tensor, bits: int, n_experts: int, hidden: int, ffn: int, out=None,
-                     stream=None):
+                     stream=None, down_bits: int = 0):
     """Blobs in the pages' row-by-row order (uint8 device tensor) -> a new
     tensor in the order the compute calls read; returns (tensor, QWeights)."""
     if out is None:
         out = torch.empty_like(data)
-    src = QWeights(ctypes.c_void_p(data.data_ptr()), bits, n_experts, hidden, ffn, LAYOUT_ROWS)
+    src = QWeights(ctypes.c_void_p(data.data_ptr()), bits, n_experts, hidden, ffn, LAYOUT_ROWS, down_bits)
     _check(lib().moe_prepare_qweights(ctypes.byref(src), _ptr(out), _stream(stream)), "moe_prepare_qweights")
-    return out, qweights(out, bits, n_experts, hidden, ffn, LAYOUT_PREPARED)
+    return out, qweights(out, bits, n_experts, hidden, ffn, LAYOUT_PREPARED, down_bits)
 
 
-def expert_bytes(bits: int, hidden: int, ffn: int) -> int:
-    return int(lib().moe_expert_bytes(bits, hidden, ffn))
+def expert_bytes(bits: int, hidden: int, ffn: int, down_bits: int = 0) -> int:
+    return int(lib().moe_expert_bytes(bits, down_bits, hidden, ffn))
 
 
 def workspace_bytes(T: int, E: int, k: int, hidden: int, ffn: int, shared_ffn: int = 0,

@@ -29,12 +29,13 @@ class DevLayer:
         self.logits = torch.from_numpy(li.logits).to(DEV)
         # the pages' block order on the host, converted once on the device
         self.routed_t, self.routed = moe.prepare_qweights(torch.from_numpy(li.routed).to(DEV), cfg.bits,
-                                                          cfg.n_experts, cfg.hidden, cfg.ffn)
+                                                          cfg.n_experts, cfg.hidden, cfg.ffn,
+                                                          down_bits=cfg.down_bits)
         self.shared_t = None
         self.shared = None
         if li.shared is not None:
             self.shared_t, self.shared = moe.prepare_qweights(torch.from_numpy(li.shared).to(DEV), cfg.bits, 1,
-                                                              cfg.hidden, cfg.shared_ffn)
+                                                              cfg.hidden, cfg.shared_ffn, down_bits=cfg.down_bits)
 
     def forward(self, path=moe.PATH_AUTO, ws=None, want_routing=True):
         cfg = self.cfg

@@ -50,6 +50,11 @@ def test_expert_bytes(L):
     assert moe.expert_bytes(3, 2048, 512) == 1376256
     assert moe.expert_bytes(5, 2048, 512) == -1
     assert moe.expert_bytes(4, 2047, 512) == -1
+    # per-projection widths: H*F/32 * (2*B_gate/up + B_down)
+    assert moe.expert_bytes(3, 2048, 512, down_bits=4) == 2048 * 16 * (2 * 14 + 18)
+    assert moe.expert_bytes(4, 2048, 768, down_bits=3) == 2048 * 24 * (2 * 18 + 14)
+    assert moe.expert_bytes(3, 2048, 512, down_bits=3) == moe.expert_bytes(3, 2048, 512)
+    assert moe.expert_bytes(3, 2048, 512, down_bits=5) == -1
 
 
 def test_workspace_bytes(L):
@@ -112,6 +117,10 @@ def test_rejects_before_launch(L):
     # refused on every path (each launch reads it in the routed format)
     for path in (moe.PATH_AUTO, moe.PATH_DECODE, moe.PATH_PREFILL):
         assert lf(s=moe.QWeights(fake, 3, 1, 256, 512, P), path=path) == moe.MOE_ERR_UNSUPPORTED
+        # ... and so is one whose down width differs
+        assert lf(s=moe.QWeights(fake, 4, 1, 256, 512, P, 3), path=path) == moe.MOE_ERR_UNSUPPORTED
+        assert lf(r=moe.QWeights(fake, 4, 8, 256, 512, P, 3), path=path) == moe.MOE_ERR_UNSUPPORTED
+        assert lf(r=moe.QWeights(fake, 4, 8, 256, 512, P, 5), path=path) == moe.MOE_ERR_UNSUPPORTED
         assert lf(r=moe.QWeights(fake, 3, 8, 256, 512, P), path=path) == moe.MOE_ERR_UNSUPPORTED
         assert lf(T=40, s=moe.QWeights(fake, 3, 1, 256, 512, P), path=path) == moe.MOE_ERR_UNSUPPORTED
     # T == 0 is a valid empty call: nothing is launched
@@ -163,3 +172,9 @@ def test_prepare_rejects_before_launch(L):
         moe.MOE_ERR_UNSUPPORTED
     assert pf(ctypes.byref(moe.QWeights(fake, 4, 8, 200, 512, 0)), ctypes.c_void_p(0x10000000), 0) == \
         moe.MOE_ERR_UNSUPPORTED
+    assert pf(ctypes.byref(moe.QWeights(fake, 4, 8, 256, 512, 0, 2)), ctypes.c_void_p(0x10000000), 0) == \
+        moe.MOE_ERR_UNSUPPORTED
+    # overlap is judged on the mixed-format size (gate/up 4-bit, down 3-bit)
+    eb_mixed = moe.expert_bytes(4, 256, 512, down_bits=3)
+    assert pf(ctypes.byref(moe.QWeights(fake, 4, 8, 256, 512, 0, 3)), ctypes.c_void_p(0x1000 + 8 * eb_mixed - 2),
+              0) == moe.MOE_ERR_INVALID_ARG
