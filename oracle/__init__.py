@@ -56,6 +56,9 @@ def _bind(lib):
     lib.orc_dequant_block.argtypes = [ctypes.c_int, u8p, f64p]
     lib.orc_dequant_matrix.restype = ctypes.c_int
     lib.orc_dequant_matrix.argtypes = [ctypes.c_int, u8p, ctypes.c_int, ctypes.c_int, f64p]
+    lib.orc_router_logits.restype = ctypes.c_int
+    lib.orc_router_logits.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_int, f64p]
     lib.orc_route.restype = ctypes.c_int
     lib.orc_route.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, i32p, f64p]
     lib.orc_group.restype = ctypes.c_int
@@ -153,7 +156,21 @@ class Oracle:
         d = self.dequant_matrix(bd, blob[2 * mb:], hidden, ffn)
         return g, u, d
 
-    # -- router and grouping ------------------------------------------------
+    # -- router projection, router and grouping ----------------------------
+    def router_logits(self, x: np.ndarray, x_dtype: int, w_router: np.ndarray) -> np.ndarray:
+        """x [T,H] (fp32, or bf16 bits as uint16), w_router [E,H] bf16 bits
+        (uint16) -> logits [T,E] float64."""
+        x = np.ascontiguousarray(x)
+        w = np.ascontiguousarray(w_router, dtype=np.uint16)
+        T, H = x.shape
+        E = w.shape[0]
+        assert w.shape[1] == H
+        out = np.zeros((T, E), dtype=np.float64)
+        rc = self.lib.orc_router_logits(_ptr(x), x_dtype, T, H, _ptr(w), E, _ptr(out, ctypes.c_double))
+        if rc:
+            raise ValueError(f"orc_router_logits rc={rc}")
+        return out
+
     def route(self, logits: np.ndarray, k: int):
         logits = np.ascontiguousarray(logits, dtype=np.float32)
         T, E = logits.shape

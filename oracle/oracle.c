@@ -173,6 +173,40 @@ int orc_dequant_matrix(int bits, const uint8_t *m, int rows, int cols, double *o
 }
 
 /* ------------------------------------------------------------------ */
+/* Router projection: the logits the router ranks                      */
+/* ------------------------------------------------------------------ */
+
+/*
+ * logits[t][e] = sum over h of x[t][h] * W[e][h], W the router matrix
+ * [E][H] in bfloat16 (row e is expert e's router vector), x fp32 or bf16.
+ * Products and the sum in binary64, h ascending.  The step that precedes
+ * the routed path: the extended-strata-moe "Reference", section "Tools"
+ * (route_dump / route_predict read a layer's router from its hidden state),
+ * and the forum thread's post "prefill 36.8 -> 334", section on the decode
+ * wall (one captured graph per window over all 48 layers).
+ */
+int orc_router_logits(const void *x, int x_dtype, int T, int H, const uint16_t *w, int E,
+                      double *logits) {
+    int t;
+    if (T < 0 || H <= 0 || E <= 0 || (x_dtype != 0 && x_dtype != 1)) return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < T; ++t) {
+        int e, h;
+        for (e = 0; e < E; ++e) {
+            const uint16_t *we = w + (int64_t)e * H;
+            double acc = 0.0;
+            for (h = 0; h < H; ++h) {
+                double xv = x_dtype == 0 ? (double)((const float *)x)[(int64_t)t * H + h]
+                                         : orc_bf16_to_double(((const uint16_t *)x)[(int64_t)t * H + h]);
+                acc += xv * orc_bf16_to_double(we[h]);
+            }
+            logits[(int64_t)t * E + e] = acc;
+        }
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
 /* Router: top-k over raw logits, softmax over the k selected           */
 /* ------------------------------------------------------------------ */
 

@@ -32,7 +32,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-TID_X, TID_LOGITS, TID_ROUTED, TID_SHARED, TID_PERM = 0, 1, 2, 3, 4
+TID_X, TID_LOGITS, TID_ROUTED, TID_SHARED, TID_PERM, TID_ROUTER = 0, 1, 2, 3, 4, 5
 
 
 @dataclasses.dataclass(frozen=True)
@@ -317,6 +317,17 @@ def logits(cfg: Config, layer: int, T: int, base_seed: int = 0) -> np.ndarray:
         logp[perm] = np.log(p)
         return (logp[None, :] + rg.gumbel(size=(T, E))).astype(np.float32)
     raise ValueError(kind)
+
+
+def router_weights(cfg: Config, layer: int, base_seed: int = 0) -> np.ndarray:
+    """The router matrix W [E, H] as bf16 bit patterns (uint16): i.i.d.
+    N(0, s / sqrt(H)) with s the logit scale of the recipe (the "normal"
+    sigma, or 1), so that x W^T for x ~ N(0,1) has about the recipe's
+    logit spread."""
+    kind, par = cfg.logits
+    s = float(par) if kind == "normal" else 1.0
+    w = rng(cfg.cid, layer, TID_ROUTER, base_seed).standard_normal((cfg.n_experts, cfg.hidden))
+    return f32_to_bf16_bits((w * (s / np.sqrt(cfg.hidden))).astype(np.float32))
 
 
 @dataclasses.dataclass

@@ -192,6 +192,35 @@ def pin_mixed_expert_indexing(o):
 
 
 # ----------------------------------------------------------------------------
+# router projection
+# ----------------------------------------------------------------------------
+
+def pin_router_logits(o, seed=21):
+    """x W^T against numpy's float64 matrix product (bf16 and fp32 x), exact
+    integers for small integer inputs, and one-hot rows picking W's columns."""
+    rg = np.random.default_rng(seed)
+    T, H, E = 5, 96, 12
+    w = synth.f32_to_bf16_bits((rg.standard_normal((E, H)) * 0.1).astype(np.float32))
+    W = npref.bf16_bits_to_f64(w)
+    for code in (0, 1):
+        xf = rg.standard_normal((T, H)).astype(np.float32)
+        x = xf if code == 0 else synth.f32_to_bf16_bits(xf)
+        got = o.router_logits(x, code, w)
+        ref = npref.x_to_f64(x, code) @ W.T
+        assert np.max(np.abs(got - ref)) <= 1e-13 * np.sqrt(np.mean(ref ** 2)), code
+    # small integers: every product and partial sum is exact in binary64
+    xi = rg.integers(-8, 9, (T, H)).astype(np.float32)
+    wi = synth.f32_to_bf16_bits(rg.integers(-8, 9, (E, H)).astype(np.float32))
+    exact = xi.astype(np.int64) @ npref.bf16_bits_to_f64(wi).astype(np.int64).T
+    assert np.array_equal(o.router_logits(xi, 0, wi), exact.astype(np.float64))
+    # one-hot rows: logits[t][e] = W[e][h_t]
+    hs = rg.integers(0, H, T)
+    oh = np.zeros((T, H), np.float32)
+    oh[np.arange(T), hs] = 1.0
+    assert np.array_equal(o.router_logits(oh, 0, w), W[:, hs].T)
+
+
+# ----------------------------------------------------------------------------
 # router
 # ----------------------------------------------------------------------------
 
@@ -366,6 +395,6 @@ def pin_expert_ffn_matches_layer(o):
 
 ALL_PINS = [pin_half, pin_bf16, pin_blocks, pin_encoder_roundtrip, pin_matrix_indexing,
             pin_numpy_dequant_agrees, pin_expert_bytes, pin_format_bits, pin_mixed_expert_indexing,
-            pin_route_bruteforce, pin_route_ties,
+            pin_router_logits, pin_route_bruteforce, pin_route_ties,
             pin_route_special, pin_group, pin_layer_dense, pin_layer_single_expert,
             pin_layer_zeros, pin_layer_invariances, pin_expert_ffn_matches_layer]

@@ -35,6 +35,8 @@ MUTATIONS = [
     ("down_read_in_gate_up_format", "orc_dequant_matrix(bd, blob + 2 * mat, H, F, ex->down);",
      "orc_dequant_matrix(bg, blob + 2 * mat, H, F, ex->down);"),
     ("format_down_width_ignored", "    if (dn == 0) dn = gu;", "    dn = gu;"),
+    ("router_row_index", "const uint16_t *we = w + (int64_t)e * H;", "const uint16_t *we = w + (int64_t)t * H;"),
+    ("router_bf16_as_half", "acc += xv * orc_bf16_to_double(we[h]);", "acc += xv * orc_half_to_double(we[h]);"),
     ("expert_bytes_uniform", "(2 * orc_block_bytes(bg) + orc_block_bytes(bd))", "(3 * orc_block_bytes(bg))"),
 ]
 
