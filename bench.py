@@ -42,12 +42,16 @@ METRIC = "MoE layer us + expert-weight GB/s at 1-16 decode rows; prefill tok/s"
 # name: (config, rows); the order of the default run (the headline first)
 WORKLOADS = {
     "decode": ("decode", 1),
+    # the decode layer with its router projection (bf16 [E][H]) in the same
+    # captured 48-layer graph: the logits come from x instead of the recipe
+    "decode_router": ("decode", 1),
     "tiny": ("tiny", 4),
     "mtp16": ("mtp16", 16),
     "e512": ("e512", 1),
     "e512x4": ("e512", 4),
     "prefill": ("prefill", 2048),
 }
+ROUTER_WORKLOADS = {"decode_router"}
 
 
 def log(msg: str):
@@ -171,9 +175,11 @@ class WeightCache:
         torch.cuda.empty_cache()
 
 
-def cpu_baseline(orc, cfg, T, wsets, xs, logits, bytes_layer, seconds, path_decode, L):
+def cpu_baseline(orc, cfg, T, wsets, xs, logits, bytes_layer, seconds, path_decode, L, routers=None):
     """The oracle on a bounded sample of the workload, on all cores (OpenMP
-    over rows) and on one; returns the cpu_baseline object."""
+    over rows) and on one; returns the cpu_baseline object.  With routers
+    (bf16 router matrices), each layer evaluation starts from the router
+    projection."""
     nthreads = orc.set_threads(0)
     res = {}
     for leg, nt in (("all_cores", nthreads), ("one_core", 1)):
@@ -184,7 +190,10 @@ def cpu_baseline(orc, cfg, T, wsets, xs, logits, bytes_layer, seconds, path_deco
             while time.time() - t_start < seconds or n_layers == 0:
                 l = n_layers % min(4, L)
                 routed, shared = wsets[l]["host"]
-                orc.layer_forward(xs[l], 0 if cfg.x_dtype == "f32" else 1, logits[l], cfg.top_k, cfg.fmt,
+                lg = logits[l]
+                if routers is not None:
+                    lg = orc.router_logits(xs[l], 0 if cfg.x_dtype == "f32" else 1, routers[l]).astype(np.float32)
+                orc.layer_forward(xs[l], 0 if cfg.x_dtype == "f32" else 1, lg, cfg.top_k, cfg.fmt,
                                   cfg.ffn, routed, shared, s_ffn=cfg.shared_ffn or None)
                 cpu_bytes += bytes_layer[l]
                 n_layers += 1
@@ -226,17 +235,25 @@ def run_workload(name, args, wcache, orc):
 
     # ---- inputs: L independent layers, resident in HBM ------------------------
     wsets = wcache.get(cfg)
-    xs, lgs, layers, bytes_layer = [], [], [], []
+    router = name in ROUTER_WORKLOADS
+    xs, lgs, layers, bytes_layer, routers = [], [], [], [], []
     eb = cfg.expert_bytes
     for l in range(L):
         x = synth.activations(cfg, l, T)
-        lg = synth.logits(cfg, l, T)
         xs.append(x)
-        lgs.append(lg)
         d = dict(wsets[l])
         d["x"] = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if cfg.x_dtype == "bf16"
                   else torch.from_numpy(x)).to(dev)
-        d["logits"] = torch.from_numpy(lg).to(dev)
+        if router:
+            wr = synth.router_weights(cfg, l)
+            routers.append(wr)
+            d["w_router"] = torch.from_numpy(wr.view(np.int16)).view(torch.bfloat16).to(dev)
+            d["logits"] = moe.router_logits(d["x"], d["w_router"])
+            lg = d["logits"].cpu().numpy()
+        else:
+            lg = synth.logits(cfg, l, T)
+            d["logits"] = torch.from_numpy(lg).to(dev)
+        lgs.append(lg)
         d["y"] = torch.empty((T, cfg.hidden), dtype=torch.float32, device=dev)
         bytes_layer.append(distinct_experts(lg, cfg.top_k) * eb + cfg.shared_bytes)
         layers.append(d)
@@ -246,6 +263,8 @@ def run_workload(name, args, wcache, orc):
 
     def one_pass(s):
         for d in layers:
+            if router:
+                moe.router_logits(d["x"], d["w_router"], logits=d["logits"], stream=s)
             moe.layer_forward(d["x"], d["logits"], cfg.top_k, d["routed"], d["shared"], d["y"], ws, path=path,
                               stream=s)
 
@@ -285,7 +304,8 @@ def run_workload(name, args, wcache, orc):
     toks = T * 1000.0 / ms_step  # tokens per second through an L-layer MoE stack
     fl_gu, fl_dn = layer_flops(cfg, T)
     desc = (f"{name}: H={cfg.hidden} E={cfg.n_experts} F={cfg.ffn} top-{cfg.top_k} + shared F={cfg.shared_ffn}, "
-            f"{cfg.bits}-bit block-32, T={T} rows, {L} layers")
+            f"{cfg.bits}-bit block-32, T={T} rows, {L} layers"
+            + (f", bf16 router projection [{cfg.n_experts}][{cfg.hidden}] per layer in the graph" if router else ""))
 
     if path == moe.PATH_DECODE:
         metric_value, unit = gbs, "GB/s"
@@ -301,6 +321,10 @@ def run_workload(name, args, wcache, orc):
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name),
                 "kernel": "k_split_layer" if split else "k_decode_layer", "bytes_per_launch": round(total_bytes / L),
                 "launch_us": round(kern_us, 3)}
+        if router:
+            # the pass holds two launches per layer: the rate covers both
+            roof["kernel"] += " + k_router_logits"
+            roof["router_bytes_per_layer"] = cfg.n_experts * cfg.hidden * 2
         # split: signed 4-bit products (codes x 15-bit integer activations cut
         # into signed radix-16 digits), int32 block sums, fp32 scale and
         # accumulate; matrix-core: f16 MFMA on exact codes and hi+lo activations
@@ -334,7 +358,7 @@ def run_workload(name, args, wcache, orc):
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(orc, cfg, T, wsets, xs, lgs, bytes_layer, args.cpu_seconds,
-                           path == moe.PATH_DECODE, L)
+                           path == moe.PATH_DECODE, L, routers if router else None)
         log(f"{name}: cpu baseline {cpu['value']} {cpu['unit']} on {cpu['cores']} threads, "
             f"{cpu['one_core']['value']} on one")
 

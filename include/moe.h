@@ -164,6 +164,23 @@ int moe_prepare_qweights(const moe_qweights *src, void *dst, int64_t stream);
 int moe_workspace_error(void *ws, int64_t ws_bytes, uint32_t *err_out, int32_t clear, int64_t stream);
 
 /*
+ * Router projection (the step before step 1): logits (device) fp32 [T][E]
+ * = x (device) [T][hidden] (fp32 or bf16, x_dtype) times the transpose of
+ * w_router (device) bf16 [E][hidden] (row e: expert e's router vector):
+ *     logits[t][e] = sum_h x[t][h] * w_router[e][h]
+ * bf16 products exact, fp32 sums (fp32 x enters as bf16 hi + lo, 16
+ * significant bits).  A row's logits do not depend on the other rows, and
+ * the same inputs give the same bits on every run.  The extended-strata-moe
+ * "Reference", section "Tools" (route_dump / route_predict read a layer's
+ * router from its hidden state); in the forum thread's post "prefill 36.8
+ * -> 334", the decode wall is met with one captured graph per window over
+ * all 48 layers: this launch and moe_layer_forward's per layer.
+ * hidden a multiple of 256, at most 4096; E <= MOE_MAX_EXPERTS.
+ */
+int moe_router_logits(const void *x, int32_t x_dtype, int32_t T, int32_t hidden,
+                      const void *w_router, int32_t E, float *logits, int64_t stream);
+
+/*
  * Router (step 1).  logits (device) fp32 [T][E]; writes topk_idx (device)
  * int32 [T][k] and topk_w (device) fp32 [T][k].  Per token the k experts are
  * listed by decreasing logit, an equal logit going to the lower expert id

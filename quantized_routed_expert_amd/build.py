@@ -16,7 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_gfx950.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["moe_api.hip", "moe_route.hip", "moe_decode.hip", "moe_split.hip", "moe_prefill.hip", "moe_prepare.hip"]
+SOURCES = ["moe_api.hip", "moe_route.hip", "moe_decode.hip", "moe_split.hip", "moe_prefill.hip", "moe_prepare.hip",
+           "moe_router.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

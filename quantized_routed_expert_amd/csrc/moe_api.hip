@@ -21,6 +21,7 @@ hipError_t decode_set_lds(int bg, int bd, int x_f32, int lds);
 hipError_t split_launch(const SplitParams &P, int grid, hipStream_t st);
 hipError_t split_set_lds(int bg, int bd, int T, int xf, int lds);
 hipError_t route_launch(const RouteParams &P, hipStream_t st);
+hipError_t router_logits_launch(const RouterParams &P, hipStream_t st);
 hipError_t group_launch(const GroupParams &P, hipStream_t st);
 }  // namespace moe
 
@@ -432,6 +433,21 @@ int moe_workspace_error(void *ws, int64_t ws_bytes, uint32_t *err_out, int32_t c
     }
     *err_out = v;
     return MOE_OK;
+}
+
+int moe_router_logits(const void *x, int32_t x_dtype, int32_t T, int32_t hidden, const void *w_router,
+                      int32_t E, float *logits, int64_t stream) {
+    if (T < 0 || hidden <= 0 || E <= 0) return MOE_ERR_INVALID_ARG;
+    if (x_dtype != MOE_DTYPE_F32 && x_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARG;
+    if (E > MOE_MAX_EXPERTS || hidden % 256 || hidden > 4096) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !logits) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)T > 65535 * 16) return MOE_ERR_UNSUPPORTED;
+    DevInfo dv;
+    const int rc = dev_info(dv);
+    if (rc) return rc;
+    RouterParams P{x, (const uint16_t *)w_router, logits, T, hidden, E, x_dtype == MOE_DTYPE_F32 ? 1 : 0};
+    return launch_err(router_logits_launch(P, S(stream)));
 }
 
 int moe_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *topk_idx, float *topk_w,

@@ -136,6 +136,12 @@ __device__ __forceinline__ uint16_t f2h_bits(float f) {
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
     return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
+// fp32 -> bf16 bit pattern, round to nearest even (finite inputs)
+__device__ __forceinline__ uint16_t f2bf_bits(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
 
 // Orderable key of an fp32 value (larger float -> larger key), -0 == +0.
 __device__ __forceinline__ uint32_t float_key(float v) {

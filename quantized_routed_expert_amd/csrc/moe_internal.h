@@ -193,6 +193,14 @@ struct RouteParams {
     float *w;
 };
 
+// Router projection: logits [T][E] = x [T][H] . W^T, W bf16 [E][H].
+struct RouterParams {
+    const void *x;          // [T][H] fp32 or bf16
+    const uint16_t *w;      // [E][H] bf16
+    float *logits;          // [T][E]
+    int T, H, E, x_f32;
+};
+
 struct GroupParams {
     const int32_t *idx;  // [T][k]
     int T, E, k, nchunks;

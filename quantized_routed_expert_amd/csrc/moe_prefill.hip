@@ -176,11 +176,6 @@ __global__ __launch_bounds__(1024) void k_prefill_plan(PlanParams P) {
     }
 }
 
-__device__ __forceinline__ uint16_t f2bf_bits(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
 
 typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));  // 4-byte aligned 16-byte load
 

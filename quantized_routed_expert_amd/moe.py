@@ -29,7 +29,7 @@ DECODE_MAX_ROWS = 16
 LAYOUT_ROWS, LAYOUT_PREPARED = 0, 1
 
 EXPORTS = ["moe_version", "moe_status_string", "moe_expert_bytes", "moe_workspace_bytes",
-           "moe_prepare_qweights", "moe_workspace_error", "moe_route", "moe_group", "moe_expert_ffn",
+           "moe_prepare_qweights", "moe_workspace_error", "moe_router_logits", "moe_route", "moe_group", "moe_expert_ffn",
            "moe_layer_forward", "moe_layer_forward_noalloc"]
 NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 
@@ -73,6 +73,8 @@ def lib():
         L.moe_prepare_qweights.argtypes = [ctypes.POINTER(QWeights), vp, i64]
         L.moe_workspace_error.restype = ctypes.c_int
         L.moe_workspace_error.argtypes = [vp, i64, ctypes.POINTER(ctypes.c_uint32), i32, i64]
+        L.moe_router_logits.restype = ctypes.c_int
+        L.moe_router_logits.argtypes = [vp, i32, i32, i32, vp, i32, vp, i64]
         L.moe_route.restype = ctypes.c_int
         L.moe_route.argtypes = [vp, i32, i32, i32, vp, vp, i64]
         L.moe_group.restype = ctypes.c_int
@@ -165,6 +167,19 @@ def workspace_error(ws: torch.Tensor, clear: bool = True, stream=None) -> int:
     _check(lib().moe_workspace_error(_ptr(ws), ws.numel(), ctypes.byref(v), 1 if clear else 0, _stream(stream)),
            "moe_workspace_error")
     return int(v.value)
+
+
+def router_logits(x: torch.Tensor, w_router: torch.Tensor, logits=None, stream=None) -> torch.Tensor:
+    """x [T, H] fp32/bf16, w_router [E, H] bf16 (device) -> logits [T, E] fp32."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    if w_router.dtype != torch.bfloat16 or tuple(w_router.shape) != (E, H):
+        raise TypeError("w_router must be a bf16 [E, H] tensor")
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _check(lib().moe_router_logits(_ptr(x), _xcode(x), T, H, _ptr(w_router), E, _ptr(logits), _stream(stream)),
+           "moe_router_logits")
+    return logits
 
 
 def route(logits: torch.Tensor, k: int, topk_idx=None, topk_w=None, stream=None):

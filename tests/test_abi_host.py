@@ -139,6 +139,21 @@ def test_rejects_before_launch(L):
     assert ef(T=0) == moe.MOE_OK
 
 
+def test_router_logits_rejects(L):
+    """The router projection validates on the host before touching a device."""
+    from quantized_routed_expert_amd import moe
+    fake = ctypes.c_void_p(0x1000)
+    rl = L.moe_router_logits
+    assert rl(fake, 1, 4, 250, fake, 8, fake, 0) == moe.MOE_ERR_UNSUPPORTED   # hidden not a multiple of 256
+    assert rl(fake, 1, 4, 8192, fake, 8, fake, 0) == moe.MOE_ERR_UNSUPPORTED  # hidden beyond 4096
+    assert rl(fake, 1, 4, 256, fake, 5000, fake, 0) == moe.MOE_ERR_UNSUPPORTED
+    assert rl(fake, 2, 4, 256, fake, 8, fake, 0) == moe.MOE_ERR_INVALID_ARG   # dtype
+    assert rl(None, 1, 4, 256, fake, 8, fake, 0) == moe.MOE_ERR_INVALID_ARG
+    assert rl(fake, 1, 4, 256, None, 8, fake, 0) == moe.MOE_ERR_INVALID_ARG
+    assert rl(fake, 1, -1, 256, fake, 8, fake, 0) == moe.MOE_ERR_INVALID_ARG
+    assert rl(fake, 1, 0, 256, fake, 8, None, 0) == moe.MOE_OK  # empty: nothing launched
+
+
 def test_workspace_error_rejects(L):
     """The error query checks its arguments before touching the device."""
     from quantized_routed_expert_amd import moe
