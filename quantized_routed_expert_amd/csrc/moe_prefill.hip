@@ -51,7 +51,6 @@ extern "C" int moe_trace_prefill_set(void *buf) {
     } while (0)
 #endif
 
-constexpr int PF_KSB = 2;        // quant blocks per K step
 constexpr int PF_THREADS = 512;  // eight waves
 constexpr int PF_NF_GU = 128;    // features per gate/up tile (8 waves x 16)
 constexpr int PF_NF_DN = 256;    // outputs per down tile (8 waves x 2 x 16)
@@ -273,169 +272,220 @@ __device__ __forceinline__ u32x4 deq_group(const BFields<BITS> &f, uint32_t g) {
     }
 }
 
-template <int MODE, int BITS, int XP>
-struct GemmSmem {
-    uint16_t a[2][XP][4][PF_KSB][4][16][8];  // A, double-buffered: [buf][part][m-tile][block][k-group][row][8]
-    int pair[64];                            // pair id of each tile row (down tiles)
+// ---------------------------------------------------------------------------
+// Grouped GEMM tiles with an LDS ring.
+//
+// A tile is 16*MT rows (MT = 1, 2, 4 by the group's size) x 128 features
+// (gate/up: the gate and the up row of each, 256 weight rows) or 256 outputs
+// (down).  Per K step the workgroup streams the step's weight bytes (256 rows
+// x KS blocks) and its activation pieces into one slot of an NS-slot ring in
+// LDS with direct-to-LDS loads (global_load_lds: no register holds data in
+// flight, so NS - 1 steps of loads stay outstanding whatever their size).
+// Every thread issues the same number of loads per step (LW weight dwords
+// and one 16-byte activation piece; slots past the real data take a copy of
+// a valid dword or piece that nothing reads), so `s_waitcnt vmcnt(L * steps
+// issued after s)` tells a wave that its share of step s has landed, and a
+// plain s_barrier then tells every wave that all shares have (__syncthreads'
+// fence would also wait for the later steps' loads).  One barrier per step.
+//
+// Reads: wave w, lane (n, g) takes k-group g of weight row n of its 16 (gate
+// and up) or 2 x 16 (down, rows of both parities) rows: the dwords of the
+// block pair, from LDS (the four k-group lanes of a row read the same
+// addresses: a broadcast); it dequantizes its k-group into the bf16 B
+// operand (exact codes minus the bias), runs v_mfma_f32_16x16x32_bf16 per
+// m-tile and adds the block's fp16 scale times the product to its fp32
+// accumulators, blocks in K order.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+template <int MODE, int BITS, int XF32>
+struct PfCfg {
+    static constexpr int KS = MODE == 0 ? 2 : 1;   // quant blocks per K step
+    // ring slots: steps in flight + the one computed (fp32 activations are
+    // split on the way into LDS, which waits for every load: two slots)
+    static constexpr int NS = XF32 ? 2 : 4;
+    static constexpr int bb = BITS == 4 ? 18 : 14;
+    // weight dwords per step: gate/up 256 rows x KS blocks (row runs of
+    // KS*bb bytes); down KS column blocks x 256 rows (one run each)
+    static constexpr int STEP_DW = 256 * KS * bb / 4;
+    static constexpr int LW = (STEP_DW + PF_THREADS - 1) / PF_THREADS;  // weight loads per thread per step
+    static constexpr int W_BYTES = LW * PF_THREADS * 4;
+    static constexpr int XP = MODE == 0 ? (XF32 ? 2 : 1) : 2;  // A parts: bf16 x; fp32 x or h as hi + lo
+    static constexpr int A_PIECES = 64 * 4 * KS * XP;          // 16-byte pieces (8 K of one row)
+    static constexpr int A_BYTES = A_PIECES * 16;
+    static constexpr int STAGE = W_BYTES + A_BYTES;
+    static constexpr int RING = NS * STAGE;
+    // dwords of one lane's block pair (7 or 9): gate/up, two blocks of a row;
+    // down, one block of the rows 2i and 2i + 1
+    static constexpr int NW = 2 * bb / 4;
+    static constexpr int L = LW + (XF32 ? 0 : 1);   // direct-to-LDS loads per thread per step
+    static_assert(STEP_DW * 4 == 256 * KS * bb, "whole dwords");
+    static_assert(NW == (BITS == 4 ? 9 : 7) && (MODE == 1 || KS == 2), "a pair is two blocks");
+    static_assert(RING + ((5 * (MOE_MAX_EXPERTS_DEV + 1) + 1) * 4 + 15) / 16 * 16 <= 159 * 1024,
+                  "the ring and the largest slot plan fit one workgroup's LDS");
+    static_assert(A_PIECES == PF_THREADS * (MODE == 0 && XF32 ? 2 : 1), "one piece per thread (two for fp32 x)");
 };
+
+// vmcnt-only wait: expcnt and lgkmcnt at their maxima (not waited on)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+// until at most L * ahead loads of this wave are outstanding (ahead <= 3)
+template <int L>
+__device__ __forceinline__ void wait_vm_steps(int ahead) {
+    if (ahead >= 3) wait_vm<3 * L>();
+    else if (ahead == 2) wait_vm<2 * L>();
+    else if (ahead == 1) wait_vm<L>();
+    else wait_vm<0>();
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0) only
 
 struct TileInfo {
     int slot, cnt, nt, r0, nrows, Fx, hrow0, mtl;
     bool shared_slot;
     const uint8_t *blob;
-    int a_pair;  // this thread's A row: its pair id (gate/up gather), -1 when none
+    int a_pair;  // gate/up: the pair id of this thread's activation row, -1 when none
     int pr64;    // thread tid < 64: pair id of tile row tid, -1 when none
 };
 
-template <int MODE, int BITS, int XP, int MTL>
-__device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BITS, XP> &sm, const TileInfo &ti) {
-    constexpr int NPASS = MODE == 0 ? 2 : 1;       // gate + up / down
-    constexpr int NTW = MODE == 0 ? 1 : 2;         // 16-column n-tiles per wave
-    constexpr int NFT = MODE == 0 ? PF_NF_GU : PF_NF_DN;
-    constexpr int NB = NPASS * NTW;                // weight fragments per lane per block
-    constexpr int bb = BITS == 4 ? 18 : 14;
-    // dwords of one block pair: gate/up, two consecutive blocks of a row;
-    // down, one block of the rows 2i (n-tile 0) and 2i+1 (n-tile 1)
-    constexpr int NW = BITS == 4 ? 9 : 7;
-    constexpr int NRAW = MODE == 0 ? NPASS : PF_KSB;  // pairs per lane per K step
-    constexpr bool XF32 = MODE == 0 && XP == 2;              // fp32 activations, split into bf16 hi + lo
+// Piece tid of a step's activations, layout [part][m][blk][g][n] x 16 bytes:
+// 8 consecutive K (k-group g of block blk) of row 16 m + n.  The pieces a
+// wave's lanes read for one MFMA operand (16 rows n of one (part, m, blk, g))
+// are consecutive: no bank conflicts.
+template <int KS>
+__device__ __forceinline__ void a_piece(int tid, int &part, int &m, int &blk, int &g, int &n) {
+    n = tid & 15;
+    g = (tid >> 4) & 3;
+    const int r = tid >> 6;
+    blk = KS == 2 ? (r & 1) : 0;
+    m = KS == 2 ? (r >> 1) : (r & 3);
+    part = KS == 2 ? 0 : (r >> 2);
+}
+template <int KS>
+__device__ __forceinline__ int a_off(int part, int m, int blk, int g, int n) {
+    return ((((part * 4 + m) * KS + blk) * 4 + g) * 16 + n) * 16;
+}
+
+template <int N>
+__device__ __forceinline__ void lds_dwords(const lds_u8 *p, uint32_t (&w)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) w[i] = *(const lds_u32_t *)(p + 4 * i);
+}
+
+template <int MODE, int BITS, int XF32, int MT>
+__device__ __forceinline__ void gemm_tile(const GemmParams &P, lds_u8 *ring, const int *s_pair,
+                                          const TileInfo &ti) {
+    using C = PfCfg<MODE, BITS, XF32>;
+    constexpr int KS = C::KS, NS = C::NS, LW = C::LW, NW = C::NW, XP = C::XP, L = C::L;
+    constexpr int NPASS = MODE == 0 ? 2 : 1;  // gate + up / down
+    constexpr int NTW = MODE == 0 ? 1 : 2;    // 16-column n-tiles per wave
+    constexpr int NB = NPASS * NTW;           // B fragments per lane per block
+    constexpr int bb = C::bb;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n_lane = lane & 15;
-    const uint32_t g_lane = (uint32_t)(lane >> 4);
-    const size_t rowH = (size_t)P.rowG;  // bytes of a gate/up row (the gate/up format's blocks)
-    const int hs = P.h_stride;  // h row: hi plane [0, hs), lo plane [hs, 2 hs) (u16)
-    // A staging: one chunk per thread = (m-tile, block, k-group, row) of 8 K-elements
-    const int a_n = tid & 15, a_g = (tid >> 4) & 3, a_blk = (tid >> 6) & 1, a_m = tid >> 7;
+    const int g_lane = lane >> 4;
+    const size_t rowG = (size_t)P.rowG;  // bytes of a gate/up row
+    const int hs = P.h_stride;           // h row: hi plane [0, hs), lo plane [hs, 2 hs) (u16)
     const int K = MODE == 0 ? P.H : ti.Fx;
-    const int nks = K / (32 * PF_KSB);
+    const int nks = K / (32 * KS);
 
-    const int a_r = 16 * a_m + a_n;
-    const bool a_st = a_m < MTL;
-    const bool a_ld = a_st && a_r < ti.nrows;
-    size_t a_off = 0;
-    if (a_ld) {
-        if (MODE == 0) {
-            const int t = ti.shared_slot ? ti.r0 + a_r : ti.a_pair / P.k;
-            a_off = (size_t)t * P.H + 32 * a_blk + 8 * a_g;
-        } else {
-            a_off = (size_t)(ti.hrow0 + ti.r0 + a_r) * (2 * hs) + 32 * a_blk + 8 * a_g;
-        }
-    }
-    constexpr int PD = (MODE == 1 && BITS == 4) ? 2 : 3;  // K steps in flight: step s loads at the end of step s - PD
-    auto load_a = [&](int ks, u32x4 (&ra)[2]) {
-        ra[0] = u32x4{0u, 0u, 0u, 0u};
-        ra[1] = u32x4{0u, 0u, 0u, 0u};
-        if (a_ld) {
-            const size_t o = a_off + (size_t)ks * (32 * PF_KSB);
-            if (MODE == 0 && !XF32) {
-                ra[0] = *(const u32x4 *)((const uint16_t *)P.x + o);
-            } else if (XF32) {
-                const u32x4 *src = (const u32x4 *)((const float *)P.x + o);
-                ra[0] = src[0];
-                ra[1] = src[1];
+    // ---- this thread's weight dword slots: byte offsets from the blob at step 0 ----
+    uint32_t woff[LW];
+#pragma unroll
+    for (int i = 0; i < LW; ++i) {
+        const int q = i * PF_THREADS + tid;
+        size_t o = 0;  // (a slot past the step's data: the blob's first dword, never read)
+        if (q < C::STEP_DW) {
+            if (MODE == 0) {
+                const int row = q / NW, j = q - row * NW;  // [256 rows: 128 gate, 128 up][NW dwords]
+                const int f = ti.nt * PF_NF_GU + (row & 127);
+                o = ((row < 128 ? 0 : ti.Fx) + f) * rowG + 4 * j;
             } else {
-                const uint16_t *hb16 = (const uint16_t *)P.hbuf;
-                ra[0] = *(const u32x4 *)(hb16 + o);
-                ra[1] = *(const u32x4 *)(hb16 + o + hs);
+                o = 2 * ti.Fx * rowG + (size_t)ti.nt * PF_NF_DN * bb + 4 * (size_t)q;  // [256 rows][bb bytes]
             }
         }
-    };
-    auto store_a = [&](int buf, const u32x4 (&ra)[2]) {
-        if (!a_st) return;
-        if (XF32) {
-            uint32_t hv[4], lv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float v0 = __builtin_bit_cast(float, i < 2 ? ra[0][2 * i] : ra[1][2 * i - 4]);
-                const float v1 = __builtin_bit_cast(float, i < 2 ? ra[0][2 * i + 1] : ra[1][2 * i - 3]);
-                const uint16_t h0 = f2bf_bits(v0), h1 = f2bf_bits(v1);
-                const uint16_t l0 = f2bf_bits(v0 - bf16_bits_to_float(h0));
-                const uint16_t l1 = f2bf_bits(v1 - bf16_bits_to_float(h1));
-                hv[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                lv[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-            }
-            *(u32x4 *)&sm.a[buf][0][a_m][a_blk][a_g][a_n][0] = u32x4{hv[0], hv[1], hv[2], hv[3]};
-            *(u32x4 *)&sm.a[buf][XP - 1][a_m][a_blk][a_g][a_n][0] = u32x4{lv[0], lv[1], lv[2], lv[3]};
-        } else {
-            *(u32x4 *)&sm.a[buf][0][a_m][a_blk][a_g][a_n][0] = ra[0];
-            if (XP == 2) *(u32x4 *)&sm.a[buf][XP - 1][a_m][a_blk][a_g][a_n][0] = ra[1];
-        }
-    };
-
-    // ---- weight sources of this lane: byte offsets from the tile's blob ----
-    uint32_t woff[NRAW];
-    size_t wstep;  // bytes per K step
-    if (MODE == 0) {
-        const uint32_t g_row = (uint32_t)((ti.nt * NFT + wave * 16 + n_lane) * rowH);
-        woff[0] = g_row;
-        if (NPASS == 2) woff[NPASS - 1] = g_row + (uint32_t)(ti.Fx * rowH);  // up row
-        wstep = (size_t)PF_KSB * bb;
-    } else {
-        // wave w, n-tile t: rows nt*256 + 32 w + 2 n + t (t = row parity); the
-        // pair (2i, 2i+1) of block c sits at (c*H + 2i)*bb
-        const int hp = ti.nt * NFT + 32 * wave + 2 * n_lane;
-        const uint32_t dn = (uint32_t)(2 * ti.Fx * rowH + (size_t)hp * bb);
-#pragma unroll
-        for (int b = 0; b < PF_KSB; ++b) woff[b] = dn + (uint32_t)(b * P.H * bb);
-        wstep = (size_t)PF_KSB * P.H * bb;
+        woff[i] = (uint32_t)o;
     }
-    auto load_w = [&](int ks, uint32_t (&dst)[NRAW][NW]) {
-        const uint8_t *base = ti.blob + (size_t)ks * wstep;
+    const size_t wstep = MODE == 0 ? (size_t)KS * bb : (size_t)KS * P.H * bb;  // blob bytes per K step
+
+    // ---- this thread's activation piece (rows past the tile: row 0's, never stored) ----
+    int ap_part, ap_m, ap_blk, ap_g, ap_n;
+    a_piece<KS>(tid, ap_part, ap_m, ap_blk, ap_g, ap_n);
+    const int a_row = 16 * ap_m + ap_n;
+    const bool a_in = ap_m < MT && a_row < ti.nrows;
+    const uint8_t *a_src;
+    size_t a_step;
+    if (MODE == 0) {
+        int tok = 0;
+        if (ti.shared_slot) tok = ti.r0 + (a_in ? a_row : 0);
+        else tok = a_in ? ti.a_pair / P.k : 0;
+        const size_t el = (size_t)tok * P.H + 32 * ap_blk + 8 * ap_g;
+        a_src = XF32 ? (const uint8_t *)((const float *)P.x + el) : (const uint8_t *)((const uint16_t *)P.x + el);
+        a_step = (size_t)32 * KS * (XF32 ? 4 : 2);
+    } else {
+        const size_t row = (size_t)ti.hrow0 + ti.r0 + (a_in ? a_row : 0);
+        a_src = (const uint8_t *)((const uint16_t *)P.hbuf + row * (2 * hs) + (size_t)ap_part * hs + 8 * ap_g);
+        a_step = (size_t)32 * KS * 2;
+    }
+
+    auto issue = [&](int s) {
+        lds_u8 *st = ring + (s % NS) * C::STAGE;
+        const uint8_t *wb = ti.blob + (size_t)s * wstep;
 #pragma unroll
-        for (int b = 0; b < NRAW; ++b) {
-            const uint32_t *s = (const uint32_t *)(base + woff[b]);
-            const u32x4 v = *(const u32x4a4 *)s;
-            dst[b][0] = v.x;
-            dst[b][1] = v.y;
-            dst[b][2] = v.z;
-            dst[b][3] = v.w;
-            if constexpr (NW == 7) {
-                dst[b][4] = s[4];
-                dst[b][5] = s[5];
-                dst[b][6] = s[6];
-            } else if constexpr (NW == 9) {
-                const u32x4 u = *(const u32x4a4 *)(s + 4);
-                dst[b][4] = u.x;
-                dst[b][5] = u.y;
-                dst[b][6] = u.z;
-                dst[b][7] = u.w;
-                dst[b][8] = s[8];
-            }
-        }
+        for (int i = 0; i < LW; ++i)
+            __builtin_amdgcn_global_load_lds(wb + woff[i], st + 4 * (i * PF_THREADS + 64 * wave), 4, 0, 0);
+        if constexpr (!XF32)
+            __builtin_amdgcn_global_load_lds(a_src + (size_t)s * a_step, st + C::W_BYTES + 16 * 64 * wave, 16, 0, 0);
     };
 
-    float4v acc[NB][MTL];
+    float4v acc[NB][MT];
 #pragma unroll
     for (int a = 0; a < NB; ++a)
 #pragma unroll
-        for (int m = 0; m < MTL; ++m) acc[a][m] = float4v{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < MT; ++m) acc[a][m] = float4v{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int cur, const uint32_t (&rw)[NRAW][NW]) {
+    auto compute = [&](const lds_u8 *st) {
+        const lds_u8 *wsl = st, *asl = st + C::W_BYTES;
+        constexpr int NRAW = MODE == 0 ? NPASS : KS;  // block pairs this lane reads per step
+        uint32_t rw[NRAW][NW];
+        if (MODE == 0) {
 #pragma unroll
-        for (int blk = 0; blk < PF_KSB; ++blk) {
-            bf16x8 av[MTL][XP];
+            for (int p = 0; p < NPASS; ++p) lds_dwords<NW>(wsl + (p * 128 + wave * 16 + n_lane) * (NW * 4), rw[p]);
+        } else {
+            // rows o, o + 1 (o = 32 w + 2 n) of block b: 2 * bb bytes from o * bb (a multiple of 4)
 #pragma unroll
-            for (int m = 0; m < MTL; ++m)
+            for (int b = 0; b < KS; ++b) lds_dwords<NW>(wsl + b * 256 * bb + (wave * 32 + 2 * n_lane) * bb, rw[b]);
+        }
 #pragma unroll
-                for (int x = 0; x < XP; ++x) av[m][x] = *(const bf16x8 *)&sm.a[cur][x][m][blk][g_lane][n_lane][0];
+        for (int blk = 0; blk < KS; ++blk) {
+            bf16x8 av[MT][XP];
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int x = 0; x < XP; ++x)
+                    av[m][x] = __builtin_bit_cast(bf16x8, *(const lds_u32x4 *)(asl + a_off<KS>(x, m, blk, g_lane, n_lane)));
 #pragma unroll
             for (int f = 0; f < NB; ++f) {
                 // fragment f: gate/up pass f, or down n-tile f (row parity f)
                 BFields<BITS> fl;
                 if (MODE == 0) fl = block_fields<BITS>(rw[f], blk == 1, BITS == 4 ? 4 : 3);
                 else fl = block_fields<BITS>(rw[blk], f == 1, BITS == 4 ? 4 : 3);
-                const bf16x8 bq = __builtin_bit_cast(bf16x8, deq_group<BITS>(fl, g_lane));
+                const bf16x8 bq = __builtin_bit_cast(bf16x8, deq_group<BITS>(fl, (uint32_t)g_lane));
                 const float d = half_bits_to_float(fl.d);
                 // the m-tiles' MFMAs issue back to back, then their scaling
-                float4v dd[MTL];
+                float4v dd[MT];
 #pragma unroll
-                for (int m = 0; m < MTL; ++m) {
+                for (int m = 0; m < MT; ++m) {
                     const float4v z = {0.f, 0.f, 0.f, 0.f};
                     dd[m] = mfma16bf(av[m][0], bq, z);
                     if (XP == 2) dd[m] = mfma16bf(av[m][XP - 1], bq, dd[m]);
                 }
 #pragma unroll
-                for (int m = 0; m < MTL; ++m) {
+                for (int m = 0; m < MT; ++m) {
                     acc[f][m].x = fmaf(d, dd[m].x, acc[f][m].x);
                     acc[f][m].y = fmaf(d, dd[m].y, acc[f][m].y);
                     acc[f][m].z = fmaf(d, dd[m].z, acc[f][m].z);
@@ -445,42 +495,49 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BI
         }
     };
 
-    // ring of PD steps in registers (static slots: the step loop is unrolled by PD)
-    uint32_t rw[PD][NRAW][NW];
-    u32x4 ra[PD][2];
+    // ---- the K loop: NS - 1 steps of loads ahead of the one computed ----
+    for (int u = 0; u < NS - 1 && u < nks; ++u) issue(u);
+    for (int s = 0; s < nks; ++s) {
+        lds_u8 *st = ring + (s % NS) * C::STAGE;
+        if constexpr (XF32) {
+            // fp32 activations: this thread's 8 values, split into bf16 hi + lo
+            // pieces here (the slot's previous reader finished NS - 1 steps ago)
+            const u32x4 *src = (const u32x4 *)(a_src + (size_t)s * a_step);
+            const u32x4 r0 = src[0], r1 = src[1];
+            wait_vm<0>();
+            const uint32_t v[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+            uint32_t hv[4], lv[4];
 #pragma unroll
-    for (int u = 0; u < PD; ++u) {
-        if (u < nks) {
-            load_a(u, ra[u]);
-            load_w(u, rw[u]);
-        }
-    }
-    store_a(0, ra[0]);
-    __syncthreads();
-    for (int k0 = 0; k0 < nks; k0 += PD) {
-#pragma unroll
-        for (int u = 0; u < PD; ++u) {
-            const int ks = k0 + u;
-            if (ks < nks) {
-                compute(ks & 1, rw[u]);
-                if (ks + 1 < nks) store_a((ks + 1) & 1, ra[(u + 1) % PD]);
-                if (ks + PD < nks) {
-                    load_a(ks + PD, ra[u]);
-                    load_w(ks + PD, rw[u]);
-                }
-                __syncthreads();
+            for (int i = 0; i < 4; ++i) {
+                const float v0 = __builtin_bit_cast(float, v[2 * i]), v1 = __builtin_bit_cast(float, v[2 * i + 1]);
+                const uint16_t h0 = f2bf_bits(v0), h1 = f2bf_bits(v1);
+                const uint16_t l0 = f2bf_bits(v0 - bf16_bits_to_float(h0));
+                const uint16_t l1 = f2bf_bits(v1 - bf16_bits_to_float(h1));
+                hv[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                lv[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
             }
+            lds_u8 *asl = st + C::W_BYTES;
+            *(lds_u32x4 *)(asl + a_off<KS>(0, ap_m, ap_blk, ap_g, ap_n)) = u32x4{hv[0], hv[1], hv[2], hv[3]};
+            *(lds_u32x4 *)(asl + a_off<KS>(1, ap_m, ap_blk, ap_g, ap_n)) = u32x4{lv[0], lv[1], lv[2], lv[3]};
+            wait_lgkm0();
+        } else {
+            wait_vm_steps<L>(min(NS - 2, nks - 1 - s));
         }
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        if (s + NS - 1 < nks) issue(s + NS - 1);
+        compute(st);
     }
+
     // ---- epilogue ----
 #pragma unroll
-    for (int m = 0; m < MTL; ++m) {
+    for (int m = 0; m < MT; ++m) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int rr = m * 16 + 4 * (int)g_lane + r;
+            const int rr = m * 16 + 4 * g_lane + r;
             if (rr >= ti.nrows) continue;
             if (MODE == 0) {
-                const int col = ti.nt * NFT + wave * 16 + n_lane;  // feature
+                const int col = ti.nt * PF_NF_GU + wave * 16 + n_lane;  // feature
                 const float g = acc[0][m][r], u = acc[NPASS - 1][m][r];
                 const float h = g * u * __frcp_rn(1.0f + __expf(-g));
                 const uint16_t hh = f2bf_bits(h);
@@ -489,13 +546,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BI
                 dst[0] = hh;
                 dst[hs] = hl;
             } else {
-                const int pr = sm.pair[rr];
+                const int pr = s_pair[rr];
                 const float wgt = (ti.shared_slot || !P.pair_w) ? 1.0f : P.pair_w[pr];
                 float *orow = ti.shared_slot ? P.out_shared + (size_t)(ti.r0 + rr) * P.H
                                              : P.out_pairs + (size_t)pr * P.H;
 #pragma unroll
                 for (int t = 0; t < NTW; ++t)
-                    orow[ti.nt * NFT + 32 * wave + 2 * n_lane + t] = wgt * acc[t][m][r];
+                    orow[ti.nt * PF_NF_DN + 32 * wave + 2 * n_lane + t] = wgt * acc[t][m][r];
             }
         }
     }
@@ -503,20 +560,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, GemmSmem<MODE, BI
 
 // ---------------------------------------------------------------------------
 // Grouped GEMM: persistent workgroups walk the tile list (slots by decreasing
-// row count; within a slot, m-tiles of one 64-output n-tile are consecutive).
-// Tile: 16*mtl rows (mtl = 1, 2, 4 by the group's size) x 128 features
-// (gate/up) or 256 outputs (down), K in steps of two quant blocks.  Eight
-// waves; wave w owns 16 features (gate/up: the gate and the up row of each)
-// or 32 output rows (down) and dequantizes exactly the B fragments of its
-// own MFMAs in registers: lane (n, g) holds k-group g of
-// weight row n, as v_mfma_f32_16x16x32_bf16 expects.  A (activations, or h
-// as bf16 hi + lo) goes through LDS, double-buffered: one barrier per K step,
-// and the next step's A and weight loads are in flight during this step's
-// math.
+// row count; within a slot, m-tiles of one n-tile are consecutive).  Dynamic
+// LDS: the slot plan (read once), then the ring.
 // ---------------------------------------------------------------------------
-template <int MODE, int BITS, int XP>
+__host__ __device__ constexpr int pf_plan_bytes(int E) { return (((5 * (E + 1) + 1) * 4) + 15) / 16 * 16; }
+
+template <int MODE, int BITS, int XF32>
 __global__ __launch_bounds__(PF_THREADS) void k_prefill_gemm(GemmParams P) {
-    __shared__ __align__(16) GemmSmem<MODE, BITS, XP> sm;
+    __shared__ int s_pair[64];  // pair id of each tile row (down tiles)
     // the slot plan, read once: prefix[ns + 1], then per slot exp, cnt, row0, hrow0
     extern __shared__ __align__(16) int s_plan[];
     const int tid = threadIdx.x;
@@ -524,6 +575,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_gemm(GemmParams P) {
     const int total = P.prefix[ns];
     int *s_prefix = s_plan, *s_exp = s_plan + ns + 1, *s_cnt = s_exp + ns, *s_row0 = s_cnt + ns,
         *s_hrow0 = s_row0 + ns;
+    lds_u8 *ring = (lds_u8 *)s_plan + pf_plan_bytes(P.E);
     for (int i = tid; i <= ns; i += PF_THREADS) s_prefix[i] = P.prefix[i];
     for (int i = tid; i < ns; i += PF_THREADS) {
         s_exp[i] = P.slot_exp[i];
@@ -558,7 +610,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_gemm(GemmParams P) {
         ti.nrows = min(MT, ti.cnt - ti.r0);
         ti.blob = ti.shared_slot ? P.w_shared : P.w_routed + (size_t)e * P.eb;
         const int row0 = s_row0[lo] + ti.r0;
-        const int a_r = 16 * (tid >> 7) + (tid & 15);  // this thread's A row (see gemm_tile)
+        const int a_r = 16 * (tid >> 7) + (tid & 15);  // this thread's activation row (gate/up pieces)
         ti.a_pair = (MODE == 0 && !ti.shared_slot && (tid >> 7) < ti.mtl && a_r < ti.nrows) ? P.pairs[row0 + a_r] : -1;
         ti.pr64 = (tid < 64 && tid < ti.nrows && !ti.shared_slot) ? P.pairs[row0 + tid] : -1;
     };
@@ -570,12 +622,13 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill_gemm(GemmParams P) {
         TileInfo nxt;
         const bool more = tile + (int)gridDim.x < total;
         if (more) tile_info(tile + gridDim.x, nxt);
-        __syncthreads();  // the previous tile's epilogue is done with sm.pair
-        if (tid < 64) sm.pair[tid] = cur.pr64;
+        __syncthreads();  // the previous tile is done with the ring and s_pair
+        if (tid < 64) s_pair[tid] = cur.pr64;
+        __syncthreads();
         PTRACE(((size_t)MODE << 20) + 4 * (size_t)tile, __builtin_amdgcn_s_memrealtime());
-        if (cur.mtl == 4) gemm_tile<MODE, BITS, XP, 4>(P, sm, cur);
-        else if (cur.mtl == 2) gemm_tile<MODE, BITS, XP, 2>(P, sm, cur);
-        else gemm_tile<MODE, BITS, XP, 1>(P, sm, cur);
+        if (cur.mtl == 4) gemm_tile<MODE, BITS, XF32, 4>(P, ring, s_pair, cur);
+        else if (cur.mtl == 2) gemm_tile<MODE, BITS, XF32, 2>(P, ring, s_pair, cur);
+        else gemm_tile<MODE, BITS, XF32, 1>(P, ring, s_pair, cur);
         PTRACE(((size_t)MODE << 20) + 4 * (size_t)tile + 1, __builtin_amdgcn_s_memrealtime());
         PTRACE(((size_t)MODE << 20) + 4 * (size_t)tile + 2, (uint64_t)cur.mtl);
         PTRACE(((size_t)MODE << 20) + 4 * (size_t)tile + 3, (uint64_t)blockIdx.x);
@@ -621,34 +674,40 @@ hipError_t prefill_plan_launch(const PlanParams &P, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Persistent grid: every workgroup resident (cus x workgroups per CU).
-template <int MODE, int BITS, int XP>
+// Persistent grid: as many workgroups as are resident at once (cus x
+// workgroups per CU for this launch's LDS).
+template <int MODE, int BITS, int XF32>
 static hipError_t gemm_t(const GemmParams &P, int cus, hipStream_t st) {
-    // dynamic LDS: the slot plan (prefix[ns + 1] + 4 arrays of ns), ns <= E + 1
-    const size_t plan_bytes = (size_t)(5 * (P.E + 1) + 1) * 4;
-    static int occ = 0;
-    if (occ == 0) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_prefill_gemm<MODE, BITS, XP>,
+    using C = PfCfg<MODE, BITS, XF32>;
+    const size_t lds = (size_t)pf_plan_bytes(P.E) + C::RING;
+    static int attr_set = 0;
+    static int occ_lds[2] = {-1, 0};  // (LDS bytes, workgroups per CU) of the last query
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)k_prefill_gemm<MODE, BITS, XF32>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (5 * (MOE_MAX_EXPERTS_DEV + 1) + 1) * 4);
+                                           pf_plan_bytes(MOE_MAX_EXPERTS_DEV) + C::RING);
         if (e != hipSuccess) return e;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void *)k_prefill_gemm<MODE, BITS, XP>, PF_THREADS,
-                                                         (5 * (MOE_MAX_EXPERTS_DEV + 1) + 1) * 4);
-        if (e != hipSuccess) return e;
-        if (occ < 1) occ = 1;
+        attr_set = 1;
     }
-    hipLaunchKernelGGL((k_prefill_gemm<MODE, BITS, XP>), dim3(cus * occ), dim3(PF_THREADS), plan_bytes, st, P);
+    if (occ_lds[0] != (int)lds) {
+        int occ = 0;
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void *)k_prefill_gemm<MODE, BITS, XF32>,
+                                                                    PF_THREADS, lds);
+        if (e != hipSuccess) return e;
+        occ_lds[0] = (int)lds;
+        occ_lds[1] = occ < 1 ? 1 : occ;
+    }
+    hipLaunchKernelGGL((k_prefill_gemm<MODE, BITS, XF32>), dim3(cus * occ_lds[1]), dim3(PF_THREADS), lds, st, P);
     return hipGetLastError();
 }
 
 hipError_t prefill_gemm_launch(int mode, int bits, const GemmParams &P, int cus, hipStream_t st) {
-    const int xp = (mode == 1 || P.x_f32) ? 2 : 1;
     if (mode == 0) {
-        if (bits == 4) return xp == 2 ? gemm_t<0, 4, 2>(P, cus, st) : gemm_t<0, 4, 1>(P, cus, st);
-        return xp == 2 ? gemm_t<0, 3, 2>(P, cus, st) : gemm_t<0, 3, 1>(P, cus, st);
+        if (bits == 4) return P.x_f32 ? gemm_t<0, 4, 1>(P, cus, st) : gemm_t<0, 4, 0>(P, cus, st);
+        return P.x_f32 ? gemm_t<0, 3, 1>(P, cus, st) : gemm_t<0, 3, 0>(P, cus, st);
     }
-    if (bits == 4) return gemm_t<1, 4, 2>(P, cus, st);
-    return gemm_t<1, 3, 2>(P, cus, st);
+    if (bits == 4) return gemm_t<1, 4, 0>(P, cus, st);
+    return gemm_t<1, 3, 0>(P, cus, st);
 }
 
 hipError_t prefill_combine_launch(const CombineParams &P, hipStream_t st) {
