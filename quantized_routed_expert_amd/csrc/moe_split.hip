@@ -49,6 +49,12 @@ __device__ uint64_t *g_trace_split = nullptr;
     do {                                                                                                          \
         if (strace_buf && threadIdx.x == 0) strace_buf[blockIdx.x * 32 + (slot)] = __builtin_amdgcn_s_memrealtime(); \
     } while (0)
+// per wave: slots base + wave (base 12 and 20, eight waves)
+#define WTRACE(base)                                                                                              \
+    do {                                                                                                          \
+        if (strace_buf && (threadIdx.x & 63) == 0)                                                               \
+            strace_buf[blockIdx.x * 32 + (base) + (threadIdx.x >> 6)] = __builtin_amdgcn_s_memrealtime();        \
+    } while (0)
 extern "C" int moe_trace_split_set(void *buf) {
     return hipMemcpyToSymbol(HIP_SYMBOL(g_trace_split), &buf, sizeof(buf)) == hipSuccess ? 0 : -1;
 }
@@ -57,6 +63,9 @@ extern "C" int moe_trace_split_set(void *buf) {
     do {            \
     } while (0)
 #define STRACE(slot) \
+    do {             \
+    } while (0)
+#define WTRACE(base) \
     do {             \
     } while (0)
 #endif
@@ -263,7 +272,8 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     int16_t *s_ah = (int16_t *)(smem + P.lds_ah);       // [T][32] integer h of the slice
     uint32_t *s_hd = (uint32_t *)(smem + P.lds_hd);     // [T][xps] h digits
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // (the wave index read into a scalar: branches on it are uniform)
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = gridDim.x;
     const int k = P.k, E = P.E, H = P.H;
     const int T = P.T;  // rows of the window, 1 <= T <= TM
@@ -336,7 +346,9 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     // ======================= Phase A: routing, activations, slots =======================
     STRACE_INIT;
     STRACE(0);
-    const uint32_t tag_v = epoch_read(P.epoch);
+    // the call's tag is read after the routing loads are issued (it is first
+    // needed by the partial stores, so its load does not delay the logits)
+    uint32_t tag_v = 0u;
 
     // activations: thread tid holds the groups of 8 elements g = tid + 512 r
     // of [T][H] (r < XR)
@@ -374,14 +386,18 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
         }
     };
     if (route_mode && wave < T) {
-        // routing of row `wave` by this wave: logits first, then its activations
+        // routing of row `wave` by this wave: logits first, then its
+        // activations and the call's tag
         const int epl = (E + 63) >> 6;
         auto route_wave = [&](auto epl_c) {
             constexpr int EPL = decltype(epl_c)::value;
-            uint32_t key[EPL];
-            route_keys<EPL>(P.logits + (size_t)wave * E, E, lane, key);
+            float lv[EPL];
+            route_load<EPL>(P.logits + (size_t)wave * E, E, lane, lv);
             load_x();
+            tag_v = epoch_read(P.epoch);
             STRACE(10);
+            uint32_t key[EPL];
+            route_keys_of<EPL>(lv, E, lane, key);
             route_pick<EPL>(key, k, sm.idx + wave * k, sm.w + wave * k, lane);
             STRACE(11);
         };
@@ -391,6 +407,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
         else route_wave(std::integral_constant<int, 16>{});
     } else {
         load_x();
+        tag_v = epoch_read(P.epoch);
     }
     {
         // per wave and row: the largest |x|
@@ -597,7 +614,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
                 if (pc < npw) *(u32x4 *)(wr + (size_t)pc * 16) = rw[i];
             }
             wave_lds_handoff();
-            if (my_items == 0) STRACE(3);
+            if (my_items == 0) WTRACE(12);
             if (nxt < n_items) issue_item(nxt, 1);
             const int r = lane >> lg_qpr, m = lane & (qpr - 1);
             if (r < 8) {
@@ -639,6 +656,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
                 }
             }
         }
+        if (my_items == 0) WTRACE(20);
         __syncthreads();  // gate/up values
         if (my_items == 0) STRACE(4);
 
