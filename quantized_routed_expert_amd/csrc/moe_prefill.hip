@@ -16,11 +16,13 @@
 //                    sums of their tile counts.
 //   k_prefill_gemm   persistent grouped GEMM, tiles of 16, 32 or 64 rows (by
 //                    the group's size) x 128 features (gate/up) or 256
-//                    outputs (down).  Each wave dequantizes the weight
-//                    fragments of its own MFMAs in registers, as bf16 holding
-//                    the exact integer codes minus the bias; the activations
-//                    (bf16, exact) are gathered into LDS by the group's row
-//                    list; v_mfma_f32_16x16x32_bf16 covers one 32-wide quant
+//                    outputs (down).  Each K step's weight bytes and the
+//                    activation rows of the group (gathered by its row list)
+//                    stream into a ring of LDS slots with direct-to-LDS loads;
+//                    each wave dequantizes the weight fragments of its own
+//                    MFMAs from LDS into registers, as bf16 holding the exact
+//                    integer codes minus the bias (bf16 activations are
+//                    exact); v_mfma_f32_16x16x32_bf16 covers one 32-wide quant
 //                    block, and the fp16 block scale multiplies that block's
 //                    fp32 partial.  Gate/up tiles compute both projections for
 //                    the same 128 features and apply SwiGLU in fp32, storing h
