@@ -291,8 +291,37 @@ __device__ __forceinline__ void route_keys(const float *row, int E, int lane, ui
     route_keys_of<EPL>(v, E, lane, key);
 }
 
-// One selection round: the largest key (an equal key goes to the lower
-// expert id), removed from the keys; returns the expert id, sets its key.
+// key back to its fp32 value
+__device__ __forceinline__ float key_value(uint32_t m) {
+    return __builtin_bit_cast(float, (m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
+}
+
+// Best key of a lane and its index i (the lowest i among equal keys): a
+// tree of depth log2(EPL).
+template <int EPL>
+__device__ __forceinline__ void lane_best(const uint32_t (&key)[EPL], uint32_t &bk, int &bi) {
+    uint32_t k1[EPL];
+    int i1[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        k1[i] = key[i];
+        i1[i] = i;
+    }
+#pragma unroll
+    for (int w = 1; w < EPL; w *= 2)
+#pragma unroll
+        for (int i = 0; i + w < EPL; i += 2 * w) {
+            const bool hi = k1[i + w] > k1[i];  // strict: the lower index keeps a tie
+            k1[i] = hi ? k1[i + w] : k1[i];
+            i1[i] = hi ? i1[i + w] : i1[i];
+        }
+    bk = k1[0];
+    bi = i1[0];
+}
+
+// One selection round with branches (more than 4 keys per lane): the lane's
+// best key, the wave's largest (DPP), its holder by ballot; the rare tie
+// across lanes resolved by a second wave reduction over the holders' ids.
 template <int EPL>
 __device__ __forceinline__ int route_round(uint32_t (&key)[EPL], uint32_t &m, int lane) {
     uint32_t bk = 0;
@@ -320,37 +349,67 @@ __device__ __forceinline__ int route_round(uint32_t (&key)[EPL], uint32_t &m, in
     return e;
 }
 
-__device__ __forceinline__ float key_value(uint32_t m) {
-    return __builtin_bit_cast(float, (m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
-}
-
-// softmax over the k selected logits of one row (lane j < k holds slot j),
-// the sum taken in slot order 0, 1, ..., k-1 like every other routing path,
-// so a row's weights do not depend on which path routed it
-__device__ __forceinline__ void route_write(float mine, int mine_id, int k, int *out_idx, float *out_w, int lane) {
-    const float l0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mine)));
-    const float ex = lane < k ? expf(mine - l0) : 0.0f;
-    float s = 0.0f;
-    for (int j = 0; j < k; ++j) s += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), j));
-    if (lane < k) {
-        out_idx[lane] = mine_id;
-        out_w[lane] = ex / s;
-    }
-}
-
+// k rounds of a wave-wide argmax.  Up to 4 keys per lane without branches:
+// each lane's best key
+// (tree), the wave's largest (DPP), and among the lanes holding it the
+// lowest expert id (one ballot per key index: the lowest index with a
+// holder, then the lowest lane); the winner's key is cleared.  The softmax
+// numerators exp(l_j - l_0) and their sum (slot order 0, 1, ..., k-1) are
+// formed as the rounds go (the same values and order in both forms);
+// out_idx / out_w (LDS, k entries) receive slot j's expert and weight.
 template <int EPL>
 __device__ __forceinline__ void route_pick(uint32_t (&key)[EPL], int k, int *out_idx, float *out_w, int lane) {
-    float mine = 0.0f;
+    float mine = 0.0f, l0 = 0.0f, s = 0.0f;
     int mine_id = 0;
-    for (int j = 0; j < k; ++j) {
-        uint32_t m;
-        const int e = route_round<EPL>(key, m, lane);
-        if (lane == j) {
-            mine = key_value(m);
-            mine_id = e;
+    if constexpr (EPL > 4) {
+        // (the numerators after the rounds: lane j holds slot j's logit)
+        for (int j = 0; j < k; ++j) {
+            uint32_t m;
+            const int e = route_round<EPL>(key, m, lane);
+            if (lane == j) {
+                mine = key_value(m);
+                mine_id = e;
+            }
         }
+        l0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mine)));
+        const float ex = lane < k ? expf(mine - l0) : 0.0f;
+        for (int j = 0; j < k; ++j)
+            s += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ex), j));
+        if (lane < k) {
+            out_idx[lane] = mine_id;
+            out_w[lane] = ex / s;
+        }
+        return;
     }
-    route_write(mine, mine_id, k, out_idx, out_w, lane);
+    for (int j = 0; j < k; ++j) {
+        uint32_t bk;
+        int bi;
+        lane_best<EPL>(key, bk, bi);
+        const uint32_t m = wave_max_u32(bk);
+        const uint64_t held = __ballot(bk == m);
+        uint64_t win = 0;
+        int wi = 0;
+#pragma unroll
+        for (int i = EPL - 1; i >= 0; --i) {
+            const uint64_t t = held & __ballot(bi == i);
+            win = t ? t : win;
+            wi = t ? i : wi;
+        }
+        const int wl = (int)__builtin_ctzll(win);
+        const bool me = lane == wl;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) key[i] = (me && i == wi) ? 0u : key[i];
+        const float v = key_value(m);
+        if (j == 0) l0 = v;
+        const float ex = expf(v - l0);
+        s += ex;
+        mine = lane == j ? ex : mine;
+        mine_id = lane == j ? wl + 64 * wi : mine_id;
+    }
+    if (lane < k) {
+        out_idx[lane] = mine_id;
+        out_w[lane] = mine / s;
+    }
 }
 
 
