@@ -310,6 +310,10 @@ bool decode_fits(int T, int E, int k, int H, int F, int Fs, int bits, int dbits,
 
 // ---- column-split decode launch (windows of one to four rows, T*k <= 64) ----
 int split_xps(int /*bits*/) { return 36; }  // digit dwords per pair slot in LDS (both formats)
+// 16-byte loads per lane of a wave's 8 gate/up rows at H = 2048 (the most)
+int split_gu_loads(int bits) { return bits == 4 ? 9 : 7; }
+// 16-byte loads per lane of a wave's H/8 down rows of one column block at H = 2048
+int split_dn_loads(int bits) { return bits == 4 ? 5 : 4; }
 
 int split_lds_layout(SplitParams &P) {
     const int bb = block_bytes_of(P.bits), bbd = block_bytes_of(P.dbits), xps = split_xps(P.bits);
@@ -320,8 +324,10 @@ int split_lds_layout(SplitParams &P) {
         return (int)a;
     };
     P.lds_small = take(sizeof(SplitSmall));
-    P.lds_wt = take((size_t)P.H * (2 * bb + bbd));  // an item's gate rows, up rows and down column block
-    P.lds_a = P.lds_wt;  // the integer activations live in the item weight area until the items start
+    // an item's gate and up rows, then its down column block: each wave's
+    // share in its own run of 1 KB loads (split_gu_loads, split_dn_loads)
+    P.lds_wt = take((size_t)8 * (split_gu_loads(P.bits) + split_dn_loads(P.dbits)) * 1024);
+    P.lds_a = take((size_t)P.T * P.H * 2);  // the integer activations
     P.lds_S = take((size_t)P.T * (P.H / 32) * 4);
     P.lds_xd = take((size_t)P.T * (P.H / 64) * xps * 4);
     P.lds_gu = take((size_t)P.T * 64 * 4);
@@ -353,7 +359,8 @@ bool split_fits(int T, int E, int k, int H, int F, int Fs, int bits, int dbits, 
     const int units = split_units(T, k, H, combine, G);
     const int nterm = combine ? k + 1 : 1;
     const int ncmax = (F > Fs ? F : Fs) / 32;
-    return (long long)units * nterm * (ncmax + 1) * 4 <= (long long)H * (2 * block_bytes_of(bits) + block_bytes_of(dbits));
+    return (long long)units * nterm * (ncmax + 1) * 4 <=
+           (long long)8 * (split_gu_loads(bits) + split_dn_loads(dbits)) * 1024;
 }
 
 }  // namespace

@@ -226,6 +226,52 @@ __device__ __forceinline__ void wave_lds_handoff() {
 // all of this wave's memory operations have completed
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Workgroup barrier for LDS data only: the wave's LDS operations complete,
+// then s_barrier.  Unlike __syncthreads() it does not wait for the wave's
+// outstanding direct-to-LDS loads (a workgroup-scope release fence counts
+// them as LDS writes and waits for all of them), so loads issued ahead stay
+// in flight across it.  Global memory written before it is not ordered by it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // (no earlier access moves below it)
+    __builtin_amdgcn_s_waitcnt(0xC07F);                     // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// LDS as an address-space-3 pointer: the form the direct-to-LDS loads
+// (global_load_lds) take their destination in (from a generic pointer the
+// compiler does not derive M0 correctly)
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// vmcnt-only wait: until at most N vector memory operations of this wave are
+// outstanding (expcnt and lgkmcnt at their maxima: not waited on)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+// the same for a wave-uniform count n (0 <= n; counts above 15 wait for 15)
+__device__ __forceinline__ void wait_vm_n(int n) {
+    switch (n) {
+        case 0: wait_vm<0>(); break;
+        case 1: wait_vm<1>(); break;
+        case 2: wait_vm<2>(); break;
+        case 3: wait_vm<3>(); break;
+        case 4: wait_vm<4>(); break;
+        case 5: wait_vm<5>(); break;
+        case 6: wait_vm<6>(); break;
+        case 7: wait_vm<7>(); break;
+        case 8: wait_vm<8>(); break;
+        case 9: wait_vm<9>(); break;
+        case 10: wait_vm<10>(); break;
+        case 11: wait_vm<11>(); break;
+        case 12: wait_vm<12>(); break;
+        case 13: wait_vm<13>(); break;
+        case 14: wait_vm<14>(); break;
+        default: wait_vm<15>(); break;
+    }
+}
+
 // The call's tag source without a grid-wide counter: EPOCH_SLOTS words, all
 // equal to the number of calls made on the workspace.  Workgroup b reads
 // word b at its start and, at its end, writes the next value into every word

@@ -298,7 +298,6 @@ __device__ __forceinline__ u32x4 deq_group(const BFields<BITS> &f, uint32_t g) {
 // m-tile and adds the block's fp16 scale times the product to its fp32
 // accumulators, blocks in K order.
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
@@ -330,12 +329,6 @@ struct PfCfg {
     static_assert(A_PIECES == PF_THREADS * (MODE == 0 && XF32 ? 2 : 1), "one piece per thread (two for fp32 x)");
 };
 
-// vmcnt-only wait: expcnt and lgkmcnt at their maxima (not waited on)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
 // until at most L * ahead loads of this wave are outstanding (ahead <= 3)
 template <int L>
 __device__ __forceinline__ void wait_vm_steps(int ahead) {

@@ -261,8 +261,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     extern __shared__ __align__(16) uint8_t smem[];
     SplitSmall &sm = *(SplitSmall *)(smem + P.lds_small);
     uint8_t *s_wt = smem + P.lds_wt;                    // item weights: gate rows | up rows | down column
-    int16_t *s_a = (int16_t *)(smem + P.lds_wt);        // [T][H] integer activations (in the item
-                                                        // weight area, unused until the items)
+    int16_t *s_a = (int16_t *)(smem + P.lds_a);         // [T][H] integer activations
     int *s_S = (int *)(smem + P.lds_S);                 // [T][H/32] block sums (3-bit)
     // [T][H/64 pair slots][xps] activation digits; pair 4m + j of a row sits in
     // slot j * (H/256) + m, so the pieces m = 0, 1, ... that the lanes of a
@@ -282,7 +281,6 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     const int hs = has_shared ? 1 : 0;
     const bool route_mode = (P.mode & DEC_MODE_ROUTE) != 0;
     const int nc = P.nc, ncs = has_shared ? P.ncs : 0;
-    const int RG = H * FG::bb;          // bytes of an item's gate (and its up) rows: 32 rows of H/32 blocks
     const int RD = H * FD::bb;          // bytes of an item's down column block: H blocks
     const int npairs = H >> 6;          // pairs per gate/up row
     // gate/up tasks: qpr pieces of 4 consecutive pairs per row (H / 256)
@@ -302,17 +300,22 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     };
     // Each wave owns a share of an item end to end: 8 of its 64 gate/up rows
     // (waves 0-3 gate rows 8w.., waves 4-7 up rows) and H/8 of its down rows.
-    // It loads that share into registers (NGU + ND 16-byte pieces per lane;
-    // pieces past the share re-read its first piece and are not staged),
-    // stages it through its own part of LDS and computes from it: no other
-    // wave's data is waited for until the gate/up values are complete, so a
-    // wave computes as soon as its own bytes arrive.  Loads complete in issue
-    // order: gate/up rows first, then down rows.
+    // Both go straight into the wave's own runs of LDS: NGU and ND
+    // direct-to-LDS loads of 16 bytes per lane, 1 KB per load (lanes past
+    // the rows load into the run's unused tail).  A wave computes its rows as
+    // soon as their loads have landed: no other wave's data is waited for
+    // until the gate/up values are complete.  The loads of a wave complete in
+    // issue order, so the number of loads issued after a given one bounds the
+    // wave's wait for it (stores in between only lengthen such a wait).  A
+    // run is reloaded, for the wave's next item, as soon as the wave is done
+    // reading it: gate/up after the gate/up part, down after the down part.
     constexpr int NGU = BG == 4 ? 9 : 7;    // ceil(8 rows * rowH / 16 / 64) at H = 2048
     constexpr int ND = BD == 4 ? 5 : 4;     // ceil(H/8 rows * bb / 16 / 64) at H = 2048
+    constexpr int GUB = 8 * NGU * 1024;     // bytes of the gate/up runs (the down runs follow)
     const int npw = (8 * P.rowH) >> 4;      // pieces of a wave's 8 gate/up rows
     const int npd = (H * FD::bb) >> 7;      // pieces of a wave's H/8 down rows
-    u32x4 rw[NGU], rdn[ND];
+    lds_u8 *const s_gu_run = (lds_u8 *)s_wt + (size_t)wave * NGU * 1024;
+    lds_u8 *const s_dn_run = (lds_u8 *)s_wt + GUB + (size_t)wave * ND * 1024;
     // parts: 1 this wave's gate/up rows, 2 its down rows; e: the routed expert, -1: the shared one
     auto issue_item_e = [&](int c, int e, int parts) {
         const bool sh = e < 0;
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
 #pragma unroll
             for (int i = 0; i < NGU; ++i) {
                 const int pc = lane + 64 * i, q = pc < npw ? pc : 0;
-                rw[i] = *(const u32x4 *)(g0 + (size_t)q * 16);
+                __builtin_amdgcn_global_load_lds(g0 + (size_t)q * 16, s_gu_run + 1024 * i, 16, 0, 0);
             }
         }
         __builtin_amdgcn_sched_barrier(0);  // (keep the issue order)
@@ -333,7 +336,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
 #pragma unroll
             for (int i = 0; i < ND; ++i) {
                 const int pc = lane + 64 * i, q = pc < npd ? pc : 0;
-                rdn[i] = *(const u32x4 *)(d0 + (size_t)q * 16);
+                __builtin_amdgcn_global_load_lds(d0 + (size_t)q * 16, s_dn_run + 1024 * i, 16, 0, 0);
             }
         }
     };
@@ -430,7 +433,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     }
     // the shared expert's items need no routing: their weights stream in now
     if ((int)blockIdx.x < ncs) issue_item_e(blockIdx.x, -1, 3);
-    __syncthreads();  // routing and the row maxima complete
+    lds_barrier();  // routing and the row maxima complete
     STRACE(1);
     const uint32_t tag = decode_tag(__builtin_amdgcn_readfirstlane(tag_v));
     // a one-row window: its first routed item is known from the routing alone
@@ -576,7 +579,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
             if (P.heat) atomicAdd(&P.heat[sm.idx[p]], 1);  // routing heat (integer adds: any order)
         }
     }
-    __syncthreads();  // slots, integer activations, block sums
+    lds_barrier();  // slots, integer activations, block sums
     STRACE(2);
     const int n_slots = sm.n_slots;
     const int n_items = ncs + (n_slots - hs) * nc;
@@ -594,7 +597,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
         }
     }
 
-    __syncthreads();  // activation digits complete
+    lds_barrier();  // activation digits complete
     // ======================= Phase B: items =======================
     int my_items = 0;  // (for the trace points)
     for (; it < n_items; it += G) {
@@ -605,28 +608,44 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
 #pragma unroll
         for (int t = 0; t < TM; ++t) row_in[t] = sm.slot_pair[s][t] >= 0;
 
-        // gate/up: this wave's 8 rows; lane (row, piece m of 4 pairs)
+        // gate/up: this wave's 8 rows once its gate/up loads have landed (the
+        // down loads, issued after them, may still be in flight); lane (row r,
+        // run m of ppl consecutive pairs): lpr lanes per row (8, or 4 at
+        // H = 256), so every lane of the 8 rows is busy at every H.
         {
-            uint8_t *wr = s_wt + (size_t)wave * 8 * P.rowH;
-#pragma unroll
-            for (int i = 0; i < NGU; ++i) {
-                const int pc = lane + 64 * i;
-                if (pc < npw) *(u32x4 *)(wr + (size_t)pc * 16) = rw[i];
-            }
-            wave_lds_handoff();
+            const lds_u8 *wr = s_gu_run;
+            const int lpr = H >= 512 ? 8 : 4;  // lanes per row
+            const int ppl = (H >> 6) / lpr;     // pairs per lane: 1, 2 or 4
+            const int r = lane / lpr, m = lane - r * lpr;
+            wait_vm_n(ND);
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             if (my_items == 0) WTRACE(12);
-            if (nxt < n_items) issue_item(nxt, 1);
-            const int r = lane >> lg_qpr, m = lane & (qpr - 1);
             if (r < 8) {
                 float acc[TM];
 #pragma unroll
                 for (int t = 0; t < TM; ++t) acc[t] = 0.0f;
-                // the piece's 4 pairs (144 or 112 bytes, 16-byte aligned)
+                // the lane's run of pairs: 16-byte reads when it holds 4 pairs
+                // (144 or 112 bytes at a 16-byte aligned offset), else dwords
                 uint32_t wq[4 * FG::pw];
-                lds_read_b128<4 * FG::pw>(wr + (size_t)r * P.rowH + (size_t)m * 4 * FG::pb, wq);
+                const lds_u8 *run = wr + (size_t)r * P.rowH + (size_t)m * ppl * FG::pb;
+                if (ppl == 4) {
+#pragma unroll
+                    for (int i = 0; i < FG::pw; ++i) {
+                        const u32x4 v = *(const __attribute__((address_space(3))) u32x4 *)(run + 16 * i);
+                        wq[4 * i] = v.x;
+                        wq[4 * i + 1] = v.y;
+                        wq[4 * i + 2] = v.z;
+                        wq[4 * i + 3] = v.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 2 * FG::pw; ++i)
+                        wq[i] = i < ppl * FG::pw ? *(const __attribute__((address_space(3))) uint32_t *)(run + 4 * i) : 0u;
+                }
 #pragma unroll
                 for (int pp = 0; pp < 4; ++pp) {
-                    const int pr = 4 * m + pp, slot = pp * qpr + m;
+                    if (pp >= ppl) break;
+                    const int pr = m * ppl + pp, slot = (pr & 3) * qpr + (pr >> 2);
                     uint32_t w[FG::pw];
 #pragma unroll
                     for (int i = 0; i < FG::pw; ++i) w[i] = wq[pp * FG::pw + i];
@@ -645,19 +664,24 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
                         acc[t] = fmaf(sp.d1, (float)A1, acc[t]);
                     }
                 }
-                // sum over the row's qpr pieces (consecutive lanes; a fixed tree)
+                // sum over the row's lpr lanes (consecutive lanes; a fixed tree)
 #pragma unroll
                 for (int t = 0; t < TM; ++t) {
                     float v = acc[t];
-                    if (qpr >= 2) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-                    if (qpr >= 4) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-                    if (qpr >= 8) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+                    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+                    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+                    if (lpr >= 8) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
                     if (m == 0) s_gu[t * 64 + 8 * wave + r] = v;
                 }
             }
+            // the gate/up run is free again: the next item's gate/up rows
+            if (nxt < n_items) {
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                issue_item(nxt, 1);
+            }
         }
         if (my_items == 0) WTRACE(20);
-        __syncthreads();  // gate/up values
+        lds_barrier();  // gate/up values
         if (my_items == 0) STRACE(4);
 
         // SwiGLU and the h digits: wave t for row t
@@ -687,21 +711,17 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             if (lane < FD::nnd) build_digits<BD>(s_ah + t * 32, 31, lane, s_hd + t * xps);
         }
-        __syncthreads();  // h digits
+        lds_barrier();  // h digits
         if (my_items == 0) STRACE(5);
 
         // down: this wave's H/8 rows of column block c, as row pairs (2 rp, 2 rp + 1);
         // partial rows stored tagged
         {
-            uint8_t *dw = s_wt + 2 * (size_t)RG + (size_t)wave * (H >> 3) * FD::bb;
-#pragma unroll
-            for (int i = 0; i < ND; ++i) {
-                const int pc = lane + 64 * i;
-                if (pc < npd) *(u32x4 *)(dw + (size_t)pc * 16) = rdn[i];
-            }
-            wave_lds_handoff();
-            if (nxt < n_items) issue_item(nxt, 2);
-            const uint8_t *dcol = s_wt + 2 * (size_t)RG;
+            // this item's down rows have landed (the next item's gate/up loads,
+            // issued after them, may still be in flight)
+            wait_vm_n(nxt < n_items ? NGU : 0);
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const lds_u8 *dcol = s_dn_run - (size_t)wave * (H >> 4) * FD::pb;  // (indexed by the global rp)
             int pid[TM];
             int hsc[TM];
             int Sh[TM];
@@ -720,7 +740,9 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
             }
             for (int rp = wave * (H >> 4) + lane; rp < (wave + 1) * (H >> 4); rp += 64) {
                 uint32_t w[FD::pw];
-                lds_read_dwords<FD::pw>(dcol + (size_t)rp * FD::pb, w);
+                const lds_u8 *pp8 = dcol + (size_t)rp * FD::pb;
+#pragma unroll
+                for (int i = 0; i < FD::pw; ++i) w[i] = *(const __attribute__((address_space(3))) uint32_t *)(pp8 + 4 * i);
                 SPair<BD> sp;
                 sp.set(w);
 #pragma unroll
@@ -741,6 +763,11 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
                 }
             }
         }
+        // the down run is free again: the next item's down rows
+        if (nxt < n_items) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            issue_item(nxt, 2);
+        }
         if (my_items == 0) STRACE(6);
         ++my_items;
         // (no barrier: every wave reuses only its own staging area; the shared
@@ -749,7 +776,9 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     }
 
     // ======================= Phase C: sums over the slices =======================
-    __syncthreads();  // every thread's partial stores are issued
+    // every wave is done with the item area (its LDS is reused below); the
+    // partial stores need not have completed: the readers check the tags
+    lds_barrier();
     STRACE(7);
     // outputs: COMBINE: (row t, output h) -> y; else (present pair, output h)
     const bool combine = (P.mode & DEC_MODE_COMBINE) != 0;
