@@ -46,6 +46,8 @@ def _bind(lib):
     lib.orc_half_to_double.argtypes = [ctypes.c_uint16]
     lib.orc_bf16_to_double.restype = ctypes.c_double
     lib.orc_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.orc_set_codebook.restype = None
+    lib.orc_set_codebook.argtypes = [ctypes.c_void_p]
     lib.orc_block_bytes.restype = ctypes.c_int
     lib.orc_block_bytes.argtypes = [ctypes.c_int]
     lib.orc_format_bits.restype = ctypes.c_int
@@ -99,6 +101,7 @@ def _ptr(a: np.ndarray, ctype=None):
 
 
 X_F32, X_BF16 = 0, 1
+BITS_NL4 = 20  # the non-linear 4-bit block (4-bit layout, codes index a 16-entry int8 table)
 
 
 class Oracle:
@@ -120,6 +123,15 @@ class Oracle:
         return self.lib.orc_bf16_to_double(int(b))
 
     # -- blocks -----------------------------------------------------------
+    def set_codebook(self, cb) -> None:
+        """The 16 signed 8-bit values that the non-linear 4-bit format's codes index."""
+        c = np.ascontiguousarray(np.asarray(cb, dtype=np.int8).reshape(16))
+        self.lib.orc_set_codebook(_ptr(c))
+
+    def _cb(self, codebook):
+        if codebook is not None:
+            self.set_codebook(codebook)
+
     def block_bytes(self, bits: int) -> int:
         return self.lib.orc_block_bytes(bits)
 
@@ -130,14 +142,16 @@ class Oracle:
     def expert_bytes(self, fmt: int, hidden: int, ffn: int) -> int:
         return self.lib.orc_expert_bytes(fmt, hidden, ffn)
 
-    def dequant_block(self, bits: int, blk: bytes | np.ndarray) -> np.ndarray:
+    def dequant_block(self, bits: int, blk: bytes | np.ndarray, codebook=None) -> np.ndarray:
+        self._cb(codebook)
         b = np.ascontiguousarray(np.frombuffer(bytes(blk), dtype=np.uint8))
         assert b.size == self.block_bytes(bits)
         out = np.zeros(32, dtype=np.float64)
         self.lib.orc_dequant_block(bits, _ptr(b), _ptr(out, ctypes.c_double))
         return out
 
-    def dequant_matrix(self, bits: int, m: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    def dequant_matrix(self, bits: int, m: np.ndarray, rows: int, cols: int, codebook=None) -> np.ndarray:
+        self._cb(codebook)
         m = np.ascontiguousarray(m, dtype=np.uint8)
         assert m.size >= rows * (cols // 32) * self.block_bytes(bits)
         out = np.zeros((rows, cols), dtype=np.float64)
@@ -145,8 +159,9 @@ class Oracle:
         assert rc == 0
         return out
 
-    def dequant_expert(self, fmt: int, blob: np.ndarray, hidden: int, ffn: int):
+    def dequant_expert(self, fmt: int, blob: np.ndarray, hidden: int, ffn: int, codebook=None):
         """(gate [F,H], up [F,H], down [H,F]) of one expert blob of format fmt."""
+        self._cb(codebook)
         blob = np.ascontiguousarray(blob, dtype=np.uint8)
         bg, bd = self.format_bits(fmt, False), self.format_bits(fmt, True)
         mb = hidden * (ffn // 32) * self.block_bytes(bg)
@@ -196,7 +211,8 @@ class Oracle:
 
     # -- FFN and layer --------------------------------------------------------
     def expert_ffn(self, x: np.ndarray, x_dtype: int, k: int, fmt: int, E: int, hidden: int,
-                   ffn: int, blobs: np.ndarray, offsets, pairs, active, pair_w=None):
+                   ffn: int, blobs: np.ndarray, offsets, pairs, active, pair_w=None, codebook=None):
+        self._cb(codebook)
         x = np.ascontiguousarray(x)
         T = x.shape[0]
         blobs = np.ascontiguousarray(blobs, dtype=np.uint8)
@@ -218,10 +234,12 @@ class Oracle:
 
     def layer_forward(self, x: np.ndarray, x_dtype: int, logits: np.ndarray, k: int, fmt: int,
                       ffn: int, routed: np.ndarray, shared: np.ndarray | None = None,
-                      s_fmt: int | None = None, s_ffn: int | None = None, rows=None):
+                      s_fmt: int | None = None, s_ffn: int | None = None, rows=None, codebook=None):
         """fmt / s_fmt: format codes of the routed / shared experts (a bit
-        width 3 or 4, or gate/up bits | down bits << 8).
+        width 3, 4 or 20 (non-linear 4-bit), or gate/up bits | down bits << 8);
+        codebook: the non-linear format's 16 int8 values (shared by both).
         Returns (y [n_rows, H] float64, idx [T,k] int32, w [T,k] float64)."""
+        self._cb(codebook)
         x = np.ascontiguousarray(x)
         logits = np.ascontiguousarray(logits, dtype=np.float32)
         T, E = logits.shape

@@ -100,8 +100,17 @@ double orc_bf16_to_double(uint16_t b) {
 /* Quantized blocks                                                     */
 /* ------------------------------------------------------------------ */
 
+/* the non-linear 4-bit format (code 20): the 4-bit block's layout, each code
+ * indexing a 16-entry table of signed 8-bit values (thread §四 names a
+ * non-linear 4-bit block of 32 values in 18 bytes; the pages print no table,
+ * so the table is an input, set with orc_set_codebook) */
+#define ORC_BITS_NL4 20
+static int8_t orc_cb[16];
+
+void orc_set_codebook(const int8_t *cb) { memcpy(orc_cb, cb, 16); }
+
 int orc_block_bytes(int bits) {
-    if (bits == 4) return 18;
+    if (bits == 4 || bits == ORC_BITS_NL4) return 18;
     if (bits == 3) return 14;
     return -1;
 }
@@ -112,7 +121,8 @@ int orc_block_bytes(int bits) {
  * width as gate/up (so a plain 3 or 4 is a uniform format).  The thread's §三
  * decode table pairs each gate/up format with a down format of its own (a
  * 2- or 3-bit gate/up with a 4-bit down); here the same per-projection choice
- * is made between the 3- and 4-bit blocks above.  -1 for anything else.
+ * is made between the 3-bit, 4-bit and non-linear 4-bit (20) blocks above.
+ * -1 for anything else.
  */
 int orc_format_bits(int fmt, int down) {
     int gu = fmt & 0xFF, dn = (fmt >> 8) & 0xFF;
@@ -137,15 +147,17 @@ int64_t orc_expert_bytes(int fmt, int hidden, int ffn) {
  *   3-bit (14 bytes): low two bits = bits 2*(i div 8).. of byte 2+(i mod 8);
  *                     third bit = bit i of the little-endian 32-bit word at
  *                     bytes 10..13; value d * (c_i - 4).
+ *   non-linear 4-bit (18 bytes, code 20): c_i as for 4-bit; value
+ *                     d * codebook[c_i] (the table set by orc_set_codebook).
  * Symmetric codes: no zero point, only the fixed bias 2^(bits-1).
  */
 void orc_dequant_block(int bits, const uint8_t *blk, double *out) {
     double d = orc_half_to_double((uint16_t)(blk[0] | (blk[1] << 8)));
     int i;
-    if (bits == 4) {
+    if (bits == 4 || bits == ORC_BITS_NL4) {
         for (i = 0; i < 32; ++i) {
             int c = (i < 16) ? (blk[2 + i] & 0x0F) : (blk[2 + (i - 16)] >> 4);
-            out[i] = d * (double)(c - 8);
+            out[i] = (bits == ORC_BITS_NL4) ? d * (double)orc_cb[c] : d * (double)(c - 8);
         }
     } else {
         uint32_t qh = (uint32_t)blk[10] | ((uint32_t)blk[11] << 8) |

@@ -16,6 +16,9 @@ the HIP kernels):
   * 3-bit, 14 bytes per 32 weights: fp16 scale d, 8 bytes of 2-bit low parts
     (code i's low two bits at bit 2*(i//8) of byte i%8), then a 32-bit
     little-endian word whose bit i is code i's third bit; weight = d*(code-4).
+  * non-linear 4-bit (format code 20), 18 bytes: the 4-bit layout, weight =
+    d * codebook[code] with a 16-entry table of signed 8-bit values (the
+    pages name the format but print no table; the table is an input).
   * A matrix [rows][cols] is stored row by row, cols/32 blocks per row; an
     expert is gate [F][H] | up [F][H] | down [H][F]; experts back to back.
     Gate and up share one bit width, down may have another (``down_bits``).
@@ -33,6 +36,14 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 TID_X, TID_LOGITS, TID_ROUTED, TID_SHARED, TID_PERM, TID_ROUTER = 0, 1, 2, 3, 4, 5
+BITS_NL4 = 20  # the non-linear 4-bit format's code
+
+
+def nl4_test_codebook() -> tuple:
+    """A non-linear, monotone table of 16 signed 8-bit values for the tests:
+    127 * sign(t) * |t|^1.6 at t = (i - 7.5) / 7.5, rounded."""
+    t = (np.arange(16) - 7.5) / 7.5
+    return tuple(int(v) for v in np.rint(127.0 * np.sign(t) * np.abs(t) ** 1.6))
 
 
 @dataclasses.dataclass(frozen=True)
@@ -52,6 +63,7 @@ class Config:
     layers: int
     weight_cid: int = 0  # seed namespace of the weights (0 = cid)
     down_bits: int = 0   # bit width of the down projection (0 = bits, the gate/up width)
+    codebook: tuple = ()  # the non-linear 4-bit format's 16 values (when a width is 20)
 
     @property
     def wcid(self) -> int:
@@ -95,7 +107,7 @@ CONFIGS = {
 
 
 def block_bytes(bits: int) -> int:
-    return {4: 18, 3: 14}[bits]
+    return {4: 18, 3: 14, BITS_NL4: 18}[bits]
 
 
 def format_code(bits: int, down_bits: int = 0) -> int:
@@ -137,7 +149,7 @@ def pack_codes(codes: np.ndarray, d16: np.ndarray, bits: int) -> np.ndarray:
     d16 = np.ascontiguousarray(np.asarray(d16, dtype=np.float16).reshape(nblk))
     out = np.empty((nblk, block_bytes(bits)), dtype=np.uint8)
     out[:, 0:2] = d16.view(np.uint8).reshape(nblk, 2)
-    if bits == 4:
+    if bits in (4, BITS_NL4):
         out[:, 2:18] = (codes[:, :16] & 0x0F) | ((codes[:, 16:] & 0x0F) << 4)
     elif bits == 3:
         lo = codes & 3
@@ -152,13 +164,25 @@ def pack_codes(codes: np.ndarray, d16: np.ndarray, bits: int) -> np.ndarray:
     return out.reshape(-1)
 
 
-def quantize(w: np.ndarray, bits: int) -> np.ndarray:
+def quantize(w: np.ndarray, bits: int, codebook=None) -> np.ndarray:
     """Quantize a [rows, cols] float32 matrix along its rows in blocks of 32:
     d = fp16(absmax / qmax), code = clip(rint(w / d), -qmax, qmax) + 2^(bits-1)
-    with qmax = 2^(bits-1) - 1 (all codes = bias when the block is zero)."""
+    with qmax = 2^(bits-1) - 1 (all codes = bias when the block is zero).
+    Non-linear 4-bit: d = fp16(absmax / max|codebook|), code = the entry
+    nearest w / d (the lowest code among equally near ones)."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     rows, cols = w.shape
     assert cols % 32 == 0
+    if bits == BITS_NL4:
+        cb = np.asarray(codebook, dtype=np.float32).reshape(16)
+        blk = w.reshape(-1, 32)
+        amax = np.abs(blk).max(axis=1)
+        d16 = (amax / np.float32(np.abs(cb).max())).astype(np.float16)
+        d32 = d16.astype(np.float32)
+        safe = np.where(d32 > 0, d32, np.float32(1.0))
+        dist = np.abs((blk / safe[:, None])[:, :, None] - cb[None, None, :])
+        codes = np.argmin(dist, axis=2).astype(np.uint8)
+        return pack_codes(codes, d16, bits)
     qmax = (1 << (bits - 1)) - 1
     bias = 1 << (bits - 1)
     blk = w.reshape(-1, 32)
@@ -179,6 +203,8 @@ def quantize_torch(w, bits: int):
     same w.  w: float32 tensor [..., cols] (cols % 32 == 0) -> uint8 tensor
     [nblk * block_bytes], blocks in row-major order."""
     import torch
+    if bits not in (3, 4):
+        raise ValueError(f"quantize_torch encodes the 3- and 4-bit formats, not {bits}")
     w = w.contiguous().to(torch.float32)
     qmax = (1 << (bits - 1)) - 1
     bias = 1 << (bits - 1)
@@ -247,13 +273,14 @@ def routed_weights_torch(cfg: Config, layer: int, device, base_seed: int = 0, ch
 
 
 def expert_blob(rg: np.random.Generator, hidden: int, ffn: int, bits: int, std: float = 0.02,
-                down_bits: int = 0) -> np.ndarray:
+                down_bits: int = 0, codebook=None) -> np.ndarray:
     """One expert: N(0, std) gate [F,H], up [F,H] (bits), down [H,F]
-    (down_bits, 0 = bits), quantized."""
+    (down_bits, 0 = bits), quantized (codebook: the non-linear format's table)."""
     g = rg.standard_normal((ffn, hidden), dtype=np.float32) * np.float32(std)
     u = rg.standard_normal((ffn, hidden), dtype=np.float32) * np.float32(std)
     d = rg.standard_normal((hidden, ffn), dtype=np.float32) * np.float32(std)
-    return np.concatenate([quantize(g, bits), quantize(u, bits), quantize(d, down_bits or bits)])
+    return np.concatenate([quantize(g, bits, codebook), quantize(u, bits, codebook),
+                           quantize(d, down_bits or bits, codebook)])
 
 
 def _threads(n: int | None) -> int:
@@ -270,7 +297,8 @@ def routed_weights(cfg: Config, layer: int, base_seed: int = 0, threads: int | N
 
     def one(e):
         buf[e * eb:(e + 1) * eb] = expert_blob(rng(cfg.wcid, layer, TID_ROUTED, base_seed, e),
-                                               cfg.hidden, cfg.ffn, cfg.bits, down_bits=cfg.down_bits)
+                                               cfg.hidden, cfg.ffn, cfg.bits, down_bits=cfg.down_bits,
+                                               codebook=cfg.codebook or None)
 
     with ThreadPoolExecutor(_threads(threads)) as ex:
         list(ex.map(one, range(cfg.n_experts)))
@@ -281,7 +309,7 @@ def shared_weights(cfg: Config, layer: int, base_seed: int = 0) -> np.ndarray | 
     if not cfg.shared_ffn:
         return None
     return expert_blob(rng(cfg.wcid, layer, TID_SHARED, base_seed), cfg.hidden, cfg.shared_ffn, cfg.bits,
-                       down_bits=cfg.down_bits)
+                       down_bits=cfg.down_bits, codebook=cfg.codebook or None)
 
 
 # --------------------------------------------------------------------------

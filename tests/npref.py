@@ -16,11 +16,20 @@ def bf16_bits_to_f64(b):
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def dequant_blocks(raw: np.ndarray, bits: int) -> np.ndarray:
+NL4 = 20  # non-linear 4-bit: the 4-bit layout, codes index a 16-entry int8 table
+BLOCK_BYTES = {4: 18, 3: 14, NL4: 18}
+
+
+def dequant_blocks(raw: np.ndarray, bits: int, codebook=None) -> np.ndarray:
     """raw uint8 [nblk * B] -> float64 [nblk, 32]."""
-    B = {4: 18, 3: 14}[bits]
+    B = BLOCK_BYTES[bits]
     blk = np.asarray(raw, dtype=np.uint8).reshape(-1, B)
     d = half_bits_to_f64(blk[:, 0].astype(np.uint16) | (blk[:, 1].astype(np.uint16) << 8))
+    if bits == NL4:
+        qs = blk[:, 2:18]
+        codes = np.concatenate([qs & 0x0F, qs >> 4], axis=1).astype(np.int64)
+        table = np.asarray(codebook, dtype=np.int8).astype(np.float64)
+        return d[:, None] * table[codes]
     if bits == 4:
         qs = blk[:, 2:18]
         codes = np.concatenate([qs & 0x0F, qs >> 4], axis=1).astype(np.int64)
@@ -37,19 +46,19 @@ def dequant_blocks(raw: np.ndarray, bits: int) -> np.ndarray:
     return d[:, None] * (codes - bias).astype(np.float64)
 
 
-def dequant_matrix(raw, bits, rows, cols):
-    return dequant_blocks(raw, bits).reshape(rows, cols)
+def dequant_matrix(raw, bits, rows, cols, codebook=None):
+    return dequant_blocks(raw, bits, codebook).reshape(rows, cols)
 
 
-def dequant_expert(blob, bits, H, F, down_bits=None):
+def dequant_expert(blob, bits, H, F, down_bits=None, codebook=None):
     """gate, up ([F,H], `bits`) and down ([H,F], `down_bits`, default `bits`)."""
     db = bits if down_bits is None else down_bits
-    mg = H * (F // 32) * {4: 18, 3: 14}[bits]
-    md = H * (F // 32) * {4: 18, 3: 14}[db]
+    mg = H * (F // 32) * BLOCK_BYTES[bits]
+    md = H * (F // 32) * BLOCK_BYTES[db]
     blob = np.asarray(blob, dtype=np.uint8)
     assert blob.size == 2 * mg + md
-    return (dequant_matrix(blob[:mg], bits, F, H), dequant_matrix(blob[mg:2 * mg], bits, F, H),
-            dequant_matrix(blob[2 * mg:], db, H, F))
+    return (dequant_matrix(blob[:mg], bits, F, H, codebook), dequant_matrix(blob[mg:2 * mg], bits, F, H, codebook),
+            dequant_matrix(blob[2 * mg:], db, H, F, codebook))
 
 
 def swiglu_mlp(X, Wg, Wu, Wd):
@@ -65,7 +74,7 @@ def x_to_f64(x, x_code):
 
 
 def dense_masked_layer(x, x_code, logits, k, bits, H, F, routed, shared=None, s_bits=None, s_F=None,
-                       down_bits=None):
+                       down_bits=None, codebook=None):
     """Every expert on every row, weighted by a [T,E] mask that is the softmax
     of the k selected logits and zero elsewhere; plus the shared expert.
     bits: gate/up width, down_bits: down width (default bits), for the routed
@@ -80,16 +89,16 @@ def dense_masked_layer(x, x_code, logits, k, bits, H, F, routed, shared=None, s_
         ex = np.exp(sel - sel.max())
         M[t, order[t]] = ex / ex.sum()
     db = bits if down_bits is None else down_bits
-    eb = H * (F // 32) * (2 * {4: 18, 3: 14}[bits] + {4: 18, 3: 14}[db])
+    eb = H * (F // 32) * (2 * BLOCK_BYTES[bits] + BLOCK_BYTES[db])
     Y = np.zeros((T, H))
     for e in range(E):
         if not M[:, e].any():
             continue
-        Wg, Wu, Wd = dequant_expert(routed[e * eb:(e + 1) * eb], bits, H, F, db)
+        Wg, Wu, Wd = dequant_expert(routed[e * eb:(e + 1) * eb], bits, H, F, db, codebook)
         Y += M[:, e:e + 1] * swiglu_mlp(X, Wg, Wu, Wd)
     if shared is not None:
         sb = bits if s_bits is None else s_bits
         sF = F if s_F is None else s_F
-        Wg, Wu, Wd = dequant_expert(shared, sb, H, sF, db)
+        Wg, Wu, Wd = dequant_expert(shared, sb, H, sF, db, codebook)
         Y += swiglu_mlp(X, Wg, Wu, Wd)
     return Y, order.astype(np.int32), M

@@ -98,6 +98,52 @@ def pin_blocks(o):
         assert np.array_equal(got, np.array(exp, dtype=np.float64)), name
 
 
+# Non-linear 4-bit: the pages name the block (32 values in 18 bytes, 4-bit
+# codes indexing a table) but print no table, so the table is an input.  The
+# pins use tables chosen to expose index, sign and layout mistakes.
+NL4 = 20
+CB_TEST = synth.nl4_test_codebook()                        # monotone, odd-symmetric
+CB_SCRAMBLE = tuple(((c * 37 + 11) % 256) - 128 for c in range(16))  # distinct, unordered, signed
+CB_EXTREME = (-128, 127, -1, 0, 1, -127, 126, -64, 64, -2, 2, 100, -100, 3, -3, 5)
+CB_IDENTITY = tuple(c - 8 for c in range(16))              # reduces to the 4-bit format
+
+
+def pin_nl4_blocks(o):
+    """Hand-built non-linear blocks: value i is d * table[code i] (codes in the
+    4-bit block's nibble order), for several tables and scales."""
+    qs = [i | ((15 - i) << 4) for i in range(16)]  # codes 0..15, then 15..0
+    for cb, d_bits, d in ((CB_TEST, 0x3C00, 1.0), (CB_SCRAMBLE, 0xB800, -0.5), (CB_EXTREME, 0x0001, 2.0 ** -24),
+                          (CB_EXTREME, 0x7BFF, 65504.0)):
+        exp = [d * cb[i] for i in range(16)] + [d * cb[15 - i] for i in range(16)]
+        got = o.dequant_block(NL4, _blk4(d_bits, qs), codebook=cb)
+        assert np.array_equal(got, np.array(exp, dtype=np.float64)), (cb, d)
+    # one code everywhere: every weight is d * table[that code]
+    for c in range(16):
+        got = o.dequant_block(NL4, _blk4(0x3400, [c | (c << 4)] * 16), codebook=CB_SCRAMBLE)
+        assert np.all(got == 0.25 * CB_SCRAMBLE[c]), c
+
+
+def pin_nl4_reductions(o, seed=5):
+    """With the table c - 8 the non-linear block is the 4-bit block, bitwise,
+    on random bytes; with other tables it agrees with the numpy decoder's
+    table lookup; random codes packed by the encoder decode to d * table[code]."""
+    rg = np.random.default_rng(seed)
+    raw = rg.integers(0, 256, size=(300, 18)).astype(np.uint8)
+    raw[:, 1] &= 0x7B
+    raw = raw.reshape(-1)
+    assert np.array_equal(o.dequant_matrix(NL4, raw, 300, 32, codebook=CB_IDENTITY),
+                          o.dequant_matrix(4, raw, 300, 32))
+    for cb in (CB_TEST, CB_SCRAMBLE, CB_EXTREME):
+        assert np.array_equal(o.dequant_matrix(NL4, raw, 300, 32, codebook=cb),
+                              npref.dequant_blocks(raw, NL4, cb)), cb
+    codes = rg.integers(0, 16, size=(64, 32)).astype(np.uint8)
+    d16 = (rg.standard_normal(64) * 0.01).astype(np.float16)
+    packed = synth.pack_codes(codes, d16, NL4)
+    got = o.dequant_matrix(NL4, packed, 64, 32, codebook=CB_SCRAMBLE)
+    exp = d16.astype(np.float64)[:, None] * np.array(CB_SCRAMBLE, dtype=np.float64)[codes]
+    assert np.array_equal(got, exp)
+
+
 def pin_encoder_roundtrip(o, seed=7):
     """Random codes and scales packed by the input encoder, decoded by the
     oracle, equal d * (code - bias) exactly."""
@@ -155,6 +201,11 @@ def pin_expert_bytes(o):
     assert o.expert_bytes(3 | (3 << 8), 2048, 512) == o.expert_bytes(3, 2048, 512)
     assert o.expert_bytes(3 | (5 << 8), 2048, 512) == -1
     assert o.expert_bytes(3 | (4 << 16), 2048, 512) == -1
+    # the non-linear 4-bit block is 18 bytes, alone or beside another width
+    assert o.block_bytes(NL4) == 18
+    assert o.expert_bytes(NL4, 2048, 768) == 2654208
+    assert o.expert_bytes(3 | (NL4 << 8), 2048, 512) == 2048 * 16 * (2 * 14 + 18)
+    assert o.expert_bytes(NL4 | (3 << 8), 2048, 512) == 2048 * 16 * (2 * 18 + 14)
 
 
 def pin_format_bits(o):
@@ -163,6 +214,9 @@ def pin_format_bits(o):
     assert (o.format_bits(3 | (4 << 8), False), o.format_bits(3 | (4 << 8), True)) == (3, 4)
     assert (o.format_bits(4 | (3 << 8), False), o.format_bits(4 | (3 << 8), True)) == (4, 3)
     assert o.format_bits(2, False) == -1 and o.format_bits(4 | (2 << 8), True) == -1
+    assert (o.format_bits(3 | (NL4 << 8), False), o.format_bits(3 | (NL4 << 8), True)) == (3, NL4)
+    assert (o.format_bits(NL4, False), o.format_bits(NL4, True)) == (NL4, NL4)
+    assert o.format_bits(21, False) == -1
 
 
 def pin_mixed_expert_indexing(o):
@@ -307,16 +361,18 @@ def small_cfg(bits, x_dtype, E=12, H=64, F=96, k=3, Fs=64, logits=("normal", 1.0
 
 def pin_layer_dense(o):
     """Oracle layer == dense-with-mask brute force (all experts on all rows),
-    uniform and per-projection formats."""
+    uniform, per-projection and non-linear formats."""
     for bits, db, xd, Fs in [(4, 0, "f32", 64), (3, 0, "bf16", 96), (4, 0, "bf16", 0), (3, 0, "f32", 32),
-                             (3, 4, "bf16", 64), (4, 3, "f32", 96)]:
-        cfg = dataclasses.replace(small_cfg(bits, xd, Fs=Fs), down_bits=db)
+                             (3, 4, "bf16", 64), (4, 3, "f32", 96), (NL4, 0, "bf16", 64), (3, NL4, "f32", 96),
+                             (NL4, 3, "bf16", 0)]:
+        cb = CB_SCRAMBLE if NL4 in (bits, db) else ()
+        cfg = dataclasses.replace(small_cfg(bits, xd, Fs=Fs), down_bits=db, codebook=cb)
         li = synth.layer_inputs(cfg, T=7, threads=1)
         y, idx, w = o.layer_forward(li.x, li.x_code, li.logits, cfg.top_k, cfg.fmt, cfg.ffn,
-                                    li.routed, li.shared, s_ffn=Fs or None)
+                                    li.routed, li.shared, s_ffn=Fs or None, codebook=cb or None)
         yr, ir, M = npref.dense_masked_layer(li.x, li.x_code, li.logits, cfg.top_k, bits,
                                              cfg.hidden, cfg.ffn, li.routed, li.shared,
-                                             s_F=Fs or None, down_bits=cfg.dbits)
+                                             s_F=Fs or None, down_bits=cfg.dbits, codebook=cb or None)
         assert np.array_equal(idx, ir)
         rms = np.sqrt(np.mean(yr ** 2))
         assert np.max(np.abs(y - yr)) <= 1e-12 * rms, (bits, db, xd, np.max(np.abs(y - yr)) / rms)
@@ -393,7 +449,7 @@ def pin_expert_ffn_matches_layer(o):
     assert np.allclose(po[nz], po1[nz] * w.reshape(-1)[nz, None], rtol=1e-13, atol=0)
 
 
-ALL_PINS = [pin_half, pin_bf16, pin_blocks, pin_encoder_roundtrip, pin_matrix_indexing,
+ALL_PINS = [pin_half, pin_bf16, pin_blocks, pin_nl4_blocks, pin_nl4_reductions, pin_encoder_roundtrip, pin_matrix_indexing,
             pin_numpy_dequant_agrees, pin_expert_bytes, pin_format_bits, pin_mixed_expert_indexing,
             pin_router_logits, pin_route_bruteforce, pin_route_ties,
             pin_route_special, pin_group, pin_layer_dense, pin_layer_single_expert,

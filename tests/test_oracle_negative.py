@@ -16,7 +16,11 @@ import oracle_pins as P
 
 MUTATIONS = [
     ("nibble_halves_swapped", "(i < 16) ? (blk[2 + i] & 0x0F)", "(i >= 16) ? (blk[2 + i] & 0x0F)"),
-    ("q4_bias_off_by_one", "out[i] = d * (double)(c - 8);", "out[i] = d * (double)(c - 7);"),
+    ("q4_bias_off_by_one", ": d * (double)(c - 8);", ": d * (double)(c - 7);"),
+    ("nl4_read_as_linear", "? d * (double)orc_cb[c] :", "? d * (double)(c - 8) :"),
+    ("nl4_table_index_off_by_one", "d * (double)orc_cb[c]", "d * (double)orc_cb[(c + 1) & 15]"),
+    ("nl4_table_entries_as_unsigned", "d * (double)orc_cb[c]", "d * (double)(uint8_t)orc_cb[c]"),
+    ("nl4_block_bytes", "if (bits == 4 || bits == ORC_BITS_NL4) return 18;", "if (bits == 4) return 18;"),
     ("q3_high_bit_weight", "int c = lo | (hi << 2);", "int c = lo | (hi << 1);"),
     ("q3_low_field_index", "(blk[2 + (i % 8)] >> (2 * (i / 8))) & 3", "(blk[2 + (i / 4)] >> (2 * (i % 4))) & 3"),
     ("half_exponent_bias", "expo - 15", "expo - 14"),
