@@ -28,6 +28,12 @@
  *             bit 2*(i/8) of byte 2+(i%8)) + a 32-bit little-endian word at
  *             bytes 10..13 whose bit i is code i's third bit;
  *             weight = d * (code - 4).
+ *   bits = MOE_BITS_NL4 (20), non-linear 4-bit: the 4-bit block's 18 bytes
+ *             and nibble order; weight = d * codebook[code], codebook the
+ *             16 signed 8-bit values the weights come with (moe_qweights).
+ *             The thread's §四 names this block (32 values in 18 bytes) and
+ *             §三 pairs it as the down format with 3-bit gate/up formats;
+ *             the pages print no table, so the table is the caller's.
  * A matrix [rows][cols] is stored row by row, cols/32 blocks per row, with
  * no padding.  One expert's blob is gate [F][H] | up [F][H] | down [H][F]
  * (gate, up and down concatenated per expert, thread §三); experts follow
@@ -36,6 +42,11 @@
  * Gate and up share one bit width (`bits`); down may have its own
  * (`down_bits`), as the thread's §三 decode table pairs each gate/up format
  * with a down format (a 2- or 3-bit gate/up with a 4-bit down).
+ * The grouped GEMM (MOE_PATH_PREFILL) takes every pair of these formats;
+ * the decode path takes pairs of the 3- and 4-bit formats, the non-linear
+ * format throughout, and a 3-bit gate/up with a non-linear down.  For other
+ * pairs MOE_PATH_AUTO serves a decode window with the grouped GEMM and
+ * MOE_PATH_DECODE returns MOE_ERR_UNSUPPORTED.
  *
  * The compute calls read MOE_LAYOUT_PREPARED, written once per weight set by
  * moe_prepare_qweights: the same blocks and sizes, gate and up unchanged,
@@ -82,7 +93,7 @@ extern "C" {
 
 #define MOE_OK 0
 #define MOE_ERR_INVALID_ARG (-1)  /* null pointer, negative or inconsistent size */
-#define MOE_ERR_UNSUPPORTED (-2)  /* bits not 3/4, H or F not a multiple of 256, weights not prepared, ... */
+#define MOE_ERR_UNSUPPORTED (-2)  /* bits not 3/4/20, H or F not a multiple of 256, weights not prepared, ... */
 #define MOE_ERR_WORKSPACE (-3)    /* workspace smaller than moe_workspace_bytes */
 #define MOE_ERR_LAUNCH (-4)       /* a kernel launch failed */
 #define MOE_ERR_DEVICE (-5)       /* no usable gfx950 device / device query failed */
@@ -109,15 +120,20 @@ extern "C" {
 #define MOE_LAYOUT_ROWS 0      /* every matrix row by row, as stored on the pages */
 #define MOE_LAYOUT_PREPARED 1  /* down column-block-major: what the compute calls read */
 
+/* the non-linear 4-bit format (see "Weight format" above) */
+#define MOE_BITS_NL4 20
+
 /* Quantized expert weights (host struct; `data` is a device pointer). */
 typedef struct moe_qweights {
     const void *data;   /* (device) n_experts blobs back to back, see above */
-    int32_t bits;       /* 3 or 4: the gate and up projections */
+    int32_t bits;       /* 3, 4 or MOE_BITS_NL4: the gate and up projections */
     int32_t n_experts;  /* routed: E; shared: 1 */
     int32_t hidden;     /* H, multiple of 256 */
     int32_t ffn;        /* F, multiple of 256 */
     int32_t layout;     /* MOE_LAYOUT_*; the compute calls take MOE_LAYOUT_PREPARED only */
-    int32_t down_bits;  /* 3 or 4: the down projection; 0 = the same as bits */
+    int32_t down_bits;  /* 3, 4 or MOE_BITS_NL4: the down projection; 0 = the same as bits */
+    int8_t codebook[16]; /* MOE_BITS_NL4: the values codes 0..15 stand for (ignored otherwise);
+                            a shared expert must carry the routed experts' table */
 } moe_qweights;
 
 /* Library version (major*100 + minor). */
@@ -127,7 +143,7 @@ int moe_version(void);
 const char *moe_status_string(int status);
 
 /* Bytes of one expert blob: hidden * ffn/32 * (2 * B(bits) + B(down_bits)),
- * B = 18 (4-bit) or 14 (3-bit) bytes per block, down_bits 0 = bits; -1 if
+ * B = 18 (4-bit, non-linear 4-bit) or 14 (3-bit) bytes per block, down_bits 0 = bits; -1 if
  * the arguments are not a valid format and shape (pure host function). */
 int64_t moe_expert_bytes(int32_t bits, int32_t down_bits, int32_t hidden, int32_t ffn);
 

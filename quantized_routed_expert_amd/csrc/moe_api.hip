@@ -18,6 +18,7 @@ namespace moe {
 hipError_t decode_launch(const DecodeParams &P, int grid, hipStream_t st);
 int decode_occupancy(int bg, int bd, int x_f32, int lds);
 hipError_t decode_set_lds(int bg, int bd, int x_f32, int lds);
+bool decode_format_ok(int bg, int bd);
 hipError_t split_launch(const SplitParams &P, int grid, hipStream_t st);
 hipError_t split_set_lds(int bg, int bd, int T, int xf, int lds);
 hipError_t route_launch(const RouteParams &P, hipStream_t st);
@@ -147,7 +148,36 @@ int check_shape(int32_t T, int32_t E, int32_t k, int32_t H, int32_t F) {
 }
 
 int down_bits_of(const moe_qweights *w) { return w->down_bits ? w->down_bits : w->bits; }
-int block_bytes_of(int bits) { return bits == 4 ? 18 : 14; }
+// the block formats: 3-bit, 4-bit and the non-linear 4-bit (the 4-bit layout)
+bool valid_bits(int b) { return b == 3 || b == 4 || b == MOE_BITS_NL4; }
+bool valid_down_bits(int b) { return b == 0 || valid_bits(b); }
+bool uses_table(const moe_qweights *w) { return w->bits == MOE_BITS_NL4 || down_bits_of(w) == MOE_BITS_NL4; }
+int block_bytes_of(int bits) { return (bits == 4 || bits == MOE_BITS_NL4) ? 18 : 14; }
+// index of a format in the per-format launch caches
+int fmt_index(int bits) { return bits == 3 ? 0 : bits == 4 ? 1 : 2; }
+
+// The non-linear table as the kernels take it: byte tables of a 16-bit
+// float of each entry (fp16 for the decode kernel, bf16 for the grouped
+// GEMM), both exact for 8-bit integers.
+NlTab nl_tables(const int8_t *cb, bool bf16) {
+    NlTab t;
+    memset(&t, 0, sizeof(t));
+    for (int c = 0; c < 16; ++c) {
+        uint16_t h;
+        if (bf16) {
+            const float f = (float)cb[c];
+            uint32_t u;
+            memcpy(&u, &f, 4);
+            h = (uint16_t)(u >> 16);  // exact: an 8-bit integer needs no rounding
+        } else {
+            const _Float16 f = (_Float16)cb[c];
+            memcpy(&h, &f, 2);
+        }
+        t.t[c >> 2] |= (uint32_t)(h & 0xFF) << (8 * (c & 3));
+        t.t[4 + (c >> 2)] |= (uint32_t)(h >> 8) << (8 * (c & 3));
+    }
+    return t;
+}
 // bytes of one expert blob: gate and up [F][H] in `bits`, down [H][F] in `dbits`
 size_t expert_bytes_of(int bits, int dbits, int H, int F) {
     return (size_t)H * (F / 32) * (2 * block_bytes_of(bits) + block_bytes_of(dbits));
@@ -155,8 +185,7 @@ size_t expert_bytes_of(int bits, int dbits, int H, int F) {
 
 int check_weights(const moe_qweights *w, int H, int n_experts) {
     if (!w || !w->data) return MOE_ERR_INVALID_ARG;
-    if (w->bits != 3 && w->bits != 4) return MOE_ERR_UNSUPPORTED;
-    if (w->down_bits != 0 && w->down_bits != 3 && w->down_bits != 4) return MOE_ERR_UNSUPPORTED;
+    if (!valid_bits(w->bits) || !valid_down_bits(w->down_bits)) return MOE_ERR_UNSUPPORTED;
     if (w->layout != MOE_LAYOUT_PREPARED) return MOE_ERR_UNSUPPORTED;
     if (w->hidden != H) return MOE_ERR_INVALID_ARG;
     if (n_experts >= 0 && w->n_experts != n_experts) return MOE_ERR_INVALID_ARG;
@@ -288,6 +317,7 @@ int launch_err(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 // chunks, and the LDS layout fits one workgroup per CU.
 constexpr int DEC_LDS_BUDGET = 160 * 1024;
 bool decode_fits(int T, int E, int k, int H, int F, int Fs, int bits, int dbits, int x_dtype) {
+    if (!decode_format_ok(bits, dbits)) return false;
     const int xf = x_dtype == MOE_DTYPE_F32;
     const int per = xf ? DEC_XG_F32 : DEC_XG_BF16;
     if ((long long)T * (H / 8) > (long long)per * DEC_THREADS) return false;
@@ -345,6 +375,8 @@ int split_units(int T, int k, int H, int combine, int G) {
 
 bool split_fits(int T, int E, int k, int H, int F, int Fs, int bits, int dbits, int combine, int G) {
     (void)E;
+    // integer dot products of linear codes: the 3- and 4-bit formats only
+    if ((bits != 3 && bits != 4) || (dbits != 3 && dbits != 4)) return false;
     if (T < 1 || T > SPL_MAX_T || k > 32 || T * k > 64) return false;
     if (H != 256 && H != 512 && H != 1024 && H != 2048) return false;
     if (F > 4096 || Fs > 4096) return false;
@@ -382,7 +414,7 @@ const char *moe_status_string(int status) {
 }
 
 int64_t moe_expert_bytes(int32_t bits, int32_t down_bits, int32_t hidden, int32_t ffn) {
-    if ((bits != 3 && bits != 4) || (down_bits != 0 && down_bits != 3 && down_bits != 4)) return -1;
+    if (!valid_bits(bits) || !valid_down_bits(down_bits)) return -1;
     if (hidden <= 0 || ffn <= 0 || hidden % 32 || ffn % 32) return -1;
     return (int64_t)expert_bytes_of(bits, down_bits ? down_bits : bits, hidden, ffn);
 }
@@ -407,8 +439,7 @@ int64_t moe_workspace_bytes(int32_t T, int32_t E, int32_t k, int32_t hidden, int
 int moe_prepare_qweights(const moe_qweights *src, void *dst, int64_t stream) {
     if (!src || !src->data || !dst) return MOE_ERR_INVALID_ARG;
     if (src->layout != MOE_LAYOUT_ROWS) return MOE_ERR_INVALID_ARG;
-    if (src->bits != 3 && src->bits != 4) return MOE_ERR_UNSUPPORTED;
-    if (src->down_bits != 0 && src->down_bits != 3 && src->down_bits != 4) return MOE_ERR_UNSUPPORTED;
+    if (!valid_bits(src->bits) || !valid_down_bits(src->down_bits)) return MOE_ERR_UNSUPPORTED;
     if (src->n_experts <= 0 || src->hidden <= 0 || src->ffn <= 0) return MOE_ERR_INVALID_ARG;
     if (src->n_experts > MOE_MAX_EXPERTS || src->hidden % 256 || src->ffn % 256 || src->hidden > 65536 ||
         src->ffn > 65536)
@@ -580,6 +611,7 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
     P.Fs = shared ? shared->ffn : 0;
     P.bits = routed->bits;
     P.dbits = dbits;
+    P.nl = nl_tables(routed->codebook, false);
     P.eb = expert_bytes_of(routed->bits, dbits, routed->hidden, routed->ffn);
     P.x_f32 = x_f32;
     P.mode = mode | (shared ? DEC_MODE_SHARED : 0);
@@ -589,11 +621,11 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
     const int lds = decode_lds_layout(P, x_f32 ? 2 : 1);
     if (lds > dv.lds_max) return MOE_ERR_UNSUPPORTED;
     static std::mutex mu;
-    static int lds_set[2][2][2] = {};
+    static int lds_set[3][3][2] = {};
     int occ;
     {
         std::lock_guard<std::mutex> lk(mu);
-        int &cur = lds_set[P.bits == 4][dbits == 4][x_f32 ? 1 : 0];
+        int &cur = lds_set[fmt_index(P.bits)][fmt_index(dbits)][x_f32 ? 1 : 0];
         if (lds > cur) {
             if (decode_set_lds(P.bits, dbits, x_f32, lds) != hipSuccess) return MOE_ERR_LAUNCH;
             cur = lds;
@@ -642,6 +674,7 @@ int prefill_gemms(const void *x, int x_f32, int T, int E, int k, const moe_qweig
     const int dbits = down_bits_of(routed);
     G.rowG = (G.H / 32) * block_bytes_of(routed->bits);
     G.eb = expert_bytes_of(routed->bits, dbits, routed->hidden, routed->ffn);
+    G.nl = nl_tables(routed->codebook, true);
     G.prefix = at<int32_t>(ws, L.prefix_gu);
     hipError_t e = prefill_gemm_launch(0, routed->bits, G, dv.cus, st);  // gate/up in their format
     if (e != hipSuccess) return MOE_ERR_LAUNCH;
@@ -706,8 +739,10 @@ int moe_layer_forward(const void *x, int32_t x_dtype, const float *logits, int32
     rc = check_shape(T, E, k, H, routed->ffn);
     if (rc) return rc;
     // every launch reads the shared expert as one more slot in the routed
-    // experts' format
+    // experts' format (and table)
     if (shared && (shared->bits != routed->bits || down_bits_of(shared) != down_bits_of(routed)))
+        return MOE_ERR_UNSUPPORTED;
+    if (shared && uses_table(routed) && memcmp(shared->codebook, routed->codebook, 16) != 0)
         return MOE_ERR_UNSUPPORTED;
     const int Fs = shared ? shared->ffn : 0;
     int p = resolve_path(path, T);

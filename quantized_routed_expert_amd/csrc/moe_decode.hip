@@ -164,7 +164,7 @@ struct Pair<4, NP> {
         w5 = lds_u32(buf + o + 20 + 4 * g);
         load_a<NP>(a, ab, 2 * p, a_stride, part_off);
     }
-    __device__ __forceinline__ BVal<4> get(int i, int g) const {
+    __device__ __forceinline__ BVal<4> get(int i, int g, const NlTab &) const {
         BVal<4> v;
         if (i == 0) {
             v.b = unpack4(__builtin_amdgcn_alignbyte(w1, w0, 2u));  // code bytes 2+4g .. 5+4g
@@ -172,6 +172,22 @@ struct Pair<4, NP> {
         } else {
             v.b = unpack4(w5);  // code bytes 20+4g .. 23+4g
             v.d = half_bits_to_float(d4 >> 16);
+        }
+        return v;
+    }
+};
+
+// Non-linear 4-bit pair: the 4-bit pair's bytes, codes looked up in the table.
+template <int NP>
+struct Pair<MOE_FMT_NL4, NP> : Pair<4, NP> {
+    __device__ __forceinline__ BVal<MOE_FMT_NL4> get(int i, int g, const NlTab &tb) const {
+        BVal<MOE_FMT_NL4> v;
+        if (i == 0) {
+            v.b = unpack_nl4(__builtin_amdgcn_alignbyte(this->w1, this->w0, 2u), tb);
+            v.d = half_bits_to_float(this->d0);
+        } else {
+            v.b = unpack_nl4(this->w5, tb);
+            v.d = half_bits_to_float(this->d4 >> 16);
         }
         return v;
     }
@@ -190,7 +206,7 @@ struct Pair<3, NP> {
         for (int i = 0; i < 7; ++i) w[i] = lds_u32(buf + o + 4 * i);
         load_a<NP>(a, ab, 2 * p, a_stride, part_off);
     }
-    __device__ __forceinline__ BVal<3> get(int i, int g) const {
+    __device__ __forceinline__ BVal<3> get(int i, int g, const NlTab &) const {
         BVal<3> v;
         if (i == 0) {
             v.b = unpack3(__builtin_amdgcn_alignbyte(w[1], w[0], 2u), __builtin_amdgcn_alignbyte(w[2], w[1], 2u),
@@ -219,8 +235,8 @@ struct PairDot {
     float s0, s1;
 };
 template <int BITS, int NP>
-__device__ __forceinline__ PairDot pair_dot(const Pair<BITS, NP> &pr, int g) {
-    const BVal<BITS> v0 = pr.get(0, g), v1 = pr.get(1, g);
+__device__ __forceinline__ PairDot pair_dot(const Pair<BITS, NP> &pr, int g, const NlTab &tb) {
+    const BVal<BITS> v0 = pr.get(0, g, tb), v1 = pr.get(1, g, tb);
     return PairDot{block_dot<BITS, NP>(v0, pr.a[0]), block_dot<BITS, NP>(v1, pr.a[1]), v0.d, v1.d};
 }
 // acc += s0 * d0 then s1 * d1 (the block order of the sum)
@@ -243,22 +259,22 @@ __device__ __forceinline__ void pair_apply(float4v &acc, const PairDot &q) {
 // blocks, part_off bytes between the NP parts.
 template <int BITS, int NP>
 __device__ __forceinline__ void chunk_mma(float4v &acc, const uint8_t *buf, int rs, int cb, int n, int g,
-                                          const uint8_t *ab, int a_stride, int part_off) {
+                                          const uint8_t *ab, int a_stride, int part_off, const NlTab &tb) {
     const int ro = n * rs;
     const int np = cb >> 1;
     Pair<BITS, NP> pa, pb;
     pa.load(buf, ro, 0, g, ab, a_stride, part_off);
     pb.load(buf, ro, 1, g, ab, a_stride, part_off);
-    PairDot qa = pair_dot<BITS, NP>(pa, g);                        // pair 0
+    PairDot qa = pair_dot<BITS, NP>(pa, g, tb);                        // pair 0
     pa.load(buf, ro, 2 < np ? 2 : 0, g, ab, a_stride, part_off);  // (np = 2: unused re-read)
-    PairDot qb = pair_dot<BITS, NP>(pb, g);                        // pair 1
+    PairDot qb = pair_dot<BITS, NP>(pb, g, tb);                        // pair 1
     pair_apply(acc, qa);
     pb.load(buf, ro, 3 < np ? 3 : 0, g, ab, a_stride, part_off);
     for (int p = 2; p < np; p += 2) {
-        qa = pair_dot<BITS, NP>(pa, g);  // pair p
+        qa = pair_dot<BITS, NP>(pa, g, tb);  // pair p
         pair_apply(acc, qb);             // pair p - 1
         pa.load(buf, ro, p + 2 < np ? p + 2 : 0, g, ab, a_stride, part_off);  // (last round: unused re-read)
-        qb = pair_dot<BITS, NP>(pb, g);  // pair p + 1
+        qb = pair_dot<BITS, NP>(pb, g, tb);  // pair p + 1
         pair_apply(acc, qa);             // pair p
         pb.load(buf, ro, p + 3 < np ? p + 3 : 0, g, ab, a_stride, part_off);
     }
@@ -294,6 +310,16 @@ struct DnBlk<4> {
 };
 
 template <>
+struct DnBlk<MOE_FMT_NL4> : DnBlk<4> {
+    __device__ __forceinline__ BVal<MOE_FMT_NL4> get(uint32_t sh_d, uint32_t sh_c, const NlTab &tb) const {
+        BVal<MOE_FMT_NL4> v;
+        v.b = unpack_nl4(__builtin_amdgcn_alignbyte(hi, lo, sh_c), tb);
+        v.d = half_bits_to_float(dw >> sh_d);
+        return v;
+    }
+};
+
+template <>
 struct DnBlk<3> {
     uint32_t dw, r0, r1, r2, r3;
     half8 a[2];
@@ -322,17 +348,18 @@ struct DnBlk<3> {
 // ab + j*128.  Two operand sets: block j+1's reads in flight while j computes.
 template <int BITS>
 __device__ __forceinline__ void dn_chunk_mma(float4v &acc, const uint8_t *buf, int rs, int cb, int n, int g,
-                                             const uint8_t *ab) {
-    constexpr int bb = BITS == 4 ? 18 : 14;
+                                             const uint8_t *ab, const NlTab &tb) {
+    constexpr int bb = blk_bytes(BITS);
     const int a0 = n * bb;                                   // block 0 of row n
     const uint32_t par = (uint32_t)(n & 1);                  // a0 mod 4 = 2 * par
     const uint32_t sh_d = 16u * par;
-    const int q = a0 + 2 + (BITS == 4 ? 4 * g : 0);          // first code / low-part byte of this lane
+    const int q = a0 + 2 + (nib_layout(BITS) ? 4 * g : 0);   // first code / low-part byte of this lane
     const int qa = q & ~3;
     const uint32_t sh_c = (uint32_t)(q & 3);
     auto step = [&](const DnBlk<BITS> &b) {
         BVal<BITS> v;
-        if constexpr (BITS == 4) v = b.get(sh_d, sh_c);
+        if constexpr (BITS == MOE_FMT_NL4) v = b.get(sh_d, sh_c, tb);
+        else if constexpr (BITS == 4) v = b.get(sh_d, sh_c);
         else v = b.get(sh_d, sh_c, g);
         const float4v d = block_dot<BITS, 2>(v, b.a);
         acc.x = fmaf(v.d, d.x, acc.x);
@@ -361,7 +388,7 @@ __device__ __forceinline__ void dn_chunk_mma(float4v &acc, const uint8_t *buf, i
 template <int BITS>
 __host__ __device__ constexpr int xslot(int e) {
     // pos_in_block(BITS, 0, e) -> its index among the loaded elements
-    return BITS == 4 ? (pos_in_block(4, 0, e) < 16 ? pos_in_block(4, 0, e) : pos_in_block(4, 0, e) - 12)
+    return nib_layout(BITS) ? (pos_in_block(4, 0, e) < 16 ? pos_in_block(4, 0, e) : pos_in_block(4, 0, e) - 12)
                      : pos_in_block(3, 0, e);
 }
 
@@ -370,7 +397,7 @@ struct XGroup {
     uint32_t w[4 * XPARTS];  // bf16: 8 values in 4 dwords; fp32: 8 dwords
     // row: the token's activations; base: element index 4g (4-bit) or 8g (3-bit) of block b
     __device__ __forceinline__ void load(const void *row, int base) {
-        if constexpr (BITS == 4) {
+        if constexpr (nib_layout(BITS)) {
             if constexpr (XPARTS == 1) {
                 const uint2 a = *(const uint2 *)((const uint16_t *)row + base);
                 const uint2 b = *(const uint2 *)((const uint16_t *)row + base + 16);
@@ -453,7 +480,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
     // ---- gate/up geometry (host-computed): a unit is 16 feature rows x one K
     // chunk of one matrix (one wave); a task is the 8 (or 16) units that
     // complete whole 16-feature groups (one workgroup)
-    constexpr int bbD = BD == 4 ? 18 : 14;  // bytes of a down block
+    constexpr int bbD = blk_bytes(BD);  // bytes of a down block
     const int cbH = P.cbH, segH = P.segH, rowH = P.rowH, rsH = P.rsH;
     const int lg_nchH = P.lg_nchH, lg_upt = P.lg_upt, lg_nfgT = P.lg_nfgT, rounds = P.rounds;
     const int nchH = 1 << lg_nchH, upt = 1 << lg_upt, nfgT = 1 << lg_nfgT;
@@ -516,7 +543,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
                 const int gc = ok ? grp : 0;  // (an in-bounds load for lanes without a group)
                 const int t = (int)__umulhi((uint32_t)gc, P.m_xgrp);
                 const int rem = gc - t * P.xgrp;  // 4 b + g
-                const int base = (rem >> 2) * 32 + (BG == 4 ? 4 : 8) * (rem & 3);
+                const int base = (rem >> 2) * 32 + (nib_layout(BG) ? 4 : 8) * (rem & 3);
                 xg[q].load((const uint8_t *)P.x + (size_t)t * H * (XPARTS == 1 ? 2 : 4), base);
                 xg_t[q] = ok ? t : -1;
                 xg_pos[q] = rem;
@@ -850,7 +877,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             // (a register array indexed by rho would be read and written through
             // select chains over all its elements)
             float4v acc = {0.f, 0.f, 0.f, 0.f};
-            chunk_mma<BG, XPARTS>(acc, s_chunk, rsH, cbH, n_lane, g_lane, ab, 64, T * P.x_rs);
+            chunk_mma<BG, XPARTS>(acc, s_chunk, rsH, cbH, n_lane, g_lane, ab, 64, T * P.x_rs, P.nl);
             if (rho == 0) accr[0] = acc;
             else accr[1] = acc;
             if (first_task && rho == 0) TRACEW(11);
@@ -1119,7 +1146,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
                     c_next = true;
                 }
             }
-            dn_chunk_mma<BD>(acc, s_chunk, rsF, cbF, n_lane, g_lane, ab + (size_t)ci * cbF * 128);
+            dn_chunk_mma<BD>(acc, s_chunk, rsF, cbF, n_lane, g_lane, ab + (size_t)ci * cbF * 128, P.nl);
             wave_lds_handoff();
         }
         // o = acc * 2^-sc_m; weighted write per pair
@@ -1176,16 +1203,25 @@ static hipError_t set_lds_t(int lds) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
 }
 
-// compile-time formats (gate/up bits, down bits) and activation parts (1: bf16, 2: fp32)
+// compile-time formats (gate/up bits, down bits) and activation parts (1: bf16, 2: fp32);
+// the pairs built here are the ones decode_format_ok accepts
 #define DECODE_DISPATCH_F(FN, BG, BD, ...) \
     return xf ? FN<BG, BD, 2>(__VA_ARGS__) : FN<BG, BD, 1>(__VA_ARGS__)
-#define DECODE_DISPATCH(FN, ...)                                             \
-    do {                                                                     \
-        if (bg == 4 && bd == 4) DECODE_DISPATCH_F(FN, 4, 4, __VA_ARGS__);    \
-        if (bg == 3 && bd == 4) DECODE_DISPATCH_F(FN, 3, 4, __VA_ARGS__);    \
-        if (bg == 4 && bd == 3) DECODE_DISPATCH_F(FN, 4, 3, __VA_ARGS__);    \
-        DECODE_DISPATCH_F(FN, 3, 3, __VA_ARGS__);                            \
+#define DECODE_DISPATCH(FN, ...)                                                                    \
+    do {                                                                                            \
+        if (bg == 4 && bd == 4) DECODE_DISPATCH_F(FN, 4, 4, __VA_ARGS__);                           \
+        if (bg == 3 && bd == 4) DECODE_DISPATCH_F(FN, 3, 4, __VA_ARGS__);                           \
+        if (bg == 4 && bd == 3) DECODE_DISPATCH_F(FN, 4, 3, __VA_ARGS__);                           \
+        if (bg == 3 && bd == 3) DECODE_DISPATCH_F(FN, 3, 3, __VA_ARGS__);                           \
+        if (bg == MOE_FMT_NL4 && bd == MOE_FMT_NL4) DECODE_DISPATCH_F(FN, MOE_FMT_NL4, MOE_FMT_NL4, __VA_ARGS__); \
+        if (bg == 3 && bd == MOE_FMT_NL4) DECODE_DISPATCH_F(FN, 3, MOE_FMT_NL4, __VA_ARGS__);       \
+        return hipErrorInvalidValue;                                                                \
     } while (0)
+
+bool decode_format_ok(int bg, int bd) {
+    return ((bg == 3 || bg == 4) && (bd == 3 || bd == 4)) || (bg == MOE_FMT_NL4 && bd == MOE_FMT_NL4) ||
+           (bg == 3 && bd == MOE_FMT_NL4);
+}
 
 hipError_t decode_launch(const DecodeParams &P, int grid, hipStream_t st) {
     const int bg = P.bits, bd = P.dbits, xf = P.x_f32;

@@ -5,6 +5,10 @@
 //   4-bit, 18 bytes: d, then byte 2+i = code i (low nibble) | code i+16 (high nibble)
 //   3-bit, 14 bytes: d, 8 bytes of 2-bit low parts (code i at bit 2*(i/8) of byte
 //                    2+(i%8)), 32-bit word at bytes 10..13 holding bit 2 of code i at bit i
+//   non-linear 4-bit (format code 20), 18 bytes: the 4-bit layout; weight =
+//                    d * table[code], a 16-entry table of signed 8-bit values
+//                    (the same section names this block; the table comes with
+//                    the weights)
 //
 // MFMA mapping (v_mfma_f32_16x16x32_{f16,bf16}, K = 32 = one block): lane l holds
 // row l%16 of A, column l%16 of B and the k-group l/16 of both; the result D
@@ -25,7 +29,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int block_bytes(int bits) { return bits == 4 ? 18 : 14; }
+// Formats with the 4-bit block's layout (linear and non-linear codes).
+__host__ __device__ constexpr bool nib_layout(int bits) { return bits == 4 || bits == MOE_FMT_NL4; }
+__host__ __device__ constexpr int blk_bytes(int bits) { return nib_layout(bits) ? 18 : 14; }
 
 // ---------------------------------------------------------------------------
 // Element order inside one k-group (8 values) for each format.
@@ -33,7 +39,7 @@ __device__ __forceinline__ int block_bytes(int bits) { return bits == 4 ? 18 : 1
 // a lane of k-group g feeds.  Used to lay activations out to match.
 // ---------------------------------------------------------------------------
 __host__ __device__ constexpr int pos_in_block(int bits, int g, int e) {
-    if (bits == 4) {
+    if (nib_layout(bits)) {
         // e: 0:(4g) 1:(4g+2) 2:(16+4g) 3:(16+4g+2) 4:(4g+1) 5:(4g+3) 6:(16+4g+1) 7:(16+4g+3)
         int r = ((e >> 2) & 1) + ((e & 1) << 1);
         return 4 * g + r + ((e >> 1) & 1) * 16;
@@ -45,7 +51,7 @@ __host__ __device__ constexpr int pos_in_block(int bits, int g, int e) {
 
 // Inverse: weight i of a block -> (k-group g, slot e).
 __host__ __device__ __forceinline__ void group_slot_of(int bits, int i, int &g, int &e) {
-    if (bits == 4) {
+    if (nib_layout(bits)) {
         int r = i & 3, hi = (i >> 4) & 1;
         g = (i & 15) >> 2;
         e = ((r & 1) << 2) | (hi << 1) | (r >> 1);
@@ -113,6 +119,37 @@ __device__ __forceinline__ half8 unpack3(uint32_t qs0, uint32_t qs1, uint32_t qh
     r.y = __builtin_amdgcn_perm(h0, h0, 0x070C060Cu);  // weights 2, 3
     r.z = __builtin_amdgcn_perm(h1, h1, 0x050C040Cu);
     r.w = __builtin_amdgcn_perm(h1, h1, 0x070C060Cu);
+    return __builtin_bit_cast(half8, r);
+}
+
+// Non-linear 4-bit codes -> 16-bit floats of their table values (fp16 or
+// bf16: both hold 8-bit integers exactly), from the two byte tables of an
+// NlTab (low bytes of entries 0..15 in t[0..3], high bytes in t[4..7]).
+// c: four codes 0..15, one per byte.  v_perm_b32 picks among 8 bytes, so
+// entries 0..7 and 8..15 are looked up apart and bit 3 of each code chooses
+// (m: 0xFF in the bytes whose code is 8..15; (t << 5) - (t >> 3) turns each
+// set bit 3 into a full byte, with no carry between bytes).
+__device__ __forceinline__ void nl_lookup(uint32_t c, const NlTab &tb, uint32_t &lo, uint32_t &hi) {
+    const uint32_t s = c & 0x07070707u;
+    const uint32_t t = c & 0x08080808u;
+    const uint32_t m = (t << 5) - (t >> 3);
+    const uint32_t l0 = __builtin_amdgcn_perm(tb.t[1], tb.t[0], s), l1 = __builtin_amdgcn_perm(tb.t[3], tb.t[2], s);
+    const uint32_t h0 = __builtin_amdgcn_perm(tb.t[5], tb.t[4], s), h1 = __builtin_amdgcn_perm(tb.t[7], tb.t[6], s);
+    lo = (l1 & m) | (l0 & ~m);
+    hi = (h1 & m) | (h0 & ~m);
+}
+
+// Non-linear 4-bit: q = bytes qs[4g..4g+3] of one block -> 8 fp16 table
+// values in the order of pos_in_block(4, g, .) (tb: fp16 byte tables).
+__device__ __forceinline__ half8 unpack_nl4(uint32_t q, const NlTab &tb) {
+    uint32_t l0, h0, l1, h1;
+    nl_lookup(q & 0x0F0F0F0Fu, tb, l0, h0);         // weights 4g .. 4g+3 (low nibbles)
+    nl_lookup((q >> 4) & 0x0F0F0F0Fu, tb, l1, h1);  // weights 16+4g .. 16+4g+3 (high nibbles)
+    u32x4 r;  // (low byte, high byte) of two values per dword
+    r.x = __builtin_amdgcn_perm(h0, l0, 0x06020400u);  // weights 4g, 4g+2
+    r.y = __builtin_amdgcn_perm(h1, l1, 0x06020400u);  // 16+4g, 16+4g+2
+    r.z = __builtin_amdgcn_perm(h0, l0, 0x07030501u);  // 4g+1, 4g+3
+    r.w = __builtin_amdgcn_perm(h1, l1, 0x07030501u);  // 16+4g+1, 16+4g+3
     return __builtin_bit_cast(half8, r);
 }
 

@@ -5,6 +5,17 @@
 
 namespace moe {
 
+// Format code of the non-linear 4-bit block (the 4-bit layout, codes index a
+// 16-entry table of signed 8-bit values).
+#define MOE_FMT_NL4 20
+
+// A non-linear 4-bit table as two byte tables of 16-bit floats of its
+// entries: t[0..3] = low bytes of entries 0..15, t[4..7] = high bytes (fp16
+// for the decode kernels, bf16 for the grouped GEMM).
+struct NlTab {
+    uint32_t t[8];
+};
+
 // ---------------------------------------------------------------------------
 // Fused decode launch (routing + grouping + gate/up/SwiGLU + down + weighted
 // write + combine in one kernel, T <= 16 rows).
@@ -100,6 +111,7 @@ struct DecodeParams {
     int T, E, k, H, F, Fs;     // Fs = shared ffn (0 = none)
     int bits, x_f32, mode, max_slots;  // bits: gate and up projections
     int dbits;                 // bit width of the down projection
+    NlTab nl;                  // fp16 tables of the non-linear format (when a width is MOE_FMT_NL4)
     size_t eb;                 // bytes of one routed expert blob
     int h_stride;              // words per hll row (Fmax)
     int x_rs, h_rs;            // LDS bytes per token row: activations (one part), staged h (hi + lo)
@@ -236,6 +248,7 @@ struct GemmParams {
     int T, E, k, H, F, Fs, h_stride, x_f32;
     int rowG;               // bytes of one gate/up row (H/32 blocks of the gate/up format)
     size_t eb;              // bytes of one routed expert blob
+    NlTab nl;               // bf16 tables of the non-linear format (when a width is MOE_FMT_NL4)
 };
 
 struct CombineParams {

@@ -234,15 +234,30 @@ __device__ __forceinline__ u32x4 deq4_group(uint32_t qa, uint32_t qb, uint32_t n
     return r;
 }
 
+// Non-linear 4-bit: the 4-bit block's codes (same bytes and nibbles as
+// deq4_group), each looked up in the bf16 byte tables of the format's table
+// (exact: bf16 holds 8-bit integers), natural order.
+__device__ __forceinline__ u32x4 deqnl_group(uint32_t qa, uint32_t qb, uint32_t ns, const NlTab &tb) {
+    uint32_t la, ha, lb, hb;
+    nl_lookup((qa >> ns) & 0x0F0F0F0Fu, tb, la, ha);
+    nl_lookup((qb >> ns) & 0x0F0F0F0Fu, tb, lb, hb);
+    u32x4 r;  // (low byte, high byte) of two values per dword
+    r.x = __builtin_amdgcn_perm(ha, la, 0x05010400u);  // weights 0, 1
+    r.y = __builtin_amdgcn_perm(ha, la, 0x07030602u);  // weights 2, 3
+    r.z = __builtin_amdgcn_perm(hb, lb, 0x05010400u);
+    r.w = __builtin_amdgcn_perm(hb, lb, 0x07030602u);
+    return r;
+}
+
 // Raw dwords of weight blocks as loaded from HBM, and the block fields.
 //   MODE 0 (gate/up): NW = one pair of consecutive blocks of one weight row
-//     (3-bit: 28 bytes = 7 dwords; 4-bit: 36 bytes = 9 dwords).
+//     (3-bit: 28 bytes = 7 dwords; 4-bit layouts: 36 bytes = 9 dwords).
 //   MODE 1 (down, column-block-major): one block of an even or odd row, the
 //     row pair's dwords from the block's first one (3-bit: 4, 4-bit: 5).
 template <int BITS>
 struct BFields {
     uint32_t d;      // fp16 scale bits (low half)
-    uint32_t q[BITS == 4 ? 4 : 3];  // 4-bit: code dwords; 3-bit: low parts (2), third bits
+    uint32_t q[nib_layout(BITS) ? 4 : 3];  // 4-bit layouts: code dwords; 3-bit: low parts (2), third bits
 };
 
 // Fields of one block from a run of dwords: `odd` = the block starts 2 bytes
@@ -251,7 +266,7 @@ struct BFields {
 template <int BITS>
 __device__ __forceinline__ BFields<BITS> block_fields(const uint32_t *w, bool odd, int o) {
     BFields<BITS> f;
-    constexpr int NQ = BITS == 4 ? 4 : 3;
+    constexpr int NQ = nib_layout(BITS) ? 4 : 3;
     if (!odd) {
         f.d = w[0];
 #pragma unroll
@@ -265,9 +280,12 @@ __device__ __forceinline__ BFields<BITS> block_fields(const uint32_t *w, bool od
 }
 
 template <int BITS>
-__device__ __forceinline__ u32x4 deq_group(const BFields<BITS> &f, uint32_t g) {
+__device__ __forceinline__ u32x4 deq_group(const BFields<BITS> &f, uint32_t g, const NlTab &tb) {
     if constexpr (BITS == 3) {
         return deq3_group(f.q[0], f.q[1], f.q[2], g);
+    } else if constexpr (BITS == MOE_FMT_NL4) {
+        const bool odd = g & 1u;
+        return deqnl_group(odd ? f.q[2] : f.q[0], odd ? f.q[3] : f.q[1], 4u * (g >> 1), tb);
     } else {
         const bool odd = g & 1u;
         return deq4_group(odd ? f.q[2] : f.q[0], odd ? f.q[3] : f.q[1], 4u * (g >> 1));
@@ -307,7 +325,7 @@ struct PfCfg {
     // ring slots: steps in flight + the one computed (fp32 activations are
     // split on the way into LDS, which waits for every load: two slots)
     static constexpr int NS = XF32 ? 2 : 4;
-    static constexpr int bb = BITS == 4 ? 18 : 14;
+    static constexpr int bb = blk_bytes(BITS);
     // weight dwords per step: gate/up 256 rows x KS blocks (row runs of
     // KS*bb bytes); down KS column blocks x 256 rows (one run each)
     static constexpr int STEP_DW = 256 * KS * bb / 4;
@@ -323,7 +341,7 @@ struct PfCfg {
     static constexpr int NW = 2 * bb / 4;
     static constexpr int L = LW + (XF32 ? 0 : 1);   // direct-to-LDS loads per thread per step
     static_assert(STEP_DW * 4 == 256 * KS * bb, "whole dwords");
-    static_assert(NW == (BITS == 4 ? 9 : 7) && (MODE == 1 || KS == 2), "a pair is two blocks");
+    static_assert(NW == (nib_layout(BITS) ? 9 : 7) && (MODE == 1 || KS == 2), "a pair is two blocks");
     static_assert(RING + ((5 * (MOE_MAX_EXPERTS_DEV + 1) + 1) * 4 + 15) / 16 * 16 <= 159 * 1024,
                   "the ring and the largest slot plan fit one workgroup's LDS");
     static_assert(A_PIECES == PF_THREADS * (MODE == 0 && XF32 ? 2 : 1), "one piece per thread (two for fp32 x)");
@@ -467,9 +485,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, lds_u8 *ring, con
             for (int f = 0; f < NB; ++f) {
                 // fragment f: gate/up pass f, or down n-tile f (row parity f)
                 BFields<BITS> fl;
-                if (MODE == 0) fl = block_fields<BITS>(rw[f], blk == 1, BITS == 4 ? 4 : 3);
-                else fl = block_fields<BITS>(rw[blk], f == 1, BITS == 4 ? 4 : 3);
-                const bf16x8 bq = __builtin_bit_cast(bf16x8, deq_group<BITS>(fl, (uint32_t)g_lane));
+                if (MODE == 0) fl = block_fields<BITS>(rw[f], blk == 1, nib_layout(BITS) ? 4 : 3);
+                else fl = block_fields<BITS>(rw[blk], f == 1, nib_layout(BITS) ? 4 : 3);
+                const bf16x8 bq = __builtin_bit_cast(bf16x8, deq_group<BITS>(fl, (uint32_t)g_lane, P.nl));
                 const float d = half_bits_to_float(fl.d);
                 // the m-tiles' MFMAs issue back to back, then their scaling
                 float4v dd[MT];
@@ -699,10 +717,15 @@ static hipError_t gemm_t(const GemmParams &P, int cus, hipStream_t st) {
 hipError_t prefill_gemm_launch(int mode, int bits, const GemmParams &P, int cus, hipStream_t st) {
     if (mode == 0) {
         if (bits == 4) return P.x_f32 ? gemm_t<0, 4, 1>(P, cus, st) : gemm_t<0, 4, 0>(P, cus, st);
-        return P.x_f32 ? gemm_t<0, 3, 1>(P, cus, st) : gemm_t<0, 3, 0>(P, cus, st);
+        if (bits == MOE_FMT_NL4)
+            return P.x_f32 ? gemm_t<0, MOE_FMT_NL4, 1>(P, cus, st) : gemm_t<0, MOE_FMT_NL4, 0>(P, cus, st);
+        if (bits == 3) return P.x_f32 ? gemm_t<0, 3, 1>(P, cus, st) : gemm_t<0, 3, 0>(P, cus, st);
+        return hipErrorInvalidValue;
     }
     if (bits == 4) return gemm_t<1, 4, 0>(P, cus, st);
-    return gemm_t<1, 3, 0>(P, cus, st);
+    if (bits == MOE_FMT_NL4) return gemm_t<1, MOE_FMT_NL4, 0>(P, cus, st);
+    if (bits == 3) return gemm_t<1, 3, 0>(P, cus, st);
+    return hipErrorInvalidValue;
 }
 
 hipError_t prefill_combine_launch(const CombineParams &P, hipStream_t st) {

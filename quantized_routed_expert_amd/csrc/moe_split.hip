@@ -916,7 +916,8 @@ static hipError_t split_attr_t(int lds) {
         if (bg == 4 && bd == 4) SPLIT_DISPATCH_T(FN, 4, 4, __VA_ARGS__);  \
         if (bg == 3 && bd == 4) SPLIT_DISPATCH_T(FN, 3, 4, __VA_ARGS__);  \
         if (bg == 4 && bd == 3) SPLIT_DISPATCH_T(FN, 4, 3, __VA_ARGS__);  \
-        SPLIT_DISPATCH_T(FN, 3, 3, __VA_ARGS__);                          \
+        if (bg == 3 && bd == 3) SPLIT_DISPATCH_T(FN, 3, 3, __VA_ARGS__);  \
+        return hipErrorInvalidValue;                                      \
     } while (0)
 
 hipError_t split_launch(const SplitParams &P, int grid, hipStream_t st) {

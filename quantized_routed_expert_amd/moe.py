@@ -48,7 +48,20 @@ class QWeights(ctypes.Structure):
     """moe_qweights: device pointer + format and shape of a set of experts."""
     _fields_ = [("data", ctypes.c_void_p), ("bits", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("hidden", ctypes.c_int32), ("ffn", ctypes.c_int32), ("layout", ctypes.c_int32),
-                ("down_bits", ctypes.c_int32)]
+                ("down_bits", ctypes.c_int32), ("codebook", ctypes.c_int8 * 16)]
+
+
+BITS_NL4 = 20  # the non-linear 4-bit format (4-bit layout, codes index a 16-entry int8 table)
+
+
+def _qw(data_ptr, bits, n_experts, hidden, ffn, layout, down_bits, codebook) -> QWeights:
+    q = QWeights(ctypes.c_void_p(data_ptr), bits, n_experts, hidden, ffn, layout, down_bits)
+    if codebook is not None:
+        cb = [int(v) for v in codebook]
+        if len(cb) != 16 or any(v < -128 or v > 127 for v in cb):
+            raise ValueError("codebook: 16 values in -128..127")
+        q.codebook = (ctypes.c_int8 * 16)(*cb)
+    return q
 
 
 _lib = None
@@ -123,23 +136,32 @@ def _xcode(x: torch.Tensor) -> int:
     raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
 
 
+def qweights_at(data_ptr, bits: int, n_experts: int, hidden: int, ffn: int, layout: int,
+                down_bits: int = 0, codebook=None) -> QWeights:
+    """QWeights for a raw device address (an int or ctypes.c_void_p)."""
+    if isinstance(data_ptr, ctypes.c_void_p):
+        data_ptr = data_ptr.value
+    return _qw(data_ptr, bits, n_experts, hidden, ffn, layout, down_bits, codebook)
+
+
 def qweights(data: torch.Tensor, bits: int, n_experts: int, hidden: int, ffn: int, layout: int,
-             down_bits: int = 0) -> QWeights:
+             down_bits: int = 0, codebook=None) -> QWeights:
     """Describe a uint8 device tensor holding n_experts expert blobs in the
     given block order (LAYOUT_ROWS or LAYOUT_PREPARED); gate/up in `bits`,
-    down in `down_bits` (0: the same)."""
-    return QWeights(ctypes.c_void_p(data.data_ptr()), bits, n_experts, hidden, ffn, layout, down_bits)
+    down in `down_bits` (0: the same); codebook: the 16 int8 values of the
+    non-linear format (BITS_NL4)."""
+    return _qw(data.data_ptr(), bits, n_experts, hidden, ffn, layout, down_bits, codebook)
 
 
 def prepare_qweights(data: torch.Tensor, bits: int, n_experts: int, hidden: int, ffn: int, out=None,
-                     stream=None, down_bits: int = 0):
+                     stream=None, down_bits: int = 0, codebook=None):
     """Blobs in the pages' row-by-row order (uint8 device tensor) -> a new
     tensor in the order the compute calls read; returns (tensor, QWeights)."""
     if out is None:
         out = torch.empty_like(data)
-    src = QWeights(ctypes.c_void_p(data.data_ptr()), bits, n_experts, hidden, ffn, LAYOUT_ROWS, down_bits)
+    src = _qw(data.data_ptr(), bits, n_experts, hidden, ffn, LAYOUT_ROWS, down_bits, codebook)
     _check(lib().moe_prepare_qweights(ctypes.byref(src), _ptr(out), _stream(stream)), "moe_prepare_qweights")
-    return out, qweights(out, bits, n_experts, hidden, ffn, LAYOUT_PREPARED, down_bits)
+    return out, qweights(out, bits, n_experts, hidden, ffn, LAYOUT_PREPARED, down_bits, codebook)
 
 
 def expert_bytes(bits: int, hidden: int, ffn: int, down_bits: int = 0) -> int:

@@ -169,19 +169,22 @@ def quantize(w: np.ndarray, bits: int, codebook=None) -> np.ndarray:
     d = fp16(absmax / qmax), code = clip(rint(w / d), -qmax, qmax) + 2^(bits-1)
     with qmax = 2^(bits-1) - 1 (all codes = bias when the block is zero).
     Non-linear 4-bit: d = fp16(absmax / max|codebook|), code = the entry
-    nearest w / d (the lowest code among equally near ones)."""
+    nearest w / d (on a tie the smaller value; among equal values the lower
+    code)."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     rows, cols = w.shape
     assert cols % 32 == 0
     if bits == BITS_NL4:
         cb = np.asarray(codebook, dtype=np.float32).reshape(16)
+        order = np.argsort(cb, kind="stable")
+        srt = cb[order]
+        mids = (srt[1:] + srt[:-1]) * np.float32(0.5)  # boundaries between neighbouring values
         blk = w.reshape(-1, 32)
         amax = np.abs(blk).max(axis=1)
         d16 = (amax / np.float32(np.abs(cb).max())).astype(np.float16)
         d32 = d16.astype(np.float32)
         safe = np.where(d32 > 0, d32, np.float32(1.0))
-        dist = np.abs((blk / safe[:, None])[:, :, None] - cb[None, None, :])
-        codes = np.argmin(dist, axis=2).astype(np.uint8)
+        codes = order[np.searchsorted(mids, blk / safe[:, None], side="left")].astype(np.uint8)
         return pack_codes(codes, d16, bits)
     qmax = (1 << (bits - 1)) - 1
     bias = 1 << (bits - 1)
@@ -197,15 +200,32 @@ def quantize(w: np.ndarray, bits: int, codebook=None) -> np.ndarray:
     return pack_codes(codes, d16, bits)
 
 
-def quantize_torch(w, bits: int):
+def quantize_torch(w, bits: int, codebook=None):
     """The encoder of ``quantize`` in torch, on w's device (any device): the
     same steps in the same fp32/fp16 arithmetic, so the same bytes for the
     same w.  w: float32 tensor [..., cols] (cols % 32 == 0) -> uint8 tensor
     [nblk * block_bytes], blocks in row-major order."""
     import torch
-    if bits not in (3, 4):
-        raise ValueError(f"quantize_torch encodes the 3- and 4-bit formats, not {bits}")
     w = w.contiguous().to(torch.float32)
+    if bits == BITS_NL4:
+        cb = torch.tensor(codebook, dtype=torch.float32, device=w.device).reshape(16)
+        srt, order = torch.sort(cb, stable=True)
+        mids = (srt[1:] + srt[:-1]) * 0.5
+        blk = w.reshape(-1, 32)
+        nblk = blk.shape[0]
+        amax = blk.abs().amax(dim=1)
+        d16 = (amax / cb.abs().max()).to(torch.float16)
+        d32 = d16.to(torch.float32)
+        safe = torch.where(d32 > 0, d32, torch.ones_like(d32))
+        codes = order[torch.searchsorted(mids, (blk / safe[:, None]).contiguous(), right=False)].to(torch.uint8)
+        out = torch.empty((nblk, 18), dtype=torch.uint8, device=w.device)
+        dv = d16.view(torch.int16).to(torch.int32)
+        out[:, 0] = (dv & 0xFF).to(torch.uint8)
+        out[:, 1] = ((dv >> 8) & 0xFF).to(torch.uint8)
+        out[:, 2:18] = (codes[:, :16] & 0x0F) | ((codes[:, 16:] & 0x0F) << 4)
+        return out.reshape(-1)
+    if bits not in (3, 4):
+        raise ValueError(bits)
     qmax = (1 << (bits - 1)) - 1
     bias = 1 << (bits - 1)
     blk = w.reshape(-1, 32)
@@ -256,6 +276,7 @@ def routed_weights_torch(cfg: Config, layer: int, device, base_seed: int = 0, ch
     eb = cfg.expert_bytes
     mb = H * (F // 32) * block_bytes(bits)  # bytes of the gate (and the up) matrix
     out = torch.empty(E * eb, dtype=torch.uint8, device=device)
+    cb = cfg.codebook or None
     gen = torch.Generator(device=device)
     for e0 in range(0, E, chunk):
         n = min(chunk, E - e0)
@@ -266,8 +287,8 @@ def routed_weights_torch(cfg: Config, layer: int, device, base_seed: int = 0, ch
             gu[i].normal_(0.0, std, generator=gen)
             dn[i].normal_(0.0, std, generator=gen)
         view = out[e0 * eb:(e0 + n) * eb].view(n, eb)
-        view[:, :2 * mb] = quantize_torch(gu, bits).view(n, 2 * mb)
-        view[:, 2 * mb:] = quantize_torch(dn, cfg.dbits).view(n, eb - 2 * mb)
+        view[:, :2 * mb] = quantize_torch(gu, bits, cb).view(n, 2 * mb)
+        view[:, 2 * mb:] = quantize_torch(dn, cfg.dbits, cb).view(n, eb - 2 * mb)
         del gu, dn
     return out
 

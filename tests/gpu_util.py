@@ -28,14 +28,16 @@ class DevLayer:
         self.x = x_to_dev(li.x, cfg.x_dtype)
         self.logits = torch.from_numpy(li.logits).to(DEV)
         # the pages' block order on the host, converted once on the device
+        cb = cfg.codebook or None
         self.routed_t, self.routed = moe.prepare_qweights(torch.from_numpy(li.routed).to(DEV), cfg.bits,
                                                           cfg.n_experts, cfg.hidden, cfg.ffn,
-                                                          down_bits=cfg.down_bits)
+                                                          down_bits=cfg.down_bits, codebook=cb)
         self.shared_t = None
         self.shared = None
         if li.shared is not None:
             self.shared_t, self.shared = moe.prepare_qweights(torch.from_numpy(li.shared).to(DEV), cfg.bits, 1,
-                                                              cfg.hidden, cfg.shared_ffn, down_bits=cfg.down_bits)
+                                                              cfg.hidden, cfg.shared_ffn, down_bits=cfg.down_bits,
+                                                              codebook=cb)
 
     def forward(self, path=moe.PATH_AUTO, ws=None, want_routing=True):
         cfg = self.cfg
@@ -60,7 +62,7 @@ def layer_inputs(name: str, T: int, layer: int = 0, seed: int = 0):
 def oracle_forward(orc, li: synth.LayerInputs, rows=None):
     cfg = li.cfg
     return orc.layer_forward(li.x, li.x_code, li.logits, cfg.top_k, cfg.fmt, cfg.ffn, li.routed, li.shared,
-                             s_ffn=cfg.shared_ffn or None, rows=rows)
+                             s_ffn=cfg.shared_ffn or None, rows=rows, codebook=cfg.codebook or None)
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:

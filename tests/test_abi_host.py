@@ -55,6 +55,10 @@ def test_expert_bytes(L):
     assert moe.expert_bytes(4, 2048, 768, down_bits=3) == 2048 * 24 * (2 * 18 + 14)
     assert moe.expert_bytes(3, 2048, 512, down_bits=3) == moe.expert_bytes(3, 2048, 512)
     assert moe.expert_bytes(3, 2048, 512, down_bits=5) == -1
+    # the non-linear 4-bit block (code 20) has the 4-bit block's 18 bytes
+    assert moe.expert_bytes(moe.BITS_NL4, 2048, 768) == 2654208
+    assert moe.expert_bytes(3, 2048, 512, down_bits=moe.BITS_NL4) == 2048 * 16 * (2 * 14 + 18)
+    assert moe.expert_bytes(21, 2048, 512) == -1
 
 
 def test_workspace_bytes(L):
@@ -123,6 +127,16 @@ def test_rejects_before_launch(L):
         assert lf(r=moe.QWeights(fake, 4, 8, 256, 512, P, 5), path=path) == moe.MOE_ERR_UNSUPPORTED
         assert lf(r=moe.QWeights(fake, 3, 8, 256, 512, P), path=path) == moe.MOE_ERR_UNSUPPORTED
         assert lf(T=40, s=moe.QWeights(fake, 3, 1, 256, 512, P), path=path) == moe.MOE_ERR_UNSUPPORTED
+    # non-linear 4-bit: the shared expert must carry the routed experts' table
+    NL = moe.BITS_NL4
+    r_nl = moe.qweights_at(fake, NL, 8, 256, 512, P, 0, tuple(range(-8, 8)))
+    s_other = moe.qweights_at(fake, NL, 1, 256, 512, P, 0, tuple(range(8, -8, -1)))
+    for path in (moe.PATH_AUTO, moe.PATH_DECODE, moe.PATH_PREFILL):
+        assert lf(r=r_nl, s=s_other, path=path) == moe.MOE_ERR_UNSUPPORTED
+    # a pair the decode launch does not build is refused on an explicit decode request
+    r_mix = moe.qweights_at(fake, NL, 8, 256, 512, P, 3, tuple(range(-8, 8)))
+    assert lf(r=r_mix, s=None, path=moe.PATH_DECODE) == moe.MOE_ERR_UNSUPPORTED
+    assert lf(r=moe.QWeights(fake, 21, 8, 256, 512, P), s=None) == moe.MOE_ERR_UNSUPPORTED
     # T == 0 is a valid empty call: nothing is launched
     assert lf(T=0) == moe.MOE_OK
 

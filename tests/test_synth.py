@@ -8,7 +8,7 @@ import torch
 from quantized_routed_expert_amd import synth
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [3, 4, synth.BITS_NL4])
 def test_quantize_torch_matches_numpy(bits):
     rg = np.random.default_rng(5 + bits)
     w = (rg.standard_normal((96, 512)) * 0.02).astype(np.float32)
@@ -17,9 +17,26 @@ def test_quantize_torch_matches_numpy(bits):
     w[7, 5] = np.float32(0.9)       # one large weight dominating its block
     w[9, 64:96] = np.float32(-0.0)
     w[11, 96:128] = np.linspace(-1, 1, 32, dtype=np.float32)  # codes at .5 boundaries
-    a = synth.quantize(w, bits)
-    b = synth.quantize_torch(torch.from_numpy(w), bits).numpy()
+    cb = synth.nl4_test_codebook() if bits == synth.BITS_NL4 else None
+    a = synth.quantize(w, bits, cb)
+    b = synth.quantize_torch(torch.from_numpy(w), bits, cb).numpy()
     assert np.array_equal(a, b)
+
+
+def test_nl4_quantizer_picks_nearest():
+    """The non-linear encoder picks a table entry nearest w / d for every
+    weight (brute force over the 16 entries), for an ordered and an
+    unordered table."""
+    rg = np.random.default_rng(8)
+    w = (rg.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    for cb in (synth.nl4_test_codebook(), tuple(((c * 37 + 11) % 256) - 128 for c in range(16))):
+        raw = synth.quantize(w, synth.BITS_NL4, cb).reshape(-1, 18)
+        d = raw[:, :2].copy().view(np.float16).astype(np.float32).ravel()
+        codes = np.concatenate([raw[:, 2:] & 15, raw[:, 2:] >> 4], axis=1)
+        v = w.reshape(-1, 32) / d[:, None]
+        table = np.array(cb, dtype=np.float32)
+        best = np.abs(v[:, :, None] - table[None, None, :]).min(axis=2)
+        assert np.allclose(np.abs(v - table[codes]), best, rtol=0, atol=1e-4)
 
 
 def test_routed_weights_torch_layout():
