@@ -5,10 +5,14 @@ activations and router logits, all resident in HBM), captured in a HIP graph
 and replayed; every step runs the whole hot path (routing, grouping, expert
 FFNs, shared expert, combine).
 
-    python bench.py [--workload all|decode|tiny|mtp16|e512|e512x4|prefill] [--steps K] [--warmup W]
+    python bench.py [--workload all|decode|decode_router|tiny|mtp16|e512|e512x4|prefill|e512_nl4|prefill_nl4]
+                    [--steps K] [--warmup W]
 
 The default runs every workload (the five configurations; the
-large-expert-count decode at 1 and 4 rows) and prints ONE JSON line.  Its
+large-expert-count decode at 1 and 4 rows; the decode layer with its router
+projection; the large-expert-count layer with a 3-bit gate/up and a
+non-linear 4-bit down projection, at one row and as a prefill chunk) and
+prints ONE JSON line.  Its
 top-level fields are the decode workload's (one row per window, 128 experts,
 top-8 + shared expert, 4-bit, hidden 2048, FFN 768); `workloads` lists every
 workload with its us/layer, tokens/s, expert-weight GB/s, roofline fraction,
@@ -39,7 +43,11 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "MoE layer us + expert-weight GB/s at 1-16 decode rows; prefill tok/s"
 
-# name: (config, rows); the order of the default run (the headline first)
+# the pairing of the thread's decode table: 3-bit gate/up, non-linear 4-bit
+# down (the table is the test table 127 sign(t)|t|^1.6, t = (i - 7.5)/7.5)
+_NL4_DOWN = {"down_bits": 20, "codebook": None}  # codebook filled in by workload_config
+
+# name: (config, rows[, format changes]); the order of the default run (the headline first)
 WORKLOADS = {
     "decode": ("decode", 1),
     # the decode layer with its router projection (bf16 [E][H]) in the same
@@ -50,8 +58,36 @@ WORKLOADS = {
     "e512": ("e512", 1),
     "e512x4": ("e512", 4),
     "prefill": ("prefill", 2048),
+    "e512_nl4": ("e512", 1, _NL4_DOWN),
+    "prefill_nl4": ("prefill", 2048, _NL4_DOWN),
 }
 ROUTER_WORKLOADS = {"decode_router"}
+
+
+def workload_config(name):
+    """(config, rows) of a workload, its format changes applied."""
+    import dataclasses
+    from quantized_routed_expert_amd import synth
+    spec = WORKLOADS[name]
+    cfg = synth.CONFIGS[spec[0]]
+    if len(spec) > 2:
+        ch = dict(spec[2])
+        if ch.get("codebook", ()) is None:
+            ch["codebook"] = synth.nl4_test_codebook()
+        cfg = dataclasses.replace(cfg, name=name, **ch)
+    return cfg, spec[1]
+
+
+def format_desc(cfg) -> str:
+    def one(b):
+        return "non-linear 4-bit" if b == 20 else f"{b}-bit"
+    if cfg.dbits == cfg.bits:
+        return f"{one(cfg.bits)} block-32"
+    return f"gate/up {one(cfg.bits)}, down {one(cfg.dbits)} block-32"
+
+
+def weight_key(cfg):
+    return (cfg.wcid, cfg.bits, cfg.dbits, tuple(cfg.codebook), cfg.hidden, cfg.ffn, cfg.n_experts, cfg.shared_ffn)
 
 
 def log(msg: str):
@@ -141,19 +177,20 @@ class WeightCache:
     def get(self, cfg):
         import torch
         from quantized_routed_expert_amd import moe, synth
-        key = (cfg.wcid, cfg.bits, cfg.hidden, cfg.ffn, cfg.n_experts, cfg.shared_ffn)
+        key = weight_key(cfg)
         if key in self.sets:
             return self.sets[key]
         t0 = time.time()
         out = []
         for l in range(self.layers):
             raw = synth.routed_weights_torch(cfg, l, self.dev)
+            cb = cfg.codebook or None
             routed_t, routed = moe.prepare_qweights(raw, cfg.bits, cfg.n_experts, cfg.hidden, cfg.ffn,
-                                                    down_bits=cfg.down_bits)
+                                                    down_bits=cfg.down_bits, codebook=cb)
             sh = synth.shared_weights(cfg, l)
             shared_raw = torch.from_numpy(sh).to(self.dev) if sh is not None else None
             shared_t, shared = (moe.prepare_qweights(shared_raw, cfg.bits, 1, cfg.hidden, cfg.shared_ffn,
-                                                     down_bits=cfg.down_bits)
+                                                     down_bits=cfg.down_bits, codebook=cb)
                                 if sh is not None else (None, None))
             # the pages' block order of a few layers stays on the host for the oracle
             host = (raw.cpu().numpy(), sh) if l < 4 else None
@@ -168,7 +205,7 @@ class WeightCache:
 
     def drop_unless(self, cfgs_left):
         import torch
-        keep = {(c.wcid, c.bits, c.hidden, c.ffn, c.n_experts, c.shared_ffn) for c in cfgs_left}
+        keep = {weight_key(c) for c in cfgs_left}
         for key in list(self.sets):
             if key not in keep:
                 del self.sets[key]
@@ -194,7 +231,8 @@ def cpu_baseline(orc, cfg, T, wsets, xs, logits, bytes_layer, seconds, path_deco
                 if routers is not None:
                     lg = orc.router_logits(xs[l], 0 if cfg.x_dtype == "f32" else 1, routers[l]).astype(np.float32)
                 orc.layer_forward(xs[l], 0 if cfg.x_dtype == "f32" else 1, lg, cfg.top_k, cfg.fmt,
-                                  cfg.ffn, routed, shared, s_ffn=cfg.shared_ffn or None)
+                                  cfg.ffn, routed, shared, s_ffn=cfg.shared_ffn or None,
+                                  codebook=cfg.codebook or None)
                 cpu_bytes += bytes_layer[l]
                 n_layers += 1
             dt = time.time() - t_start
@@ -210,7 +248,7 @@ def cpu_baseline(orc, cfg, T, wsets, xs, logits, bytes_layer, seconds, path_deco
                 rows = np.arange(rows_done, min(rows_done + step, T), dtype=np.int32)
                 orc.layer_forward(xs[0], 0 if cfg.x_dtype == "f32" else 1, logits[0], cfg.top_k, cfg.fmt,
                                   cfg.ffn, routed, shared,
-                                  s_ffn=cfg.shared_ffn or None, rows=rows)
+                                  s_ffn=cfg.shared_ffn or None, rows=rows, codebook=cfg.codebook or None)
                 rows_done += rows.size
             dt = time.time() - t_start
             res[leg] = {"value": round(rows_done / dt / L, 4), "unit": "tok/s", "threads": nt,
@@ -227,8 +265,7 @@ def run_workload(name, args, wcache, orc):
     import torch
     from quantized_routed_expert_amd import moe, synth
 
-    cname, T = WORKLOADS[name]
-    cfg = synth.CONFIGS[cname]
+    cfg, T = workload_config(name)
     L = args.layers
     dev = wcache.dev
     path = moe.PATH_DECODE if T <= moe.DECODE_MAX_ROWS else moe.PATH_PREFILL
@@ -304,7 +341,7 @@ def run_workload(name, args, wcache, orc):
     toks = T * 1000.0 / ms_step  # tokens per second through an L-layer MoE stack
     fl_gu, fl_dn = layer_flops(cfg, T)
     desc = (f"{name}: H={cfg.hidden} E={cfg.n_experts} F={cfg.ffn} top-{cfg.top_k} + shared F={cfg.shared_ffn}, "
-            f"{cfg.bits}-bit block-32, T={T} rows, {L} layers"
+            f"{format_desc(cfg)}, T={T} rows, {L} layers"
             + (f", bf16 router projection [{cfg.n_experts}][{cfg.hidden}] per layer in the graph" if router else ""))
 
     if path == moe.PATH_DECODE:
@@ -316,7 +353,7 @@ def run_workload(name, args, wcache, orc):
         ach = (total_bytes / L) / (kern_us * 1e-6) / 1e9
         # windows of one to four rows (T * k <= 64) take the column-split
         # launch (integer nibble dot products), larger windows the matrix-core launch
-        split = T <= 4 and T * cfg.top_k <= 64
+        split = T <= 4 and T * cfg.top_k <= 64 and cfg.bits in (3, 4) and cfg.dbits in (3, 4)
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name),
                 "kernel": "k_split_layer" if split else "k_decode_layer", "bytes_per_launch": round(total_bytes / L),
@@ -419,7 +456,7 @@ def main():
     results = []
     for i, name in enumerate(names):
         results.append(run_workload(name, args, wcache, orc))
-        wcache.drop_unless([synth.CONFIGS[WORKLOADS[n][0]] for n in names[i + 1:]])
+        wcache.drop_unless([workload_config(n)[0] for n in names[i + 1:]])
 
     head = results[0]
     out = {

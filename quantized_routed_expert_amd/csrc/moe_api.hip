@@ -341,9 +341,9 @@ bool decode_fits(int T, int E, int k, int H, int F, int Fs, int bits, int dbits,
 // ---- column-split decode launch (windows of one to four rows, T*k <= 64) ----
 int split_xps(int /*bits*/) { return 36; }  // digit dwords per pair slot in LDS (both formats)
 // 16-byte loads per lane of a wave's 8 gate/up rows at H = 2048 (the most)
-int split_gu_loads(int bits) { return bits == 4 ? 9 : 7; }
+int split_gu_loads(int bits) { return block_bytes_of(bits) == 18 ? 9 : 7; }
 // 16-byte loads per lane of a wave's H/8 down rows of one column block at H = 2048
-int split_dn_loads(int bits) { return bits == 4 ? 5 : 4; }
+int split_dn_loads(int bits) { return block_bytes_of(bits) == 18 ? 5 : 4; }
 
 int split_lds_layout(SplitParams &P) {
     const int bb = block_bytes_of(P.bits), bbd = block_bytes_of(P.dbits), xps = split_xps(P.bits);
@@ -375,8 +375,8 @@ int split_units(int T, int k, int H, int combine, int G) {
 
 bool split_fits(int T, int E, int k, int H, int F, int Fs, int bits, int dbits, int combine, int G) {
     (void)E;
-    // integer dot products of linear codes: the 3- and 4-bit formats only
-    if ((bits != 3 && bits != 4) || (dbits != 3 && dbits != 4)) return false;
+    // the pairs the launch is built for (as decode_format_ok)
+    if (!decode_format_ok(bits, dbits)) return false;
     if (T < 1 || T > SPL_MAX_T || k > 32 || T * k > 64) return false;
     if (H != 256 && H != 512 && H != 1024 && H != 2048) return false;
     if (F > 4096 || Fs > 4096) return false;
@@ -553,6 +553,7 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
         S_.Fs = Fs_;
         S_.bits = routed->bits;
         S_.dbits = dbits;
+        memcpy(S_.nl8, routed->codebook, 16);
         S_.eb = expert_bytes_of(routed->bits, dbits, routed->hidden, routed->ffn);
         S_.mode = mode | (shared ? DEC_MODE_SHARED : 0);
         S_.x_f32 = x_f32;
@@ -568,10 +569,10 @@ int run_decode(const void *x, int x_f32, const float *logits, const int32_t *g_o
         const int lds = split_lds_layout(S_);
         if (lds > dv.lds_max) return MOE_ERR_UNSUPPORTED;
         static std::mutex smu;
-        static int s_lds_set[2][2][SPL_MAX_T][2] = {};
+        static int s_lds_set[3][3][SPL_MAX_T][2] = {};
         {
             std::lock_guard<std::mutex> lk(smu);
-            int &cur = s_lds_set[S_.bits == 4][dbits == 4][T - 1][x_f32 ? 1 : 0];
+            int &cur = s_lds_set[fmt_index(S_.bits)][fmt_index(dbits)][T - 1][x_f32 ? 1 : 0];
             if (lds > cur) {
                 if (split_set_lds(S_.bits, dbits, T, x_f32, lds) != hipSuccess) return MOE_ERR_LAUNCH;
                 cur = lds;

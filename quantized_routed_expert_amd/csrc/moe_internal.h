@@ -181,6 +181,7 @@ struct SplitParams {
     uint32_t *err, *epoch;     // error word (as DecodeParams::err); [EPOCH_SLOTS] calls completed (the tag source)
     int T, E, k, H, F, Fs, bits, mode, x_f32;
     int dbits;                 // bit width of the down projection (bits: gate and up)
+    uint32_t nl8[4];           // the non-linear format's table, 16 signed bytes (when a width is MOE_FMT_NL4)
     size_t eb;                 // bytes of one routed expert blob
     int nc, ncs, ncmax;        // 32-column slices of F and Fs; the partial buffer's stride
     uint32_t m_nc;             // ceil(2^32 / nc) (0 when nc = 1)

@@ -15,7 +15,11 @@
 //    block's sum of a is staged with the digits);
 //  - a block's integer dot product is exact (it fits fp32's 24-bit
 //    significand) and is scaled by the block's fp16 scale in fp32, the same
-//    rounding point as the dequantized fp32 dot product of the pages.
+//    rounding point as the dequantized fp32 dot product of the pages;
+//  - non-linear 4-bit codes become their table's signed bytes (byte-table
+//    lookups), multiplied by two signed radix-256 digits of the activations
+//    (v_dot4_i32_i8: four 8-bit products per instruction); the block's int32
+//    sum is exact and rounds once (below 2^-24 relative) on its way to fp32.
 //
 // Work items: (expert, 32-column slice c of its FFN).  An item needs the 32
 // gate rows and 32 up rows of the slice and column block c of down (the
@@ -82,6 +86,13 @@ extern "C" int moe_trace_split_set(void *buf) {
 // ---------------------------------------------------------------------------
 template <int BITS>
 struct SFmt;
+// non-linear 4-bit: the 4-bit pair's bytes; digit dwords [digit 2][parity 2][nibble-dword 9]
+template <>
+struct SFmt<MOE_FMT_NL4> {
+    static constexpr int bb = 18, pb = 36, pw = 9, nnd = 9;
+    static constexpr int xpd = 36;
+    static constexpr int xps = 36;
+};
 template <>
 struct SFmt<4> {
     static constexpr int bb = 18;   // bytes per block
@@ -105,7 +116,7 @@ struct SFmt<3> {
 template <int BITS>
 __device__ __forceinline__ int nibble_k(int nd, int i) {
     const int h = i & 1;
-    if constexpr (BITS == 4) {
+    if constexpr (nib_layout(BITS)) {
         // byte 2+j of a block: code j (low nibble), code j+16 (high nibble)
         const int beta = 4 * nd + (i >> 1);
         if (beta >= 2 && beta <= 17) return beta - 2 + 16 * h;
@@ -130,6 +141,22 @@ __device__ __forceinline__ int nibble_k(int nd, int i) {
 template <int BITS>
 __device__ __forceinline__ void build_digits(const int16_t *src, int kmask, int nd, uint32_t *dst) {
     uint32_t D[4] = {0u, 0u, 0u, 0u};
+    if constexpr (BITS == MOE_FMT_NL4) {
+        // two signed radix-256 digits v = a0 + 256 a1 (a0 in [-128, 127],
+        // |a1| <= 64); nibble i of the code dword is byte i/2 of the even
+        // (i even) or the odd (i odd) code bytes: D[2 * digit + parity]
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int kk = nibble_k<BITS>(nd, i);
+            const int v = kk >= 0 ? (int)src[kk & kmask] : 0;
+            const int a0 = (int)(int8_t)(v & 0xFF), a1 = (v - a0) >> 8;
+            D[i & 1] |= (uint32_t)(a0 & 0xFF) << (8 * (i >> 1));
+            D[2 + (i & 1)] |= (uint32_t)(a1 & 0xFF) << (8 * (i >> 1));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[j * SFmt<BITS>::nnd + nd] = D[j];
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int kk = nibble_k<BITS>(nd, i);
@@ -145,6 +172,18 @@ __device__ __forceinline__ void build_digits(const int16_t *src, int kmask, int 
 __device__ __forceinline__ int sdot8(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot8((int)a, (int)b, c, false);
 }
+__device__ __forceinline__ int sdot4(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+// four codes (0..15, one per byte) -> their table's signed bytes (tb: the
+// 16-byte table; entries 0..7 and 8..15 looked up apart, bit 3 choosing)
+__device__ __forceinline__ uint32_t nl8_lookup(uint32_t c, const uint32_t *tb) {
+    const uint32_t s = c & 0x07070707u;
+    const uint32_t t = c & 0x08080808u;
+    const uint32_t m = (t << 5) - (t >> 3);  // 0xFF in the bytes whose code is 8..15
+    const uint32_t lo = __builtin_amdgcn_perm(tb[1], tb[0], s), hi = __builtin_amdgcn_perm(tb[3], tb[2], s);
+    return (hi & m) | (lo & ~m);
+}
 // a0 + 16 a1 + 256 a2 + ...
 template <int N>
 __device__ __forceinline__ int radix16(const int (&a)[N]) {
@@ -157,6 +196,42 @@ __device__ __forceinline__ int radix16(const int (&a)[N]) {
 // Weights of one pair, unpacked once for all rows.
 template <int BITS>
 struct SPair;
+
+template <>
+struct SPair<MOE_FMT_NL4> {
+    uint32_t be[9], bo[9];  // table bytes of the codes at even / odd nibbles of each code dword
+    float d0, d1;
+    __device__ __forceinline__ void set(const uint32_t (&w)[9], const uint32_t *tb) {
+#pragma unroll
+        for (int q = 0; q < 9; ++q) {  // (scale bytes give table bytes too: they meet zero digits)
+            be[q] = nl8_lookup(w[q] & 0x0F0F0F0Fu, tb);
+            bo[q] = nl8_lookup((w[q] >> 4) & 0x0F0F0F0Fu, tb);
+        }
+        d0 = half_bits_to_float(w[0] & 0xFFFFu);
+        d1 = half_bits_to_float(w[4] >> 16);
+    }
+    __device__ __forceinline__ void blocks(const uint32_t *xd, int, int, int &A0, int &A1) const {
+        int a0[2], a1[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            int s0 = 0, s1 = 0;
+#pragma unroll
+            for (int q = 0; q < 5; ++q) {
+                s0 = sdot4(be[q], xd[(2 * j) * 9 + q], s0);
+                s0 = sdot4(bo[q], xd[(2 * j + 1) * 9 + q], s0);
+            }
+#pragma unroll
+            for (int q = 5; q < 9; ++q) {
+                s1 = sdot4(be[q], xd[(2 * j) * 9 + q], s1);
+                s1 = sdot4(bo[q], xd[(2 * j + 1) * 9 + q], s1);
+            }
+            a0[j] = s0;
+            a1[j] = s1;
+        }
+        A0 = a0[0] + (a0[1] << 8);
+        A1 = a1[0] + (a1[1] << 8);
+    }
+};
 
 template <>
 struct SPair<4> {
@@ -309,8 +384,8 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     // wave's wait for it (stores in between only lengthen such a wait).  A
     // run is reloaded, for the wave's next item, as soon as the wave is done
     // reading it: gate/up after the gate/up part, down after the down part.
-    constexpr int NGU = BG == 4 ? 9 : 7;    // ceil(8 rows * rowH / 16 / 64) at H = 2048
-    constexpr int ND = BD == 4 ? 5 : 4;     // ceil(H/8 rows * bb / 16 / 64) at H = 2048
+    constexpr int NGU = nib_layout(BG) ? 9 : 7;  // ceil(8 rows * rowH / 16 / 64) at H = 2048
+    constexpr int ND = nib_layout(BD) ? 5 : 4;   // ceil(H/8 rows * bb / 16 / 64) at H = 2048
     constexpr int GUB = 8 * NGU * 1024;     // bytes of the gate/up runs (the down runs follow)
     const int npw = (8 * P.rowH) >> 4;      // pieces of a wave's 8 gate/up rows
     const int npd = (H * FD::bb) >> 7;      // pieces of a wave's H/8 down rows
@@ -650,7 +725,8 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
 #pragma unroll
                     for (int i = 0; i < FG::pw; ++i) w[i] = wq[pp * FG::pw + i];
                     SPair<BG> sp;
-                    sp.set(w);
+                    if constexpr (BG == MOE_FMT_NL4) sp.set(w, P.nl8);
+                    else sp.set(w);
 #pragma unroll
                     for (int t = 0; t < TM; ++t) {
                         if (!row_in[t]) continue;  // (uniform over the workgroup)
@@ -744,7 +820,8 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
 #pragma unroll
                 for (int i = 0; i < FD::pw; ++i) w[i] = *(const __attribute__((address_space(3))) uint32_t *)(pp8 + 4 * i);
                 SPair<BD> sp;
-                sp.set(w);
+                if constexpr (BD == MOE_FMT_NL4) sp.set(w, P.nl8);
+                else sp.set(w);
 #pragma unroll
                 for (int t = 0; t < TM; ++t) {
                     if (pid[t] < 0) continue;
@@ -917,6 +994,10 @@ static hipError_t split_attr_t(int lds) {
         if (bg == 3 && bd == 4) SPLIT_DISPATCH_T(FN, 3, 4, __VA_ARGS__);  \
         if (bg == 4 && bd == 3) SPLIT_DISPATCH_T(FN, 4, 3, __VA_ARGS__);  \
         if (bg == 3 && bd == 3) SPLIT_DISPATCH_T(FN, 3, 3, __VA_ARGS__);  \
+        if (bg == MOE_FMT_NL4 && bd == MOE_FMT_NL4)                       \
+            SPLIT_DISPATCH_T(FN, MOE_FMT_NL4, MOE_FMT_NL4, __VA_ARGS__);  \
+        if (bg == 3 && bd == MOE_FMT_NL4)                                 \
+            SPLIT_DISPATCH_T(FN, 3, MOE_FMT_NL4, __VA_ARGS__);            \
         return hipErrorInvalidValue;                                      \
     } while (0)
 

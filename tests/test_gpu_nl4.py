@@ -7,9 +7,9 @@ here: a non-linear test table of our own (127 sign(t)|t|^1.6) and an
 unordered one; the identity table c - 8 turns the format into the 4-bit
 block, which pins the layout against the linear path bit for bit.
 
-Paths: the matrix-core decode launch (windows of 1-16 rows; the column-split
-launch takes linear codes only), the grouped GEMMs, moe_expert_ffn, and the
-pairs the decode launch does not build (served by the grouped GEMMs under
+Paths: the column-split decode launch (1-4 rows), the matrix-core decode
+launch (5-16 rows), the grouped GEMMs, moe_expert_ffn, and the pairs the
+decode launches do not build (served by the grouped GEMMs under
 MOE_PATH_AUTO).  Bar: routing bit-exact; max |err| <= 2e-3 * rms(oracle)."""
 import dataclasses
 
@@ -46,7 +46,7 @@ def _check(orc, li, path):
 
 @pytest.mark.parametrize("bg,bd", PAIRS)
 @pytest.mark.parametrize("name,T,path", [
-    ("decode", 1, D), ("e512", 1, D), ("e512", 4, D),  # one to four rows: the matrix-core launch
+    ("decode", 1, D), ("e512", 1, D), ("e512", 4, D),  # one to four rows: the column-split launch
     ("mtp16", 16, D), ("e512", 8, D),
     ("e512", 64, P),                                  # grouped GEMMs
 ])
@@ -91,7 +91,7 @@ def test_nl4_pairs_served_by_gemm(orc, bg, bd, T):
             DevLayer(li).forward(D)
 
 
-@pytest.mark.parametrize("T,path", [(8, D), (64, P)])
+@pytest.mark.parametrize("T,path", [(1, D), (3, D), (8, D), (64, P)])
 def test_identity_table_is_the_4bit_format(T, path):
     """The same bytes read as 4-bit and as non-linear 4-bit with the table
     c - 8 give the same bits on the launches that serve both formats."""

@@ -9,12 +9,16 @@ byte mask), then interleave low and high bytes into 16-bit values.  This
 models those integer steps bit for bit and checks them against the format's
 definition (the weight = table[code], as an exact 16-bit float) for random
 tables and blocks: the decode lane order (pos_in_block of the 4-bit layout)
-and the grouped GEMM's natural order."""
+and the grouped GEMM's natural order.  The column-split launch instead looks
+the codes up in the table's own signed bytes and multiplies them by two
+signed radix-256 digits of the integer activations (v_dot4_i32_i8); its
+block sums must be the exact integer dot products."""
 import struct
 
 import numpy as np
 
 from test_prefill_dequant import alignbit, bf16, perm
+from test_split_digits import nibble_k  # the 4-bit layout's nibble -> k map
 
 
 def fp16(x):
@@ -129,3 +133,74 @@ def test_tables_are_exact():
     for v in range(-128, 128):
         assert np.float16(v) == v
         assert struct.unpack("<f", struct.pack("<I", bf16(v) << 16))[0] == v
+
+
+# ---------------------------------------------------------------------------
+# The column-split launch: table bytes times signed radix-256 digits
+# ---------------------------------------------------------------------------
+
+
+def sdot4(a, b, c):
+    for i in range(4):
+        x, y = (a >> 8 * i) & 255, (b >> 8 * i) & 255
+        c += (x - 256 if x >= 128 else x) * (y - 256 if y >= 128 else y)
+    return c
+
+
+def nl8_lookup(c, tb):
+    s = c & 0x07070707
+    t = c & 0x08080808
+    m = ((t << 5) - (t >> 3)) & 0xFFFFFFFF
+    lo, hi = perm(tb[1], tb[0], s), perm(tb[3], tb[2], s)
+    return (hi & m) | (lo & ~m & 0xFFFFFFFF)
+
+
+def digit_words8(a, kmask):
+    """[digit 2][parity 2][nibble-dword 9] words of signed bytes."""
+    out = [0] * 36
+    for nd in range(9):
+        D = [0] * 4
+        for i in range(8):
+            kk = nibble_k(4, nd, i)
+            v = int(a[kk & kmask]) if kk >= 0 else 0
+            a0 = ((v + 128) & 255) - 128
+            a1 = (v - a0) >> 8
+            assert -128 <= a1 <= 127 and a0 + 256 * a1 == v
+            D[i & 1] |= (a0 & 255) << (8 * (i >> 1))
+            D[2 + (i & 1)] |= (a1 & 255) << (8 * (i >> 1))
+        for j in range(4):
+            out[j * 9 + nd] = D[j]
+    return out
+
+
+def split_blocks(w, tb, xd):
+    be = [nl8_lookup(w[q] & 0x0F0F0F0F, tb) for q in range(9)]
+    bo = [nl8_lookup((w[q] >> 4) & 0x0F0F0F0F, tb) for q in range(9)]
+    a0, a1 = [0, 0], [0, 0]
+    for j in range(2):
+        for q in range(9):
+            dst = a0 if q < 5 else a1
+            dst[j] = sdot4(be[q], xd[(2 * j) * 9 + q], dst[j])
+            dst[j] = sdot4(bo[q], xd[(2 * j + 1) * 9 + q], dst[j])
+    return a0[0] + 256 * a0[1], a1[0] + 256 * a1[1]
+
+
+def test_split_pair_exact_dot_products():
+    """Gate/up (two blocks of a row, kmask 63) and down (one block read by
+    two rows, kmask 31): the launch's sums equal sum table[code] * a."""
+    rng = np.random.default_rng(34)
+    for cb in random_tables(rng, 6):
+        tb = [int.from_bytes(bytes(np.array(cb, dtype=np.int8).view(np.uint8)[4 * i:4 * i + 4]), "little")
+              for i in range(4)]
+        for trial in range(30):
+            pair = rng.integers(0, 256, 36, dtype=np.uint8).tobytes()
+            w = list(struct.unpack("<9I", pair))
+            c0, c1 = block_codes(pair[:18]), block_codes(pair[18:])
+            for kmask in (63, 31):
+                n = kmask + 1
+                a = rng.integers(-(1 << 14), (1 << 14) + 1, n)
+                if trial == 0:
+                    a[:] = (1 << 14) * (1 if kmask == 63 else -1)  # the extremes
+                A0, A1 = split_blocks(w, tb, digit_words8(a, kmask))
+                assert A0 == sum(cb[c0[i]] * int(a[i & kmask]) for i in range(32))
+                assert A1 == sum(cb[c1[i]] * int(a[(32 + i) & kmask]) for i in range(32))
