@@ -301,9 +301,11 @@ __device__ __forceinline__ u32x4 deq_group(const BFields<BITS> &f, uint32_t g, c
 // x KS blocks) and its activation pieces into one slot of an NS-slot ring in
 // LDS with direct-to-LDS loads (global_load_lds: no register holds data in
 // flight, so NS - 1 steps of loads stay outstanding whatever their size).
-// Every thread issues the same number of loads per step (LW weight dwords
-// and one 16-byte activation piece; slots past the real data take a copy of
-// a valid dword or piece that nothing reads), so `s_waitcnt vmcnt(L * steps
+// Every thread issues the same number of loads per step (LW weight loads --
+// dwords for gate/up, whose 256 row runs of a step are 28 or 36 bytes at
+// 4-byte alignment, 16-byte pieces for down, whose step is one contiguous
+// 16-byte aligned run -- and one 16-byte activation piece; slots past the
+// real data take a copy of a valid load that nothing reads), so `s_waitcnt vmcnt(L * steps
 // issued after s)` tells a wave that its share of step s has landed, and a
 // plain s_barrier then tells every wave that all shares have (__syncthreads'
 // fence would also wait for the later steps' loads).  One barrier per step.
@@ -326,11 +328,13 @@ struct PfCfg {
     // split on the way into LDS, which waits for every load: two slots)
     static constexpr int NS = XF32 ? 2 : 4;
     static constexpr int bb = blk_bytes(BITS);
-    // weight dwords per step: gate/up 256 rows x KS blocks (row runs of
-    // KS*bb bytes); down KS column blocks x 256 rows (one run each)
-    static constexpr int STEP_DW = 256 * KS * bb / 4;
-    static constexpr int LW = (STEP_DW + PF_THREADS - 1) / PF_THREADS;  // weight loads per thread per step
-    static constexpr int W_BYTES = LW * PF_THREADS * 4;
+    // weight loads per step: gate/up 256 rows x KS blocks (row runs of KS*bb
+    // bytes, 4-byte aligned: dwords); down KS column blocks x 256 rows (one
+    // contiguous run each, 16-byte aligned: 16-byte pieces)
+    static constexpr int WV = MODE == 0 ? 4 : 16;  // bytes per weight load
+    static constexpr int STEP_W = 256 * KS * bb / WV;
+    static constexpr int LW = (STEP_W + PF_THREADS - 1) / PF_THREADS;  // weight loads per thread per step
+    static constexpr int W_BYTES = LW * PF_THREADS * WV;
     static constexpr int XP = MODE == 0 ? (XF32 ? 2 : 1) : 2;  // A parts: bf16 x; fp32 x or h as hi + lo
     static constexpr int A_PIECES = 64 * 4 * KS * XP;          // 16-byte pieces (8 K of one row)
     static constexpr int A_BYTES = A_PIECES * 16;
@@ -340,7 +344,7 @@ struct PfCfg {
     // down, one block of the rows 2i and 2i + 1
     static constexpr int NW = 2 * bb / 4;
     static constexpr int L = LW + (XF32 ? 0 : 1);   // direct-to-LDS loads per thread per step
-    static_assert(STEP_DW * 4 == 256 * KS * bb, "whole dwords");
+    static_assert(STEP_W * WV == 256 * KS * bb, "whole loads");
     static_assert(NW == (nib_layout(BITS) ? 9 : 7) && (MODE == 1 || KS == 2), "a pair is two blocks");
     static_assert(RING + ((5 * (MOE_MAX_EXPERTS_DEV + 1) + 1) * 4 + 15) / 16 * 16 <= 159 * 1024,
                   "the ring and the largest slot plan fit one workgroup's LDS");
@@ -406,19 +410,19 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, lds_u8 *ring, con
     const int K = MODE == 0 ? P.H : ti.Fx;
     const int nks = K / (32 * KS);
 
-    // ---- this thread's weight dword slots: byte offsets from the blob at step 0 ----
+    // ---- this thread's weight load slots: byte offsets from the blob at step 0 ----
     uint32_t woff[LW];
 #pragma unroll
     for (int i = 0; i < LW; ++i) {
         const int q = i * PF_THREADS + tid;
-        size_t o = 0;  // (a slot past the step's data: the blob's first dword, never read)
-        if (q < C::STEP_DW) {
+        size_t o = 0;  // (a slot past the step's data: the blob's first bytes, never read)
+        if (q < C::STEP_W) {
             if (MODE == 0) {
                 const int row = q / NW, j = q - row * NW;  // [256 rows: 128 gate, 128 up][NW dwords]
                 const int f = ti.nt * PF_NF_GU + (row & 127);
                 o = ((row < 128 ? 0 : ti.Fx) + f) * rowG + 4 * j;
             } else {
-                o = 2 * ti.Fx * rowG + (size_t)ti.nt * PF_NF_DN * bb + 4 * (size_t)q;  // [256 rows][bb bytes]
+                o = 2 * ti.Fx * rowG + (size_t)ti.nt * PF_NF_DN * bb + 16 * (size_t)q;  // [256 rows][bb bytes]
             }
         }
         woff[i] = (uint32_t)o;
@@ -450,7 +454,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, lds_u8 *ring, con
         const uint8_t *wb = ti.blob + (size_t)s * wstep;
 #pragma unroll
         for (int i = 0; i < LW; ++i)
-            __builtin_amdgcn_global_load_lds(wb + woff[i], st + 4 * (i * PF_THREADS + 64 * wave), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(wb + woff[i], st + C::WV * (i * PF_THREADS + 64 * wave), C::WV, 0, 0);
         if constexpr (!XF32)
             __builtin_amdgcn_global_load_lds(a_src + (size_t)s * a_step, st + C::W_BYTES + 16 * 64 * wave, 16, 0, 0);
     };
@@ -579,7 +583,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, lds_u8 *ring, con
 __host__ __device__ constexpr int pf_plan_bytes(int E) { return (((5 * (E + 1) + 1) * 4) + 15) / 16 * 16; }
 
 template <int MODE, int BITS, int XF32>
-__global__ __launch_bounds__(PF_THREADS) void k_prefill_gemm(GemmParams P) {
+// (four waves per SIMD: two workgroups share a CU, so one's loads and
+// barriers overlap the other's compute; the register limit this sets spills
+// a few per-tile values, none in the K loop)
+__global__ __launch_bounds__(PF_THREADS, 4) void k_prefill_gemm(GemmParams P) {
     __shared__ int s_pair[64];  // pair id of each tile row (down tiles)
     // the slot plan, read once: prefix[ns + 1], then per slot exp, cnt, row0, hrow0
     extern __shared__ __align__(16) int s_plan[];
