@@ -301,14 +301,18 @@ __device__ __forceinline__ u32x4 deq_group(const BFields<BITS> &f, uint32_t g, c
 // x KS blocks) and its activation pieces into one slot of an NS-slot ring in
 // LDS with direct-to-LDS loads (global_load_lds: no register holds data in
 // flight, so NS - 1 steps of loads stay outstanding whatever their size).
-// Every thread issues the same number of loads per step (LW weight loads --
-// dwords for gate/up, whose 256 row runs of a step are 28 or 36 bytes at
-// 4-byte alignment, 16-byte pieces for down, whose step is one contiguous
-// 16-byte aligned run -- and one 16-byte activation piece; slots past the
-// real data take a copy of a valid load that nothing reads), so `s_waitcnt vmcnt(L * steps
-// issued after s)` tells a wave that its share of step s has landed, and a
-// plain s_barrier then tells every wave that all shares have (__syncthreads'
-// fence would also wait for the later steps' loads).  One barrier per step.
+// All loads are 16-byte pieces.  Down: a step is one contiguous, 16-byte
+// aligned run (256 rows of one column block).  Gate/up: a step's 256 row
+// runs (KS * bb = 28 or 36 bytes each) start at one common 4-byte phase
+// within a 16-byte piece (rows are 16-byte multiples apart), so each row
+// takes the 3 aligned pieces covering its run (48 bytes; the compute reads
+// from the phase on).  Every thread of a wave issues the same loads per step
+// (LW weight pieces, fewer for the waves past the step's pieces, slots past
+// the real data taking a copy of a valid piece that nothing reads; and one
+// activation piece), so `s_waitcnt vmcnt(loads per step * steps issued after
+// s)` tells a wave that its share of step s has landed, and a plain
+// s_barrier then tells every wave that all shares have (__syncthreads' fence
+// would also wait for the later steps' loads).  One barrier per step.
 //
 // Reads: wave w, lane (n, g) takes k-group g of weight row n of its 16 (gate
 // and up) or 2 x 16 (down, rows of both parities) rows: the dwords of the
@@ -325,16 +329,17 @@ template <int MODE, int BITS, int XF32>
 struct PfCfg {
     static constexpr int KS = MODE == 0 ? 2 : 1;   // quant blocks per K step
     // ring slots: steps in flight + the one computed (fp32 activations are
-    // split on the way into LDS, which waits for every load: two slots)
-    static constexpr int NS = XF32 ? 2 : 4;
+    // split on the way into LDS, which waits for every load: two slots); the
+    // ring of a bf16 gate/up or a down launch leaves room for two workgroups
+    static constexpr int NS = XF32 ? 2 : (MODE == 0 ? 3 : 4);
     static constexpr int bb = blk_bytes(BITS);
-    // weight loads per step: gate/up 256 rows x KS blocks (row runs of KS*bb
-    // bytes, 4-byte aligned: dwords); down KS column blocks x 256 rows (one
-    // contiguous run each, 16-byte aligned: 16-byte pieces)
-    static constexpr int WV = MODE == 0 ? 4 : 16;  // bytes per weight load
-    static constexpr int STEP_W = 256 * KS * bb / WV;
-    static constexpr int LW = (STEP_W + PF_THREADS - 1) / PF_THREADS;  // weight loads per thread per step
-    static constexpr int W_BYTES = LW * PF_THREADS * WV;
+    // 16-byte weight pieces per step: gate/up 256 rows x PPR pieces covering
+    // each row's KS*bb bytes at any 4-byte phase; down KS column blocks x 256
+    // rows (one contiguous run each)
+    static constexpr int PPR = 3;
+    static constexpr int STEP_W = MODE == 0 ? 256 * PPR : 256 * KS * bb / 16;
+    static constexpr int LW = (STEP_W + PF_THREADS - 1) / PF_THREADS;  // weight loads per thread per step (at most)
+    static constexpr int W_BYTES = MODE == 0 ? STEP_W * 16 : LW * PF_THREADS * 16;
     static constexpr int XP = MODE == 0 ? (XF32 ? 2 : 1) : 2;  // A parts: bf16 x; fp32 x or h as hi + lo
     static constexpr int A_PIECES = 64 * 4 * KS * XP;          // 16-byte pieces (8 K of one row)
     static constexpr int A_BYTES = A_PIECES * 16;
@@ -343,22 +348,14 @@ struct PfCfg {
     // dwords of one lane's block pair (7 or 9): gate/up, two blocks of a row;
     // down, one block of the rows 2i and 2i + 1
     static constexpr int NW = 2 * bb / 4;
-    static constexpr int L = LW + (XF32 ? 0 : 1);   // direct-to-LDS loads per thread per step
-    static_assert(STEP_W * WV == 256 * KS * bb, "whole loads");
+    static_assert(MODE == 0 ? (STEP_W % 64 == 0 && PPR * 16 >= 12 + KS * bb) : STEP_W * 16 == 256 * KS * bb,
+                  "gate/up: whole waves of pieces covering a run at any phase; down: whole pieces");
     static_assert(NW == (nib_layout(BITS) ? 9 : 7) && (MODE == 1 || KS == 2), "a pair is two blocks");
     static_assert(RING + ((5 * (MOE_MAX_EXPERTS_DEV + 1) + 1) * 4 + 15) / 16 * 16 <= 159 * 1024,
                   "the ring and the largest slot plan fit one workgroup's LDS");
     static_assert(A_PIECES == PF_THREADS * (MODE == 0 && XF32 ? 2 : 1), "one piece per thread (two for fp32 x)");
 };
 
-// until at most L * ahead loads of this wave are outstanding (ahead <= 3)
-template <int L>
-__device__ __forceinline__ void wait_vm_steps(int ahead) {
-    if (ahead >= 3) wait_vm<3 * L>();
-    else if (ahead == 2) wait_vm<2 * L>();
-    else if (ahead == 1) wait_vm<L>();
-    else wait_vm<0>();
-}
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0) only
 
 struct TileInfo {
@@ -397,7 +394,7 @@ template <int MODE, int BITS, int XF32, int MT>
 __device__ __forceinline__ void gemm_tile(const GemmParams &P, lds_u8 *ring, const int *s_pair,
                                           const TileInfo &ti) {
     using C = PfCfg<MODE, BITS, XF32>;
-    constexpr int KS = C::KS, NS = C::NS, LW = C::LW, NW = C::NW, XP = C::XP, L = C::L;
+    constexpr int KS = C::KS, NS = C::NS, LW = C::LW, NW = C::NW, XP = C::XP;
     constexpr int NPASS = MODE == 0 ? 2 : 1;  // gate + up / down
     constexpr int NTW = MODE == 0 ? 1 : 2;    // 16-column n-tiles per wave
     constexpr int NB = NPASS * NTW;           // B fragments per lane per block
@@ -412,15 +409,17 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, lds_u8 *ring, con
 
     // ---- this thread's weight load slots: byte offsets from the blob at step 0 ----
     uint32_t woff[LW];
+    int nw = 0;  // weight loads of this wave per step (wave-uniform)
 #pragma unroll
     for (int i = 0; i < LW; ++i) {
         const int q = i * PF_THREADS + tid;
+        nw += (MODE == 1 || i * PF_THREADS + 64 * wave < C::STEP_W) ? 1 : 0;
         size_t o = 0;  // (a slot past the step's data: the blob's first bytes, never read)
         if (q < C::STEP_W) {
             if (MODE == 0) {
-                const int row = q / NW, j = q - row * NW;  // [256 rows: 128 gate, 128 up][NW dwords]
+                const int row = q / C::PPR, j = q - row * C::PPR;  // [256 rows: 128 gate, 128 up][PPR pieces]
                 const int f = ti.nt * PF_NF_GU + (row & 127);
-                o = ((row < 128 ? 0 : ti.Fx) + f) * rowG + 4 * j;
+                o = ((row < 128 ? 0 : ti.Fx) + f) * rowG + 16 * j;
             } else {
                 o = 2 * ti.Fx * rowG + (size_t)ti.nt * PF_NF_DN * bb + 16 * (size_t)q;  // [256 rows][bb bytes]
             }
@@ -449,12 +448,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, lds_u8 *ring, con
         a_step = (size_t)32 * KS * 2;
     }
 
+    const int lw_step = nw + (XF32 ? 0 : 1);  // direct-to-LDS loads of this wave per step
+    // gate/up: step s's runs start (s * wstep) & 15 bytes into their first piece
     auto issue = [&](int s) {
         lds_u8 *st = ring + (s % NS) * C::STAGE;
-        const uint8_t *wb = ti.blob + (size_t)s * wstep;
+        const uint8_t *wb = ti.blob + (MODE == 0 ? (((size_t)s * wstep) & ~(size_t)15) : (size_t)s * wstep);
 #pragma unroll
         for (int i = 0; i < LW; ++i)
-            __builtin_amdgcn_global_load_lds(wb + woff[i], st + C::WV * (i * PF_THREADS + 64 * wave), C::WV, 0, 0);
+            if (MODE == 1 || i * PF_THREADS + 64 * wave < C::STEP_W)
+                __builtin_amdgcn_global_load_lds(wb + woff[i], st + 16 * (i * PF_THREADS + 64 * wave), 16, 0, 0);
         if constexpr (!XF32)
             __builtin_amdgcn_global_load_lds(a_src + (size_t)s * a_step, st + C::W_BYTES + 16 * 64 * wave, 16, 0, 0);
     };
@@ -465,13 +467,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, lds_u8 *ring, con
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[a][m] = float4v{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const lds_u8 *st) {
+    auto compute = [&](const lds_u8 *st, int s) {
         const lds_u8 *wsl = st, *asl = st + C::W_BYTES;
         constexpr int NRAW = MODE == 0 ? NPASS : KS;  // block pairs this lane reads per step
         uint32_t rw[NRAW][NW];
         if (MODE == 0) {
+            const int ph = (int)(((size_t)s * wstep) & 15);  // the step's phase in each row's pieces
 #pragma unroll
-            for (int p = 0; p < NPASS; ++p) lds_dwords<NW>(wsl + (p * 128 + wave * 16 + n_lane) * (NW * 4), rw[p]);
+            for (int p = 0; p < NPASS; ++p)
+                lds_dwords<NW>(wsl + (p * 128 + wave * 16 + n_lane) * (16 * C::PPR) + ph, rw[p]);
         } else {
             // rows o, o + 1 (o = 32 w + 2 n) of block b: 2 * bb bytes from o * bb (a multiple of 4)
 #pragma unroll
@@ -538,12 +542,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, lds_u8 *ring, con
             *(lds_u32x4 *)(asl + a_off<KS>(1, ap_m, ap_blk, ap_g, ap_n)) = u32x4{lv[0], lv[1], lv[2], lv[3]};
             wait_lgkm0();
         } else {
-            wait_vm_steps<L>(min(NS - 2, nks - 1 - s));
+            wait_vm_n(lw_step * min(NS - 2, nks - 1 - s));
         }
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         if (s + NS - 1 < nks) issue(s + NS - 1);
-        compute(st);
+        compute(st, s);
     }
 
     // ---- epilogue ----
