@@ -71,7 +71,13 @@ __global__ __launch_bounds__(1024) void k_group_scan(GroupParams P) {
         const int e = tid * per + i;
         int run = 0;
         if (e < E)
-            for (int c = 0; c < nc; ++c) run += (int)P.chunk_counts[(size_t)c * E + e];
+            for (int c0 = 0; c0 < nc; c0 += 8) {  // eight independent loads per round trip
+                uint32_t v[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = c0 + j < nc ? P.chunk_counts[(size_t)(c0 + j) * E + e] : 0u;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) run += (int)v[j];
+            }
         tot[i] = run;
         my += run;
         myact += (run > 0);
