@@ -381,9 +381,10 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     // soon as their loads have landed: no other wave's data is waited for
     // until the gate/up values are complete.  The loads of a wave complete in
     // issue order, so the number of loads issued after a given one bounds the
-    // wave's wait for it (stores in between only lengthen such a wait).  A
-    // run is reloaded, for the wave's next item, as soon as the wave is done
-    // reading it: gate/up after the gate/up part, down after the down part.
+    // wave's wait for it (stores in between only lengthen such a wait).  The
+    // gate/up run is reloaded for the wave's next item as soon as the wave
+    // has read it; the down run is loaded once the item's gate/up rows have
+    // landed (so that all workgroups' gate/up bytes stream first).
     constexpr int NGU = nib_layout(BG) ? 9 : 7;  // ceil(8 rows * rowH / 16 / 64) at H = 2048
     constexpr int ND = nib_layout(BD) ? 5 : 4;   // ceil(H/8 rows * bb / 16 / 64) at H = 2048
     constexpr int GUB = 8 * NGU * 1024;     // bytes of the gate/up runs (the down runs follow)
@@ -507,7 +508,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
         }
     }
     // the shared expert's items need no routing: their weights stream in now
-    if ((int)blockIdx.x < ncs) issue_item_e(blockIdx.x, -1, 3);
+    if ((int)blockIdx.x < ncs) issue_item_e(blockIdx.x, -1, 1);
     lds_barrier();  // routing and the row maxima complete
     STRACE(1);
     const uint32_t tag = decode_tag(__builtin_amdgcn_readfirstlane(tag_v));
@@ -519,7 +520,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
         const int n_items1 = ncs + k * nc;
         if (it < n_items1 && it >= ncs) {
             const int j = it - ncs, sl = nc == 1 ? j : (int)__umulhi((uint32_t)j, P.m_nc);
-            issue_item_e(j - sl * nc, sm.idx[sl], 3);
+            issue_item_e(j - sl * nc, sm.idx[sl], 1);
         }
     }
 
@@ -658,7 +659,7 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
     STRACE(2);
     const int n_slots = sm.n_slots;
     const int n_items = ncs + (n_slots - hs) * nc;
-    if (!early && it < n_items && it >= ncs) issue_item(it, 3);
+    if (!early && it < n_items && it >= ncs) issue_item(it, 1);
 
     // activation digits: (row, pair, nibble-dword) tasks
     {
@@ -683,17 +684,21 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
 #pragma unroll
         for (int t = 0; t < TM; ++t) row_in[t] = sm.slot_pair[s][t] >= 0;
 
-        // gate/up: this wave's 8 rows once its gate/up loads have landed (the
-        // down loads, issued after them, may still be in flight); lane (row r,
-        // run m of ppl consecutive pairs): lpr lanes per row (8, or 4 at
-        // H = 256), so every lane of the 8 rows is busy at every H.
+        // gate/up: this wave's 8 rows once its gate/up loads have landed; only
+        // then are the item's down rows issued, so the gate/up bytes of every
+        // workgroup stream first and the down rows stream while the gate/up
+        // values, SwiGLU and the h digits are computed.  Lane (row r, run m of
+        // ppl consecutive pairs): lpr lanes per row (8, or 4 at H = 256), so
+        // every lane of the 8 rows is busy at every H.
         {
             const lds_u8 *wr = s_gu_run;
             const int lpr = H >= 512 ? 8 : 4;  // lanes per row
             const int ppl = (H >> 6) / lpr;     // pairs per lane: 1, 2 or 4
             const int r = lane / lpr, m = lane - r * lpr;
-            wait_vm_n(ND);
+            wait_vm_n(0);
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the previous item's down rows are read
+            issue_item(it, 2);
             if (my_items == 0) WTRACE(12);
             if (r < 8) {
                 float acc[TM];
@@ -839,11 +844,6 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
                     st_tagged(dst + 1, ldexpf(sp.d1 * (float)A1, -hsc[t]), tag);
                 }
             }
-        }
-        // the down run is free again: the next item's down rows
-        if (nxt < n_items) {
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-            issue_item(nxt, 2);
         }
         if (my_items == 0) STRACE(6);
         ++my_items;
