@@ -797,9 +797,17 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
 
     // Down tiles (slot, 128 output rows) continue the round robin of the
     // gate/up tasks over the workgroups: tile i is work item n_tasks + i.
+    // The round robin decides how many tiles a workgroup takes; which ones is
+    // a contiguous run of the (slot-major) tile list, so that its tiles share
+    // a slot and its staged h: workgroup r of the round robin, taking c_r =
+    // n_tiles / G tiles (one more for r < n_tiles % G), takes the run that
+    // starts after those of the workgroups before it.
     const int tiles_per_slot = P.tps;
     const int n_tiles = n_slots * tiles_per_slot;
     const int first_tile = (int)(((long long)blockIdx.x - n_tasks % G + G) % G);
+    const int tl_m1 = n_tiles / G, tl_e = n_tiles - tl_m1 * G;
+    const int tl_start = first_tile * tl_m1 + min(first_tile, tl_e);
+    auto run_tile = [&](int ti) { return tl_start + (ti - first_tile) / G; };  // (ti < n_tiles, ti = first_tile mod G)
     struct Tile {
         const uint8_t *rows;  // this wave's 16 down rows
         int s, rg, Fx, cbF, nchF, segF, rowF, rsF, perF;
@@ -833,7 +841,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
     bool c_holds_tile = false;
     auto prefetch_first_tile = [&]() {
         if (first_tile < n_tiles) {
-            const Tile t = tile_of(first_tile);
+            const Tile t = tile_of(run_tile(first_tile));
             chunk_map(mapF, t.cbF, t.perF, t.invF, t.rsF, t.rowF, lane);
             map_fx = t.Fx;
             chunk_load(c, t.rows, mapF);
@@ -1023,7 +1031,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             combine_part(ti - n_tiles);
             continue;
         }
-        const Tile tl = tile_of(ti);
+        const Tile tl = tile_of(run_tile(ti));
         const int s = tl.s, rg = tl.rg, Fx = tl.Fx;
         const bool shared_slot = tl.shared;
         const int cbF = tl.cbF, nchF = tl.nchF, segF = tl.segF, rsF = tl.rsF;
@@ -1140,7 +1148,7 @@ __global__ __launch_bounds__(DEC_THREADS, 1) void k_decode_layer(DecodeParams P)
             } else if (ti + G < n_tiles) {
                 // the next tile's first chunk streams in while this one computes
                 // (same chunk geometry only: the map is per FFN width)
-                const Tile tn = tile_of(ti + G);
+                const Tile tn = tile_of(run_tile(ti + G));
                 if (tn.Fx == map_fx) {
                     chunk_load(c, tn.rows, mapF);
                     c_next = true;
