@@ -295,7 +295,8 @@ __device__ __forceinline__ u32x4 deq_group(const BFields<BITS> &f, uint32_t g, c
 // ---------------------------------------------------------------------------
 // Grouped GEMM tiles with an LDS ring.
 //
-// A tile is 16*MT rows (MT = 1, 2, 4 by the group's size) x 128 features
+// A tile is 16, 32 or 64 rows (by the group's size; MT = its non-empty 16-row
+// m-tiles, 1 to 4) x 128 features
 // (gate/up: the gate and the up row of each, 256 weight rows) or 256 outputs
 // (down).  Per K step the workgroup streams the step's weight bytes (256 rows
 // x KS blocks) and its activation pieces into one slot of an NS-slot ring in
@@ -650,8 +651,12 @@ __global__ __launch_bounds__(PF_THREADS, 4) void k_prefill_gemm(GemmParams P) {
         if (tid < 64) s_pair[tid] = cur.pr64;
         __syncthreads();
         PTRACE(((size_t)MODE << 20) + 4 * (size_t)tile, __builtin_amdgcn_s_memrealtime());
-        if (cur.mtl == 4) gemm_tile<MODE, BITS, XF32, 4>(P, ring, s_pair, cur);
-        else if (cur.mtl == 2) gemm_tile<MODE, BITS, XF32, 2>(P, ring, s_pair, cur);
+        // the MFMAs cover the tile's non-empty 16-row m-tiles only (the last
+        // 64-row tile of a group may hold 1 to 64 rows)
+        const int mact = (cur.nrows + 15) >> 4;
+        if (mact == 4) gemm_tile<MODE, BITS, XF32, 4>(P, ring, s_pair, cur);
+        else if (mact == 3) gemm_tile<MODE, BITS, XF32, 3>(P, ring, s_pair, cur);
+        else if (mact == 2) gemm_tile<MODE, BITS, XF32, 2>(P, ring, s_pair, cur);
         else gemm_tile<MODE, BITS, XF32, 1>(P, ring, s_pair, cur);
         PTRACE(((size_t)MODE << 20) + 4 * (size_t)tile + 1, __builtin_amdgcn_s_memrealtime());
         PTRACE(((size_t)MODE << 20) + 4 * (size_t)tile + 2, (uint64_t)cur.mtl);
