@@ -186,30 +186,6 @@ __device__ __forceinline__ uint32_t float_key(float v) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Wave-wide max of a 64-bit key.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
-        uint32_t olo = __shfl_xor(lo, off, 64), ohi = __shfl_xor(hi, off, 64);
-        uint64_t o = ((uint64_t)ohi << 32) | olo;
-        k = o > k ? o : k;
-    }
-    return k;
-}
-
-__device__ __forceinline__ float wave_max_f(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
-}
-
-__device__ __forceinline__ float wave_sum_f(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
-
 // Cross-workgroup handoff without cache-wide maintenance.  On gfx950 each
 // XCD has its own L2, so an agent-scope release/acquire fence turns into an
 // L2 write-back / invalidate of the whole XCD cache.  Instead the data that
@@ -217,12 +193,6 @@ __device__ __forceinline__ float wave_sum_f(float v) {
 // relaxed atomic accesses, a wave waits for its own stores to complete
 // (s_waitcnt) before it raises a counter, and counters are polled with relaxed
 // agent-scope loads.
-__device__ __forceinline__ void st_dev(float *p, float v) {
-    __hip_atomic_store((uint32_t *)p, __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(const float *p) {
-    return __builtin_bit_cast(float, __hip_atomic_load((const uint32_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
 // tagged words: fp32 value in the low half, a tag in the high half, read and
 // written as one 64-bit access
 __device__ __forceinline__ uint64_t ld_dev_u64(const uint64_t *p) {
@@ -259,9 +229,6 @@ __device__ __forceinline__ void wave_lds_handoff() {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
-
-// all of this wave's memory operations have completed
-__device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Workgroup barrier for LDS data only: the wave's LDS operations complete,
 // then s_barrier.  Unlike __syncthreads() it does not wait for the wave's

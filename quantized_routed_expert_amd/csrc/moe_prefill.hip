@@ -177,9 +177,6 @@ __global__ __launch_bounds__(1024) void k_prefill_plan(PlanParams P) {
     }
 }
 
-
-typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));  // 4-byte aligned 16-byte load
-
 // ---------------------------------------------------------------------------
 // In-register dequantization of one k-group (8 consecutive weights 8g..8g+7 of
 // a 32-weight block) into 8 bf16 values that hold the integer codes minus the

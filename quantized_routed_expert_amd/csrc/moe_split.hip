@@ -303,11 +303,6 @@ struct SPair<3> {
     }
 };
 
-template <int N>
-__device__ __forceinline__ void lds_read_dwords(const uint8_t *p, uint32_t (&w)[N]) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) w[i] = *(const uint32_t *)(p + 4 * i);
-}
 // 16-byte aligned
 template <int N>
 __device__ __forceinline__ void lds_read_b128(const uint8_t *p, uint32_t (&w)[N]) {
