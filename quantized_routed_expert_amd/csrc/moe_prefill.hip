@@ -362,6 +362,7 @@ struct TileInfo {
     const uint8_t *blob;
     int a_pair;  // gate/up: the pair id of this thread's activation row, -1 when none
     int pr64;    // thread tid < 64: pair id of tile row tid, -1 when none
+    float w64;   // thread tid < 64, down tiles: the router weight of tile row tid (1 for the shared expert)
 };
 
 // Piece tid of a step's activations, layout [part][m][blk][g][n] x 16 bytes:
@@ -389,7 +390,7 @@ __device__ __forceinline__ void lds_dwords(const lds_u8 *p, uint32_t (&w)[N]) {
 }
 
 template <int MODE, int BITS, int XF32, int MT>
-__device__ __forceinline__ void gemm_tile(const GemmParams &P, lds_u8 *ring, const int *s_pair,
+__device__ __forceinline__ void gemm_tile(const GemmParams &P, lds_u8 *ring, const int *s_pair, const float *s_w,
                                           const TileInfo &ti) {
     using C = PfCfg<MODE, BITS, XF32>;
     constexpr int KS = C::KS, NS = C::NS, LW = C::LW, NW = C::NW, XP = C::XP;
@@ -566,7 +567,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, lds_u8 *ring, con
                 dst[hs] = hl;
             } else {
                 const int pr = s_pair[rr];
-                const float wgt = (ti.shared_slot || !P.pair_w) ? 1.0f : P.pair_w[pr];
+                const float wgt = s_w[rr];
                 float *orow = ti.shared_slot ? P.out_shared + (size_t)(ti.r0 + rr) * P.H
                                              : P.out_pairs + (size_t)pr * P.H;
 #pragma unroll
@@ -589,7 +590,8 @@ template <int MODE, int BITS, int XF32>
 // barriers overlap the other's compute; the register limit this sets spills
 // a few per-tile values, none in the K loop)
 __global__ __launch_bounds__(PF_THREADS, 4) void k_prefill_gemm(GemmParams P) {
-    __shared__ int s_pair[64];  // pair id of each tile row (down tiles)
+    __shared__ int s_pair[64];   // pair id of each tile row
+    __shared__ float s_w[64];    // router weight of each tile row (down tiles)
     // the slot plan, read once: prefix[ns + 1], then per slot exp, cnt, row0, hrow0
     extern __shared__ __align__(16) int s_plan[];
     const int tid = threadIdx.x;
@@ -635,6 +637,7 @@ __global__ __launch_bounds__(PF_THREADS, 4) void k_prefill_gemm(GemmParams P) {
         const int a_r = 16 * (tid >> 7) + (tid & 15);  // this thread's activation row (gate/up pieces)
         ti.a_pair = (MODE == 0 && !ti.shared_slot && (tid >> 7) < ti.mtl && a_r < ti.nrows) ? P.pairs[row0 + a_r] : -1;
         ti.pr64 = (tid < 64 && tid < ti.nrows && !ti.shared_slot) ? P.pairs[row0 + tid] : -1;
+        ti.w64 = (MODE == 1 && ti.pr64 >= 0 && P.pair_w) ? P.pair_w[ti.pr64] : 1.0f;
     };
 
     int tile = blockIdx.x;
@@ -644,17 +647,23 @@ __global__ __launch_bounds__(PF_THREADS, 4) void k_prefill_gemm(GemmParams P) {
         TileInfo nxt;
         const bool more = tile + (int)gridDim.x < total;
         if (more) tile_info(tile + gridDim.x, nxt);
-        __syncthreads();  // the previous tile is done with the ring and s_pair
-        if (tid < 64) s_pair[tid] = cur.pr64;
-        __syncthreads();
+        // the previous tile is done with the ring, s_pair and s_w (LDS only:
+        // its output stores need not have completed, and the next tile's
+        // loads go out meanwhile)
+        lds_barrier();
+        if (tid < 64) {
+            s_pair[tid] = cur.pr64;
+            s_w[tid] = cur.w64;
+        }
+        lds_barrier();
         PTRACE(((size_t)MODE << 20) + 4 * (size_t)tile, __builtin_amdgcn_s_memrealtime());
         // the MFMAs cover the tile's non-empty 16-row m-tiles only (the last
         // 64-row tile of a group may hold 1 to 64 rows)
         const int mact = (cur.nrows + 15) >> 4;
-        if (mact == 4) gemm_tile<MODE, BITS, XF32, 4>(P, ring, s_pair, cur);
-        else if (mact == 3) gemm_tile<MODE, BITS, XF32, 3>(P, ring, s_pair, cur);
-        else if (mact == 2) gemm_tile<MODE, BITS, XF32, 2>(P, ring, s_pair, cur);
-        else gemm_tile<MODE, BITS, XF32, 1>(P, ring, s_pair, cur);
+        if (mact == 4) gemm_tile<MODE, BITS, XF32, 4>(P, ring, s_pair, s_w, cur);
+        else if (mact == 3) gemm_tile<MODE, BITS, XF32, 3>(P, ring, s_pair, s_w, cur);
+        else if (mact == 2) gemm_tile<MODE, BITS, XF32, 2>(P, ring, s_pair, s_w, cur);
+        else gemm_tile<MODE, BITS, XF32, 1>(P, ring, s_pair, s_w, cur);
         PTRACE(((size_t)MODE << 20) + 4 * (size_t)tile + 1, __builtin_amdgcn_s_memrealtime());
         PTRACE(((size_t)MODE << 20) + 4 * (size_t)tile + 2, (uint64_t)cur.mtl);
         PTRACE(((size_t)MODE << 20) + 4 * (size_t)tile + 3, (uint64_t)blockIdx.x);
