@@ -195,7 +195,7 @@ struct SplitParams {
 // ---------------------------------------------------------------------------
 // Prefill / general path.
 // ---------------------------------------------------------------------------
-constexpr int GRP_CHUNK_TOKENS = 64;  // tokens per grouping chunk
+constexpr int GRP_CHUNK_TOKENS = 16;  // tokens per grouping chunk
 #define MOE_TOPK_MAX_LDS 32               // k <= 32
 #define MOE_SCAN_PER_MAX 4                // experts per thread in the 1024-thread scan (E <= 4096)
 

@@ -9,7 +9,7 @@
 //
 // Grouping: pairs p = t*k + j bucketed per expert so each expert computes only
 // its own rows (thread §二, the expert-scoped layout), ordered by
-// (expert, token, slot).  Three passes over chunks of 64 tokens: per-chunk
+// (expert, token, slot).  Three passes over chunks of 16 tokens: per-chunk
 // histograms (LDS atomics: counts do not depend on order), one workgroup
 // scanning (expert, chunk) counts into start positions, then each chunk
 // placing its pairs in token order.  No global atomics, so the placement is
@@ -57,7 +57,9 @@ __global__ __launch_bounds__(256) void k_group_count(GroupParams P) {
 }
 
 // One workgroup: chunk_counts[c][e] -> first position of chunk c's pairs of
-// expert e; offsets; active list.
+// expert e; offsets; active list.  Each thread reads its experts' counts in
+// batches of GRP_SCAN_BATCH independent loads (one round trip per batch).
+constexpr int GRP_SCAN_BATCH = 32;
 __global__ __launch_bounds__(1024) void k_group_scan(GroupParams P) {
     __shared__ int s_part[1024];
     __shared__ int s_act[1024];
@@ -71,12 +73,13 @@ __global__ __launch_bounds__(1024) void k_group_scan(GroupParams P) {
         const int e = tid * per + i;
         int run = 0;
         if (e < E)
-            for (int c0 = 0; c0 < nc; c0 += 8) {  // eight independent loads per round trip
-                uint32_t v[8];
+            for (int c0 = 0; c0 < nc; c0 += GRP_SCAN_BATCH) {  // independent loads per round trip
+                uint32_t v[GRP_SCAN_BATCH];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) v[j] = c0 + j < nc ? P.chunk_counts[(size_t)(c0 + j) * E + e] : 0u;
+                for (int j = 0; j < GRP_SCAN_BATCH; ++j)
+                    v[j] = c0 + j < nc ? P.chunk_counts[(size_t)(c0 + j) * E + e] : 0u;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) run += (int)v[j];
+                for (int j = 0; j < GRP_SCAN_BATCH; ++j) run += (int)v[j];
             }
         tot[i] = run;
         my += run;
@@ -100,15 +103,15 @@ __global__ __launch_bounds__(1024) void k_group_scan(GroupParams P) {
         if (e >= E) break;
         P.offsets[e] = base;
         // chunk c's first position: base + pairs of e in chunks before c
-        // (eight counts read before any is overwritten)
+        // (a batch of counts read before any is overwritten)
         int run = base;
-        for (int c0 = 0; c0 < nc; c0 += 8) {
-            uint32_t v[8];
+        for (int c0 = 0; c0 < nc; c0 += GRP_SCAN_BATCH) {
+            uint32_t v[GRP_SCAN_BATCH];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < GRP_SCAN_BATCH; ++j)
                 v[j] = c0 + j < nc ? P.chunk_counts[(size_t)(c0 + j) * E + e] : 0u;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < GRP_SCAN_BATCH; ++j) {
                 if (c0 + j < nc) P.chunk_counts[(size_t)(c0 + j) * E + e] = (uint32_t)run;
                 run += (int)v[j];
             }
