@@ -876,69 +876,121 @@ __global__ __launch_bounds__(SPL_THREADS, 1) void k_split_layer(SplitParams P) {
             wgt = p < TK ? sm.w[p] : 1.0f;
         }
     };
-    {
-        // every word in flight at once (consecutive threads on consecutive
-        // words), words not yet written by this call read again
-        const int per_term = ncm * 8, nw = nchk * nterm * per_term;
-        for (int q0 = tid; q0 < nw; q0 += 4 * SPL_THREADS) {
-            uint64_t wd[4];
-            const uint64_t *src[4];
-            bool need[4];
+    // per (output, term): the sum over the slices in slice order, times the
+    // router weight.  With many (output, term) pairs (windows of three or four
+    // rows) each pair's thread reads its slices' words straight into
+    // registers; with few, every thread of the workgroup polls a share of the
+    // words and the sums read them from LDS (more threads polling).  (The
+    // direct form is compiled only where it can be taken: its registers cost
+    // the one- and two-row kernels time even unused.)
+    bool direct = false;
+    if constexpr (TM >= 3) direct = nu * nterm >= 256;
+    if (direct) {
+        const int per_term = ncm * 8;
+        constexpr int RB = 24;  // words in flight per thread
+        for (int q = tid; q < nu * nterm; q += SPL_THREADS) {
+            const int ul = q / nterm, j = q - ul * nterm;
+            const int g = ul >> 3, rr = ul & 7;
+            int p, rowc;
+            float wgt;
+            term(g, j, p, wgt, rowc);
+            const int ncx = p >= TK ? ncs : nc;
+            const uint64_t *src = P.part + ((size_t)p * (H >> 3) + rowc) * per_term + rr;  // slice c: word 8 c
+            float sum = 0.0f;
+            for (int c0 = 0; c0 < ncx; c0 += RB) {
+                uint64_t wd[RB];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int q = q0 + i * SPL_THREADS;
-                const int r = q % per_term, gj = q / per_term;
-                const int g = gj / nterm, j = gj - g * nterm;
-                int p = 0, rowc = 0;
-                float wgt;
-                if (q < nw) term(g, j, p, wgt, rowc);
-                need[i] = q < nw && (r >> 3) < (p >= TK ? ncs : nc);
-                src[i] = P.part + ((size_t)p * (H >> 3) + rowc) * per_term + (need[i] ? r : 0);
-                wd[i] = need[i] ? ld_dev_u64(src[i]) : 0ull;
-            }
-            for (uint32_t spins = 0;; ++spins) {
-                bool ok = true;
+                for (int i = 0; i < RB; ++i) wd[i] = c0 + i < ncx ? ld_dev_u64(src + 8 * (c0 + i)) : 0ull;
+                for (uint32_t spins = 0;; ++spins) {
+                    bool ok = true;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ok = ok && (!need[i] || (uint32_t)(wd[i] >> 32) == tag);
-                if (ok) break;
-                if (spins > DEC_SPIN_LIMIT) {
-                    note_timeout(P.err, tag);
-                    break;
+                    for (int i = 0; i < RB; ++i) ok = ok && (c0 + i >= ncx || (uint32_t)(wd[i] >> 32) == tag);
+                    if (ok) break;
+                    if (spins > DEC_SPIN_LIMIT) {
+                        note_timeout(P.err, tag);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(4);
+#pragma unroll
+                    for (int i = 0; i < RB; ++i)
+                        if (c0 + i < ncx && (uint32_t)(wd[i] >> 32) != tag) wd[i] = ld_dev_u64(src + 8 * (c0 + i));
                 }
-                __builtin_amdgcn_s_sleep(4);
+#pragma unroll
+                for (int i = 0; i < RB; ++i)
+                    if (c0 + i < ncx) sum += __builtin_bit_cast(float, (uint32_t)wd[i]);
+            }
+            s_red[q] = wgt * sum;
+            if (!combine) {
+                const int u = u0 + ul, t = u / H, row = u - t * H;
+                if (p < TK) P.out_pairs[(size_t)p * H + row] = wgt * sum;
+                else P.out_shared[(size_t)(p - TK) * H + row] = sum;
+            }
+        }
+    } else {
+        {
+            // every word in flight at once (consecutive threads on consecutive
+            // words), words not yet written by this call read again
+            const int per_term = ncm * 8, nw = nchk * nterm * per_term;
+            for (int q0 = tid; q0 < nw; q0 += 4 * SPL_THREADS) {
+                uint64_t wd[4];
+                const uint64_t *src[4];
+                bool need[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int q = q0 + i * SPL_THREADS;
+                    const int r = q % per_term, gj = q / per_term;
+                    const int g = gj / nterm, j = gj - g * nterm;
+                    int p = 0, rowc = 0;
+                    float wgt;
+                    if (q < nw) term(g, j, p, wgt, rowc);
+                    need[i] = q < nw && (r >> 3) < (p >= TK ? ncs : nc);
+                    src[i] = P.part + ((size_t)p * (H >> 3) + rowc) * per_term + (need[i] ? r : 0);
+                    wd[i] = need[i] ? ld_dev_u64(src[i]) : 0ull;
+                }
+                for (uint32_t spins = 0;; ++spins) {
+                    bool ok = true;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ok = ok && (!need[i] || (uint32_t)(wd[i] >> 32) == tag);
+                    if (ok) break;
+                    if (spins > DEC_SPIN_LIMIT) {
+                        note_timeout(P.err, tag);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(4);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (need[i] && (uint32_t)(wd[i] >> 32) != tag) wd[i] = ld_dev_u64(src[i]);
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (need[i] && (uint32_t)(wd[i] >> 32) != tag) wd[i] = ld_dev_u64(src[i]);
+                    if (q0 + i * SPL_THREADS < nw) s_val[q0 + i * SPL_THREADS] = __builtin_bit_cast(float, (uint32_t)wd[i]);
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (q0 + i * SPL_THREADS < nw) s_val[q0 + i * SPL_THREADS] = __builtin_bit_cast(float, (uint32_t)wd[i]);
         }
-    }
-    __syncthreads();
-    // per (output, term): the sum over the slices in slice order, times the router weight
-    for (int q = tid; q < nu * nterm; q += SPL_THREADS) {
-        const int ul = q / nterm, j = q - ul * nterm;
-        const int g = ul >> 3, rr = ul & 7;
-        int p, rowc;
-        float wgt;
-        term(g, j, p, wgt, rowc);
-        const int ncx = p >= TK ? ncs : nc;
-        const float *v = s_val + ((size_t)g * nterm + j) * ncm * 8 + rr;
-        float sum = 0.0f;
-        for (int c0 = 0; c0 < ncx; c0 += 8) {  // eight reads in flight, added in order
-            float vv[8];
+        __syncthreads();
+        // per (output, term): the sum over the slices in slice order, times the router weight
+        for (int q = tid; q < nu * nterm; q += SPL_THREADS) {
+            const int ul = q / nterm, j = q - ul * nterm;
+            const int g = ul >> 3, rr = ul & 7;
+            int p, rowc;
+            float wgt;
+            term(g, j, p, wgt, rowc);
+            const int ncx = p >= TK ? ncs : nc;
+            const float *v = s_val + ((size_t)g * nterm + j) * ncm * 8 + rr;
+            float sum = 0.0f;
+            for (int c0 = 0; c0 < ncx; c0 += 8) {  // eight reads in flight, added in order
+                float vv[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) vv[i] = c0 + i < ncx ? v[(c0 + i) * 8] : 0.0f;
+                for (int i = 0; i < 8; ++i) vv[i] = c0 + i < ncx ? v[(c0 + i) * 8] : 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (c0 + i < ncx) sum += vv[i];
-        }
-        s_red[q] = wgt * sum;
-        if (!combine) {
-            const int u = u0 + ul, t = u / H, row = u - t * H;
-            if (p < TK) P.out_pairs[(size_t)p * H + row] = wgt * sum;
-            else P.out_shared[(size_t)(p - TK) * H + row] = sum;
+                for (int i = 0; i < 8; ++i)
+                    if (c0 + i < ncx) sum += vv[i];
+            }
+            s_red[q] = wgt * sum;
+            if (!combine) {
+                const int u = u0 + ul, t = u / H, row = u - t * H;
+                if (p < TK) P.out_pairs[(size_t)p * H + row] = wgt * sum;
+                else P.out_shared[(size_t)(p - TK) * H + row] = sum;
+            }
         }
     }
     STRACE(8);
