@@ -123,8 +123,8 @@ Layout make_layout(int T, int E, int k, int H, int F, int Fs, int path) {
         L.slot_row0 = take((size_t)(E + 1) * 4);
         L.slot_cnt = take((size_t)(E + 1) * 4);
         L.slot_hrow0 = take((size_t)(E + 1) * 4);
-        L.prefix_gu = take((size_t)(E + 3) * 4);
-        L.prefix_dn = take((size_t)(E + 3) * 4);
+        L.prefix_gu = take((size_t)(E + 4) * 4);  // [E+2] slots, [E+3] the GEMM's tile counter
+        L.prefix_dn = take((size_t)(E + 4) * 4);
         L.hbuf = take((TK + T) * (size_t)Fmax * 4);
     }
     L.total = off;

@@ -232,8 +232,8 @@ struct PlanParams {
     int32_t *slot_row0;      // [E+1]  first entry in pairs[] (routed) / 0 (shared)
     int32_t *slot_cnt;       // [E+1]
     int32_t *slot_hrow0;     // [E+1]  first row in the h buffer
-    int32_t *prefix_gu;      // [E+3]: tile prefix per slot; [E+2] = number of slots
-    int32_t *prefix_dn;      // [E+3]
+    int32_t *prefix_gu;      // [E+4]: tile prefix per slot; [E+2] = number of slots; [E+3] = tile counter
+    int32_t *prefix_dn;      // [E+4]
 };
 
 struct GemmParams {

@@ -174,6 +174,8 @@ __global__ __launch_bounds__(1024) void k_prefill_plan(PlanParams P) {
         P.prefix_dn[ns] = s_sd[1023];
         P.prefix_gu[P.E + 2] = ns;  // number of slots, for the GEMM kernels
         P.prefix_dn[P.E + 2] = ns;
+        P.prefix_gu[P.E + 3] = 0;   // the GEMMs' tile counters
+        P.prefix_dn[P.E + 3] = 0;
     }
 }
 
@@ -580,7 +582,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &P, lds_u8 *ring, con
 
 // ---------------------------------------------------------------------------
 // Grouped GEMM: persistent workgroups walk the tile list (slots by decreasing
-// row count; within a slot, m-tiles of one n-tile are consecutive).  Dynamic
+// row count; within a slot, m-tiles of one n-tile are consecutive): each takes
+// tiles blockIdx.x and blockIdx.x + G, then the next untaken ones from a
+// counter in list order (tiles differ in cost: a fixed stride left the last
+// workgroups ~20 % behind the mean), each id taken one tile ahead so that the
+// atomic's round trip hides behind a tile's work.  Dynamic
 // LDS: the slot plan (read once), then the ring.
 // ---------------------------------------------------------------------------
 __host__ __device__ constexpr int pf_plan_bytes(int E) { return (((5 * (E + 1) + 1) * 4) + 15) / 16 * 16; }
@@ -640,17 +646,24 @@ __global__ __launch_bounds__(PF_THREADS, 4) void k_prefill_gemm(GemmParams P) {
         ti.w64 = (MODE == 1 && ti.pr64 >= 0 && P.pair_w) ? P.pair_w[ti.pr64] : 1.0f;
     };
 
+    const int G = gridDim.x;
+    uint32_t *const ctr = (uint32_t *)(P.prefix + P.E + 3);  // zeroed by the plan
+    __shared__ int s_grab;  // the tile after the next one (thread 0's take, published at a tile's end)
     int tile = blockIdx.x;
+    int nid = tile + G;  // the next tile
     TileInfo cur;
     if (tile < total) tile_info(tile, cur);
-    for (; tile < total; tile += gridDim.x) {
-        TileInfo nxt;
-        const bool more = tile + (int)gridDim.x < total;
-        if (more) tile_info(tile + gridDim.x, nxt);
-        // the previous tile is done with the ring, s_pair and s_w (LDS only:
-        // its output stores need not have completed, and the next tile's
-        // loads go out meanwhile)
+    for (bool first = true; tile < total; first = false) {
+        // the previous tile is done with the ring, s_pair and s_w, and s_grab
+        // holds its take (LDS only: its output stores need not have
+        // completed, and this tile's loads go out meanwhile)
         lds_barrier();
+        if (!first) nid = s_grab;
+        uint32_t grab = 0;  // the tile after nid: its counter round trip overlaps this tile
+        if (tid == 0 && nid < total) grab = add_dev(ctr, 1u);
+        TileInfo nxt;
+        const bool more = nid < total;
+        if (more) tile_info(nid, nxt);
         if (tid < 64) {
             s_pair[tid] = cur.pr64;
             s_w[tid] = cur.w64;
@@ -667,7 +680,9 @@ __global__ __launch_bounds__(PF_THREADS, 4) void k_prefill_gemm(GemmParams P) {
         PTRACE(((size_t)MODE << 20) + 4 * (size_t)tile + 1, __builtin_amdgcn_s_memrealtime());
         PTRACE(((size_t)MODE << 20) + 4 * (size_t)tile + 2, (uint64_t)cur.mtl);
         PTRACE(((size_t)MODE << 20) + 4 * (size_t)tile + 3, (uint64_t)blockIdx.x);
+        if (tid == 0) s_grab = nid < total ? 2 * G + (int)grab : total;
         if (more) cur = nxt;
+        tile = nid;
     }
 }
 
